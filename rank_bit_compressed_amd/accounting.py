@@ -1,0 +1,57 @@
+"""Algorithmic byte and flop counts of one decode step (closed forms).
+
+These count what the method must read, not what a kernel happens to fetch:
+the roofline figures divide them by measured kernel time.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+
+def dense_bytes_per_token(n_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """Bytes of one token's keys and values in one layer of a dense cache."""
+    return n_kv_heads * head_dim * 2 * elem_bytes
+
+
+def compressed_stream_bytes(w, ranks: torch.Tensor | None, seq_len) -> dict:
+    """Bytes of the compressed cache one decode step reads (all sequences, heads and layers).
+
+    per (token, kv head): K codes r_k/2 + 4 bytes per group, V likewise, and for the rotated residual
+    2 x (32 code bytes + 2 scale bytes); block-shared mode: per token latent/2 + 4 per group, read once
+    for all layers and heads.  Variable rank adds the per-token rank byte and 4-byte offset word.
+    """
+    seq_len = [int(x) for x in seq_len]
+    n_tok = sum(seq_len)
+    if w.shared:
+        per_tok = w.r_k // 2 + 4 * math.ceil(w.r_k / w.group)
+        return {"stream": n_tok * per_tok, "tables": 0, "tokens": n_tok}
+    Hkv = w.n_kv_heads
+    if w.variable_rank:
+        r = torch.cat([ranks[b, :n].to(torch.int64).cpu() for b, n in enumerate(seq_len)])
+        g = (r + w.group - 1) // w.group
+        per_head = int(r.sum()) + 4 * 2 * int(g.sum())          # (r/2 + r/2) code bytes + K and V pairs
+        stream = Hkv * per_head
+        tables = n_tok * (1 + 4)
+    else:
+        per_tok_head = w.r_k // 2 + w.r_v // 2 + 4 * (math.ceil(w.r_k / w.group) + math.ceil(w.r_v / w.group))
+        if w.latent_bits == 32:
+            per_tok_head = 4 * (w.r_k + w.r_v)
+        stream = n_tok * Hkv * per_tok_head
+        tables = 0
+    if w.residual_bits:
+        stream += n_tok * Hkv * 2 * (w.head_dim * w.residual_bits // 8 + 2)
+    return {"stream": stream, "tables": tables, "tokens": n_tok}
+
+
+def upprojection_flops(w, ranks: torch.Tensor | None, seq_len) -> int:
+    """Flops of the key up-projection (the one dense contraction per token and head)."""
+    seq_len = [int(x) for x in seq_len]
+    if w.shared:
+        return 2 * w.head_dim * w.r_k * w.n_kv_heads * w.n_layers * sum(seq_len)
+    if w.variable_rank:
+        r = sum(int(ranks[b, :n].to(torch.int64).sum()) for b, n in enumerate(seq_len))
+    else:
+        r = w.r_k * sum(seq_len)
+    return 2 * w.head_dim * r * w.n_kv_heads

@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs shaped like the pages' Llama-3.1-8B-class decode
+workloads.  This module only draws random inputs (queries, bases, latents,
+ranks, residuals, page tables); it holds none of the method's arithmetic (no
+quantization, projection, rotation or attention).  Both the GPU path and the
+CPU oracle read the tensors it returns.
+
+Distributions (the pages give shapes, not data):
+  * bases: per-KV-head orthonormal d x r matrices, the Q factor of a seeded
+    Gaussian matrix, stored as bf16;
+  * latents: coordinate i (1-based) drawn N(0, 1) * i^-decay, i.e. standard
+    deviation i^-0.7 for the decaying-spectrum workloads; i.i.d. N(0, 1) for
+    the block-shared latent, whose coordinates mix all layers' channels and so
+    have a flat dynamic range;
+  * rotated residual: drawn directly in the rotated domain, N(0, 0.05^2) per
+    element.  An orthonormal rotation of an i.i.d. Gaussian vector is again
+    i.i.d. Gaussian with the same variance, so this has exactly the law of
+    "draw N(0, 0.05^2), then rotate";
+  * queries: N(0, 1) / 8, rounded to bf16 where the workload says bf16;
+  * variable ranks: i.i.d. per (sequence, token) from a discrete distribution;
+  * block tables: identity (contiguous storage) or a seeded permutation of
+    all physical pages.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    r_k: int                      # key rank (cap); block-shared mode: latent dimension
+    r_v: int                      # value rank (cap); block-shared mode: latent dimension
+    group: int = 32
+    latent_bits: int = 4
+    residual_bits: int = 0
+    page_size: int = 256
+    variable_rank: bool = False
+    shared: bool = False
+    n_layers: int = 1
+    rope_theta: float = 0.0
+    q_bf16: bool = True
+    shuffle_pages: bool = False
+    rank_choices: tuple = ()
+    rank_probs: tuple = ()
+    latent_decay: float = 0.7     # 0 = i.i.d. N(0, 1)
+    residual_std: float = 0.05
+    w_std: float = 0.0            # block-shared mode: W entries N(0, w_std^2)
+    seed: int = 0
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def max_blocks(self) -> int:
+        return -(-self.T // self.page_size)
+
+    @property
+    def n_pages(self) -> int:
+        return self.B * self.max_blocks
+
+    def layout_kwargs(self) -> dict:
+        """Geometry common to the GPU library and the oracle."""
+        return dict(n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads, head_dim=self.head_dim,
+                    r_k_cap=self.r_k, r_v_cap=self.r_v, group=self.group, latent_bits=self.latent_bits,
+                    residual_bits=self.residual_bits, page_size=self.page_size,
+                    variable_rank=int(self.variable_rank), shared=int(self.shared), n_layers=self.n_layers,
+                    rope_theta=float(self.rope_theta))
+
+
+# The five workloads of the build's target list; sizes as stated there.
+WORKLOADS = {
+    # batch 1, 4 query / 1 KV head, d 64, 256 tokens, rank-16 bases, fp32 latents, no RoPE
+    "tiny": Workload("tiny", B=1, T=256, n_q_heads=4, n_kv_heads=1, head_dim=64, r_k=16, r_v=16,
+                     group=16, latent_bits=32, rope_theta=0.0, q_bf16=False, seed=11),
+    # one Llama-3.1-8B-shaped layer, batch 1, 8K context, INT4 G32, ranks 48 (K) / 64 (V)
+    "llama8b_layer_8k": Workload("llama8b_layer_8k", B=1, T=8192, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                 r_k=48, r_v=64, group=32, rope_theta=500000.0, seed=12),
+    # batch 16, 32K context, per-token rank in {8,16,32,64}, paged (256) with a shuffled table
+    "varrank_paged_32k": Workload("varrank_paged_32k", B=16, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                  r_k=64, r_v=64, group=32, rope_theta=500000.0, variable_rank=True,
+                                  rank_choices=(8, 16, 32, 64), rank_probs=(0.4, 0.3, 0.2, 0.1),
+                                  shuffle_pages=True, seed=13),
+    # 4 layers share one 512-dim INT4 G64 latent per token; W_k, W_v 512 -> 8 x 128 per layer
+    "shared_latent_32k": Workload("shared_latent_32k", B=4, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                  r_k=512, r_v=512, group=64, shared=True, n_layers=4, rope_theta=500000.0,
+                                  latent_decay=0.0, w_std=1.0 / math.sqrt(512.0), seed=14),
+    # batch 8, 128K context, ranks 48/64, 2-bit rotated residual, paged (256) shuffled
+    "residual_128k": Workload("residual_128k", B=8, T=131072, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                              r_k=48, r_v=64, group=32, residual_bits=2, rope_theta=500000.0,
+                              shuffle_pages=True, seed=15),
+}
+
+
+def _gen(w: Workload, stream: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000 + stream)
+    return g
+
+
+def _decay_scale(r: int, decay: float, device) -> torch.Tensor:
+    i = torch.arange(1, r + 1, dtype=torch.float64, device=device)
+    return (i ** (-decay)).to(torch.float32)
+
+
+def _orthonormal(w: Workload, stream: int, rows: int, cols: int, n: int) -> torch.Tensor:
+    """n matrices rows x cols with orthonormal columns (QR of a seeded Gaussian), fp64 on the CPU."""
+    g = _gen(w, stream, "cpu")
+    a = torch.randn(n, rows, cols, generator=g, dtype=torch.float64)
+    q, r = torch.linalg.qr(a)
+    return q * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1)).unsqueeze(-2)
+
+
+def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
+    """All inputs of one decode step of workload w (seeded, deterministic per device)."""
+    dev = torch.device(device)
+    B, T, Hkv, d, P = w.B, w.T, w.n_kv_heads, w.head_dim, w.page_size
+    out = {}
+    if seq_len is None:
+        seq_len = [T] * B
+    sl = torch.tensor(seq_len, dtype=torch.int32)
+    assert int(sl.max()) <= T and int(sl.min()) >= 1
+    out["seq_len"] = sl.to(dev)
+    out["q_pos"] = sl.clone().to(dev)
+    nb = w.max_blocks
+    if w.shuffle_pages:
+        perm = torch.randperm(w.n_pages, generator=_gen(w, 1, "cpu")).to(torch.int32)
+    else:
+        perm = torch.arange(w.n_pages, dtype=torch.int32)
+    out["block_table"] = perm.view(B, nb).to(dev)
+    if w.variable_rank:
+        u = torch.rand(B, T, generator=_gen(w, 2, "cpu"), dtype=torch.float64)
+        cdf = torch.cumsum(torch.tensor(w.rank_probs, dtype=torch.float64), 0)
+        cdf[-1] = 1.0
+        idx = torch.searchsorted(cdf, u.reshape(-1), right=True).clamp_(max=len(w.rank_choices) - 1)
+        ranks = torch.tensor(w.rank_choices, dtype=torch.uint8)[idx].view(B, T)
+        out["ranks"] = ranks.to(dev)
+    else:
+        out["ranks"] = None
+    gl = _gen(w, 3, dev)
+    if w.shared:
+        lat = torch.randn(B, T, w.r_k, generator=gl, device=dev, dtype=torch.float32)
+        if w.latent_decay:
+            lat *= _decay_scale(w.r_k, w.latent_decay, dev)
+        out["lat_k"], out["lat_v"] = lat, None
+    else:
+        lk = torch.randn(B, T, Hkv, w.r_k, generator=gl, device=dev, dtype=torch.float32)
+        lv = torch.randn(B, T, Hkv, w.r_v, generator=_gen(w, 4, dev), device=dev, dtype=torch.float32)
+        if w.latent_decay:
+            lk *= _decay_scale(w.r_k, w.latent_decay, dev)
+            lv *= _decay_scale(w.r_v, w.latent_decay, dev)
+        out["lat_k"], out["lat_v"] = lk, lv
+    if w.residual_bits:
+        out["res_k"] = torch.randn(B, T, Hkv, d, generator=_gen(w, 5, dev), device=dev) * w.residual_std
+        out["res_v"] = torch.randn(B, T, Hkv, d, generator=_gen(w, 6, dev), device=dev) * w.residual_std
+    else:
+        out["res_k"] = out["res_v"] = None
+    if w.shared:
+        gw = _gen(w, 7, "cpu")
+        shape = (w.n_layers, w.r_k, Hkv * d)
+        out["wk"] = (torch.randn(shape, generator=gw) * w.w_std).to(torch.bfloat16).to(dev)
+        out["wv"] = (torch.randn(shape, generator=gw) * w.w_std).to(torch.bfloat16).to(dev)
+    else:
+        out["wk"] = _orthonormal(w, 8, d, w.r_k, Hkv).to(torch.bfloat16).to(dev)
+        out["wv"] = _orthonormal(w, 9, d, w.r_v, Hkv).to(torch.bfloat16).to(dev)
+    qshape = ((w.n_layers,) if w.shared else ()) + (B, w.n_q_heads, d)
+    q = torch.randn(qshape, generator=_gen(w, 10, "cpu"), dtype=torch.float32) / 8.0
+    out["q"] = (q.to(torch.bfloat16) if w.q_bf16 else q).to(dev)
+    return out
+
+
+def make_dense_inputs(w: Workload, device="cpu") -> dict:
+    """A dense paged bf16 cache of the same geometry (keys already rotated) and a rotated bf16 query."""
+    dev = torch.device(device)
+    shape = (w.n_pages * (w.n_layers if w.shared else 1), w.n_kv_heads, w.page_size, w.head_dim)
+    g = _gen(w, 20, dev)
+    k = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = (torch.randn(w.B, w.n_q_heads, w.head_dim, generator=_gen(w, 21, "cpu")) / 8.0).to(torch.bfloat16)
+    return {"k_pages": k, "v_pages": v, "q": q.to(dev)}
