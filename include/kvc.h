@@ -1,0 +1,221 @@
+/*
+ * kvc.h -- C ABI of librbc_kvc.so: decode-step attention read directly from
+ * a rank/bit-compressed KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page titles and sections of the method's descriptions):
+ *  - Keys and values of each cached token are kept as rank-r latent
+ *    coefficients against a per-KV-head basis ("BELT Connects KV-Cache
+ *    Compression ...", s.2-3; JoLT thesis page, "Key findings": per-head
+ *    SVD), or as one latent per token shared by a block of layers, from
+ *    which each layer rebuilds its own K and V through its own
+ *    up-projection ("BellowsKV Architecture ...", "Share the Input, Not
+ *    the Cache").
+ *  - The latents are stored as INT4 codes with one fp16 scale and one fp16
+ *    zero per group of coordinates (BellowsKV, "Three Measurements, Three
+ *    Operators"; "Worked Example" gives the min/max quantizer form).
+ *  - Optional: a per-token rank, every token kept at nonzero rank
+ *    ("VarRate", "Method"); a 2-bit residual in a Hadamard-rotated domain
+ *    ("A JoLT for the KV cache", abstract: rotated low-bit residual).
+ *  - Keys are stored before RoPE and rotated after reconstruction (JoLT
+ *    thesis page, "Key findings"); attention is evaluated over the stored
+ *    factors without writing a dense K/V to memory (JoLT abstract,
+ *    FlashJoLT decode kernel).
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device memory on the current device; the
+ *    caller owns and allocates all of it (inputs, outputs, workspace).
+ *    Structs and their host fields are read during the call only.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    Nothing synchronizes; errors raised by kernels surface on the stream.
+ *  - A non-zero return means nothing was launched.  All argument checks
+ *    happen before the first launch.  No C++ exception crosses the ABI.
+ *  - Device data is trusted: out-of-range page ids in a block table or
+ *    ranks that disagree with the offset tables are undefined behaviour.
+ *  - Pointers must be 16-byte aligned (KVC_ERR_MISALIGNED otherwise).
+ *  - Same inputs and the same num_splits give bit-identical output; the
+ *    summation order depends on logical positions only, so a permuted page
+ *    table changes nothing.
+ *
+ * Byte layout of the compressed cache ("KVC-1"):
+ *  The pool is a sequence of page records, one per physical page p, at byte
+ *  offset page_off[p] (the exclusive prefix sum of record sizes over p).
+ *  Token t of sequence b sits in page block_table[b][t / P], slot t % P.
+ *  Per-head mode: a record is n_kv_heads head blocks of equal size, head 0
+ *  first; a head block is the sections
+ *     Kc key codes   | Vc value codes | Km key (scale, zero) | Vm value pairs
+ *     [Kr key residual codes P x 32 B | Vr | Ks key residual scale P x fp16 | Vs]
+ *  each padded to a multiple of 16 bytes.  Codes of a slot are its rank r
+ *  INT4 values, coordinate 2j in the low nibble of byte j (r/2 bytes; fp32
+ *  latents: 4r bytes and no pairs); pairs are (fp16 scale, fp16 zero), one
+ *  per group of `group` coordinates, ceil(r/group) per slot; residual
+ *  element i is bits 2(i%4).. of byte i/4, value (code - 1.5) * scale.
+ *  Slots follow one another in slot order inside each section.  Uniform
+ *  rank: every slot of every page holds r_k_cap / r_v_cap.  Variable rank:
+ *  tok_rank[p][s] (0 for unused slots) is the rank of K and V for all heads,
+ *  and tok_off[p][s] holds the exclusive prefix over slots of the ranks
+ *  (bits 0-15) and of ceil(rank/group) (bits 16-31); tok_off[p][P] = totals.
+ *  Block-shared mode: a record is Lc (P x latent/2 code bytes) and Lm
+ *  (P x latent/group pairs), each padded to 16 bytes.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = -1,     /* a size, pointer or layout field is out of range        */
+  KVC_ERR_UNSUPPORTED = -2,     /* valid, but no kernel for this geometry                 */
+  KVC_ERR_WORKSPACE = -3,       /* workspace or pool smaller than required                */
+  KVC_ERR_MISALIGNED = -4,      /* a pointer is not 16-byte aligned                       */
+  KVC_ERR_HIP = -5              /* a HIP runtime call failed (see kvc_last_hip_error)     */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Geometry and format of a compressed cache. */
+typedef struct {
+  int32_t n_q_heads;      /* query heads per layer                                         */
+  int32_t n_kv_heads;     /* KV heads per layer; q head h reads kv head h / (Hq / Hkv)     */
+  int32_t head_dim;       /* d: 64 or 128                                                  */
+  int32_t shared;         /* 0: per-KV-head bases; 1: one latent per token for n_layers    */
+  int32_t n_layers;       /* layers served by a shared latent (1 when shared = 0)          */
+  int32_t r_k_cap;        /* key rank (cap with variable_rank); shared: latent dimension   */
+  int32_t r_v_cap;        /* value rank (cap); shared: equal to r_k_cap                    */
+  int32_t group;          /* quantization group along the latent axis (multiple of 16)     */
+  int32_t latent_bits;    /* 4: INT4 codes + fp16 scale/zero; 32: fp32 latents             */
+  int32_t residual_bits;  /* 0 or 2 (Hadamard-rotated residual; head_dim 128, per-head)    */
+  int32_t page_size;      /* tokens per page, a multiple of 32, at most 256                */
+  int32_t variable_rank;  /* 1: per-token rank in tok_rank / tok_off                       */
+  double rope_theta;      /* RoPE base (rotate-half pairs (j, j + d/2)); 0 = no RoPE       */
+} kvc_layout;
+
+/* A compressed cache in device memory (caller-allocated). */
+typedef struct {
+  uint8_t* pool;          /* page records                                                  */
+  int64_t pool_bytes;     /* capacity of pool                                              */
+  int64_t* page_off;      /* [n_pages] byte offset of each record                          */
+  uint8_t* tok_rank;      /* [n_pages][page_size], variable rank only (else NULL)          */
+  uint32_t* tok_off;      /* [n_pages][page_size + 1], variable rank only (else NULL)      */
+  int64_t* used_bytes;    /* [1] written by kvc_compress: bytes of pool in use (may be NULL) */
+  int32_t n_pages;
+} kvc_cache;
+
+typedef enum { KVC_FROM_LATENT = 0, KVC_FROM_DENSE = 1 } kvc_compress_mode;
+
+/* Inputs of kvc_compress.  All arrays are device memory. */
+typedef struct {
+  int32_t mode;                  /* kvc_compress_mode                                          */
+  int32_t B, max_T, max_blocks;  /* sequences, row length of the token arrays, table width     */
+  const int32_t* block_table;    /* [B][max_blocks]; distinct pages for blocks in use           */
+  const int32_t* seq_len;        /* [B], 1..max_T tokens to compress per sequence               */
+  const uint8_t* ranks;          /* [B][max_T] variable rank: multiple of 8 in [8, cap]        */
+  /* FROM_LATENT: fp32 latents [B][max_T][Hkv][r_cap] (shared mode: lat_k [B][max_T][latent]),
+   * rotated-domain residuals [B][max_T][Hkv][head_dim] (residual_bits = 2).
+   * FROM_DENSE: these four are outputs (required): the fp32 projection c = B_r^T k truncated to
+   * the token's rank, and the rotated truncation residual H (k - B_r c), which are then quantized. */
+  float* lat_k;
+  float* lat_v;
+  float* res_k;
+  float* res_v;
+  /* FROM_DENSE only: pre-RoPE keys/values [B][max_T][Hkv][head_dim] fp32, bases bf16 [Hkv][d][r_cap] */
+  const float* k;
+  const float* v;
+  const uint16_t* basis_k;
+  const uint16_t* basis_v;
+} kvc_compress_in;
+
+/* Inputs of kvc_decode_attn.  All arrays are device memory. */
+typedef struct {
+  int32_t B, max_blocks;         /* sequences, block-table width                               */
+  int32_t max_T;                 /* host-side upper bound of seq_len (sizes the grid)          */
+  const int32_t* block_table;    /* [B][max_blocks]                                             */
+  const int32_t* seq_len;        /* [B], cached tokens, 1..max_T                                */
+  const int32_t* q_pos;          /* [B] RoPE position of the query, NULL = seq_len              */
+  const void* q;                 /* [(n_layers)][B][Hq][d] pre-RoPE, q_dtype                     */
+  int32_t q_dtype;               /* kvc_dtype                                                   */
+  const uint16_t* wk;            /* bf16 basis [Hkv][d][r_k_cap]; shared: W_k [L][latent][Hkv*d] */
+  const uint16_t* wv;            /* bf16 basis [Hkv][d][r_v_cap]; shared: W_v [L][latent][Hkv*d] */
+  int32_t num_splits;            /* context splits per (sequence, head); 0 = automatic          */
+} kvc_decode_in;
+
+/* Inputs of kvc_dense_decode_attn: plain attention over a paged bf16 cache. */
+typedef struct {
+  int32_t n_q_heads, n_kv_heads, head_dim, page_size;
+  int32_t B, max_blocks, max_T;
+  const int32_t* block_table;    /* [B][max_blocks]                                             */
+  const int32_t* seq_len;        /* [B]                                                          */
+  const uint16_t* k_pages;       /* bf16 [n_pages][Hkv][page_size][d], keys already rotated     */
+  const uint16_t* v_pages;       /* bf16 [n_pages][Hkv][page_size][d]                           */
+  const void* q;                 /* [B][Hq][d], already rotated, q_dtype                        */
+  int32_t q_dtype;
+  int32_t num_splits;            /* 0 = automatic                                               */
+} kvc_dense_in;
+
+/* ABI version of the loaded library (KVC_ABI_VERSION). */
+int32_t kvc_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* kvc_status_string(int32_t status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int32_t kvc_last_hip_error(void);
+
+/* Checks a layout against what the library supports. KVC_OK, INVALID_ARG or UNSUPPORTED. */
+kvc_status kvc_layout_check(const kvc_layout* layout);
+
+/* Upper bound of the pool bytes for n_pages pages (every slot at the rank cap). */
+kvc_status kvc_pool_bytes_max(const kvc_layout* layout, int32_t n_pages, int64_t* bytes);
+
+/* Compression (the prefill side; "BELT ...", s.3 low rank + quantization; BellowsKV
+ * "Three Measurements, Three Operators"; JoLT abstract for the rotated residual).
+ * FROM_LATENT quantizes given fp32 latents (and rotated residuals) and packs them into
+ * the pool; FROM_DENSE first projects dense pre-RoPE K/V onto the bases (truncated to each
+ * token's rank), forms the truncation residual and rotates it with the normalized
+ * 128-point Sylvester Hadamard, then quantizes as FROM_LATENT.  Quantizer, per group of
+ * `group` coordinates of one token (the last group of a token may be shorter):
+ * lo/hi = min/max, scale = fp16((hi - lo) / 15), zero = fp16(lo),
+ * code = clamp(rint((x - zero) / scale), 0, 15) in fp32 (0 when scale = 0).  Residual
+ * (128 values): scale = fp16(max|y| / 1.5), code = clamp(rint(y / scale + 1.5), 0, 3)
+ * (2 when scale = 0).  Writes pool, page_off, tok_rank, tok_off and used_bytes;
+ * fills every byte of the pool in use (padding zero).  Slots of pages that no sequence
+ * uses hold rank 0 (variable rank).  Returns KVC_ERR_WORKSPACE if pool_bytes is below
+ * kvc_pool_bytes_max. */
+kvc_status kvc_compress(const kvc_layout* layout, const kvc_compress_in* in, const kvc_cache* cache,
+                        void* stream);
+
+/* Bytes of workspace kvc_decode_attn needs for B sequences of up to max_T tokens and the
+ * given num_splits (0 = automatic: the same choice kvc_decode_attn makes). */
+kvc_status kvc_decode_workspace_bytes(const kvc_layout* layout, int32_t B, int32_t max_T, int32_t num_splits,
+                                      size_t* bytes);
+
+/* One decode step of softmax attention over the compressed cache (hot path).
+ * For every sequence b, layer l (shared mode) and query head h with kv head g = h / (Hq/Hkv):
+ *   k_t = B_k[g] c_k(t) [+ H e_k(t)]   (shared: W_k[l][:, g*d:(g+1)*d]^T c(t))
+ *   v_t = B_v[g] c_v(t) [+ H e_v(t)]
+ *   out[l][b][h] = sum_t softmax_t( RoPE(q, q_pos) . RoPE(k_t, t) / sqrt(d) ) v_t,  t < seq_len[b]
+ * with c the dequantized latent (code * scale + zero, zero beyond the token's rank), e the
+ * dequantized rotated residual and H the normalized 128-point Sylvester Hadamard.
+ * out: fp32 [(n_layers)][B][Hq][d].  ws: workspace of kvc_decode_workspace_bytes. */
+kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                           float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of kvc_dense_decode_attn for these inputs. */
+kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
+
+/* Plain softmax decode attention over a paged bf16 cache whose keys are already rotated: the
+ * dense comparison the JoLT thesis page measures against (FlashJoLT vs a dense bf16 cache).
+ * out: fp32 [B][Hq][d]. */
+kvc_status kvc_dense_decode_attn(const kvc_dense_in* in, float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

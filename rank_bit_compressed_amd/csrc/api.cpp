@@ -1,0 +1,173 @@
+// api.cpp -- the C ABI of librbc_kvc.so: argument checks, launch geometry, dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "kvc_common.hpp"
+
+namespace kvc {
+
+static thread_local int32_t g_last_hip_error = 0;
+
+kvc_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return KVC_ERR_HIP;
+}
+
+// launchers (defined with their kernels)
+bool head_supported(const kvc_layout& L);
+int head_part_stride(int rv_cap, int residual);
+hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
+                              int n_splits, int st_per_split, hipStream_t st, bool* unsupported);
+bool shared_supported(const kvc_layout& L);
+size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits);
+hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
+                                void* ws, int n_splits, int st_per_split, hipStream_t st);
+kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const kvc_cache& C, hipStream_t st);
+kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
+                      size_t* need);
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static kvc_status check_layout(const kvc_layout* L) {
+  if (!L) return KVC_ERR_INVALID_ARG;
+  if (L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->n_q_heads % L->n_kv_heads) return KVC_ERR_INVALID_ARG;
+  if (L->head_dim <= 0 || L->head_dim % 2) return KVC_ERR_INVALID_ARG;
+  if (L->page_size <= 0 || L->page_size > 256) return KVC_ERR_INVALID_ARG;
+  if (L->latent_bits != 4 && L->latent_bits != 32) return KVC_ERR_INVALID_ARG;
+  if (L->r_k_cap <= 0 || L->r_v_cap <= 0 || L->r_k_cap % 8 || L->r_v_cap % 8) return KVC_ERR_INVALID_ARG;
+  if (L->r_k_cap > 1024 || L->r_v_cap > 1024) return KVC_ERR_INVALID_ARG;
+  if (L->latent_bits == 4 && (L->group <= 0 || L->group % 8)) return KVC_ERR_INVALID_ARG;
+  if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_ERR_INVALID_ARG;
+  if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_ERR_INVALID_ARG;
+  if (L->shared) {
+    if (L->n_layers <= 0 || L->latent_bits != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
+      return KVC_ERR_INVALID_ARG;
+  } else if (L->n_layers != 1) {
+    return KVC_ERR_INVALID_ARG;
+  }
+  if (L->variable_rank && (L->latent_bits != 4 || L->r_k_cap != L->r_v_cap)) return KVC_ERR_INVALID_ARG;
+  if (L->variable_rank && L->page_size * L->r_k_cap > 65535) return KVC_ERR_INVALID_ARG;
+  if (!(L->rope_theta >= 0.0) || std::isinf(L->rope_theta)) return KVC_ERR_INVALID_ARG;
+  // what the gfx950 kernels implement
+  if (L->page_size % 32) return KVC_ERR_UNSUPPORTED;
+  if (L->latent_bits == 4 && L->group % 16) return KVC_ERR_UNSUPPORTED;
+  if (L->shared ? !shared_supported(*L) : !head_supported(*L)) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+// Context splits per (sequence, kv head[, layer]) and super-tiles (32 tokens) per split.
+static void choose_splits(const kvc_layout& L, int B, int max_T, int requested, int* n_splits, int* st_per_split) {
+  const int n_st = (max_T + 31) / 32;
+  int units = B * L.n_kv_heads * (L.shared ? L.n_layers : 1);
+  int s = requested;
+  if (s <= 0) {
+    const int target = 1024;  // workgroups: about four per compute unit
+    s = std::max(1, (target + units - 1) / units);
+    s = std::min(s, std::max(1, n_st / 4));  // at least one super-tile per wave
+  }
+  s = std::max(1, std::min(s, n_st));
+  *st_per_split = (n_st + s - 1) / s;
+  *n_splits = (n_st + *st_per_split - 1) / *st_per_split;
+}
+
+static size_t decode_ws_bytes(const kvc_layout& L, int B, int n_splits) {
+  if (L.shared) return shared_ws_bytes(L, B, n_splits);
+  return (size_t)B * L.n_kv_heads * n_splits * 4 * head_part_stride(L.r_v_cap, L.residual_bits) * sizeof(float);
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_string(int32_t s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "unsupported geometry";
+    case KVC_ERR_WORKSPACE: return "workspace or pool too small";
+    case KVC_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case KVC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t kvc_last_hip_error(void) { return g_last_hip_error; }
+
+kvc_status kvc_layout_check(const kvc_layout* layout) { return check_layout(layout); }
+
+kvc_status kvc_pool_bytes_max(const kvc_layout* layout, int32_t n_pages, int64_t* bytes) {
+  kvc_status s = check_layout(layout);
+  if (s == KVC_ERR_INVALID_ARG) return s;
+  if (!bytes || n_pages < 0) return KVC_ERR_INVALID_ARG;
+  *bytes = uniform_page_bytes(*layout) * (int64_t)n_pages;
+  return KVC_OK;
+}
+
+kvc_status kvc_decode_workspace_bytes(const kvc_layout* layout, int32_t B, int32_t max_T, int32_t num_splits,
+                                      size_t* bytes) {
+  kvc_status s = check_layout(layout);
+  if (s) return s;
+  if (!bytes || B <= 0 || max_T <= 0 || num_splits < 0) return KVC_ERR_INVALID_ARG;
+  int ns, sps;
+  choose_splits(*layout, B, max_T, num_splits, &ns, &sps);
+  *bytes = decode_ws_bytes(*layout, B, ns);
+  return KVC_OK;
+}
+
+kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in, float* out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  kvc_status s = check_layout(layout);
+  if (s) return s;
+  if (!cache || !in || !out || !ws) return KVC_ERR_INVALID_ARG;
+  const kvc_layout& L = *layout;
+  if (in->B <= 0 || in->max_blocks <= 0 || in->max_T <= 0 || in->num_splits < 0) return KVC_ERR_INVALID_ARG;
+  if ((int64_t)in->max_blocks * L.page_size < in->max_T) return KVC_ERR_INVALID_ARG;
+  if (in->q_dtype != KVC_F32 && in->q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
+  if (!cache->pool || !cache->page_off || cache->n_pages <= 0) return KVC_ERR_INVALID_ARG;
+  if (L.variable_rank && (!cache->tok_rank || !cache->tok_off)) return KVC_ERR_INVALID_ARG;
+  if (!in->block_table || !in->seq_len || !in->q || !in->wk || !in->wv) return KVC_ERR_INVALID_ARG;
+  const void* ptrs[] = {cache->pool, cache->page_off, cache->tok_rank, cache->tok_off, in->block_table, in->seq_len,
+                        in->q_pos, in->q, in->wk, in->wv, out, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVC_ERR_MISALIGNED;
+  int ns, sps;
+  choose_splits(L, in->B, in->max_T, in->num_splits, &ns, &sps);
+  if (ws_bytes < decode_ws_bytes(L, in->B, ns)) return KVC_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (L.shared) {
+    e = launch_decode_shared(L, *cache, *in, out, ws, ns, sps, st);
+  } else {
+    bool unsupported = false;
+    e = launch_decode_head(L, *cache, *in, out, ws, ns, sps, st, &unsupported);
+    if (unsupported) return KVC_ERR_UNSUPPORTED;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return KVC_OK;
+}
+
+kvc_status kvc_compress(const kvc_layout* layout, const kvc_compress_in* in, const kvc_cache* cache, void* stream) {
+  kvc_status s = check_layout(layout);
+  if (s) return s;
+  if (!in || !cache) return KVC_ERR_INVALID_ARG;
+  return compress_impl(*layout, *in, *cache, (hipStream_t)stream);
+}
+
+kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {
+  if (!in || !bytes) return KVC_ERR_INVALID_ARG;
+  return dense_impl(*in, nullptr, nullptr, 0, nullptr, bytes);
+}
+
+kvc_status kvc_dense_decode_attn(const kvc_dense_in* in, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!in || !out) return KVC_ERR_INVALID_ARG;
+  return dense_impl(*in, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,476 @@
+// decode_head.hip -- one decode step of attention over a per-KV-head compressed cache (gfx950).
+//
+// Work decomposition: one workgroup (4 waves) per (sequence b, KV head h, context split).  The
+// split's tokens are cut into super-tiles of 32 tokens (two 16-token MFMA blocks, never
+// straddling a page); wave w takes super-tiles w, w+4, ...  Each wave keeps its own online-softmax
+// state and writes one partial (max, sum, latent accumulator) per query head; the merge kernel
+// combines the partials and applies the value basis.
+//
+// Per 16-token block (lane l: token l%16, group g = l/16):
+//   K latent codes -> fp16 in registers -> MFMA K_pre = B_k c (basis fragments held in registers;
+//   rows = head dims, columns = tokens) [+ rotated residual: MFMA with the +-1 Hadamard] ->
+//   RoPE in registers (pairs (j, j+d/2) sit in one lane) -> MFMA scores S^T = K~^T Q~^T, whose
+//   output layout is already the A operand of the value product.
+//   V latent codes -> fp16 -> MFMA with a one-hot matrix (a register transpose: tokens move from
+//   lanes into the reduction slots) -> MFMA acc += P V_latent, in the latent space: the value basis
+//   is applied once per (b, head) in the merge (sum_t p_t B c_t = B sum_t p_t c_t).
+// RoPE is split as R(t0 + s) = R(t0) R(s): R(s), s < 32, comes from an LDS table built once per
+// workgroup; R(t0) is applied to the query once per super-tile (q~ = R(q_pos - t0) q).
+#include <math.h>
+
+#include "kvc_common.hpp"
+
+namespace kvc {
+
+struct DecodeHeadArgs {
+  const uint8_t* pool;
+  const int64_t* page_off;
+  const uint8_t* tok_rank;
+  const uint32_t* tok_off;
+  const int32_t* block_table;
+  const int32_t* seq_len;
+  const int32_t* q_pos;
+  const void* q;
+  const uint16_t* wk;
+  float* ws;
+  int q_bf16;
+  int B, Hkv, Hq, max_blocks, P, rk, rv, G, n_splits, st_per_split, part_stride;
+  double theta;
+  HeadSections S_uniform;
+};
+
+static constexpr int GQ = 4;  // query heads per KV head handled by these kernels
+
+template <int D, int KC, int VC, bool LAT32, bool RES, bool VAR>
+__global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
+  constexpr int MT = D / 16;   // M-tiles of the up-projection (16 head dims each)
+  constexpr int QC = D / 32;   // K-chunks of the score product
+  constexpr int NP = D / 2;    // RoPE pairs
+  constexpr int NV = 2 * VC;   // N-tiles of the value product (16 latent dims each)
+  __shared__ uint32_t rope_tab[32][NP];
+  __shared__ uint32_t qbuf[4][16][NP];
+  __shared__ h8 hfrag[RES ? MT * 4 * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x % a.n_splits;
+  const int h = (blockIdx.x / a.n_splits) % a.Hkv;
+  const int b = blockIdx.x / (a.n_splits * a.Hkv);
+  const int T = a.seq_len[b];
+  const int qpos = a.q_pos ? a.q_pos[b] : T;
+  const int P = a.P;
+
+  // in-tile RoPE factors (cos, sin)(s * theta_j), s < 32
+  for (int e = tid; e < 32 * NP; e += 256) {
+    const int s = e / NP, j = e % NP;
+    const double th = a.theta > 0.0 ? pow(a.theta, -2.0 * j / D) : 0.0;
+    float sn, cs;
+    sincosf((float)(s * th), &sn, &cs);
+    rope_tab[s][j] = pack_h2(cs, sn);
+  }
+  for (int e = tid; e < 4 * 16 * NP; e += 256) (&qbuf[0][0][0])[e] = 0u;
+  if constexpr (RES) {
+    // +-1 Sylvester Hadamard as MFMA A fragments: row d = 16m + n, k-slot 8g + j <-> rotated dim
+    // 32c + 8g + perm8(j); entry (-1)^popcount(d & dim)
+    for (int e = tid; e < MT * 4 * 64; e += 256) {
+      const int m = e / 256, c = (e / 64) % 4, l = e % 64;
+      const int d = 16 * m + (l & 15);
+      h8 f;
+      for (int j = 0; j < 8; ++j) {
+        const int dim = 32 * c + 8 * (l >> 4) + perm8(j);
+        f[j] = (__builtin_popcount(d & dim) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      }
+      hfrag[e] = f;
+    }
+  }
+
+  // key basis as A fragments: row d = 16m + n, k-slot 8g + j <-> latent coordinate 8(4c + g) + perm8(j)
+  h8 bk[MT][KC];
+  {
+    const uint16_t* Bk = a.wk + (size_t)h * D * a.rk;
+    for (int m = 0; m < MT; ++m)
+      for (int c = 0; c < KC; ++c)
+        for (int j = 0; j < 8; ++j) {
+          const int col = 8 * (4 * c + g) + (LAT32 ? j : perm8(j));
+          bk[m][c][j] = col < a.rk ? bf16_to_h(Bk[(size_t)(16 * m + n) * a.rk + col]) : (_Float16)0.0f;
+        }
+  }
+  // one-hot B operands of the register transpose: column n of half e takes k-slot with coordinate 16e + n
+  h8 oh[2];
+  for (int e = 0; e < 2; ++e)
+    for (int j = 0; j < 8; ++j)
+      oh[e][j] = (8 * g + (LAT32 ? j : perm8(j)) == 16 * e + n) ? (_Float16)1.0f : (_Float16)0.0f;
+
+  // query pairs (j, j + d/2) of the GQ heads in lane j, scaled by log2(e) / sqrt(d) for exp2
+  float qa[GQ], qb[GQ];
+  double fj = 0.0;
+  {
+    const float sc = 1.4426950408889634f / sqrtf((float)D);
+    const int jj = lane < NP ? lane : 0;
+    for (int hq = 0; hq < GQ; ++hq) {
+      const size_t base = ((size_t)b * a.Hq + h * GQ + hq) * D;
+      float x0, x1;
+      if (a.q_bf16) {
+        const uint16_t* q = (const uint16_t*)a.q + base;
+        x0 = __builtin_bit_cast(float, (uint32_t)q[jj] << 16);
+        x1 = __builtin_bit_cast(float, (uint32_t)q[jj + NP] << 16);
+      } else {
+        const float* q = (const float*)a.q + base;
+        x0 = q[jj];
+        x1 = q[jj + NP];
+      }
+      qa[hq] = x0 * sc;
+      qb[hq] = x1 * sc;
+    }
+    if (a.theta > 0.0) fj = pow(a.theta, -2.0 * jj / D) * 0.15915494309189535;  // revolutions per position
+  }
+  __syncthreads();
+
+  f4 acc[NV];
+  f4 accr[RES ? 8 : 1];
+  for (int i = 0; i < NV; ++i) acc[i] = f4{0, 0, 0, 0};
+  for (int i = 0; i < (RES ? 8 : 1); ++i) accr[i] = f4{0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int kcode_b = LAT32 ? 4 * a.rk : a.rk / 2, vcode_b = LAT32 ? 4 * a.rv : a.rv / 2;
+  const int kmeta_b = LAT32 ? 0 : 4 * ceil_div(a.rk, a.G), vmeta_b = LAT32 ? 0 : 4 * ceil_div(a.rv, a.G);
+  const int n_st = (T + 31) / 32;
+  const int st_begin = split * a.st_per_split;
+  const int st_end = min(n_st, st_begin + a.st_per_split);
+  for (int st = st_begin + wv; st < st_end; st += 4) {
+    const int t0 = st * 32;
+    const int slot0 = t0 % P;
+    const int page = uniform(a.block_table[(size_t)b * a.max_blocks + t0 / P]);
+    const uint8_t* rec = a.pool + uniform64(a.page_off[page]);
+    HeadSections S;
+    if constexpr (VAR) {
+      const uint32_t tot = uniform(a.tok_off[(size_t)page * (P + 1) + P]);
+      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      S = head_sections(cb, cb, mb, mb, P, D, RES);
+    } else {
+      S = a.S_uniform;
+    }
+    const uint8_t* hbase = rec + (int64_t)h * S.hb;
+
+    // query rotated by the super-tile base: q~ = R(q_pos - t0) q
+    if (lane < NP) {
+      double rev = (double)(qpos - t0) * fj;
+      rev -= rint(rev);
+      float sn, cs;
+      sincosf((float)(rev * 6.283185307179586), &sn, &cs);
+      for (int hq = 0; hq < GQ; ++hq) qbuf[wv][hq][lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    h8 qop[QC];
+    for (int c = 0; c < QC; ++c) qop[c] = *(const h8*)&qbuf[wv][n][16 * c + 4 * g];
+
+    float sc[2][4];
+    h4 vtb[NV][2];
+    h4 vrtb[RES ? 8 : 1][2];
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tt = 16 * blk + n;
+      const int t = t0 + tt;
+      const bool valid = t < T;
+      const int slot = slot0 + tt;
+      int rk_t, rv_t;
+      int64_t kco, vco, kmo, vmo;
+      if constexpr (VAR) {
+        const uint32_t o = valid ? a.tok_off[(size_t)page * (P + 1) + slot] : 0u;
+        const int r = valid ? (int)a.tok_rank[(size_t)page * P + slot] : 0;
+        rk_t = rv_t = r;
+        kco = vco = (o & 0xFFFFu) / 2;
+        kmo = vmo = 4 * (int64_t)(o >> 16);
+      } else {
+        rk_t = valid ? a.rk : 0;
+        rv_t = valid ? a.rv : 0;
+        kco = (int64_t)slot * kcode_b; vco = (int64_t)slot * vcode_b;
+        kmo = (int64_t)slot * kmeta_b; vmo = (int64_t)slot * vmeta_b;
+      }
+
+      // ---- keys: latent -> fp16 B operand, up-projection
+      h8 kb[KC];
+      for (int c = 0; c < KC; ++c) {
+        const int w = 4 * c + g;
+        const bool ok = 8 * w < rk_t;
+        if constexpr (LAT32) {
+          const float* src = (const float*)(hbase + S.kc + kco) + 8 * w;
+          for (int j = 0; j < 8; ++j) kb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
+        } else {
+          const uint32_t x = ok ? *(const uint32_t*)(hbase + S.kc + kco + 4 * w) : 0u;
+          const uint32_t sz = ok ? *(const uint32_t*)(hbase + S.km + kmo + 4 * ((8 * w) / a.G)) : 0u;
+          kb[c] = dequant_int4x8(x, sz);
+        }
+      }
+      f4 kp[MT];
+      for (int m = 0; m < MT; ++m) kp[m] = f4{0, 0, 0, 0};
+      for (int c = 0; c < KC; ++c) {
+        if (c > 0 && __builtin_amdgcn_ballot_w64(rk_t > 32 * c) == 0) break;
+        for (int m = 0; m < MT; ++m) kp[m] = mfma16x16x32(bk[m][c], kb[c], kp[m]);
+      }
+      uint32_t rres[8];
+      h2 rss = {(_Float16)0.0f, (_Float16)0.0f};
+      if constexpr (RES) {
+        // key residual: 32 code bytes of the slot (k-slot 8g + j of chunk c <-> rotated dim 32c + 8g + perm8(j))
+        const u4* src = (const u4*)(hbase + S.kr + (int64_t)slot * 32);
+        const u4 lo = valid ? src[0] : u4{0, 0, 0, 0}, hi = valid ? src[1] : u4{0, 0, 0, 0};
+        rres[0] = lo.x; rres[1] = lo.y; rres[2] = lo.z; rres[3] = lo.w;
+        rres[4] = hi.x; rres[5] = hi.y; rres[6] = hi.z; rres[7] = hi.w;
+        const uint16_t s16 = valid ? *(const uint16_t*)(hbase + S.ks + 2 * slot) : (uint16_t)0;
+        const float s = (float)__builtin_bit_cast(_Float16, s16) * 0.04419417382415922f;  // 1/(2 sqrt(128)): codes decode as 2c - 3
+        rss = h2{(_Float16)s, (_Float16)s};
+        for (int c = 0; c < 4; ++c) {
+          const int byte = 8 * c + 2 * g;  // 8 codes of k-slots 8g..8g+7 of chunk c
+          const uint32_t u16 = (rres[byte >> 2] >> (8 * (byte & 3))) & 0xFFFFu;
+          const h8 e = dequant_res2x8(u16, rss);
+          for (int m = 0; m < MT; ++m) kp[m] = mfma16x16x32(hfrag[(m * 4 + c) * 64 + lane], e, kp[m]);
+        }
+      }
+
+      // ---- RoPE on the reconstructed key (offset tt inside the super-tile), packed as the score A operand
+      h8 kq[QC];
+      for (int c = 0; c < QC; ++c)
+        for (int i = 0; i < 4; ++i) {
+          const h2 v = {(_Float16)kp[c][i], (_Float16)kp[c + QC][i]};
+          const h2 f = as_h2(rope_tab[tt][16 * c + 4 * g + i]);
+          const h2 sgn = {-f.y, f.y};
+          const h2 r = v * f.xx + v.yx * sgn;
+          kq[c][2 * i] = r.x;
+          kq[c][2 * i + 1] = r.y;
+        }
+      f4 s4 = {0, 0, 0, 0};
+      for (int c = 0; c < QC; ++c) s4 = mfma16x16x32(kq[c], qop[c], s4);
+      for (int i = 0; i < 4; ++i) sc[blk][i] = s4[i];
+
+      // ---- values: latent -> fp16, register transpose through a one-hot MFMA
+      h8 vb[VC];
+      for (int c = 0; c < VC; ++c) {
+        const int w = 4 * c + g;
+        const bool ok = 8 * w < rv_t;
+        if constexpr (LAT32) {
+          const float* src = (const float*)(hbase + S.vc + vco) + 8 * w;
+          for (int j = 0; j < 8; ++j) vb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
+        } else {
+          const uint32_t x = ok ? *(const uint32_t*)(hbase + S.vc + vco + 4 * w) : 0u;
+          const uint32_t sz = ok ? *(const uint32_t*)(hbase + S.vm + vmo + 4 * ((8 * w) / a.G)) : 0u;
+          vb[c] = dequant_int4x8(x, sz);
+        }
+      }
+      for (int nt = 0; nt < NV; ++nt) {
+        f4 tr = {0, 0, 0, 0};
+        if (nt == 0 || __builtin_amdgcn_ballot_w64(rv_t > 16 * nt) != 0) tr = mfma16x16x32(vb[nt >> 1], oh[nt & 1], tr);
+        vtb[nt][blk] = h4{(_Float16)tr[0], (_Float16)tr[1], (_Float16)tr[2], (_Float16)tr[3]};
+      }
+      if constexpr (RES) {
+        const u4* src = (const u4*)(hbase + S.vr + (int64_t)slot * 32);
+        const u4 lo = valid ? src[0] : u4{0, 0, 0, 0}, hi = valid ? src[1] : u4{0, 0, 0, 0};
+        rres[0] = lo.x; rres[1] = lo.y; rres[2] = lo.z; rres[3] = lo.w;
+        rres[4] = hi.x; rres[5] = hi.y; rres[6] = hi.z; rres[7] = hi.w;
+        const uint16_t s16 = valid ? *(const uint16_t*)(hbase + S.vs + 2 * slot) : (uint16_t)0;
+        const float s = (float)__builtin_bit_cast(_Float16, s16) * 0.04419417382415922f;
+        rss = h2{(_Float16)s, (_Float16)s};
+        for (int c = 0; c < 4; ++c) {
+          const int byte = 8 * c + 2 * g;
+          const uint32_t u16 = (rres[byte >> 2] >> (8 * (byte & 3))) & 0xFFFFu;
+          const h8 e = dequant_res2x8(u16, rss);
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            const f4 tr = mfma16x16x32(e, oh[hlf], f4{0, 0, 0, 0});
+            vrtb[2 * c + hlf][blk] = h4{(_Float16)tr[0], (_Float16)tr[1], (_Float16)tr[2], (_Float16)tr[3]};
+          }
+        }
+      }
+    }
+
+    // ---- online softmax over the 32 scores; lane (head n, group g) holds tokens 4g..4g+3 of each block
+    float mx = -INFINITY;
+    for (int blk = 0; blk < 2; ++blk)
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (n < GQ) && (t0 + 16 * blk + 4 * g + i < T);
+        sc[blk][i] = ok ? sc[blk][i] : -INFINITY;
+        mx = fmaxf(mx, sc[blk][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    h8 pop;
+    float psum = 0.0f;
+    for (int blk = 0; blk < 2; ++blk)
+      for (int i = 0; i < 4; ++i) {
+        const float p = (m_new == -INFINITY) ? 0.0f : exp2f(sc[blk][i] - m_new);
+        const _Float16 ph = (_Float16)p;
+        pop[4 * blk + i] = ph;
+        psum += (float)ph;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      float al[4];
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+      for (int nt = 0; nt < NV; ++nt)
+        for (int i = 0; i < 4; ++i) acc[nt][i] *= al[i];
+      if constexpr (RES)
+        for (int nt = 0; nt < 8; ++nt)
+          for (int i = 0; i < 4; ++i) accr[nt][i] *= al[i];
+    }
+    for (int nt = 0; nt < NV; ++nt) {
+      const h8 vt = {vtb[nt][0][0], vtb[nt][0][1], vtb[nt][0][2], vtb[nt][0][3],
+                     vtb[nt][1][0], vtb[nt][1][1], vtb[nt][1][2], vtb[nt][1][3]};
+      acc[nt] = mfma16x16x32(pop, vt, acc[nt]);
+    }
+    if constexpr (RES)
+      for (int nt = 0; nt < 8; ++nt) {
+        const h8 vt = {vrtb[nt][0][0], vrtb[nt][0][1], vrtb[nt][0][2], vrtb[nt][0][3],
+                       vrtb[nt][1][0], vrtb[nt][1][1], vrtb[nt][1][2], vrtb[nt][1][3]};
+        accr[nt] = mfma16x16x32(pop, vt, accr[nt]);
+      }
+  }
+
+  // ---- partial of this wave: m[GQ], l[GQ], acc[GQ][NV*16] (latent), accr[GQ][128] (rotated residual)
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  float* part = a.ws + ((size_t)((b * a.Hkv + h) * a.n_splits + split) * 4 + wv) * a.part_stride;
+  if (lane < GQ) {
+    part[lane] = m_run;
+    part[GQ + lane] = l_run;
+  }
+  float* pacc = part + 2 * GQ;
+  for (int nt = 0; nt < NV; ++nt)
+    for (int i = 0; i < 4; ++i) {
+      const int hq = 4 * g + i;
+      if (hq < GQ) pacc[hq * (NV * 16) + 16 * nt + n] = acc[nt][i];
+    }
+  if constexpr (RES) {
+    float* pr = pacc + GQ * NV * 16;
+    for (int nt = 0; nt < 8; ++nt)
+      for (int i = 0; i < 4; ++i) {
+        const int hq = 4 * g + i;
+        if (hq < GQ) pr[hq * 128 + 16 * nt + n] = accr[nt][i];
+      }
+  }
+}
+
+// Combine the partials of one (b, kv head): m* = max m, w_p = 2^(m_p - m*), l* = sum w_p l_p,
+// c* = sum w_p acc_p; out = (B_v c* [+ H r*]) / l*.
+template <int D, int NV, bool RES>
+__global__ __launch_bounds__(256) void merge_head_kernel(const float* ws, const uint16_t* wv, float* out, int Hkv,
+                                                         int Hq, int rv, int n_parts, int part_stride) {
+  __shared__ float cst[GQ][NV * 16];
+  __shared__ float rst[RES ? GQ : 1][RES ? 128 : 1];
+  __shared__ float lst[GQ];
+  const int bh = blockIdx.x, h = bh % Hkv, b = bh / Hkv;
+  const int tid = threadIdx.x, hq = tid / 64, l = tid % 64;
+  const float* parts = ws + (size_t)bh * n_parts * part_stride;
+  float m = -INFINITY;
+  for (int p = 0; p < n_parts; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
+  float lsum = 0.0f, c0 = 0.0f, c1 = 0.0f, r0 = 0.0f, r1 = 0.0f;
+  for (int p = 0; p < n_parts; ++p) {
+    const float* pp = parts + (size_t)p * part_stride;
+    const float mp = pp[hq];
+    if (mp == -INFINITY) continue;
+    const float wgt = exp2f(mp - m);
+    lsum += wgt * pp[GQ + hq];
+    const float* pa = pp + 2 * GQ + hq * NV * 16;
+    if (l < NV * 16) c0 += wgt * pa[l];
+    if (NV * 16 > 64 && l + 64 < NV * 16) c1 += wgt * pa[l + 64];
+    if constexpr (RES) {
+      const float* pr = pp + 2 * GQ + GQ * NV * 16 + hq * 128;
+      r0 += wgt * pr[l];
+      r1 += wgt * pr[l + 64];
+    }
+  }
+  if (l < NV * 16) cst[hq][l] = c0;
+  if (NV * 16 > 64 && l + 64 < NV * 16) cst[hq][l + 64] = c1;
+  if constexpr (RES) {
+    rst[hq][l] = r0;
+    rst[hq][l + 64] = r1;
+  }
+  if (l == 0) lst[hq] = lsum;
+  __syncthreads();
+  const float inv = 1.0f / lst[hq];
+  const uint16_t* Bv = wv + (size_t)h * D * rv;
+  for (int d = l; d < D; d += 64) {
+    float o = 0.0f;
+    for (int i = 0; i < rv; ++i) o += __builtin_bit_cast(float, (uint32_t)Bv[(size_t)d * rv + i] << 16) * cst[hq][i];
+    if constexpr (RES) {
+      float rr = 0.0f;
+      for (int i = 0; i < 128; ++i) rr += (__builtin_popcount(d & i) & 1) ? -rst[hq][i] : rst[hq][i];
+      o += rr;
+    }
+    out[((size_t)b * Hq + h * GQ + hq) * D + d] = o * inv;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct HeadVariant {
+  int D, KC, VC;
+  bool lat32, res, var;
+};
+
+template <int D, int KC, int VC, bool LAT32, bool RES, bool VAR>
+static hipError_t launch_variant(const DecodeHeadArgs& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
+  hipLaunchKernelGGL((decode_head_kernel<D, KC, VC, LAT32, RES, VAR>), dim3(grid), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_head_kernel<D, 2 * VC, RES>), dim3(a.B * a.Hkv), dim3(256), 0, st, a.ws, wv, out, a.Hkv,
+                     a.Hq, a.rv, a.n_splits * 4, a.part_stride);
+  return hipGetLastError();
+}
+
+int head_part_stride(int rv_cap, int residual) {
+  const int NV = 2 * ceil_div(rv_cap, 32);
+  return 2 * GQ + GQ * NV * 16 + (residual ? GQ * 128 : 0);
+}
+
+bool head_supported(const kvc_layout& L) {
+  if (L.shared) return false;
+  if (L.n_q_heads != GQ * L.n_kv_heads) return false;
+  if (L.head_dim != 64 && L.head_dim != 128) return false;
+  if (L.r_k_cap > 64 || L.r_v_cap > 64) return false;
+  if (L.residual_bits && L.head_dim != 128) return false;
+  if (L.latent_bits == 4 && L.group % 16) return false;
+  return true;
+}
+
+// Returns hipSuccess or the launch error; `unsupported` set when no variant matches.
+hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
+                              int n_splits, int st_per_split, hipStream_t st, bool* unsupported) {
+  DecodeHeadArgs a;
+  a.pool = C.pool; a.page_off = C.page_off; a.tok_rank = C.tok_rank; a.tok_off = C.tok_off;
+  a.block_table = in.block_table; a.seq_len = in.seq_len; a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk;
+  a.ws = (float*)ws; a.q_bf16 = in.q_dtype == KVC_BF16;
+  a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.max_blocks = in.max_blocks; a.P = L.page_size;
+  a.rk = L.r_k_cap; a.rv = L.r_v_cap; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
+  a.part_stride = head_part_stride(L.r_v_cap, L.residual_bits);
+  a.theta = L.rope_theta;
+  const int P = L.page_size;
+  a.S_uniform = head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
+                              (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
+                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
+                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
+                              L.residual_bits);
+  const int grid = in.B * L.n_kv_heads * n_splits;
+  const int KC = ceil_div(L.r_k_cap, 32), VC = ceil_div(L.r_v_cap, 32);
+  const bool lat32 = L.latent_bits == 32, res = L.residual_bits != 0, var = L.variable_rank != 0;
+  *unsupported = false;
+#define KVC_TRY(D_, KC_, VC_, L32_, RES_, VAR_)                                                          \
+  if (L.head_dim == D_ && KC == KC_ && VC == VC_ && lat32 == L32_ && res == RES_ && var == VAR_)         \
+    return launch_variant<D_, KC_, VC_, L32_, RES_, VAR_>(a, grid, in.wv, out, st);
+  KVC_TRY(128, 2, 2, false, false, false)
+  KVC_TRY(128, 2, 2, false, false, true)
+  KVC_TRY(128, 2, 2, false, true, false)
+  KVC_TRY(128, 1, 1, false, false, false)
+  KVC_TRY(128, 1, 1, false, false, true)
+  KVC_TRY(64, 1, 1, true, false, false)
+  KVC_TRY(64, 2, 2, true, false, false)
+  KVC_TRY(64, 2, 2, false, false, false)
+  KVC_TRY(64, 2, 2, false, false, true)
+  KVC_TRY(64, 1, 1, false, false, false)
+#undef KVC_TRY
+  *unsupported = true;
+  return hipSuccess;
+}
+
+}  // namespace kvc

@@ -1,0 +1,141 @@
+// kvc_common.hpp -- shared definitions of the gfx950 kernels and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+#define KVC_WAVE 64
+
+namespace kvc {
+
+// Record the HIP error of this thread and map it to a status.
+kvc_status hip_fail(hipError_t e);
+
+__host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t(15); }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Byte offsets of the sections of one head block (per-head mode) relative to the head block start,
+// and the head block size.  ck/cv: code bytes of the page, mk/mv: pair bytes of the page.
+struct HeadSections {
+  int64_t kc, vc, km, vm, kr, vr, ks, vs, hb;
+};
+
+__host__ __device__ inline HeadSections head_sections(int64_t ck, int64_t cv, int64_t mk, int64_t mv, int P,
+                                                      int d, int residual) {
+  HeadSections S;
+  int64_t off = 0;
+  S.kc = off; off += pad16(ck);
+  S.vc = off; off += pad16(cv);
+  S.km = off; off += pad16(mk);
+  S.vm = off; off += pad16(mv);
+  S.kr = S.vr = S.ks = S.vs = off;
+  if (residual) {
+    S.kr = off; off += pad16((int64_t)P * d / 4);
+    S.vr = off; off += pad16((int64_t)P * d / 4);
+    S.ks = off; off += pad16((int64_t)P * 2);
+    S.vs = off; off += pad16((int64_t)P * 2);
+  }
+  S.hb = off;
+  return S;
+}
+
+// Code and pair bytes of a slot of rank r.
+__host__ __device__ inline int slot_code_bytes(int latent_bits, int r) { return latent_bits == 4 ? r / 2 : 4 * r; }
+__host__ __device__ inline int slot_meta_bytes(int latent_bits, int r, int G) {
+  return latent_bits == 4 ? 4 * ceil_div(r, G) : 0;
+}
+
+// Uniform-rank page record size (per-head or shared mode).
+__host__ __device__ inline int64_t uniform_page_bytes(const kvc_layout& L) {
+  const int P = L.page_size;
+  if (L.shared) return pad16((int64_t)P * L.r_k_cap / 2) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
+  HeadSections S = head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
+                                 (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
+                                 (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
+                                 (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
+                                 L.residual_bits);
+  return S.hb * L.n_kv_heads;
+}
+
+// ---- device helpers ----
+
+__device__ inline h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ inline uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// fp32 pair -> packed fp16 pair, round to nearest even.
+__device__ inline uint32_t pack_h2(float a, float b) {
+  h2 v = {(_Float16)a, (_Float16)b};
+  return as_u32(v);
+}
+
+// bf16 bits -> fp16 (exact for the normal range of fp16).
+__device__ inline _Float16 bf16_to_h(uint16_t b) {
+  return (_Float16)__builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Eight INT4 codes (one dword, coordinate 2j in the low nibble of byte j) dequantized as
+// code * scale + zero in fp16; sz holds (scale, zero) as two fp16.  The result is in the order
+// (0,4,1,5,2,6,3,7): element j is coordinate perm8(j) = j/2 + 4 (j%2).  Each step is exact
+// except the final fused multiply-add, which rounds once.
+__device__ inline h8 dequant_int4x8(uint32_t x, uint32_t sz) {
+  const uint32_t magic = 0x64006400u;  // fp16 1024.0 in both halves: 1024 + q is exact for q < 1024
+  uint32_t y0 = (x & 0x000F000Fu) | magic;
+  uint32_t y1 = ((x >> 4) & 0x000F000Fu) | magic;
+  uint32_t y2 = ((x >> 8) & 0x000F000Fu) | magic;
+  uint32_t y3 = ((x >> 12) & 0x000F000Fu) | magic;
+  const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  h2 s = as_h2(sz);
+  h2 ss = s.xx, zz = s.yy;
+  h2 a0 = (as_h2(y0) - k1024) * ss + zz;
+  h2 a1 = (as_h2(y1) - k1024) * ss + zz;
+  h2 a2 = (as_h2(y2) - k1024) * ss + zz;
+  h2 a3 = (as_h2(y3) - k1024) * ss + zz;
+  h8 r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+  return r;
+}
+
+__host__ __device__ inline int perm8(int j) { return (j >> 1) + 4 * (j & 1); }
+
+// Eight 2-bit residual codes (16 bits, code j at bits 2j) as (2 code - 3) * s2 in fp16, order perm8.
+// Each code is placed doubled in the low mantissa bits of fp16 1024, so (1024 + 2c) - 1027 = 2c - 3 is
+// exact (1027 is an fp16 integer; 1025.5 would not be); with s2 = scale / 2 this is (c - 1.5) * scale.
+__device__ inline h8 dequant_res2x8(uint32_t u16, h2 s2) {
+  const uint32_t magic = 0x64006400u;
+  const uint32_t w = ((u16 & 0xFFu) | ((u16 & 0xFF00u) << 8)) << 1;  // codes 0-3 at bits 1-8, 4-7 at 17-24
+  const uint32_t y0 = (w & 0x00060006u) | magic;
+  const uint32_t y1 = ((w >> 2) & 0x00060006u) | magic;
+  const uint32_t y2 = ((w >> 4) & 0x00060006u) | magic;
+  const uint32_t y3 = ((w >> 6) & 0x00060006u) | magic;
+  const h2 off = {(_Float16)1027.0f, (_Float16)1027.0f};
+  const h2 a0 = (as_h2(y0) - off) * s2;
+  const h2 a1 = (as_h2(y1) - off) * s2;
+  const h2 a2 = (as_h2(y2) - off) * s2;
+  const h2 a3 = (as_h2(y3) - off) * s2;
+  h8 r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+  return r;
+}
+
+__device__ inline f4 mfma16x16x32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+template <typename T>
+__device__ inline T uniform(T v) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ inline int64_t uniform64(int64_t v) {
+  int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)v);
+  int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+}  // namespace kvc

@@ -1,0 +1,231 @@
+"""Thin Python binding of librbc_kvc.so (include/kvc.h): argument marshalling only.
+
+Every step of compression and decode runs in the library's HIP kernels; this
+module turns torch tensors (device memory) into raw pointers and the current
+HIP stream into the stream argument.  If the library is not built, importing
+any call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librbc_kvc.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kvc.h")
+
+KVC_F32, KVC_BF16 = 0, 1
+KVC_FROM_LATENT, KVC_FROM_DENSE = 0, 1
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "workspace or pool too small",
+          -4: "pointer not 16-byte aligned", -5: "HIP runtime error"}
+EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
+           "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
+           "kvc_dense_decode_attn"]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if hip:
+            msg += f" (hipError {hip})"
+        super().__init__(msg)
+        self.status = status
+
+
+class Layout(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("shared", C.c_int32), ("n_layers", C.c_int32), ("r_k_cap", C.c_int32), ("r_v_cap", C.c_int32),
+                ("group", C.c_int32), ("latent_bits", C.c_int32), ("residual_bits", C.c_int32),
+                ("page_size", C.c_int32), ("variable_rank", C.c_int32), ("rope_theta", C.c_double)]
+
+
+class Cache(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("pool_bytes", C.c_int64), ("page_off", C.c_void_p),
+                ("tok_rank", C.c_void_p), ("tok_off", C.c_void_p), ("used_bytes", C.c_void_p),
+                ("n_pages", C.c_int32)]
+
+
+class CompressIn(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("B", C.c_int32), ("max_T", C.c_int32), ("max_blocks", C.c_int32),
+                ("block_table", C.c_void_p), ("seq_len", C.c_void_p), ("ranks", C.c_void_p),
+                ("lat_k", C.c_void_p), ("lat_v", C.c_void_p), ("res_k", C.c_void_p), ("res_v", C.c_void_p),
+                ("k", C.c_void_p), ("v", C.c_void_p), ("basis_k", C.c_void_p), ("basis_v", C.c_void_p)]
+
+
+class DecodeIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32), ("block_table", C.c_void_p),
+                ("seq_len", C.c_void_p), ("q_pos", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32),
+                ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32)]
+
+
+class DenseIn(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_size", C.c_int32), ("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32),
+                ("block_table", C.c_void_p), ("seq_len", C.c_void_p), ("k_pages", C.c_void_p),
+                ("v_pages", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32), ("num_splits", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librbc_kvc.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with rank_bit_compressed_amd.build.build()")
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        L.kvc_abi_version.restype = C.c_int32
+        L.kvc_status_string.argtypes = [C.c_int32]; L.kvc_status_string.restype = C.c_char_p
+        L.kvc_last_hip_error.restype = C.c_int32
+        L.kvc_layout_check.argtypes = [P]; L.kvc_layout_check.restype = C.c_int32
+        L.kvc_pool_bytes_max.argtypes = [P, C.c_int32, P]; L.kvc_pool_bytes_max.restype = C.c_int32
+        L.kvc_compress.argtypes = [P, P, P, P]; L.kvc_compress.restype = C.c_int32
+        L.kvc_decode_workspace_bytes.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P]
+        L.kvc_decode_workspace_bytes.restype = C.c_int32
+        L.kvc_decode_attn.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_decode_attn.restype = C.c_int32
+        L.kvc_dense_workspace_bytes.argtypes = [P, P]; L.kvc_dense_workspace_bytes.restype = C.c_int32
+        L.kvc_dense_decode_attn.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_dense_decode_attn.restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KvcError(status, where, lib().kvc_last_hip_error() if status == -5 else 0)
+
+
+def make_layout(**kw) -> Layout:
+    f = dict(n_q_heads=0, n_kv_heads=0, head_dim=0, shared=0, n_layers=1, r_k_cap=0, r_v_cap=0, group=32,
+             latent_bits=4, residual_bits=0, page_size=256, variable_rank=0, rope_theta=0.0)
+    f.update(kw)
+    return Layout(**f)
+
+
+def layout_check(layout: Layout) -> int:
+    return lib().kvc_layout_check(C.byref(layout))
+
+
+def pool_bytes_max(layout: Layout, n_pages: int) -> int:
+    out = C.c_int64()
+    _check(lib().kvc_pool_bytes_max(C.byref(layout), n_pages, C.byref(out)), "kvc_pool_bytes_max")
+    return out.value
+
+
+@dataclass
+class DeviceCache:
+    """Device buffers of one compressed cache (allocated by torch, filled by kvc_compress)."""
+    layout: Layout
+    pool: torch.Tensor
+    page_off: torch.Tensor
+    tok_rank: torch.Tensor | None
+    tok_off: torch.Tensor | None
+    used_bytes: torch.Tensor
+    n_pages: int
+
+    @classmethod
+    def allocate(cls, layout: Layout, n_pages: int, device="cuda") -> "DeviceCache":
+        nbytes = pool_bytes_max(layout, n_pages)
+        P = layout.page_size
+        var = bool(layout.variable_rank)
+        return cls(layout, torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device),
+                   torch.empty(n_pages, dtype=torch.int64, device=device),
+                   torch.empty(n_pages, P, dtype=torch.uint8, device=device) if var else None,
+                   torch.empty(n_pages, P + 1, dtype=torch.int32, device=device) if var else None,
+                   torch.zeros(2, dtype=torch.int64, device=device), n_pages)
+
+    def c(self) -> Cache:
+        return Cache(_ptr(self.pool), self.pool.numel(), _ptr(self.page_off), _ptr(self.tok_rank),
+                     _ptr(self.tok_off), _ptr(self.used_bytes), self.n_pages)
+
+
+def compress(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, ranks=None, lat_k=None, lat_v=None,
+             res_k=None, res_v=None, k=None, v=None, basis_k=None, basis_v=None):
+    """kvc_compress.  FROM_DENSE when k/v are given (lat_*/res_* are then outputs)."""
+    mode = KVC_FROM_DENSE if k is not None else KVC_FROM_LATENT
+    B, max_blocks = block_table.shape
+    bk = basis_k.view(torch.int16) if basis_k is not None else None
+    bv = basis_v.view(torch.int16) if basis_v is not None else None
+    inp = CompressIn(mode, B, max_T, max_blocks, _ptr(block_table), _ptr(seq_len), _ptr(ranks), _ptr(lat_k),
+                     _ptr(lat_v), _ptr(res_k), _ptr(res_v), _ptr(k), _ptr(v), _ptr(bk), _ptr(bv))
+    c = cache.c()
+    _check(lib().kvc_compress(C.byref(layout), C.byref(inp), C.byref(c), _stream()), "kvc_compress")
+
+
+def decode_workspace_bytes(layout: Layout, B: int, max_T: int, num_splits: int = 0) -> int:
+    out = C.c_size_t()
+    _check(lib().kvc_decode_workspace_bytes(C.byref(layout), B, max_T, num_splits, C.byref(out)),
+           "kvc_decode_workspace_bytes")
+    return out.value
+
+
+def _q_dtype(q):
+    if q.dtype == torch.bfloat16:
+        return KVC_BF16
+    if q.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError("q must be fp32 or bf16")
+
+
+def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0) -> DecodeIn:
+    B, max_blocks = block_table.shape
+    return DecodeIn(B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len), _ptr(q_pos), _ptr(q), _q_dtype(q),
+                    _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits)
+
+
+def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
+                num_splits=0, out=None, ws=None):
+    """kvc_decode_attn -> fp32 [(L,) B, Hq, d]."""
+    B = block_table.shape[0]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(layout, B, max_T, num_splits)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits)
+    c = cache.c()
+    _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream()), "kvc_decode_attn")
+    return out
+
+
+def dense_in(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, max_T, num_splits=0) -> DenseIn:
+    B, max_blocks = block_table.shape
+    return DenseIn(Hq, Hkv, d, P, B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len),
+                   _ptr(k_pages.view(torch.int16)), _ptr(v_pages.view(torch.int16)), _ptr(q), _q_dtype(q),
+                   num_splits)
+
+
+def dense_workspace_bytes(inp: DenseIn) -> int:
+    out = C.c_size_t()
+    _check(lib().kvc_dense_workspace_bytes(C.byref(inp), C.byref(out)), "kvc_dense_workspace_bytes")
+    return out.value
+
+
+def dense_decode_attn(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, max_T, num_splits=0, out=None,
+                      ws=None):
+    """kvc_dense_decode_attn -> fp32 [B, Hq, d]."""
+    inp = dense_in(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, max_T, num_splits)
+    need = dense_workspace_bytes(inp)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kvc_dense_decode_attn(C.byref(inp), _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "kvc_dense_decode_attn")
+    return out

@@ -1,0 +1,67 @@
+"""The C ABI library loads, exports every call include/kvc.h declares, and rejects bad
+arguments before launching anything (these calls need no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from rank_bit_compressed_amd import kvc, synth
+
+
+def header_functions():
+    src = open(kvc.HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(kvc_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_header():
+    names = header_functions()
+    assert set(names) == set(kvc.EXPORTS)
+    L = C.CDLL(kvc.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert kvc.lib().kvc_abi_version() == 1
+    assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
+
+
+def test_layout_checks():
+    for name, w in synth.WORKLOADS.items():
+        st = kvc.layout_check(kvc.make_layout(**w.layout_kwargs()))
+        assert st in (0, -2), (name, st)
+    ok = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].layout_kwargs())
+    assert kvc.layout_check(ok) == 0
+    for field, val, want in [("n_kv_heads", 0, -1), ("r_k_cap", 12, -1), ("latent_bits", 8, -1),
+                             ("residual_bits", 3, -1), ("page_size", 512, -1), ("page_size", 48, -2),
+                             ("group", 24, -2), ("n_q_heads", 48, -2), ("rope_theta", -1.0, -1)]:
+        bad = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].layout_kwargs())
+        setattr(bad, field, val)
+        assert kvc.layout_check(bad) == want, (field, val)
+
+
+def test_pool_bytes_closed_form():
+    w = synth.WORKLOADS["llama8b_layer_8k"]
+    L = kvc.make_layout(**w.layout_kwargs())
+    # per head block: K codes 256*24, V codes 256*32, K pairs 256*2*4, V pairs 256*2*4 (all 16-aligned)
+    assert kvc.pool_bytes_max(L, 10) == 10 * 8 * 256 * (24 + 32 + 8 + 8)
+
+
+def test_calls_reject_bad_arguments_without_launching():
+    w = synth.WORKLOADS["varrank_paged_32k"]
+    L = kvc.make_layout(**w.layout_kwargs())
+    lib = kvc.lib()
+    out = C.c_size_t()
+    assert lib.kvc_decode_workspace_bytes(C.byref(L), 0, 100, 0, C.byref(out)) == -1
+    assert lib.kvc_decode_workspace_bytes(C.byref(L), 2, 100, 0, C.byref(out)) == 0 and out.value > 0
+    cache = kvc.Cache(None, 0, None, None, None, None, 0)
+    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0)
+    assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(16), C.c_void_p(16), 1 << 20,
+                               None) == -1
+    cin = kvc.CompressIn(0, 2, 100, 1, *([None] * 11))
+    assert lib.kvc_compress(C.byref(L), C.byref(cin), C.byref(cache), None) == -1
+    # misaligned pointers are refused before any launch
+    cache = kvc.Cache(C.c_void_p(16), 1 << 30, C.c_void_p(32), C.c_void_p(48), C.c_void_p(64), None, 4)
+    inp = kvc.DecodeIn(2, 1, 100, C.c_void_p(80), C.c_void_p(96), None, C.c_void_p(113), 1, C.c_void_p(128),
+                       C.c_void_p(144), 0)
+    assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(160), C.c_void_p(176), 1 << 30,
+                               None) == -4

@@ -1,0 +1,37 @@
+"""kvc_decode_attn on the GPU vs the fp64 oracle on the same stored bytes.
+
+Tolerance: max |out - ref| <= 2e-3 * max |ref| over all outputs (the bound
+the target states for the attention output)."""
+import numpy as np
+import pytest
+import torch
+
+from rank_bit_compressed_amd import synth
+from tests.gpu_helpers import dev, gpu_cache, gpu_decode, rel_err
+from tests.helpers import np_any, oracle_cache, oracle_decode
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+CASES = [
+    ("tiny", {}, None),
+    ("llama8b_layer_8k", dict(T=1000), None),
+    ("llama8b_layer_8k", dict(B=2, T=333, page_size=64), [333, 1]),
+    ("varrank_paged_32k", dict(B=3, T=2000), [2000, 1999, 33]),
+    ("varrank_paged_32k", dict(B=2, T=300, page_size=32), [300, 17]),
+    ("residual_128k", dict(B=2, T=700), [700, 512]),
+]
+
+
+@pytest.mark.parametrize("name,kw,seq", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_decode_matches_oracle(name, kw, seq):
+    w = synth.WORKLOADS[name].scaled(**kw)
+    inp = synth.make_inputs(w, seq_len=seq)
+    print(f"[decode] {name} {kw} seq={seq}", flush=True)
+    ref = oracle_decode(w, inp, oracle_cache(w, inp))
+    d = dev(inp)
+    out = gpu_decode(w, d, gpu_cache(w, d))
+    torch.cuda.synchronize()
+    err = rel_err(out, ref)
+    print(f"    rel err {err:.3e}", flush=True)
+    assert err <= TOL
