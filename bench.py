@@ -1,0 +1,192 @@
+"""Benchmark: one decode step of attention over the compressed KV cache (the whole hot path:
+paging, latent stream, dequantization, key up-projection, RoPE, scores, online softmax, latent value
+accumulation, split merge and value up-projection) on one MI355X, on the batch-16, 32K-context
+variable-rank paged workload; the dense bf16 decode kernel on the same geometry is timed beside it,
+and the CPU oracle on a bounded sample.
+
+Prints ONE JSON line.  Timing: W untimed warmup steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); each step reads a different replica of the compressed cache (4 replicas,
+more than the 256 MB last-level cache holds) so the stream comes from HBM.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+WORKLOAD = "varrank_paged_32k"
+HBM_PEAK_GBS = 8000.0
+REPLICAS = 4
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_head.hip", "kvc_common.hpp"):
+        h.update(open(os.path.join(HERE, "rank_bit_compressed_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is for this source."""
+    path = os.path.join(HERE, "profiles", "decode_head_varrank_paged_32k_counters.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, n_seq=4):
+    """The oracle as it stands, on the first n_seq sequences of the batch (all kv heads, full context)."""
+    import numpy as np
+    import torch
+    from oracle import ref
+
+    def np_u16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    sub = {k: (v[:n_seq].cpu() if v is not None and k in ("lat_k", "lat_v", "ranks", "seq_len", "q_pos", "q") else v)
+           for k, v in inp.items()}
+    L = ref.Layout(**w.layout_kwargs())
+    bt = inp["block_table"][:n_seq].cpu().numpy()
+    pool, page_off, tok_rank, tok_off = ref.compress(
+        L, bt, sub["seq_len"].numpy(), w.T, sub["ranks"].numpy(), sub["lat_k"].float().numpy(),
+        sub["lat_v"].float().numpy(), None, None, w.n_pages, ref.page_bytes_uniform(L) * w.n_pages)
+    q = sub["q"].float().numpy()
+    wk, wv = np_u16(inp["wk"]), np_u16(inp["wv"])
+    t0 = time.perf_counter()
+    out = ref.decode_attn(L, bt, sub["seq_len"].numpy(), sub["q_pos"].numpy(), pool, page_off, tok_rank, tok_off,
+                          q, wk, wv)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    return {"value": round(n_seq / dt, 4), "unit": "tokens/s", "cores": min(ref.threads(), n_seq * w.n_kv_heads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.B} sequences (all {w.n_kv_heads} kv heads, {w.T} tokens each), fp64 C oracle "
+                      f"(OpenMP over sequence x kv head), {dt:.2f} s for one decode step of those sequences"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path here "
+              f"has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_bit_compressed_amd import accounting, kvc, synth
+
+    w = synth.WORKLOADS[WORKLOAD]
+    dev = "cuda"
+    inp = synth.make_inputs(w, device=dev)
+    L = kvc.make_layout(**w.layout_kwargs())
+    base = kvc.DeviceCache.allocate(L, w.n_pages)
+    kvc.compress(L, base, inp["block_table"], inp["seq_len"], w.T, ranks=inp["ranks"], lat_k=inp["lat_k"],
+                 lat_v=inp["lat_v"])
+    torch.cuda.synchronize()
+    used = int(base.used_bytes[0])
+    caches = [base]
+    for _ in range(REPLICAS - 1):
+        c = kvc.DeviceCache(L, base.pool.clone(), base.page_off.clone(), base.tok_rank.clone(), base.tok_off.clone(),
+                            base.used_bytes.clone(), w.n_pages)
+        caches.append(c)
+    cpu_inp = {k: inp[k] for k in ("lat_k", "lat_v", "ranks", "seq_len", "q_pos", "q", "wk", "wv", "block_table")}
+    bt, sl, q, wk, wv, qp = inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], inp["q_pos"]
+    ws = torch.empty(kvc.decode_workspace_bytes(L, w.B, w.T), dtype=torch.uint8, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+    def step(i):
+        kvc.decode_attn(L, caches[i % REPLICAS], bt, sl, q, wk, wv, w.T, q_pos=qp, out=out, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    assert torch.isfinite(out).all()
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    launch_avg = sum(launch_ms) / len(launch_ms)
+
+    acct = accounting.compressed_stream_bytes(w, inp["ranks"], [w.T] * w.B)
+    alg_bytes = acct["stream"] + acct["tables"]
+    achieved = alg_bytes / (launch_avg * 1e-3) / 1e9
+
+    dense = None
+    if not args.no_dense:
+        del inp
+        dd = synth.make_dense_inputs(w, device=dev)
+        dws = torch.empty(kvc.dense_workspace_bytes(kvc.dense_in(w.n_q_heads, w.n_kv_heads, w.head_dim, w.page_size,
+                                                                  bt, sl, dd["k_pages"], dd["v_pages"], dd["q"],
+                                                                  w.T)), dtype=torch.uint8, device=dev)
+        dout = torch.empty(dd["q"].shape, dtype=torch.float32, device=dev)
+
+        def dstep():
+            kvc.dense_decode_attn(w.n_q_heads, w.n_kv_heads, w.head_dim, w.page_size, bt, sl, dd["k_pages"],
+                                  dd["v_pages"], dd["q"], w.T, out=dout, ws=dws)
+
+        for _ in range(max(3, args.warmup // 4)):
+            dstep()
+        torch.cuda.synchronize()
+        nd = max(10, args.steps // 4)
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nd)]
+        for i in range(nd):
+            dev_ev[i][0].record()
+            dstep()
+            dev_ev[i][1].record()
+        torch.cuda.synchronize()
+        d_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / nd
+        d_bytes = w.B * w.T * accounting.dense_bytes_per_token(w.n_kv_heads, w.head_dim)
+        dense = {"ms_per_step": round(d_ms, 5), "hbm_gbs": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                 "bytes": d_bytes, "speedup_compressed_vs_dense": round(d_ms / launch_avg, 3)}
+        del dd
+
+    tokens_per_s = w.B / (ms_per_step * 1e-3)
+    line = {
+        "metric": "compressed decode-attn tokens/s & HBM GB/s (% peak), speedup vs dense bf16 @32K",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": w.B, "context": w.T, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ranks": "8/16/32/64 w.p. .4/.3/.2/.1",
+                   "rank_cap": w.r_k, "latent": "INT4, group 32, fp16 scale+zero", "page_size": w.page_size,
+                   "block_table": "shuffled", "rope_theta": w.rope_theta},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_head_kernel")},
+        "launch_ms_avg": round(launch_avg, 5),
+        "context_tokens_per_s": round(w.B * w.T / (ms_per_step * 1e-3), 1),
+        "compressed_bytes_per_step": alg_bytes,
+        "dense": dense,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, {k: (v.cpu() if v is not None else None) for k, v in cpu_inp.items()})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,8 @@ LIB = os.path.join(HERE, "librbc_kvc.so")
 SOURCES = ["api.cpp", "decode_head.hip", "decode_shared.hip", "compress.hip", "dense.hip"]
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated (fp16 packed math is unaffected)
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-Wall", "-Wno-unused-result",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]  # MFMA results in VGPRs: no accumulator copies
 
 
 def build(verbose: bool = False, extra=()) -> str:

@@ -20,7 +20,8 @@ kvc_status hip_fail(hipError_t e) {
 bool head_supported(const kvc_layout& L);
 int head_part_stride(int rv_cap, int residual);
 hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
-                              int n_splits, int st_per_split, hipStream_t st, bool* unsupported);
+                              int n_splits, int pages_per_split, hipStream_t st, bool* unsupported);
+int head_max_pages_per_split();
 bool shared_supported(const kvc_layout& L);
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits);
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
@@ -58,19 +59,22 @@ static kvc_status check_layout(const kvc_layout* L) {
   return KVC_OK;
 }
 
-// Context splits per (sequence, kv head[, layer]) and super-tiles (32 tokens) per split.
-static void choose_splits(const kvc_layout& L, int B, int max_T, int requested, int* n_splits, int* st_per_split) {
-  const int n_st = (max_T + 31) / 32;
-  int units = B * L.n_kv_heads * (L.shared ? L.n_layers : 1);
+// Context splits per (sequence, kv head[, layer]) and the work of one split: pages (per-head mode)
+// or 32-token super-tiles (block-shared mode).
+static void choose_splits(const kvc_layout& L, int B, int max_T, int requested, int* n_splits, int* per_split) {
+  const int unit = L.shared ? 32 : L.page_size;
+  const int n_units = (max_T + unit - 1) / unit;
+  const int items = B * L.n_kv_heads * (L.shared ? L.n_layers : 1);
   int s = requested;
   if (s <= 0) {
-    const int target = 1024;  // workgroups: about four per compute unit
-    s = std::max(1, (target + units - 1) / units);
-    s = std::min(s, std::max(1, n_st / 4));  // at least one super-tile per wave
+    const int target = 512;  // workgroups: two per compute unit
+    s = std::max(1, (target + items - 1) / items);
   }
-  s = std::max(1, std::min(s, n_st));
-  *st_per_split = (n_st + s - 1) / s;
-  *n_splits = (n_st + *st_per_split - 1) / *st_per_split;
+  s = std::max(1, std::min(s, n_units));
+  int per = (n_units + s - 1) / s;
+  if (!L.shared) per = std::min(per, head_max_pages_per_split());
+  *per_split = per;
+  *n_splits = (n_units + per - 1) / per;
 }
 
 static size_t decode_ws_bytes(const kvc_layout& L, int B, int n_splits) {

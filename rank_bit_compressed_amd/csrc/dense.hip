@@ -1,6 +1,225 @@
-// dense.hip -- dense bf16 paged decode attention (placeholder until implemented).
+// dense.hip -- plain softmax decode attention over a paged bf16 cache (gfx950): the dense comparison.
+//
+// Same decomposition as the compressed kernel: one workgroup (4 waves) per (sequence, kv head,
+// context split), 32-token super-tiles, per-wave online softmax and a merge kernel.  Per 16-token
+// block, lane (token l%16, group g) loads its token's key dims (d/4)g .. (d/4)(g+1)-1 with 16-byte
+// loads; scores S^T = K Q^T on the bf16 MFMA (k-slot 8g + j of chunk c <-> dim (d/4)g + 8c + j); values go
+// through a one-hot bf16 MFMA (a register transpose, exact) and the value product runs on the fp16
+// MFMA with fp16 probabilities.
+#include <math.h>
+
+#include <algorithm>
+
 #include "kvc_common.hpp"
 
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
 namespace kvc {
-kvc_status dense_impl(const kvc_dense_in&, float*, void*, size_t, hipStream_t, size_t*) { return KVC_ERR_UNSUPPORTED; }
+
+struct DenseArgs {
+  const int32_t* block_table;
+  const int32_t* seq_len;
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const void* q;
+  float* ws;
+  int q_bf16, B, Hkv, Hq, max_blocks, P, n_splits, st_per_split, part_stride;
+};
+
+static constexpr int DGQ = 4;
+
+__device__ inline f4 mfma_bf16(bf8 a, bf8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
+template <int D>
+__global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
+  constexpr int QC = D / 32;  // chunks of the score product
+  constexpr int NT = D / 16;  // N-tiles of the value product
+  constexpr int DL = D / 4;   // head dims per lane group: lane group g holds dims DL*g .. DL*g + DL - 1
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x % a.n_splits;
+  const int h = (blockIdx.x / a.n_splits) % a.Hkv;
+  const int b = blockIdx.x / (a.n_splits * a.Hkv);
+  const int T = a.seq_len[b];
+  const int P = a.P;
+
+  // Q^T as the B operand: column hq = n (rows >= DGQ zero), k-slot 8g + j of chunk c <-> dim DL*g + 8c + j
+  bf8 qop[QC];
+  for (int c = 0; c < QC; ++c)
+    for (int j = 0; j < 8; ++j) {
+      const int dim = DL * g + 8 * c + j;
+      float x = 0.0f;
+      if (n < DGQ) {
+        const size_t idx = ((size_t)b * a.Hq + h * DGQ + n) * D + dim;
+        x = a.q_bf16 ? __builtin_bit_cast(float, (uint32_t)((const uint16_t*)a.q)[idx] << 16) : ((const float*)a.q)[idx];
+      }
+      qop[c][j] = (__bf16)x;
+    }
+  bf8 oh[2];
+  for (int e = 0; e < 2; ++e)
+    for (int j = 0; j < 8; ++j) oh[e][j] = (__bf16)((8 * g + j == 16 * e + n) ? 1.0f : 0.0f);
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+
+  f4 acc[NT];
+  for (int i = 0; i < NT; ++i) acc[i] = f4{0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const int n_st = (T + 31) / 32;
+  const int st_begin = split * a.st_per_split;
+  const int st_end = min(n_st, st_begin + a.st_per_split);
+  for (int st = st_begin + wv; st < st_end; st += 4) {
+    const int t0 = st * 32;
+    const int page = uniform(a.block_table[(size_t)b * a.max_blocks + t0 / P]);
+    const size_t head_base = ((size_t)page * a.Hkv + h) * P;
+    float sc[2][4];
+    h4 vtb[NT][2];
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tt = 16 * blk + n;
+      const bool valid = t0 + tt < T;
+      const size_t row = (head_base + (t0 % P) + tt) * D + DL * g;
+      bf8 kc[QC], vc[QC];
+      for (int c = 0; c < QC; ++c) {
+        kc[c] = valid ? *(const bf8*)(a.k_pages + row + 8 * c) : bf8{};
+        vc[c] = valid ? *(const bf8*)(a.v_pages + row + 8 * c) : bf8{};
+      }
+      f4 s4 = {0, 0, 0, 0};
+      for (int c = 0; c < QC; ++c) s4 = mfma_bf16(kc[c], qop[c], s4);
+      for (int i = 0; i < 4; ++i) sc[blk][i] = s4[i] * qscale;
+      // transpose: chunk c, half e -> column n holds dim DL(2e + n/8) + 8c + n%8 of tokens 4g..4g+3
+      for (int c = 0; c < QC; ++c)
+        for (int e = 0; e < 2; ++e) {
+          const f4 tr = mfma_bf16(vc[c], oh[e], f4{0, 0, 0, 0});
+          vtb[2 * c + e][blk] = h4{(_Float16)tr[0], (_Float16)tr[1], (_Float16)tr[2], (_Float16)tr[3]};
+        }
+    }
+    float mx = -INFINITY;
+    for (int blk = 0; blk < 2; ++blk)
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (n < DGQ) && (t0 + 16 * blk + 4 * g + i < T);
+        sc[blk][i] = ok ? sc[blk][i] : -INFINITY;
+        mx = fmaxf(mx, sc[blk][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+    h8 pop;
+    float psum = 0.0f;
+    for (int blk = 0; blk < 2; ++blk)
+      for (int i = 0; i < 4; ++i) {
+        const float p = (m_new == -INFINITY) ? 0.0f : exp2f(sc[blk][i] - m_new);
+        const _Float16 ph = (_Float16)p;
+        pop[4 * blk + i] = ph;
+        psum += (float)ph;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      float al[4];
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+      for (int nt = 0; nt < NT; ++nt)
+        for (int i = 0; i < 4; ++i) acc[nt][i] *= al[i];
+    }
+    for (int nt = 0; nt < NT; ++nt) {
+      const h8 vt = {vtb[nt][0][0], vtb[nt][0][1], vtb[nt][0][2], vtb[nt][0][3],
+                     vtb[nt][1][0], vtb[nt][1][1], vtb[nt][1][2], vtb[nt][1][3]};
+      acc[nt] = mfma16x16x32(pop, vt, acc[nt]);
+    }
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  float* part = a.ws + ((size_t)((b * a.Hkv + h) * a.n_splits + split) * 4 + wv) * a.part_stride;
+  if (lane < DGQ) {
+    part[lane] = m_run;
+    part[DGQ + lane] = l_run;
+  }
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = nt >> 1, e = nt & 1;
+    const int dim = DL * (2 * e + (n >> 3)) + 8 * c + (n & 7);
+    for (int i = 0; i < 4; ++i) {
+      const int hq = 4 * g + i;
+      if (hq < DGQ) part[2 * DGQ + hq * D + dim] = acc[nt][i];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dense_merge_kernel(const float* ws, float* out, int Hkv, int Hq, int n_parts,
+                                                          int part_stride) {
+  const int bh = blockIdx.x, h = bh % Hkv, b = bh / Hkv;
+  const int hq = threadIdx.x / 64, l = threadIdx.x % 64;
+  const float* parts = ws + (size_t)bh * n_parts * part_stride;
+  float m = -INFINITY;
+  for (int p = 0; p < n_parts; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
+  float lsum = 0.0f, o[D / 64];
+  for (int k = 0; k < D / 64; ++k) o[k] = 0.0f;
+  for (int p = 0; p < n_parts; ++p) {
+    const float* pp = parts + (size_t)p * part_stride;
+    if (pp[hq] == -INFINITY) continue;
+    const float wgt = exp2f(pp[hq] - m);
+    lsum += wgt * pp[DGQ + hq];
+    for (int k = 0; k < D / 64; ++k) o[k] += wgt * pp[2 * DGQ + hq * D + l + 64 * k];
+  }
+  for (int k = 0; k < D / 64; ++k) out[((size_t)b * Hq + h * DGQ + hq) * D + l + 64 * k] = o[k] / lsum;
+}
+
+static void dense_splits(int B, int Hkv, int max_T, int requested, int* ns, int* sps) {
+  const int n_st = (max_T + 31) / 32;
+  int s = requested;
+  if (s <= 0) {
+    s = std::max(1, (1024 + B * Hkv - 1) / (B * Hkv));
+    s = std::min(s, std::max(1, n_st / 4));
+  }
+  s = std::max(1, std::min(s, n_st));
+  *sps = (n_st + s - 1) / s;
+  *ns = (n_st + *sps - 1) / *sps;
+}
+
+kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st, size_t* need) {
+  if (in.n_q_heads <= 0 || in.n_kv_heads <= 0 || in.B <= 0 || in.max_T <= 0 || in.max_blocks <= 0 ||
+      in.page_size <= 0 || in.num_splits < 0)
+    return KVC_ERR_INVALID_ARG;
+  if (in.n_q_heads % in.n_kv_heads || (int64_t)in.max_blocks * in.page_size < in.max_T) return KVC_ERR_INVALID_ARG;
+  if (in.q_dtype != KVC_F32 && in.q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
+  if (in.n_q_heads != DGQ * in.n_kv_heads || (in.head_dim != 64 && in.head_dim != 128) || in.page_size % 32 ||
+      in.page_size > 256)
+    return KVC_ERR_UNSUPPORTED;
+  int ns, sps;
+  dense_splits(in.B, in.n_kv_heads, in.max_T, in.num_splits, &ns, &sps);
+  const int stride = 2 * DGQ + DGQ * in.head_dim;
+  const size_t bytes = (size_t)in.B * in.n_kv_heads * ns * 4 * stride * sizeof(float);
+  if (need) {
+    *need = bytes;
+    return KVC_OK;
+  }
+  if (!in.block_table || !in.seq_len || !in.k_pages || !in.v_pages || !in.q || !out || !ws)
+    return KVC_ERR_INVALID_ARG;
+  const void* ptrs[] = {in.block_table, in.seq_len, in.k_pages, in.v_pages, in.q, out, ws};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15u) return KVC_ERR_MISALIGNED;
+  if (ws_bytes < bytes) return KVC_ERR_WORKSPACE;
+  DenseArgs a;
+  a.block_table = in.block_table; a.seq_len = in.seq_len; a.k_pages = in.k_pages; a.v_pages = in.v_pages;
+  a.q = in.q; a.ws = (float*)ws; a.q_bf16 = in.q_dtype == KVC_BF16; a.B = in.B; a.Hkv = in.n_kv_heads;
+  a.Hq = in.n_q_heads; a.max_blocks = in.max_blocks; a.P = in.page_size; a.n_splits = ns; a.st_per_split = sps;
+  a.part_stride = stride;
+  const int grid = in.B * in.n_kv_heads * ns;
+  if (in.head_dim == 128) {
+    hipLaunchKernelGGL(dense_kernel<128>, dim3(grid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(dense_kernel<64>, dim3(grid), dim3(256), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  if (in.head_dim == 128) {
+    hipLaunchKernelGGL(dense_merge_kernel<128>, dim3(in.B * in.n_kv_heads), dim3(256), 0, st, a.ws, out,
+                       in.n_kv_heads, in.n_q_heads, ns * 4, stride);
+  } else {
+    hipLaunchKernelGGL(dense_merge_kernel<64>, dim3(in.B * in.n_kv_heads), dim3(256), 0, st, a.ws, out,
+                       in.n_kv_heads, in.n_q_heads, ns * 4, stride);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return KVC_OK;
+}
+
 }  // namespace kvc

@@ -83,29 +83,38 @@ __device__ inline _Float16 bf16_to_h(uint16_t b) {
 }
 
 // Eight INT4 codes (one dword, coordinate 2j in the low nibble of byte j) dequantized as
-// code * scale + zero in fp16; sz holds (scale, zero) as two fp16.  The result is in the order
-// (0,4,1,5,2,6,3,7): element j is coordinate perm8(j) = j/2 + 4 (j%2).  Each step is exact
-// except the final fused multiply-add, which rounds once.
+// code * scale + zero in fp16; sz holds (scale, zero) as two fp16.  A code q placed in a byte is the
+// fp8 e4m3 bit pattern of q * 2^-9 (0x00-0x07 subnormal, 0x08-0x0F the first binade), so the gfx950
+// fp8 -> fp16 conversion with the power-of-two scale 2^9 yields q exactly; one fused multiply-add in
+// fp16 then applies scale and zero (a single rounding).  Result order: element j is coordinate
+// perm8(j) = 2j for j < 4 and 2(j - 4) + 1 otherwise.
 __device__ inline h8 dequant_int4x8(uint32_t x, uint32_t sz) {
-  const uint32_t magic = 0x64006400u;  // fp16 1024.0 in both halves: 1024 + q is exact for q < 1024
-  uint32_t y0 = (x & 0x000F000Fu) | magic;
-  uint32_t y1 = ((x >> 4) & 0x000F000Fu) | magic;
-  uint32_t y2 = ((x >> 8) & 0x000F000Fu) | magic;
-  uint32_t y3 = ((x >> 12) & 0x000F000Fu) | magic;
-  const h2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  h2 s = as_h2(sz);
-  h2 ss = s.xx, zz = s.yy;
-  h2 a0 = (as_h2(y0) - k1024) * ss + zz;
-  h2 a1 = (as_h2(y1) - k1024) * ss + zz;
-  h2 a2 = (as_h2(y2) - k1024) * ss + zz;
-  h2 a3 = (as_h2(y3) - k1024) * ss + zz;
+  const uint32_t lo = x & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+  const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+  const h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+  const h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+  const h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
+  const h2 s = as_h2(sz);
+  const h2 ss = s.xx, zz = s.yy;
+  const h2 a0 = c0 * ss + zz, a1 = c1 * ss + zz, a2 = c2 * ss + zz, a3 = c3 * ss + zz;
   h8 r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
   return r;
 }
 
-__host__ __device__ inline int perm8(int j) { return (j >> 1) + 4 * (j & 1); }
+// RoPE on one fp16 pair v = (x, y) with f = (cos, sin): (x cos - y sin, y cos + x sin).  Written so
+// that it compiles to two packed instructions (the swap and the sign become operand selects).
+__device__ inline uint32_t rope_pair(uint32_t v, uint32_t f) {
+  const h2 x = as_h2(v), c = as_h2(f);
+  const h2 t = x * c.yy;  // (x sin, y sin)
+  const h2 m = {-t.y, t.x};
+  return as_u32(x * c.xx + m);
+}
 
-// Eight 2-bit residual codes (16 bits, code j at bits 2j) as (2 code - 3) * s2 in fp16, order perm8.
+__host__ __device__ inline int perm8(int j) { return j < 4 ? 2 * j : 2 * (j - 4) + 1; }
+
+// Eight 2-bit residual codes (16 bits, code j at bits 2j) as (2 code - 3) * s2 in fp16, order
+// permr(j) = j/2 + 4 (j%2).
 // Each code is placed doubled in the low mantissa bits of fp16 1024, so (1024 + 2c) - 1027 = 2c - 3 is
 // exact (1027 is an fp16 integer; 1025.5 would not be); with s2 = scale / 2 this is (c - 1.5) * scale.
 __device__ inline h8 dequant_res2x8(uint32_t u16, h2 s2) {
@@ -123,6 +132,8 @@ __device__ inline h8 dequant_res2x8(uint32_t u16, h2 s2) {
   h8 r = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
   return r;
 }
+
+__host__ __device__ inline int permr(int j) { return (j >> 1) + 4 * (j & 1); }
 
 __device__ inline f4 mfma16x16x32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 

@@ -116,7 +116,7 @@ def _orthonormal(w: Workload, stream: int, rows: int, cols: int, n: int) -> torc
     g = _gen(w, stream, "cpu")
     a = torch.randn(n, rows, cols, generator=g, dtype=torch.float64)
     q, r = torch.linalg.qr(a)
-    return q * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1)).unsqueeze(-2)
+    return (q * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1)).unsqueeze(-2)).contiguous()
 
 
 def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
