@@ -14,6 +14,7 @@ CASES = [
     ("llama8b_layer_8k", dict(T=1000), None),
     ("varrank_paged_32k", dict(B=3, T=2000), [2000, 1999, 33]),
     ("residual_128k", dict(B=2, T=700), [700, 512]),
+    ("shared_latent_32k", dict(B=2, T=600), [600, 1]),
 ]
 
 
