@@ -40,6 +40,7 @@
 #include "kvc_ref.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -617,6 +618,17 @@ int kvc_ref_decode_attn(const kvc_ref_layout* L, int B, int max_blocks, const in
   }
   free(H);
   return 0;
+}
+
+/* OpenMP threads a parallel region of this library uses (1 without OpenMP). */
+int kvc_ref_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
 }
 
 int kvc_ref_dense_attn(int Hq, int Hkv, int d, int P, int B, int max_blocks, const int32_t* block_table,

@@ -100,6 +100,9 @@ int kvc_ref_decode_attn(const kvc_ref_layout* L, int B, int max_blocks, const in
                         const float* q, const uint16_t* wk, const uint16_t* wv,
                         const uint8_t* sel_b, const uint8_t* sel_h, double* out);
 
+/* OpenMP threads the parallel loops above use */
+int kvc_ref_threads(void);
+
 /* --- plain softmax attention over a paged bf16 cache (the dense comparison) ---
  * k_pages, v_pages: bf16 bits [n_pages][Hkv][P][d] (K already rotated); q fp32 [B][Hq][d] */
 int kvc_ref_dense_attn(int Hq, int Hkv, int d, int P, int B, int max_blocks, const int32_t* block_table,

@@ -40,6 +40,7 @@ def lib():
         L.kvc_ref_decode_attn.restype = C.c_int
         L.kvc_ref_dense_attn.argtypes = [C.c_int] * 6 + [P] * 7
         L.kvc_ref_dense_attn.restype = C.c_int
+        L.kvc_ref_threads.argtypes = []; L.kvc_ref_threads.restype = C.c_int
         _lib = L
     return _lib
 
@@ -199,4 +200,5 @@ def dense_attn(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, sel_b=N
 
 
 def threads() -> int:
-    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(lib().kvc_ref_threads())
