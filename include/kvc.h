@@ -207,6 +207,13 @@ kvc_status kvc_decode_workspace_bytes(const kvc_layout* layout, int32_t B, int32
 kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
                            float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Which decode kernel kvc_decode_attn runs for a layout: KVC_PATH_INT4 (per-head INT4 latents,
+ * head_dim 128, no residual: the fast kernel), KVC_PATH_HEAD (the general per-head kernel: fp32
+ * latents, head_dim 64, rotated residual) or KVC_PATH_SHARED (block-shared latents).  Host-only;
+ * returns the layout check's status when the layout is not runnable. */
+enum { KVC_PATH_HEAD = 0, KVC_PATH_INT4 = 1, KVC_PATH_SHARED = 2 };
+kvc_status kvc_decode_path(const kvc_layout* layout, int32_t* path);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

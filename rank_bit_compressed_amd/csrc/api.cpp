@@ -22,6 +22,7 @@ int head_part_stride(int rv_cap, int residual);
 hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
                               int n_splits, int pages_per_split, hipStream_t st, bool* unsupported);
 int head_max_pages_per_split();
+int head_decode_path(const kvc_layout& L);
 bool shared_supported(const kvc_layout& L);
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits);
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
@@ -162,6 +163,14 @@ kvc_status kvc_compress(const kvc_layout* layout, const kvc_compress_in* in, con
   if (s) return s;
   if (!in || !cache) return KVC_ERR_INVALID_ARG;
   return compress_impl(*layout, *in, *cache, (hipStream_t)stream);
+}
+
+kvc_status kvc_decode_path(const kvc_layout* layout, int32_t* path) {
+  kvc_status s = check_layout(layout);
+  if (s) return s;
+  if (!path) return KVC_ERR_INVALID_ARG;
+  *path = layout->shared ? KVC_PATH_SHARED : head_decode_path(*layout);
+  return KVC_OK;
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

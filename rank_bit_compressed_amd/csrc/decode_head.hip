@@ -43,7 +43,7 @@ struct DecodeHeadArgs {
 };
 
 static constexpr int GQ = 4;            // query heads per KV head handled by these kernels
-static constexpr int MAX_SPLIT_PAGES = 256;
+static constexpr int MAX_SPLIT_PAGES = 128;
 
 // LDS layout (bytes) of the decode kernel, given the head-block buffer size.
 struct HeadLds {
@@ -495,6 +495,20 @@ static hipError_t launch_variant(const DecodeHeadArgs& a, int grid, const uint16
   return hipGetLastError();
 }
 
+// Merge of per-wave partials for head dimension 128 without residual (also used by the INT4 fast path).
+hipError_t launch_merge_head128(int NV, const float* ws, const uint16_t* wv, float* out, int B, int Hkv, int Hq,
+                                int rv, int n_parts, int part_stride, hipStream_t st) {
+  if (NV == 4)
+    hipLaunchKernelGGL((merge_head_kernel<128, 4, false>), dim3(B * Hkv), dim3(256), 0, st, ws, wv, out, Hkv, Hq, rv,
+                       n_parts, part_stride);
+  else if (NV == 2)
+    hipLaunchKernelGGL((merge_head_kernel<128, 2, false>), dim3(B * Hkv), dim3(256), 0, st, ws, wv, out, Hkv, Hq, rv,
+                       n_parts, part_stride);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 int head_part_stride(int rv_cap, int residual) {
   const int NV = 2 * ceil_div(rv_cap, 32);
   return 2 * GQ + GQ * NV * 16 + (residual ? GQ * 128 : 0);
@@ -513,6 +527,12 @@ static int64_t head_block_max(const kvc_layout& L) {
 
 int head_max_pages_per_split() { return MAX_SPLIT_PAGES; }
 
+// INT4 fast path (decode_int4.hip)
+bool int4_supported(const kvc_layout& L, int64_t hb_max);
+hipError_t launch_decode_int4(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
+                              int n_splits, int pages_per_split, int part_stride, const HeadSections& S_uniform,
+                              int hb_max, hipStream_t st);
+
 bool head_supported(const kvc_layout& L) {
   if (L.shared) return false;
   if (L.n_q_heads != GQ * L.n_kv_heads) return false;
@@ -526,6 +546,8 @@ bool head_supported(const kvc_layout& L) {
     return false;
   return true;
 }
+
+int head_decode_path(const kvc_layout& L) { return int4_supported(L, head_block_max(L)) ? KVC_PATH_INT4 : KVC_PATH_HEAD; }
 
 hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
                               int n_splits, int pages_per_split, hipStream_t st, bool* unsupported) {
@@ -544,11 +566,13 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
                               (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
                               L.residual_bits);
   a.hb_max = (int)head_block_max(L);
+  *unsupported = false;
+  if (int4_supported(L, a.hb_max))
+    return launch_decode_int4(L, C, in, out, ws, n_splits, pages_per_split, a.part_stride, a.S_uniform, a.hb_max, st);
   const int stg = ceil_div(a.hb_max, 16 * 256);
   const int grid = in.B * L.n_kv_heads * n_splits;
   const int KC = ceil_div(L.r_k_cap, 32), VC = ceil_div(L.r_v_cap, 32);
   const bool lat32 = L.latent_bits == 32, res = L.residual_bits != 0, var = L.variable_rank != 0;
-  *unsupported = false;
 #define KVC_TRY(D_, KC_, VC_, L32_, RES_, VAR_, STG_)                                                        \
   if (L.head_dim == D_ && KC == KC_ && VC == VC_ && lat32 == L32_ && res == RES_ && var == VAR_ && stg <= STG_) \
     return launch_variant<D_, KC_, VC_, L32_, RES_, VAR_, STG_>(a, grid, in.wv, out, st);

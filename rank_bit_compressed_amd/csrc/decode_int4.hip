@@ -1,0 +1,519 @@
+// decode_int4.hip -- one decode step of attention over a per-KV-head INT4 compressed cache, head
+// dimension 128, four query heads per KV head (gfx950).  The fast path of the per-head mode.
+//
+// Work decomposition: one workgroup (4 waves) per (sequence b, KV head h, context split of pages).
+// The workgroup copies each page's head-h block (codes, scale/zero pairs) and the page's offset row
+// from HBM into LDS with buffer loads that write LDS directly, three buffers deep (two pages in
+// flight while one is decoded).  Wave w decodes the 32-token super-tiles w and w + 4 of every page
+// and keeps its own online-softmax state.
+//
+// All products are v_mfma_f32_32x32x16_f16 (on gfx950 it does twice the work of the 16x16x32 form in
+// the same issue time).  Lane l serves token l % 32 of the super-tile, and its half l / 32 selects
+// the eight k-slots it supplies.  Per super-tile:
+//   K codes -> fp16 (code * scale + zero; 8 coordinates per lane per 16-coordinate step)
+//   -> K_pre = B_k c (4 tiles of 32 head dims; the basis fragments stay in registers)
+//   -> RoPE R(s) in packed fp16 on the pairs (j, j + 64), which sit in one lane (tiles m and m + 2)
+//   -> S = Q~ K~^T (rows: query heads, replicated; columns: tokens), accumulated onto -m so the
+//      scores come out shifted by the running reference maximum; each lane then holds the four
+//      heads' scores of its token
+//   -> p = 2^s; P^T through a one-hot MFMA (tokens move into the reduction slots)
+//   V codes -> fp16 -> V^T through one-hot MFMAs -> acc += P V_latent (rows: heads, columns:
+//   latent coordinates).  The value basis is applied once per (b, head) in the merge, since
+//   sum_t p_t B c_t = B sum_t p_t c_t.
+// RoPE is split as R(t0 + s) = R(t0) R(s): R(s) for the lane's slot s < 32 is held in registers;
+// R(q_pos - t0) is applied to the query once per super-tile.
+// Softmax keeps a reference maximum m per head and only raises it (rescaling acc and l) when a score
+// exceeds it by more than 2^8 in the exp2 domain; the probabilities then stay below 256, within the
+// fp16 operand range at full relative precision.  The merge uses the same m.
+#include <math.h>
+
+#include "kvc_common.hpp"
+
+namespace kvc {
+
+struct Int4Args {
+  const uint8_t* pool;
+  const int64_t* page_off;
+  const uint32_t* tok_off;
+  const int32_t* block_table;
+  const int32_t* seq_len;
+  const int32_t* q_pos;
+  const void* q;
+  const uint16_t* wk;
+  float* ws;
+  int q_bf16;
+  int B, Hkv, Hq, max_blocks, P, rk, rv, G, n_splits, pages_per_split, part_stride;
+  int hb_max;
+  double theta;
+  HeadSections S_uniform;
+};
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+namespace i4 {
+constexpr int D = 128, GQ = 4, NP = 64;
+constexpr int MAX_SPLIT_PAGES = 128;
+constexpr float TAU = 8.0f;  // lazy-max slack, log2 units
+
+struct Lds {
+  int meta_addr, meta_hb, meta_page, theta, qsrc, qbuf, stage, stage_bytes, off_bytes, total;
+};
+__host__ __device__ inline Lds lds_layout(int P, int hb_max) {
+  Lds L;
+  int o = 0;
+  L.meta_addr = o; o += MAX_SPLIT_PAGES * 8;
+  L.meta_hb = o; o += MAX_SPLIT_PAGES * 4;
+  L.meta_page = o; o += MAX_SPLIT_PAGES * 4;
+  L.theta = o; o += NP * 8;                     // RoPE frequencies, turns per position
+  L.qsrc = o; o += NP * 2 * GQ * 4;             // scaled query, pair j: x_j of heads 0-3, then x_{j+64}
+  L.qbuf = o; o += 4 * 2 * GQ * (NP + 4) * 4;  // per wave two super-tiles, rows padded by 4 dwords
+  // stage buffer: the page's offset row (whole 64-dword rows, the tail zero-filled), then the head block
+  L.off_bytes = 256 * ceil_div(P + 1, 64);
+  L.stage_bytes = L.off_bytes + (int)pad16(hb_max);
+  L.stage = o; o += 3 * L.stage_bytes;
+  L.total = o;
+  return L;
+}
+}  // namespace i4
+
+__device__ inline uint32_t lds_u32(const uint8_t* base, int byte_off) { return *(const uint32_t*)(base + byte_off); }
+
+// Scale/zero pair, or zero when the lane's eight coordinates lie beyond the token's rank.
+__device__ inline uint32_t pair_if(bool ok, uint32_t sz) { return ok ? sz : 0u; }
+
+__device__ inline f16v mfma32(h8 a, h8 b, f16v c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+
+// eight consecutive accumulator entries (from entry e0) as an fp16 operand
+__device__ inline h8 cvt_h8(const f16v& v, int e0) {
+  h8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (_Float16)v[e0 + j];
+  return r;
+}
+
+// s_waitcnt vmcnt(k) for a run-time k (this wave's vector-memory operations still allowed in flight)
+__device__ inline void vmcnt_wait(int k) {
+  switch (k) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+  }
+}
+
+// KS, VS: 16-coordinate steps of the key / value rank caps (2..4); VT: 32-coordinate value tiles
+template <int KS, int VS, bool VAR, int STG>
+__global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
+  using namespace i4;
+  constexpr int VT = (VS + 1) / 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int P = a.P;
+  const Lds LY = lds_layout(P, a.hb_max);
+  int64_t* meta_addr = (int64_t*)(smem + LY.meta_addr);
+  int32_t* meta_hb = (int32_t*)(smem + LY.meta_hb);
+  int32_t* meta_page = (int32_t*)(smem + LY.meta_page);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t = lane & 31, hf = lane >> 5;
+  const int split = blockIdx.x % a.n_splits;
+  const int h = (blockIdx.x / a.n_splits) % a.Hkv;
+  const int b = blockIdx.x / (a.n_splits * a.Hkv);
+  const int T = a.seq_len[b];
+  const int qpos = a.q_pos ? a.q_pos[b] : T;
+  const int lb0 = split * a.pages_per_split;
+  const int n_pages = max(0, min((T + P - 1) / P, lb0 + a.pages_per_split) - lb0);
+  uint32_t* qbuf = (uint32_t*)(smem + LY.qbuf) + wv * 2 * GQ * (NP + 4);
+
+  // ---- page addresses of the split
+  for (int i = tid; i < n_pages; i += 256) {
+    const int page = a.block_table[(size_t)b * a.max_blocks + lb0 + i];
+    int64_t hb = a.S_uniform.hb;
+    if constexpr (VAR) {
+      const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
+      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      hb = head_sections(cb, cb, mb, mb, P, D, 0).hb;
+    }
+    meta_addr[i] = a.page_off[page] + (int64_t)h * hb;
+    meta_hb[i] = (int32_t)hb;
+    meta_page[i] = page;
+  }
+
+  // ---- key basis as A fragments (registers): row = head dim 32m + t, k-slot 8hf + j <-> coordinate
+  // 16s + 8hf + perm8(j) (the order in which a code dword dequantizes)
+  h8 bf[KS][4];
+  {
+    const uint16_t* Bk = a.wk + (size_t)h * D * a.rk;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col0 = 16 * s + 8 * hf;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h8 f = {};
+        if (col0 < a.rk) {
+          const u4 raw = *(const u4*)(Bk + (size_t)(32 * m + t) * a.rk + col0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int e = perm8(j);
+            const uint32_t w = raw[e >> 1];
+            f[j] = bf16_to_h((uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
+          }
+        }
+        bf[s][m] = f;
+      }
+    }
+  }
+  // ---- RoPE frequencies, once per workgroup: theta_j (fp64 pow) in turns per position
+  double* tturn = (double*)(smem + LY.theta);
+  if (tid < NP) tturn[tid] = (a.theta > 0.0 ? pow(a.theta, -2.0 * tid / D) : 0.0) * 0.15915494309189535;
+  __syncthreads();
+  // RoPE factors (cos, sin)(t theta_j) of this lane's slot t: pair j = 32m + 8(i/4) + 4hf + i%4 for
+  // accumulator entry i of tiles m and m + 2; |t theta_j| < 32 turns, where v_sin / v_cos are accurate
+  uint32_t rf[2][16];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 32 * m + 8 * (i / 4) + 4 * hf + i % 4;
+      const float rev = (float)(t * tturn[j]);
+      rf[m][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    }
+  // one-hot B operands.  Value transpose: k-slot 8hf + j of step s holds coordinate 16s + 8hf + perm8(j);
+  // it goes to column (16 (s % 2) + 8hf + perm8(j)) of value tile s / 2.  Probability transpose: k-slot
+  // j < 4 (lanes of half 0) holds head j; column c takes head c % 4.
+  h8 ohv[2], ohp;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ohv[e][j] = (t == 16 * e + 8 * hf + perm8(j)) ? (_Float16)1.0f : (_Float16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ohp[j] = (hf == 0 && j < 4 && (t & 3) == j) ? (_Float16)1.0f : (_Float16)0.0f;
+
+  // scaled query (log2(e) / sqrt(d), for exp2) into LDS
+  float* qsrc = (float*)(smem + LY.qsrc);
+  for (int e = tid; e < NP * GQ; e += 256) {
+    const int j = e % NP, hq = e / NP;
+    const size_t base = ((size_t)b * a.Hq + h * GQ + hq) * D;
+    float x0, x1;
+    if (a.q_bf16) {
+      const uint16_t* q = (const uint16_t*)a.q + base;
+      x0 = __builtin_bit_cast(float, (uint32_t)q[j] << 16);
+      x1 = __builtin_bit_cast(float, (uint32_t)q[j + NP] << 16);
+    } else {
+      const float* q = (const float*)a.q + base;
+      x0 = q[j];
+      x1 = q[j + NP];
+    }
+    const float sc = 1.4426950408889634f / sqrtf((float)D);
+    qsrc[j * 8 + hq] = x0 * sc;
+    qsrc[j * 8 + 4 + hq] = x1 * sc;
+  }
+  const double fj = tturn[lane];  // turns per position of pair `lane` (query rotation)
+
+  // ---- page staging.  Wave w copies the 16-byte chunks 256k + 64w + l of the head block (and a share of
+  // the page's offset row); issue() returns the number of copy instructions the wave issued, so that the
+  // wait for a page leaves exactly the later page's copies in flight.
+  auto issue = [&](int i) -> int {
+    uint8_t* dst = smem + LY.stage + (i % 3) * LY.stage_bytes;
+    const int bytes = __builtin_amdgcn_readfirstlane(meta_hb[i]);
+    // buffer resources: scalar base and size (reads past the size return zeros)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.pool + uniform64(meta_addr[i])), (short)0, bytes, 0x00020000);
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < STG; ++k) {
+      const int base = 16 * (256 * k + 64 * wv);
+      if (base >= bytes) break;  // wave-uniform: every issued copy has lane 0 active
+      if (base + 16 * lane < bytes)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + LY.off_bytes + base),
+                                                 16, 16 * lane, base, 0, 0);
+      ++cnt;
+    }
+    if constexpr (VAR) {
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.tok_off + (size_t)__builtin_amdgcn_readfirstlane(meta_page[i]) * (P + 1)), (short)0, 4 * (P + 1),
+          0x00020000);
+      for (int base = 64 * wv; base <= P; base += 256) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(dst + 4 * base), 4,
+                                                 4 * lane, 4 * base, 0, 0);
+        ++cnt;
+      }
+    }
+    return cnt;
+  };
+  // this wave's copies except the last `keep` issued have landed; the barrier publishes everyone's
+  auto settle = [&](int keep) {
+    vmcnt_wait(keep);
+    __syncthreads();
+  };
+
+  // running state: value accumulator (4 heads x the lane's latent coordinates), sums, reference maxima
+  float acc[VT][4], psum[4], m_ref[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    psum[i] = 0.0f;
+    m_ref[i] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < VT; ++w) acc[w][i] = 0.0f;
+  }
+  bool fresh = true;  // no token seen yet
+
+  const int kcb = a.rk / 2, vcb = a.rv / 2;                                  // uniform: code bytes per slot
+  const int kmb = 4 * ceil_div(a.rk, a.G), vmb = 4 * ceil_div(a.rv, a.G);  // uniform: pair bytes per slot
+
+  struct Words {  // a lane's LDS words for one super-tile: code dword and (scale, zero) word per step
+    uint32_t k[KS], pk[KS], v[VS], pv[VS];
+  };
+
+  __syncthreads();  // page addresses and the scaled query visible
+  int kn = 0;
+  if (n_pages > 0) issue(0);
+  if (n_pages > 1) kn = issue(1);
+  settle(kn);
+  for (int ip = 0; ip < n_pages; ++ip) {
+    kn = (ip + 2 < n_pages) ? issue(ip + 2) : 0;
+    const uint32_t* so = (const uint32_t*)(smem + LY.stage + (ip % 3) * LY.stage_bytes);
+    const uint8_t* sb = (const uint8_t*)so + LY.off_bytes;
+    HeadSections S;
+    if constexpr (VAR) {
+      const uint32_t tot = so[P];
+      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      S = head_sections(cb, cb, mb, mb, P, D, 0);
+    } else {
+      S = a.S_uniform;
+    }
+    const uint8_t* kcs = sb + S.kc + 4 * hf;
+    const uint8_t* vcs = sb + S.vc + 4 * hf;
+    const uint8_t* kms = sb + S.km;
+    const uint8_t* vms = sb + S.vm;
+    const int page_t0 = (lb0 + ip) * P;
+    const int n_st = min(P, T - page_t0 + 31) / 32;    // super-tiles of this page holding tokens
+    const int nst_w = (n_st > wv) + (n_st > wv + 4);  // this wave's: super-tiles wv and wv + 4
+    if (nst_w > 0) {
+      // queries rotated by the bases of this wave's super-tiles, q~ = R(q_pos - t0) q; lane j: pair j
+      {
+        const f4 qa = *(const f4*)&qsrc[lane * 8], qb = *(const f4*)&qsrc[lane * 8 + 4];
+        for (int k = 0; k < nst_w; ++k) {
+          double rev = (double)(qpos - page_t0 - 32 * (wv + 4 * k)) * fj;
+          rev -= rint(rev);  // |rev| <= 1/2 turn; v_sin / v_cos take turns
+          const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+#pragma unroll
+          for (int hq = 0; hq < GQ; ++hq)
+            qbuf[(k * GQ + hq) * (NP + 4) + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // the LDS words of super-tile k of this wave (slot 32 (wv + 4k) + t), issued one super-tile ahead
+      auto fetch = [&](int k) -> Words {
+        const int slot = 32 * (wv + 4 * k) + t;
+        int r, co_k, co_v, po_k, po_v;
+        if constexpr (VAR) {
+          const uint32_t o0 = so[slot], o1 = so[slot + 1];
+          r = (int)((o1 - o0) & 0xFFFFu);  // 0 for slots past the sequence end
+          co_k = co_v = (int)((o0 & 0xFFFFu) >> 1);
+          po_k = po_v = (int)(o0 >> 16) * 4;
+        } else {
+          r = a.rk;
+          co_k = slot * kcb;
+          co_v = slot * vcb;
+          po_k = slot * kmb;
+          po_v = slot * vmb;
+        }
+        Words w;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          w.k[s] = lds_u32(kcs, co_k + 8 * s);
+          w.pk[s] = lds_u32(kms, po_k + 4 * ((16 * s + 8 * hf) / a.G));
+          if constexpr (VAR) w.pk[s] = pair_if(16 * s + 8 * hf < r, w.pk[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          w.v[s] = lds_u32(vcs, co_v + 8 * s);
+          w.pv[s] = lds_u32(vms, po_v + 4 * ((16 * s + 8 * hf) / a.G));
+          if constexpr (VAR) w.pv[s] = pair_if(16 * s + 8 * hf < r, w.pv[s]);
+        }
+        return w;
+      };
+
+      Words nxt = fetch(0);
+      for (int k = 0; k < nst_w; ++k) {
+        const Words cur = nxt;
+        if (k + 1 < nst_w) nxt = fetch(k + 1);
+        const uint32_t* qrow = qbuf + (k * GQ + (t & 3)) * (NP + 4) + 4 * hf;
+        const int t0 = page_t0 + 32 * (wv + 4 * k);
+
+        // ---- keys: dequantize all steps, then per half m the tiles m and m + 2 (head dims d and d + 64),
+        // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
+        h8 kb[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(cur.k[s], cur.pk[s]);
+        f16v sc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = -m_ref[i & 3];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          f16v ka = {}, kz = {};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            ka = mfma32(bf[s][m], kb[s], ka);
+            kz = mfma32(bf[s][m + 2], kb[s], kz);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h8 kq;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const h2 rr = as_h2(rope_pair(pack_h2(ka[4 * q + p], kz[4 * q + p]), rf[m][4 * q + p]));
+              kq[2 * p] = rr.x;
+              kq[2 * p + 1] = rr.y;
+            }
+            const h8 qf = *(const h8*)(qrow + 32 * m + 8 * q);
+            sc = mfma32(qf, kq, sc);
+          }
+        }
+
+        // ---- values: dequantize, transpose into (coordinate, token) tiles through one-hot MFMAs
+        h8 vop[VT][2];
+        {
+          f16v vt[VT];
+#pragma unroll
+          for (int w = 0; w < VT; ++w) vt[w] = f16v{};
+#pragma unroll
+          for (int s = 0; s < VS; ++s) vt[s / 2] = mfma32(dequant_int4x8(cur.v[s], cur.pv[s]), ohv[s & 1], vt[s / 2]);
+#pragma unroll
+          for (int w = 0; w < VT; ++w) {
+            vop[w][0] = cvt_h8(vt[w], 0);
+            vop[w][1] = cvt_h8(vt[w], 8);
+          }
+        }
+
+        // ---- online softmax; lane (token t) holds the scores of heads 0-3 in sc[0..3]
+        float s4[4] = {sc[0], sc[1], sc[2], sc[3]};
+        if (t0 + 32 > T && t0 + t >= T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] = -INFINITY;
+        const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+        if (fresh || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
+          // exact per-head maximum over the super-tile, then raise the reference (or set it, first time)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float c = s4[i];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) c = fmaxf(c, __shfl_xor(c, o));
+            const float d = fresh ? c : fmaxf(c, 0.0f);
+            const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+            for (int w = 0; w < VT; ++w) acc[w][i] *= alpha;
+            psum[i] *= alpha;
+            s4[i] -= d;
+            m_ref[i] += d;
+          }
+          fresh = false;
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(s4[i]);  // 2^-inf = 0
+          psum[i] += p[i];
+        }
+        // P^T: k-slots 0-3 of half 0 carry heads 0-3 of token t; the one-hot product moves tokens into rows
+        h8 pa = {};
+        if (hf == 0) pa = h8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3], 0, 0, 0, 0};
+        const f16v pt = mfma32(pa, ohp, f16v{});
+        const h8 pop0 = cvt_h8(pt, 0), pop1 = cvt_h8(pt, 8);
+        // acc[head, coordinate] += sum_t p[head, t] v[t, coordinate]; rows replicate the 4 heads
+#pragma unroll
+        for (int w = 0; w < VT; ++w) {
+          const f16v o = mfma32(pop1, vop[w][1], mfma32(pop0, vop[w][0], f16v{}));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[w][i] += o[i];
+        }
+      }
+    }
+    settle(kn);
+  }
+
+  // ---- partial of this wave: m[GQ], l[GQ], acc[GQ][2 VT * 16] (latent); m = -inf for an empty wave
+  float* part = a.ws + ((size_t)((b * a.Hkv + h) * a.n_splits + split) * 4 + wv) * a.part_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float l = hf == 0 ? psum[i] : 0.0f;  // the two halves of the wave hold the same tokens
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    psum[i] = l;
+  }
+  if (lane < GQ) {
+    part[lane] = fresh ? -INFINITY : m_ref[lane];
+    part[GQ + lane] = psum[lane];
+  }
+  float* pacc = part + 2 * GQ;
+  if (hf == 0)
+#pragma unroll
+    for (int w = 0; w < VT; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pacc[i * (2 * VT * 16) + 32 * w + t] = acc[w][i];
+}
+
+// ---------------------------------------------------------------- host side
+
+hipError_t launch_merge_head128(int NV, const float* ws, const uint16_t* wv, float* out, int B, int Hkv, int Hq,
+                                int rv, int n_parts, int part_stride, hipStream_t st);
+
+template <int KS, int VS, bool VAR, int STG>
+static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
+  const int lds = i4::lds_layout(a.P, a.hb_max).total;
+  auto kern = decode_int4_kernel<KS, VS, VAR, STG>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge_head128(2 * ((VS + 1) / 2), a.ws, wv, out, a.B, a.Hkv, a.Hq, a.rv, a.n_splits * 4,
+                              a.part_stride, st);
+}
+
+int int4_max_pages_per_split() { return i4::MAX_SPLIT_PAGES; }
+
+bool int4_supported(const kvc_layout& L, int64_t hb_max) {
+  if (L.shared || L.latent_bits != 4 || L.residual_bits || L.head_dim != 128) return false;
+  if (L.n_q_heads != i4::GQ * L.n_kv_heads) return false;
+  if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
+  if (L.variable_rank && L.r_k_cap != L.r_v_cap) return false;
+  if (hb_max > 16 * 256 * 5) return false;
+  return i4::lds_layout(L.page_size, (int)hb_max).total <= 80 * 1024;
+}
+
+hipError_t launch_decode_int4(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
+                              int n_splits, int pages_per_split, int part_stride, const HeadSections& S_uniform,
+                              int hb_max, hipStream_t st) {
+  Int4Args a;
+  a.pool = C.pool; a.page_off = C.page_off; a.tok_off = C.tok_off;
+  a.block_table = in.block_table; a.seq_len = in.seq_len; a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk;
+  a.ws = (float*)ws; a.q_bf16 = in.q_dtype == KVC_BF16;
+  a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.max_blocks = in.max_blocks; a.P = L.page_size;
+  a.rk = L.r_k_cap; a.rv = L.r_v_cap; a.G = L.group; a.n_splits = n_splits; a.pages_per_split = pages_per_split;
+  a.part_stride = part_stride; a.hb_max = hb_max; a.theta = L.rope_theta; a.S_uniform = S_uniform;
+  const int grid = in.B * L.n_kv_heads * n_splits;
+  const int KS = ceil_div(L.r_k_cap, 16), VS = ceil_div(L.r_v_cap, 16);
+  const bool var = L.variable_rank != 0;
+  const int stg = ceil_div(hb_max, 16 * 256);
+#define KVC_TRY4(KS_, VS_, VAR_, STG_) \
+  if (KS == KS_ && VS == VS_ && var == VAR_ && stg <= STG_) return launch_int4<KS_, VS_, VAR_, STG_>(a, grid, in.wv, out, st);
+  KVC_TRY4(4, 4, true, 5)
+  KVC_TRY4(4, 4, false, 5)
+  KVC_TRY4(3, 4, false, 5)
+  KVC_TRY4(2, 2, true, 3)
+  KVC_TRY4(2, 2, false, 3)
+#undef KVC_TRY4
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvc

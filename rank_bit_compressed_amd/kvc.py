@@ -23,7 +23,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "work
           -4: "pointer not 16-byte aligned", -5: "HIP runtime error"}
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
-           "kvc_dense_decode_attn"]
+           "kvc_dense_decode_attn", "kvc_decode_path"]
 
 
 class KvcError(RuntimeError):
@@ -90,6 +90,7 @@ def lib():
         L.kvc_decode_attn.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_decode_attn.restype = C.c_int32
         L.kvc_dense_workspace_bytes.argtypes = [P, P]; L.kvc_dense_workspace_bytes.restype = C.c_int32
         L.kvc_dense_decode_attn.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_dense_decode_attn.restype = C.c_int32
+        L.kvc_decode_path.argtypes = [P, P]; L.kvc_decode_path.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -165,6 +166,16 @@ def compress(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, ra
                      _ptr(lat_v), _ptr(res_k), _ptr(res_v), _ptr(k), _ptr(v), _ptr(bk), _ptr(bv))
     c = cache.c()
     _check(lib().kvc_compress(C.byref(layout), C.byref(inp), C.byref(c), _stream()), "kvc_compress")
+
+
+PATH_HEAD, PATH_INT4, PATH_SHARED = 0, 1, 2
+
+
+def decode_path(layout: Layout) -> int:
+    """Which decode kernel serves the layout (PATH_INT4, PATH_HEAD or PATH_SHARED)."""
+    out = C.c_int32()
+    _check(lib().kvc_decode_path(C.byref(layout), C.byref(out)), "kvc_decode_path")
+    return out.value
 
 
 def decode_workspace_bytes(layout: Layout, B: int, max_T: int, num_splits: int = 0) -> int:
