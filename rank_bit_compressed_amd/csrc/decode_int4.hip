@@ -49,6 +49,7 @@ struct Int4Args {
 };
 
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 namespace i4 {
 constexpr int D = 128, GQ = 4, NP = 64;
@@ -56,7 +57,7 @@ constexpr int MAX_SPLIT_PAGES = 128;
 constexpr float TAU = 8.0f;  // lazy-max slack, log2 units
 
 struct Lds {
-  int meta_addr, meta_hb, meta_page, theta, qsrc, qbuf, stage, stage_bytes, off_bytes, total;
+  int meta_addr, meta_hb, meta_page, theta, qsrc, qbuf, pbuf, stage, stage_bytes, off_bytes, total;
 };
 __host__ __device__ inline Lds lds_layout(int P, int hb_max) {
   Lds L;
@@ -67,6 +68,7 @@ __host__ __device__ inline Lds lds_layout(int P, int hb_max) {
   L.theta = o; o += NP * 8;                     // RoPE frequencies, turns per position
   L.qsrc = o; o += NP * 2 * GQ * 4;             // scaled query, pair j: x_j of heads 0-3, then x_{j+64}
   L.qbuf = o; o += 4 * 2 * GQ * (NP + 4) * 4;  // per wave two super-tiles, rows padded by 4 dwords
+  L.pbuf = o; o += 4 * 32 * GQ * 2;             // per wave: probabilities of 32 tokens x 4 heads, fp16
   // stage buffer: the page's offset row (whole 64-dword rows, the tail zero-filled), then the head block
   L.off_bytes = 256 * ceil_div(P + 1, 64);
   L.stage_bytes = L.off_bytes + (int)pad16(hb_max);
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   int32_t* meta_hb = (int32_t*)(smem + LY.meta_hb);
   int32_t* meta_page = (int32_t*)(smem + LY.meta_page);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int t = lane & 31, hf = lane >> 5;
   const int split = blockIdx.x % a.n_splits;
   const int h = (blockIdx.x / a.n_splits) % a.Hkv;
@@ -181,16 +184,16 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
       const float rev = (float)(t * tturn[j]);
       rf[m][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
     }
-  // one-hot B operands.  Value transpose: k-slot 8hf + j of step s holds coordinate 16s + 8hf + perm8(j);
-  // it goes to column (16 (s % 2) + 8hf + perm8(j)) of value tile s / 2.  Probability transpose: k-slot
-  // j < 4 (lanes of half 0) holds head j; column c takes head c % 4.
-  h8 ohv[2], ohp;
+  // one-hot B operands of the value transpose: k-slot 8hf + j of step s holds coordinate 16s + 8hf + perm8(j);
+  // it goes to column (16 (s % 2) + 8hf + perm8(j)) of value tile s / 2
+  h8 ohv[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
     for (int j = 0; j < 8; ++j) ohv[e][j] = (t == 16 * e + 8 * hf + perm8(j)) ? (_Float16)1.0f : (_Float16)0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ohp[j] = (hf == 0 && j < 4 && (t & 3) == j) ? (_Float16)1.0f : (_Float16)0.0f;
+  // probabilities of this wave's super-tile, [token][head] fp16: the transposing LDS read turns them into
+  // the A operand of the value product (row = head, k-slot 8hf + j <-> token 16w + 8(j / 4) + 4hf + j % 4)
+  _Float16* pbuf = (_Float16*)(smem + LY.pbuf) + wv * 32 * GQ;
 
   // scaled query (log2(e) / sqrt(d), for exp2) into LDS
   float* qsrc = (float*)(smem + LY.qsrc);
@@ -265,7 +268,8 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   const int kmb = 4 * ceil_div(a.rk, a.G), vmb = 4 * ceil_div(a.rv, a.G);  // uniform: pair bytes per slot
 
   struct Words {  // a lane's LDS words for one super-tile: code dword and (scale, zero) word per step
-    uint32_t k[KS], pk[KS], v[VS], pv[VS];
+    uint32_t k[KS], pk[KS];
+    int co_v, po_v, r;
   };
 
   __syncthreads();  // page addresses and the scaled query visible
@@ -309,34 +313,30 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      // the LDS words of super-tile k of this wave (slot 32 (wv + 4k) + t), issued one super-tile ahead
+      // the key LDS words of super-tile k of this wave (slot 32 (wv + 4k) + t), issued one super-tile ahead,
+      // and the value offsets (the value words are read when the keys are done)
       auto fetch = [&](int k) -> Words {
         const int slot = 32 * (wv + 4 * k) + t;
-        int r, co_k, co_v, po_k, po_v;
+        int r, co_k, po_k;
+        Words w;
         if constexpr (VAR) {
           const uint32_t o0 = so[slot], o1 = so[slot + 1];
           r = (int)((o1 - o0) & 0xFFFFu);  // 0 for slots past the sequence end
-          co_k = co_v = (int)((o0 & 0xFFFFu) >> 1);
-          po_k = po_v = (int)(o0 >> 16) * 4;
+          co_k = w.co_v = (int)((o0 & 0xFFFFu) >> 1);
+          po_k = w.po_v = (int)(o0 >> 16) * 4;
         } else {
           r = a.rk;
           co_k = slot * kcb;
-          co_v = slot * vcb;
+          w.co_v = slot * vcb;
           po_k = slot * kmb;
-          po_v = slot * vmb;
+          w.po_v = slot * vmb;
         }
-        Words w;
+        w.r = r;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           w.k[s] = lds_u32(kcs, co_k + 8 * s);
           w.pk[s] = lds_u32(kms, po_k + 4 * ((16 * s + 8 * hf) / a.G));
           if constexpr (VAR) w.pk[s] = pair_if(16 * s + 8 * hf < r, w.pk[s]);
-        }
-#pragma unroll
-        for (int s = 0; s < VS; ++s) {
-          w.v[s] = lds_u32(vcs, co_v + 8 * s);
-          w.pv[s] = lds_u32(vms, po_v + 4 * ((16 * s + 8 * hf) / a.G));
-          if constexpr (VAR) w.pv[s] = pair_if(16 * s + 8 * hf < r, w.pv[s]);
         }
         return w;
       };
@@ -347,15 +347,20 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         if (k + 1 < nst_w) nxt = fetch(k + 1);
         const uint32_t* qrow = qbuf + (k * GQ + (t & 3)) * (NP + 4) + 4 * hf;
         const int t0 = page_t0 + 32 * (wv + 4 * k);
+        uint32_t vw[VS], vp[VS];
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          vw[s] = lds_u32(vcs, cur.co_v + 8 * s);
+          vp[s] = lds_u32(vms, cur.po_v + 4 * ((16 * s + 8 * hf) / a.G));
+          if constexpr (VAR) vp[s] = pair_if(16 * s + 8 * hf < cur.r, vp[s]);
+        }
 
         // ---- keys: dequantize all steps, then per half m the tiles m and m + 2 (head dims d and d + 64),
         // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
         h8 kb[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(cur.k[s], cur.pk[s]);
-        f16v sc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = -m_ref[i & 3];
+        f16v sc = {};
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           f16v ka = {}, kz = {};
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
 #pragma unroll
           for (int w = 0; w < VT; ++w) vt[w] = f16v{};
 #pragma unroll
-          for (int s = 0; s < VS; ++s) vt[s / 2] = mfma32(dequant_int4x8(cur.v[s], cur.pv[s]), ohv[s & 1], vt[s / 2]);
+          for (int s = 0; s < VS; ++s) vt[s / 2] = mfma32(dequant_int4x8(vw[s], vp[s]), ohv[s & 1], vt[s / 2]);
 #pragma unroll
           for (int w = 0; w < VT; ++w) {
             vop[w][0] = cvt_h8(vt[w], 0);
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         }
 
         // ---- online softmax; lane (token t) holds the scores of heads 0-3 in sc[0..3]
-        float s4[4] = {sc[0], sc[1], sc[2], sc[3]};
+        float s4[4] = {sc[0] - m_ref[0], sc[1] - m_ref[1], sc[2] - m_ref[2], sc[3] - m_ref[3]};
         if (t0 + 32 > T && t0 + t >= T)
 #pragma unroll
           for (int i = 0; i < 4; ++i) s4[i] = -INFINITY;
@@ -422,15 +427,33 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
           p[i] = __builtin_amdgcn_exp2f(s4[i]);  // 2^-inf = 0
           psum[i] += p[i];
         }
-        // P^T: k-slots 0-3 of half 0 carry heads 0-3 of token t; the one-hot product moves tokens into rows
-        h8 pa = {};
-        if (hf == 0) pa = h8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3], 0, 0, 0, 0};
-        const f16v pt = mfma32(pa, ohp, f16v{});
-        const h8 pop0 = cvt_h8(pt, 0), pop1 = cvt_h8(pt, 8);
+        // P^T through LDS: token t's four probabilities, then the transposing read.  Lane group G (lanes
+        // 16G..16G+15, half G / 2) reads the rows of tokens 16w + 8u + 4(G / 2) + (l % 16) / 4; lane i of the group
+        // receives head i % 4 of those 4 tokens (k-slots 8hf + 4u + 0..3)
+        if (hf == 0) {
+          const h4 pv4 = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+          *(h4*)(pbuf + 4 * t) = pv4;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        h8 pop[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tok = 16 * w + 8 * u + 4 * hf + (lane & 15) / 4;
+            const h4 x = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (__attribute__((address_space(3))) i16x4*)(pbuf + 4 * tok)));
+            pop[w][4 * u + 0] = x[0];
+            pop[w][4 * u + 1] = x[1];
+            pop[w][4 * u + 2] = x[2];
+            pop[w][4 * u + 3] = x[3];
+          }
         // acc[head, coordinate] += sum_t p[head, t] v[t, coordinate]; rows replicate the 4 heads
 #pragma unroll
         for (int w = 0; w < VT; ++w) {
-          const f16v o = mfma32(pop1, vop[w][1], mfma32(pop0, vop[w][0], f16v{}));
+          const f16v o = mfma32(pop[1], vop[w][1], mfma32(pop[0], vop[w][0], f16v{}));
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[w][i] += o[i];
         }
@@ -439,8 +462,9 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     settle(kn);
   }
 
-  // ---- partial of this wave: m[GQ], l[GQ], acc[GQ][2 VT * 16] (latent); m = -inf for an empty wave
-  float* part = a.ws + ((size_t)((b * a.Hkv + h) * a.n_splits + split) * 4 + wv) * a.part_stride;
+  // ---- partial of the workgroup: the four waves' (m, l, acc) combined in LDS (the staging buffers are
+  // idle now), then m[GQ], l[GQ], acc[GQ][2 VT * 16] (latent coordinates) for the merge; m = -inf when
+  // the split holds no token
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float l = hf == 0 ? psum[i] : 0.0f;  // the two halves of the wave hold the same tokens
@@ -448,22 +472,83 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
     psum[i] = l;
   }
+  constexpr int NC = 2 * VT * 16;  // latent coordinates per head in the partial
+  float* red = (float*)(smem + LY.stage);  // [wave][2 GQ + GQ NC]
+  float* mine = red + wv * (2 * GQ + GQ * NC);
   if (lane < GQ) {
-    part[lane] = fresh ? -INFINITY : m_ref[lane];
-    part[GQ + lane] = psum[lane];
+    mine[lane] = fresh ? -INFINITY : m_ref[lane];
+    mine[GQ + lane] = psum[lane];
   }
-  float* pacc = part + 2 * GQ;
   if (hf == 0)
 #pragma unroll
     for (int w = 0; w < VT; ++w)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pacc[i * (2 * VT * 16) + 32 * w + t] = acc[w][i];
+      for (int i = 0; i < 4; ++i) mine[2 * GQ + i * NC + 32 * w + t] = acc[w][i];
+  __syncthreads();
+  float* part = a.ws + (size_t)((b * a.Hkv + h) * a.n_splits + split) * a.part_stride;
+  for (int e = tid; e < GQ * NC; e += 256) {
+    const int hq = e / NC, c = e % NC;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w * (2 * GQ + GQ * NC) + hq]);
+    float av = 0.0f, lv = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* pw = red + w * (2 * GQ + GQ * NC);
+      const float wt = pw[hq] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pw[hq] - mx);
+      av += wt * pw[2 * GQ + hq * NC + c];
+      lv += wt * pw[GQ + hq];
+    }
+    part[2 * GQ + hq * NC + c] = av;
+    if (c == 0) {
+      part[hq] = mx;
+      part[GQ + hq] = lv;
+    }
+  }
+}
+
+// Final combine over the context splits and the value basis: one workgroup per (sequence, query head),
+// thread d computes out[d] = (B_v c*)[d] / l* with c* = sum_s 2^(m_s - m*) acc_s, l* = sum_s 2^(m_s - m*) l_s.
+template <int NC>
+__global__ __launch_bounds__(128) void merge_int4_kernel(const float* ws, const uint16_t* wv, float* out, int Hkv,
+                                                          int Hq, int rv, int n_splits, int part_stride) {
+  __shared__ float cst[NC];
+  __shared__ float lst;
+  const int bq = blockIdx.x, hq_all = bq % Hq, b = bq / Hq;
+  const int h = hq_all / i4::GQ, hq = hq_all % i4::GQ;
+  const int tid = threadIdx.x;
+  const float* parts = ws + (size_t)(b * Hkv + h) * n_splits * part_stride;
+  if (tid < NC) {
+    float mx = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, parts[(size_t)s * part_stride + hq]);
+    float c = 0.0f, l = 0.0f;
+    for (int s = 0; s < n_splits; ++s) {
+      const float* ps = parts + (size_t)s * part_stride;
+      const float ms = ps[hq];
+      if (ms == -INFINITY) continue;
+      const float wt = exp2f(ms - mx);
+      c += wt * ps[2 * i4::GQ + hq * NC + tid];
+      l += wt * ps[i4::GQ + hq];
+    }
+    cst[tid] = c;
+    if (tid == 0) lst = l;
+  }
+  __syncthreads();
+  const uint16_t* row = wv + ((size_t)h * i4::D + tid) * rv;  // B_v row d = tid, rv bf16 values
+  float o = 0.0f;
+  for (int i = 0; i < rv; i += 8) {
+    const u4 raw = *(const u4*)(row + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = raw[e >> 1];
+      o += __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * cst[i + e];
+    }
+  }
+  out[((size_t)b * Hq + hq_all) * i4::D + tid] = o / lst;
 }
 
 // ---------------------------------------------------------------- host side
 
-hipError_t launch_merge_head128(int NV, const float* ws, const uint16_t* wv, float* out, int B, int Hkv, int Hq,
-                                int rv, int n_parts, int part_stride, hipStream_t st);
 
 template <int KS, int VS, bool VAR, int STG>
 static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
@@ -476,8 +561,10 @@ static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, f
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_merge_head128(2 * ((VS + 1) / 2), a.ws, wv, out, a.B, a.Hkv, a.Hq, a.rv, a.n_splits * 4,
-                              a.part_stride, st);
+  constexpr int NC = 32 * ((VS + 1) / 2);
+  hipLaunchKernelGGL((merge_int4_kernel<NC>), dim3(a.B * a.Hq), dim3(128), 0, st, a.ws, wv, out, a.Hkv, a.Hq, a.rv,
+                     a.n_splits, a.part_stride);
+  return hipGetLastError();
 }
 
 int int4_max_pages_per_split() { return i4::MAX_SPLIT_PAGES; }
