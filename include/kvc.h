@@ -207,6 +207,16 @@ kvc_status kvc_decode_workspace_bytes(const kvc_layout* layout, int32_t B, int32
 kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
                            float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* kvc_decode_attn with a measurement hook: ev_begin and ev_end are caller-created hipEvent_t
+ * handles (passed as void*), recorded on `stream` immediately before and after the launch of the
+ * attention kernel; the split merge that follows lies outside the pair.  hipEventElapsedTime of
+ * the pair is then the attention kernel's own duration.  Same results and errors as
+ * kvc_decode_attn; both events are required (INVALID_ARG otherwise), and on an error returned
+ * before the launch neither event is recorded.  The events stay owned by the caller. */
+kvc_status kvc_decode_attn_timed(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                                 float* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin,
+                                 void* ev_end);
+
 /* Which decode kernel kvc_decode_attn runs for a layout: KVC_PATH_INT4 (per-head INT4 latents,
  * head_dim 128, no residual: the fast kernel), KVC_PATH_HEAD (the general per-head kernel: fp32
  * latents, head_dim 64, rotated residual) or KVC_PATH_SHARED (block-shared latents).  Host-only;

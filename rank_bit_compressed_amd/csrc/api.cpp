@@ -10,6 +10,7 @@
 namespace kvc {
 
 static thread_local int32_t g_last_hip_error = 0;
+thread_local LaunchMarks g_marks;
 
 kvc_status hip_fail(hipError_t e) {
   g_last_hip_error = (int32_t)e;
@@ -156,6 +157,17 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
   }
   if (e != hipSuccess) return hip_fail(e);
   return KVC_OK;
+}
+
+kvc_status kvc_decode_attn_timed(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                                 float* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin, void* ev_end) {
+  if (!ev_begin || !ev_end) return KVC_ERR_INVALID_ARG;
+  struct Reset {
+    ~Reset() { g_marks = LaunchMarks{}; }
+  } reset;
+  g_marks.begin = (hipEvent_t)ev_begin;
+  g_marks.end = (hipEvent_t)ev_end;
+  return kvc_decode_attn(layout, cache, in, out, ws, ws_bytes, stream);
 }
 
 kvc_status kvc_compress(const kvc_layout* layout, const kvc_compress_in* in, const kvc_cache* cache, void* stream) {

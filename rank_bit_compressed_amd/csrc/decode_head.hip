@@ -487,8 +487,11 @@ static hipError_t launch_variant(const DecodeHeadArgs& a, int grid, const uint16
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
+  hipError_t e = mark(g_marks.begin, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_head_kernel<D, 2 * VC, RES>), dim3(a.B * a.Hkv), dim3(256), 0, st, a.ws, wv, out, a.Hkv,
                      a.Hq, a.rv, a.n_splits * 4, a.part_stride);

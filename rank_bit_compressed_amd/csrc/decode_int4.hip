@@ -558,8 +558,11 @@ static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, f
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
+  hipError_t e = mark(g_marks.begin, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   constexpr int NC = 32 * ((VS + 1) / 2);
   hipLaunchKernelGGL((merge_int4_kernel<NC>), dim3(a.B * a.Hq), dim3(128), 0, st, a.ws, wv, out, a.Hkv, a.Hq, a.rv,

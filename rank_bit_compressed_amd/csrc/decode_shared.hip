@@ -298,8 +298,11 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   hipError_t e = hipFuncSetAttribute((const void*)decode_shared_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
+  e = mark(g_marks.begin, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_shared_kernel, dim3(grid), dim3(256), lds, st, a);
   e = hipGetLastError();
+  if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * L.n_kv_heads * in.B), dim3(256), 0, st, a.ws, in.wv, out,
                      in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride);

@@ -20,6 +20,15 @@ namespace kvc {
 // Record the HIP error of this thread and map it to a status.
 kvc_status hip_fail(hipError_t e);
 
+// Optional pair of caller-owned HIP events that the decode launchers record on their stream right
+// before and right after the attention kernel (not the split merge).  Set only for the duration of
+// one kvc_decode_attn_timed call on the calling thread; null otherwise.
+struct LaunchMarks {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+extern thread_local LaunchMarks g_marks;
+inline hipError_t mark(hipEvent_t e, hipStream_t st) { return e ? hipEventRecord(e, st) : hipSuccess; }
+
 __host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t(15); }
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

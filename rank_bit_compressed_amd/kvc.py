@@ -23,7 +23,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "work
           -4: "pointer not 16-byte aligned", -5: "HIP runtime error"}
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
-           "kvc_dense_decode_attn", "kvc_decode_path"]
+           "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed"]
 
 
 class KvcError(RuntimeError):
@@ -88,6 +88,8 @@ def lib():
         L.kvc_decode_workspace_bytes.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P]
         L.kvc_decode_workspace_bytes.restype = C.c_int32
         L.kvc_decode_attn.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_decode_attn.restype = C.c_int32
+        L.kvc_decode_attn_timed.argtypes = [P, P, P, P, P, C.c_size_t, P, P, P]
+        L.kvc_decode_attn_timed.restype = C.c_int32
         L.kvc_dense_workspace_bytes.argtypes = [P, P]; L.kvc_dense_workspace_bytes.restype = C.c_int32
         L.kvc_dense_decode_attn.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_dense_decode_attn.restype = C.c_int32
         L.kvc_decode_path.argtypes = [P, P]; L.kvc_decode_path.restype = C.c_int32
@@ -200,8 +202,10 @@ def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0) 
 
 
 def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                num_splits=0, out=None, ws=None):
-    """kvc_decode_attn -> fp32 [(L,) B, Hq, d]."""
+                num_splits=0, out=None, ws=None, events=None):
+    """kvc_decode_attn -> fp32 [(L,) B, Hq, d].  events: optional (begin, end) pair of recorded-once
+    torch.cuda.Event objects; the call then goes through kvc_decode_attn_timed, which records them around
+    the attention kernel alone."""
     B = block_table.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -210,9 +214,52 @@ def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk,
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits)
     c = cache.c()
-    _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
-                                 _stream()), "kvc_decode_attn")
+    if events is None:
+        _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream()), "kvc_decode_attn")
+    else:
+        eb, ee = (_event_handle(e) for e in events)
+        _check(lib().kvc_decode_attn_timed(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws),
+                                           ws.numel(), _stream(), eb, ee), "kvc_decode_attn_timed")
     return out
+
+
+class DecodePlan:
+    """kvc_decode_attn with its arguments marshalled once, for calling in a loop (a decode step per call).
+
+    The tensors given here must stay alive and in place while the plan is used; each call reads whatever
+    they hold at launch time.  Calls enqueue on the current stream, like decode_attn."""
+
+    def __init__(self, layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
+                 num_splits=0, out=None, ws=None):
+        B = block_table.shape[0]
+        self.out = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        need = decode_workspace_bytes(layout, B, max_T, num_splits)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws)
+        self._layout, self._cache = layout, cache.c()
+        self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits)
+        self._args = (C.byref(self._layout), C.byref(self._cache), C.byref(self._in), _ptr(self.out), _ptr(ws),
+                      ws.numel())
+        self._fn, self._fn_timed = lib().kvc_decode_attn, lib().kvc_decode_attn_timed
+
+    def __call__(self, events=None):
+        if events is None:
+            st = self._fn(*self._args, _stream())
+        else:
+            st = self._fn_timed(*self._args, _stream(), *(_event_handle(e) for e in events))
+        if st != 0:
+            _check(st, "kvc_decode_attn")
+        return self.out
+
+
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (torch creates the event at its first record)."""
+    h = ev.cuda_event
+    if not h:
+        raise ValueError("record the torch.cuda.Event once before passing it (its HIP event is created lazily)")
+    return C.c_void_p(h)
 
 
 def dense_in(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, max_T, num_splits=0) -> DenseIn:

@@ -113,3 +113,29 @@ def test_compress_from_dense(name, kw):
                                         ref.page_bytes_uniform(layout(w)) * w.n_pages)
     assert np.array_equal(cache.pool[: len(pool)].cpu().numpy(), pool)
     assert np.array_equal(cache.page_off.cpu().numpy(), page_off)
+
+
+@pytest.mark.parametrize("name", ["varrank_paged_32k", "residual_128k", "shared_latent_32k"])
+def test_timed_entry_matches_and_brackets_the_kernel(name):
+    """kvc_decode_attn_timed gives the same bits as kvc_decode_attn; its event pair (attention kernel
+    only) lies inside a pair recorded around the whole call (kernel + split merge)."""
+    kw = dict(B=2, T=1500) if name != "shared_latent_32k" else dict(B=1, T=1500, n_layers=2)
+    w = synth.WORKLOADS[name].scaled(**kw)
+    d = dev(synth.make_inputs(w))
+    cache = gpu_cache(w, d)
+    L = gpu_layout(w)
+    plain = gpu_decode(w, d, cache)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev[2:]:
+        e.record()
+    torch.cuda.synchronize()
+    ev[0].record()
+    timed = kvc.decode_attn(L, cache, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
+                            q_pos=d["q_pos"], events=(ev[2], ev[3]))
+    ev[1].record()
+    torch.cuda.synchronize()
+    assert torch.equal(plain, timed)
+    call_ms, kern_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    print(f"    call {call_ms:.4f} ms, attention kernel {kern_ms:.4f} ms", flush=True)
+    assert 0.0 < kern_ms <= call_ms
+    assert ev[0].elapsed_time(ev[2]) >= 0.0 and ev[3].elapsed_time(ev[1]) >= 0.0
