@@ -1,11 +1,12 @@
 // dense.hip -- plain softmax decode attention over a paged bf16 cache (gfx950): the dense comparison.
 //
 // Same decomposition as the compressed kernel: one workgroup (4 waves) per (sequence, kv head,
-// context split), 32-token super-tiles, per-wave online softmax and a merge kernel.  Per 16-token
-// block, lane (token l%16, group g) loads its token's key dims (d/4)g .. (d/4)(g+1)-1 with 16-byte
-// loads; scores S^T = K Q^T on the bf16 MFMA (k-slot 8g + j of chunk c <-> dim (d/4)g + 8c + j); values go
-// through a one-hot bf16 MFMA (a register transpose, exact) and the value product runs on the fp16
-// MFMA with fp16 probabilities.
+// context split), 32-token super-tiles, per-wave online softmax, the four waves combined in LDS at the
+// end, and a merge kernel over the splits.  Per 16-token block, lane (token l%16, group g) loads its
+// token's key dims (d/4)g .. (d/4)(g+1)-1 with 16-byte loads, one super-tile ahead of the one it computes
+// (the stream is the whole cost, so loads stay in flight during the arithmetic); scores S^T = K Q^T on
+// the bf16 MFMA (k-slot 8g + j of chunk c <-> dim (d/4)g + 8c + j); values go through a one-hot bf16 MFMA
+// (a register transpose, exact) and the value product runs on the fp16 MFMA with fp16 probabilities.
 #include <math.h>
 
 #include <algorithm>
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
   constexpr int QC = D / 32;  // chunks of the score product
   constexpr int NT = D / 16;  // N-tiles of the value product
   constexpr int DL = D / 4;   // head dims per lane group: lane group g holds dims DL*g .. DL*g + DL - 1
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int n = lane & 15, g = lane >> 4;
   const int split = blockIdx.x % a.n_splits;
   const int h = (blockIdx.x / a.n_splits) % a.Hkv;
@@ -66,21 +68,43 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
   const int n_st = (T + 31) / 32;
   const int st_begin = split * a.st_per_split;
   const int st_end = min(n_st, st_begin + a.st_per_split);
-  for (int st = st_begin + wv; st < st_end; st += 4) {
+  // this lane's keys and values of super-tile st.  Tokens past the sequence end read the last token's row
+  // instead (real, finite data; their scores are masked, so they get probability 0): the loads are then
+  // unconditional and the compiler can count them, leaving the next super-tile's loads in flight.
+  auto load = [&](int st, bf8 (&kc)[2][QC], bf8 (&vc)[2][QC]) {
     const int t0 = st * 32;
     const int page = uniform(a.block_table[(size_t)b * a.max_blocks + t0 / P]);
     const size_t head_base = ((size_t)page * a.Hkv + h) * P;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tt = min(16 * blk + n, T - 1 - t0);
+      const size_t row = (head_base + (t0 % P) + tt) * D + DL * g;
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        kc[blk][c] = *(const bf8*)(a.k_pages + row + 8 * c);
+        vc[blk][c] = *(const bf8*)(a.v_pages + row + 8 * c);
+      }
+    }
+  };
+  bf8 kn[2][QC], vn[2][QC];
+  if (st_begin + wv < st_end) load(st_begin + wv, kn, vn);
+  for (int st = st_begin + wv; st < st_end; st += 4) {
+    const int t0 = st * 32;
+    bf8 kcur[2][QC], vcur[2][QC];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        kcur[blk][c] = kn[blk][c];
+        vcur[blk][c] = vn[blk][c];
+      }
+    if (st + 4 < st_end) load(st + 4, kn, vn);
     float sc[2][4];
     h4 vtb[NT][2];
+#pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int tt = 16 * blk + n;
-      const bool valid = t0 + tt < T;
-      const size_t row = (head_base + (t0 % P) + tt) * D + DL * g;
-      bf8 kc[QC], vc[QC];
-      for (int c = 0; c < QC; ++c) {
-        kc[c] = valid ? *(const bf8*)(a.k_pages + row + 8 * c) : bf8{};
-        vc[c] = valid ? *(const bf8*)(a.v_pages + row + 8 * c) : bf8{};
-      }
+      const bf8* kc = kcur[blk];
+      const bf8* vc = vcur[blk];
       f4 s4 = {0, 0, 0, 0};
       for (int c = 0; c < QC; ++c) s4 = mfma_bf16(kc[c], qop[c], s4);
       for (int i = 0; i < 4; ++i) sc[blk][i] = s4[i] * qscale;
@@ -127,39 +151,60 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  float* part = a.ws + ((size_t)((b * a.Hkv + h) * a.n_splits + split) * 4 + wv) * a.part_stride;
+  // the four waves' (m, l, acc) combined in LDS into the split's partial
+  __shared__ float red[4][2 * DGQ + DGQ * D];
+  float* mine = red[wv];
   if (lane < DGQ) {
-    part[lane] = m_run;
-    part[DGQ + lane] = l_run;
+    mine[lane] = m_run;
+    mine[DGQ + lane] = l_run;
   }
   for (int nt = 0; nt < NT; ++nt) {
     const int c = nt >> 1, e = nt & 1;
     const int dim = DL * (2 * e + (n >> 3)) + 8 * c + (n & 7);
     for (int i = 0; i < 4; ++i) {
       const int hq = 4 * g + i;
-      if (hq < DGQ) part[2 * DGQ + hq * D + dim] = acc[nt][i];
+      if (hq < DGQ) mine[2 * DGQ + hq * D + dim] = acc[nt][i];
+    }
+  }
+  __syncthreads();
+  float* part = a.ws + (size_t)((b * a.Hkv + h) * a.n_splits + split) * a.part_stride;
+  for (int e = tid; e < DGQ * D; e += 256) {
+    const int hq = e / D;
+    float mx = -INFINITY;
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][hq]);
+    float av = 0.0f, lv = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+      const float wt = red[w][hq] == -INFINITY ? 0.0f : exp2f(red[w][hq] - mx);
+      av += wt * red[w][2 * DGQ + e];
+      lv += wt * red[w][DGQ + hq];
+    }
+    part[2 * DGQ + e] = av;
+    if (e % D == 0) {
+      part[hq] = mx;
+      part[DGQ + hq] = lv;
     }
   }
 }
 
+// One workgroup per (sequence, query head); thread d combines output dim d over the splits.
 template <int D>
-__global__ __launch_bounds__(256) void dense_merge_kernel(const float* ws, float* out, int Hkv, int Hq, int n_parts,
-                                                          int part_stride) {
-  const int bh = blockIdx.x, h = bh % Hkv, b = bh / Hkv;
-  const int hq = threadIdx.x / 64, l = threadIdx.x % 64;
-  const float* parts = ws + (size_t)bh * n_parts * part_stride;
+__global__ __launch_bounds__(D) void dense_merge_kernel(const float* ws, float* out, int Hkv, int Hq, int n_parts,
+                                                        int part_stride) {
+  const int bq = blockIdx.x, hq_all = bq % Hq, b = bq / Hq;
+  const int h = hq_all / DGQ, hq = hq_all % DGQ, d = threadIdx.x;
+  const float* parts = ws + (size_t)(b * Hkv + h) * n_parts * part_stride;
   float m = -INFINITY;
   for (int p = 0; p < n_parts; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
-  float lsum = 0.0f, o[D / 64];
-  for (int k = 0; k < D / 64; ++k) o[k] = 0.0f;
+  float lsum = 0.0f, o = 0.0f;
+#pragma unroll 8
   for (int p = 0; p < n_parts; ++p) {
     const float* pp = parts + (size_t)p * part_stride;
-    if (pp[hq] == -INFINITY) continue;
-    const float wgt = exp2f(pp[hq] - m);
+    const float mp = pp[hq];
+    const float wgt = mp == -INFINITY ? 0.0f : exp2f(mp - m);
     lsum += wgt * pp[DGQ + hq];
-    for (int k = 0; k < D / 64; ++k) o[k] += wgt * pp[2 * DGQ + hq * D + l + 64 * k];
+    o += wgt * pp[2 * DGQ + hq * D + d];
   }
-  for (int k = 0; k < D / 64; ++k) out[((size_t)b * Hq + h * DGQ + hq) * D + l + 64 * k] = o[k] / lsum;
+  out[((size_t)b * Hq + hq_all) * D + d] = o / lsum;
 }
 
 static void dense_splits(int B, int Hkv, int max_T, int requested, int* ns, int* sps) {
@@ -186,7 +231,7 @@ kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_by
   int ns, sps;
   dense_splits(in.B, in.n_kv_heads, in.max_T, in.num_splits, &ns, &sps);
   const int stride = 2 * DGQ + DGQ * in.head_dim;
-  const size_t bytes = (size_t)in.B * in.n_kv_heads * ns * 4 * stride * sizeof(float);
+  const size_t bytes = (size_t)in.B * in.n_kv_heads * ns * stride * sizeof(float);
   if (need) {
     *need = bytes;
     return KVC_OK;
@@ -211,11 +256,11 @@ kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_by
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   if (in.head_dim == 128) {
-    hipLaunchKernelGGL(dense_merge_kernel<128>, dim3(in.B * in.n_kv_heads), dim3(256), 0, st, a.ws, out,
-                       in.n_kv_heads, in.n_q_heads, ns * 4, stride);
+    hipLaunchKernelGGL(dense_merge_kernel<128>, dim3(in.B * in.n_q_heads), dim3(128), 0, st, a.ws, out,
+                       in.n_kv_heads, in.n_q_heads, ns, stride);
   } else {
-    hipLaunchKernelGGL(dense_merge_kernel<64>, dim3(in.B * in.n_kv_heads), dim3(256), 0, st, a.ws, out,
-                       in.n_kv_heads, in.n_q_heads, ns * 4, stride);
+    hipLaunchKernelGGL(dense_merge_kernel<64>, dim3(in.B * in.n_q_heads), dim3(64), 0, st, a.ws, out,
+                       in.n_kv_heads, in.n_q_heads, ns, stride);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
