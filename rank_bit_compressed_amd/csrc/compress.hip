@@ -255,9 +255,9 @@ __global__ __launch_bounds__(256) void project_kernel(const float* k, const floa
   const float* x = (which ? v : k) + (((size_t)b * max_T + t) * Hkv + h) * d;
   const uint16_t* Bm = (which ? basis_v : basis_k) + (size_t)h * d * rcap;
   for (int j = lane; j < d; j += 64) xs[wv][j] = x[j];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   float* c_out = (which ? lat_v : lat_k) + (((size_t)b * max_T + t) * Hkv + h) * rcap;
   for (int i = lane; i < rcap; i += 64) {
     float acc = 0.0f;
@@ -267,18 +267,18 @@ __global__ __launch_bounds__(256) void project_kernel(const float* k, const floa
     if (i < 64) cs[wv][i] = acc;
   }
   if (!residual) return;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   for (int j = lane; j < d; j += 64) {
     float acc = 0.0f;
     for (int i = 0; i < r; ++i) acc = fmaf(__builtin_bit_cast(float, (uint32_t)Bm[(size_t)j * rcap + i] << 16), cs[wv][i], acc);
     es[wv][j] = xs[wv][j] - acc;
   }
   for (int hstep = 1; hstep < d; hstep <<= 1) {  // Sylvester order: pairs (i, i + hstep) in blocks of 2*hstep
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     float lo_v = 0.0f, hi_v = 0.0f;
     int i0 = 0;
     if (lane < d / 2) {
@@ -288,17 +288,17 @@ __global__ __launch_bounds__(256) void project_kernel(const float* k, const floa
       lo_v = a0 + a1;
       hi_v = a0 - a1;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     if (lane < d / 2) {
       es[wv][i0] = lo_v;
       es[wv][i0 + hstep] = hi_v;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   float* y_out = (which ? res_v : res_k) + (((size_t)b * max_T + t) * Hkv + h) * d;
   const float sc = 1.0f / sqrtf((float)d);
   for (int j = lane; j < d; j += 64) y_out[j] = es[wv][j] * sc;

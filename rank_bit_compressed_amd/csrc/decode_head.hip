@@ -246,9 +246,9 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
         for (int hq = 0; hq < GQ; ++hq)
           qbuf[wv][hq][lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
       float sc[2][4];
       h4 vtb[NV][2];

@@ -55,9 +55,10 @@ namespace i4 {
 constexpr int D = 128, GQ = 4, NP = 64;
 constexpr int MAX_SPLIT_PAGES = 128;
 constexpr float TAU = 8.0f;  // lazy-max slack, log2 units
+constexpr int STATIC_LDS = 4 * 2 * GQ * (NP + 4) * 4 + 4 * 32 * GQ * 2;  // the kernel's own LDS arrays (bytes)
 
 struct Lds {
-  int meta_addr, meta_hb, meta_page, theta, qsrc, qbuf, pbuf, stage, stage_bytes, off_bytes, total;
+  int meta_addr, meta_hb, meta_page, theta, qsrc, stage, stage_bytes, off_bytes, total;
 };
 __host__ __device__ inline Lds lds_layout(int P, int hb_max) {
   Lds L;
@@ -67,8 +68,6 @@ __host__ __device__ inline Lds lds_layout(int P, int hb_max) {
   L.meta_page = o; o += MAX_SPLIT_PAGES * 4;
   L.theta = o; o += NP * 8;                     // RoPE frequencies, turns per position
   L.qsrc = o; o += NP * 2 * GQ * 4;             // scaled query, pair j: x_j of heads 0-3, then x_{j+64}
-  L.qbuf = o; o += 4 * 2 * GQ * (NP + 4) * 4;  // per wave two super-tiles, rows padded by 4 dwords
-  L.pbuf = o; o += 4 * 32 * GQ * 2;             // per wave: probabilities of 32 tokens x 4 heads, fp16
   // stage buffer: the page's offset row (whole 64-dword rows, the tail zero-filled), then the head block
   L.off_bytes = 256 * ceil_div(P + 1, 64);
   L.stage_bytes = L.off_bytes + (int)pad16(hb_max);
@@ -129,7 +128,14 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   const int qpos = a.q_pos ? a.q_pos[b] : T;
   const int lb0 = split * a.pages_per_split;
   const int n_pages = max(0, min((T + P - 1) / P, lb0 + a.pages_per_split) - lb0);
-  uint32_t* qbuf = (uint32_t*)(smem + LY.qbuf) + wv * 2 * GQ * (NP + 4);
+  // Per-wave buffers that the page copies never touch live in arrays of their own, so that the compiler can
+  // tell their reads apart from the LDS the copies write and does not wait for copies in flight before them.
+  // qbuf: per wave two super-tiles of rotated query, rows padded by 4 dwords; pbuf: per wave the
+  // probabilities of 32 tokens x 4 heads, fp16.
+  __shared__ __attribute__((aligned(16))) uint32_t qbuf_all[4 * 2 * GQ * (NP + 4)];
+  __shared__ __attribute__((aligned(16))) _Float16 pbuf_all[4 * 32 * GQ];
+  static_assert(sizeof(qbuf_all) + sizeof(pbuf_all) == STATIC_LDS, "static LDS accounting");
+  uint32_t* qbuf = qbuf_all + wv * 2 * GQ * (NP + 4);
 
   // ---- page addresses of the split
   for (int i = tid; i < n_pages; i += 256) {
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     for (int j = 0; j < 8; ++j) ohv[e][j] = (t == 16 * e + 8 * hf + perm8(j)) ? (_Float16)1.0f : (_Float16)0.0f;
   // probabilities of this wave's super-tile, [token][head] fp16: the transposing LDS read turns them into
   // the A operand of the value product (row = head, k-slot 8hf + j <-> token 16w + 8(j / 4) + 4hf + j % 4)
-  _Float16* pbuf = (_Float16*)(smem + LY.pbuf) + wv * 32 * GQ;
+  _Float16* pbuf = pbuf_all + wv * 32 * GQ;
 
   // scaled query (log2(e) / sqrt(d), for exp2) into LDS
   float* qsrc = (float*)(smem + LY.qsrc);
@@ -247,10 +253,15 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     }
     return cnt;
   };
-  // this wave's copies except the last `keep` issued have landed; the barrier publishes everyone's
+  // this wave's copies except the last `keep` issued have landed (the explicit wait), and after the barrier
+  // everyone's have.  The copies write LDS directly, and LDS is coherent within the workgroup, so the barrier
+  // needs no memory fence of its own: a workgroup-scope one would make every wave wait for its copies still
+  // in flight.  The wavefront-scope LDS fences only keep the compiler from moving LDS accesses across it.
   auto settle = [&](int keep) {
     vmcnt_wait(keep);
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   };
 
   // running state: value accumulator (4 heads x the lane's latent coordinates), sums, reference maxima
@@ -309,9 +320,9 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
             qbuf[(k * GQ + hq) * (NP + 4) + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
       // the key LDS words of super-tile k of this wave (slot 32 (wv + 4k) + t), issued one super-tile ahead,
       // and the value offsets (the value words are read when the keys are done)
@@ -434,9 +445,9 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
           const h4 pv4 = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
           *(h4*)(pbuf + 4 * t) = pv4;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         h8 pop[2];
 #pragma unroll
         for (int w = 0; w < 2; ++w)
@@ -578,7 +589,8 @@ bool int4_supported(const kvc_layout& L, int64_t hb_max) {
   if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
   if (L.variable_rank && L.r_k_cap != L.r_v_cap) return false;
   if (hb_max > 16 * 256 * 5) return false;
-  return i4::lds_layout(L.page_size, (int)hb_max).total <= 80 * 1024;
+  // two workgroups per compute unit: dynamic and static LDS within half of the 160 KiB
+  return i4::lds_layout(L.page_size, (int)hb_max).total + i4::STATIC_LDS <= 80 * 1024;
 }
 
 hipError_t launch_decode_int4(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,

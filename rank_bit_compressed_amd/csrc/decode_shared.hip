@@ -143,9 +143,9 @@ __global__ __launch_bounds__(256) void decode_shared_kernel(DecodeSharedArgs a) 
       for (int hq = 0; hq < SGQ; ++hq)
         qbuf[hq][j] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
     // ---- key up-projection of this wave's 32 head dims for both blocks, streaming latent chunks
     f4 kp[2][2];  // [m-tile w | w+4][block]
