@@ -81,6 +81,81 @@ def cpu_baseline(w, inp, min_seconds=10.0):
                       f"compression excluded"}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+# The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
+# a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
+# and head from the 512-dim latent) and the 128K rotated-residual cache (HBM).
+OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k")
+
+
+def decode_flops(w) -> int:
+    """Algorithmic flops of one decode step: key up-projection, scores and the latent value product (the
+    residual's Hadamard rotations are a fast transform, a few adds per element, and are not counted)."""
+    n_tok = w.B * w.T * (w.n_layers if w.shared else 1)
+    if w.shared:
+        per_tok = 2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.head_dim * w.n_q_heads + 2 * w.r_v * w.n_q_heads
+    else:
+        per_tok = (2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.head_dim * w.n_q_heads
+                   + 2 * w.r_v * w.n_q_heads)
+    return n_tok * per_tok
+
+
+def other_workloads(steps: int, warmup: int) -> dict:
+    """Each other workload at its full size: median kernel time (library events around the attention
+    kernel), wall time per call, and the figure of its own bound."""
+    import torch
+    from rank_bit_compressed_amd import accounting, kvc, synth
+
+    res = {}
+    for name in OTHER:
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w, device="cuda")
+        L = kvc.make_layout(**w.layout_kwargs())
+        cache = kvc.DeviceCache.allocate(L, w.n_pages)
+        kvc.compress(L, cache, inp["block_table"], inp["seq_len"], w.T, ranks=inp["ranks"], lat_k=inp["lat_k"],
+                     lat_v=inp["lat_v"], res_k=inp["res_k"], res_v=inp["res_v"])
+        plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
+                              q_pos=inp["q_pos"])
+        for k in ("lat_k", "lat_v", "res_k", "res_v"):
+            inp[k] = None
+        n = max(20, steps // 10)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        for _ in range(max(20, warmup // 10)):
+            plan()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            plan(ev[i])
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / n
+        ks = sorted(a.elapsed_time(b) for a, b in ev)
+        k_ms = ks[n // 2]
+        acct = accounting.compressed_stream_bytes(w, inp["ranks"], [w.T] * w.B)
+        nbytes = acct["stream"] + acct["tables"]
+        flops = decode_flops(w)
+        path = {kvc.PATH_HEAD: "general per-head kernel", kvc.PATH_INT4: "INT4 kernel",
+                kvc.PATH_SHARED: "block-shared kernel"}[kvc.decode_path(L)]
+        r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),
+             "compressed_bytes": nbytes, "hbm_gbs": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
+             "flops": flops, "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1)}
+        if name == "llama8b_layer_8k":
+            r["bound"] = "latency (the 4.7 MB cache stays in the last-level cache between calls)"
+        elif w.shared:
+            r["bound"] = "mfma"
+            r["frac_of_f16_mfma_peak"] = round(r["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)
+        else:
+            r["bound"] = "hbm"
+            r["frac_of_hbm_peak"] = round(r["hbm_gbs"] / HBM_PEAK_GBS, 4)
+        res[name] = r
+        del plan, cache, inp
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +164,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other workloads' figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path here "
@@ -200,6 +276,8 @@ def main():
         "compressed_bytes_per_step": alg_bytes,
         "dense": dense,
     }
+    if not args.no_other:
+        line["other_workloads"] = other_workloads(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, {k: (v.cpu() if v is not None else None) for k, v in cpu_inp.items()})
     print(json.dumps(line), flush=True)
