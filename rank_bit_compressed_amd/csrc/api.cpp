@@ -25,6 +25,7 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
 int head_max_pages_per_split();
 int head_decode_path(const kvc_layout& L);
 bool shared_supported(const kvc_layout& L);
+int shared_max_tiles_per_split();
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits);
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
                                 void* ws, int n_splits, int st_per_split, hipStream_t st);
@@ -69,12 +70,12 @@ static void choose_splits(const kvc_layout& L, int B, int max_T, int requested, 
   const int items = B * L.n_kv_heads * (L.shared ? L.n_layers : 1);
   int s = requested;
   if (s <= 0) {
-    const int target = 512;  // workgroups: two per compute unit
+    const int target = L.shared ? 256 : 512;  // workgroups: one (block-shared) or two per compute unit
     s = std::max(1, (target + items - 1) / items);
   }
   s = std::max(1, std::min(s, n_units));
   int per = (n_units + s - 1) / s;
-  if (!L.shared) per = std::min(per, head_max_pages_per_split());
+  per = std::min(per, L.shared ? shared_max_tiles_per_split() : head_max_pages_per_split());
   *per_split = per;
   *n_splits = (n_units + per - 1) / per;
 }
