@@ -11,11 +11,12 @@
 // (j, j + 64) meet in one lane, and holds W_k's 512 x 32 slice for them as v_mfma_f32_32x32x16_f16
 // A fragments in registers.  The workgroup walks 32-token super-tiles:
 //   - the super-tile's codes and scale/zero pairs (contiguous in the page record) go HBM -> LDS with
-//     buffer loads that write LDS directly, four super-tiles deep;
-//   - the workgroup dequantizes them once into an fp16 tile of 16-byte chunks (8 coordinates of one token):
-//     chunk (d, token), d = 2 step + half, sits at slot 32 d + (token ^ (d % 16)), so that every wave's
-//     up-projection operand is one 1 KiB read per step and the dequantization writes (one token's 64
-//     chunks per wave instruction) both avoid LDS bank conflicts; the
+//     buffer loads that write LDS directly, four super-tiles deep, gathered into chunk-major order (16-byte
+//     chunk c of token t at slot 32c + t), so that lanes reading the same dword of consecutive tokens hit
+//     different LDS banks;
+//   - the workgroup dequantizes them once into an fp16 tile of 16-byte chunks (8 coordinates of one token),
+//     chunk (d, token), d = 2 step + half, at slot 32 d + token: every wave's up-projection operand is one
+//     contiguous 1 KiB read per step; the
 //     next super-tile is dequantized (into a second tile) while the matrix cores run this one's
 //     up-projection;
 //   - each wave: K_pre (its 32 dims x 32 tokens, 32 MFMAs), RoPE, partial scores over its dims for the
@@ -192,18 +193,19 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     uint8_t* dst = smem + LY.raw + (k & 3) * LY.raw_bytes;
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {  // codes: 8 KiB, 512 chunks of 16 bytes
-      const int base = 16 * (256 * r + 64 * wv);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + base), 16,
-                                               16 * lane, base, 0, 0);
+    for (int r = 0; r < 2; ++r) {  // codes: 8 KiB, 512 chunks; slot p = 32c + t <- token t's chunk c
+      const int p0 = 256 * r + 64 * wv, p = p0 + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 16 * p0), 16,
+                                               (p & 31) * (SLAT / 2) + 16 * (p >> 5), 0, 0, 0);
       ++cnt;
     }
-    const int pbytes = 32 * mpt;
-    const int pbase = 16 * 64 * wv;
-    if (pbase < pbytes) {  // wave-uniform
-      if (pbase + 16 * lane < pbytes)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + LY.pairs_off + pbase),
-                                                 16, 16 * lane, pairs_at + pbase, 0, 0);
+    const int pchunks = 2 * mpt;  // pairs: mpt / 16 chunks per token, slot 32c + t as above
+    const int p0 = 64 * wv;
+    if (p0 < pchunks) {  // wave-uniform
+      const int p = p0 + lane;
+      if (p < pchunks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + LY.pairs_off + 16 * p0),
+                                                 16, pairs_at + (p & 31) * mpt + 16 * (p >> 5), 0, 0, 0);
       ++cnt;
     }
     return cnt;
@@ -220,22 +222,24 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   }
   bool fresh = true;
 
-  // super-tile k's sources of the dequantization: item i of this thread is chunk d = tid % 64 (coordinates
-  // 8d..8d+7) of token tid / 64 + 4i, so that a wave reads one token's 256 contiguous code bytes; then its fp16
-  // tile, and its rotated query q~ = R(q_pos - t0) q
-  const int dq_d = tid & 63, dq_t0 = tid >> 6;
-  auto chunk = [](int d, int tok) { return (32 * d + (tok ^ (d & 15))) * 16; };  // byte offset in a tile
+  // super-tile k's sources of the dequantization: item i of this thread is chunk d = 2s + hf (coordinates 8d..8d+7)
+  // of token tid % 32, s = tid / 64 + 4i, hf = (tid / 32) % 2; code dword d of token t sits in raw slot
+  // 32 (d / 4) + t at word d % 4, pair g in pair slot 32 (g / 4) + t at word g % 4.  Then its fp16 tile, and its
+  // rotated query q~ = R(q_pos - t0) q.
+  const int dq_t = tid & 31, dq_d0 = 2 * (tid >> 6) + ((tid >> 5) & 1);  // d = dq_d0 + 8i
+  const int lg = __builtin_ctz(a.G);                                      // G is a power of two (32 .. 512)
   auto dq_load = [&](int k, uint32_t (&xs)[8], uint32_t (&szs)[8]) {
     const uint8_t* raw = smem + LY.raw + (k & 3) * LY.raw_bytes;
+    const uint8_t* xb = raw + ((dq_d0 >> 2) * 32 + dq_t) * 16 + (dq_d0 & 3) * 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int tok = dq_t0 + 4 * i;
-      xs[i] = *(const uint32_t*)(raw + tok * (SLAT / 2) + 4 * dq_d);
-      szs[i] = *(const uint32_t*)(raw + LY.pairs_off + tok * mpt + 4 * ((8 * dq_d) / a.G));
+      xs[i] = *(const uint32_t*)(xb + 1024 * i);  // d + 8 -> chunk + 2
+      const int g = (8 * (dq_d0 + 8 * i)) >> lg;
+      szs[i] = *(const uint32_t*)(raw + LY.pairs_off + ((g >> 2) * 32 + dq_t) * 16 + (g & 3) * 4);
     }
   };
   auto dq_store = [&](int k, int i, uint32_t x, uint32_t sz) {
-    *(h8*)(tiles + (k & 1) * (SKS * 64 * 16) + chunk(dq_d, dq_t0 + 4 * i)) = dequant_int4x8(x, sz);
+    *(h8*)(tiles + (k & 1) * (SKS * 64 * 16) + ((dq_d0 + 8 * i) * 32 + dq_t) * 16) = dequant_int4x8(x, sz);
   };
   auto rot_q = [&](int k) {
     double rev = (double)(qpos - (st_begin + k) * 32) * fq;
@@ -273,7 +277,8 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     f16v_t kp = {};
     {
       // step s: chunk (2s + hf, t)
-      auto bsrc = [&](int s) { return *(const h8*)(tile + chunk(2 * s + hf, t)); };
+      const uint8_t* bb = tile + (32 * hf + t) * 16;
+      auto bsrc = [&](int s) { return *(const h8*)(bb + 1024 * s); };
       constexpr int PF = 8;
       h8 bq[PF];
 #pragma unroll
@@ -357,13 +362,11 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // 16s + 8(n/8) + perm8(n%8), read token-major from the fp16 tile (4 columns of one token per lane pointer)
     {
       // step s = 8w + nt: lane rho points at the 4 columns 4(q4 % 2).. of chunk (2s + q4 / 2, 8g + 4v + rho / 4)
-      const int q4 = rho & 3, tk = 8 * grp + (rho >> 2);
+      const int q4 = rho & 3;
+      const uint8_t* vb = tile + ((16 * wv + (q4 >> 1)) * 32 + 8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
       h8 vt[8];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int d = 2 * (8 * wv + nt) + (q4 >> 1);
-        vt[nt] = lds_tr8s(tile + chunk(d, tk) + (q4 & 1) * 8, tile + chunk(d, tk + 4) + (q4 & 1) * 8);
-      }
+      for (int nt = 0; nt < 8; ++nt) vt[nt] = lds_tr8s(vb + 1024 * nt, vb + 1024 * nt + 64);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[nt] = mfma16x16x32(pop, vt[nt], acc[nt]);
@@ -434,7 +437,7 @@ int shared_max_tiles_per_split() { return SMAX_TILES; }
 
 bool shared_supported(const kvc_layout& L) {
   return L.shared && L.head_dim == SD && L.r_k_cap == SLAT && L.n_q_heads == SGQ * L.n_kv_heads &&
-         L.latent_bits == 4 && L.group % 32 == 0 && L.group <= SLAT && SLAT % L.group == 0;
+         L.latent_bits == 4 && L.group >= 32 && L.group <= SLAT && (L.group & (L.group - 1)) == 0;
 }
 
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {
