@@ -399,38 +399,46 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   }
 }
 
-// out[l][b][h*4 + hq] = W_v[l][:, h*128 : (h+1)*128]^T c* / l*, over the splits' partials.
-__global__ __launch_bounds__(256) void merge_shared_kernel(const float* ws, const uint16_t* wv, float* out, int B,
-                                                           int Hkv, int Hq, int n_splits, int part_stride) {
-  __shared__ float cst[SGQ][SLAT];
-  __shared__ float lst[SGQ];
+// out[l][b][h*4 + hq] = W_v[l][:, h*128 : (h+1)*128]^T c* / l*, over the splits' partials: one workgroup per
+// (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the threads,
+// eight independent partial sums).
+__global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, float* out, int B,
+                                                          int Hkv, int Hq, int n_splits, int part_stride) {
+  __shared__ float cst[SLAT];
+  __shared__ float lst;
   int id = blockIdx.x;
-  const int b = id % B; id /= B;
-  const int h = id % Hkv;
-  const int l = id / Hkv;
-  const int tid = threadIdx.x, hq = tid / 64, t64 = tid % 64;
+  const int hq_all = id % Hq; id /= Hq;
+  const int b = id % B;
+  const int l = id / B;
+  const int h = hq_all / SGQ, hq = hq_all % SGQ;
+  const int d = threadIdx.x;
   const float* parts = ws + (((size_t)l * Hkv + h) * B + b) * n_splits * part_stride;
   float m = -INFINITY;
   for (int p = 0; p < n_splits; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
-  float lsum = 0.0f, c[SLAT / 64];
-  for (int k = 0; k < SLAT / 64; ++k) c[k] = 0.0f;
+  float lsum = 0.0f, c[SLAT / SD];
+#pragma unroll
+  for (int k = 0; k < SLAT / SD; ++k) c[k] = 0.0f;
   for (int p = 0; p < n_splits; ++p) {
     const float* pp = parts + (size_t)p * part_stride;
-    if (pp[hq] == -INFINITY) continue;
-    const float w = exp2f(pp[hq] - m);
+    const float mp = pp[hq];
+    const float w = mp == -INFINITY ? 0.0f : exp2f(mp - m);
     lsum += w * pp[SGQ + hq];
-    for (int k = 0; k < SLAT / 64; ++k) c[k] += w * pp[2 * SGQ + hq * SLAT + t64 + 64 * k];
+#pragma unroll
+    for (int k = 0; k < SLAT / SD; ++k) c[k] += w * pp[2 * SGQ + hq * SLAT + d + SD * k];
   }
-  for (int k = 0; k < SLAT / 64; ++k) cst[hq][t64 + 64 * k] = c[k];
-  if (t64 == 0) lst[hq] = lsum;
+#pragma unroll
+  for (int k = 0; k < SLAT / SD; ++k) cst[d + SD * k] = c[k];
+  if (d == 0) lst = lsum;
   __syncthreads();
-  const uint16_t* W = wv + (size_t)l * SLAT * Hkv * SD + (size_t)h * SD;
-  const float inv = 1.0f / lst[hq];
-  for (int d = t64; d < SD; d += 64) {
-    float o = 0.0f;
-    for (int i = 0; i < SLAT; ++i) o += __builtin_bit_cast(float, (uint32_t)W[(size_t)i * Hkv * SD + d] << 16) * cst[hq][i];
-    out[(((size_t)l * B + b) * Hq + h * SGQ + hq) * SD + d] = o * inv;
+  const size_t width = (size_t)Hkv * SD;
+  const uint16_t* W = wv + (size_t)l * SLAT * width + (size_t)h * SD + d;
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < SLAT; i += 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __builtin_bit_cast(float, (uint32_t)W[(size_t)(i + e) * width] << 16) * cst[i + e];
   }
+  const float sum = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+  out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = sum / lst;
 }
 
 int shared_max_tiles_per_split() { return SMAX_TILES; }
@@ -462,7 +470,7 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * L.n_kv_heads * in.B), dim3(256), 0, st, a.ws, in.wv, out,
+  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv, out,
                      in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride);
   return hipGetLastError();
 }
