@@ -6,24 +6,24 @@
 // the path (512 -> 128 per token, layer and head), so the kernel is laid out for the matrix cores.
 //
 // One workgroup (4 waves, one workgroup per CU so that each wave has the full register file) per
-// (layer, KV head, sequence, context split).  Wave w
-// owns 32 of the head's 128 dims, {16w..16w+15} and {64+16w..64+16w+15}, so that its RoPE pairs
-// (j, j + 64) meet in one lane, and holds W_k's 512 x 32 slice for them as v_mfma_f32_32x32x16_f16
-// A fragments in registers.  The workgroup walks 32-token super-tiles:
-//   - the super-tile's codes and scale/zero pairs (contiguous in the page record) go HBM -> LDS with
-//     buffer loads that write LDS directly, four super-tiles deep, gathered into chunk-major order (16-byte
-//     chunk c of token t at slot 32c + t), so that lanes reading the same dword of consecutive tokens hit
-//     different LDS banks;
-//   - the workgroup dequantizes them once into an fp16 tile of 16-byte chunks (8 coordinates of one token),
-//     chunk (d, token), d = 2 step + half, at slot 32 d + token: every wave's up-projection operand is one
-//     contiguous 1 KiB read per step; the
-//     next super-tile is dequantized (into a second tile) while the matrix cores run this one's
-//     up-projection;
-//   - each wave: K_pre (its 32 dims x 32 tokens, 32 MFMAs), RoPE, partial scores over its dims for the
-//     four query heads; the partials are summed through LDS;
-//   - every wave repeats the (identical) online softmax and accumulates the value latent on its 128
-//     coordinates with v_mfma_f32_16x16x32_f16, whose token-major operands come from the same fp16 tile
-//     through transposing LDS reads.
+// (layer, KV head, sequence, context split).  The latent is split among the waves, not the head dims:
+// wave w owns latent coordinates 128w..128w+127 and holds W_k's 128 x 128 slice for them (all head dims)
+// as v_mfma_f32_32x32x16_f16 A fragments in registers.  RoPE and the scores are linear in the key, so
+// each wave up-projects, rotates and scores its partial key; the four partial scores are summed through
+// LDS, the one exchange (and the one barrier) per 32-token super-tile.  The value latent is accumulated
+// on the same 128 coordinates, so everything else a wave touches is its own:
+//   - its quarter of each super-tile's codes (64 bytes per token) and its scale/zero pairs go HBM -> LDS
+//     through its own four-deep ring of buffer loads that write LDS directly, gathered chunk-major
+//     (16-byte chunk c of token t at slot 32c + t, so that lanes of consecutive tokens hit different banks);
+//     each wave counts and waits for its own copies only;
+//   - it dequantizes its codes once, straight into the up-projection's B fragments (lane = token, k-slots =
+//     8 coordinates of one code dword), one super-tile ahead, and stores the same fp16 chunks in a private
+//     LDS tile for the value product;
+//   - per super-tile: 32 up-projection MFMAs (4 blocks of 32 head dims x 8 steps), RoPE on the pairs
+//     (j, j + 64), which sit in one lane, 8 score MFMAs into the partial scores; after the exchange every
+//     wave repeats the (identical) online softmax and accumulates its 128 value coordinates with
+//     v_mfma_f32_16x16x32_f16, whose token-major operands come from the private tile through transposing
+//     LDS reads.
 // The value up-projection W_v is applied once per (layer, sequence, head) in the merge kernel.
 #include <math.h>
 
@@ -33,11 +33,15 @@
 
 namespace kvc {
 
-static constexpr int SGQ = 4;     // query heads per KV head
-static constexpr int SLAT = 512;  // latent dimension handled here
-static constexpr int SD = 128;    // head dimension handled here
-static constexpr int SKS = SLAT / 16;  // 16-coordinate steps of the latent
-static constexpr float STAU = 8.0f;    // lazy-max slack, log2 units
+static constexpr int SGQ = 4;           // query heads per KV head
+static constexpr int SLAT = 512;        // latent dimension handled here
+static constexpr int SD = 128;          // head dimension handled here
+static constexpr int SQC = SLAT / 4;    // latent coordinates per wave
+static constexpr int SNJ = SQC / 16;    // 16-coordinate steps per wave
+static constexpr int SNB = SD / 32;     // 32-dim blocks of the head
+static constexpr float STAU = 8.0f;     // lazy-max slack, log2 units
+static constexpr int SRAW = 2048 + 512; // ring slot: a wave's codes of 32 tokens, then its pairs (two copies)
+static constexpr int SVT = 16 * 32 * 16; // a wave's fp16 tile: 16 chunks x 32 tokens x 16 bytes
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -57,20 +61,18 @@ struct DecodeSharedArgs {
 static constexpr int SMAX_TILES = 1024;  // super-tiles per split (the page record address of each)
 
 struct SharedLds {
-  int raw, raw_bytes, pairs_off, tile, qt, theta, sp, pt, addr, total;
+  int raw, vt, qt, theta, sp, pt, addr, total;
 };
-__host__ __device__ inline SharedLds shared_lds(int G) {
-  SharedLds L;
+__host__ __device__ constexpr SharedLds shared_lds() {
+  SharedLds L{};
   int o = 0;
-  L.pairs_off = 32 * (SLAT / 2);                                       // codes of 32 tokens, then their pairs
-  L.raw_bytes = (int)pad16(L.pairs_off + 32 * 4 * (SLAT / G));
-  L.raw = o; o += 4 * L.raw_bytes;                                     // staging ring of 4 super-tiles
-  L.tile = o; o += 2 * SKS * 2 * 32 * 16;                              // dequantized latents, 2 x 32 KB
-  L.qt = o; o += 2 * SGQ * SD * 2;                                     // rotated query [head][dim] fp16, x 2
-  L.theta = o; o += (SD / 2) * 8;                                      // RoPE frequencies, turns per position
-  L.sp = o; o += 4 * 32 * SGQ * 4;                                     // partial scores [wave][token][head]
-  L.pt = o; o += 4 * 32 * SGQ * 2;                                     // probabilities [wave][token][head] fp16
-  L.addr = o; o += SMAX_TILES * 8;                                     // page record address of each super-tile
+  L.raw = o; o += 4 * 4 * SRAW;                 // per wave: staging ring of 4 super-tiles
+  L.vt = o; o += 4 * 2 * SVT;                   // per wave: fp16 value tiles, x 2
+  L.qt = o; o += 3 * SGQ * SD * 2;              // rotated query in fragment order, fp16, x 3
+  L.theta = o; o += (SD / 2) * 8;               // RoPE frequencies, turns per position
+  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;          // partial scores [buffer][wave][token][head], x 2
+  L.pt = o; o += 4 * 32 * SGQ * 2;              // probabilities [wave][token][head] fp16
+  L.addr = o; o += SMAX_TILES * 8;              // page record address of each super-tile
   L.total = o;
   return L;
 }
@@ -85,28 +87,58 @@ __device__ inline h8 lds_tr8s(const void* p0, const void* p1) {
   return r;
 }
 
-// s_waitcnt vmcnt(k) for a run-time k (copies of this wave still allowed in flight)
-__device__ inline void vmcnt_wait_s(int k) {
-  switch (k) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-  }
-}
-
 // workgroup barrier for LDS data: the staging copies write LDS directly and every wave waits for its own
-// before this barrier, so the fences only have to keep the compiler from moving LDS accesses across it
+// before it reads them, so the fences only have to keep the compiler from moving LDS accesses across it
 // (a workgroup-scope fence would also wait for the copies still in flight)
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource for the bytes [base, base + n): no stride, raw buffer, the same flags as
+// __builtin_amdgcn_make_buffer_rsrc is given elsewhere.
+__device__ inline i32x4_t buffer_rsrc(const void* base, int n) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4_t{(int)(uint32_t)p, (int)((p >> 32) & 0xFFFFu), n, 0x00020000};
+}
+// One copy instruction HBM -> LDS: lane i's 16 (4) bytes at byte offset voff of the buffer go to LDS byte address
+// lds + 16 i (4 i).  Written as assembly, not as the compiler builtin: the compiler treats every vector-typed LDS
+// read after a builtin copy as possibly aliasing it and waits for all copies in flight (vmcnt(0)), which would
+// empty the staging pipeline each super-tile.  The kernel waits for its own copies (s_waitcnt vmcnt) before it
+// reads them, and the instruction writes no register.
+__device__ inline void copy16_to_lds(i32x4_t rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ inline void copy4_to_lds(i32x4_t rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// fragment order of the rotated query: element e of (head, block g, step st, lane half hf) is head dim
+// 64 (e % 2) + 16 g + 8 st + 4 hf + e / 2, the k-slot order of the rotated keys of block g (each RoPE pair's
+// x and y side by side)
+__device__ inline int qfrag_index(int head, int dim) {
+  const int xy = dim >> 6, r = dim & 63, g = r >> 4, rem = r & 15;
+  const int st = rem >> 3, hf = (rem >> 2) & 1, e = 2 * (rem & 3) + xy;
+  return (((head * SNB + g) * 2 + st) * 2 + hf) * 8 + e;
+}
 
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const SharedLds LY = shared_lds(a.G);
+  constexpr SharedLds LY = shared_lds();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 31, hf = lane >> 5, rho = lane & 15, grp = lane >> 4;
@@ -118,21 +150,31 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   const int T = a.seq_len[b];
   const int qpos = a.q_pos ? a.q_pos[b] : T;
   const int P = a.P;
-  const int mpt = 4 * (SLAT / a.G);  // pair bytes per token
+  const int mpt = 4 * (SLAT / a.G);             // pair bytes per token
+  const int lg = __builtin_ctz(a.G);            // G is a power of two (32 .. 512)
+  const int npw = max(1, SQC >> lg);            // pairs per token over this wave's coordinates (1, 2 or 4)
+  const int g0 = (SQC * wv) >> lg;              // the first of them
 
-  // ---- W_k[l] slice of this wave as A fragments: row r = t <-> head dim r < 16 ? 16w + r : 64 + 16w + r - 16,
-  // k-slot 8hf + j of step s <-> latent coordinate 16s + 8hf + perm8(j) (the order a code dword dequantizes)
-  h8 wf[SKS];
+  // ---- W_k[l] slice of this wave as A fragments.  Block g: row r = t <-> head dim r < 16 ? 16g + r :
+  // 64 + 16g + r - 16; step j: k-slot 8hf + e <-> latent coordinate 128w + 8 (8hf + j) + perm8(e), i.e.
+  // element e of code dword 8hf + j of the wave's 64 code bytes (the order a code dword dequantizes).
+  h8 wf[SNB][SNJ];
   {
-    const int dim = t < 16 ? 16 * wv + t : 64 + 16 * wv + (t - 16);
     const int width = a.Hkv * SD;
-    const uint16_t* W = a.wk + (size_t)l * SLAT * width + (size_t)h * SD + dim;
+    const uint16_t* W = a.wk + (size_t)l * SLAT * width + (size_t)h * SD;
 #pragma unroll
-    for (int s = 0; s < SKS; ++s) {
-      h8 f;
+    for (int g = 0; g < SNB; ++g) {
+      const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = bf16_to_h(W[(size_t)(16 * s + 8 * hf + perm8(j)) * width]);
-      wf[s] = f;
+      for (int j = 0; j < SNJ; ++j) {
+        h8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          f[e] = bf16_to_h(W[(size_t)(SQC * wv + 8 * (8 * hf + j) + perm8(e)) * width + dim]);
+        // the fragments stay in the accumulator registers (the matrix instructions read their A operand from
+        // there directly; the vector registers are needed for the rest)
+        asm volatile("" : "=a"(wf[g][j]) : "0"(f));
+      }
     }
   }
   double* tturn = (double*)(smem + LY.theta);
@@ -153,6 +195,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       qy = q[qj + SD / 2] * sc;
     }
   }
+  const int qix = qfrag_index(qh, qj), qiy = qfrag_index(qh, qj + SD / 2);
   const int n_st = (T + 31) / 32;
   const int st_begin = split * a.st_per_split;
   const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
@@ -164,56 +207,55 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   }
   __syncthreads();
   const double fq = tturn[qj];
-  // RoPE factors of this lane's slot t: up-projection entry i (0..7) is row 8(i/4) + 4hf + i%4 (< 16), paired
-  // with entry i + 8 (that row + 16): frequency 16w + row; |t theta| < 32 turns, where v_sin / v_cos are accurate
-  uint32_t rf[8];
+  // RoPE factors of this lane's slot t: block g's up-projection entry i (0..7) is row 8(i/4) + 4hf + i%4 (< 16),
+  // paired with entry i + 8 (that row + 16): frequency 16g + row; |t theta| < 32 turns, where v_sin / v_cos are
+  // accurate
+  uint32_t rf[SNB][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float rev = (float)(t * tturn[16 * wv + 8 * (i >> 2) + 4 * hf + (i & 3)]);
-    rf[i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-  }
+  for (int g = 0; g < SNB; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
+      rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    }
 
-  uint8_t* tiles = smem + LY.tile;            // tile of super-tile k: tiles + (k & 1) * 32 KiB
-  _Float16* qts = (_Float16*)(smem + LY.qt);  // query of super-tile k: qts + (k & 1) * SGQ * SD
+  uint8_t* raw_w = smem + LY.raw + wv * 4 * SRAW;  // this wave's ring; super-tile k in slot k % 4
+  const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw_w));
+  uint8_t* vt_w = smem + LY.vt + wv * 2 * SVT;     // this wave's fp16 tiles; super-tile k in k % 2
+  _Float16* qts = (_Float16*)(smem + LY.qt);       // rotated query of super-tile k: qts + (k % 3) * SGQ * SD
   float* sp = (float*)(smem + LY.sp);
   _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * SGQ;
 
   const int64_t meta_base = pad16((int64_t)P * SLAT / 2);
 
-  // ---- staging: super-tile k's codes (32 x 256 bytes) and pairs (32 x mpt bytes) into ring slot k % 3.
-  // Returns the number of copy instructions this wave issued.
-  auto issue = [&](int k) -> int {
-    const int slot0 = ((st_begin + k) * 32) % P;
-    // resource based at the super-tile's codes: the codes run 8 KiB from there, its pairs start meta_base - 256 slot0
-    // bytes further (within the same page record)
-    const int64_t at = uniform64(taddr[k]);
+  // ---- staging: this wave's part of super-tile k into ring slot k % 4; past the last super-tile the slot gets a
+  // copy of the last one, which keeps the number of copies in flight constant.  Always four copy instructions:
+  //   codes: 32 tokens x 4 chunks (bytes 64w + 16c .. of each token), slot p = 32c + t <- token t's chunk c;
+  //   pairs: dword 4 t + i <- pair g0 + (i mod npw) of token t, i < 4 (two instructions, 16 tokens each).
+  auto issue = [&](int k) {
+    const int kk = min(k, n_tiles - 1);
+    const int slot0 = ((st_begin + kk) * 32) % P;
+    // resource based at the super-tile's codes: its pairs start meta_base - 256 slot0 bytes further (within the
+    // same page record)
+    const int64_t at = uniform64(taddr[kk]);
     const int pairs_at = (int)meta_base - slot0 * (SLAT / 2) + slot0 * mpt;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.pool + at), (short)0, pairs_at + 32 * mpt, 0x00020000);
-    uint8_t* dst = smem + LY.raw + (k & 3) * LY.raw_bytes;
-    int cnt = 0;
+    const i32x4_t rs = buffer_rsrc(a.pool + at, pairs_at + 32 * mpt);
+    const uint32_t dst = raw_lds + (k & 3) * SRAW;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {  // codes: 8 KiB, 512 chunks; slot p = 32c + t <- token t's chunk c
-      const int p0 = 256 * r + 64 * wv, p = p0 + lane;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 16 * p0), 16,
-                                               (p & 31) * (SLAT / 2) + 16 * (p >> 5), 0, 0, 0);
-      ++cnt;
+    for (int r = 0; r < 2; ++r) {
+      const int p = 64 * r + lane;
+      copy16_to_lds(rs, dst + 1024 * r, (p & 31) * (SLAT / 2) + 64 * wv + 16 * (p >> 5));
     }
-    const int pchunks = 2 * mpt;  // pairs: mpt / 16 chunks per token, slot 32c + t as above
-    const int p0 = 64 * wv;
-    if (p0 < pchunks) {  // wave-uniform
-      const int p = p0 + lane;
-      if (p < pchunks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + LY.pairs_off + 16 * p0),
-                                                 16, pairs_at + (p & 31) * mpt + 16 * (p >> 5), 0, 0, 0);
-      ++cnt;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int q = 64 * r + lane, tok = q >> 2, i = q & 3;
+      copy4_to_lds(rs, dst + 2048 + 256 * r, pairs_at + tok * mpt + 4 * (g0 + (i & (npw - 1))));
     }
-    return cnt;
   };
 
-  f4 acc[8];  // value latent on coordinates of steps 8w..8w+7 (16 each), rows = query heads (replicated)
+  f4 acc[SNJ];  // value latent on this wave's coordinates, 16 per step, rows = query heads (replicated)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f4{0, 0, 0, 0};
+  for (int i = 0; i < SNJ; ++i) acc[i] = f4{0, 0, 0, 0};
   float m_ref[SGQ], psum[SGQ];
 #pragma unroll
   for (int i = 0; i < SGQ; ++i) {
@@ -221,107 +263,101 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     psum[i] = 0.0f;
   }
   bool fresh = true;
-
-  // super-tile k's sources of the dequantization: item i of this thread is chunk d = 2s + hf (coordinates 8d..8d+7)
-  // of token tid % 32, s = tid / 64 + 4i, hf = (tid / 32) % 2; code dword d of token t sits in raw slot
-  // 32 (d / 4) + t at word d % 4, pair g in pair slot 32 (g / 4) + t at word g % 4.  Then its fp16 tile, and its
-  // rotated query q~ = R(q_pos - t0) q.
-  const int dq_t = tid & 31, dq_d0 = 2 * (tid >> 6) + ((tid >> 5) & 1);  // d = dq_d0 + 8i
-  const int lg = __builtin_ctz(a.G);                                      // G is a power of two (32 .. 512)
-  auto dq_load = [&](int k, uint32_t (&xs)[8], uint32_t (&szs)[8]) {
-    const uint8_t* raw = smem + LY.raw + (k & 3) * LY.raw_bytes;
-    const uint8_t* xb = raw + ((dq_d0 >> 2) * 32 + dq_t) * 16 + (dq_d0 & 3) * 4;
+  // ---- super-tile k (ring slot k % 4) dequantized into the B fragments bf (lane = token t, step j: code dword
+  // 8hf + j of the wave's part, the k-slot order of wf) and into fp16 tile vb: chunk c (code dword c, 8
+  // coordinates) of token t at slot 32c + t
+  const int gr0 = ((SQC * wv + 64 * hf) >> lg) - g0, gr1 = ((SQC * wv + 64 * hf + 32) >> lg) - g0;
+  auto dequant = [&](int k, h8 (&bf)[SNJ], int vb) {
+    const uint8_t* raw = raw_w + (k & 3) * SRAW;
+    // (dword reads: the compiler merges them, and unlike a vector read of this copy target it then adds no wait
+    // for every copy in flight)
+    const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);       // chunk 2hf: dwords 8hf + 0..3
+    const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
+    const uint32_t z0 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr0));
+    const uint32_t z1 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr1));
+    uint8_t* dst = vt_w + vb * SVT + (256 * hf + t) * 16;
+    const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xs[i] = *(const uint32_t*)(xb + 1024 * i);  // d + 8 -> chunk + 2
-      const int g = (8 * (dq_d0 + 8 * i)) >> lg;
-      szs[i] = *(const uint32_t*)(raw + LY.pairs_off + ((g >> 2) * 32 + dq_t) * 16 + (g & 3) * 4);
+    for (int j = 0; j < SNJ; ++j) {
+      bf[j] = dequant_int4x8(xs[j], j < 4 ? z0 : z1);
+      *(h8*)(dst + 512 * j) = bf[j];
     }
   };
-  auto dq_store = [&](int k, int i, uint32_t x, uint32_t sz) {
-    *(h8*)(tiles + (k & 1) * (SKS * 64 * 16) + ((dq_d0 + 8 * i) * 32 + dq_t) * 16) = dequant_int4x8(x, sz);
-  };
+  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order
   auto rot_q = [&](int k) {
     double rev = (double)(qpos - (st_begin + k) * 32) * fq;
     rev -= rint(rev);
     const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-    _Float16* qt = qts + (k & 1) * SGQ * SD;
-    qt[qh * SD + qj] = (_Float16)(qx * cs - qy * sn);
-    qt[qh * SD + qj + SD / 2] = (_Float16)(qy * cs + qx * sn);
+    _Float16* qt = qts + (k % 3) * SGQ * SD;
+    qt[qix] = (_Float16)(qx * cs - qy * sn);
+    qt[qiy] = (_Float16)(qy * cs + qx * sn);
   };
 
-  // prologue: super-tiles 0-2 in flight, wait for 0 and 1, dequantize 0
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) issue(1);
-  const int c2 = n_tiles > 2 ? issue(2) : 0;
-  vmcnt_wait_s(c2);
-  lds_barrier();
-  if (n_tiles > 0) {
-    uint32_t xs[8], szs[8];
-    dq_load(0, xs, szs);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dq_store(0, i, xs[i], szs[i]);
-    rot_q(0);
-  }
-  lds_barrier();
-  for (int k = 0; k < n_tiles; ++k) {
-    // ring slot (k + 3) % 4 held super-tile k - 1, dequantized two iterations ago
-    const int c_new = (k + 3 < n_tiles) ? issue(k + 3) : 0;
+  // One super-tile: bc holds its B fragments (its fp16 tile is buffer k % 2); the next super-tile is dequantized
+  // into bn on the way.
+  auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ]) {
+    issue(k + 4);  // ring slot k % 4 held super-tile k, dequantized in the previous step
     const int t0 = (st_begin + k) * 32;
-    const uint8_t* tile = tiles + (k & 1) * (SKS * 64 * 16);
-    const _Float16* qt = qts + (k & 1) * SGQ * SD;
+    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each) may still be in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    // sources of super-tile k + 1's dequantization (dword reads: see dequant)
+    const uint8_t* rawn = raw_w + ((k + 1) & 3) * SRAW;
+    const uint32_t* c0 = (const uint32_t*)(rawn + (64 * hf + t) * 16);
+    const uint32_t* c1 = (const uint32_t*)(rawn + (64 * hf + 32 + t) * 16);
+    const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const uint32_t z0 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr0));
+    const uint32_t z1 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr1));
+    uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + (256 * hf + t) * 16;
 
-    // ---- key up-projection of this wave's 32 dims for super-tile k, operands read 8 steps ahead, with the
-    // dequantization of super-tile k + 1 (landed, and its tile free since the last barrier) in between; past the
-    // last super-tile that work reads a stale ring slot into the unused tile
-    f16v_t kp = {};
-    {
-      // step s: chunk (2s + hf, t)
-      const uint8_t* bb = tile + (32 * hf + t) * 16;
-      auto bsrc = [&](int s) { return *(const h8*)(bb + 1024 * s); };
-      constexpr int PF = 8;
-      h8 bq[PF];
+    // ---- partial keys over this wave's coordinates (block by block), RoPE, partial scores of the four heads.
+    // The instruction stream interleaves each block's matrix instructions with vector work that does not wait
+    // for them (two chunks of the next super-tile's dequantization, the previous block's RoPE), so that one
+    // wave keeps both units busy.
+    const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SD) + (t & 3) * (SNB * 4) + hf;
+    f16v_t sc = {};
+    f16v_t kp[SNB];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) bq[i] = bsrc(i);
-      uint32_t xs[8], szs[8];
-      dq_load(k + 1, xs, szs);
-      // scheduling fences keep each read PF steps ahead of its product and the dequantization spread over
-      // the matrix instructions (the scheduler would otherwise sink the reads next to their uses)
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g <= SNB; ++g) {
+      if (g < SNB) {
+        kp[g] = f16v_t{};
 #pragma unroll
-      for (int s = 0; s < SKS; ++s) {
-        kp = mfma32s(wf[s], bq[s % PF], kp);
-        if (s + PF < SKS) bq[s % PF] = bsrc(s + PF);
-        if ((s & 3) == 3) dq_store(k + 1, s >> 2, xs[s >> 2], szs[s >> 2]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
+#pragma unroll
+        for (int jj = 2 * g; jj < 2 * g + 2; ++jj) {
+          bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
+          *(h8*)(vdst + 512 * jj) = bn[jj];
+        }
       }
-      rot_q(k + 1);
-    }
-    h8 kq0, kq1;  // score steps: k-slot 8hf + j <-> pair 8(j/4) + 4hf + j%4 of the wave, x (step 0) and y (step 1)
+      if (g > 0) {
+        // rotated pairs (x, y) of rows 8st + 4hf + m, m < 4, are the k-slots 8hf + 2m, 2m + 1 of score step st
+        u32x4_t kr[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const h2 r = as_h2(rope_pair(pack_h2(kp[i], kp[i + 8]), rf[i]));
-      kq0[i] = r.x;
-      kq1[i] = r.y;
+        for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rf[g - 1][i]);
+        sc = mfma32s(qf[4 * (g - 1)], __builtin_bit_cast(h8, kr[0]), sc);
+        sc = mfma32s(qf[4 * (g - 1) + 2], __builtin_bit_cast(h8, kr[1]), sc);
+      }
     }
-    const _Float16* qrow = qt + (t & 3) * SD + 16 * wv + 4 * hf;
-    h8 qf0, qf1;
-    {
-      const h4 a0 = *(const h4*)qrow, a1 = *(const h4*)(qrow + 8);
-      const h4 b0 = *(const h4*)(qrow + SD / 2), b1 = *(const h4*)(qrow + SD / 2 + 8);
-      qf0 = h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf1 = h8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+    for (int g = 0; g < SNB; ++g) {
+#pragma unroll
+      for (int j = 0; j < SNJ; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five vector instructions
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the previous block's score products
     }
-    const f16v_t sc = mfma32s(qf1, kq1, mfma32s(qf0, kq0, f16v_t{}));
-    if (hf == 0) *(f4*)(sp + (wv * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
+    float* spb = sp + (k & 1) * (4 * 32 * SGQ);
+    if (hf == 0) *(f4*)(spb + (wv * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
     lds_barrier();
+    rot_q(k + 2);  // buffer (k + 2) % 3 was last read before the previous barrier
 
     // ---- scores of the four heads for token t (the same in every wave), lazy online softmax
     float s4[SGQ];
     {
-      f4 tot = *(const f4*)(sp + t * SGQ);
+      f4 tot = *(const f4*)(spb + t * SGQ);
 #pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(sp + (w2 * 32 + t) * SGQ);
+      for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) s4[i] = (t0 + t < T) ? tot[i] - m_ref[i] : -INFINITY;
     }
@@ -340,7 +376,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         m_ref[i] += d;
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < SNJ; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha[i];
       fresh = false;
@@ -352,28 +388,41 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       psum[i] += p[i];
     }
     if (hf == 0) *(h4*)(pt + SGQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    wave_lds_sync();
     // P as the A operand of the 16x16x32 value product: row l % 16 <-> head l % 4, k-slot 8g + j <-> token 8g + j
     // (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
     const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
-    // value latent on this wave's coordinates: step s = 8w + nt covers 16 coordinates; column n <-> coordinate
-    // 16s + 8(n/8) + perm8(n%8), read token-major from the fp16 tile (4 columns of one token per lane pointer)
+    // value latent: step nt covers chunks 2nt, 2nt + 1; column n <-> coordinate 128w + 16nt + 8(n/8) + perm8(n%8);
+    // lane rho points at the 4 columns 4(q4 % 2).. of chunk (2nt + q4 / 2, token 8g + 4v + rho / 4)
     {
-      // step s = 8w + nt: lane rho points at the 4 columns 4(q4 % 2).. of chunk (2s + q4 / 2, 8g + 4v + rho / 4)
       const int q4 = rho & 3;
-      const uint8_t* vb = tile + ((16 * wv + (q4 >> 1)) * 32 + 8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
-      h8 vt[8];
+      const uint8_t* vb = vt_w + (k & 1) * SVT + ((q4 >> 1) * 32 + 8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
+      h8 vt[SNJ];
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) vt[nt] = lds_tr8s(vb + 1024 * nt, vb + 1024 * nt + 64);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < SNJ; ++nt) vt[nt] = lds_tr8s(vb + 1024 * nt, vb + 1024 * nt + 64);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[nt] = mfma16x16x32(pop, vt[nt], acc[nt]);
+      for (int nt = 0; nt < SNJ; ++nt) acc[nt] = mfma16x16x32(pop, vt[nt], acc[nt]);
     }
-    // super-tile k + 2 landed (k + 3 may be in flight), and everyone is done with tile k before it is rewritten
-    vmcnt_wait_s(c_new);
+  };
+
+  if (n_tiles > 0) {
+    // prologue: super-tiles 0-3 in flight, wait for 0, dequantize it; rotated queries of 0 and 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue(j);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    h8 ba[SNJ], bb[SNJ];
+    dequant(0, ba, 0);
+    rot_q(0);
+    rot_q(1);
     lds_barrier();
+    int k = 0;
+    for (; k + 1 < n_tiles; k += 2) {
+      step(k, ba, bb);
+      step(k + 1, bb, ba);
+    }
+    if (k < n_tiles) step(k, ba, bb);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies past the end land before the workgroup exits
   }
 
   // ---- partial: m[4], l[4] (the same in every wave), acc[4][512] (wave w: coordinates 128w..128w+127)
@@ -391,8 +440,8 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   }
   if (grp == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int coord = 16 * (8 * wv + nt) + 8 * (rho >> 3) + perm8(rho & 7);
+    for (int nt = 0; nt < SNJ; ++nt) {
+      const int coord = SQC * wv + 16 * nt + 8 * (rho >> 3) + perm8(rho & 7);
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[2 * SGQ + i * SLAT + coord] = acc[nt][i];
     }
@@ -460,7 +509,7 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.L = L.n_layers; a.max_blocks = in.max_blocks;
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
-  const int lds = shared_lds(L.group).total;
+  const int lds = shared_lds().total;
   hipError_t e = hipFuncSetAttribute((const void*)decode_shared_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
