@@ -138,7 +138,7 @@ def other_workloads(steps: int, warmup: int) -> dict:
         nbytes = acct["stream"] + acct["tables"]
         flops = decode_flops(w)
         path = {kvc.PATH_HEAD: "general per-head kernel", kvc.PATH_INT4: "INT4 kernel",
-                kvc.PATH_SHARED: "block-shared kernel"}[kvc.decode_path(L)]
+                kvc.PATH_SHARED: "block-shared kernel", kvc.PATH_RES: "INT4 residual kernel"}[kvc.decode_path(L)]
         r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),
              "compressed_bytes": nbytes, "hbm_gbs": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
              "flops": flops, "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1)}

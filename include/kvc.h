@@ -218,10 +218,12 @@ kvc_status kvc_decode_attn_timed(const kvc_layout* layout, const kvc_cache* cach
                                  void* ev_end);
 
 /* Which decode kernel kvc_decode_attn runs for a layout: KVC_PATH_INT4 (per-head INT4 latents,
- * head_dim 128, no residual: the fast kernel), KVC_PATH_HEAD (the general per-head kernel: fp32
- * latents, head_dim 64, rotated residual) or KVC_PATH_SHARED (block-shared latents).  Host-only;
- * returns the layout check's status when the layout is not runnable. */
-enum { KVC_PATH_HEAD = 0, KVC_PATH_INT4 = 1, KVC_PATH_SHARED = 2 };
+ * head_dim 128, no residual: the fast kernel), KVC_PATH_RES (per-head INT4 latents with the 2-bit
+ * rotated residual, head_dim 128, four query heads per KV head, uniform ranks that are multiples of
+ * 16 up to 64), KVC_PATH_HEAD (the general per-head kernel: fp32 latents, head_dim 64, the other
+ * residual layouts) or KVC_PATH_SHARED (block-shared latents).  Host-only; returns the layout
+ * check's status when the layout is not runnable. */
+enum { KVC_PATH_HEAD = 0, KVC_PATH_INT4 = 1, KVC_PATH_SHARED = 2, KVC_PATH_RES = 3 };
 kvc_status kvc_decode_path(const kvc_layout* layout, int32_t* path);
 
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */

@@ -535,6 +535,11 @@ bool int4_supported(const kvc_layout& L, int64_t hb_max);
 hipError_t launch_decode_int4(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
                               int n_splits, int pages_per_split, int part_stride, const HeadSections& S_uniform,
                               int hb_max, hipStream_t st);
+// INT4 latents with the rotated residual (decode_res.hip)
+bool res_supported(const kvc_layout& L, int64_t hb);
+hipError_t launch_decode_res(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
+                             int n_splits, int pages_per_split, int part_stride, const HeadSections& S,
+                             hipStream_t st);
 
 bool head_supported(const kvc_layout& L) {
   if (L.shared) return false;
@@ -550,7 +555,10 @@ bool head_supported(const kvc_layout& L) {
   return true;
 }
 
-int head_decode_path(const kvc_layout& L) { return int4_supported(L, head_block_max(L)) ? KVC_PATH_INT4 : KVC_PATH_HEAD; }
+int head_decode_path(const kvc_layout& L) {
+  const int64_t hb = head_block_max(L);
+  return int4_supported(L, hb) ? KVC_PATH_INT4 : res_supported(L, hb) ? KVC_PATH_RES : KVC_PATH_HEAD;
+}
 
 hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out, void* ws,
                               int n_splits, int pages_per_split, hipStream_t st, bool* unsupported) {
@@ -572,6 +580,8 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
   *unsupported = false;
   if (int4_supported(L, a.hb_max))
     return launch_decode_int4(L, C, in, out, ws, n_splits, pages_per_split, a.part_stride, a.S_uniform, a.hb_max, st);
+  if (res_supported(L, a.hb_max))
+    return launch_decode_res(L, C, in, out, ws, n_splits, pages_per_split, a.part_stride, a.S_uniform, st);
   const int stg = ceil_div(a.hb_max, 16 * 256);
   const int grid = in.B * L.n_kv_heads * n_splits;
   const int KC = ceil_div(L.r_k_cap, 32), VC = ceil_div(L.r_v_cap, 32);

@@ -29,7 +29,7 @@
 
 #include <algorithm>
 
-#include "kvc_common.hpp"
+#include "lds_copy.hpp"
 
 namespace kvc {
 
@@ -78,54 +78,6 @@ __host__ __device__ constexpr SharedLds shared_lds() {
 }
 
 __device__ inline f16v_t mfma32s(h8 a, h8 b, f16v_t c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
-
-__device__ inline h8 lds_tr8s(const void* p0, const void* p1) {
-  typedef short s4_t __attribute__((ext_vector_type(4)));
-  const h4 x = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)p0));
-  const h4 y = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)p1));
-  h8 r = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  return r;
-}
-
-// workgroup barrier for LDS data: the staging copies write LDS directly and every wave waits for its own
-// before it reads them, so the fences only have to keep the compiler from moving LDS accesses across it
-// (a workgroup-scope fence would also wait for the copies still in flight)
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer resource for the bytes [base, base + n): no stride, raw buffer, the same flags as
-// __builtin_amdgcn_make_buffer_rsrc is given elsewhere.
-__device__ inline i32x4_t buffer_rsrc(const void* base, int n) {
-  const uint64_t p = (uint64_t)base;
-  return i32x4_t{(int)(uint32_t)p, (int)((p >> 32) & 0xFFFFu), n, 0x00020000};
-}
-// One copy instruction HBM -> LDS: lane i's 16 (4) bytes at byte offset voff of the buffer go to LDS byte address
-// lds + 16 i (4 i).  Written as assembly, not as the compiler builtin: the compiler treats every vector-typed LDS
-// read after a builtin copy as possibly aliasing it and waits for all copies in flight (vmcnt(0)), which would
-// empty the staging pipeline each super-tile.  The kernel waits for its own copies (s_waitcnt vmcnt) before it
-// reads them, and the instruction writes no register.
-__device__ inline void copy16_to_lds(i32x4_t rsrc, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-__device__ inline void copy4_to_lds(i32x4_t rsrc, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-__device__ inline uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // fragment order of the rotated query: element e of (head, block g, step st, lane half hf) is head dim
 // 64 (e % 2) + 16 g + 8 st + 4 hf + e / 2, the k-slot order of the rotated keys of block g (each RoPE pair's

@@ -170,11 +170,11 @@ def compress(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, ra
     _check(lib().kvc_compress(C.byref(layout), C.byref(inp), C.byref(c), _stream()), "kvc_compress")
 
 
-PATH_HEAD, PATH_INT4, PATH_SHARED = 0, 1, 2
+PATH_HEAD, PATH_INT4, PATH_SHARED, PATH_RES = 0, 1, 2, 3
 
 
 def decode_path(layout: Layout) -> int:
-    """Which decode kernel serves the layout (PATH_INT4, PATH_HEAD or PATH_SHARED)."""
+    """Which decode kernel serves the layout (PATH_INT4, PATH_RES, PATH_HEAD or PATH_SHARED)."""
     out = C.c_int32()
     _check(lib().kvc_decode_path(C.byref(layout), C.byref(out)), "kvc_decode_path")
     return out.value

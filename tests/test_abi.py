@@ -69,9 +69,10 @@ def test_calls_reject_bad_arguments_without_launching():
 
 def test_decode_path_selection():
     """The INT4 fast kernel serves every INT4, head-dim-128, residual-free per-head layout of the workloads
-    (and their scaled test copies); the others go to the general per-head or the block-shared kernel."""
+    (and their scaled test copies), the INT4 residual kernel the residual workload; the others go to the
+    general per-head or the block-shared kernel."""
     want = {"tiny": kvc.PATH_HEAD, "llama8b_layer_8k": kvc.PATH_INT4, "varrank_paged_32k": kvc.PATH_INT4,
-            "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_HEAD}
+            "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)

@@ -20,6 +20,9 @@ CASES = [
     ("varrank_paged_32k", dict(B=3, T=2000), [2000, 1999, 33]),
     ("varrank_paged_32k", dict(B=2, T=300, page_size=32), [300, 17]),
     ("residual_128k", dict(B=2, T=700), [700, 512]),
+    ("residual_128k", dict(B=3, T=1500, page_size=64), [1500, 1025, 31]),
+    # ranks that are not multiples of 16: the general per-head kernel's residual path
+    ("residual_128k", dict(B=2, T=700, r_k=40, r_v=56), [700, 300]),
     ("shared_latent_32k", dict(B=2, T=600), [600, 33]),
     ("shared_latent_32k", dict(B=1, T=300, n_layers=2, page_size=64), None),
 ]
