@@ -12,16 +12,18 @@
 // buffers deep (the next page in flight while this one is decoded).  Wave w decodes the 32-token super-tiles
 // w and w + 4 of every page and keeps its own online-softmax state; lane l serves token l % 32, its half l / 32
 // supplies eight of the sixteen k-slots of each matrix step.  Per super-tile:
-//   keys: latent codes -> fp16 (fp8-conversion trick, one fp16 FMA for scale and zero); residual codes ->
-//     fp16 (2c - 3) s / (2 sqrt(128)); K_pre = B_k c + H' e' on v_mfma_f32_32x32x16_f16 with H' the +-1
-//     Hadamard, whose fragments for every (head-dim tile, step) are +-A0 or +-A0 with its upper 16 rows
-//     negated (a compile-time choice, so four fragments serve all 32 products); RoPE on the pairs (j, j + 64)
-//     (tiles m and m + 2: one lane, one accumulator entry); scores S = Q~ K~^T with the query heads
-//     replicated over the 32 rows;
-//   values: latent and residual chunks dequantized into per-wave fp16 tiles in LDS, read back token-major
-//     with ds_read_b64_tr_b16 as the B operand of v_mfma_f32_16x16x32_f16 (A = the probabilities, also
-//     transposed through LDS); the value latent and the rotated value residual accumulate in registers, and
-//     B_v and H are applied once per (b, query head) in the merge (sum_t p_t B c_t = B sum_t p_t c_t).
+//   keys: latent codes -> fp16 (fp8-conversion trick, one fp16 FMA for scale and zero); residual codes c ->
+//     exact fp16 2c - 3 (bit operations only: each pair of a code dword's codes k, k + 8 lands in the mantissa
+//     of 1024 in one shift and one and-or), times S = s / (2 sqrt(128)); K_pre = B_k c + H' e' on
+//     v_mfma_f32_32x32x16_f16 with H' the +-1 Hadamard, whose fragments for every (head-dim tile, step) are
+//     +-A0 or +-A0 with its upper 16 rows negated (a compile-time choice, so four fragments serve all 32
+//     products); RoPE on the pairs (j, j + 64) (tiles m and m + 2: one lane, one accumulator entry); scores
+//     S = Q~ K~^T with the query heads replicated over the 32 rows;
+//   values: latent chunks and residual 2c - 3 (exact) into per-wave fp16 tiles in LDS, read back token-major
+//     with ds_read_b64_tr_b16 as the B operand of v_mfma_f32_16x16x32_f16.  The A operand is the
+//     probabilities for the latent and the probabilities times the token's residual scale S for the residual
+//     (both transposed through LDS).  The value latent and the rotated value residual accumulate in registers,
+//     and B_v and H are applied once per (b, query head) in the merge (sum_t p_t B c_t = B sum_t p_t c_t).
 // RoPE is split as R(t0 + s) = R(t0) R(s): R(s) of the lane's slot s < 32 is held in registers, R(q_pos - t0)
 // is applied to the query per super-tile.  Softmax keeps a reference maximum per head that is only raised
 // when a score exceeds it by 2^8 in the exp2 domain.
@@ -50,8 +52,11 @@ namespace rsd {
 constexpr int D = 128, GQ = 4, NP = 64;
 constexpr int MAX_SPLIT_PAGES = 128;
 constexpr float TAU = 8.0f;                // lazy-max slack, log2 units
-constexpr int VLT = 8 * 32 * 16;          // a wave's value-latent tile: 8 chunks x 32 tokens x 16 bytes
-constexpr int VRT = 16 * 32 * 16;         // a wave's value-residual tile: 16 chunks
+// value tiles: chunk c (8 coordinates) of token t at byte CS c + 16 t; the row of a chunk is padded from 512 to
+// 576 bytes so that the transposing reads of a step (two chunks, token groups 256 bytes apart) hit distinct banks
+constexpr int CS = 32 * 16 + 64;
+constexpr int VLT = 8 * CS;               // a wave's value-latent tile: 8 chunks
+constexpr int VRT = 16 * CS;              // a wave's value-residual tile: 16 chunks
 
 struct Lds {
   int meta_addr, theta, qsrc, qbuf, pt, vlat, vres, stage, stage_bytes, total;
@@ -63,7 +68,7 @@ __host__ __device__ inline Lds lds_layout(int64_t hb) {
   L.theta = o; o += NP * 8;                   // RoPE frequencies, turns per position
   L.qsrc = o; o += NP * 2 * GQ * 4;           // scaled query, pair j: x_j of heads 0-3, then x_{j+64}
   L.qbuf = o; o += 4 * 2 * GQ * (NP + 4) * 4;  // per wave: rotated query of its two super-tiles, packed fp16
-  L.pt = o; o += 4 * 32 * GQ * 2;             // per wave: probabilities [token][head] fp16
+  L.pt = o; o += 2 * 4 * 32 * GQ * 2;         // per wave: probabilities [token][head] fp16, then times S
   L.vlat = o; o += 4 * VLT;
   L.vres = o; o += 4 * VRT;
   L.stage_bytes = (int)pad16(hb);
@@ -92,6 +97,27 @@ __device__ inline void vmcnt_wait_r(int k) {
     default: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
   }
 }
+
+// Eight 2-bit residual codes c of a code dword x (code k at bits 2k) as exact fp16 2c - 3 for lane half hf:
+// element e is code 4hf + e / 2 + 8 (e % 2).  In xs = x >> 8hf, codes 4hf + kk and 4hf + kk + 8 sit at bits 2kk
+// and 2kk + 16; one shift (left by one for kk = 0, right by 2kk - 1 otherwise) and a mask and an or put them
+// into the mantissas of two fp16 1024s (1024 + 2c, exact), and subtracting 1027 leaves 2c - 3.  Bit operations
+// and one packed subtraction per pair: the fp8 and permute conversions issue at about a third of their rate.
+__device__ inline h8 res_2c3(uint32_t x, int hf) {
+  const uint32_t xs = x >> (8 * hf);
+  const h2 off = {(_Float16)1027.0f, (_Float16)1027.0f};
+  h8 r;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t sh = kk == 0 ? xs << 1 : xs >> (2 * kk - 1);
+    const uint32_t y = (sh & 0x00060006u) | 0x64006400u;
+    const h2 v = as_h2(y) - off;
+    r[2 * kk] = v.x;
+    r[2 * kk + 1] = v.y;
+  }
+  return r;
+}
+__device__ inline int res_coord(int hf, int e) { return 4 * hf + (e >> 1) + 8 * (e & 1); }
 
 // Sign of the Hadamard fragment of head-dim tile mt (dims 32 mt + r) and residual step j (coordinates
 // 16 j + il): (-1)^popcount(d & i) splits into (-1)^popcount(r & il & 15) (the fragment A0), (-1)^(r4 j0) (rows
@@ -146,13 +172,13 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
       }
     }
   }
-  // ---- +-1 Hadamard fragments: A0 at row r = t, k-slot 8hf + e <-> coordinate offset 8hf + permr(e) of a
-  // residual step (permr(e) = e / 2 + 4 (e % 2), the order dequant_res2x8 produces); A0 with rows 16-31
-  // negated; and the negatives of both (selected by hsel)
+  // ---- +-1 Hadamard fragments: A0 at row r = t, k-slot 8hf + e <-> coordinate offset res_coord(hf, e) of a
+  // residual step (the order res_2c3 produces); A0 with rows 16-31 negated; and the negatives of both
+  // (selected by hsel)
   h8 hz[4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int il = 8 * hf + (e >> 1) + 4 * (e & 1);
+    const int il = res_coord(hf, e);
     const _Float16 v = (__builtin_popcount(t & il & 15) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
     const _Float16 vf = t >= 16 ? -v : v;
     hz[0][e] = v;
@@ -196,7 +222,8 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
     }
   const double fj = tturn[lane];  // turns per position of pair `lane` (query rotation)
   uint32_t* qbuf = (uint32_t*)(smem + LY.qbuf) + wv * 2 * GQ * (NP + 4);
-  _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * GQ;
+  _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 2 * 32 * GQ;  // then pt2 = pt + 32 GQ
+  _Float16* pt2 = pt + 32 * GQ;
   uint8_t* vlat = smem + LY.vlat + wv * VLT;
   uint8_t* vres = smem + LY.vres + wv * VRT;
   const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.stage));
@@ -239,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
 
   const int kcb = a.rk / 2, vcb = a.rv / 2;                                  // code bytes per slot
   const int kmb = 4 * ceil_div(a.rk, a.G), vmb = 4 * ceil_div(a.rv, a.G);  // pair bytes per slot
-  const float rscale = 0.04419417382415922f;  // 1 / (2 sqrt(128)): (2c - 3) s / (2 sqrt(128)) = e / sqrt(128)
+  const float rscale = 0.04419417382415922f;  // 1 / (2 sqrt(128)): e / sqrt(128) = (2c - 3) s / (2 sqrt(128))
 
   if (n_pages > 0) {
     issue(0);
@@ -270,8 +297,8 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
       const int t0 = page_t0 + 32 * (wv + 4 * k);
       const uint32_t* qrow = qbuf + (k * GQ + (t & 3)) * (NP + 4) + 4 * hf;
 
-      // ---- this lane's words: key and value code dwords (2s + hf) with their pairs, residual codes (32 bytes
-      // per token, chunk 2j + hf = bits 16 hf .. of dword j), residual scales
+      // ---- this lane's words: key and value code dwords (2s + hf) with their pairs, residual code dwords (32
+      // bytes per token; dword j holds the codes of coordinates 16j ..), residual scales
       uint32_t kw[KS], kp[KS], vw[VS], vp[VS], krw[8], vrw[8];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -290,16 +317,15 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
       }
       const float ks = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.ks + 2 * slot)) * rscale;
       const float vs = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.vs + 2 * slot)) * rscale;
-      const h2 kss = {(_Float16)ks, (_Float16)ks}, vss = {(_Float16)vs, (_Float16)vs};
+      const h2 kss = {(_Float16)ks, (_Float16)ks};
 
-      // ---- values into this wave's fp16 tiles (chunk c of token t at slot 32c + t): latent chunks 2s + hf,
-      // residual chunks 2j + hf
+      // ---- values into this wave's fp16 tiles (chunk c of token t at byte CS c + 16 t): latent chunks 2s + hf,
+      // residual 2c - 3 of chunk 2j + hf (coordinates 16j + res_coord(hf, e))
 #pragma unroll
       for (int s = 0; s < VS; ++s)
-        *(h8*)(vlat + (32 * (2 * s + hf) + t) * 16) = dequant_int4x8(vw[s], vp[s]);
+        *(h8*)(vlat + CS * (2 * s + hf) + 16 * t) = dequant_int4x8(vw[s], vp[s]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *(h8*)(vres + (32 * (2 * j + hf) + t) * 16) = dequant_res2x8(hf ? (vrw[j] >> 16) : (vrw[j] & 0xFFFFu), vss);
+      for (int j = 0; j < 8; ++j) *(h8*)(vres + CS * (2 * j + hf) + 16 * t) = res_2c3(vrw[j], hf);
 
       // ---- keys: latent and residual operands, then per half m the tiles m and m + 2 (head dims d, d + 64),
       // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
@@ -307,7 +333,17 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(kw[s], kp[s]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) er[j] = dequant_res2x8(hf ? (krw[j] >> 16) : (krw[j] & 0xFFFFu), kss);
+      for (int j = 0; j < 8; ++j) {
+        const h8 c = res_2c3(krw[j], hf);
+        h8 e;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const h2 v = h2{c[2 * q], c[2 * q + 1]} * kss;
+          e[2 * q] = v.x;
+          e[2 * q + 1] = v.y;
+        }
+        er[j] = e;
+      }
       f16v_r sc = {};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -363,29 +399,36 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
         fresh = false;
       }
       float p[GQ];
+      _Float16 ph[GQ], pv[GQ];
 #pragma unroll
       for (int i = 0; i < GQ; ++i) {
         p[i] = __builtin_amdgcn_exp2f(s4[i]);  // 2^-inf = 0
         psum[i] += p[i];
+        ph[i] = (_Float16)p[i];
+        pv[i] = (_Float16)(p[i] * vs);
       }
-      if (hf == 0) *(h4*)(pt + GQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      if (hf == 0) {
+        *(h4*)(pt + GQ * t) = h4{ph[0], ph[1], ph[2], ph[3]};
+        *(h4*)(pt2 + GQ * t) = h4{pv[0], pv[1], pv[2], pv[3]};
+      }
       wave_lds_sync();
       // P as the A operand of the 16x16x32 value products: row l % 16 <-> head l % 4, k-slot 8g + j <-> token
       // 8g + j (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
       const h8 pop = lds_tr8s(pt + GQ * (8 * grp + (rho >> 2)), pt + GQ * (8 * grp + 4 + (rho >> 2)));
+      const h8 pops = lds_tr8s(pt2 + GQ * (8 * grp + (rho >> 2)), pt2 + GQ * (8 * grp + 4 + (rho >> 2)));
       // value step nt covers chunks 2nt, 2nt + 1; lane rho points at the 4 columns 4(q4 % 2).. of chunk
       // (2nt + q4 / 2, token 8g + 4v + rho / 4)
       const int q4 = rho & 3;
-      const int voff = ((q4 >> 1) * 32 + 8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
+      const int voff = CS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
 #pragma unroll
       for (int nt = 0; nt < VS; ++nt) {
-        const uint8_t* vb = vlat + voff + 1024 * nt;
+        const uint8_t* vb = vlat + voff + 2 * CS * nt;
         acc[nt] = mfma16x16x32(pop, lds_tr8s(vb, vb + 64), acc[nt]);
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const uint8_t* vb = vres + voff + 1024 * nt;
-        accr[nt] = mfma16x16x32(pop, lds_tr8s(vb, vb + 64), accr[nt]);
+        const uint8_t* vb = vres + voff + 2 * CS * nt;
+        accr[nt] = mfma16x16x32(pops, lds_tr8s(vb, vb + 64), accr[nt]);
       }
       wave_lds_sync();  // the tiles and probabilities are rewritten by the next super-tile
     }
@@ -420,9 +463,10 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
     if (VS * 16 < NC)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mine[2 * GQ + i * NC + VS * 16 + rho] = 0.0f;
+    // residual column n of step nt: chunk 2nt + n / 8, element n % 8
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const int coord = 16 * nt + 8 * (rho >> 3) + ((rho & 7) >> 1) + 4 * (rho & 1);
+      const int coord = 16 * nt + res_coord(rho >> 3, rho & 7);
 #pragma unroll
       for (int i = 0; i < 4; ++i) mine[2 * GQ + GQ * NC + i * D + coord] = accr[nt][i];
     }
