@@ -41,7 +41,11 @@ static constexpr int SNJ = SQC / 16;    // 16-coordinate steps per wave
 static constexpr int SNB = SD / 32;     // 32-dim blocks of the head
 static constexpr float STAU = 8.0f;     // lazy-max slack, log2 units
 static constexpr int SRAW = 2048 + 512; // ring slot: a wave's codes of 32 tokens, then its pairs (two copies)
-static constexpr int SVT = 16 * 32 * 16; // a wave's fp16 tile: 16 chunks x 32 tokens x 16 bytes
+// a wave's fp16 tile: chunk c (8 coordinates) of token t at byte SCS c + 16 t, 16 chunks; the row of a chunk is
+// padded from 512 to 576 bytes so that the transposing reads of a step (two chunks, token groups 256 bytes
+// apart) hit distinct banks
+static constexpr int SCS = 32 * 16 + 64;
+static constexpr int SVT = 16 * SCS;
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   bool fresh = true;
   // ---- super-tile k (ring slot k % 4) dequantized into the B fragments bf (lane = token t, step j: code dword
   // 8hf + j of the wave's part, the k-slot order of wf) and into fp16 tile vb: chunk c (code dword c, 8
-  // coordinates) of token t at slot 32c + t
+  // coordinates) of token t at byte SCS c + 16 t
   const int gr0 = ((SQC * wv + 64 * hf) >> lg) - g0, gr1 = ((SQC * wv + 64 * hf + 32) >> lg) - g0;
   auto dequant = [&](int k, h8 (&bf)[SNJ], int vb) {
     const uint8_t* raw = raw_w + (k & 3) * SRAW;
@@ -227,12 +231,12 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
     const uint32_t z0 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr1));
-    uint8_t* dst = vt_w + vb * SVT + (256 * hf + t) * 16;
+    uint8_t* dst = vt_w + vb * SVT + SCS * 8 * hf + 16 * t;
     const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
 #pragma unroll
     for (int j = 0; j < SNJ; ++j) {
       bf[j] = dequant_int4x8(xs[j], j < 4 ? z0 : z1);
-      *(h8*)(dst + 512 * j) = bf[j];
+      *(h8*)(dst + SCS * j) = bf[j];
     }
   };
   // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     const uint32_t z0 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr1));
-    uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + (256 * hf + t) * 16;
+    uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + SCS * 8 * hf + 16 * t;
 
     // ---- partial keys over this wave's coordinates (block by block), RoPE, partial scores of the four heads.
     // The instruction stream interleaves each block's matrix instructions with vector work that does not wait
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
         for (int jj = 2 * g; jj < 2 * g + 2; ++jj) {
           bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
-          *(h8*)(vdst + 512 * jj) = bn[jj];
+          *(h8*)(vdst + SCS * jj) = bn[jj];
         }
       }
       if (g > 0) {
@@ -348,10 +352,10 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // lane rho points at the 4 columns 4(q4 % 2).. of chunk (2nt + q4 / 2, token 8g + 4v + rho / 4)
     {
       const int q4 = rho & 3;
-      const uint8_t* vb = vt_w + (k & 1) * SVT + ((q4 >> 1) * 32 + 8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
+      const uint8_t* vb = vt_w + (k & 1) * SVT + SCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
       h8 vt[SNJ];
 #pragma unroll
-      for (int nt = 0; nt < SNJ; ++nt) vt[nt] = lds_tr8s(vb + 1024 * nt, vb + 1024 * nt + 64);
+      for (int nt = 0; nt < SNJ; ++nt) vt[nt] = lds_tr8s(vb + 2 * SCS * nt, vb + 2 * SCS * nt + 64);
 #pragma unroll
       for (int nt = 0; nt < SNJ; ++nt) acc[nt] = mfma16x16x32(pop, vt[nt], acc[nt]);
     }
