@@ -12,13 +12,13 @@
 // buffers deep (the next page in flight while this one is decoded).  Wave w decodes the 32-token super-tiles
 // w and w + 4 of every page and keeps its own online-softmax state; lane l serves token l % 32, its half l / 32
 // supplies eight of the sixteen k-slots of each matrix step.  Per super-tile:
-//   keys: latent codes -> fp16 (fp8-conversion trick, one fp16 FMA for scale and zero); residual codes c ->
-//     exact fp16 2c - 3 (bit operations only: each pair of a code dword's codes k, k + 8 lands in the mantissa
-//     of 1024 in one shift and one and-or), times S = s / (2 sqrt(128)); K_pre = B_k c + H' e' on
-//     v_mfma_f32_32x32x16_f16 with H' the +-1 Hadamard, whose fragments for every (head-dim tile, step) are
-//     +-A0 or +-A0 with its upper 16 rows negated (a compile-time choice, so four fragments serve all 32
-//     products); RoPE on the pairs (j, j + 64) (tiles m and m + 2: one lane, one accumulator entry); scores
-//     S = Q~ K~^T with the query heads replicated over the 32 rows;
+//   keys: latent codes -> fp16 (fp8-conversion trick, one fp16 FMA for scale and zero), K_pre = B_k c on
+//     v_mfma_f32_32x32x16_f16.  Residual: the 2-bit codes c are spread one per byte (one shift and one mask
+//     per four codes), where each byte is the fp8 e4m3 pattern of c 2^-9; v_mfma_scale_f32_32x32x64_f8f6f4
+//     with the +-1 Hadamard H' in fp8 and a B scale of 2^9 gives H' c exactly (two products per head-dim
+//     tile over the 128 coordinates).  H' 1 is 128 at head dim 0 and 0 elsewhere, so
+//     K_pre += (s / sqrt(128)) (H' c - 192 [d = 0]).  RoPE on the pairs (j, j + 64) (tiles m and m + 2:
+//     one lane, one accumulator entry); scores S = Q~ K~^T with the query heads replicated over the 32 rows;
 //   values: latent chunks and residual 2c - 3 (exact) into per-wave fp16 tiles in LDS, read back token-major
 //     with ds_read_b64_tr_b16 as the B operand of v_mfma_f32_16x16x32_f16.  The A operand is the
 //     probabilities for the latent and the probabilities times the token's residual scale S for the residual
@@ -79,7 +79,18 @@ __host__ __device__ inline Lds lds_layout(int64_t hb) {
 }  // namespace rsd
 
 typedef float f16v_r __attribute__((ext_vector_type(16)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 __device__ inline f16v_r mfma32r(h8 a, h8 b, f16v_r c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+// fp8 (e4m3) x fp8 32x32x64 product, fp32 accumulate; A unscaled, B scaled by 2^9 (E8M0 exponents 127, 136): a
+// residual code c stored alone in a byte is the e4m3 pattern of c * 2^-9, so B reads as the integer c
+__device__ inline f16v_r mfma_f8_codes(v8i_t a, v8i_t b, f16v_r c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 136);
+}
+// Coordinate (within a 64-coordinate block) of byte b of lane half hf's key residual operand: byte q of dword o is
+// code m + 4q (m = o % 4) of the block's code dword 2hf + o / 4.
+__host__ __device__ constexpr int res8_coord(int hf, int b) {
+  return 16 * (2 * hf + (b >> 4)) + ((b >> 2) & 3) + 4 * (b & 3);
+}
 
 // s_waitcnt vmcnt(k) for a run-time k (this wave's copies still allowed in flight)
 __device__ inline void vmcnt_wait_r(int k) {
@@ -118,13 +129,6 @@ __device__ inline h8 res_2c3(uint32_t x, int hf) {
   return r;
 }
 __device__ inline int res_coord(int hf, int e) { return 4 * hf + (e >> 1) + 8 * (e & 1); }
-
-// Sign of the Hadamard fragment of head-dim tile mt (dims 32 mt + r) and residual step j (coordinates
-// 16 j + il): (-1)^popcount(d & i) splits into (-1)^popcount(r & il & 15) (the fragment A0), (-1)^(r4 j0) (rows
-// 16-31 negated for odd j) and (-1)^popcount(mt & (j >> 1)), uniform over the fragment.
-__host__ __device__ constexpr int hsel(int mt, int j) {
-  return (j & 1) + 2 * (__builtin_popcount(mt & (j >> 1)) & 1);
-}
 
 // KS, VS: 16-coordinate steps of the key / value ranks (2..4); STG: 4 KiB rounds of a page copy
 template <int KS, int VS, int STG>
@@ -172,20 +176,30 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
       }
     }
   }
-  // ---- +-1 Hadamard fragments: A0 at row r = t, k-slot 8hf + e <-> coordinate offset res_coord(hf, e) of a
-  // residual step (the order res_2c3 produces); A0 with rows 16-31 negated; and the negatives of both
-  // (selected by hsel)
-  h8 hz[4];
+  // ---- +-1 Hadamard fragments of the fp8 key residual product: head-dim tile mt (row r = t <-> dim 32 mt + r),
+  // coordinate block be; byte b of this lane's 32 <-> coordinate 64 be + res8_coord(hf, b); e4m3 +1 = 0x38,
+  // -1 = 0xB8.  The A and B operands share the lane/byte -> k assignment, so the pairing holds whatever it is.
+  v8i_t hf8[4][2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int il = res_coord(hf, e);
-    const _Float16 v = (__builtin_popcount(t & il & 15) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
-    const _Float16 vf = t >= 16 ? -v : v;
-    hz[0][e] = v;
-    hz[1][e] = vf;
-    hz[2][e] = -v;
-    hz[3][e] = -vf;
-  }
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int be = 0; be < 2; ++be)
+#pragma unroll
+      for (int o = 0; o < 8; ++o) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 64 * be + res8_coord(hf, 4 * o + q);
+          w |= ((__builtin_popcount((32 * mt + t) & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
+        }
+        hf8[mt][be][o] = (int)w;
+      }
+  // kept in the accumulator registers, which the fp8 products read directly (left to the allocator, they were
+  // copied back into vector registers before every product)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int be = 0; be < 2; ++be) asm volatile("" : "=a"(hf8[mt][be]) : "0"(hf8[mt][be]));
   // ---- RoPE frequencies, once per workgroup: theta_j (fp64 pow) in turns per position
   double* tturn = (double*)(smem + LY.theta);
   if (tid < NP) tturn[tid] = (a.theta > 0.0 ? pow(a.theta, -2.0 * tid / D) : 0.0) * 0.15915494309189535;
@@ -299,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
 
       // ---- this lane's words: key and value code dwords (2s + hf) with their pairs, residual code dwords (32
       // bytes per token; dword j holds the codes of coordinates 16j ..), residual scales
-      uint32_t kw[KS], kp[KS], vw[VS], vp[VS], krw[8], vrw[8];
+      uint32_t kw[KS], kp[KS], vw[VS], vp[VS], krw[4], vrw[8];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         kw[s] = *(const uint32_t*)(sb + S.kc + slot * kcb + 8 * s + 4 * hf);
@@ -311,13 +325,14 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
         vp[s] = *(const uint32_t*)(sb + S.vm + slot * vmb + 4 * ((16 * s + 8 * hf) / a.G));
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        krw[j] = *(const uint32_t*)(sb + S.kr + 32 * slot + 4 * j);
-        vrw[j] = *(const uint32_t*)(sb + S.vr + 32 * slot + 4 * j);
-      }
-      const float ks = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.ks + 2 * slot)) * rscale;
+      for (int j = 0; j < 8; ++j) vrw[j] = *(const uint32_t*)(sb + S.vr + 32 * slot + 4 * j);
+#pragma unroll
+      for (int be = 0; be < 2; ++be)  // key residual dwords 4 be + 2hf, + 1 (this lane half's codes of block be)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(sb + S.kr + 32 * slot + 4 * (4 * be + 2 * hf + i));
+      // key residual: K_res = (s / sqrt(128)) (H' c - 1.5 H' 1); value residual: (2c - 3) s / (2 sqrt(128))
+      const float ks = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.ks + 2 * slot)) * (2.0f * rscale);
       const float vs = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.vs + 2 * slot)) * rscale;
-      const h2 kss = {(_Float16)ks, (_Float16)ks};
 
       // ---- values into this wave's fp16 tiles (chunk c of token t at byte CS c + 16 t): latent chunks 2s + hf,
       // residual 2c - 3 of chunk 2j + hf (coordinates 16j + res_coord(hf, e))
@@ -329,21 +344,16 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
 
       // ---- keys: latent and residual operands, then per half m the tiles m and m + 2 (head dims d, d + 64),
       // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
-      h8 kb[KS], er[8];
+      h8 kb[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(kw[s], kp[s]);
+      // key residual codes one per byte (fp8 B operands of blocks 0 and 1): byte q of dword o = code m + 4q of
+      // source dword o / 4, m = o % 4
+      v8i_t er[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const h8 c = res_2c3(krw[j], hf);
-        h8 e;
+      for (int be = 0; be < 2; ++be)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const h2 v = h2{c[2 * q], c[2 * q + 1]} * kss;
-          e[2 * q] = v.x;
-          e[2 * q + 1] = v.y;
-        }
-        er[j] = e;
-      }
+        for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
       f16v_r sc = {};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -353,10 +363,18 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
           ka = mfma32r(bf[s][m], kb[s], ka);
           kz = mfma32r(bf[s][m + 2], kb[s], kz);
         }
+        f16v_r ra = {}, rz = {};  // H' c over the 128 residual coordinates (exact integers)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          ka = mfma32r(hz[hsel(m, j)], er[j], ka);
-          kz = mfma32r(hz[hsel(m + 2, j)], er[j], kz);
+        for (int be = 0; be < 2; ++be) {
+          ra = mfma_f8_codes(hf8[m][be], er[be], ra);
+          rz = mfma_f8_codes(hf8[m + 2][be], er[be], rz);
+        }
+        // H' 1 is 128 at head dim 0 (entry 0 of tile 0 in the lanes of half 0) and 0 elsewhere
+        if (m == 0 && hf == 0) ra[0] -= 192.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ka[i] += ks * ra[i];
+          kz[i] += ks * rz[i];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
