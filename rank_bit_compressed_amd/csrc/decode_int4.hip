@@ -3,8 +3,8 @@
 //
 // Work decomposition: one workgroup (4 waves) per (sequence b, KV head h, context split of pages).
 // The workgroup copies each page's head-h block (codes, scale/zero pairs) and the page's offset row
-// from HBM into LDS with buffer loads that write LDS directly, three buffers deep (two pages in
-// flight while one is decoded).  Wave w decodes the 32-token super-tiles w and w + 4 of every page
+// from HBM into LDS with buffer loads that write LDS directly, two buffers deep (the next page in
+// flight while one is decoded; a third buffer measured no faster).  Wave w decodes the 32-token super-tiles w and w + 4 of every page
 // and keeps its own online-softmax state.
 //
 // All products are v_mfma_f32_32x32x16_f16 (on gfx950 it does twice the work of the 16x16x32 form in
@@ -71,7 +71,7 @@ __host__ __device__ inline Lds lds_layout(int P, int hb_max) {
   // stage buffer: the page's offset row (whole 64-dword rows, the tail zero-filled), then the head block
   L.off_bytes = 256 * ceil_div(P + 1, 64);
   L.stage_bytes = L.off_bytes + (int)pad16(hb_max);
-  L.stage = o; o += 3 * L.stage_bytes;
+  L.stage = o; o += 2 * L.stage_bytes;
   L.total = o;
   return L;
 }
@@ -223,10 +223,9 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   const double fj = tturn[lane];  // turns per position of pair `lane` (query rotation)
 
   // ---- page staging.  Wave w copies the 16-byte chunks 256k + 64w + l of the head block (and a share of
-  // the page's offset row); issue() returns the number of copy instructions the wave issued, so that the
-  // wait for a page leaves exactly the later page's copies in flight.
+  // the page's offset row) into buffer i % 2; it returns the number of copy instructions the wave issued.
   auto issue = [&](int i) -> int {
-    uint8_t* dst = smem + LY.stage + (i % 3) * LY.stage_bytes;
+    uint8_t* dst = smem + LY.stage + (i % 2) * LY.stage_bytes;
     const int bytes = __builtin_amdgcn_readfirstlane(meta_hb[i]);
     // buffer resources: scalar base and size (reads past the size return zeros)
     const __amdgpu_buffer_rsrc_t rs =
@@ -284,13 +283,11 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   };
 
   __syncthreads();  // page addresses and the scaled query visible
-  int kn = 0;
   if (n_pages > 0) issue(0);
-  if (n_pages > 1) kn = issue(1);
-  settle(kn);
+  settle(0);
   for (int ip = 0; ip < n_pages; ++ip) {
-    kn = (ip + 2 < n_pages) ? issue(ip + 2) : 0;
-    const uint32_t* so = (const uint32_t*)(smem + LY.stage + (ip % 3) * LY.stage_bytes);
+    if (ip + 1 < n_pages) issue(ip + 1);  // into the buffer everyone finished with before the last barrier
+    const uint32_t* so = (const uint32_t*)(smem + LY.stage + (ip % 2) * LY.stage_bytes);
     const uint8_t* sb = (const uint8_t*)so + LY.off_bytes;
     HeadSections S;
     if constexpr (VAR) {
@@ -470,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         }
       }
     }
-    settle(kn);
+    settle(0);  // the next page landed (and everyone is done with this buffer)
   }
 
   // ---- partial of the workgroup: the four waves' (m, l, acc) combined in LDS (the staging buffers are
