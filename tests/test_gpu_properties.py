@@ -20,8 +20,9 @@ def _run(w, inp, num_splits=0):
     return out.cpu()
 
 
-def test_deterministic_and_page_table_invariant():
-    w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=3, T=3000)
+@pytest.mark.parametrize("name", ["varrank_paged_32k", "residual_128k"])
+def test_deterministic_and_page_table_invariant(name):
+    w = synth.WORKLOADS[name].scaled(B=3, T=3000)
     inp = synth.make_inputs(w, seq_len=[3000, 2999, 1234])
     a = _run(w, inp)
     b = _run(w, inp)
@@ -42,24 +43,27 @@ def test_split_sweep(name):
         assert rel_err(o, ref_out) <= TOL
 
 
+@pytest.mark.parametrize("name", ["varrank_paged_32k", "residual_128k"])
 @pytest.mark.parametrize("seq", [[1], [31, 32, 33], [255, 256, 257, 511]])
-def test_ragged_lengths_and_tails(seq):
-    w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=len(seq), T=max(seq), page_size=128)
+def test_ragged_lengths_and_tails(name, seq):
+    w = synth.WORKLOADS[name].scaled(B=len(seq), T=max(seq), page_size=128)
     inp = synth.make_inputs(w, seq_len=seq)
     ref_out = oracle_decode(w, inp, oracle_cache(w, inp))
     assert rel_err(_run(w, inp), ref_out) <= TOL
 
 
-def test_single_token_sequence_returns_its_value():
-    w = synth.WORKLOADS["llama8b_layer_8k"].scaled(B=2, T=64, page_size=64)
+@pytest.mark.parametrize("name", ["llama8b_layer_8k", "residual_128k"])
+def test_single_token_sequence_returns_its_value(name):
+    w = synth.WORKLOADS[name].scaled(B=2, T=64, page_size=64)
     inp = synth.make_inputs(w, seq_len=[1, 64])
     ref_out = oracle_decode(w, inp, oracle_cache(w, inp))
     out = _run(w, inp).double().numpy()
     assert np.abs(out[0] - ref_out[0]).max() <= TOL * np.abs(ref_out[0]).max()
 
 
-def test_query_dtype_and_explicit_positions():
-    w = synth.WORKLOADS["llama8b_layer_8k"].scaled(B=2, T=900, q_bf16=False)
+@pytest.mark.parametrize("name", ["llama8b_layer_8k", "residual_128k"])
+def test_query_dtype_and_explicit_positions(name):
+    w = synth.WORKLOADS[name].scaled(B=2, T=900, q_bf16=False)
     inp = synth.make_inputs(w, seq_len=[900, 500])
     inp["q_pos"] = torch.tensor([123456, 7], dtype=torch.int32)
     ref_out = oracle_decode(w, inp, oracle_cache(w, inp))
