@@ -226,6 +226,37 @@ kvc_status kvc_decode_attn_timed(const kvc_layout* layout, const kvc_cache* cach
 enum { KVC_PATH_HEAD = 0, KVC_PATH_INT4 = 1, KVC_PATH_SHARED = 2, KVC_PATH_RES = 3 };
 kvc_status kvc_decode_path(const kvc_layout* layout, int32_t* path);
 
+/* Inputs of kvc_fit_basis.  All arrays are device memory. */
+typedef struct {
+  int32_t B, max_T;              /* sequences, row length of x                                  */
+  int32_t n_kv_heads;            /* Hkv                                                          */
+  int32_t head_dim;              /* d: 128                                                       */
+  int32_t rank;                  /* r: 1..head_dim columns of the basis                          */
+  int32_t r_cap;                 /* columns of the bf16 basis, rank..head_dim (zero beyond rank) */
+  const int32_t* seq_len;        /* [B] rows used per sequence, 0..max_T                         */
+  const float* x;                /* [B][max_T][Hkv][head_dim] pre-RoPE keys (or values), fp32     */
+} kvc_fit_in;
+
+/* Workspace bytes of kvc_fit_basis for these sizes (pointers are not read). */
+kvc_status kvc_fit_workspace_bytes(const kvc_fit_in* in, size_t* bytes);
+
+/* Basis fitting for the prefill side: per KV head h, the rank leading right singular vectors of X_h, the
+ * matrix whose rows are x[b][t][h][:] for every t < seq_len[b] of every sequence ("JoLT: Near-Lossless KV
+ * Cache Compression", "Key findings": per-head SVD, keys taken before RoPE; "A JoLT for the KV cache",
+ * abstract: the feature mode is the truncated one).  No mean is removed.  Columns are ordered by
+ * decreasing singular value and signed so that each column's entry of largest magnitude is positive.
+ * Computed as the eigenvectors of X_h^T X_h (fp32 accumulation on the matrix cores, then Jacobi rotations
+ * in fp32).  Outputs (any may be NULL, not all):
+ *   basis_bf16 [Hkv][d][r_cap] bf16, round to nearest even, columns rank..r_cap-1 zero: the layout
+ *     kvc_compress (basis_k / basis_v) and kvc_decode_attn (wk / wv) take;
+ *   basis_f32 [Hkv][d][rank];
+ *   sigma2 [Hkv][d] the eigenvalues of X_h^T X_h (squared singular values), decreasing, clamped at 0.
+ * A head with no rows gets the first rank coordinate axes.  Where singular values coincide the
+ * columns are any orthonormal basis of their common space.  Non-finite inputs give unspecified (but
+ * finite-time) results.  ws: workspace of kvc_fit_workspace_bytes.  Deterministic. */
+kvc_status kvc_fit_basis(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

@@ -30,6 +30,8 @@ size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits);
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
                                 void* ws, int n_splits, int st_per_split, hipStream_t st);
 kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const kvc_cache& C, hipStream_t st);
+kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                    size_t ws_bytes, hipStream_t st, size_t* bytes_out);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                       size_t* need);
 
@@ -184,6 +186,17 @@ kvc_status kvc_decode_path(const kvc_layout* layout, int32_t* path) {
   if (!path) return KVC_ERR_INVALID_ARG;
   *path = layout->shared ? KVC_PATH_SHARED : head_decode_path(*layout);
   return KVC_OK;
+}
+
+kvc_status kvc_fit_workspace_bytes(const kvc_fit_in* in, size_t* bytes) {
+  if (!in || !bytes) return KVC_ERR_INVALID_ARG;
+  return fit_impl(*in, nullptr, nullptr, nullptr, nullptr, 0, nullptr, bytes);
+}
+
+kvc_status kvc_fit_basis(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return fit_impl(*in, basis_bf16, basis_f32, sigma2, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

@@ -1,0 +1,344 @@
+// fit.hip -- per-KV-head basis fitting for the prefill side (gfx950): the r leading right singular vectors of
+// each head's pre-RoPE rows ("JoLT: Near-Lossless KV Cache Compression", "Key findings": per-head SVD, keys
+// decomposed before RoPE; "A JoLT for the KV cache", abstract: the feature mode is the one truncated).
+//
+// At head dimension 128 the decomposition is exact through the 128 x 128 Gram matrix G = X^T X: its
+// eigenvectors are the right singular vectors of X and its eigenvalues the squared singular values.
+//   1. fit_gram_kernel: G on v_mfma_f32_32x32x2_f32 (fp32 operands and accumulation).  Features are tiled
+//      as four 32-row tiles with row i of tile I <-> feature 4i + I, so one 16-byte load per lane (features
+//      4i..4i+3 of one token) supplies the operands of all ten upper tiles (I <= J) of a two-token step.
+//      A workgroup (h, slice) walks the 1024-token chunks slice, slice + n_slices, ... of all sequences, its
+//      four waves each take a quarter of every chunk, and their sums are added in a fixed order in LDS into
+//      one partial per workgroup.
+//   2. fit_reduce_kernel: the partials of a head summed in slice order into the symmetric G.
+//   3. fit_eig_kernel: one workgroup of 1024 threads per head runs cyclic Jacobi (Golub & Van Loan's
+//      symmetric Schur rotations) on G in LDS, 64 disjoint rotations per round in round-robin order (127
+//      rounds a sweep, every pair once), until a sweep rotates nothing; eigenvalues sorted in decreasing
+//      order, each column's entry of largest magnitude made positive.
+// Every summation order is fixed, so the same inputs give bit-identical outputs.
+#include <math.h>
+
+#include <algorithm>
+
+#include "kvc_common.hpp"
+
+namespace kvc {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace fit {
+constexpr int D = 128;
+constexpr int NT = 10;          // upper tiles I <= J of the 4 x 4 tiling
+constexpr int TF = 1024;        // floats per 32 x 32 tile
+constexpr int CHUNK = 1024;     // tokens of one sequence per work item
+constexpr int WTOK = CHUNK / 4;  // tokens per wave per work item
+constexpr int U = 8;            // two-token steps per load batch
+constexpr int MAX_SWEEPS = 30;
+constexpr int EIG_THREADS = 1024;
+
+__host__ __device__ constexpr int tile_i(int k) { return k < 4 ? 0 : k < 7 ? 1 : k < 9 ? 2 : 3; }
+__host__ __device__ constexpr int tile_j(int k) { return k < 4 ? k : k < 7 ? k - 3 : k < 9 ? k - 5 : 3; }
+
+inline int slices(int Hkv, int B, int max_T) {
+  const int items = B * ceil_div(max_T, CHUNK);
+  const int target = std::max(1, 512 / std::max(Hkv, 1));  // about 512 workgroups: two per compute unit
+  return std::max(1, std::min(items, target));
+}
+inline size_t part_floats(int Hkv, int n_slices) { return (size_t)Hkv * n_slices * NT * TF; }
+}  // namespace fit
+
+__device__ inline f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 2) void fit_gram_kernel(const float* __restrict__ x, const int32_t* __restrict__ seq_len,
+                                                          int B, int max_T, int Hkv, int n_slices, float* __restrict__ part) {
+  using namespace fit;
+  __shared__ float red[NT * TF];
+  const int h = blockIdx.x % Hkv, slice = blockIdx.x / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m = lane & 31, hh = lane >> 5;
+  const int n_chunks = ceil_div(max_T, CHUNK);
+  const size_t tstride = (size_t)Hkv * D;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) acc[k] = f32x16{};
+
+  for (int item = slice; item < B * n_chunks; item += n_slices) {
+    const int b = item / n_chunks, c = item % n_chunks;
+    const int T = min(max(seq_len[b], 0), max_T);
+    const int t0 = c * CHUNK + wv * WTOK;
+    const int t1 = min(t0 + WTOK, T);
+    if (t0 >= t1) continue;  // wave-uniform
+    const float* base = x + ((size_t)b * max_T * Hkv + h) * D + 4 * m;
+    // step s covers tokens t0 + 2s (lanes 0-31) and t0 + 2s + 1 (lanes 32-63); rows past t1 read as zero
+    const int nsteps = (t1 - t0 + 1) / 2;
+    auto load = [&](int s) -> f4 {
+      const int t = t0 + 2 * s + hh;
+      return t < t1 ? *(const f4*)(base + (size_t)t * tstride) : f4{0, 0, 0, 0};
+    };
+    f4 cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = load(u);
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u] = load(s0 + U + u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const f4 v = cur[u];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) acc[k] = mfma_f32(v[tile_i(k)], v[tile_j(k)], acc[k]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+  }
+  // the four waves' sums, added in wave order; entry (k, e = 64 v + lane) of the tile layout
+  for (int w = 0; w < 4; ++w) {
+    if (wv == w)
+#pragma unroll
+      for (int k = 0; k < NT; ++k)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int e = k * TF + 64 * v + lane;
+          red[e] = (w == 0 ? 0.0f : red[e]) + acc[k][v];
+        }
+    __syncthreads();
+  }
+  float* dst = part + ((size_t)h * n_slices + slice) * NT * TF;
+  for (int e = tid; e < NT * TF; e += 256) dst[e] = red[e];
+}
+
+// G[h] (row-major 128 x 128, symmetric) = sum over slices of the partials, in slice order.  Entry e = 64 v +
+// lane of tile k holds G[4 i + I][4 j + J] with i = 8 (v / 4) + 4 (lane / 32) + v % 4, j = lane % 32.
+__global__ __launch_bounds__(256) void fit_reduce_kernel(const float* __restrict__ part, int n_slices, float* __restrict__ gram) {
+  using namespace fit;
+  const int h = blockIdx.x / (NT * 4), k = (blockIdx.x / 4) % NT;
+  const int e = (blockIdx.x % 4) * 256 + threadIdx.x;
+  const float* src = part + (size_t)h * n_slices * NT * TF + (size_t)k * TF + e;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int sl = 0;
+  for (; sl + 4 <= n_slices; sl += 4) {
+    s0 += src[(size_t)(sl + 0) * NT * TF];
+    s1 += src[(size_t)(sl + 1) * NT * TF];
+    s2 += src[(size_t)(sl + 2) * NT * TF];
+    s3 += src[(size_t)(sl + 3) * NT * TF];
+  }
+  for (; sl < n_slices; ++sl) s0 += src[(size_t)sl * NT * TF];
+  const float s = (s0 + s1) + (s2 + s3);
+  const int v = e / 64, lane = e % 64;
+  const int i = 8 * (v / 4) + 4 * (lane / 32) + v % 4, j = lane % 32;
+  const int I = tile_i(k), J = tile_j(k);
+  const int fi = 4 * i + I, fj = 4 * j + J;
+  float* G = gram + (size_t)h * D * D;
+  if (I < J) {
+    G[fi * D + fj] = s;
+    G[fj * D + fi] = s;
+  } else if (i <= j) {  // diagonal tile: one of the two mirrored entries defines both
+    G[fi * D + fj] = s;
+    G[fj * D + fi] = s;
+  }
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Pair P of round k (0..126) of the round-robin schedule over 128 indices: (k, 127) for P = 0, else
+// {(k + P) mod 127, (k - P) mod 127}; over the 127 rounds every pair meets once (127 is prime).
+__device__ inline void rr_pair(int k, int P, int& p, int& q) {
+  if (P == 0) {
+    p = k;
+    q = 127;
+  } else {
+    const int a = (k + P) % 127, b = (k - P + 127) % 127;
+    p = min(a, b);
+    q = max(a, b);
+  }
+}
+
+__global__ __launch_bounds__(1024) void fit_eig_kernel(const float* __restrict__ gram, int rank, int r_cap,
+                                                        uint16_t* __restrict__ basis_bf16, float* __restrict__ basis_f32,
+                                                        float* __restrict__ sigma2) {
+  using namespace fit;
+  extern __shared__ __attribute__((aligned(16))) float eig_smem[];
+  float* A = eig_smem;            // [128][128]
+  float* V = A + D * D;           // [128][128], eigenvectors in columns
+  float* cs = V + D * D;          // [64][4] (c, s, t = s / c) of the round's rotations
+  float* lam = cs + 256;          // [128]
+  int* order = (int*)(lam + D);   // [128] column of V for output column c
+  int* nrot = order + D;          // [2] rotation flags of alternate sweeps
+  float* sgn = (float*)(nrot + 2);  // [128]
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* G = gram + (size_t)h * D * D;
+  for (int e = tid; e < D * D; e += EIG_THREADS) {
+    A[e] = G[e];
+    V[e] = (e / D == e % D) ? 1.0f : 0.0f;
+  }
+  if (tid < 2) nrot[tid] = 0;
+  __syncthreads();
+  // trace (the sum of the eigenvalues of a positive semidefinite G) sets the absolute floor of the
+  // off-diagonal entries worth rotating away
+  float tr = 0.0f;
+  for (int i = 0; i < D; ++i) tr += fabsf(A[i * D + i]);
+  const float floor_abs = tr * 0x1p-48f;
+
+  for (int sweep = 0; sweep < MAX_SWEEPS; ++sweep) {
+    for (int k = 0; k < 127; ++k) {
+      if (tid < 64) {
+        int p, q;
+        rr_pair(k, tid, p, q);
+        const float app = A[p * D + p], aqq = A[q * D + q], apq = A[p * D + q];
+        float c = 1.0f, s = 0.0f, ts = 0.0f;
+        if (fabsf(apq) > floor_abs && fabsf(apq) > 0x1p-24f * sqrtf(fabsf(app)) * sqrtf(fabsf(aqq))) {
+          const float tau = (aqq - app) / (2.0f * apq);
+          const float at = fabsf(tau);
+          const float t = (at > 1e18f ? 0.5f / at : 1.0f / (at + sqrtf(1.0f + tau * tau)));
+          ts = tau >= 0.0f ? t : -t;
+          c = 1.0f / sqrtf(1.0f + ts * ts);
+          s = ts * c;
+          nrot[sweep & 1] = 1;
+        }
+        cs[4 * tid] = c;
+        cs[4 * tid + 1] = s;
+        cs[4 * tid + 2] = ts;
+      }
+      __syncthreads();
+      // A <- J^T A J on the 64 x 64 blocks of the round's pairs (the blocks partition A)
+      for (int u = tid; u < 64 * 64; u += EIG_THREADS) {
+        const int P = u >> 6, Q = u & 63;
+        int p1, q1, p2, q2;
+        rr_pair(k, P, p1, q1);
+        rr_pair(k, Q, p2, q2);
+        const float c1 = cs[4 * P], s1 = cs[4 * P + 1], c2 = cs[4 * Q], s2 = cs[4 * Q + 1];
+        if (s1 == 0.0f && s2 == 0.0f) continue;
+        const float m00 = A[p1 * D + p2], m01 = A[p1 * D + q2], m10 = A[q1 * D + p2], m11 = A[q1 * D + q2];
+        float r00, r01, r10, r11;
+        if (P == Q) {
+          // the rotated pair's own block: a_pq becomes zero, and the diagonal moves by t a_pq (the direct
+          // form keeps the rounding of a thousand updates per sweep series off the eigenvalues)
+          const float t = cs[4 * P + 2];
+          r00 = m00 - t * m01;
+          r11 = m11 + t * m01;
+          r01 = 0.0f;
+          r10 = 0.0f;
+        } else {
+          const float n00 = c1 * m00 - s1 * m10, n01 = c1 * m01 - s1 * m11;
+          const float n10 = s1 * m00 + c1 * m10, n11 = s1 * m01 + c1 * m11;
+          r00 = c2 * n00 - s2 * n01;
+          r01 = s2 * n00 + c2 * n01;
+          r10 = c2 * n10 - s2 * n11;
+          r11 = s2 * n10 + c2 * n11;
+        }
+        A[p1 * D + p2] = r00;
+        A[p1 * D + q2] = r01;
+        A[q1 * D + p2] = r10;
+        A[q1 * D + q2] = r11;
+      }
+      // V <- V J
+      for (int u = tid; u < D * 64; u += EIG_THREADS) {
+        const int i = u >> 6, P = u & 63;
+        const float c = cs[4 * P], s = cs[4 * P + 1];
+        if (s == 0.0f) continue;
+        int p, q;
+        rr_pair(k, P, p, q);
+        const float vp = V[i * D + p], vq = V[i * D + q];
+        V[i * D + p] = c * vp - s * vq;
+        V[i * D + q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+    const int rotated = nrot[sweep & 1];
+    // the next sweep's flag: its only writers are the first wave's lanes, which clear it here, in program
+    // order before they can set it; the other waves read it only after the sweep's closing barrier
+    if (tid == 0) nrot[(sweep + 1) & 1] = 0;
+    if (!rotated) break;  // uniform: every thread read the flag after the same barrier
+  }
+  if (tid < D) order[tid] = tid;  // a complete permutation even if non-finite values make positions collide
+  __syncthreads();
+  // eigenvalues in decreasing order (index order among equal values)
+  if (tid < D) {
+    const float l = A[tid * D + tid];
+    int pos = 0;
+    for (int j = 0; j < D; ++j) {
+      const float lj = A[j * D + j];
+      pos += (lj > l) || (lj == l && j < tid);
+    }
+    order[pos] = tid;
+    lam[pos] = l;
+  }
+  __syncthreads();
+  // output column c: unit norm (the rotations' rounding lets the norms drift by a few ulps per sweep), its
+  // entry of largest magnitude positive (the first one on ties)
+  if (tid < D) {
+    const int col = order[tid];
+    float best = -1.0f, val = 0.0f, nrm = 0.0f;
+    for (int i = 0; i < D; ++i) {
+      const float v = V[i * D + col];
+      nrm += v * v;
+      if (fabsf(v) > best) {
+        best = fabsf(v);
+        val = v;
+      }
+    }
+    sgn[tid] = (val < 0.0f ? -1.0f : 1.0f) / sqrtf(nrm);
+    if (sigma2) sigma2[(size_t)h * D + tid] = fmaxf(lam[tid], 0.0f);
+  }
+  __syncthreads();
+  if (basis_bf16)
+    for (int e = tid; e < D * r_cap; e += EIG_THREADS) {
+      const int d = e / r_cap, c = e % r_cap;
+      basis_bf16[(size_t)h * D * r_cap + e] = c < rank ? f32_to_bf16_rne(sgn[c] * V[d * D + order[c]]) : (uint16_t)0;
+    }
+  if (basis_f32)
+    for (int e = tid; e < D * rank; e += EIG_THREADS) {
+      const int d = e / rank, c = e % rank;
+      basis_f32[(size_t)h * D * rank + e] = sgn[c] * V[d * D + order[c]];
+    }
+}
+
+namespace fit {
+constexpr size_t EIG_LDS = (2 * D * D + 256 + D) * 4 + (D + 2) * 4 + D * 4;
+}
+
+kvc_status hip_fail(hipError_t e);
+
+kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                    size_t ws_bytes, hipStream_t st, size_t* bytes_out) {
+  using namespace fit;
+  if (in.B < 1 || in.max_T < 1 || in.n_kv_heads < 1 || in.head_dim < 1) return KVC_ERR_INVALID_ARG;
+  if (in.head_dim != D) return KVC_ERR_UNSUPPORTED;
+  if (in.rank < 1 || in.rank > D || in.r_cap < in.rank || in.r_cap > D) return KVC_ERR_INVALID_ARG;
+  if ((int64_t)in.B * in.max_T * in.n_kv_heads * D >= ((int64_t)1 << 40)) return KVC_ERR_UNSUPPORTED;
+  const int n_slices = slices(in.n_kv_heads, in.B, in.max_T);
+  const size_t pf = part_floats(in.n_kv_heads, n_slices);
+  const size_t need = (pf + (size_t)in.n_kv_heads * D * D) * sizeof(float);
+  if (bytes_out) {
+    *bytes_out = need;
+    return KVC_OK;
+  }
+  if (!in.seq_len || !in.x || !ws || (!basis_bf16 && !basis_f32 && !sigma2)) return KVC_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)in.seq_len, (const void*)in.x, (const void*)basis_bf16, (const void*)basis_f32,
+                        (const void*)sigma2, (const void*)ws})
+    if ((uintptr_t)p & 15u) return KVC_ERR_MISALIGNED;
+  if (ws_bytes < need) return KVC_ERR_WORKSPACE;
+  float* part = (float*)ws;
+  float* gram = part + pf;
+  fit_gram_kernel<<<in.n_kv_heads * n_slices, 256, 0, st>>>(in.x, in.seq_len, in.B, in.max_T, in.n_kv_heads, n_slices,
+                                                             part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  fit_reduce_kernel<<<in.n_kv_heads * NT * 4, 256, 0, st>>>(part, n_slices, gram);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipFuncSetAttribute((const void*)fit_eig_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)EIG_LDS);
+  if (e != hipSuccess) return hip_fail(e);
+  fit_eig_kernel<<<in.n_kv_heads, EIG_THREADS, EIG_LDS, st>>>(gram, in.rank, in.r_cap, basis_bf16, basis_f32, sigma2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return KVC_OK;
+}
+
+}  // namespace kvc

@@ -23,7 +23,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "work
           -4: "pointer not 16-byte aligned", -5: "HIP runtime error"}
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
-           "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed"]
+           "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
+           "kvc_fit_basis"]
 
 
 class KvcError(RuntimeError):
@@ -68,6 +69,11 @@ class DenseIn(C.Structure):
                 ("v_pages", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32), ("num_splits", C.c_int32)]
 
 
+class FitIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_T", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("rank", C.c_int32), ("r_cap", C.c_int32), ("seq_len", C.c_void_p), ("x", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -93,6 +99,8 @@ def lib():
         L.kvc_dense_workspace_bytes.argtypes = [P, P]; L.kvc_dense_workspace_bytes.restype = C.c_int32
         L.kvc_dense_decode_attn.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_dense_decode_attn.restype = C.c_int32
         L.kvc_decode_path.argtypes = [P, P]; L.kvc_decode_path.restype = C.c_int32
+        L.kvc_fit_workspace_bytes.argtypes = [P, P]; L.kvc_fit_workspace_bytes.restype = C.c_int32
+        L.kvc_fit_basis.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_fit_basis.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -287,3 +295,31 @@ def dense_decode_attn(Hq, Hkv, d, P, block_table, seq_len, k_pages, v_pages, q, 
     _check(lib().kvc_dense_decode_attn(C.byref(inp), _ptr(out), _ptr(ws), ws.numel(), _stream()),
            "kvc_dense_decode_attn")
     return out
+
+
+def fit_in(x, seq_len, rank, r_cap=None) -> FitIn:
+    B, max_T, Hkv, d = x.shape
+    return FitIn(B, max_T, Hkv, d, rank, rank if r_cap is None else r_cap, _ptr(seq_len), _ptr(x))
+
+
+def fit_workspace_bytes(inp: FitIn) -> int:
+    out = C.c_size_t()
+    _check(lib().kvc_fit_workspace_bytes(C.byref(inp), C.byref(out)), "kvc_fit_workspace_bytes")
+    return out.value
+
+
+def fit_basis(x, seq_len, rank, r_cap=None, want_f32=True, want_sigma2=True, ws=None):
+    """kvc_fit_basis: x fp32 [B, max_T, Hkv, d] pre-RoPE rows, seq_len int32 [B] ->
+    (basis bf16 [Hkv, d, r_cap], basis fp32 [Hkv, d, rank] or None, sigma2 fp32 [Hkv, d] or None)."""
+    inp = fit_in(x, seq_len, rank, r_cap)
+    B, max_T, Hkv, d = x.shape
+    need = fit_workspace_bytes(inp)
+    dev = x.device
+    bb = torch.empty((Hkv, d, inp.r_cap), dtype=torch.bfloat16, device=dev)
+    bf = torch.empty((Hkv, d, rank), dtype=torch.float32, device=dev) if want_f32 else None
+    s2 = torch.empty((Hkv, d), dtype=torch.float32, device=dev) if want_sigma2 else None
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib().kvc_fit_basis(C.byref(inp), _ptr(bb.view(torch.int16)), _ptr(bf), _ptr(s2), _ptr(ws), ws.numel(),
+                               _stream()), "kvc_fit_basis")
+    return bb, bf, s2

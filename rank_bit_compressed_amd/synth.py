@@ -18,7 +18,12 @@ Distributions (the pages give shapes, not data):
   * queries: N(0, 1) / 8, rounded to bf16 where the workload says bf16;
   * variable ranks: i.i.d. per (sequence, token) from a discrete distribution;
   * block tables: identity (contiguous storage) or a seeded permutation of
-    all physical pages.
+    all physical pages;
+  * prefill rows for basis fitting (pre-RoPE keys or values, fp32): per KV
+    head h, x = mu_h + Q_h (z * s) with z ~ N(0, I), s_i = 4 i^-0.7 (the same
+    decaying spectrum as the latents), Q_h a seeded orthogonal d x d matrix
+    and mu_h a seeded direction of length 1.5, so the rows carry a mean and a
+    spread of singular values without repeated ones.
 """
 from __future__ import annotations
 
@@ -186,3 +191,24 @@ def make_dense_inputs(w: Workload, device="cpu") -> dict:
     v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     q = (torch.randn(w.B, w.n_q_heads, w.head_dim, generator=_gen(w, 21, "cpu")) / 8.0).to(torch.bfloat16)
     return {"k_pages": k, "v_pages": v, "q": q.to(dev)}
+
+
+def make_prefill_rows(B: int, max_T: int, n_kv_heads: int, head_dim: int, seed: int = 0, device="cpu",
+                      decay: float = 0.7, scale: float = 4.0, mean_norm: float = 1.5) -> torch.Tensor:
+    """fp32 rows [B, max_T, Hkv, d] for basis fitting (seeded; the law is in the module docstring)."""
+    dev = torch.device(device)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000 + 30)
+    a = torch.randn(n_kv_heads, head_dim, head_dim, generator=g, dtype=torch.float64)
+    q, r = torch.linalg.qr(a)
+    q = (q * torch.sign(torch.diagonal(r, dim1=-2, dim2=-1)).unsqueeze(-2)).to(torch.float32)
+    mu = torch.randn(n_kv_heads, head_dim, generator=g, dtype=torch.float64)
+    mu = (mu / mu.norm(dim=-1, keepdim=True) * mean_norm).to(torch.float32)
+    s = scale * _decay_scale(head_dim, decay, "cpu")
+    gz = torch.Generator(device=dev)
+    gz.manual_seed(seed * 1000 + 31)
+    x = torch.empty(B, max_T, n_kv_heads, head_dim, dtype=torch.float32, device=dev)
+    for h in range(n_kv_heads):
+        z = torch.randn(B * max_T, head_dim, generator=gz, device=dev, dtype=torch.float32) * s.to(dev)
+        x[:, :, h, :] = (z @ q[h].T.to(dev) + mu[h].to(dev)).view(B, max_T, head_dim)
+    return x

@@ -77,3 +77,24 @@ def test_decode_path_selection():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
         assert kvc.decode_path(kvc.make_layout(**small.layout_kwargs())) == want[name], name
+
+
+def test_fit_calls_reject_bad_arguments_without_launching():
+    lib = kvc.lib()
+    out = C.c_size_t()
+    ok = kvc.FitIn(2, 1000, 8, 128, 64, 64, None, None)
+    assert lib.kvc_fit_workspace_bytes(C.byref(ok), C.byref(out)) == 0
+    # 2 x 1000 rows -> 2 work items of 1024 tokens, so 2 slices: partials 8 x 2 x 10 tiles, and G 8 x 128 x 128
+    assert out.value == (8 * 2 * 10 * 1024 + 8 * 128 * 128) * 4
+    for fields, want in [((0, 1000, 8, 128, 64, 64), -1), ((2, 1000, 8, 64, 32, 32), -2),
+                         ((2, 1000, 8, 128, 0, 64), -1), ((2, 1000, 8, 128, 65, 64), -1),
+                         ((2, 1000, 8, 128, 64, 129), -1)]:
+        bad = kvc.FitIn(*fields, None, None)
+        assert lib.kvc_fit_workspace_bytes(C.byref(bad), C.byref(out)) == want, fields
+    # null inputs, no outputs, misaligned pointers and a short workspace are refused before any launch
+    v = C.c_void_p
+    assert lib.kvc_fit_basis(C.byref(ok), v(16), None, None, v(32), 1 << 30, None) == -1
+    good = kvc.FitIn(2, 1000, 8, 128, 64, 64, v(48), v(64))
+    assert lib.kvc_fit_basis(C.byref(good), None, None, None, v(32), 1 << 30, None) == -1
+    assert lib.kvc_fit_basis(C.byref(good), v(18), None, None, v(32), 1 << 30, None) == -4
+    assert lib.kvc_fit_basis(C.byref(good), v(16), None, None, v(32), 1024, None) == -3
