@@ -35,6 +35,9 @@ constexpr int WTOK = CHUNK / 4;  // tokens per wave per work item
 constexpr int U = 8;            // two-token steps per load batch
 constexpr int MAX_SWEEPS = 30;
 constexpr int EIG_THREADS = 1024;
+constexpr int EIG_WAVES = EIG_THREADS / 64;
+constexpr int BPW = 64 / EIG_WAVES;            // row pairs per wave in the block update
+constexpr int VPT = D * 64 / EIG_THREADS;      // entries of V^T rows p and q per thread
 
 __host__ __device__ constexpr int tile_i(int k) { return k < 4 ? 0 : k < 7 ? 1 : k < 9 ? 2 : 3; }
 __host__ __device__ constexpr int tile_j(int k) { return k < 4 ? k : k < 7 ? k - 3 : k < 9 ? k - 5 : 3; }
@@ -147,136 +150,190 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 }
 
 // Pair P of round k (0..126) of the round-robin schedule over 128 indices: (k, 127) for P = 0, else
-// {(k + P) mod 127, (k - P) mod 127}; over the 127 rounds every pair meets once (127 is prime).
+// ((k + P) mod 127, (k - P) mod 127); over the 127 rounds every pair meets once (127 is prime).  The pair is
+// left unordered: across the lanes of a wave (consecutive P) both members then run through consecutive
+// indices, so the block updates' LDS accesses fall on distinct banks.
 __device__ inline void rr_pair(int k, int P, int& p, int& q) {
   if (P == 0) {
     p = k;
     q = 127;
   } else {
-    const int a = (k + P) % 127, b = (k - P + 127) % 127;
-    p = min(a, b);
-    q = max(a, b);
+    p = k + P;
+    q = k - P;
+    p -= p >= 127 ? 127 : 0;
+    q += q < 0 ? 127 : 0;
   }
 }
 
-__global__ __launch_bounds__(1024) void fit_eig_kernel(const float* __restrict__ gram, int rank, int r_cap,
+namespace fit {
+constexpr int VS = D + 4;  // row stride of V^T (floats): 16-byte rows, and column walks spread over the banks
+constexpr int AS = D + 1;  // row stride of A (floats): rows and columns both walk across the banks
+}
+
+// Storage: A (the matrix being diagonalized) keeps its upper triangle only, entry (i, j), i <= j, at
+// A[i * AS + j]; V^T keeps eigenvector c in row c.  Per round, the 64 disjoint pairs (p_P, q_P) split A into
+// 2 x 2 blocks (P, Q); block (P, Q) with P <= Q owns every stored entry it touches, so the blocks update in
+// place without conflicts.
+__global__ __launch_bounds__(fit::EIG_THREADS) void fit_eig_kernel(const float* __restrict__ gram, int rank, int r_cap,
                                                         uint16_t* __restrict__ basis_bf16, float* __restrict__ basis_f32,
                                                         float* __restrict__ sigma2) {
   using namespace fit;
   extern __shared__ __attribute__((aligned(16))) float eig_smem[];
-  float* A = eig_smem;            // [128][128]
-  float* V = A + D * D;           // [128][128], eigenvectors in columns
-  float* cs = V + D * D;          // [64][4] (c, s, t = s / c) of the round's rotations
-  float* lam = cs + 256;          // [128]
-  int* order = (int*)(lam + D);   // [128] column of V for output column c
-  int* nrot = order + D;          // [2] rotation flags of alternate sweeps
-  float* sgn = (float*)(nrot + 2);  // [128]
+  float* A = eig_smem;                  // [128][AS], upper triangle
+  float* Vt = A + D * AS;               // [128][VS] (16-byte aligned: D * AS is a multiple of 4)
+  float* cs = Vt + D * VS;              // [2 rounds][64][4]: c, s, t = s / c
+  int* pq = (int*)(cs + 2 * 256);       // [2 rounds][64][2]: the pair
+  float* lam = (float*)(pq + 2 * 128);  // [128]
+  int* order = (int*)(lam + D);         // [128] eigenvector index of output column c
+  int* flag = order + D;                // [0..1] rotated in round parity; [2..3] rotated in sweep parity
+  float* sgn = (float*)(flag + 4);      // [128]
   const int h = blockIdx.x, tid = threadIdx.x;
   const float* G = gram + (size_t)h * D * D;
-  for (int e = tid; e < D * D; e += EIG_THREADS) {
-    A[e] = G[e];
-    V[e] = (e / D == e % D) ? 1.0f : 0.0f;
-  }
-  if (tid < 2) nrot[tid] = 0;
+  for (int e = tid; e < D * D; e += EIG_THREADS) A[(e / D) * AS + e % D] = G[e];
+  for (int e = tid; e < D * VS; e += EIG_THREADS) Vt[e] = (e / VS == e % VS) ? 1.0f : 0.0f;
+  if (tid < 4) flag[tid] = 0;
   __syncthreads();
-  // trace (the sum of the eigenvalues of a positive semidefinite G) sets the absolute floor of the
-  // off-diagonal entries worth rotating away
+  // trace (the sum of the eigenvalues of a positive semidefinite G, at least its largest) sets the absolute
+  // floor of the off-diagonal entries worth rotating away: u tr(G).  Entries below it bound the angle error of
+  // eigenvector c by about sqrt(128) u tr / gap_c, far below what the fp32 Gram matrix itself carries; rotating
+  // them away would only chase rounding noise for another sweep or two.
   float tr = 0.0f;
-  for (int i = 0; i < D; ++i) tr += fabsf(A[i * D + i]);
-  const float floor_abs = tr * 0x1p-48f;
+  for (int i = 0; i < D; ++i) tr += fabsf(A[i * AS + i]);
+  const float floor_abs = tr * 0x1p-24f;
+  auto sym = [](int i, int j) -> int { return i <= j ? i * AS + j : j * AS + i; };  // stored entry (i, j)
 
   for (int sweep = 0; sweep < MAX_SWEEPS; ++sweep) {
     for (int k = 0; k < 127; ++k) {
+      const int rb = (sweep * 127 + k) & 1;  // parity of the global round count: consecutive rounds alternate
+      float* csr = cs + rb * 256;
+      int* pqr = pq + rb * 128;
       if (tid < 64) {
+        // this wave alone writes the round's tables and flags; the slots of parity rb were last read before the
+        // previous round's first barrier (tables) or right after it (the round flag, then known to be 0 if the
+        // round was skipped); the other parity's round flag is cleared here for the next round
+        if (tid == 0) flag[rb ^ 1] = 0;
         int p, q;
         rr_pair(k, tid, p, q);
-        const float app = A[p * D + p], aqq = A[q * D + q], apq = A[p * D + q];
+        const float app = A[p * AS + p], aqq = A[q * AS + q], apq = A[sym(p, q)];
+        // the rotation of the symmetric 2 x 2 problem (Golub & Van Loan's symmetric Schur step), with the
+        // hardware square root, reciprocal and reciprocal square root (about 1 ulp): any c, s with c^2 + s^2 = 1
+        // to a few ulps serve, and the correctly rounded sequences would lengthen the round's serial part
         float c = 1.0f, s = 0.0f, ts = 0.0f;
-        if (fabsf(apq) > floor_abs && fabsf(apq) > 0x1p-24f * sqrtf(fabsf(app)) * sqrtf(fabsf(aqq))) {
-          const float tau = (aqq - app) / (2.0f * apq);
-          const float at = fabsf(tau);
-          const float t = (at > 1e18f ? 0.5f / at : 1.0f / (at + sqrtf(1.0f + tau * tau)));
+        if (fabsf(apq) > floor_abs &&
+            fabsf(apq) > 0x1p-24f * __builtin_amdgcn_sqrtf(fabsf(app)) * __builtin_amdgcn_sqrtf(fabsf(aqq))) {
+          const float tau = (aqq - app) * (0.5f * __builtin_amdgcn_rcpf(apq));
+          const float atau = fabsf(tau);
+          const float t = atau > 1e18f ? 0.5f * __builtin_amdgcn_rcpf(atau)
+                                       : __builtin_amdgcn_rcpf(atau + __builtin_amdgcn_sqrtf(1.0f + tau * tau));
           ts = tau >= 0.0f ? t : -t;
-          c = 1.0f / sqrtf(1.0f + ts * ts);
+          c = __builtin_amdgcn_rsqf(1.0f + ts * ts);
           s = ts * c;
-          nrot[sweep & 1] = 1;
+          flag[rb] = 1;
+          flag[2 + (sweep & 1)] = 1;
         }
-        cs[4 * tid] = c;
-        cs[4 * tid + 1] = s;
-        cs[4 * tid + 2] = ts;
+        *(f4*)(csr + 4 * tid) = f4{c, s, ts, 0.0f};
+        pqr[2 * tid] = p;
+        pqr[2 * tid + 1] = q;
       }
       __syncthreads();
-      // A <- J^T A J on the 64 x 64 blocks of the round's pairs (the blocks partition A)
-      for (int u = tid; u < 64 * 64; u += EIG_THREADS) {
-        const int P = u >> 6, Q = u & 63;
-        int p1, q1, p2, q2;
-        rr_pair(k, P, p1, q1);
-        rr_pair(k, Q, p2, q2);
-        const float c1 = cs[4 * P], s1 = cs[4 * P + 1], c2 = cs[4 * Q], s2 = cs[4 * Q + 1];
-        if (s1 == 0.0f && s2 == 0.0f) continue;
-        const float m00 = A[p1 * D + p2], m01 = A[p1 * D + q2], m10 = A[q1 * D + p2], m11 = A[q1 * D + q2];
-        float r00, r01, r10, r11;
-        if (P == Q) {
-          // the rotated pair's own block: a_pq becomes zero, and the diagonal moves by t a_pq (the direct
-          // form keeps the rounding of a thousand updates per sweep series off the eigenvalues)
-          const float t = cs[4 * P + 2];
-          r00 = m00 - t * m01;
-          r11 = m11 + t * m01;
-          r01 = 0.0f;
-          r10 = 0.0f;
-        } else {
+      if (!flag[rb]) continue;  // uniform: nothing rotates this round
+      // A <- J^T A J on the blocks P <= Q (wave w takes the row pairs P = BPW w .., lane = Q) and V <- V J on
+      // rows p, q of V^T (VPT entries per thread: pair tid / (D / VPT), entries VPT (tid % (D / VPT)) ..).  The blocks of
+      // a round are disjoint, so every read is issued first, then the arithmetic, then the writes: one LDS
+      // round trip per round instead of one per block.
+      {
+        const int Q = tid & 63;
+        const f4 cq = *(const f4*)(csr + 4 * Q);
+        const int p2 = pqr[2 * Q], q2 = pqr[2 * Q + 1];
+        int ad[BPW][4];
+        float m[BPW][4];
+        f4 cpj[BPW];
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          const int P = BPW * (tid >> 6) + j;
+          cpj[j] = *(const f4*)(csr + 4 * P);
+          const int p1 = pqr[2 * P], q1 = pqr[2 * P + 1];
+          ad[j][0] = sym(p1, p2);
+          ad[j][1] = sym(p1, q2);
+          ad[j][2] = sym(q1, p2);
+          ad[j][3] = sym(q1, q2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m[j][e] = A[ad[j][e]];
+        }
+        constexpr int NV = VPT / 4;
+        const int PV = tid / (D / VPT), seg = VPT * (tid % (D / VPT));
+        const f4 cv = *(const f4*)(csr + 4 * PV);
+        f4* vp = (f4*)(Vt + pqr[2 * PV] * VS + seg);
+        f4* vq = (f4*)(Vt + pqr[2 * PV + 1] * VS + seg);
+        f4 va[NV], vb[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          va[i] = vp[i];
+          vb[i] = vq[i];
+        }
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          const int P = BPW * (tid >> 6) + j;
+          const float c1 = cpj[j][0], s1 = cpj[j][1], c2 = cq[0], s2 = cq[1];
+          const float m00 = m[j][0], m01 = m[j][1], m10 = m[j][2], m11 = m[j][3];
           const float n00 = c1 * m00 - s1 * m10, n01 = c1 * m01 - s1 * m11;
           const float n10 = s1 * m00 + c1 * m10, n11 = s1 * m01 + c1 * m11;
-          r00 = c2 * n00 - s2 * n01;
-          r01 = s2 * n00 + c2 * n01;
-          r10 = c2 * n10 - s2 * n11;
-          r11 = s2 * n10 + c2 * n11;
+          float r00 = c2 * n00 - s2 * n01, r01 = s2 * n00 + c2 * n01;
+          float r10 = c2 * n10 - s2 * n11, r11 = s2 * n10 + c2 * n11;
+          if (P == Q) {
+            // the rotated pair's own block (entries (p,p), (p,q) twice, (q,q)): a_pq becomes zero and the
+            // diagonal moves by t a_pq (the direct form keeps the rounding of the many small updates off the
+            // eigenvalues); a pair left unrotated keeps its entries
+            r00 = m00 - cpj[j][2] * m01;
+            r11 = m11 + cpj[j][2] * m01;
+            r01 = s1 != 0.0f ? 0.0f : m01;
+            r10 = r01;
+          }
+          if (P <= Q && (s1 != 0.0f || s2 != 0.0f)) {
+            A[ad[j][0]] = r00;
+            A[ad[j][1]] = r01;
+            A[ad[j][2]] = r10;
+            A[ad[j][3]] = r11;
+          }
         }
-        A[p1 * D + p2] = r00;
-        A[p1 * D + q2] = r01;
-        A[q1 * D + p2] = r10;
-        A[q1 * D + q2] = r11;
-      }
-      // V <- V J
-      for (int u = tid; u < D * 64; u += EIG_THREADS) {
-        const int i = u >> 6, P = u & 63;
-        const float c = cs[4 * P], s = cs[4 * P + 1];
-        if (s == 0.0f) continue;
-        int p, q;
-        rr_pair(k, P, p, q);
-        const float vp = V[i * D + p], vq = V[i * D + q];
-        V[i * D + p] = c * vp - s * vq;
-        V[i * D + q] = s * vp + c * vq;
+        if (cv[1] != 0.0f)
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            vp[i] = cv[0] * va[i] - cv[1] * vb[i];
+            vq[i] = cv[1] * va[i] + cv[0] * vb[i];
+          }
       }
       __syncthreads();
     }
-    const int rotated = nrot[sweep & 1];
-    // the next sweep's flag: its only writers are the first wave's lanes, which clear it here, in program
-    // order before they can set it; the other waves read it only after the sweep's closing barrier
-    if (tid == 0) nrot[(sweep + 1) & 1] = 0;
-    if (!rotated) break;  // uniform: every thread read the flag after the same barrier
+    // the sweep flags: set only by the first wave; the one for the next sweep is cleared by that wave here,
+    // in program order before it can set it, and every thread read this sweep's after the same barrier
+    const int rotated = flag[2 + (sweep & 1)];
+    __syncthreads();
+    if (tid == 0) flag[2 + ((sweep + 1) & 1)] = 0;
+    if (!rotated) break;
   }
+  __syncthreads();
   if (tid < D) order[tid] = tid;  // a complete permutation even if non-finite values make positions collide
   __syncthreads();
   // eigenvalues in decreasing order (index order among equal values)
   if (tid < D) {
-    const float l = A[tid * D + tid];
+    const float l = A[tid * AS + tid];
     int pos = 0;
     for (int j = 0; j < D; ++j) {
-      const float lj = A[j * D + j];
+      const float lj = A[j * AS + j];
       pos += (lj > l) || (lj == l && j < tid);
     }
     order[pos] = tid;
     lam[pos] = l;
   }
   __syncthreads();
-  // output column c: unit norm (the rotations' rounding lets the norms drift by a few ulps per sweep), its
-  // entry of largest magnitude positive (the first one on ties)
+  // output column c: unit norm (the rotations' rounding lets the norms drift by a few ulps), its entry of
+  // largest magnitude positive (the first one on ties)
   if (tid < D) {
-    const int col = order[tid];
+    const float* row = Vt + order[tid] * VS;
     float best = -1.0f, val = 0.0f, nrm = 0.0f;
     for (int i = 0; i < D; ++i) {
-      const float v = V[i * D + col];
+      const float v = row[i];
       nrm += v * v;
       if (fabsf(v) > best) {
         best = fabsf(v);
@@ -290,17 +347,17 @@ __global__ __launch_bounds__(1024) void fit_eig_kernel(const float* __restrict__
   if (basis_bf16)
     for (int e = tid; e < D * r_cap; e += EIG_THREADS) {
       const int d = e / r_cap, c = e % r_cap;
-      basis_bf16[(size_t)h * D * r_cap + e] = c < rank ? f32_to_bf16_rne(sgn[c] * V[d * D + order[c]]) : (uint16_t)0;
+      basis_bf16[(size_t)h * D * r_cap + e] = c < rank ? f32_to_bf16_rne(sgn[c] * Vt[order[c] * VS + d]) : (uint16_t)0;
     }
   if (basis_f32)
     for (int e = tid; e < D * rank; e += EIG_THREADS) {
       const int d = e / rank, c = e % rank;
-      basis_f32[(size_t)h * D * rank + e] = sgn[c] * V[d * D + order[c]];
+      basis_f32[(size_t)h * D * rank + e] = sgn[c] * Vt[order[c] * VS + d];
     }
 }
 
 namespace fit {
-constexpr size_t EIG_LDS = (2 * D * D + 256 + D) * 4 + (D + 2) * 4 + D * 4;
+constexpr size_t EIG_LDS = ((size_t)D * AS + D * VS + 2 * 256 + 2 * 128 + D + D + 4 + D) * 4;
 }
 
 kvc_status hip_fail(hipError_t e);
