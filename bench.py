@@ -9,7 +9,8 @@ torch.cuda.synchronize() (wall clock: ms_per_step and value); a pair of HIP even
 around each timed launch of the attention kernel gives its average duration (the roofline figure); the
 dense kernel is timed by wall clock too, after its own warmup.  Each step reads a different replica of
 the compressed cache (4 replicas, more than the 256 MB last-level cache holds) so the stream comes from
-HBM.
+HBM.  Beside the headline line, `other_workloads` gives the other decode workloads at full size and the
+basis fit (kvc_fit_basis) on the prefill rows of the 32K workload.
 """
 import argparse
 import hashlib
@@ -82,6 +83,10 @@ def cpu_baseline(w, inp, min_seconds=10.0):
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+# basis fitting on the prefill of the 32K decode workload: 16 sequences x 32768 rows x 8 KV heads x 128
+FIT_SHAPE = (16, 32768, 8, 128)
+FIT_RANK = 64
 
 # The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
@@ -154,6 +159,46 @@ def other_workloads(steps: int, warmup: int) -> dict:
         del plan, cache, inp
         torch.cuda.empty_cache()
     return res
+
+
+def fit_workload(steps: int) -> dict:
+    """kvc_fit_basis on the prefill rows of the 32K workload: the Gram-matrix kernel's median duration (library
+    events around it), the whole call's wall time, and the Gram kernel's figure against the fp32 matrix peak.
+    Algorithmic flops: 2 per multiply-add over the d (d + 1) / 2 distinct entries of each head's symmetric
+    Gram matrix, per row."""
+    import torch
+    from rank_bit_compressed_amd import kvc, synth
+
+    B, T, Hkv, d = FIT_SHAPE
+    x = synth.make_prefill_rows(B, T, Hkv, d, seed=6, device="cuda")
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvc.fit_workspace_bytes(kvc.fit_in(x, sl, FIT_RANK)), dtype=torch.uint8, device="cuda")
+    n = max(10, steps // 100)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    for _ in range(3):
+        kvc.fit_basis(x, sl, FIT_RANK, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        kvc.fit_basis(x, sl, FIT_RANK, ws=ws, events=ev[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / n
+    g_ms = sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+    rows = B * T * Hkv
+    flops = 2 * rows * (d * (d + 1) // 2)
+    tflops = flops / (g_ms * 1e-3) / 1e12
+    nbytes = rows * d * 4
+    del x, ws
+    torch.cuda.empty_cache()
+    return {"kernel": "fit_gram_kernel (Gram matrix, fp32 matrix instructions)", "rows": rows, "rank": FIT_RANK,
+            "gram_kernel_ms_median": round(g_ms, 5), "ms_per_call": round(wall_ms, 5),
+            "gram_flops": flops, "tflops": round(tflops, 1), "bound": "mfma",
+            "frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4), "input_bytes": nbytes,
+            "hbm_gbs": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
+            "rest_of_call": "split reduction and the per-head Jacobi eigensolver (one workgroup per head)"}
 
 
 def main():
@@ -278,6 +323,7 @@ def main():
     }
     if not args.no_other:
         line["other_workloads"] = other_workloads(args.steps, args.warmup)
+        line["other_workloads"]["basis_fit_prefill_32k"] = fit_workload(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, {k: (v.cpu() if v is not None else None) for k, v in cpu_inp.items()})
     print(json.dumps(line), flush=True)

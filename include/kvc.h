@@ -257,6 +257,15 @@ kvc_status kvc_fit_workspace_bytes(const kvc_fit_in* in, size_t* bytes);
 kvc_status kvc_fit_basis(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* kvc_fit_basis with a measurement hook: ev_begin and ev_end are caller-created hipEvent_t handles
+ * (passed as void*), recorded on `stream` immediately before and after the launch of the Gram-matrix
+ * kernel (the data-parallel pass over the rows); the reduction and the eigensolver that follow lie
+ * outside the pair.  Same results and errors as kvc_fit_basis; both events are required (INVALID_ARG
+ * otherwise), and on an error returned before the launch neither event is recorded.  The events stay
+ * owned by the caller. */
+kvc_status kvc_fit_basis_timed(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                               size_t ws_bytes, void* stream, void* ev_begin, void* ev_end);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

@@ -199,6 +199,17 @@ kvc_status kvc_fit_basis(const kvc_fit_in* in, uint16_t* basis_bf16, float* basi
   return fit_impl(*in, basis_bf16, basis_f32, sigma2, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
+kvc_status kvc_fit_basis_timed(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
+                               size_t ws_bytes, void* stream, void* ev_begin, void* ev_end) {
+  if (!ev_begin || !ev_end) return KVC_ERR_INVALID_ARG;
+  struct Reset {
+    ~Reset() { g_marks = LaunchMarks{}; }
+  } reset;
+  g_marks.begin = (hipEvent_t)ev_begin;
+  g_marks.end = (hipEvent_t)ev_end;
+  return kvc_fit_basis(in, basis_bf16, basis_f32, sigma2, ws, ws_bytes, stream);
+}
+
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {
   if (!in || !bytes) return KVC_ERR_INVALID_ARG;
   return dense_impl(*in, nullptr, nullptr, 0, nullptr, bytes);

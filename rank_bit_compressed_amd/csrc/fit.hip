@@ -383,9 +383,13 @@ kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32
   if (ws_bytes < need) return KVC_ERR_WORKSPACE;
   float* part = (float*)ws;
   float* gram = part + pf;
+  hipError_t e = mark(g_marks.begin, st);
+  if (e != hipSuccess) return hip_fail(e);
   fit_gram_kernel<<<in.n_kv_heads * n_slices, 256, 0, st>>>(in.x, in.seq_len, in.B, in.max_T, in.n_kv_heads, n_slices,
                                                              part);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  e = mark(g_marks.end, st);
   if (e != hipSuccess) return hip_fail(e);
   fit_reduce_kernel<<<in.n_kv_heads * NT * 4, 256, 0, st>>>(part, n_slices, gram);
   e = hipGetLastError();

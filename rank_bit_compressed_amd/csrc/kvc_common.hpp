@@ -20,9 +20,10 @@ namespace kvc {
 // Record the HIP error of this thread and map it to a status.
 kvc_status hip_fail(hipError_t e);
 
-// Optional pair of caller-owned HIP events that the decode launchers record on their stream right
-// before and right after the attention kernel (not the split merge).  Set only for the duration of
-// one kvc_decode_attn_timed call on the calling thread; null otherwise.
+// Optional pair of caller-owned HIP events that the launchers record on their stream right before and
+// right after the measured kernel: the attention kernel of a decode (not the split merge), the Gram
+// kernel of a basis fit.  Set only for the duration of one kvc_decode_attn_timed / kvc_fit_basis_timed
+// call on the calling thread; null otherwise.
 struct LaunchMarks {
   hipEvent_t begin = nullptr, end = nullptr;
 };

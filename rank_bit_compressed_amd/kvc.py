@@ -24,7 +24,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "work
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
-           "kvc_fit_basis"]
+           "kvc_fit_basis", "kvc_fit_basis_timed"]
 
 
 class KvcError(RuntimeError):
@@ -101,6 +101,8 @@ def lib():
         L.kvc_decode_path.argtypes = [P, P]; L.kvc_decode_path.restype = C.c_int32
         L.kvc_fit_workspace_bytes.argtypes = [P, P]; L.kvc_fit_workspace_bytes.restype = C.c_int32
         L.kvc_fit_basis.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_fit_basis.restype = C.c_int32
+        L.kvc_fit_basis_timed.argtypes = [P, P, P, P, P, C.c_size_t, P, P, P]
+        L.kvc_fit_basis_timed.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -308,9 +310,11 @@ def fit_workspace_bytes(inp: FitIn) -> int:
     return out.value
 
 
-def fit_basis(x, seq_len, rank, r_cap=None, want_f32=True, want_sigma2=True, ws=None):
+def fit_basis(x, seq_len, rank, r_cap=None, want_f32=True, want_sigma2=True, ws=None, events=None):
     """kvc_fit_basis: x fp32 [B, max_T, Hkv, d] pre-RoPE rows, seq_len int32 [B] ->
-    (basis bf16 [Hkv, d, r_cap], basis fp32 [Hkv, d, rank] or None, sigma2 fp32 [Hkv, d] or None)."""
+    (basis bf16 [Hkv, d, r_cap], basis fp32 [Hkv, d, rank] or None, sigma2 fp32 [Hkv, d] or None).
+    events: optional (begin, end) torch.cuda.Event pair recorded around the Gram-matrix kernel
+    (kvc_fit_basis_timed)."""
     inp = fit_in(x, seq_len, rank, r_cap)
     B, max_T, Hkv, d = x.shape
     need = fit_workspace_bytes(inp)
@@ -320,6 +324,10 @@ def fit_basis(x, seq_len, rank, r_cap=None, want_f32=True, want_sigma2=True, ws=
     s2 = torch.empty((Hkv, d), dtype=torch.float32, device=dev) if want_sigma2 else None
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check(lib().kvc_fit_basis(C.byref(inp), _ptr(bb.view(torch.int16)), _ptr(bf), _ptr(s2), _ptr(ws), ws.numel(),
-                               _stream()), "kvc_fit_basis")
+    args = (C.byref(inp), _ptr(bb.view(torch.int16)), _ptr(bf), _ptr(s2), _ptr(ws), ws.numel(), _stream())
+    if events is None:
+        _check(lib().kvc_fit_basis(*args), "kvc_fit_basis")
+    else:
+        _check(lib().kvc_fit_basis_timed(*args, _event_handle(events[0]), _event_handle(events[1])),
+               "kvc_fit_basis_timed")
     return bb, bf, s2

@@ -98,3 +98,6 @@ def test_fit_calls_reject_bad_arguments_without_launching():
     assert lib.kvc_fit_basis(C.byref(good), None, None, None, v(32), 1 << 30, None) == -1
     assert lib.kvc_fit_basis(C.byref(good), v(18), None, None, v(32), 1 << 30, None) == -4
     assert lib.kvc_fit_basis(C.byref(good), v(16), None, None, v(32), 1024, None) == -3
+    # the timed entry needs both events, and otherwise checks as the plain one
+    assert lib.kvc_fit_basis_timed(C.byref(good), v(16), None, None, v(32), 1 << 30, None, None, v(64)) == -1
+    assert lib.kvc_fit_basis_timed(C.byref(good), v(18), None, None, v(32), 1 << 30, None, v(48), v(64)) == -4

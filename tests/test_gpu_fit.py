@@ -183,3 +183,23 @@ def test_fit_full_size_sampled_heads():
                 assert _sin(B_[:, c], ob[0][:, c]) <= bound, (h, c)
                 tested += 1
         assert tested >= 8
+
+
+def test_fit_timed_entry_matches_and_brackets_the_gram_kernel():
+    x = synth.make_prefill_rows(3, 3000, 8, 128, seed=7).cuda().contiguous()
+    sl = torch.tensor([3000, 2000, 1], dtype=torch.int32).cuda()
+    plain = kvc.fit_basis(x, sl, 64)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev[2:]:
+        e.record()
+    torch.cuda.synchronize()
+    ev[0].record()
+    timed = kvc.fit_basis(x, sl, 64, events=(ev[2], ev[3]))
+    ev[1].record()
+    torch.cuda.synchronize()
+    for a, b in zip(plain, timed):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    inner, outer = ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[1])
+    assert 0 < inner <= outer
+    assert ev[0].elapsed_time(ev[2]) >= 0 and ev[3].elapsed_time(ev[1]) >= 0
