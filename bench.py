@@ -10,7 +10,8 @@ around each timed launch of the attention kernel gives its average duration (the
 dense kernel is timed by wall clock too, after its own warmup.  Each step reads a different replica of
 the compressed cache (4 replicas, more than the 256 MB last-level cache holds) so the stream comes from
 HBM.  Beside the headline line, `other_workloads` gives the other decode workloads at full size and the
-basis fit (kvc_fit_basis) on the prefill rows of the 32K workload.
+basis fit (kvc_fit_basis) and the salience-driven rank allocation (kvc_salience, kvc_rank_alloc) on the prefill
+rows of the 32K workload.
 """
 import argparse
 import hashlib
@@ -87,6 +88,9 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 # basis fitting on the prefill of the 32K decode workload: 16 sequences x 32768 rows x 8 KV heads x 128
 FIT_SHAPE = (16, 32768, 8, 128)
 FIT_RANK = 64
+# salience-driven rank allocation on the same prefill: a 32-query window, the 32K workload's ladder and mean rank
+SAL_WINDOW = 32
+ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.8
 
 # The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
@@ -199,6 +203,49 @@ def fit_workload(steps: int) -> dict:
             "frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4), "input_bytes": nbytes,
             "hbm_gbs": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
             "rest_of_call": "split reduction and the per-head Jacobi eigensolver (one workgroup per head)"}
+
+
+def alloc_workload(steps: int) -> dict:
+    """kvc_salience (window queries over the prefill keys) and kvc_rank_alloc on the prefill of the 32K workload:
+    median times from events on the library's stream (the current torch stream).  Algorithmic flops of the
+    salience: one q.k per (window query, query head, key), 2 d each; the two passes recompute them."""
+    import torch
+    from rank_bit_compressed_amd import kvc, synth
+
+    B, T, Hkv, d = FIT_SHAPE
+    Hq = 4 * Hkv
+    k = synth.make_prefill_rows(B, T, Hkv, d, seed=3, device="cuda")
+    q = synth.make_window_queries(B, SAL_WINDOW, Hq, d, seed=3, device="cuda")
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    sal = torch.empty(B, T, device="cuda")
+    ranks = torch.empty(B, T, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kvc.salience_workspace_bytes(kvc.salience_in(q, k, sl, 5e5)), dtype=torch.uint8, device="cuda")
+    n = max(10, steps // 100)
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+
+    s_ms = timed(lambda: kvc.salience(q, k, sl, 5e5, out=sal, ws=ws))
+    a_ms = timed(lambda: kvc.rank_alloc(sal, sl, ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN, out=ranks))
+    mean_rank = float(ranks.float().mean().item())
+    flops = 2 * d * SAL_WINDOW * Hq * B * T
+    tflops = flops / (s_ms * 1e-3) / 1e12
+    del k, q, ws
+    torch.cuda.empty_cache()
+    return {"kernel": "sal_kernel (two passes, fp32 matrix instructions) + rank_alloc_kernel", "window": SAL_WINDOW,
+            "salience_ms_median": round(s_ms, 5), "alloc_ms_median": round(a_ms, 5),
+            "salience_flops": flops, "tflops": round(tflops, 1), "bound": "mfma",
+            "frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+            "ladder": ALLOC_LADDER, "mean_rank_target": ALLOC_MEAN, "mean_rank_allocated": round(mean_rank, 3)}
 
 
 def main():
@@ -324,6 +371,7 @@ def main():
     if not args.no_other:
         line["other_workloads"] = other_workloads(args.steps, args.warmup)
         line["other_workloads"]["basis_fit_prefill_32k"] = fit_workload(args.steps)
+        line["other_workloads"]["rank_alloc_prefill_32k"] = alloc_workload(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, {k: (v.cpu() if v is not None else None) for k, v in cpu_inp.items()})
     print(json.dumps(line), flush=True)

@@ -266,6 +266,52 @@ kvc_status kvc_fit_basis(const kvc_fit_in* in, uint16_t* basis_bf16, float* basi
 kvc_status kvc_fit_basis_timed(const kvc_fit_in* in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
                                size_t ws_bytes, void* stream, void* ev_begin, void* ev_end);
 
+/* Inputs of kvc_salience.  All arrays are device memory. */
+typedef struct {
+  int32_t B, max_T;              /* sequences, row length of k                                  */
+  int32_t W;                     /* window queries per sequence, 1..32                           */
+  int32_t n_q_heads, n_kv_heads; /* Hq = 4 Hkv                                                   */
+  int32_t head_dim;              /* d: 128                                                       */
+  double rope_theta;             /* RoPE base (rotate-half pairs (j, j + d/2)); 0 = no RoPE      */
+  const int32_t* seq_len;        /* [B] tokens per sequence, 0..max_T                            */
+  const float* q;                /* [B][W][Hq][d] pre-RoPE; query i at position seq_len - W + i  */
+  const float* k;                /* [B][max_T][Hkv][d] pre-RoPE keys                             */
+} kvc_salience_in;
+
+/* Workspace bytes of kvc_salience for these sizes (pointers are not read). */
+kvc_status kvc_salience_workspace_bytes(const kvc_salience_in* in, size_t* bytes);
+
+/* Query salience of every cached token, the input of the per-token rank choice ("VarRate: Training-Free
+ * Variable-Rate KV Cache Compression for Long-Context LLMs", "Method": a token's rank follows its query
+ * salience).  The page defines no formula; the one computed: sal[b][t] is the attention probability that
+ * the window queries put on token t, summed over the queries present (positions >= 0) and all query heads;
+ * each query attends causally (keys t <= its position), RoPE rotates queries and keys at their positions,
+ * scores are q.k / sqrt(d), and query head h reads KV head h / (Hq / Hkv).  A sequence's values sum to
+ * (queries present) x Hq.  Scores in fp32 on the matrix cores, exp2 in fp32.  out: fp32 [B][max_T], zero
+ * at t >= seq_len.  ws: workspace of kvc_salience_workspace_bytes.  Deterministic. */
+kvc_status kvc_salience(const kvc_salience_in* in, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Inputs of kvc_rank_alloc.  sal and seq_len are device memory; the rest is read on the host. */
+typedef struct {
+  int32_t B, max_T;
+  int32_t n_ladder;              /* m, 2..8 rungs                                               */
+  int32_t ladder[8];             /* ranks r_0 < ... < r_{m-1}, each 1..255                       */
+  float step_w[7];               /* w_j >= 0, non-increasing: value per rank unit of step j       */
+  double mean_rank;              /* budget per token, in [r_0, r_{m-1}]                          */
+  const int32_t* seq_len;        /* [B] tokens per sequence, 0..max_T                            */
+  const float* sal;              /* [B][max_T] salience, >= 0 (for instance kvc_salience's)      */
+} kvc_alloc_in;
+
+/* Per-token ranks under a budget ("VarRate ...", "Method" and "Principles": ranks follow query salience
+ * and no token drops to rank zero).  Every token starts at r_0; the step r_j -> r_{j+1} of token t costs
+ * r_{j+1} - r_j and gains the fp32 product sal[b][t] * w_j.  Steps are taken in decreasing order of
+ * gain, equal gains together, while the sequence's total rank stays within floor(mean_rank * seq_len[b])
+ * (evaluated in double); the first group that does not fit ends it.  With w non-increasing a token's
+ * steps are taken in order, and a more salient token never gets a lower rank.  ranks: uint8 [B][max_T],
+ * 0 at t >= seq_len (the per-token ranks kvc_compress takes, with a ladder of multiples of 8).  One
+ * workgroup per sequence.  Deterministic. */
+kvc_status kvc_rank_alloc(const kvc_alloc_in* in, uint8_t* ranks, void* stream);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

@@ -32,6 +32,9 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
 kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const kvc_cache& C, hipStream_t st);
 kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
                     size_t ws_bytes, hipStream_t st, size_t* bytes_out);
+kvc_status salience_impl(const kvc_salience_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
+                         size_t* bytes_out);
+kvc_status rank_alloc_impl(const kvc_alloc_in& in, uint8_t* ranks, hipStream_t st);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                       size_t* need);
 
@@ -208,6 +211,21 @@ kvc_status kvc_fit_basis_timed(const kvc_fit_in* in, uint16_t* basis_bf16, float
   g_marks.begin = (hipEvent_t)ev_begin;
   g_marks.end = (hipEvent_t)ev_end;
   return kvc_fit_basis(in, basis_bf16, basis_f32, sigma2, ws, ws_bytes, stream);
+}
+
+kvc_status kvc_salience_workspace_bytes(const kvc_salience_in* in, size_t* bytes) {
+  if (!in || !bytes) return KVC_ERR_INVALID_ARG;
+  return salience_impl(*in, nullptr, nullptr, 0, nullptr, bytes);
+}
+
+kvc_status kvc_salience(const kvc_salience_in* in, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return salience_impl(*in, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+kvc_status kvc_rank_alloc(const kvc_alloc_in* in, uint8_t* ranks, void* stream) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return rank_alloc_impl(*in, ranks, (hipStream_t)stream);
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

@@ -24,7 +24,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "work
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
-           "kvc_fit_basis", "kvc_fit_basis_timed"]
+           "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
+           "kvc_rank_alloc"]
 
 
 class KvcError(RuntimeError):
@@ -74,6 +75,18 @@ class FitIn(C.Structure):
                 ("rank", C.c_int32), ("r_cap", C.c_int32), ("seq_len", C.c_void_p), ("x", C.c_void_p)]
 
 
+class SalienceIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_T", C.c_int32), ("W", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rope_theta", C.c_double),
+                ("seq_len", C.c_void_p), ("q", C.c_void_p), ("k", C.c_void_p)]
+
+
+class AllocIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_T", C.c_int32), ("n_ladder", C.c_int32), ("ladder", C.c_int32 * 8),
+                ("step_w", C.c_float * 7), ("mean_rank", C.c_double), ("seq_len", C.c_void_p),
+                ("sal", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -103,6 +116,9 @@ def lib():
         L.kvc_fit_basis.argtypes = [P, P, P, P, P, C.c_size_t, P]; L.kvc_fit_basis.restype = C.c_int32
         L.kvc_fit_basis_timed.argtypes = [P, P, P, P, P, C.c_size_t, P, P, P]
         L.kvc_fit_basis_timed.restype = C.c_int32
+        L.kvc_salience_workspace_bytes.argtypes = [P, P]; L.kvc_salience_workspace_bytes.restype = C.c_int32
+        L.kvc_salience.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_salience.restype = C.c_int32
+        L.kvc_rank_alloc.argtypes = [P, P, P]; L.kvc_rank_alloc.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -331,3 +347,44 @@ def fit_basis(x, seq_len, rank, r_cap=None, want_f32=True, want_sigma2=True, ws=
         _check(lib().kvc_fit_basis_timed(*args, _event_handle(events[0]), _event_handle(events[1])),
                "kvc_fit_basis_timed")
     return bb, bf, s2
+
+
+def salience_in(q, k, seq_len, theta) -> SalienceIn:
+    B, W, Hq, d = q.shape
+    _, max_T, Hkv, _ = k.shape
+    return SalienceIn(B, max_T, W, Hq, Hkv, d, float(theta), _ptr(seq_len), _ptr(q), _ptr(k))
+
+
+def salience_workspace_bytes(inp: SalienceIn) -> int:
+    out = C.c_size_t()
+    _check(lib().kvc_salience_workspace_bytes(C.byref(inp), C.byref(out)), "kvc_salience_workspace_bytes")
+    return out.value
+
+
+def salience(q, k, seq_len, theta, out=None, ws=None):
+    """kvc_salience: q fp32 [B, W, Hq, d] window queries, k fp32 [B, max_T, Hkv, d] keys (both pre-RoPE),
+    seq_len int32 [B] -> fp32 [B, max_T]."""
+    inp = salience_in(q, k, seq_len, theta)
+    need = salience_workspace_bytes(inp)
+    if out is None:
+        out = torch.empty((k.shape[0], k.shape[1]), dtype=torch.float32, device=k.device)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=k.device)
+    _check(lib().kvc_salience(C.byref(inp), _ptr(out), _ptr(ws), ws.numel(), _stream()), "kvc_salience")
+    return out
+
+
+def alloc_in(sal, seq_len, ladder, step_w, mean_rank) -> AllocIn:
+    B, max_T = sal.shape
+    lad = (C.c_int32 * 8)(*(list(ladder) + [0] * (8 - len(ladder))))
+    w = (C.c_float * 7)(*(list(step_w) + [0.0] * (7 - len(step_w))))
+    return AllocIn(B, max_T, len(ladder), lad, w, float(mean_rank), _ptr(seq_len), _ptr(sal))
+
+
+def rank_alloc(sal, seq_len, ladder, step_w, mean_rank, out=None):
+    """kvc_rank_alloc: sal fp32 [B, max_T] -> uint8 ranks [B, max_T]."""
+    inp = alloc_in(sal, seq_len, ladder, step_w, mean_rank)
+    if out is None:
+        out = torch.empty(sal.shape, dtype=torch.uint8, device=sal.device)
+    _check(lib().kvc_rank_alloc(C.byref(inp), _ptr(out), _stream()), "kvc_rank_alloc")
+    return out

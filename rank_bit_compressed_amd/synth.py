@@ -23,7 +23,10 @@ Distributions (the pages give shapes, not data):
     head h, x = mu_h + Q_h (z * s) with z ~ N(0, I), s_i = 4 i^-0.7 (the same
     decaying spectrum as the latents), Q_h a seeded orthogonal d x d matrix
     and mu_h a seeded direction of length 1.5, so the rows carry a mean and a
-    spread of singular values without repeated ones.
+    spread of singular values without repeated ones;
+  * window queries for salience (pre-RoPE, fp32): N(0, 1) per element;
+  * salience for the rank-allocation tests: exp(N(0, 1.5^2)) per token, a
+    heavy-tailed positive spread like attention mass, rounded to fp32.
 """
 from __future__ import annotations
 
@@ -212,3 +215,17 @@ def make_prefill_rows(B: int, max_T: int, n_kv_heads: int, head_dim: int, seed: 
         z = torch.randn(B * max_T, head_dim, generator=gz, device=dev, dtype=torch.float32) * s.to(dev)
         x[:, :, h, :] = (z @ q[h].T.to(dev) + mu[h].to(dev)).view(B, max_T, head_dim)
     return x
+
+
+def make_window_queries(B: int, W: int, n_q_heads: int, head_dim: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [B, W, Hq, d] pre-RoPE queries of the prefill's last W positions (seeded, N(0, 1))."""
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed * 1000 + 32)
+    return torch.randn(B, W, n_q_heads, head_dim, generator=g, device=device, dtype=torch.float32)
+
+
+def make_salience(B: int, max_T: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [B, max_T] positive saliences (seeded, exp(N(0, 1.5^2)))."""
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed * 1000 + 33)
+    return torch.exp(1.5 * torch.randn(B, max_T, generator=g, device=device, dtype=torch.float64)).to(torch.float32)

@@ -101,3 +101,32 @@ def test_fit_calls_reject_bad_arguments_without_launching():
     # the timed entry needs both events, and otherwise checks as the plain one
     assert lib.kvc_fit_basis_timed(C.byref(good), v(16), None, None, v(32), 1 << 30, None, None, v(64)) == -1
     assert lib.kvc_fit_basis_timed(C.byref(good), v(18), None, None, v(32), 1 << 30, None, v(48), v(64)) == -4
+
+
+def test_salience_and_alloc_reject_bad_arguments_without_launching():
+    lib = kvc.lib()
+    v = C.c_void_p
+    out = C.c_size_t()
+    ok = kvc.SalienceIn(2, 1000, 32, 32, 8, 128, 5e5, None, None, None)
+    assert lib.kvc_salience_workspace_bytes(C.byref(ok), C.byref(out)) == 0 and out.value > 0
+    for f, val, want in [("W", 0, -1), ("W", 33, -2), ("n_q_heads", 20, -1), ("n_q_heads", 24, -2),
+                         ("head_dim", 64, -2), ("rope_theta", -1.0, -1)]:
+        bad = kvc.SalienceIn(2, 1000, 32, 32, 8, 128, 5e5, None, None, None)
+        setattr(bad, f, val)
+        assert lib.kvc_salience_workspace_bytes(C.byref(bad), C.byref(out)) == want, f
+    good = kvc.SalienceIn(2, 1000, 32, 32, 8, 128, 5e5, v(16), v(32), v(48))
+    assert lib.kvc_salience(C.byref(ok), v(64), v(80), 1 << 30, None) == -1          # null inputs
+    assert lib.kvc_salience(C.byref(good), v(66), v(80), 1 << 30, None) == -4        # misaligned output
+    assert lib.kvc_salience(C.byref(good), v(64), v(80), 16, None) == -3             # short workspace
+
+    def ain(**kw):
+        d = dict(B=2, max_T=100, ladder=[8, 16, 32, 64], w=[4.0, 2.0, 1.0], mean=20.0, seq=v(16), sal=v(32))
+        d.update(kw)
+        lad = (C.c_int32 * 8)(*(d["ladder"] + [0] * (8 - len(d["ladder"]))))
+        w = (C.c_float * 7)(*(d["w"] + [0.0] * (7 - len(d["w"]))))
+        return kvc.AllocIn(d["B"], d["max_T"], len(d["ladder"]), lad, w, d["mean"], d["seq"], d["sal"])
+    for kw in [dict(ladder=[8]), dict(ladder=[8, 8, 16], w=[1.0, 0.5]), dict(ladder=[8, 300], w=[1.0]),
+               dict(w=[1.0, 2.0, 0.5]), dict(w=[1.0, -0.5, 0.0]), dict(mean=7.0), dict(mean=65.0), dict(sal=None),
+               dict(B=0)]:
+        assert lib.kvc_rank_alloc(C.byref(ain(**kw)), v(48), None) == -1, kw
+    assert lib.kvc_rank_alloc(C.byref(ain(sal=v(33))), v(48), None) == -4
