@@ -517,46 +517,62 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
 
 // Final combine over the context splits and the value basis: one workgroup per (sequence, query head),
 // thread d computes out[d] = (B_v c*)[d] / l* with c* = sum_s 2^(m_s - m*) acc_s, l* = sum_s 2^(m_s - m*) l_s.
+// The kernel is a chain of memory round trips, so its loads are issued together: the value basis row at the
+// start, then every split's (m, l, acc) in groups of up to 16, combined with a running maximum (the same
+// value as a maximum taken first, up to rounding).
 template <int NC>
 __global__ __launch_bounds__(128) void merge_int4_kernel(const float* ws, const uint16_t* wv, float* out, int Hkv,
                                                           int Hq, int rv, int n_splits, int part_stride) {
+  constexpr int NB = NC / 8;  // 16-byte groups of the value basis row
+  constexpr int SG = 16;      // splits loaded together
   __shared__ float cst[NC];
   __shared__ float lst;
   const int bq = blockIdx.x, hq_all = bq % Hq, b = bq / Hq;
   const int h = hq_all / i4::GQ, hq = hq_all % i4::GQ;
   const int tid = threadIdx.x;
+  const uint16_t* row = wv + ((size_t)h * i4::D + tid) * rv;  // B_v row d = tid, rv bf16 values
+  u4 braw[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) braw[i] = 8 * i < rv ? *(const u4*)(row + 8 * i) : u4{0, 0, 0, 0};
   const float* parts = ws + (size_t)(b * Hkv + h) * n_splits * part_stride;
   if (tid < NC) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, parts[(size_t)s * part_stride + hq]);
-    float c = 0.0f, l = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float* ps = parts + (size_t)s * part_stride;
-      const float ms = ps[hq];
-      if (ms == -INFINITY) continue;
-      const float wt = exp2f(ms - mx);
-      c += wt * ps[2 * i4::GQ + hq * NC + tid];
-      l += wt * ps[i4::GQ + hq];
+    float mx = -INFINITY, c = 0.0f, l = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += SG) {
+      float ms[SG], ls[SG], as[SG];
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const bool ok = s0 + u < n_splits;
+        const float* ps = parts + (size_t)(ok ? s0 + u : 0) * part_stride;
+        ms[u] = ok ? ps[hq] : -INFINITY;
+        ls[u] = ok ? ps[i4::GQ + hq] : 0.0f;
+        as[u] = ok ? ps[2 * i4::GQ + hq * NC + tid] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        if (ms[u] == -INFINITY) continue;  // a split with no token
+        const float mn = fmaxf(mx, ms[u]);
+        const float a0 = mx == -INFINITY ? 0.0f : exp2f(mx - mn), a1 = exp2f(ms[u] - mn);
+        c = c * a0 + a1 * as[u];
+        l = l * a0 + a1 * ls[u];
+        mx = mn;
+      }
     }
     cst[tid] = c;
     if (tid == 0) lst = l;
   }
   __syncthreads();
-  const uint16_t* row = wv + ((size_t)h * i4::D + tid) * rv;  // B_v row d = tid, rv bf16 values
   float o = 0.0f;
-  for (int i = 0; i < rv; i += 8) {
-    const u4 raw = *(const u4*)(row + i);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (8 * i >= rv) break;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t w = raw[e >> 1];
-      o += __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * cst[i + e];
+      const uint32_t w = braw[i][e >> 1];
+      o += __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * cst[8 * i + e];
     }
   }
   out[((size_t)b * Hq + hq_all) * i4::D + tid] = o / lst;
 }
-
-// ---------------------------------------------------------------- host side
-
 
 template <int KS, int VS, bool VAR, int STG>
 static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
