@@ -21,9 +21,11 @@
  *     Vr  value residual codes, P x 32 bytes         (residual_bits = 2)
  *     Ks  key residual scale, P x fp16               (residual_bits = 2)
  *     Vs  value residual scale, P x fp16             (residual_bits = 2)
- *   each section padded to a multiple of 16 bytes.  code_bytes(r) = r/2 for
- *   INT4 (coordinate 2j in the low nibble of byte j, 2j+1 in the high
- *   nibble) and 4r for fp32 latents (no Km/Vm then).  A (scale, zero) pair
+ *   each section padded to a multiple of 16 bytes.  code_bytes(r) = r*b/8 for
+ *   b-bit codes (b = 2, 3, 4; code i at bits b*i .. b*i + b - 1 of the slot's
+ *   little-endian bit string, so for INT4 coordinate 2j is the low nibble of
+ *   byte j) and 4r for fp32 latents (no Km/Vm then).  Keys use latent_bits,
+ *   values latent_bits_v (0 = the same).  A (scale, zero) pair
  *   is two fp16 values, scale first.  Residual element i of a slot is bits
  *   2(i%4)..2(i%4)+1 of byte i/4.
  *
@@ -98,18 +100,21 @@ double kvc_ref_bf16_to_f64(uint16_t b) { return (double)bits_f32((uint32_t)b << 
 /* quantizers (fp32, every operation rounded to nearest even, no FMA)       */
 /* ------------------------------------------------------------------------ */
 
-/* INT4 asymmetric min/max quantizer of one group, the form of the BellowsKV
- * page's "Worked Example" (scale = (max - min) / (2^4 - 1), offset = min,
+/* b-bit asymmetric min/max quantizer of one group, the form of the BellowsKV
+ * page's "Worked Example" (scale = (max - min) / (2^bits - 1), offset = min,
  * Python's round = half to even), with the scale and offset stored as fp16
- * and the codes taken against the stored fp16 values. */
-void kvc_ref_quant_int4(const float* x, int n, uint16_t* s16, uint16_t* z16, uint8_t* codes) {
+ * and the codes taken against the stored fp16 values.  INT4 is the main
+ * form; the same page's INT3 and 2-bit variants ("Reading the Retention
+ * Table") use bits 3 and 2. */
+void kvc_ref_quant_intb(const float* x, int n, int bits, uint16_t* s16, uint16_t* z16, uint8_t* codes) {
   float lo = x[0], hi = x[0];
   for (int i = 1; i < n; ++i) {
     if (x[i] < lo) lo = x[i];
     if (x[i] > hi) hi = x[i];
   }
+  float levels = (float)((1 << bits) - 1);
   float range = hi - lo;
-  float s32 = range / 15.0f;
+  float s32 = range / levels;
   *s16 = kvc_ref_f32_to_f16(s32);
   *z16 = kvc_ref_f32_to_f16(lo);
   float s = (float)kvc_ref_f16_to_f64(*s16);
@@ -120,9 +125,13 @@ void kvc_ref_quant_int4(const float* x, int n, uint16_t* s16, uint16_t* z16, uin
     float ratio = diff / s;
     float r = rintf(ratio);
     if (r < 0.0f) r = 0.0f;
-    if (r > 15.0f) r = 15.0f;
+    if (r > levels) r = levels;
     codes[i] = (uint8_t)r;
   }
+}
+
+void kvc_ref_quant_int4(const float* x, int n, uint16_t* s16, uint16_t* z16, uint8_t* codes) {
+  kvc_ref_quant_intb(x, n, 4, s16, z16, codes);
 }
 
 /* 2-bit symmetric quantizer of a rotated residual vector (JoLT's rotated
@@ -188,6 +197,11 @@ void kvc_ref_quant_int4_n(const float* x, int64_t n_groups, int n, uint16_t* s16
   for (int64_t g = 0; g < n_groups; ++g) kvc_ref_quant_int4(x + g * n, n, s16 + g, z16 + g, codes + g * n);
 }
 
+void kvc_ref_quant_intb_n(const float* x, int64_t n_groups, int n, int bits, uint16_t* s16, uint16_t* z16,
+                          uint8_t* codes) {
+  for (int64_t g = 0; g < n_groups; ++g) kvc_ref_quant_intb(x + g * n, n, bits, s16 + g, z16 + g, codes + g * n);
+}
+
 void kvc_ref_quant_res2_n(const float* y, int64_t n_rows, int n, uint16_t* s16, uint8_t* codes) {
   for (int64_t r = 0; r < n_rows; ++r) kvc_ref_quant_res2(y + r * n, n, s16 + r, codes + r * n);
 }
@@ -198,25 +212,41 @@ void kvc_ref_quant_res2_n(const float* y, int64_t n_rows, int n, uint16_t* s16, 
 
 static int64_t pad16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
-static int code_bytes(const kvc_ref_layout* L, int r) { return L->latent_bits == 4 ? r / 2 : 4 * r; }
-static int meta_bytes(const kvc_ref_layout* L, int r) { return L->latent_bits == 4 ? 4 * ceil_div(r, L->group) : 0; }
+/* bits of the key (which = 0) or value (which = 1) latent */
+static int lat_bits(const kvc_ref_layout* L, int which) {
+  return which && L->latent_bits_v ? L->latent_bits_v : L->latent_bits;
+}
+static int code_bytes(const kvc_ref_layout* L, int which, int r) {
+  int b = lat_bits(L, which);
+  return b == 32 ? 4 * r : r * b / 8;
+}
+static int meta_bytes(const kvc_ref_layout* L, int which, int r) {
+  return lat_bits(L, which) == 32 ? 0 : 4 * ceil_div(r, L->group);
+}
+static int quant_bits_ok(int b) { return b == 2 || b == 3 || b == 4; }
 
 int kvc_ref_layout_check(const kvc_ref_layout* L) {
   if (!L) return KVC_REF_EINVAL;
   if (L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->n_q_heads % L->n_kv_heads) return KVC_REF_EINVAL;
   if (L->head_dim <= 0 || L->head_dim % 2) return KVC_REF_EINVAL;
   if (L->page_size <= 0 || L->page_size > 256) return KVC_REF_EINVAL;
-  if (L->latent_bits != 4 && L->latent_bits != 32) return KVC_REF_EINVAL;
+  {
+    int bk = L->latent_bits, bv = lat_bits(L, 1);
+    if (L->latent_bits_v != 0 && !quant_bits_ok(L->latent_bits_v) && L->latent_bits_v != 32) return KVC_REF_EINVAL;
+    if (!(quant_bits_ok(bk) && quant_bits_ok(bv)) && !(bk == 32 && bv == 32)) return KVC_REF_EINVAL;
+  }
   if (L->r_k_cap <= 0 || L->r_v_cap <= 0 || L->r_k_cap % 8 || L->r_v_cap % 8) return KVC_REF_EINVAL;
-  if (L->latent_bits == 4 && (L->group <= 0 || L->group % 8)) return KVC_REF_EINVAL;
+  if (L->latent_bits != 32 && (L->group <= 0 || L->group % 8)) return KVC_REF_EINVAL;
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_REF_EINVAL;
   if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_REF_EINVAL;
   if (L->shared) {
-    if (L->n_layers <= 0 || L->latent_bits != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap) return KVC_REF_EINVAL;
+    if (L->n_layers <= 0 || L->latent_bits != 4 || lat_bits(L, 1) != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
+      return KVC_REF_EINVAL;
   } else if (L->n_layers != 1) {
     return KVC_REF_EINVAL;
   }
-  if (L->variable_rank && (L->latent_bits != 4 || L->r_k_cap != L->r_v_cap)) return KVC_REF_EINVAL;
+  if (L->variable_rank && (L->latent_bits == 32 || lat_bits(L, 1) != L->latent_bits || L->r_k_cap != L->r_v_cap))
+    return KVC_REF_EINVAL;
   if (L->r_k_cap > 1024 || L->r_v_cap > 1024) return KVC_REF_EINVAL;
   if (L->variable_rank && L->page_size * L->r_k_cap > 65535) return KVC_REF_EINVAL;
   if (L->rope_theta < 0.0) return KVC_REF_EINVAL;
@@ -250,8 +280,8 @@ int64_t kvc_ref_page_bytes_uniform(const kvc_ref_layout* L) {
   if (kvc_ref_layout_check(L)) return KVC_REF_EINVAL;
   int64_t P = L->page_size;
   if (L->shared) return pad16(P * L->r_k_cap / 2) + pad16(P * 4 * ceil_div(L->r_k_cap, L->group));
-  sections S = head_sections(L, (int)(P * code_bytes(L, L->r_k_cap)), (int)(P * code_bytes(L, L->r_v_cap)),
-                             (int)(P * meta_bytes(L, L->r_k_cap)), (int)(P * meta_bytes(L, L->r_v_cap)));
+  sections S = head_sections(L, (int)(P * code_bytes(L, 0, L->r_k_cap)), (int)(P * code_bytes(L, 1, L->r_v_cap)),
+                             (int)(P * meta_bytes(L, 0, L->r_k_cap)), (int)(P * meta_bytes(L, 1, L->r_v_cap)));
   return S.total * L->n_kv_heads;
 }
 
@@ -270,8 +300,8 @@ static void page_sums(const kvc_ref_layout* L, const uint8_t* ranks_of_page, int
   for (int s = 0; s < L->page_size; ++s) {
     int rk = L->variable_rank ? ranks_of_page[s] : L->r_k_cap;
     int rv = L->variable_rank ? ranks_of_page[s] : L->r_v_cap;
-    *ck += code_bytes(L, rk); *cv += code_bytes(L, rv);
-    *mk += meta_bytes(L, rk); *mv += meta_bytes(L, rv);
+    *ck += code_bytes(L, 0, rk); *cv += code_bytes(L, 1, rv);
+    *mk += meta_bytes(L, 0, rk); *mv += meta_bytes(L, 1, rv);
   }
 }
 
@@ -286,15 +316,15 @@ static slot_view locate(const kvc_ref_layout* L, const uint8_t* pool, const int6
     int tot_r = (int)(off[P] & 0xffffu), tot_g = (int)(off[P] >> 16);
     int pre_r = (int)(off[slot] & 0xffffu), pre_g = (int)(off[slot] >> 16);
     v.rk = v.rv = tok_rank[(size_t)page * P + slot];
-    ck = cv = tot_r / 2; mk = mv = 4 * tot_g;
-    pre_code_k = pre_code_v = pre_r / 2;
+    ck = cv = tot_r * L->latent_bits / 8; mk = mv = 4 * tot_g;  /* K and V share the bits (variable rank) */
+    pre_code_k = pre_code_v = pre_r * L->latent_bits / 8;
     pre_meta_k = pre_meta_v = 4 * pre_g;
   } else {
     v.rk = L->r_k_cap; v.rv = L->r_v_cap;
-    ck = P * code_bytes(L, v.rk); cv = P * code_bytes(L, v.rv);
-    mk = P * meta_bytes(L, v.rk); mv = P * meta_bytes(L, v.rv);
-    pre_code_k = slot * code_bytes(L, v.rk); pre_code_v = slot * code_bytes(L, v.rv);
-    pre_meta_k = slot * meta_bytes(L, v.rk); pre_meta_v = slot * meta_bytes(L, v.rv);
+    ck = P * code_bytes(L, 0, v.rk); cv = P * code_bytes(L, 1, v.rv);
+    mk = P * meta_bytes(L, 0, v.rk); mv = P * meta_bytes(L, 1, v.rv);
+    pre_code_k = slot * code_bytes(L, 0, v.rk); pre_code_v = slot * code_bytes(L, 1, v.rv);
+    pre_meta_k = slot * meta_bytes(L, 0, v.rk); pre_meta_v = slot * meta_bytes(L, 1, v.rv);
   }
   sections S = head_sections(L, ck, cv, mk, mv);
   const uint8_t* hb = rec + (int64_t)head * S.total;
@@ -313,9 +343,11 @@ static void wr16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] = (u
 /* compression                                                              */
 /* ------------------------------------------------------------------------ */
 
-/* quantize the first r coordinates of x in groups of G, write codes + pairs */
-static void pack_latent(const kvc_ref_layout* L, const float* x, int r, uint8_t* codes, uint8_t* meta) {
-  if (L->latent_bits == 32) {
+/* quantize the first r coordinates of x in groups of G with `bits`-bit codes, write codes + pairs; code i
+ * occupies bits bits*i .. bits*i + bits - 1 of the slot's little-endian bit string (for INT4: coordinate 2j
+ * in the low nibble of byte j) */
+static void pack_latent(const kvc_ref_layout* L, int bits, const float* x, int r, uint8_t* codes, uint8_t* meta) {
+  if (bits == 32) {
     memcpy(codes, x, (size_t)4 * r);
     return;
   }
@@ -324,11 +356,14 @@ static void pack_latent(const kvc_ref_layout* L, const float* x, int r, uint8_t*
   for (int g0 = 0, gi = 0; g0 < r; g0 += G, ++gi) {
     int n = r - g0 < G ? r - g0 : G;
     uint16_t s16, z16;
-    kvc_ref_quant_int4(x + g0, n, &s16, &z16, q + g0);
+    kvc_ref_quant_intb(x + g0, n, bits, &s16, &z16, q + g0);
     wr16(meta + 4 * gi, s16);
     wr16(meta + 4 * gi + 2, z16);
   }
-  for (int i = 0; i < r; i += 2) codes[i / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+  memset(codes, 0, (size_t)r * bits / 8);
+  for (int i = 0; i < r; ++i)
+    for (int k = 0; k < bits; ++k)
+      if ((q[i] >> k) & 1) codes[(bits * i + k) / 8] |= (uint8_t)(1u << ((bits * i + k) % 8));
 }
 
 static void pack_residual(const float* y, int n, uint8_t* codes, uint8_t* scale) {
@@ -409,14 +444,14 @@ int64_t kvc_ref_compress(const kvc_ref_layout* L, int B, int max_T, int max_bloc
         uint8_t* rec = pool + page_off[p];
         uint8_t* codes = rec + (int64_t)s * (lat / 2);
         uint8_t* meta = rec + pad16((int64_t)P * lat / 2) + (int64_t)s * 4 * ceil_div(lat, G);
-        pack_latent(L, lat_k + ((size_t)b * max_T + t) * lat, lat, codes, meta);
+        pack_latent(L, 4, lat_k + ((size_t)b * max_T + t) * lat, lat, codes, meta);
         continue;
       }
       for (int h = 0; h < Hkv; ++h) {
         slot_view v = locate(L, pool, page_off, tok_rank, tok_off, p, s, h);
         size_t tk = (((size_t)b * max_T + t) * Hkv + h);
-        pack_latent(L, lat_k + tk * rk, v.rk, (uint8_t*)v.kc, (uint8_t*)v.km);
-        pack_latent(L, lat_v + tk * rv, v.rv, (uint8_t*)v.vc, (uint8_t*)v.vm);
+        pack_latent(L, lat_bits(L, 0), lat_k + tk * rk, v.rk, (uint8_t*)v.kc, (uint8_t*)v.km);
+        pack_latent(L, lat_bits(L, 1), lat_v + tk * rv, v.rv, (uint8_t*)v.vc, (uint8_t*)v.vm);
         if (L->residual_bits) {
           int d = L->head_dim;
           pack_residual(res_k + tk * d, d, (uint8_t*)v.kr, (uint8_t*)v.ks);
@@ -477,14 +512,16 @@ int kvc_ref_project(const kvc_ref_layout* L, int B, int max_T, const int32_t* se
 
 /* dequantized latent of one slot: c_i = q_i * scale_g + zero_g, g = i / G;
  * coordinates at or beyond the slot's rank are zero */
-static void unpack_latent(const kvc_ref_layout* L, const uint8_t* codes, const uint8_t* meta, int r, int rcap, double* c) {
+static void unpack_latent(const kvc_ref_layout* L, int bits, const uint8_t* codes, const uint8_t* meta, int r, int rcap,
+                          double* c) {
   for (int i = 0; i < rcap; ++i) c[i] = 0.0;
-  if (L->latent_bits == 32) {
+  if (bits == 32) {
     for (int i = 0; i < r; ++i) { float f; memcpy(&f, codes + 4 * i, 4); c[i] = f; }
     return;
   }
   for (int i = 0; i < r; ++i) {
-    int q = (codes[i / 2] >> (4 * (i % 2))) & 15;
+    int q = 0;
+    for (int k = 0; k < bits; ++k) q |= ((codes[(bits * i + k) / 8] >> ((bits * i + k) % 8)) & 1) << k;
     int g = i / L->group;
     double s = kvc_ref_f16_to_f64(rd16(meta + 4 * g)), z = kvc_ref_f16_to_f64(rd16(meta + 4 * g + 2));
     c[i] = q * s + z;
@@ -536,13 +573,13 @@ static void rebuild_token(const kvc_ref_layout* L, int which, int layer, int b, 
     const uint8_t* rec = pool + page_off[p];
     const uint8_t* codes = rec + (int64_t)s * (lat / 2);
     const uint8_t* meta = rec + pad16((int64_t)P * lat / 2) + (int64_t)s * 4 * ceil_div(lat, L->group);
-    unpack_latent(L, codes, meta, lat, lat, c);
+    unpack_latent(L, 4, codes, meta, lat, lat, c);
     rebuild_shared(w + (size_t)layer * lat * Hkv * d, lat, Hkv * d, h * d, d, c, x);
     return;
   }
   slot_view v = locate(L, pool, page_off, tok_rank, tok_off, p, s, h);
   int rcap = which ? L->r_v_cap : L->r_k_cap, r = which ? v.rv : v.rk;
-  unpack_latent(L, which ? v.vc : v.kc, which ? v.vm : v.km, r, rcap, c);
+  unpack_latent(L, lat_bits(L, which), which ? v.vc : v.kc, which ? v.vm : v.km, r, rcap, c);
   rebuild_per_head(w + (size_t)h * d * rcap, d, rcap, c, r, x);
   if (L->residual_bits) {
     unpack_residual(which ? v.vr : v.kr, which ? v.vs : v.ks, d, e);

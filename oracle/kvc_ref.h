@@ -44,11 +44,12 @@ typedef struct {
   int r_k_cap;       /* key rank (cap when variable_rank); shared: latent dim  */
   int r_v_cap;       /* value rank (cap); shared: equal to r_k_cap             */
   int group;         /* quantization group size along the latent axis          */
-  int latent_bits;   /* 4 (INT4 codes + fp16 scale/zero) or 32 (fp32 latents)  */
+  int latent_bits;   /* key latent: 2, 3, 4 (codes + fp16 scale/zero) or 32 (fp32) */
   int residual_bits; /* 0 or 2 (Hadamard-rotated 2-bit residual, head_dim 128) */
   int page_size;     /* tokens per page                                        */
   int variable_rank; /* 1: one rank per token, shared by K, V and all heads    */
   double rope_theta; /* RoPE base; 0 switches RoPE off                         */
+  int latent_bits_v; /* value latent bits; 0 = latent_bits                     */
 } kvc_ref_layout;
 
 /* status codes: 0 ok, negative = invalid input */
@@ -61,12 +62,16 @@ uint16_t kvc_ref_f32_to_f16(float x);     /* IEEE binary16, round to nearest eve
 double   kvc_ref_f16_to_f64(uint16_t h);
 double   kvc_ref_bf16_to_f64(uint16_t b);
 void kvc_ref_quant_int4(const float* x, int n, uint16_t* s16, uint16_t* z16, uint8_t* codes);
+/* the same quantizer with 2^bits - 1 levels, bits 2..4 */
+void kvc_ref_quant_intb(const float* x, int n, int bits, uint16_t* s16, uint16_t* z16, uint8_t* codes);
 void kvc_ref_quant_res2(const float* y, int n, uint16_t* s16, uint8_t* codes);
 void kvc_ref_hadamard(int n, double* H);  /* normalized Sylvester matrix, row-major */
 void kvc_ref_rope(double* x, int d, double pos, double theta);
 /* array forms of the above, for tests */
 void kvc_ref_f32_to_f16_n(const float* x, int64_t n, uint16_t* out);
 void kvc_ref_quant_int4_n(const float* x, int64_t n_groups, int n, uint16_t* s16, uint16_t* z16, uint8_t* codes);
+void kvc_ref_quant_intb_n(const float* x, int64_t n_groups, int n, int bits, uint16_t* s16, uint16_t* z16,
+                          uint8_t* codes);
 void kvc_ref_quant_res2_n(const float* y, int64_t n_rows, int n, uint16_t* s16, uint8_t* codes);
 
 /* --- compression (from fp32 latents / rotated residuals) ---

@@ -29,6 +29,7 @@ def lib():
         L.kvc_ref_bf16_to_f64.argtypes = [C.c_uint16]; L.kvc_ref_bf16_to_f64.restype = f64
         L.kvc_ref_f32_to_f16_n.argtypes = [P, i64, P]; L.kvc_ref_f32_to_f16_n.restype = None
         L.kvc_ref_quant_int4_n.argtypes = [P, i64, C.c_int, P, P, P]; L.kvc_ref_quant_int4_n.restype = None
+        L.kvc_ref_quant_intb_n.argtypes = [P, i64, C.c_int, C.c_int, P, P, P]; L.kvc_ref_quant_intb_n.restype = None
         L.kvc_ref_quant_res2_n.argtypes = [P, i64, C.c_int, P, P]; L.kvc_ref_quant_res2_n.restype = None
         L.kvc_ref_hadamard.argtypes = [C.c_int, P]; L.kvc_ref_hadamard.restype = None
         L.kvc_ref_rope.argtypes = [P, C.c_int, f64, f64]; L.kvc_ref_rope.restype = None
@@ -48,7 +49,7 @@ def lib():
 class _Layout(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("n_q_heads", "n_kv_heads", "head_dim", "shared", "n_layers", "r_k_cap",
                                        "r_v_cap", "group", "latent_bits", "residual_bits", "page_size",
-                                       "variable_rank")] + [("rope_theta", C.c_double)]
+                                       "variable_rank")] + [("rope_theta", C.c_double), ("latent_bits_v", C.c_int)]
 
 
 @dataclass
@@ -66,11 +67,12 @@ class Layout:
     shared: int = 0
     n_layers: int = 1
     rope_theta: float = 0.0
+    latent_bits_v: int = 0
 
     def c(self):
         return _Layout(self.n_q_heads, self.n_kv_heads, self.head_dim, self.shared, self.n_layers, self.r_k_cap,
                        self.r_v_cap, self.group, self.latent_bits, self.residual_bits, self.page_size,
-                       self.variable_rank, self.rope_theta)
+                       self.variable_rank, self.rope_theta, self.latent_bits_v)
 
 
 def _p(a):
@@ -110,6 +112,15 @@ def quant_int4(x):
     ng, n = x.shape
     s = np.empty(ng, np.uint16); z = np.empty(ng, np.uint16); q = np.empty((ng, n), np.uint8)
     lib().kvc_ref_quant_int4_n(_p(x), ng, n, _p(s), _p(z), _p(q))
+    return s, z, q
+
+
+def quant_intb(x, bits):
+    """x [n_groups, n] fp32 -> (s16, z16, codes) of the bits-bit quantizer (bits 2..4)."""
+    x = _c(x, np.float32)
+    ng, n = x.shape
+    s = np.empty(ng, np.uint16); z = np.empty(ng, np.uint16); q = np.empty((ng, n), np.uint8)
+    lib().kvc_ref_quant_intb_n(_p(x), ng, n, int(bits), _p(s), _p(z), _p(q))
     return s, z, q
 
 

@@ -95,12 +95,14 @@ def test_identical_keys_average_the_values():
         assert np.allclose(out[0, hq], v[:, hq // 4].mean(0), atol=1e-13)
 
 
-@pytest.mark.parametrize("ranks", [(64,), (8, 16, 32, 64)])
-def test_int4_latents_dequantize_as_scale_times_code_plus_zero(ranks):
-    # identity bases with INT4 latents: every key/value is the dequantized latent q * scale + zero of its
+@pytest.mark.parametrize("ranks,bits", [((64,), (4, 0)), ((8, 16, 32, 64), (4, 0)), ((64,), (3, 0)), ((64,), (3, 2)),
+                                        ((8, 16, 32, 64), (2, 0))])
+def test_int4_latents_dequantize_as_scale_times_code_plus_zero(ranks, bits):
+    # identity bases with b-bit latents: every key/value is the dequantized latent q * scale + zero of its
     # group (zero beyond the token's rank), computed here from the quantizer's outputs
     w = synth.Workload("t", B=2, T=333, n_q_heads=8, n_kv_heads=2, head_dim=64, r_k=64, r_v=64, group=32,
-                       latent_bits=4, page_size=64, shuffle_pages=True, rope_theta=500000.0, seed=21,
+                       latent_bits=bits[0], latent_bits_v=bits[1], page_size=64, shuffle_pages=True,
+                       rope_theta=500000.0, seed=21,
                        variable_rank=len(ranks) > 1, rank_choices=ranks, rank_probs=(0.4, 0.3, 0.2, 0.1)[-len(ranks):])
     inp = identity_bases(synth.make_inputs(w, seq_len=[333, 200]), w)
     out = oracle_decode(w, inp, oracle_cache(w, inp))
@@ -116,7 +118,8 @@ def test_int4_latents_dequantize_as_scale_times_code_plus_zero(ranks):
                     r = int(inp["ranks"][b, t]) if w.variable_rank else 64
                     for g0 in range(0, r, 32):
                         n = min(32, r - g0)
-                        S, Z, Q = ref.quant_int4(x[t, g0: g0 + n][None])
+                        nb = bits[0] if name == "lat_k" else (bits[1] or bits[0])
+                        S, Z, Q = ref.quant_intb(x[t, g0: g0 + n][None], nb)
                         deq[t, g0: g0 + n] = (Q[0] * S.view(np.float16).astype(np.float64)[0]
                                               + Z.view(np.float16).astype(np.float64)[0])
                 kv.append(deq)
@@ -236,9 +239,12 @@ def test_dense_oracle_is_textbook_attention():
 # ---------------------------------------------------------------- compressor: layout and byte accounting
 
 def parse_pool_per_head(w, cache, b, t, h, bt):
-    """Independent reader of one slot's INT4 codes and pairs, from the layout description."""
+    """Independent reader of one slot's codes and pairs, from the layout description: b-bit codes are the
+    slot's little-endian bit string (numpy's unpackbits), code i at bits b*i .."""
     pool, page_off, tok_rank, tok_off = cache
     P = w.page_size
+    bk = w.latent_bits
+    bv = w.latent_bits_v or w.latent_bits
     p = int(bt[b, t // P]); s = t % P
     rec = int(page_off[p])
     pad = lambda x: (x + 15) // 16 * 16
@@ -246,32 +252,35 @@ def parse_pool_per_head(w, cache, b, t, h, bt):
         tot_r, tot_g = int(tok_off[p, P]) & 0xFFFF, int(tok_off[p, P]) >> 16
         pre_r, pre_g = int(tok_off[p, s]) & 0xFFFF, int(tok_off[p, s]) >> 16
         rk = rv = int(tok_rank[p, s])
-        ck = cv = tot_r // 2; mk = mv = 4 * tot_g
-        prk = prv = pre_r // 2; pmk = pmv = 4 * pre_g
+        ck = cv = tot_r * bk // 8; mk = mv = 4 * tot_g
+        prk = prv = pre_r * bk // 8; pmk = pmv = 4 * pre_g
     else:
         rk, rv = w.r_k, w.r_v
-        ck, cv = P * rk // 2, P * rv // 2
+        ck, cv = P * rk * bk // 8, P * rv * bv // 8
         mk, mv = P * 4 * -(-rk // w.group), P * 4 * -(-rv // w.group)
-        prk, prv = s * rk // 2, s * rv // 2
+        prk, prv = s * rk * bk // 8, s * rv * bv // 8
         pmk, pmv = s * 4 * -(-rk // w.group), s * 4 * -(-rv // w.group)
     hb = pad(ck) + pad(cv) + pad(mk) + pad(mv)
     if w.residual_bits:
         hb += 2 * pad(P * 32) + 2 * pad(P * 2)
     base = rec + h * hb
     out = {}
-    for name, r, sec, pre, msec, mpre in (("k", rk, 0, prk, pad(ck) + pad(cv), pmk),
-                                          ("v", rv, pad(ck), prv, pad(ck) + pad(cv) + pad(mk), pmv)):
-        by = pool[base + sec + pre: base + sec + pre + r // 2]
-        codes = np.stack([by & 15, by >> 4], 1).reshape(-1)
+    for name, r, nb, sec, pre, msec, mpre in (("k", rk, bk, 0, prk, pad(ck) + pad(cv), pmk),
+                                              ("v", rv, bv, pad(ck), prv, pad(ck) + pad(cv) + pad(mk), pmv)):
+        by = pool[base + sec + pre: base + sec + pre + r * nb // 8]
+        bitstr = np.unpackbits(by, bitorder="little")[: r * nb].reshape(r, nb)
+        codes = (bitstr.astype(np.int64) << np.arange(nb)).sum(1)
         ng = -(-r // w.group)
         meta = pool[base + msec + mpre: base + msec + mpre + 4 * ng].view(np.uint16).reshape(ng, 2)
         out[name] = (codes, meta)
     return out
 
 
-@pytest.mark.parametrize("name", ["llama8b_layer_8k", "varrank_paged_32k"])
-def test_pool_holds_the_quantizer_outputs(name):
-    w = synth.WORKLOADS[name].scaled(B=2, T=700, page_size=128)
+@pytest.mark.parametrize("name,bits", [("llama8b_layer_8k", (4, 0)), ("varrank_paged_32k", (4, 0)),
+                                       ("llama8b_layer_8k", (3, 0)), ("llama8b_layer_8k", (2, 0)),
+                                       ("llama8b_layer_8k", (3, 2)), ("varrank_paged_32k", (3, 0))])
+def test_pool_holds_the_quantizer_outputs(name, bits):
+    w = synth.WORKLOADS[name].scaled(B=2, T=700, page_size=128, latent_bits=bits[0], latent_bits_v=bits[1])
     inp = synth.make_inputs(w, seq_len=[700, 450])
     cache = oracle_cache(w, inp)
     bt = np_any(inp["block_table"])
@@ -283,7 +292,8 @@ def test_pool_holds_the_quantizer_outputs(name):
             codes, meta = got[kv]
             for g0 in range(0, r, w.group):
                 n = min(w.group, r - g0)
-                S, Z, Q = ref.quant_int4(lat[kv][b, t, h, g0: g0 + n][None])
+                nb = w.latent_bits if kv == "k" else (w.latent_bits_v or w.latent_bits)
+                S, Z, Q = ref.quant_intb(lat[kv][b, t, h, g0: g0 + n][None], nb)
                 assert np.array_equal(codes[g0: g0 + n], Q[0])
                 assert meta[g0 // w.group, 0] == S[0] and meta[g0 // w.group, 1] == Z[0]
 

@@ -93,6 +93,31 @@ def test_int4_brute_force_nearest_level_and_bounds():
     assert np.all(err <= 0.5 * s64[:, None] + slack[:, None] + 1e-12)
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_low_bit_brute_force_nearest_level_and_bounds(bits):
+    # the INT3 and 2-bit variants of the same min/max quantizer ("BellowsKV Architecture ...", "Reading the
+    # Retention Table"): 2^bits - 1 steps over the group's range
+    L = (1 << bits) - 1
+    x = (RNG.standard_normal((20000, 32)) * RNG.uniform(0.01, 3.0, (20000, 1))).astype(np.float32)
+    S, Z, Q = ref.quant_intb(x, bits)
+    s64 = S.view(np.float16).astype(np.float64)
+    z64 = Z.view(np.float16).astype(np.float64)
+    levels = np.arange(L + 1)[None, None, :] * s64[:, None, None] + z64[:, None, None]
+    dist = np.abs(x.astype(np.float64)[:, :, None] - levels)
+    mism = dist.argmin(-1) != Q
+    if mism.any():
+        d_code = np.take_along_axis(dist, Q[..., None].astype(np.int64), -1)[..., 0]
+        assert np.all((d_code - dist.min(-1))[mism] <= 1e-6 * s64[:, None].repeat(32, 1)[mism])
+    assert Q.max() <= L
+    assert np.all(Q[np.arange(len(x)), x.argmin(1)] == 0)
+    assert np.all(Q[np.arange(len(x)), x.argmax(1)] == L)
+    # the scale is the fp16 of range / (2^bits - 1)
+    rng = x.max(1) - x.min(1)
+    assert np.array_equal(S, ref.f32_to_f16(rng / np.float32(L)))
+    # 4 bits through the general form is the INT4 quantizer
+    assert all(np.array_equal(a, b) for a, b in zip(ref.quant_intb(x[:500], 4), ref.quant_int4(x[:500])))
+
+
 def test_int4_requantize_round_trip():
     # quantizing the dequantized group again returns the same codes and the same fp16 scale/zero
     x = (RNG.standard_normal((50000, 32)) * (np.arange(1, 33) ** -0.7)).astype(np.float32)
