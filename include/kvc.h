@@ -45,8 +45,10 @@
  *     Kc key codes   | Vc value codes | Km key (scale, zero) | Vm value pairs
  *     [Kr key residual codes P x 32 B | Vr | Ks key residual scale P x fp16 | Vs]
  *  each padded to a multiple of 16 bytes.  Codes of a slot are its rank r
- *  INT4 values, coordinate 2j in the low nibble of byte j (r/2 bytes; fp32
- *  latents: 4r bytes and no pairs); pairs are (fp16 scale, fp16 zero), one
+ *  b-bit values (b = latent_bits for keys, latent_bits_v for values; 2, 3 or
+ *  4), code i at bits b*i .. b*i + b - 1 of the slot's little-endian bit
+ *  string, r*b/8 bytes (INT4: coordinate 2j in the low nibble of byte j;
+ *  fp32 latents: 4r bytes and no pairs); pairs are (fp16 scale, fp16 zero), one
  *  per group of `group` coordinates, ceil(r/group) per slot; residual
  *  element i is bits 2(i%4).. of byte i/4, value (code - 1.5) * scale.
  *  Slots follow one another in slot order inside each section.  Uniform
@@ -67,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -90,11 +92,12 @@ typedef struct {
   int32_t r_k_cap;        /* key rank (cap with variable_rank); shared: latent dimension   */
   int32_t r_v_cap;        /* value rank (cap); shared: equal to r_k_cap                    */
   int32_t group;          /* quantization group along the latent axis (multiple of 16)     */
-  int32_t latent_bits;    /* 4: INT4 codes + fp16 scale/zero; 32: fp32 latents             */
+  int32_t latent_bits;    /* key latent: 2, 3, 4 (codes + fp16 scale/zero) or 32 (fp32)   */
   int32_t residual_bits;  /* 0 or 2 (Hadamard-rotated residual; head_dim 128, per-head)    */
   int32_t page_size;      /* tokens per page, a multiple of 32, at most 256                */
   int32_t variable_rank;  /* 1: per-token rank in tok_rank / tok_off                       */
   double rope_theta;      /* RoPE base (rotate-half pairs (j, j + d/2)); 0 = no RoPE       */
+  int32_t latent_bits_v;  /* value latent bits, 2..4 or 32; 0 = latent_bits (ABI version 2)  */
 } kvc_layout;
 
 /* A compressed cache in device memory (caller-allocated). */

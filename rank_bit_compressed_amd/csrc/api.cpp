@@ -45,24 +45,30 @@ static kvc_status check_layout(const kvc_layout* L) {
   if (L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->n_q_heads % L->n_kv_heads) return KVC_ERR_INVALID_ARG;
   if (L->head_dim <= 0 || L->head_dim % 2) return KVC_ERR_INVALID_ARG;
   if (L->page_size <= 0 || L->page_size > 256) return KVC_ERR_INVALID_ARG;
-  if (L->latent_bits != 4 && L->latent_bits != 32) return KVC_ERR_INVALID_ARG;
+  {
+    auto qb = [](int b) { return b == 2 || b == 3 || b == 4; };
+    const int bk = L->latent_bits, bv = L->latent_bits_v ? L->latent_bits_v : L->latent_bits;
+    if (L->latent_bits_v != 0 && !qb(L->latent_bits_v) && L->latent_bits_v != 32) return KVC_ERR_INVALID_ARG;
+    if (!(qb(bk) && qb(bv)) && !(bk == 32 && bv == 32)) return KVC_ERR_INVALID_ARG;
+  }
   if (L->r_k_cap <= 0 || L->r_v_cap <= 0 || L->r_k_cap % 8 || L->r_v_cap % 8) return KVC_ERR_INVALID_ARG;
   if (L->r_k_cap > 1024 || L->r_v_cap > 1024) return KVC_ERR_INVALID_ARG;
-  if (L->latent_bits == 4 && (L->group <= 0 || L->group % 8)) return KVC_ERR_INVALID_ARG;
+  if (L->latent_bits != 32 && (L->group <= 0 || L->group % 8)) return KVC_ERR_INVALID_ARG;
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_ERR_INVALID_ARG;
   if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_ERR_INVALID_ARG;
   if (L->shared) {
-    if (L->n_layers <= 0 || L->latent_bits != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
+    if (L->n_layers <= 0 || lat_bits_k(*L) != 4 || lat_bits_v(*L) != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
       return KVC_ERR_INVALID_ARG;
   } else if (L->n_layers != 1) {
     return KVC_ERR_INVALID_ARG;
   }
-  if (L->variable_rank && (L->latent_bits != 4 || L->r_k_cap != L->r_v_cap)) return KVC_ERR_INVALID_ARG;
+  if (L->variable_rank && (L->latent_bits == 32 || lat_bits_v(*L) != L->latent_bits || L->r_k_cap != L->r_v_cap))
+    return KVC_ERR_INVALID_ARG;
   if (L->variable_rank && L->page_size * L->r_k_cap > 65535) return KVC_ERR_INVALID_ARG;
   if (!(L->rope_theta >= 0.0) || std::isinf(L->rope_theta)) return KVC_ERR_INVALID_ARG;
   // what the gfx950 kernels implement
   if (L->page_size % 32) return KVC_ERR_UNSUPPORTED;
-  if (L->latent_bits == 4 && L->group % 16) return KVC_ERR_UNSUPPORTED;
+  if (L->latent_bits != 32 && L->group % 16) return KVC_ERR_UNSUPPORTED;
   if (L->shared ? !shared_supported(*L) : !head_supported(*L)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }

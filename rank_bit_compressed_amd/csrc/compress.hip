@@ -40,7 +40,7 @@ __global__ void scatter_ranks_kernel(const int32_t* block_table, const int32_t* 
 // One workgroup per page: tok_off prefix over slots and the page record size (into page_off).
 __global__ __launch_bounds__(256) void page_prefix_kernel(const uint8_t* tok_rank, uint32_t* tok_off,
                                                           int64_t* page_off, int P, int G, int Hkv, int residual,
-                                                          int d) {
+                                                          int d, int bits) {
   __shared__ uint32_t sr[256], sg[256];
   const int page = blockIdx.x, s = threadIdx.x;
   const uint32_t r = s < P ? tok_rank[(size_t)page * P + s] : 0u;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void page_prefix_kernel(const uint8_t* tok_ran
   if (s < P) tok_off[(size_t)page * (P + 1) + s] = (sr[s] - r) | ((sg[s] - gcount) << 16);
   if (s == P - 1) {
     tok_off[(size_t)page * (P + 1) + P] = sr[s] | (sg[s] << 16);
-    const int64_t cb = sr[s] / 2, mb = 4 * (int64_t)sg[s];
+    const int64_t cb = (int64_t)sr[s] * bits / 8, mb = 4 * (int64_t)sg[s];
     page_off[page] = head_sections(cb, cb, mb, mb, P, d, residual).hb * Hkv;
   }
 }
@@ -108,7 +108,7 @@ struct PackArgs {
   const int64_t* page_off;
   const uint8_t* tok_rank;
   const uint32_t* tok_off;
-  int B, max_T, max_blocks, P, Hkv, d, rk, rv, G, latent_bits, residual, variable_rank, shared;
+  int B, max_T, max_blocks, P, Hkv, d, rk, rv, G, latent_bits, latent_bits_v, residual, variable_rank, shared;
   HeadSections S_uniform;
 };
 
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(PackArgs a, int groups
   const float* src;
   uint8_t* codes;
   uint8_t* meta;
-  int r;
+  int r, bits = a.latent_bits;
   if (a.shared) {
     r = a.rk;
     src = a.lat_k + ((size_t)b * a.max_T + t) * r;
@@ -136,27 +136,28 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(PackArgs a, int groups
   } else {
     const int h = item >> 1, which = item & 1;
     const int rcap = which ? a.rv : a.rk;
+    bits = which ? a.latent_bits_v : a.latent_bits;
     HeadSections S;
     int64_t co, mo;
     if (a.variable_rank) {
       const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P], o = a.tok_off[(size_t)page * (P + 1) + slot];
-      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * bits / 8, mb = 4 * (int64_t)(tot >> 16);  // K, V share bits
       S = head_sections(cb, cb, mb, mb, P, a.d, a.residual);
       r = a.tok_rank[(size_t)page * P + slot];
-      co = (o & 0xFFFFu) / 2;
+      co = (int64_t)(o & 0xFFFFu) * bits / 8;
       mo = 4 * (int64_t)(o >> 16);
     } else {
       S = a.S_uniform;
       r = rcap;
-      co = (int64_t)slot * slot_code_bytes(a.latent_bits, r);
-      mo = (int64_t)slot * slot_meta_bytes(a.latent_bits, r, a.G);
+      co = (int64_t)slot * slot_code_bytes(bits, r);
+      mo = (int64_t)slot * slot_meta_bytes(bits, r, a.G);
     }
     uint8_t* hb = rec + (int64_t)h * S.hb;
     src = (which ? a.lat_v : a.lat_k) + (((size_t)b * a.max_T + t) * a.Hkv + h) * rcap;
     codes = hb + (which ? S.vc : S.kc) + co;
     meta = hb + (which ? S.vm : S.km) + mo;
   }
-  if (a.latent_bits == 32) {  // fp32 latents: one thread copies the token's r values
+  if (bits == 32) {  // fp32 latents: one thread copies the token's r values
     if (gi == 0)
       for (int i = 0; i < r; ++i) ((float*)codes)[i] = src[i];
     return;
@@ -170,20 +171,22 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(PackArgs a, int groups
     lo = x < lo ? x : lo;
     hi = x > hi ? x : hi;
   }
-  const float s32 = __fdiv_rn(hi - lo, 15.0f);
+  const float levels = (float)((1 << bits) - 1);
+  const float s32 = __fdiv_rn(hi - lo, levels);
   const uint16_t s16 = f16_bits(s32), z16 = f16_bits(lo);
   const float s = f16_val(s16), z = f16_val(z16);
-  for (int i0 = 0; i0 < n; i0 += 8) {  // n is a multiple of 8: whole dwords of 8 codes
+  for (int i0 = 0; i0 < n; i0 += 8) {  // n is a multiple of 8: 8 codes fill `bits` whole bytes
     uint32_t word = 0;
     for (int j = 0; j < 8; ++j) {
       uint32_t q = 0;
       if (s != 0.0f) {
         const float ratio = __fdiv_rn(__fsub_rn(src[g0 + i0 + j], z), s);
-        q = (uint32_t)fminf(fmaxf(rintf(ratio), 0.0f), 15.0f);
+        q = (uint32_t)fminf(fmaxf(rintf(ratio), 0.0f), levels);
       }
-      word |= q << (4 * j);
+      word |= q << (bits * j);
     }
-    *(uint32_t*)(codes + (g0 + i0) / 2) = word;
+    uint8_t* dst = codes + (g0 + i0) * bits / 8;
+    for (int k = 0; k < bits; ++k) dst[k] = (uint8_t)(word >> (8 * k));
   }
   *(uint32_t*)(meta + 4 * gi) = (uint32_t)s16 | ((uint32_t)z16 << 16);
 }
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void pack_residual_kernel(PackArgs a) {
   HeadSections S;
   if (a.variable_rank) {
     const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
-    const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+    const int64_t cb = (int64_t)(tot & 0xFFFFu) * a.latent_bits / 8, mb = 4 * (int64_t)(tot >> 16);
     S = head_sections(cb, cb, mb, mb, P, a.d, 1);
   } else {
     S = a.S_uniform;
@@ -315,7 +318,8 @@ kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const k
   if (!in.lat_k || (!L.shared && !in.lat_v)) return KVC_ERR_INVALID_ARG;
   if (L.residual_bits && (!in.res_k || !in.res_v)) return KVC_ERR_INVALID_ARG;
   if (in.mode == KVC_FROM_DENSE) {
-    if (L.shared || L.latent_bits != 4 || !in.k || !in.v || !in.basis_k || !in.basis_v) return KVC_ERR_INVALID_ARG;
+    if (L.shared || lat_bits_k(L) == 32 || lat_bits_v(L) == 32 || !in.k || !in.v || !in.basis_k || !in.basis_v)
+      return KVC_ERR_INVALID_ARG;
     if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.head_dim > 128) return KVC_ERR_UNSUPPORTED;
   }
   const void* ptrs[] = {in.block_table, in.seq_len, in.ranks, in.lat_k, in.lat_v, in.res_k, in.res_v, in.k, in.v,
@@ -349,7 +353,7 @@ kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const k
                        in.seq_len, in.ranks, C.tok_rank, in.max_T, in.max_blocks, P, L.r_k_cap);
     KVC_CHECK();
     hipLaunchKernelGGL(page_prefix_kernel, dim3(C.n_pages), dim3(256), 0, st, C.tok_rank, C.tok_off, C.page_off, P,
-                       L.group, Hkv, L.residual_bits, d);
+                       L.group, Hkv, L.residual_bits, d, L.latent_bits);
     KVC_CHECK();
     hipLaunchKernelGGL(page_scan_kernel, dim3(1), dim3(1024), 0, st, C.page_off, C.n_pages, (int64_t)-1,
                        C.used_bytes);
@@ -362,12 +366,13 @@ kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const k
   a.block_table = in.block_table; a.seq_len = in.seq_len; a.lat_k = in.lat_k; a.lat_v = in.lat_v;
   a.res_k = in.res_k; a.res_v = in.res_v; a.pool = C.pool; a.page_off = C.page_off; a.tok_rank = C.tok_rank;
   a.tok_off = C.tok_off; a.B = in.B; a.max_T = in.max_T; a.max_blocks = in.max_blocks; a.P = P; a.Hkv = Hkv;
-  a.d = d; a.rk = L.r_k_cap; a.rv = L.r_v_cap; a.G = L.group; a.latent_bits = L.latent_bits;
+  a.d = d; a.rk = L.r_k_cap; a.rv = L.r_v_cap; a.G = L.group; a.latent_bits = lat_bits_k(L);
+  a.latent_bits_v = lat_bits_v(L);
   a.residual = L.residual_bits; a.variable_rank = L.variable_rank; a.shared = L.shared;
-  a.S_uniform = head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
-                              (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
-                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
-                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, d, L.residual_bits);
+  a.S_uniform = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
+                              (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
+                              (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),
+                              (int64_t)P * slot_meta_bytes(lat_bits_v(L), L.r_v_cap, L.group), P, d, L.residual_bits);
   const int gpi = L.latent_bits == 32 ? 1 : ceil_div(std::max(L.r_k_cap, L.r_v_cap), L.group);
   const int64_t threads = (int64_t)in.B * in.max_T * (L.shared ? 1 : 2 * Hkv) * gpi;
   hipLaunchKernelGGL(pack_latent_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a, gpi);

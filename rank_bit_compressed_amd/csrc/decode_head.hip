@@ -66,8 +66,11 @@ __host__ __device__ inline HeadLds head_lds(int D, int KC, int P, bool res, int 
   return L;
 }
 
-template <int D, int KC, int VC, bool LAT32, bool RES, bool VAR, int STG>
+template <int D, int KC, int VC, int KB, int VB, bool RES, bool VAR, int STG>
 __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
+  // KB, VB: latent bits of keys and values (2, 3, 4; 32 = fp32 latents for both)
+  constexpr bool LAT32 = KB == 32;
+  static_assert(LAT32 == (VB == 32), "fp32 latents for both or neither");
   constexpr int MT = D / 16;   // M-tiles of the up-projection (16 head dims each)
   constexpr int QC = D / 32;   // K-chunks of the score product
   constexpr int NP = D / 2;    // RoPE pairs
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
     int64_t hb = a.S_uniform.hb;
     if constexpr (VAR) {
       const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
-      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * KB / 8, mb = 4 * (int64_t)(tot >> 16);  // variable rank: KB == VB
       hb = head_sections(cb, cb, mb, mb, P, D, RES).hb;
     }
     meta_addr[i] = a.page_off[page] + (int64_t)h * hb;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
 
   // Every code / pair read below stays inside the staged buffer, also for slots past the sequence end
   // or beyond a token's rank (their values are discarded through a zero scale and zero).
-  const int kcode_b = LAT32 ? 4 * a.rk : a.rk / 2, vcode_b = LAT32 ? 4 * a.rv : a.rv / 2;
+  const int kcode_b = slot_code_bytes(KB, a.rk), vcode_b = slot_code_bytes(VB, a.rv);
   const int kmeta_b = LAT32 ? 0 : 4 * ceil_div(a.rk, a.G), vmeta_b = LAT32 ? 0 : 4 * ceil_div(a.rv, a.G);
 
   if (n_pages > 0) issue(0, 0);
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
     HeadSections S;
     if constexpr (VAR) {
       const uint32_t tot = so[P];
-      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * KB / 8, mb = 4 * (int64_t)(tot >> 16);
       S = head_sections(cb, cb, mb, mb, P, D, RES);
     } else {
       S = a.S_uniform;
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
           const uint32_t o0 = so[slot], o1 = so[slot + 1];
           const int r = valid ? (int)((o1 - o0) & 0xFFFFu) : 0;
           rk_t = rv_t = r;
-          kco = vco = (o0 & 0xFFFFu) / 2;
+          kco = vco = (int)((o0 & 0xFFFFu) * KB / 8);
           kmo = vmo = 4 * (o0 >> 16);
         } else {
           rk_t = valid ? a.rk : 0;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
             const float* src = (const float*)(sb + S.kc + kco) + 8 * w;
             for (int j = 0; j < 8; ++j) kb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
           } else {
-            const uint32_t x = *(const uint32_t*)(sb + S.kc + kco + 4 * w);
+            const uint32_t x = codes8_as_nibbles<KB>(sb + S.kc + kco + KB * w);
             const uint32_t sz = *(const uint32_t*)(sb + S.km + kmo + 4 * ((8 * w) / a.G));
             kb[c] = dequant_int4x8(x, ok ? sz : 0u);
           }
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
             const float* src = (const float*)(sb + S.vc + vco) + 8 * w;
             for (int j = 0; j < 8; ++j) vb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
           } else {
-            const uint32_t x = *(const uint32_t*)(sb + S.vc + vco + 4 * w);
+            const uint32_t x = codes8_as_nibbles<VB>(sb + S.vc + vco + VB * w);
             const uint32_t sz = *(const uint32_t*)(sb + S.vm + vmo + 4 * ((8 * w) / a.G));
             vb[c] = dequant_int4x8(x, ok ? sz : 0u);
           }
@@ -479,10 +482,10 @@ __global__ __launch_bounds__(256) void merge_head_kernel(const float* ws, const 
 
 // ---------------------------------------------------------------- host side
 
-template <int D, int KC, int VC, bool LAT32, bool RES, bool VAR, int STG>
+template <int D, int KC, int VC, int KB, int VB, bool RES, bool VAR, int STG>
 static hipError_t launch_variant(const DecodeHeadArgs& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
   const int lds = head_lds(D, KC, a.P, RES, a.hb_max).total;
-  auto kern = decode_head_kernel<D, KC, VC, LAT32, RES, VAR, STG>;
+  auto kern = decode_head_kernel<D, KC, VC, KB, VB, RES, VAR, STG>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -520,10 +523,10 @@ int head_part_stride(int rv_cap, int residual) {
 // Largest head block (every slot at the rank cap).
 static int64_t head_block_max(const kvc_layout& L) {
   const int P = L.page_size;
-  return head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
-                       (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
-                       (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
-                       (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
+  return head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
+                       (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
+                       (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),
+                       (int64_t)P * slot_meta_bytes(lat_bits_v(L), L.r_v_cap, L.group), P, L.head_dim,
                        L.residual_bits)
       .hb;
 }
@@ -547,7 +550,7 @@ bool head_supported(const kvc_layout& L) {
   if (L.head_dim != 64 && L.head_dim != 128) return false;
   if (L.r_k_cap > 64 || L.r_v_cap > 64) return false;
   if (L.residual_bits && L.head_dim != 128) return false;
-  if (L.latent_bits == 4 && L.group % 16) return false;
+  if (L.latent_bits != 32 && L.group % 16) return false;
   const int64_t hb = head_block_max(L);
   if (hb > 16 * 256 * 9) return false;  // staging registers: at most 9 x 16 bytes per thread
   if (head_lds(L.head_dim, ceil_div(L.r_k_cap, 32), L.page_size, L.residual_bits != 0, (int)hb).total > 160 * 1024)
@@ -571,10 +574,10 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
   a.part_stride = head_part_stride(L.r_v_cap, L.residual_bits);
   a.theta = L.rope_theta;
   const int P = L.page_size;
-  a.S_uniform = head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
-                              (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
-                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
-                              (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
+  a.S_uniform = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
+                              (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
+                              (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),
+                              (int64_t)P * slot_meta_bytes(lat_bits_v(L), L.r_v_cap, L.group), P, L.head_dim,
                               L.residual_bits);
   a.hb_max = (int)head_block_max(L);
   *unsupported = false;
@@ -585,20 +588,29 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
   const int stg = ceil_div(a.hb_max, 16 * 256);
   const int grid = in.B * L.n_kv_heads * n_splits;
   const int KC = ceil_div(L.r_k_cap, 32), VC = ceil_div(L.r_v_cap, 32);
-  const bool lat32 = L.latent_bits == 32, res = L.residual_bits != 0, var = L.variable_rank != 0;
-#define KVC_TRY(D_, KC_, VC_, L32_, RES_, VAR_, STG_)                                                        \
-  if (L.head_dim == D_ && KC == KC_ && VC == VC_ && lat32 == L32_ && res == RES_ && var == VAR_ && stg <= STG_) \
-    return launch_variant<D_, KC_, VC_, L32_, RES_, VAR_, STG_>(a, grid, in.wv, out, st);
-  KVC_TRY(128, 2, 2, false, false, false, 5)
-  KVC_TRY(128, 2, 2, false, false, true, 5)
-  KVC_TRY(128, 2, 2, false, true, false, 9)
-  KVC_TRY(128, 1, 1, false, false, false, 3)
-  KVC_TRY(128, 1, 1, false, false, true, 3)
-  KVC_TRY(64, 1, 1, true, false, false, 9)
-  KVC_TRY(64, 2, 2, true, false, false, 9)
-  KVC_TRY(64, 2, 2, false, false, false, 5)
-  KVC_TRY(64, 2, 2, false, false, true, 5)
-  KVC_TRY(64, 1, 1, false, false, false, 3)
+  const int kb = lat_bits_k(L), vb = lat_bits_v(L);
+  const bool res = L.residual_bits != 0, var = L.variable_rank != 0;
+#define KVC_TRY(D_, KC_, VC_, KB_, VB_, RES_, VAR_, STG_)                                                       \
+  if (L.head_dim == D_ && KC == KC_ && VC == VC_ && kb == KB_ && vb == VB_ && res == RES_ && var == VAR_ && \
+      stg <= STG_)                                                                                          \
+    return launch_variant<D_, KC_, VC_, KB_, VB_, RES_, VAR_, STG_>(a, grid, in.wv, out, st);
+  KVC_TRY(128, 2, 2, 4, 4, false, false, 5)
+  KVC_TRY(128, 2, 2, 4, 4, false, true, 5)
+  KVC_TRY(128, 2, 2, 4, 4, true, false, 9)
+  KVC_TRY(128, 1, 1, 4, 4, false, false, 3)
+  KVC_TRY(128, 1, 1, 4, 4, false, true, 3)
+  KVC_TRY(64, 1, 1, 32, 32, false, false, 9)
+  KVC_TRY(64, 2, 2, 32, 32, false, false, 9)
+  KVC_TRY(64, 2, 2, 4, 4, false, false, 5)
+  KVC_TRY(64, 2, 2, 4, 4, false, true, 5)
+  KVC_TRY(64, 1, 1, 4, 4, false, false, 3)
+  // lower-bit codecs: INT3, INT2 and 3-bit keys with 2-bit values
+  KVC_TRY(128, 2, 2, 3, 3, false, false, 5)
+  KVC_TRY(128, 2, 2, 2, 2, false, false, 5)
+  KVC_TRY(128, 2, 2, 3, 2, false, false, 5)
+  KVC_TRY(128, 2, 2, 3, 3, false, true, 5)
+  KVC_TRY(128, 2, 2, 2, 2, false, true, 5)
+  KVC_TRY(128, 2, 2, 3, 3, true, false, 9)
 #undef KVC_TRY
   *unsupported = true;
   return hipSuccess;

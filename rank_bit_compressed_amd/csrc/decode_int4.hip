@@ -597,7 +597,7 @@ static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, f
 int int4_max_pages_per_split() { return i4::MAX_SPLIT_PAGES; }
 
 bool int4_supported(const kvc_layout& L, int64_t hb_max) {
-  if (L.shared || L.latent_bits != 4 || L.residual_bits || L.head_dim != 128) return false;
+  if (L.shared || lat_bits_k(L) != 4 || lat_bits_v(L) != 4 || L.residual_bits || L.head_dim != 128) return false;
   if (L.n_q_heads != i4::GQ * L.n_kv_heads) return false;
   if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
   if (L.variable_rank && L.r_k_cap != L.r_v_cap) return false;

@@ -576,7 +576,7 @@ int res_max_pages_per_split() { return rsd::MAX_SPLIT_PAGES; }
 
 // The layouts this kernel serves; the rest of the residual layouts go to the general kernel.
 bool res_supported(const kvc_layout& L, int64_t hb) {
-  if (L.shared || L.latent_bits != 4 || L.residual_bits != 2 || L.head_dim != 128 || L.variable_rank) return false;
+  if (L.shared || lat_bits_k(L) != 4 || lat_bits_v(L) != 4 || L.residual_bits != 2 || L.head_dim != 128 || L.variable_rank) return false;
   if (L.n_q_heads != rsd::GQ * L.n_kv_heads) return false;
   if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
   if (L.r_k_cap % 16 || L.r_v_cap % 16) return false;  // whole steps: no code or pair read past the rank

@@ -450,7 +450,7 @@ int shared_max_tiles_per_split() { return SMAX_TILES; }
 
 bool shared_supported(const kvc_layout& L) {
   return L.shared && L.head_dim == SD && L.r_k_cap == SLAT && L.n_q_heads == SGQ * L.n_kv_heads &&
-         L.latent_bits == 4 && L.group >= 32 && L.group <= SLAT && (L.group & (L.group - 1)) == 0;
+         lat_bits_k(L) == 4 && lat_bits_v(L) == 4 && L.group >= 32 && L.group <= SLAT && (L.group & (L.group - 1)) == 0;
 }
 
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {

@@ -58,22 +58,53 @@ __host__ __device__ inline HeadSections head_sections(int64_t ck, int64_t cv, in
   return S;
 }
 
-// Code and pair bytes of a slot of rank r.
-__host__ __device__ inline int slot_code_bytes(int latent_bits, int r) { return latent_bits == 4 ? r / 2 : 4 * r; }
+// Latent bits of keys and values (latent_bits_v = 0: the same as the keys).
+__host__ __device__ inline int lat_bits_k(const kvc_layout& L) { return L.latent_bits; }
+__host__ __device__ inline int lat_bits_v(const kvc_layout& L) { return L.latent_bits_v ? L.latent_bits_v : L.latent_bits; }
+
+// Code and pair bytes of a slot of rank r with b-bit codes (b = 32: fp32 latents, no pairs).
+__host__ __device__ inline int slot_code_bytes(int latent_bits, int r) { return latent_bits == 32 ? 4 * r : r * latent_bits / 8; }
 __host__ __device__ inline int slot_meta_bytes(int latent_bits, int r, int G) {
-  return latent_bits == 4 ? 4 * ceil_div(r, G) : 0;
+  return latent_bits == 32 ? 0 : 4 * ceil_div(r, G);
 }
 
 // Uniform-rank page record size (per-head or shared mode).
 __host__ __device__ inline int64_t uniform_page_bytes(const kvc_layout& L) {
   const int P = L.page_size;
   if (L.shared) return pad16((int64_t)P * L.r_k_cap / 2) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
-  HeadSections S = head_sections((int64_t)P * slot_code_bytes(L.latent_bits, L.r_k_cap),
-                                 (int64_t)P * slot_code_bytes(L.latent_bits, L.r_v_cap),
-                                 (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_k_cap, L.group),
-                                 (int64_t)P * slot_meta_bytes(L.latent_bits, L.r_v_cap, L.group), P, L.head_dim,
+  HeadSections S = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
+                                 (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
+                                 (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),
+                                 (int64_t)P * slot_meta_bytes(lat_bits_v(L), L.r_v_cap, L.group), P, L.head_dim,
                                  L.residual_bits);
   return S.hb * L.n_kv_heads;
+}
+
+// Eight b-bit codes (b = 2, 3, 4) starting at a byte address of LDS or global memory (any alignment), as the
+// INT4 dword layout (code k in the low b bits of nibble k) that dequant_int4x8 takes.  The codes of a slot form a
+// little-endian bit string, code i at bits b*i.., so the 8 codes of group w start at byte b*w.  Reads up to 7
+// bytes past the group, which the 16-byte padding of every section keeps inside the block.
+template <int B>
+__device__ inline uint32_t codes8_as_nibbles(const uint8_t* p) {
+  if constexpr (B == 4) {
+    return *(const uint32_t*)p;
+  } else if constexpr (B == 2) {
+    uint32_t y = *(const uint16_t*)p;  // 2-byte aligned: slot offsets are multiples of r / 4 bytes, r % 8 == 0
+    y = (y | (y << 8)) & 0x00FF00FFu;
+    y = (y | (y << 4)) & 0x0F0F0F0Fu;
+    y = (y | (y << 2)) & 0x33333333u;
+    return y;
+  } else {
+    const uintptr_t ad = (uintptr_t)p;
+    const uint32_t* w = (const uint32_t*)(ad & ~(uintptr_t)3);
+    const uint32_t sh = 8u * (uint32_t)(ad & 3u);
+    const uint64_t both = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+    const uint32_t x = (uint32_t)(both >> sh) & 0xFFFFFFu;   // codes 0..7 at bits 3k
+    uint32_t y = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);      // codes 0-3 at bits 0.., codes 4-7 at bits 16..
+    y = (y & 0x003F003Fu) | ((y & 0x0FC00FC0u) << 2);        // code pairs at bytes 0..3
+    y = (y & 0x07070707u) | ((y & 0x38383838u) << 1);        // code k at bits 4k
+    return y;
+  }
 }
 
 // ---- device helpers ----

@@ -41,7 +41,8 @@ class Layout(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("shared", C.c_int32), ("n_layers", C.c_int32), ("r_k_cap", C.c_int32), ("r_v_cap", C.c_int32),
                 ("group", C.c_int32), ("latent_bits", C.c_int32), ("residual_bits", C.c_int32),
-                ("page_size", C.c_int32), ("variable_rank", C.c_int32), ("rope_theta", C.c_double)]
+                ("page_size", C.c_int32), ("variable_rank", C.c_int32), ("rope_theta", C.c_double),
+                ("latent_bits_v", C.c_int32)]
 
 
 class Cache(C.Structure):
@@ -141,7 +142,7 @@ def _check(status: int, where: str):
 
 def make_layout(**kw) -> Layout:
     f = dict(n_q_heads=0, n_kv_heads=0, head_dim=0, shared=0, n_layers=1, r_k_cap=0, r_v_cap=0, group=32,
-             latent_bits=4, residual_bits=0, page_size=256, variable_rank=0, rope_theta=0.0)
+             latent_bits=4, residual_bits=0, page_size=256, variable_rank=0, rope_theta=0.0, latent_bits_v=0)
     f.update(kw)
     return Layout(**f)
 

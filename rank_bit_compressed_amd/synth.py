@@ -49,6 +49,7 @@ class Workload:
     r_v: int                      # value rank (cap); block-shared mode: latent dimension
     group: int = 32
     latent_bits: int = 4
+    latent_bits_v: int = 0        # value latent bits; 0 = latent_bits
     residual_bits: int = 0
     page_size: int = 256
     variable_rank: bool = False
@@ -81,7 +82,7 @@ class Workload:
                     r_k_cap=self.r_k, r_v_cap=self.r_v, group=self.group, latent_bits=self.latent_bits,
                     residual_bits=self.residual_bits, page_size=self.page_size,
                     variable_rank=int(self.variable_rank), shared=int(self.shared), n_layers=self.n_layers,
-                    rope_theta=float(self.rope_theta))
+                    rope_theta=float(self.rope_theta), latent_bits_v=self.latent_bits_v)
 
 
 # The five workloads of the build's target list; sizes as stated there.

@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 1
+    assert kvc.lib().kvc_abi_version() == 2
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -130,3 +130,26 @@ def test_salience_and_alloc_reject_bad_arguments_without_launching():
                dict(B=0)]:
         assert lib.kvc_rank_alloc(C.byref(ain(**kw)), v(48), None) == -1, kw
     assert lib.kvc_rank_alloc(C.byref(ain(sal=v(33))), v(48), None) == -4
+
+
+def test_low_bit_layouts_check_and_route_to_the_general_kernel():
+    # INT3, INT2 and 3-bit keys with 2-bit values are valid per-head layouts served by the general kernel; the
+    # INT4-specialised kernels keep INT4 only; the block-shared mode stays INT4
+    base = synth.WORKLOADS["llama8b_layer_8k"]
+    for kb, vb in [(3, 0), (2, 0), (3, 2), (4, 2)]:
+        L = kvc.make_layout(**base.scaled(latent_bits=kb, latent_bits_v=vb).layout_kwargs())
+        assert kvc.layout_check(L) == 0 and kvc.decode_path(L) == kvc.PATH_HEAD, (kb, vb)
+    res = kvc.make_layout(**synth.WORKLOADS["residual_128k"].scaled(latent_bits=3).layout_kwargs())
+    assert kvc.decode_path(res) == kvc.PATH_HEAD
+    var = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].scaled(latent_bits=2).layout_kwargs())
+    assert kvc.layout_check(var) == 0 and kvc.decode_path(var) == kvc.PATH_HEAD
+    for kw, want in [(dict(latent_bits=5), -1), (dict(latent_bits=4, latent_bits_v=1), -1),
+                     (dict(latent_bits=32, latent_bits_v=4), -1), (dict(latent_bits=4, latent_bits_v=32), -1)]:
+        assert kvc.layout_check(kvc.make_layout(**base.scaled(**kw).layout_kwargs())) == want, kw
+    bad_var = synth.WORKLOADS["varrank_paged_32k"].scaled(latent_bits=3, latent_bits_v=2)
+    assert kvc.layout_check(kvc.make_layout(**bad_var.layout_kwargs())) == -1
+    shared3 = synth.WORKLOADS["shared_latent_32k"].scaled(latent_bits=3)
+    assert kvc.layout_check(kvc.make_layout(**shared3.layout_kwargs())) == -1
+    # pool sizes follow r * b / 8 code bytes: K 48 x 3 / 8 = 18, V 64 x 2 / 8 = 16 per slot
+    L = kvc.make_layout(**base.scaled(latent_bits=3, latent_bits_v=2).layout_kwargs())
+    assert kvc.pool_bytes_max(L, 10) == 10 * 8 * 256 * (18 + 16 + 8 + 8)

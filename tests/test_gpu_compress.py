@@ -15,6 +15,10 @@ CASES = [
     ("varrank_paged_32k", dict(B=3, T=2000), [2000, 1999, 33]),
     ("residual_128k", dict(B=2, T=700), [700, 512]),
     ("shared_latent_32k", dict(B=2, T=600), [600, 1]),
+    ("llama8b_layer_8k", dict(T=1000, latent_bits=3), None),
+    ("llama8b_layer_8k", dict(T=600, latent_bits=3, latent_bits_v=2), None),
+    ("varrank_paged_32k", dict(B=3, T=2000, latent_bits=2), [2000, 1999, 33]),
+    ("residual_128k", dict(B=2, T=700, latent_bits=3), [700, 512]),
 ]
 
 

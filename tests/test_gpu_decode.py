@@ -25,6 +25,13 @@ CASES = [
     ("residual_128k", dict(B=2, T=700, r_k=40, r_v=56), [700, 300]),
     ("shared_latent_32k", dict(B=2, T=600), [600, 33]),
     ("shared_latent_32k", dict(B=1, T=300, n_layers=2, page_size=64), None),
+    # lower-bit codecs on the general per-head kernel: INT3, INT2, 3-bit keys with 2-bit values
+    ("llama8b_layer_8k", dict(T=1000, latent_bits=3), None),
+    ("llama8b_layer_8k", dict(B=2, T=333, page_size=64, latent_bits=2), [333, 1]),
+    ("llama8b_layer_8k", dict(T=700, latent_bits=3, latent_bits_v=2), None),
+    ("varrank_paged_32k", dict(B=2, T=1000, latent_bits=3), [1000, 517]),
+    ("varrank_paged_32k", dict(B=2, T=600, latent_bits=2), [600, 33]),
+    ("residual_128k", dict(B=2, T=700, latent_bits=3), [700, 300]),
 ]
 
 
