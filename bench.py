@@ -95,7 +95,7 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
 # and head from the 512-dim latent) and the 128K rotated-residual cache (HBM).
-OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k")
+OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2")
 
 
 def decode_flops(w) -> int:
@@ -151,7 +151,7 @@ def other_workloads(steps: int, warmup: int) -> dict:
         r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),
              "compressed_bytes": nbytes, "hbm_gbs": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
              "flops": flops, "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1)}
-        if name == "llama8b_layer_8k":
+        if name.startswith("llama8b_layer_8k"):
             r["bound"] = "latency (the 4.7 MB cache stays in the last-level cache between calls)"
         elif w.shared:
             r["bound"] = "mfma"

@@ -18,7 +18,8 @@ def dense_bytes_per_token(n_kv_heads: int, head_dim: int, elem_bytes: int = 2) -
 def compressed_stream_bytes(w, ranks: torch.Tensor | None, seq_len) -> dict:
     """Bytes of the compressed cache one decode step reads (all sequences, heads and layers).
 
-    per (token, kv head): K codes r_k/2 + 4 bytes per group, V likewise, and for the rotated residual
+    per (token, kv head): K codes r_k * b_k / 8 + 4 bytes per group (b_k the key latent bits), V likewise with b_v,
+    and for the rotated residual
     2 x (32 code bytes + 2 scale bytes); block-shared mode: per token latent/2 + 4 per group, read once
     for all layers and heads.  Variable rank adds the per-token rank byte and 4-byte offset word.
     """
@@ -28,14 +29,17 @@ def compressed_stream_bytes(w, ranks: torch.Tensor | None, seq_len) -> dict:
         per_tok = w.r_k // 2 + 4 * math.ceil(w.r_k / w.group)
         return {"stream": n_tok * per_tok, "tables": 0, "tokens": n_tok}
     Hkv = w.n_kv_heads
+    bk = w.latent_bits
+    bv = getattr(w, "latent_bits_v", 0) or w.latent_bits
     if w.variable_rank:
         r = torch.cat([ranks[b, :n].to(torch.int64).cpu() for b, n in enumerate(seq_len)])
         g = (r + w.group - 1) // w.group
-        per_head = int(r.sum()) + 4 * 2 * int(g.sum())          # (r/2 + r/2) code bytes + K and V pairs
+        per_head = int(r.sum()) * (bk + bv) // 8 + 4 * 2 * int(g.sum())  # K and V code bytes + K and V pairs
         stream = Hkv * per_head
         tables = n_tok * (1 + 4)
     else:
-        per_tok_head = w.r_k // 2 + w.r_v // 2 + 4 * (math.ceil(w.r_k / w.group) + math.ceil(w.r_v / w.group))
+        per_tok_head = (w.r_k * bk // 8 + w.r_v * bv // 8
+                        + 4 * (math.ceil(w.r_k / w.group) + math.ceil(w.r_v / w.group)))
         if w.latent_bits == 32:
             per_tok_head = 4 * (w.r_k + w.r_v)
         stream = n_tok * Hkv * per_tok_head

@@ -544,6 +544,35 @@ hipError_t launch_decode_res(const kvc_layout& L, const kvc_cache& C, const kvc_
                              int n_splits, int pages_per_split, int part_stride, const HeadSections& S,
                              hipStream_t st);
 
+// The compiled variants (head dim, key chunks, value chunks, key bits, value bits, residual, variable rank,
+// staging chunks), used both to decide support and to launch, so that a supported layout always has one.
+#define KVC_HEAD_VARIANTS(X)                 \
+  X(128, 2, 2, 4, 4, false, false, 5)        \
+  X(128, 2, 2, 4, 4, false, true, 5)         \
+  X(128, 2, 2, 4, 4, true, false, 9)         \
+  X(128, 1, 1, 4, 4, false, false, 3)        \
+  X(128, 1, 1, 4, 4, false, true, 3)         \
+  X(64, 1, 1, 32, 32, false, false, 9)       \
+  X(64, 2, 2, 32, 32, false, false, 9)       \
+  X(64, 2, 2, 4, 4, false, false, 5)         \
+  X(64, 2, 2, 4, 4, false, true, 5)          \
+  X(64, 1, 1, 4, 4, false, false, 3)         \
+  X(128, 2, 2, 3, 3, false, false, 5)        \
+  X(128, 2, 2, 2, 2, false, false, 5)        \
+  X(128, 2, 2, 3, 2, false, false, 5)        \
+  X(128, 2, 2, 3, 3, false, true, 5)         \
+  X(128, 2, 2, 2, 2, false, true, 5)         \
+  X(128, 2, 2, 3, 3, true, false, 9)
+
+static bool head_has_variant(int d, int KC, int VC, int kb, int vb, bool res, bool var, int stg) {
+#define KVC_HAS(D_, KC_, VC_, KB_, VB_, RES_, VAR_, STG_)                                                   \
+  if (d == D_ && KC == KC_ && VC == VC_ && kb == KB_ && vb == VB_ && res == RES_ && var == VAR_ && stg <= STG_) \
+    return true;
+  KVC_HEAD_VARIANTS(KVC_HAS)
+#undef KVC_HAS
+  return false;
+}
+
 bool head_supported(const kvc_layout& L) {
   if (L.shared) return false;
   if (L.n_q_heads != GQ * L.n_kv_heads) return false;
@@ -553,6 +582,10 @@ bool head_supported(const kvc_layout& L) {
   if (L.latent_bits != 32 && L.group % 16) return false;
   const int64_t hb = head_block_max(L);
   if (hb > 16 * 256 * 9) return false;  // staging registers: at most 9 x 16 bytes per thread
+  if (!int4_supported(L, hb) && !res_supported(L, hb) &&
+      !head_has_variant(L.head_dim, ceil_div(L.r_k_cap, 32), ceil_div(L.r_v_cap, 32), lat_bits_k(L), lat_bits_v(L),
+                        L.residual_bits != 0, L.variable_rank != 0, ceil_div((int)hb, 16 * 256)))
+    return false;
   if (head_lds(L.head_dim, ceil_div(L.r_k_cap, 32), L.page_size, L.residual_bits != 0, (int)hb).total > 160 * 1024)
     return false;
   return true;
@@ -594,23 +627,7 @@ hipError_t launch_decode_head(const kvc_layout& L, const kvc_cache& C, const kvc
   if (L.head_dim == D_ && KC == KC_ && VC == VC_ && kb == KB_ && vb == VB_ && res == RES_ && var == VAR_ && \
       stg <= STG_)                                                                                          \
     return launch_variant<D_, KC_, VC_, KB_, VB_, RES_, VAR_, STG_>(a, grid, in.wv, out, st);
-  KVC_TRY(128, 2, 2, 4, 4, false, false, 5)
-  KVC_TRY(128, 2, 2, 4, 4, false, true, 5)
-  KVC_TRY(128, 2, 2, 4, 4, true, false, 9)
-  KVC_TRY(128, 1, 1, 4, 4, false, false, 3)
-  KVC_TRY(128, 1, 1, 4, 4, false, true, 3)
-  KVC_TRY(64, 1, 1, 32, 32, false, false, 9)
-  KVC_TRY(64, 2, 2, 32, 32, false, false, 9)
-  KVC_TRY(64, 2, 2, 4, 4, false, false, 5)
-  KVC_TRY(64, 2, 2, 4, 4, false, true, 5)
-  KVC_TRY(64, 1, 1, 4, 4, false, false, 3)
-  // lower-bit codecs: INT3, INT2 and 3-bit keys with 2-bit values
-  KVC_TRY(128, 2, 2, 3, 3, false, false, 5)
-  KVC_TRY(128, 2, 2, 2, 2, false, false, 5)
-  KVC_TRY(128, 2, 2, 3, 2, false, false, 5)
-  KVC_TRY(128, 2, 2, 3, 3, false, true, 5)
-  KVC_TRY(128, 2, 2, 2, 2, false, true, 5)
-  KVC_TRY(128, 2, 2, 3, 3, true, false, 9)
+  KVC_HEAD_VARIANTS(KVC_TRY)
 #undef KVC_TRY
   *unsupported = true;
   return hipSuccess;

@@ -106,8 +106,9 @@ __device__ inline void vmcnt_wait(int k) {
   }
 }
 
-// KS, VS: 16-coordinate steps of the key / value rank caps (2..4); VT: 32-coordinate value tiles
-template <int KS, int VS, bool VAR, int STG>
+// KS, VS: 16-coordinate steps of the key / value rank caps (2..4); VT: 32-coordinate value tiles; KB, VB: bits
+// of the key / value codes (4, or the lower-bit codecs 3 and 2, spread to the INT4 nibble layout as they are read)
+template <int KS, int VS, bool VAR, int STG, int KB, int VB>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   using namespace i4;
   constexpr int VT = (VS + 1) / 2;
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     int64_t hb = a.S_uniform.hb;
     if constexpr (VAR) {
       const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
-      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * KB / 8, mb = 4 * (int64_t)(tot >> 16);  // variable rank: KB == VB
       hb = head_sections(cb, cb, mb, mb, P, D, 0).hb;
     }
     meta_addr[i] = a.page_off[page] + (int64_t)h * hb;
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   }
   bool fresh = true;  // no token seen yet
 
-  const int kcb = a.rk / 2, vcb = a.rv / 2;                                  // uniform: code bytes per slot
+  const int kcb = a.rk * KB / 8, vcb = a.rv * VB / 8;                        // uniform: code bytes per slot
   const int kmb = 4 * ceil_div(a.rk, a.G), vmb = 4 * ceil_div(a.rv, a.G);  // uniform: pair bytes per slot
 
   struct Words {  // a lane's LDS words for one super-tile: code dword and (scale, zero) word per step
@@ -292,13 +293,14 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     HeadSections S;
     if constexpr (VAR) {
       const uint32_t tot = so[P];
-      const int64_t cb = (tot & 0xFFFFu) / 2, mb = 4 * (int64_t)(tot >> 16);
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * KB / 8, mb = 4 * (int64_t)(tot >> 16);
       S = head_sections(cb, cb, mb, mb, P, D, 0);
     } else {
       S = a.S_uniform;
     }
-    const uint8_t* kcs = sb + S.kc + 4 * hf;
-    const uint8_t* vcs = sb + S.vc + 4 * hf;
+    // the 16 codes of step s take 2 KB bytes; this lane's half hf reads the KB bytes of codes 16 s + 8 hf ..
+    const uint8_t* kcs = sb + S.kc + KB * hf;
+    const uint8_t* vcs = sb + S.vc + VB * hf;
     const uint8_t* kms = sb + S.km;
     const uint8_t* vms = sb + S.vm;
     const int page_t0 = (lb0 + ip) * P;
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         if constexpr (VAR) {
           const uint32_t o0 = so[slot], o1 = so[slot + 1];
           r = (int)((o1 - o0) & 0xFFFFu);  // 0 for slots past the sequence end
-          co_k = w.co_v = (int)((o0 & 0xFFFFu) >> 1);
+          co_k = w.co_v = (int)((o0 & 0xFFFFu) * KB / 8);
           po_k = w.po_v = (int)(o0 >> 16) * 4;
         } else {
           r = a.rk;
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         w.r = r;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          w.k[s] = lds_u32(kcs, co_k + 8 * s);
+          w.k[s] = codes8_as_nibbles<KB>(kcs + co_k + 2 * KB * s);
           w.pk[s] = lds_u32(kms, po_k + 4 * ((16 * s + 8 * hf) / a.G));
           if constexpr (VAR) w.pk[s] = pair_if(16 * s + 8 * hf < r, w.pk[s]);
         }
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         uint32_t vw[VS], vp[VS];
 #pragma unroll
         for (int s = 0; s < VS; ++s) {
-          vw[s] = lds_u32(vcs, cur.co_v + 8 * s);
+          vw[s] = codes8_as_nibbles<VB>(vcs + cur.co_v + 2 * VB * s);
           vp[s] = lds_u32(vms, cur.po_v + 4 * ((16 * s + 8 * hf) / a.G));
           if constexpr (VAR) vp[s] = pair_if(16 * s + 8 * hf < cur.r, vp[s]);
         }
@@ -574,10 +576,10 @@ __global__ __launch_bounds__(128) void merge_int4_kernel(const float* ws, const 
   out[((size_t)b * Hq + hq_all) * i4::D + tid] = o / lst;
 }
 
-template <int KS, int VS, bool VAR, int STG>
+template <int KS, int VS, bool VAR, int STG, int KB, int VB>
 static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, float* out, hipStream_t st) {
   const int lds = i4::lds_layout(a.P, a.hb_max).total;
-  auto kern = decode_int4_kernel<KS, VS, VAR, STG>;
+  auto kern = decode_int4_kernel<KS, VS, VAR, STG, KB, VB>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -596,8 +598,35 @@ static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, f
 
 int int4_max_pages_per_split() { return i4::MAX_SPLIT_PAGES; }
 
+// The compiled variants (key steps, value steps, variable rank, staging chunks, key bits, value bits), used both to
+// decide support and to launch, so that a layout this kernel accepts always has a variant.
+#define KVC_INT4_VARIANTS(X)  \
+  X(4, 4, true, 5, 4, 4)      \
+  X(4, 4, false, 5, 4, 4)     \
+  X(3, 4, false, 5, 4, 4)     \
+  X(2, 2, true, 3, 4, 4)      \
+  X(2, 2, false, 3, 4, 4)     \
+  X(4, 4, true, 5, 3, 3)      \
+  X(4, 4, true, 5, 2, 2)      \
+  X(4, 4, false, 5, 3, 3)     \
+  X(4, 4, false, 5, 3, 2)     \
+  X(3, 4, false, 5, 3, 3)     \
+  X(3, 4, false, 5, 3, 2)     \
+  X(3, 4, false, 5, 2, 2)
+
+static bool int4_has_variant(int KS, int VS, bool var, int stg, int kb, int vb) {
+#define KVC_HAS(KS_, VS_, VAR_, STG_, KB_, VB_) \
+  if (KS == KS_ && VS == VS_ && var == VAR_ && stg <= STG_ && kb == KB_ && vb == VB_) return true;
+  KVC_INT4_VARIANTS(KVC_HAS)
+#undef KVC_HAS
+  return false;
+}
+
 bool int4_supported(const kvc_layout& L, int64_t hb_max) {
-  if (L.shared || lat_bits_k(L) != 4 || lat_bits_v(L) != 4 || L.residual_bits || L.head_dim != 128) return false;
+  if (L.shared || L.residual_bits || L.head_dim != 128 || L.latent_bits == 32) return false;
+  if (!int4_has_variant(ceil_div(L.r_k_cap, 16), ceil_div(L.r_v_cap, 16), L.variable_rank != 0,
+                        ceil_div((int)hb_max, 16 * 256), lat_bits_k(L), lat_bits_v(L)))
+    return false;
   if (L.n_q_heads != i4::GQ * L.n_kv_heads) return false;
   if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
   if (L.variable_rank && L.r_k_cap != L.r_v_cap) return false;
@@ -620,13 +649,11 @@ hipError_t launch_decode_int4(const kvc_layout& L, const kvc_cache& C, const kvc
   const int KS = ceil_div(L.r_k_cap, 16), VS = ceil_div(L.r_v_cap, 16);
   const bool var = L.variable_rank != 0;
   const int stg = ceil_div(hb_max, 16 * 256);
-#define KVC_TRY4(KS_, VS_, VAR_, STG_) \
-  if (KS == KS_ && VS == VS_ && var == VAR_ && stg <= STG_) return launch_int4<KS_, VS_, VAR_, STG_>(a, grid, in.wv, out, st);
-  KVC_TRY4(4, 4, true, 5)
-  KVC_TRY4(4, 4, false, 5)
-  KVC_TRY4(3, 4, false, 5)
-  KVC_TRY4(2, 2, true, 3)
-  KVC_TRY4(2, 2, false, 3)
+  const int kb = lat_bits_k(L), vb = lat_bits_v(L);
+#define KVC_TRY4(KS_, VS_, VAR_, STG_, KB_, VB_)                                              \
+  if (KS == KS_ && VS == VS_ && var == VAR_ && stg <= STG_ && kb == KB_ && vb == VB_)         \
+    return launch_int4<KS_, VS_, VAR_, STG_, KB_, VB_>(a, grid, in.wv, out, st);
+  KVC_INT4_VARIANTS(KVC_TRY4)
 #undef KVC_TRY4
   return hipErrorInvalidValue;
 }

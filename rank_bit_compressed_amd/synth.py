@@ -106,6 +106,15 @@ WORKLOADS = {
     "residual_128k": Workload("residual_128k", B=8, T=131072, n_q_heads=32, n_kv_heads=8, head_dim=128,
                               r_k=48, r_v=64, group=32, residual_bits=2, rope_theta=500000.0,
                               shuffle_pages=True, seed=15),
+    # the lower-bit codecs of the BellowsKV page's retention table on per-head latents: the 32K variable-rank
+    # workload with INT3 latents, and the 8K layer with 3-bit keys and 2-bit values
+    "varrank_paged_32k_int3": Workload("varrank_paged_32k_int3", B=16, T=32768, n_q_heads=32, n_kv_heads=8,
+                                       head_dim=128, r_k=64, r_v=64, group=32, latent_bits=3,
+                                       rope_theta=500000.0, variable_rank=True, rank_choices=(8, 16, 32, 64),
+                                       rank_probs=(0.4, 0.3, 0.2, 0.1), shuffle_pages=True, seed=13),
+    "llama8b_layer_8k_k3v2": Workload("llama8b_layer_8k_k3v2", B=1, T=8192, n_q_heads=32, n_kv_heads=8,
+                                      head_dim=128, r_k=48, r_v=64, group=32, latent_bits=3, latent_bits_v=2,
+                                      rope_theta=500000.0, seed=12),
 }
 
 

@@ -72,7 +72,8 @@ def test_decode_path_selection():
     (and their scaled test copies), the INT4 residual kernel the residual workload; the others go to the
     general per-head or the block-shared kernel."""
     want = {"tiny": kvc.PATH_HEAD, "llama8b_layer_8k": kvc.PATH_INT4, "varrank_paged_32k": kvc.PATH_INT4,
-            "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES}
+            "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
+            "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
@@ -132,17 +133,25 @@ def test_salience_and_alloc_reject_bad_arguments_without_launching():
     assert lib.kvc_rank_alloc(C.byref(ain(sal=v(33))), v(48), None) == -4
 
 
-def test_low_bit_layouts_check_and_route_to_the_general_kernel():
-    # INT3, INT2 and 3-bit keys with 2-bit values are valid per-head layouts served by the general kernel; the
-    # INT4-specialised kernels keep INT4 only; the block-shared mode stays INT4
+def test_low_bit_layouts_check_and_route():
+    # INT3, INT2 and 3-bit keys with 2-bit values are valid per-head layouts: the fast kernel serves the
+    # combinations it is compiled for, the general kernel the others (and the residual); block-shared stays INT4
     base = synth.WORKLOADS["llama8b_layer_8k"]
-    for kb, vb in [(3, 0), (2, 0), (3, 2), (4, 2)]:
-        L = kvc.make_layout(**base.scaled(latent_bits=kb, latent_bits_v=vb).layout_kwargs())
-        assert kvc.layout_check(L) == 0 and kvc.decode_path(L) == kvc.PATH_HEAD, (kb, vb)
+    for kw, path in [(dict(latent_bits=3), kvc.PATH_INT4), (dict(latent_bits=2), kvc.PATH_INT4),
+                     (dict(latent_bits=3, latent_bits_v=2), kvc.PATH_INT4),
+                     (dict(latent_bits=4, latent_bits_v=2), None),  # valid, but no kernel variant: UNSUPPORTED
+                     (dict(r_k=40, r_v=40, latent_bits=3), kvc.PATH_HEAD),
+                     (dict(r_k=40, r_v=40, latent_bits=3, latent_bits_v=2), kvc.PATH_HEAD),
+                     (dict(r_v=48), kvc.PATH_HEAD)]:  # no fast variant for 3 key and 3 value steps: the general one
+        L = kvc.make_layout(**base.scaled(**kw).layout_kwargs())
+        st = kvc.layout_check(L)
+        assert (st == -2) if path is None else (st == 0 and kvc.decode_path(L) == path), kw
     res = kvc.make_layout(**synth.WORKLOADS["residual_128k"].scaled(latent_bits=3).layout_kwargs())
     assert kvc.decode_path(res) == kvc.PATH_HEAD
     var = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].scaled(latent_bits=2).layout_kwargs())
-    assert kvc.layout_check(var) == 0 and kvc.decode_path(var) == kvc.PATH_HEAD
+    assert kvc.layout_check(var) == 0 and kvc.decode_path(var) == kvc.PATH_INT4
+    var48 = synth.WORKLOADS["varrank_paged_32k"].scaled(r_k=48, r_v=48, rank_choices=(8, 16, 32, 48), latent_bits=2)
+    assert kvc.decode_path(kvc.make_layout(**var48.layout_kwargs())) == kvc.PATH_HEAD
     for kw, want in [(dict(latent_bits=5), -1), (dict(latent_bits=4, latent_bits_v=1), -1),
                      (dict(latent_bits=32, latent_bits_v=4), -1), (dict(latent_bits=4, latent_bits_v=32), -1)]:
         assert kvc.layout_check(kvc.make_layout(**base.scaled(**kw).layout_kwargs())) == want, kw

@@ -32,6 +32,10 @@ CASES = [
     ("varrank_paged_32k", dict(B=2, T=1000, latent_bits=3), [1000, 517]),
     ("varrank_paged_32k", dict(B=2, T=600, latent_bits=2), [600, 33]),
     ("residual_128k", dict(B=2, T=700, latent_bits=3), [700, 300]),
+    # lower-bit codecs that the fast kernel has no variant for: the general per-head kernel
+    ("llama8b_layer_8k", dict(T=700, r_k=40, r_v=40, latent_bits=3), None),
+    ("llama8b_layer_8k", dict(B=2, T=500, r_k=40, r_v=40, latent_bits=3, latent_bits_v=2), [500, 77]),
+    ("varrank_paged_32k", dict(B=2, T=800, r_k=48, r_v=48, rank_choices=(8, 16, 32, 48), latent_bits=2), [800, 301]),
 ]
 
 

@@ -84,3 +84,16 @@ def test_fullsize_residual_128k():
     w = synth.WORKLOADS["residual_128k"]
     inp = synth.make_inputs(w, device="cuda")
     _check(w, inp, [6], [1, 6], compare_whole_pool=False)
+
+
+def test_fullsize_varrank_paged_32k_int3():
+    # the 32K variable-rank workload with INT3 latents (general per-head kernel)
+    w = synth.WORKLOADS["varrank_paged_32k_int3"]
+    inp = synth.make_inputs(w, device="cuda")
+    _check(w, inp, [4], [2, 5], compare_whole_pool=True)
+
+
+def test_fullsize_llama8b_layer_8k_k3v2():
+    w = synth.WORKLOADS["llama8b_layer_8k_k3v2"]
+    inp = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in synth.make_inputs(w).items()}
+    _check(w, inp, [0], list(range(8)), compare_whole_pool=True)
