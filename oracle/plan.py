@@ -8,67 +8,87 @@ JoLT for the KV cache", abstract): the keys and the values of each layer group a
 Lagrangian multiplier chooses every cell's ranks and residual bit width under a shared byte budget, before
 anything is compressed.  Reading: each cell c has options o (a rank and a residual width, say) with a
 distortion D[c][o] and a storage cost B[c][o].  For a multiplier lam >= 0 every cell takes the option that
-minimizes D + lam B (ties: fewer bytes, then the lower option index).  The multiplier is the smallest lam whose
-total bytes fit the budget.  The total only changes where some cell's choice does, at the crossing points
-lam = (D[c][o1] - D[c][o2]) / (B[c][o2] - B[c][o1]); those and 0 are the candidates.  At that multiplier several
-cells may tie between options (that is where they switch), and taking all of them at their cheapest can leave
-budget unused: cell by cell, in order, a tied cell then takes its tied option of most bytes that still fits
-(equal bytes: the lower index).  Every cell still minimizes D + lam B, so no allocation of at most the same
-bytes has less total distortion (Everett's theorem).
+minimizes D + lam B (ties: fewer bytes).  As lam falls from infinity each cell walks up its lower convex hull of
+(bytes, distortion) points, switching at its crossing multipliers (the breakpoints); the allocation uses the
+smallest of 0 and all breakpoints whose choices fit the budget.  The choice at a multiplier is decided by
+comparing it with the breakpoints themselves, not by evaluating D + lam B in floating point, so that rounding
+cannot make the bytes non-monotone in lam.  At the chosen multiplier, cells sitting exactly on a breakpoint (a
+tie between two vertices) then move on, cell by cell in order, while the bytes still fit.  Every cell's choice
+minimizes D + lam B, so no allocation of at most the same bytes has less total distortion (Everett's theorem).
 """
 import numpy as np
 
 
-def choose(D, B, lam):
-    """Per-cell option minimizing D + lam B, ties to fewer bytes, then the lower index: int [n_cells]."""
-    D = np.asarray(D, dtype=np.float64)
-    B = np.asarray(B, dtype=np.float64)
-    out = np.zeros(D.shape[0], dtype=np.int64)
-    for c in range(D.shape[0]):
+def hull(D_c, B_c):
+    """One cell's Lagrangian path: (vertices, breakpoints).  From the cheapest option (fewest bytes, then least
+    distortion, then lowest index), each step goes to the option of more bytes and less distortion with the
+    largest crossing multiplier (D_v - D_p) / (B_p - B_v), the farthest of equal ones (most bytes, then the lowest
+    index); breakpoints are kept non-increasing.  Choosing vertex k for multipliers in [lam_k, lam_(k-1)) is what
+    minimizing D + lam B with ties to fewer bytes gives, decided by comparisons with these numbers only."""
+    n = len(D_c)
+    order = sorted(range(n), key=lambda o: (B_c[o], D_c[o], o))
+    v = order[0]
+    verts, lams = [v], []
+    while True:
         best = None
-        for o in range(D.shape[1]):
-            key = (D[c, o] + lam * B[c, o], B[c, o], o)
-            if best is None or key < best:
-                best = key
-        out[c] = best[2]
-    return out
+        for p in range(n):
+            if B_c[p] > B_c[v] and D_c[p] < D_c[v]:
+                lam = (D_c[v] - D_c[p]) / (B_c[p] - B_c[v])
+                key = (lam, B_c[p], -p)
+                if best is None or key > best[0]:
+                    best = (key, p)
+        if best is None:
+            return verts, lams
+        lam, p = best[0][0], best[1]
+        if lams and lam > lams[-1]:
+            lam = lams[-1]
+        verts.append(p)
+        lams.append(lam)
+        v = p
 
 
-def candidates(D, B):
-    """0 and every positive crossing point of two options of one cell, increasing."""
-    D = np.asarray(D, dtype=np.float64)
-    B = np.asarray(B, dtype=np.float64)
-    lams = {0.0}
-    for c in range(D.shape[0]):
-        for o1 in range(D.shape[1]):
-            for o2 in range(D.shape[1]):
-                if B[c, o2] > B[c, o1] and D[c, o1] > D[c, o2]:
-                    lams.add((D[c, o1] - D[c, o2]) / (B[c, o2] - B[c, o1]))
-    return sorted(lams)
+def walk(lams, lam):
+    """Index of the vertex chosen at multiplier lam: every breakpoint strictly above lam is passed."""
+    k = 0
+    while k < len(lams) and lams[k] > lam:
+        k += 1
+    return k
 
 
 def plan(D, B, budget):
-    """(choice int [n_cells], lam) of the smallest candidate lam whose choices fit the budget; None if even the
-    cheapest options do not fit."""
+    """(choice int [n_cells], lam) for the smallest of 0 and the cells' breakpoints whose choices fit; then the
+    tie fill.  None if even the cheapest options do not fit."""
     D = np.asarray(D, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
-    rows = np.arange(D.shape[0])
-    for lam in candidates(D, B):
-        ch = choose(D, B, lam)
-        used = B[rows, ch].sum()
+    nc = D.shape[0]
+    hulls = [hull(list(D[c]), list(B[c])) for c in range(nc)]
+    cands = sorted({0.0} | {l for _, ls in hulls for l in ls})
+    for lam in cands:
+        ks = [walk(ls, lam) for _, ls in hulls]
+        used = sum(B[c, hulls[c][0][ks[c]]] for c in range(nc))
         if used > budget:
             continue
-        for c in range(D.shape[0]):
-            v = D[c] + lam * B[c]
-            tied = [o for o in range(D.shape[1]) if v[o] == v[ch[c]]]
-            for o in sorted(tied, key=lambda o: (-B[c, o], o)):
-                if used - B[c, ch[c]] + B[c, o] <= budget:
-                    used += B[c, o] - B[c, ch[c]]
-                    ch[c] = o
+        for c in range(nc):  # tie fill: a cell on a breakpoint equal to lam moves on while the bytes fit
+            verts, ls = hulls[c]
+            while ks[c] < len(ls) and ls[ks[c]] == lam:
+                extra = B[c, verts[ks[c] + 1]] - B[c, verts[ks[c]]]
+                if used + extra > budget:
                     break
-        return ch, lam
-    # at the largest crossing every cell already holds its cheapest option (ties go to fewer bytes)
+                used += extra
+                ks[c] += 1
+        return np.array([hulls[c][0][ks[c]] for c in range(nc)], dtype=np.int64), lam
     return None
+
+
+def choose(D, B, lam):
+    """Per-cell option at multiplier lam (no tie fill): int [n_cells]."""
+    D = np.asarray(D, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    out = []
+    for c in range(D.shape[0]):
+        verts, ls = hull(list(D[c]), list(B[c]))
+        out.append(verts[walk(ls, lam)])
+    return np.array(out, dtype=np.int64)
 
 
 def tail_energy(sigma2, r):
