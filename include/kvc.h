@@ -315,6 +315,29 @@ typedef struct {
  * workgroup per sequence.  Deterministic. */
 kvc_status kvc_rank_alloc(const kvc_alloc_in* in, uint8_t* ranks, void* stream);
 
+/* Inputs of kvc_plan_budget (host memory). */
+typedef struct {
+  int32_t n_cells;               /* cells, e.g. the keys and the values of each layer (group)   */
+  int32_t n_options;             /* options per cell, 1..1024 (pad a shorter list with a copy); */
+                                 /*   n_cells * n_options <= 2^22                                */
+  const double* distortion;      /* [n_cells][n_options] reconstruction error of each option   */
+  const double* bytes;           /* [n_cells][n_options] storage cost, >= 0 (whole numbers keep */
+                                 /*   the sums exact)                                           */
+  double budget;                 /* total bytes                                                 */
+} kvc_plan_in;
+
+/* Lagrangian allocation of a byte budget ("JoLT: Near-Lossless KV Cache Compression" thesis page, "How
+ * JoLT works": one multiplier picks every cell's ranks and residual bit width under a shared budget).  For
+ * a multiplier lam >= 0 each cell takes the option minimizing distortion + lam * bytes (ties: fewer bytes);
+ * as lam falls the choice walks up the cell's lower convex hull of (bytes, distortion) points, switching at
+ * breakpoints, and the choice at lam is decided by comparing lam with those breakpoints.  lam is the
+ * smallest of 0 and the breakpoints whose choices fit the budget; then cells on a breakpoint equal to lam
+ * move on along their hull, in cell order, while the bytes still fit.  No allocation of at most the same
+ * bytes has less total distortion.  Host code, no device work.  choice: [n_cells] option per cell;
+ * lambda (optional): the multiplier.  INVALID_ARG for non-finite or negative inputs, sizes out of range,
+ * or a budget below the cheapest options. */
+kvc_status kvc_plan_budget(const kvc_plan_in* in, int32_t* choice, double* lambda);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

@@ -35,6 +35,7 @@ kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32
 kvc_status salience_impl(const kvc_salience_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                          size_t* bytes_out);
 kvc_status rank_alloc_impl(const kvc_alloc_in& in, uint8_t* ranks, hipStream_t st);
+kvc_status plan_impl(const kvc_plan_in& in, int32_t* choice, double* lambda);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                       size_t* need);
 
@@ -232,6 +233,11 @@ kvc_status kvc_salience(const kvc_salience_in* in, float* out, void* ws, size_t 
 kvc_status kvc_rank_alloc(const kvc_alloc_in* in, uint8_t* ranks, void* stream) {
   if (!in) return KVC_ERR_INVALID_ARG;
   return rank_alloc_impl(*in, ranks, (hipStream_t)stream);
+}
+
+kvc_status kvc_plan_budget(const kvc_plan_in* in, int32_t* choice, double* lambda) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return plan_impl(*in, choice, lambda);
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

@@ -25,7 +25,7 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
-           "kvc_rank_alloc"]
+           "kvc_rank_alloc", "kvc_plan_budget"]
 
 
 class KvcError(RuntimeError):
@@ -88,6 +88,11 @@ class AllocIn(C.Structure):
                 ("sal", C.c_void_p)]
 
 
+class PlanIn(C.Structure):
+    _fields_ = [("n_cells", C.c_int32), ("n_options", C.c_int32), ("distortion", C.c_void_p), ("bytes", C.c_void_p),
+                ("budget", C.c_double)]
+
+
 _lib = None
 
 
@@ -120,6 +125,7 @@ def lib():
         L.kvc_salience_workspace_bytes.argtypes = [P, P]; L.kvc_salience_workspace_bytes.restype = C.c_int32
         L.kvc_salience.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_salience.restype = C.c_int32
         L.kvc_rank_alloc.argtypes = [P, P, P]; L.kvc_rank_alloc.restype = C.c_int32
+        L.kvc_plan_budget.argtypes = [P, P, P]; L.kvc_plan_budget.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -389,3 +395,15 @@ def rank_alloc(sal, seq_len, ladder, step_w, mean_rank, out=None):
         out = torch.empty(sal.shape, dtype=torch.uint8, device=sal.device)
     _check(lib().kvc_rank_alloc(C.byref(inp), _ptr(out), _stream()), "kvc_rank_alloc")
     return out
+
+
+def plan_budget(distortion, bytes_, budget):
+    """kvc_plan_budget (host): distortion, bytes_ array-likes [n_cells, n_options] -> (choice int32 [n_cells], lam)."""
+    import numpy as np
+    D = np.ascontiguousarray(distortion, dtype=np.float64)
+    Bb = np.ascontiguousarray(bytes_, dtype=np.float64)
+    choice = np.zeros(D.shape[0], dtype=np.int32)
+    lam = C.c_double()
+    inp = PlanIn(D.shape[0], D.shape[1], D.ctypes.data_as(C.c_void_p), Bb.ctypes.data_as(C.c_void_p), float(budget))
+    _check(lib().kvc_plan_budget(C.byref(inp), choice.ctypes.data_as(C.c_void_p), C.byref(lam)), "kvc_plan_budget")
+    return choice, lam.value
