@@ -130,10 +130,9 @@ def test_fit_empty_heads_give_axes():
 
 
 def test_fit_feeds_compress_from_dense():
-    # the fitted bf16 bases are the layout kvc_compress takes: its fp32 projections of the same rows agree
-    # with the oracle's projection onto those bases
-    from oracle import ref
-    from tests.helpers import layout, np_any, np_u16
+    # the fitted bf16 bases are the layout kvc_compress takes: the latents it projects the same rows to hold
+    # (per head) the energy the optimal rank-r subspace captures, up to the bf16 rounding of the basis (each
+    # entry within 2^-9 of itself moves the captured energy by well under 1%) and the fit's own tolerance
     w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=2, T=600)
     inp = synth.make_inputs(w, seq_len=[600, 523])
     k = synth.make_prefill_rows(w.B, w.T, w.n_kv_heads, 128, seed=4)
@@ -143,17 +142,19 @@ def test_fit_feeds_compress_from_dense():
     bv, _, _ = kvc.fit_basis(v.cuda().contiguous(), sl, w.r_v, w.r_v, want_f32=False, want_sigma2=False)
     L = kvc.make_layout(**w.layout_kwargs())
     cache = kvc.DeviceCache.allocate(L, w.n_pages)
+    ranks = torch.full_like(inp["ranks"], w.r_k).cuda()          # every token at the full rank
     lk = torch.zeros_like(inp["lat_k"]).cuda(); lv = torch.zeros_like(inp["lat_v"]).cuda()
-    kvc.compress(L, cache, inp["block_table"].cuda(), sl, w.T, ranks=inp["ranks"].cuda(), lat_k=lk, lat_v=lv,
+    kvc.compress(L, cache, inp["block_table"].cuda(), sl, w.T, ranks=ranks, lat_k=lk, lat_v=lv,
                  k=k.cuda().contiguous(), v=v.cuda().contiguous(), basis_k=bk, basis_v=bv)
     torch.cuda.synchronize()
-    olk, olv, _, _ = ref.project(layout(w), np_any(inp["seq_len"]), w.T, np_any(inp["ranks"]), k.numpy(), v.numpy(),
-                                 np_u16(bk.cpu()), np_u16(bv.cpu()))
-    seq = np_any(inp["seq_len"])
-    for got, want in ((lk, olk), (lv, olv)):
-        g_ = got.cpu().numpy()
-        for b in range(w.B):
-            assert np.allclose(g_[b, :seq[b]], want[b, :seq[b]], rtol=0, atol=1e-5 * np.abs(want).max())
+    seq = [600, 523]
+    for x, lat, r in ((k, lk, w.r_k), (v, lv, w.r_v)):
+        _, os2 = F.fit_basis(x.numpy(), seq, r)
+        lat_ = lat.cpu().double().numpy()
+        for h in range(w.n_kv_heads):
+            captured = sum(float((lat_[b, :seq[b], h] ** 2).sum()) for b in range(w.B))
+            opt = float(os2[h][:r].sum())
+            assert abs(captured - opt) <= 1e-2 * opt, (h, captured, opt)
 
 
 def test_fit_full_size_sampled_heads():
