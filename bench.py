@@ -94,15 +94,19 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 
 # The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
-# and head from the 512-dim latent) and the 128K rotated-residual cache (HBM).
-OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2")
+# and head from the 512-dim latent) and the 128K rotated-residual cache (HBM); the lower-bit codecs; and a layer
+# group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core).
+OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2",
+         "tucker_group_32k")
 
 
 def decode_flops(w) -> int:
     """Algorithmic flops of one decode step: key up-projection, scores and the latent value product (the
     residual's Hadamard rotations are a fast transform, a few adds per element, and are not counted)."""
     n_tok = w.B * w.T * (w.n_layers if w.shared else 1)
-    if w.shared:
+    if w.tucker:  # keys need only the key factor's rows of the latent; the values' product runs over all of it
+        per_tok = 2 * w.head_dim * w.tucker[0] * w.n_kv_heads + 2 * w.head_dim * w.n_q_heads + 2 * w.r_v * w.n_q_heads
+    elif w.shared:
         per_tok = 2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.head_dim * w.n_q_heads + 2 * w.r_v * w.n_q_heads
     else:
         per_tok = (2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.head_dim * w.n_q_heads
@@ -124,6 +128,20 @@ def other_workloads(steps: int, warmup: int) -> dict:
         cache = kvc.DeviceCache.allocate(L, w.n_pages)
         kvc.compress(L, cache, inp["block_table"], inp["seq_len"], w.T, ranks=inp["ranks"], lat_k=inp["lat_k"],
                      lat_v=inp["lat_v"], res_k=inp["res_k"], res_v=inp["res_v"])
+        extra = {}
+        if w.tucker:  # per-sequence up-projections from the factors (prefill side; timed on its own)
+            xe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            for _ in range(5):
+                xe[0].record()
+                wk, _ = kvc.tucker_expand(inp["tk_uf"], inp["tk_core"], w.r_k, 0)
+                wv, _ = kvc.tucker_expand(inp["tv_uf"], inp["tv_core"], w.r_k, w.tucker[0])
+                xe[1].record()
+                torch.cuda.synchronize()
+                times.append(xe[0].elapsed_time(xe[1]))
+            inp["wk"], inp["wv"] = wk, wv
+            extra = {"tucker_expand_ms_median": round(sorted(times)[2], 5),
+                     "per_sequence_w_bytes": 2 * wk.numel() * 2}
         plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
                               q_pos=inp["q_pos"])
         for k in ("lat_k", "lat_v", "res_k", "res_v"):
@@ -150,7 +168,7 @@ def other_workloads(steps: int, warmup: int) -> dict:
                 kvc.PATH_SHARED: "block-shared kernel", kvc.PATH_RES: "INT4 residual kernel"}[kvc.decode_path(L)]
         r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),
              "compressed_bytes": nbytes, "hbm_gbs": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
-             "flops": flops, "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1)}
+             "flops": flops, "tflops": round(flops / (k_ms * 1e-3) / 1e12, 1), **extra}
         if name.startswith("llama8b_layer_8k"):
             r["bound"] = "latency (the 4.7 MB cache stays in the last-level cache between calls)"
         elif w.shared:

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -147,6 +147,10 @@ typedef struct {
   const uint16_t* wk;            /* bf16 basis [Hkv][d][r_k_cap]; shared: W_k [L][latent][Hkv*d] */
   const uint16_t* wv;            /* bf16 basis [Hkv][d][r_v_cap]; shared: W_v [L][latent][Hkv*d] */
   int32_t num_splits;            /* context splits per (sequence, head); 0 = automatic          */
+  int64_t w_seq_stride;          /* shared mode: elements from one sequence's W_k (and W_v) to  */
+                                 /*   the next, a multiple of 8; 0 = one pair for all sequences  */
+                                 /*   (per-sequence up-projections, e.g. expanded from a Tucker */
+                                 /*   core fitted per prefill cache).  Per-head mode: 0          */
 } kvc_decode_in;
 
 /* Inputs of kvc_dense_decode_attn: plain attention over a paged bf16 cache. */
@@ -337,6 +341,35 @@ typedef struct {
  * lambda (optional): the multiplier.  INVALID_ARG for non-finite or negative inputs, sizes out of range,
  * or a budget below the cheapest options. */
 kvc_status kvc_plan_budget(const kvc_plan_in* in, int32_t* choice, double* lambda);
+
+/* Inputs of kvc_tucker_expand (device memory). */
+typedef struct {
+  int32_t n_seq;                 /* sequences, each with its own factors and up-projections      */
+  int32_t n_layers;              /* L, layers of the group                                       */
+  int32_t n_kv_heads;            /* Hkv                                                          */
+  int32_t head_dim;              /* d (128)                                                      */
+  int32_t r_t;                   /* token rank: latent rows written                              */
+  int32_t r_f;                   /* feature rank, 1..d                                           */
+  int32_t latent;                /* rows of each W[l] (the shared latent dimension), <= 4096     */
+  int32_t row0;                  /* first row written; row0 + r_t <= latent                      */
+  const float* u_f;              /* [n_seq][d][r_f] feature factor                               */
+  const float* core;             /* [n_seq][L][Hkv][r_t][r_f] core, one (layer, head) slice after */
+                                 /*   another                                                    */
+} kvc_tucker_in;
+
+/* Up-projections of a partial Tucker cache ("JoLT: Near-Lossless KV Cache Compression" thesis page, "How
+ * JoLT works": a layer group's keys or values as a token x feature x head x layer tensor, only the token
+ * and feature modes truncated, X ~ G x_1 U_t x_2 U_f).  Token t's factor row U_t[t] is the block-shared
+ * latent of every head and layer of the group; head h of layer l rebuilds its pre-RoPE key (value) as
+ * W_hl^T U_t[t] with W_hl = U_f G[:, :, h, l]^T.  Writes, for c < r_t,
+ *   w[s][l][row0 + c][h*d + i] = sum_j u_f[s][i][j] core[s][l][h][c][j]
+ * (fp32 fused multiply-adds in increasing j, stored as bf16 rounded to nearest even; w_f32, optional, the
+ * fp32 sums) in the layout kvc_decode_attn takes for per-sequence up-projections ([n_seq][L][latent][Hkv*d],
+ * w_seq_stride = L * latent * Hkv * d).  Rows outside row0..row0+r_t-1 are not written: keys and values
+ * with their own token factors share one latent as [U_t(keys) | U_t(values)], W_k holding the key rows
+ * (values' rows zero) and W_v the reverse.  Asynchronous on stream.  INVALID_ARG for bad sizes or null
+ * pointers, UNSUPPORTED for d != 128, MISALIGNED for pointers not 4-byte aligned. */
+kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32, void* stream);
 
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);

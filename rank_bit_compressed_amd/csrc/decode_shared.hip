@@ -57,6 +57,7 @@ struct DecodeSharedArgs {
   const int32_t* q_pos;
   const void* q;
   const uint16_t* wk;
+  int64_t w_stride;  // elements between sequences' W_k (0: one for all)
   float* ws;
   int q_bf16, B, Hkv, Hq, L, max_blocks, P, G, n_splits, st_per_split, part_stride;
   double theta;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   h8 wf[SNB][SNJ];
   {
     const int width = a.Hkv * SD;
-    const uint16_t* W = a.wk + (size_t)l * SLAT * width + (size_t)h * SD;
+    const uint16_t* W = a.wk + (size_t)b * a.w_stride + (size_t)l * SLAT * width + (size_t)h * SD;
 #pragma unroll
     for (int g = 0; g < SNB; ++g) {
       const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
@@ -407,8 +408,9 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 // out[l][b][h*4 + hq] = W_v[l][:, h*128 : (h+1)*128]^T c* / l*, over the splits' partials: one workgroup per
 // (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the threads,
 // eight independent partial sums).
-__global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, float* out, int B,
-                                                          int Hkv, int Hq, int n_splits, int part_stride) {
+__global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, int64_t w_stride,
+                                                          float* out, int B, int Hkv, int Hq, int n_splits,
+                                                          int part_stride) {
   __shared__ float cst[SLAT];
   __shared__ float lst;
   int id = blockIdx.x;
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
   if (d == 0) lst = lsum;
   __syncthreads();
   const size_t width = (size_t)Hkv * SD;
-  const uint16_t* W = wv + (size_t)l * SLAT * width + (size_t)h * SD + d;
+  const uint16_t* W = wv + (size_t)b * w_stride + (size_t)l * SLAT * width + (size_t)h * SD + d;
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int i = 0; i < SLAT; i += 8) {
 #pragma unroll
@@ -461,7 +463,8 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
                                 void* ws, int n_splits, int st_per_split, hipStream_t st) {
   DecodeSharedArgs a;
   a.pool = C.pool; a.page_off = C.page_off; a.block_table = in.block_table; a.seq_len = in.seq_len;
-  a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk; a.ws = (float*)ws; a.q_bf16 = in.q_dtype == KVC_BF16;
+  a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk; a.w_stride = in.w_seq_stride; a.ws = (float*)ws;
+  a.q_bf16 = in.q_dtype == KVC_BF16;
   a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.L = L.n_layers; a.max_blocks = in.max_blocks;
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
@@ -475,8 +478,8 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv, out,
-                     in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride);
+  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,
+                     in.w_seq_stride, out, in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride);
   return hipGetLastError();
 }
 

@@ -143,12 +143,6 @@ __global__ __launch_bounds__(256) void fit_reduce_kernel(const float* __restrict
   }
 }
 
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 // Pair P of round k (0..126) of the round-robin schedule over 128 indices: (k, 127) for P = 0, else
 // ((k + P) mod 127, (k - P) mod 127); over the 127 rounds every pair meets once (127 is prime).  The pair is
 // left unordered: across the lanes of a wave (consecutive P) both members then run through consecutive

@@ -118,6 +118,13 @@ __device__ inline uint32_t pack_h2(float a, float b) {
   return as_u32(v);
 }
 
+// fp32 -> bf16 bits, rounded to nearest even.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 // bf16 bits -> fp16 (exact for the normal range of fp16).
 __device__ inline _Float16 bf16_to_h(uint16_t b) {
   return (_Float16)__builtin_bit_cast(float, (uint32_t)b << 16);

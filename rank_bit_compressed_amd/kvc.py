@@ -25,7 +25,7 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
-           "kvc_rank_alloc", "kvc_plan_budget"]
+           "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand"]
 
 
 class KvcError(RuntimeError):
@@ -61,7 +61,7 @@ class CompressIn(C.Structure):
 class DecodeIn(C.Structure):
     _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32), ("block_table", C.c_void_p),
                 ("seq_len", C.c_void_p), ("q_pos", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32),
-                ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32)]
+                ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32), ("w_seq_stride", C.c_int64)]
 
 
 class DenseIn(C.Structure):
@@ -126,6 +126,7 @@ def lib():
         L.kvc_salience.argtypes = [P, P, P, C.c_size_t, P]; L.kvc_salience.restype = C.c_int32
         L.kvc_rank_alloc.argtypes = [P, P, P]; L.kvc_rank_alloc.restype = C.c_int32
         L.kvc_plan_budget.argtypes = [P, P, P]; L.kvc_plan_budget.restype = C.c_int32
+        L.kvc_tucker_expand.argtypes = [P, P, P, P]; L.kvc_tucker_expand.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -228,24 +229,34 @@ def _q_dtype(q):
     raise TypeError("q must be fp32 or bf16")
 
 
-def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0) -> DecodeIn:
+def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, w_seq_stride=0) -> DecodeIn:
     B, max_blocks = block_table.shape
     return DecodeIn(B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len), _ptr(q_pos), _ptr(q), _q_dtype(q),
-                    _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits)
+                    _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits, w_seq_stride)
+
+
+def _w_stride(layout, wk, wv, B):
+    """Elements between sequences' up-projections: 0 unless shared mode with per-sequence [B, L, latent, Hkv d]."""
+    if not (layout.shared and wk.dim() == 4):
+        return 0
+    if wv.shape != wk.shape or wk.shape[0] != B or not (wk.is_contiguous() and wv.is_contiguous()):
+        raise ValueError("per-sequence W_k / W_v must both be contiguous [B, L, latent, Hkv * d]")
+    return wk[0].numel()
 
 
 def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
                 num_splits=0, out=None, ws=None, events=None):
     """kvc_decode_attn -> fp32 [(L,) B, Hq, d].  events: optional (begin, end) pair of recorded-once
     torch.cuda.Event objects; the call then goes through kvc_decode_attn_timed, which records them around
-    the attention kernel alone."""
+    the attention kernel alone.  Shared mode: wk, wv [L, latent, Hkv * d] for all sequences, or
+    [B, L, latent, Hkv * d] (contiguous), one pair per sequence."""
     B = block_table.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(layout, B, max_T, num_splits)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits)
+    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B))
     c = cache.c()
     if events is None:
         _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
@@ -272,7 +283,7 @@ class DecodePlan:
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws)
         self._layout, self._cache = layout, cache.c()
-        self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits)
+        self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B))
         self._args = (C.byref(self._layout), C.byref(self._cache), C.byref(self._in), _ptr(self.out), _ptr(ws),
                       ws.numel())
         self._fn, self._fn_timed = lib().kvc_decode_attn, lib().kvc_decode_attn_timed
@@ -407,3 +418,26 @@ def plan_budget(distortion, bytes_, budget):
     inp = PlanIn(D.shape[0], D.shape[1], D.ctypes.data_as(C.c_void_p), Bb.ctypes.data_as(C.c_void_p), float(budget))
     _check(lib().kvc_plan_budget(C.byref(inp), choice.ctypes.data_as(C.c_void_p), C.byref(lam)), "kvc_plan_budget")
     return choice, lam.value
+
+
+class TuckerIn(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("n_seq", "n_layers", "n_kv_heads", "head_dim", "r_t", "r_f", "latent",
+                                         "row0")] + [("u_f", C.c_void_p), ("core", C.c_void_p)]
+
+
+def tucker_expand(u_f, core, latent, row0=0, w=None, want_f32=False):
+    """kvc_tucker_expand: u_f fp32 [S, d, r_f], core fp32 [S, L, Hkv, r_t, r_f] (device) -> (w bf16
+    [S, L, latent, Hkv * d], w32 fp32 of the same shape or None).  Rows outside row0..row0+r_t-1 of a given w
+    are left as they are; a new w starts at zero."""
+    S, d, r_f = u_f.shape
+    _, L, Hkv, r_t, _ = core.shape
+    if w is None:
+        w = torch.zeros(S, L, latent, Hkv * d, dtype=torch.bfloat16, device=u_f.device)
+    w32 = torch.zeros(w.shape, dtype=torch.float32, device=u_f.device) if want_f32 else None
+    for t in (u_f, core, w):
+        if not t.is_contiguous():
+            raise ValueError("tucker_expand takes contiguous tensors")
+    inp = TuckerIn(S, L, Hkv, d, r_t, r_f, latent, row0, _ptr(u_f), _ptr(core))
+    _check(lib().kvc_tucker_expand(C.byref(inp), _ptr(w.view(torch.int16)), _ptr(w32), _stream()),
+           "kvc_tucker_expand")
+    return w, w32

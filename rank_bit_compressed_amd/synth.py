@@ -26,7 +26,15 @@ Distributions (the pages give shapes, not data):
     spread of singular values without repeated ones;
   * window queries for salience (pre-RoPE, fp32): N(0, 1) per element;
   * salience for the rank-allocation tests: exp(N(0, 1.5^2)) per token, a
-    heavy-tailed positive spread like attention mass, rounded to fp32.
+    heavy-tailed positive spread like attention mass, rounded to fp32;
+  * partial Tucker factors of a layer group (keys and values separately), per
+    sequence: token factor rows N(0, 1/T) per element (the scale of a factor
+    with orthonormal columns over T tokens); the feature factor an orthonormal
+    d x r_f matrix as for bases; the core [L][Hkv][r_t][r_f] N(0, 1) scaled by
+    sqrt(T d / (r_t r_f)) * s_c, s_c = (c + 1)^-0.35 normalised to mean square
+    1 over c (a decaying token-mode spectrum), so rebuilt keys and values have
+    about unit variance like the other workloads.  The block-shared latent of
+    such a workload is the key factor row followed by the value factor row.
 """
 from __future__ import annotations
 
@@ -63,6 +71,7 @@ class Workload:
     latent_decay: float = 0.7     # 0 = i.i.d. N(0, 1)
     residual_std: float = 0.05
     w_std: float = 0.0            # block-shared mode: W entries N(0, w_std^2)
+    tucker: tuple = ()            # block-shared from partial Tucker factors: (key r_t, value r_t, r_f)
     seed: int = 0
 
     def scaled(self, **kw) -> "Workload":
@@ -106,6 +115,11 @@ WORKLOADS = {
     "residual_128k": Workload("residual_128k", B=8, T=131072, n_q_heads=32, n_kv_heads=8, head_dim=128,
                               r_k=48, r_v=64, group=32, residual_bits=2, rope_theta=500000.0,
                               shuffle_pages=True, seed=15),
+    # a 4-layer group of keys and values in partial Tucker form per sequence (token ranks 256 + 256 = the
+    # 512-dim block-shared latent, feature rank 64), decoded through per-sequence up-projections
+    "tucker_group_32k": Workload("tucker_group_32k", B=4, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                 r_k=512, r_v=512, group=64, shared=True, n_layers=4, rope_theta=500000.0,
+                                 latent_decay=0.0, tucker=(256, 256, 64), seed=16),
     # the lower-bit codecs of the BellowsKV page's retention table on per-head latents: the 32K variable-rank
     # workload with INT3 latents, and the 8K layer with 3-bit keys and 2-bit values
     "varrank_paged_32k_int3": Workload("varrank_paged_32k_int3", B=16, T=32768, n_q_heads=32, n_kv_heads=8,
@@ -164,7 +178,20 @@ def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
     else:
         out["ranks"] = None
     gl = _gen(w, 3, dev)
-    if w.shared:
+    if w.tucker:
+        rtk, rtv, rf = w.tucker
+        assert w.shared and rtk + rtv == w.r_k
+        utk = torch.randn(B, T, rtk, generator=gl, device=dev, dtype=torch.float32) / math.sqrt(T)
+        utv = torch.randn(B, T, rtv, generator=_gen(w, 4, dev), device=dev, dtype=torch.float32) / math.sqrt(T)
+        out["lat_k"], out["lat_v"] = torch.cat([utk, utv], dim=2).contiguous(), None
+        for tag, rt, s_uf, s_core in (("k", rtk, 8, 7), ("v", rtv, 9, 17)):
+            out[f"t{tag}_uf"] = _orthonormal(w, s_uf, d, rf, B).to(torch.float32).to(dev)
+            c = torch.arange(1, rt + 1, dtype=torch.float64) ** -0.35
+            c = c / c.pow(2).mean().sqrt()
+            core = torch.randn(B, w.n_layers, Hkv, rt, rf, generator=_gen(w, s_core, "cpu"), dtype=torch.float64)
+            core *= math.sqrt(T * d / (rt * rf)) * c[:, None]
+            out[f"t{tag}_core"] = core.to(torch.float32).to(dev)
+    elif w.shared:
         lat = torch.randn(B, T, w.r_k, generator=gl, device=dev, dtype=torch.float32)
         if w.latent_decay:
             lat *= _decay_scale(w.r_k, w.latent_decay, dev)
@@ -181,7 +208,9 @@ def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
         out["res_v"] = torch.randn(B, T, Hkv, d, generator=_gen(w, 6, dev), device=dev) * w.residual_std
     else:
         out["res_k"] = out["res_v"] = None
-    if w.shared:
+    if w.tucker:
+        out["wk"] = out["wv"] = None                     # expanded from the factors by each side
+    elif w.shared:
         gw = _gen(w, 7, "cpu")
         shape = (w.n_layers, w.r_k, Hkv * d)
         out["wk"] = (torch.randn(shape, generator=gw) * w.w_std).to(torch.bfloat16).to(dev)

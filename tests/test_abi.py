@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 2
+    assert kvc.lib().kvc_abi_version() == 3
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -54,7 +54,7 @@ def test_calls_reject_bad_arguments_without_launching():
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 0, 100, 0, C.byref(out)) == -1
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 2, 100, 0, C.byref(out)) == 0 and out.value > 0
     cache = kvc.Cache(None, 0, None, None, None, None, 0)
-    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0)
+    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(16), C.c_void_p(16), 1 << 20,
                                None) == -1
     cin = kvc.CompressIn(0, 2, 100, 1, *([None] * 11))
@@ -62,7 +62,7 @@ def test_calls_reject_bad_arguments_without_launching():
     # misaligned pointers are refused before any launch
     cache = kvc.Cache(C.c_void_p(16), 1 << 30, C.c_void_p(32), C.c_void_p(48), C.c_void_p(64), None, 4)
     inp = kvc.DecodeIn(2, 1, 100, C.c_void_p(80), C.c_void_p(96), None, C.c_void_p(113), 1, C.c_void_p(128),
-                       C.c_void_p(144), 0)
+                       C.c_void_p(144), 0, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(160), C.c_void_p(176), 1 << 30,
                                None) == -4
 
@@ -73,7 +73,8 @@ def test_decode_path_selection():
     general per-head or the block-shared kernel."""
     want = {"tiny": kvc.PATH_HEAD, "llama8b_layer_8k": kvc.PATH_INT4, "varrank_paged_32k": kvc.PATH_INT4,
             "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
-            "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4}
+            "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4,
+            "tucker_group_32k": kvc.PATH_SHARED}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
@@ -162,3 +163,28 @@ def test_low_bit_layouts_check_and_route():
     # pool sizes follow r * b / 8 code bytes: K 48 x 3 / 8 = 18, V 64 x 2 / 8 = 16 per slot
     L = kvc.make_layout(**base.scaled(latent_bits=3, latent_bits_v=2).layout_kwargs())
     assert kvc.pool_bytes_max(L, 10) == 10 * 8 * 256 * (18 + 16 + 8 + 8)
+
+
+def test_tucker_and_per_sequence_w_rejections_without_launching():
+    lib = kvc.lib()
+    p = C.c_void_p
+    good = dict(n_seq=2, n_layers=4, n_kv_heads=8, head_dim=128, r_t=256, r_f=64, latent=512, row0=0)
+
+    def tin(**kw):
+        v = dict(good, **kw)
+        return kvc.TuckerIn(*(v[n] for n in ("n_seq", "n_layers", "n_kv_heads", "head_dim", "r_t", "r_f", "latent",
+                                             "row0")), p(64), p(128))
+
+    for bad in (dict(n_seq=0), dict(r_t=0), dict(r_f=0), dict(r_f=129), dict(row0=300), dict(latent=5000),
+                dict(row0=-1)):
+        assert lib.kvc_tucker_expand(C.byref(tin(**bad)), p(256), None, None) == -1, bad
+    assert lib.kvc_tucker_expand(C.byref(tin()), None, None, None) == -1
+    assert lib.kvc_tucker_expand(C.byref(tin(head_dim=64, r_f=32)), p(256), None, None) == -2
+    assert lib.kvc_tucker_expand(C.byref(tin()), p(258), None, None) == -4
+    # a per-sequence stride is for block-shared layouts only, in whole 16-byte units
+    cache = kvc.Cache(p(16), 1 << 30, p(32), p(48), p(64), None, 4)
+    for name, stride in (("varrank_paged_32k", 8), ("shared_latent_32k", 12), ("shared_latent_32k", -8)):
+        w = synth.WORKLOADS[name]
+        L = kvc.make_layout(**w.layout_kwargs())
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, stride)
+        assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == -1
