@@ -593,7 +593,8 @@ static void rebuild_token(const kvc_ref_layout* L, int which, int layer, int b, 
 static void attend_group(const kvc_ref_layout* L, int layer, int b, int h, int T, int qpos, int max_blocks,
                          const int32_t* block_table, const uint8_t* pool, const int64_t* page_off,
                          const uint8_t* tok_rank, const uint32_t* tok_off, const float* q,
-                         const uint16_t* wk, const uint16_t* wv, const double* H, double* out) {
+                         const uint16_t* wk, const uint16_t* wv, const double* H, const uint32_t* keep,
+                         double* out) {
   int d = L->head_dim, gsz = L->n_q_heads / L->n_kv_heads;
   double* qr = (double*)malloc(sizeof(double) * gsz * d);
   double* w = (double*)malloc(sizeof(double) * (size_t)gsz * T);
@@ -604,7 +605,11 @@ static void attend_group(const kvc_ref_layout* L, int layer, int b, int h, int T
     for (int j = 0; j < d; ++j) qr[g * d + j] = q[(size_t)(h * gsz + g) * d + j];
     kvc_ref_rope(qr + g * d, d, (double)qpos, L->rope_theta);
   }
-  for (int t = 0; t < T; ++t) {                 /* scores q~ . k~_t / sqrt(d) */
+  for (int t = 0; t < T; ++t) {                 /* scores q~ . k~_t / sqrt(d); an evicted token takes no part */
+    if (keep && !((keep[t >> 5] >> (t & 31)) & 1u)) {
+      for (int g = 0; g < gsz; ++g) w[(size_t)g * T + t] = -INFINITY;
+      continue;
+    }
     rebuild_token(L, 0, layer, b, h, t, max_blocks, block_table, pool, page_off, tok_rank, tok_off, wk, H, c, e, x);
     kvc_ref_rope(x, d, (double)t, L->rope_theta);
     for (int g = 0; g < gsz; ++g) {
@@ -617,11 +622,16 @@ static void attend_group(const kvc_ref_layout* L, int layer, int b, int h, int T
     double* wg = w + (size_t)g * T;
     double m = -INFINITY, l = 0.0;
     for (int t = 0; t < T; ++t) if (wg[t] > m) m = wg[t];
+    if (m == -INFINITY) {                       /* every token evicted: no weight anywhere, output zero */
+      for (int t = 0; t < T; ++t) wg[t] = 0.0;
+      continue;
+    }
     for (int t = 0; t < T; ++t) { wg[t] = exp(wg[t] - m); l += wg[t]; }
     for (int t = 0; t < T; ++t) wg[t] /= l;
   }
   for (int i = 0; i < gsz * d; ++i) out[i] = 0.0;
   for (int t = 0; t < T; ++t) {                 /* out = sum_t p_t v_t */
+    if (keep && !((keep[t >> 5] >> (t & 31)) & 1u)) continue;
     rebuild_token(L, 1, layer, b, h, t, max_blocks, block_table, pool, page_off, tok_rank, tok_off, wv, H, c, e, x);
     for (int g = 0; g < gsz; ++g)
       for (int j = 0; j < d; ++j) out[(size_t)g * d + j] += w[(size_t)g * T + t] * x[j];
@@ -634,13 +644,25 @@ int kvc_ref_decode_attn(const kvc_ref_layout* L, int B, int max_blocks, const in
                         const int64_t* page_off, const uint8_t* tok_rank, const uint32_t* tok_off,
                         const float* q, const uint16_t* wk, const uint16_t* wv,
                         const uint8_t* sel_b, const uint8_t* sel_h, double* out) {
+  return kvc_ref_decode_attn_masked(L, B, max_blocks, block_table, seq_len, q_pos, pool, page_off, tok_rank, tok_off,
+                                    q, wk, wv, NULL, 0, sel_b, sel_h, out);
+}
+
+int kvc_ref_decode_attn_masked(const kvc_ref_layout* L, int B, int max_blocks, const int32_t* block_table,
+                               const int32_t* seq_len, const int32_t* q_pos, const uint8_t* pool,
+                               const int64_t* page_off, const uint8_t* tok_rank, const uint32_t* tok_off,
+                               const float* q, const uint16_t* wk, const uint16_t* wv, const uint32_t* keep,
+                               int keep_words, const uint8_t* sel_b, const uint8_t* sel_h, double* out) {
   if (kvc_ref_layout_check(L)) return KVC_REF_EINVAL;
   int d = L->head_dim, Hq = L->n_q_heads, Hkv = L->n_kv_heads, NL = L->n_layers;
   int gsz = Hq / Hkv;
   double* H = NULL;
   if (L->residual_bits) { H = (double*)malloc(sizeof(double) * d * d); kvc_ref_hadamard(d, H); }
   for (int b = 0; b < B; ++b)
-    if (seq_len[b] < 1 || seq_len[b] > max_blocks * L->page_size) { free(H); return KVC_REF_EINVAL; }
+    if (seq_len[b] < 1 || seq_len[b] > max_blocks * L->page_size || (keep && seq_len[b] > 32 * keep_words)) {
+      free(H);
+      return KVC_REF_EINVAL;
+    }
   int n_items = NL * B * Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int it = 0; it < n_items; ++it) {
@@ -651,7 +673,7 @@ int kvc_ref_decode_attn(const kvc_ref_layout* L, int B, int max_blocks, const in
     const float* ql = q + (((size_t)layer * B + b) * Hq) * d;
     double* o = out + ((((size_t)layer * B + b) * Hq) + (size_t)h * gsz) * d;
     attend_group(L, layer, b, h, seq_len[b], qpos, max_blocks, block_table, pool, page_off, tok_rank,
-                 tok_off, ql, wk, wv, H, o);
+                 tok_off, ql, wk, wv, H, keep ? keep + (size_t)b * keep_words : NULL, o);
   }
   free(H);
   return 0;

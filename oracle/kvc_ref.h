@@ -105,6 +105,16 @@ int kvc_ref_decode_attn(const kvc_ref_layout* L, int B, int max_blocks, const in
                         const float* q, const uint16_t* wk, const uint16_t* wv,
                         const uint8_t* sel_b, const uint8_t* sel_h, double* out);
 
+/* The same with a token keep mask (BellowsKV-Evict: one eviction decision per block of layers, applied to
+ * the shared latent, so to every layer and head): keep [B][keep_words], bit t % 32 of word t / 32 set for a
+ * kept token; an evicted token takes no part in the softmax or the value sum; a sequence that keeps no token
+ * gets zero output.  keep NULL = every token kept.  seq_len[b] <= 32 keep_words. */
+int kvc_ref_decode_attn_masked(const kvc_ref_layout* L, int B, int max_blocks, const int32_t* block_table,
+                               const int32_t* seq_len, const int32_t* q_pos, const uint8_t* pool,
+                               const int64_t* page_off, const uint8_t* tok_rank, const uint32_t* tok_off,
+                               const float* q, const uint16_t* wk, const uint16_t* wv, const uint32_t* keep,
+                               int keep_words, const uint8_t* sel_b, const uint8_t* sel_h, double* out);
+
 /* OpenMP threads the parallel loops above use */
 int kvc_ref_threads(void);
 

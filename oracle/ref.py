@@ -39,6 +39,8 @@ def lib():
         L.kvc_ref_project.restype = C.c_int
         L.kvc_ref_decode_attn.argtypes = [P, C.c_int, C.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.kvc_ref_decode_attn.restype = C.c_int
+        L.kvc_ref_decode_attn_masked.argtypes = [P, C.c_int, C.c_int, P, P, P, P, P, P, P, P, P, P, P, C.c_int, P, P, P]
+        L.kvc_ref_decode_attn_masked.restype = C.c_int
         L.kvc_ref_dense_attn.argtypes = [C.c_int] * 6 + [P] * 7
         L.kvc_ref_dense_attn.restype = C.c_int
         L.kvc_ref_threads.argtypes = []; L.kvc_ref_threads.restype = C.c_int
@@ -181,17 +183,20 @@ def project(L: Layout, seq_len, max_T, ranks, k, v, basis_k, basis_v):
 
 
 def decode_attn(L: Layout, block_table, seq_len, q_pos, pool, page_off, tok_rank, tok_off, q, wk, wv,
-                sel_b=None, sel_h=None):
-    """fp64 attention output [(L,) B, Hq, d]; rows of unselected (b, kv head) are NaN."""
+                sel_b=None, sel_h=None, keep=None):
+    """fp64 attention output [(L,) B, Hq, d]; rows of unselected (b, kv head) are NaN.  keep: optional uint32
+    token keep mask [B, words] (bit t % 32 of word t // 32)."""
     bt = _c(block_table, np.int32)
     B, max_blocks = bt.shape
     q = _c(q, np.float32)
     out = np.full(q.shape, np.nan, np.float64)
-    rc = lib().kvc_ref_decode_attn(C.byref(L.c()), B, max_blocks, _p(bt), _p(_c(seq_len, np.int32)),
-                                   _p(_c(q_pos, np.int32)), _p(_c(pool, np.uint8)), _p(_c(page_off, np.int64)),
-                                   _p(_c(tok_rank, np.uint8)), _p(_c(tok_off, np.uint32)), _p(q),
-                                   _p(_c(wk, np.uint16)), _p(_c(wv, np.uint16)), _p(_c(sel_b, np.uint8)),
-                                   _p(_c(sel_h, np.uint8)), _p(out))
+    keep_words = 0 if keep is None else int(np.asarray(keep).shape[1])
+    rc = lib().kvc_ref_decode_attn_masked(C.byref(L.c()), B, max_blocks, _p(bt), _p(_c(seq_len, np.int32)),
+                                          _p(_c(q_pos, np.int32)), _p(_c(pool, np.uint8)),
+                                          _p(_c(page_off, np.int64)), _p(_c(tok_rank, np.uint8)),
+                                          _p(_c(tok_off, np.uint32)), _p(q), _p(_c(wk, np.uint16)),
+                                          _p(_c(wv, np.uint16)), _p(_c(keep, np.uint32)), keep_words,
+                                          _p(_c(sel_b, np.uint8)), _p(_c(sel_h, np.uint8)), _p(out))
     if rc:
         raise ValueError("kvc_ref_decode_attn rejected its input")
     return out
