@@ -95,9 +95,10 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # The other workloads of the hot path, each timed on its own bound: the uniform-rank 8K layer (cache-resident,
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
 # and head from the 512-dim latent) and the 128K rotated-residual cache (HBM); the lower-bit codecs; and a layer
-# group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core).
+# group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core);
+# the block-shared latent under one eviction decision for its layers (the decision timed on its own).
 OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2",
-         "tucker_group_32k")
+         "tucker_group_32k", "shared_latent_32k_evict30")
 
 
 def decode_flops(w) -> int:
@@ -142,8 +143,20 @@ def other_workloads(steps: int, warmup: int) -> dict:
             inp["wk"], inp["wv"] = wk, wv
             extra = {"tucker_expand_ms_median": round(sorted(times)[2], 5),
                      "per_sequence_w_bytes": 2 * wk.numel() * 2}
+        keep = None
+        if w.evict_ratio:  # the block's eviction decision from its layers' scores (prefill side; timed on its own)
+            xe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            for _ in range(5):
+                xe[0].record()
+                keep = kvc.evict_select(inp["layer_scores"], inp["seq_len"], w.evict_ratio)
+                xe[1].record()
+                torch.cuda.synchronize()
+                times.append(xe[0].elapsed_time(xe[1]))
+            kept = int(sum(bin(x & 0xFFFFFFFF).count("1") for x in keep.view(-1).tolist()))
+            extra = {"evict_select_ms_median": round(sorted(times)[2], 5), "kept_fraction": round(kept / (w.B * w.T), 4)}
         plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
-                              q_pos=inp["q_pos"])
+                              q_pos=inp["q_pos"], keep_mask=keep)
         for k in ("lat_k", "lat_v", "res_k", "res_v"):
             inp[k] = None
         n = max(20, steps // 10)

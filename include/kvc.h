@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
@@ -151,6 +151,14 @@ typedef struct {
                                  /*   the next, a multiple of 8; 0 = one pair for all sequences  */
                                  /*   (per-sequence up-projections, e.g. expanded from a Tucker */
                                  /*   core fitted per prefill cache).  Per-head mode: 0          */
+  const uint32_t* keep_mask;     /* shared mode, optional: token keep mask [B][keep_words], bit  */
+                                 /*   t % 32 of word t / 32 set for a kept token (BellowsKV-Evict */
+                                 /*   page: one eviction decision for the block's layers, applied */
+                                 /*   to the shared latent).  Evicted tokens take no part in the  */
+                                 /*   softmax; a sequence keeping none gets zero output.  NULL =  */
+                                 /*   all kept; per-head mode: NULL.  4-byte aligned              */
+  int32_t keep_words;            /* words per sequence of keep_mask (tokens past 32 keep_words   */
+                                 /*   count as evicted)                                           */
 } kvc_decode_in;
 
 /* Inputs of kvc_dense_decode_attn: plain attention over a paged bf16 cache. */
@@ -370,6 +378,27 @@ typedef struct {
  * (values' rows zero) and W_v the reverse.  Asynchronous on stream.  INVALID_ARG for bad sizes or null
  * pointers, UNSUPPORTED for d != 128, MISALIGNED for pointers not 4-byte aligned. */
 kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32, void* stream);
+
+/* Inputs of kvc_evict_select (device memory). */
+typedef struct {
+  int32_t B, max_T;              /* sequences, scores per sequence and layer                     */
+  int32_t n_layers;              /* layers of the block whose scores decide together             */
+  double keep_ratio;             /* in (0, 1]: a sequence of T tokens keeps                      */
+                                 /*   min(T, max(1, floor(keep_ratio * T))) of them (none if T=0)*/
+  const int32_t* seq_len;        /* [B] tokens per sequence, 0..max_T                            */
+  const float* scores;           /* [n_layers][B][max_T] per-layer token importance, not NaN      */
+                                 /*   (for instance kvc_salience of each layer)                   */
+} kvc_evict_in;
+
+/* Block-level eviction decision ("BellowsKV" page, "Three Measurements, Three Operators": layers of a block
+ * rank token importance alike, so one decision made from all the block's layers' scores is applied once to
+ * the shared latent).  A token's block score is the fp32 sum of its layers' scores in layer order; each
+ * sequence keeps the tokens of largest block score, equal scores in increasing position, as many as
+ * keep_ratio gives (at least one).  keep_mask: [B][ceil(max_T / 32)] words, bit t % 32 of word t / 32 set
+ * for a kept token, zero past seq_len: the mask kvc_decode_attn takes (keep_words = ceil(max_T / 32)).
+ * One workgroup per sequence; deterministic; asynchronous on stream.  INVALID_ARG for bad sizes, a ratio
+ * outside (0, 1] or null pointers, MISALIGNED for pointers not 4-byte aligned. */
+kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream);
 
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);

@@ -37,6 +37,7 @@ kvc_status salience_impl(const kvc_salience_in& in, float* out, void* ws, size_t
 kvc_status rank_alloc_impl(const kvc_alloc_in& in, uint8_t* ranks, hipStream_t st);
 kvc_status plan_impl(const kvc_plan_in& in, int32_t* choice, double* lambda);
 kvc_status tucker_impl(const kvc_tucker_in& in, uint16_t* w, float* w32, hipStream_t st);
+kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                       size_t* need);
 
@@ -149,6 +150,8 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
   const kvc_layout& L = *layout;
   if (in->B <= 0 || in->max_blocks <= 0 || in->max_T <= 0 || in->num_splits < 0) return KVC_ERR_INVALID_ARG;
   if (in->w_seq_stride < 0 || in->w_seq_stride % 8 || (!L.shared && in->w_seq_stride)) return KVC_ERR_INVALID_ARG;
+  if (in->keep_mask && (!L.shared || in->keep_words < 1)) return KVC_ERR_INVALID_ARG;
+  if (in->keep_mask && ((uintptr_t)in->keep_mask & 3)) return KVC_ERR_MISALIGNED;
   if ((int64_t)in->max_blocks * L.page_size < in->max_T) return KVC_ERR_INVALID_ARG;
   if (in->q_dtype != KVC_F32 && in->q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
   if (!cache->pool || !cache->page_off || cache->n_pages <= 0) return KVC_ERR_INVALID_ARG;
@@ -245,6 +248,11 @@ kvc_status kvc_plan_budget(const kvc_plan_in* in, int32_t* choice, double* lambd
 kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32, void* stream) {
   if (!in) return KVC_ERR_INVALID_ARG;
   return tucker_impl(*in, w, w_f32, (hipStream_t)stream);
+}
+
+kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return evict_impl(*in, keep_mask, (hipStream_t)stream);
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

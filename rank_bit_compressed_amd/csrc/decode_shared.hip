@@ -58,6 +58,8 @@ struct DecodeSharedArgs {
   const void* q;
   const uint16_t* wk;
   int64_t w_stride;  // elements between sequences' W_k (0: one for all)
+  const uint32_t* keep;  // token keep mask [B][keep_words] (bit t % 32 of word t / 32), or null
+  int keep_words;
   float* ws;
   int q_bf16, B, Hkv, Hq, L, max_blocks, P, G, n_splits, st_per_split, part_stride;
   double theta;
@@ -66,7 +68,7 @@ struct DecodeSharedArgs {
 static constexpr int SMAX_TILES = 1024;  // super-tiles per split (the page record address of each)
 
 struct SharedLds {
-  int raw, vt, qt, theta, sp, pt, addr, total;
+  int raw, vt, qt, theta, sp, pt, addr, keep, total;
 };
 __host__ __device__ constexpr SharedLds shared_lds() {
   SharedLds L{};
@@ -78,6 +80,7 @@ __host__ __device__ constexpr SharedLds shared_lds() {
   L.sp = o; o += 2 * 4 * 32 * SGQ * 4;          // partial scores [buffer][wave][token][head], x 2
   L.pt = o; o += 4 * 32 * SGQ * 2;              // probabilities [wave][token][head] fp16
   L.addr = o; o += SMAX_TILES * 8;              // page record address of each super-tile
+  L.keep = o; o += SMAX_TILES * 4;              // keep-mask word of each super-tile
   L.total = o;
   return L;
 }
@@ -93,6 +96,8 @@ __device__ inline int qfrag_index(int head, int dim) {
   return (((head * SNB + g) * 2 + st) * 2 + hf) * 8 + e;
 }
 
+// KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it)
+template <bool KEEP>
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr SharedLds LY = shared_lds();
@@ -157,10 +162,13 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   const int st_begin = split * a.st_per_split;
   const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
   int64_t* taddr = (int64_t*)(smem + LY.addr);
-  for (int k = tid; k < n_tiles; k += 256) {  // page record of each super-tile, and its first slot
+  uint32_t* tkeep = (uint32_t*)(smem + LY.keep);
+  for (int k = tid; k < n_tiles; k += 256) {  // page record of each super-tile, its first slot, its keep word
     const int t0 = (st_begin + k) * 32;
     const int page = a.block_table[(size_t)b * a.max_blocks + t0 / P];
     taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * (SLAT / 2);
+    const int wd = t0 >> 5;
+    if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
   }
   __syncthreads();
   const double fq = tturn[qj];
@@ -315,11 +323,15 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       f4 tot = *(const f4*)(spb + t * SGQ);
 #pragma unroll
       for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
+      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u));  // past the end or evicted: no weight
 #pragma unroll
-      for (int i = 0; i < SGQ; ++i) s4[i] = (t0 + t < T) ? tot[i] - m_ref[i] : -INFINITY;
+      for (int i = 0; i < SGQ; ++i) s4[i] = kept ? tot[i] - m_ref[i] : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-    if (fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
+    // the first super-tile with a kept token sets the reference maximum; one with none (possible under a keep
+    // mask only) leaves it unset
+    if (KEEP ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
+             : fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
       float alpha[SGQ];
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) {
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
     for (int e = 0; e < 8; ++e) o[e] += __builtin_bit_cast(float, (uint32_t)W[(size_t)(i + e) * width] << 16) * cst[i + e];
   }
   const float sum = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
-  out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = sum / lst;
+  out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = lst > 0.0f ? sum / lst : 0.0f;  // zero: no token kept
 }
 
 int shared_max_tiles_per_split() { return SMAX_TILES; }
@@ -464,17 +476,22 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   DecodeSharedArgs a;
   a.pool = C.pool; a.page_off = C.page_off; a.block_table = in.block_table; a.seq_len = in.seq_len;
   a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk; a.w_stride = in.w_seq_stride; a.ws = (float*)ws;
+  a.keep = in.keep_mask; a.keep_words = in.keep_words;
   a.q_bf16 = in.q_dtype == KVC_BF16;
   a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.L = L.n_layers; a.max_blocks = in.max_blocks;
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
   const int lds = shared_lds().total;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_shared_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const void* kern = in.keep_mask ? (const void*)decode_shared_kernel<true> : (const void*)decode_shared_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
   e = mark(g_marks.begin, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_shared_kernel, dim3(grid), dim3(256), lds, st, a);
+  if (in.keep_mask)
+    hipLaunchKernelGGL(decode_shared_kernel<true>, dim3(grid), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL(decode_shared_kernel<false>, dim3(grid), dim3(256), lds, st, a);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;

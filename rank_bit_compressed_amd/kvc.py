@@ -25,7 +25,8 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
-           "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand"]
+           "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
+           "kvc_evict_select"]
 
 
 class KvcError(RuntimeError):
@@ -61,7 +62,8 @@ class CompressIn(C.Structure):
 class DecodeIn(C.Structure):
     _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32), ("block_table", C.c_void_p),
                 ("seq_len", C.c_void_p), ("q_pos", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32),
-                ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32), ("w_seq_stride", C.c_int64)]
+                ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32), ("w_seq_stride", C.c_int64),
+                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32)]
 
 
 class DenseIn(C.Structure):
@@ -127,6 +129,7 @@ def lib():
         L.kvc_rank_alloc.argtypes = [P, P, P]; L.kvc_rank_alloc.restype = C.c_int32
         L.kvc_plan_budget.argtypes = [P, P, P]; L.kvc_plan_budget.restype = C.c_int32
         L.kvc_tucker_expand.argtypes = [P, P, P, P]; L.kvc_tucker_expand.restype = C.c_int32
+        L.kvc_evict_select.argtypes = [P, P, P]; L.kvc_evict_select.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -229,10 +232,17 @@ def _q_dtype(q):
     raise TypeError("q must be fp32 or bf16")
 
 
-def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, w_seq_stride=0) -> DecodeIn:
+def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, w_seq_stride=0,
+              keep_mask=None) -> DecodeIn:
     B, max_blocks = block_table.shape
+    words = 0
+    if keep_mask is not None:
+        if keep_mask.dtype != torch.int32 or keep_mask.dim() != 2 or keep_mask.shape[0] != B:
+            raise ValueError("keep_mask must be an int32 (uint32 bits) tensor [B, words]")
+        words = keep_mask.shape[1]
     return DecodeIn(B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len), _ptr(q_pos), _ptr(q), _q_dtype(q),
-                    _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits, w_seq_stride)
+                    _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits, w_seq_stride,
+                    _ptr(keep_mask), words)
 
 
 def _w_stride(layout, wk, wv, B):
@@ -245,18 +255,20 @@ def _w_stride(layout, wk, wv, B):
 
 
 def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                num_splits=0, out=None, ws=None, events=None):
+                num_splits=0, out=None, ws=None, events=None, keep_mask=None):
     """kvc_decode_attn -> fp32 [(L,) B, Hq, d].  events: optional (begin, end) pair of recorded-once
     torch.cuda.Event objects; the call then goes through kvc_decode_attn_timed, which records them around
     the attention kernel alone.  Shared mode: wk, wv [L, latent, Hkv * d] for all sequences, or
-    [B, L, latent, Hkv * d] (contiguous), one pair per sequence."""
+    [B, L, latent, Hkv * d] (contiguous), one pair per sequence; keep_mask: optional int32 [B, words] token
+    keep mask (as kvc_evict_select writes it)."""
     B = block_table.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(layout, B, max_T, num_splits)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B))
+    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
+                    keep_mask)
     c = cache.c()
     if events is None:
         _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
@@ -275,15 +287,16 @@ class DecodePlan:
     they hold at launch time.  Calls enqueue on the current stream, like decode_attn."""
 
     def __init__(self, layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                 num_splits=0, out=None, ws=None):
+                 num_splits=0, out=None, ws=None, keep_mask=None):
         B = block_table.shape[0]
         self.out = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
         need = decode_workspace_bytes(layout, B, max_T, num_splits)
         if ws is None or ws.numel() < need:
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-        self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws)
+        self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws, keep_mask)
         self._layout, self._cache = layout, cache.c()
-        self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B))
+        self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
+                             keep_mask)
         self._args = (C.byref(self._layout), C.byref(self._cache), C.byref(self._in), _ptr(self.out), _ptr(ws),
                       ws.numel())
         self._fn, self._fn_timed = lib().kvc_decode_attn, lib().kvc_decode_attn_timed
@@ -441,3 +454,19 @@ def tucker_expand(u_f, core, latent, row0=0, w=None, want_f32=False):
     _check(lib().kvc_tucker_expand(C.byref(inp), _ptr(w.view(torch.int16)), _ptr(w32), _stream()),
            "kvc_tucker_expand")
     return w, w32
+
+
+class EvictIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_T", C.c_int32), ("n_layers", C.c_int32), ("keep_ratio", C.c_double),
+                ("seq_len", C.c_void_p), ("scores", C.c_void_p)]
+
+
+def evict_select(scores, seq_len, keep_ratio, out=None):
+    """kvc_evict_select: scores fp32 [n_layers, B, max_T], seq_len int32 [B] (device) -> keep mask int32
+    (uint32 bits) [B, ceil(max_T / 32)]."""
+    n_layers, B, max_T = scores.shape
+    if out is None:
+        out = torch.empty(B, (max_T + 31) // 32, dtype=torch.int32, device=scores.device)
+    inp = EvictIn(B, max_T, n_layers, float(keep_ratio), _ptr(seq_len), _ptr(scores))
+    _check(lib().kvc_evict_select(C.byref(inp), _ptr(out), _stream()), "kvc_evict_select")
+    return out

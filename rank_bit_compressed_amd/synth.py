@@ -26,7 +26,9 @@ Distributions (the pages give shapes, not data):
     spread of singular values without repeated ones;
   * window queries for salience (pre-RoPE, fp32): N(0, 1) per element;
   * salience for the rank-allocation tests: exp(N(0, 1.5^2)) per token, a
-    heavy-tailed positive spread like attention mass, rounded to fp32;
+    heavy-tailed positive spread like attention mass, rounded to fp32; the
+    per-layer token scores of an evicting block-shared workload are one such
+    draw per layer;
   * partial Tucker factors of a layer group (keys and values separately), per
     sequence: token factor rows N(0, 1/T) per element (the scale of a factor
     with orthonormal columns over T tokens); the feature factor an orthonormal
@@ -72,6 +74,7 @@ class Workload:
     residual_std: float = 0.05
     w_std: float = 0.0            # block-shared mode: W entries N(0, w_std^2)
     tucker: tuple = ()            # block-shared from partial Tucker factors: (key r_t, value r_t, r_f)
+    evict_ratio: float = 0.0      # block-shared: share of tokens the block's eviction decision keeps
     seed: int = 0
 
     def scaled(self, **kw) -> "Workload":
@@ -120,6 +123,11 @@ WORKLOADS = {
     "tucker_group_32k": Workload("tucker_group_32k", B=4, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
                                  r_k=512, r_v=512, group=64, shared=True, n_layers=4, rope_theta=500000.0,
                                  latent_decay=0.0, tucker=(256, 256, 64), seed=16),
+    # the block-shared latent with one eviction decision for its 4 layers, keeping 30% of every sequence
+    "shared_latent_32k_evict30": Workload("shared_latent_32k_evict30", B=4, T=32768, n_q_heads=32, n_kv_heads=8,
+                                          head_dim=128, r_k=512, r_v=512, group=64, shared=True, n_layers=4,
+                                          rope_theta=500000.0, latent_decay=0.0, w_std=1.0 / math.sqrt(512.0),
+                                          evict_ratio=0.3, seed=14),
     # the lower-bit codecs of the BellowsKV page's retention table on per-head latents: the 32K variable-rank
     # workload with INT3 latents, and the 8K layer with 3-bit keys and 2-bit values
     "varrank_paged_32k_int3": Workload("varrank_paged_32k_int3", B=16, T=32768, n_q_heads=32, n_kv_heads=8,
@@ -218,6 +226,9 @@ def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
     else:
         out["wk"] = _orthonormal(w, 8, d, w.r_k, Hkv).to(torch.bfloat16).to(dev)
         out["wv"] = _orthonormal(w, 9, d, w.r_v, Hkv).to(torch.bfloat16).to(dev)
+    if w.evict_ratio:  # per-layer token importance of the block (the salience law, one draw per layer)
+        out["layer_scores"] = torch.stack([make_salience(B, T, seed=w.seed * 10 + l, device=dev)
+                                           for l in range(w.n_layers)]).contiguous()
     qshape = ((w.n_layers,) if w.shared else ()) + (B, w.n_q_heads, d)
     q = torch.randn(qshape, generator=_gen(w, 10, "cpu"), dtype=torch.float32) / 8.0
     out["q"] = (q.to(torch.bfloat16) if w.q_bf16 else q).to(dev)

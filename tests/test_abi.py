@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 3
+    assert kvc.lib().kvc_abi_version() == 4
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -54,7 +54,7 @@ def test_calls_reject_bad_arguments_without_launching():
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 0, 100, 0, C.byref(out)) == -1
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 2, 100, 0, C.byref(out)) == 0 and out.value > 0
     cache = kvc.Cache(None, 0, None, None, None, None, 0)
-    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0, 0)
+    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0, 0, None, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(16), C.c_void_p(16), 1 << 20,
                                None) == -1
     cin = kvc.CompressIn(0, 2, 100, 1, *([None] * 11))
@@ -62,7 +62,7 @@ def test_calls_reject_bad_arguments_without_launching():
     # misaligned pointers are refused before any launch
     cache = kvc.Cache(C.c_void_p(16), 1 << 30, C.c_void_p(32), C.c_void_p(48), C.c_void_p(64), None, 4)
     inp = kvc.DecodeIn(2, 1, 100, C.c_void_p(80), C.c_void_p(96), None, C.c_void_p(113), 1, C.c_void_p(128),
-                       C.c_void_p(144), 0, 0)
+                       C.c_void_p(144), 0, 0, None, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(160), C.c_void_p(176), 1 << 30,
                                None) == -4
 
@@ -74,7 +74,7 @@ def test_decode_path_selection():
     want = {"tiny": kvc.PATH_HEAD, "llama8b_layer_8k": kvc.PATH_INT4, "varrank_paged_32k": kvc.PATH_INT4,
             "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
             "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4,
-            "tucker_group_32k": kvc.PATH_SHARED}
+            "tucker_group_32k": kvc.PATH_SHARED, "shared_latent_32k_evict30": kvc.PATH_SHARED}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
@@ -186,5 +186,24 @@ def test_tucker_and_per_sequence_w_rejections_without_launching():
     for name, stride in (("varrank_paged_32k", 8), ("shared_latent_32k", 12), ("shared_latent_32k", -8)):
         w = synth.WORKLOADS[name]
         L = kvc.make_layout(**w.layout_kwargs())
-        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, stride)
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, stride, None, 0)
         assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == -1
+
+
+def test_evict_and_keep_mask_rejections_without_launching():
+    lib = kvc.lib()
+    p = C.c_void_p
+    for B, T, nl, ratio in ((0, 100, 2, 0.5), (2, 0, 2, 0.5), (2, 100, 0, 0.5), (2, 100, 2, 0.0), (2, 100, 2, 1.5),
+                            (2, 100, 2, float("nan"))):
+        inp = kvc.EvictIn(B, T, nl, ratio, p(64), p(128))
+        assert lib.kvc_evict_select(C.byref(inp), p(256), None) == -1, (B, T, nl, ratio)
+    assert lib.kvc_evict_select(C.byref(kvc.EvictIn(2, 100, 2, 0.5, p(64), p(128))), None, None) == -1
+    assert lib.kvc_evict_select(C.byref(kvc.EvictIn(2, 100, 2, 0.5, p(64), p(130))), p(256), None) == -4
+    # a keep mask is for block-shared layouts, with at least one word per sequence, 4-byte aligned
+    cache = kvc.Cache(p(16), 1 << 30, p(32), p(48), p(64), None, 4)
+    for name, mask, words, want in (("varrank_paged_32k", p(192), 4, -1), ("shared_latent_32k", p(192), 0, -1),
+                                    ("shared_latent_32k", p(194), 4, -4)):
+        w = synth.WORKLOADS[name]
+        L = kvc.make_layout(**w.layout_kwargs())
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, mask, words)
+        assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == want

@@ -1,0 +1,136 @@
+"""Block-level eviction on the GPU: kvc_evict_select against the eviction oracle (bit for bit: the block scores
+are fp32 sums in the same order on both sides, and the rest is integer work), and the block-shared decode under
+a keep mask against the oracle's masked attention (max |out - ref| <= 2e-3 max |ref|, the bound of every
+decode path)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import evict as E
+from oracle import ref
+from rank_bit_compressed_amd import kvc, synth
+from tests.gpu_helpers import dev, gpu_cache, gpu_layout, rel_err
+from tests.helpers import layout, np_any, np_f32, np_u16, oracle_cache
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _select_case(scores, seq, ratio):
+    print(f"[evict] select scores={tuple(scores.shape)} seq={list(seq)[:6]} ratio={ratio}", flush=True)
+    got = kvc.evict_select(scores.cuda().contiguous(), torch.tensor(seq, dtype=torch.int32).cuda(), ratio)
+    again = kvc.evict_select(scores.cuda().contiguous(), torch.tensor(seq, dtype=torch.int32).cuda(), ratio)
+    torch.cuda.synchronize()
+    assert torch.equal(got, again)
+    want = E.keep_mask(scores.numpy(), seq, ratio)
+    assert np.array_equal(_u32(got), want), ratio
+
+
+def test_select_ragged_ties_and_layers():
+    B, T = 5, 3000
+    seq = [3000, 2999, 1, 0, 1777]
+    for n_layers in (1, 2, 4):
+        s = torch.stack([synth.make_salience(B, T, seed=40 + l) for l in range(n_layers)])
+        s[:, 0, :700] = 1.0                       # a block of ties across chunk boundaries
+        s[:, 1, 100:200] = 0.0
+        s[0, 1, 300] = -0.0                       # minus zero equals zero
+        for ratio in (0.3, 1e-9, 1.0, 0.5):
+            _select_case(s, seq, ratio)
+
+
+def test_select_many_ties_integer_scores():
+    g = torch.Generator().manual_seed(7)
+    s = torch.randint(0, 4, (3, 4, 5000), generator=g).float()
+    _select_case(s, [5000, 4097, 1024, 33], 0.37)
+    _select_case(s, [5000, 4097, 1024, 33], 0.999)
+
+
+def test_select_full_size():
+    w = synth.WORKLOADS["shared_latent_32k_evict30"]
+    inp = synth.make_inputs(w)
+    _select_case(inp["layer_scores"], [w.T] * w.B, w.evict_ratio)
+
+
+def _masked_oracle(w, inp, cache, mask, sel_b=None, sel_h=None):
+    pool, page_off, tok_rank, tok_off = cache
+    return ref.decode_attn(layout(w), np_any(inp["block_table"]), np_any(inp["seq_len"]), np_any(inp["q_pos"]), pool,
+                           page_off, tok_rank, tok_off, np_f32(inp["q"]), np_u16(inp["wk"]), np_u16(inp["wv"]),
+                           sel_b, sel_h, keep=mask)
+
+
+def _masks(w, seq, rng):
+    words = -(-w.T // 32)
+    kept = rng.random((w.B, words * 32)) < 0.3
+    kept[:, :64] = False                          # the first two super-tiles evicted: no reference yet
+    kept[0, :160] = False                         # with four splits of five super-tiles, split 0 holds none
+    m = {"random": kept}
+    one = np.zeros_like(kept)
+    one[0, 417] = True
+    one[1, 5] = True
+    m["one token"] = one
+    none = kept.copy()
+    none[1] = False                               # sequence 1 keeps no token: zero output
+    m["none in one sequence"] = none
+    weights = np.left_shift(np.uint64(1), np.arange(32, dtype=np.uint64))
+    return {k: (v.reshape(w.B, words, 32).astype(np.uint64) * weights).sum(-1).astype(np.uint32) for k, v in m.items()}
+
+
+@pytest.mark.parametrize("num_splits", [0, 4])
+def test_masked_decode_matches_oracle(num_splits):
+    w = synth.WORKLOADS["shared_latent_32k_evict30"].scaled(B=2, T=600)
+    seq = [600, 333]
+    inp = synth.make_inputs(w, seq_len=seq)
+    cache = oracle_cache(w, inp)
+    d = dev(inp)
+    gc = gpu_cache(w, d)
+    L = gpu_layout(w)
+    plain = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T, q_pos=d["q_pos"],
+                            num_splits=num_splits)
+    words = -(-w.T // 32)
+    ones = torch.full((w.B, words), -1, dtype=torch.int32, device="cuda")
+    all_kept = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
+                               q_pos=d["q_pos"], num_splits=num_splits, keep_mask=ones)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, all_kept)
+    masks = _masks(w, seq, np.random.default_rng(5))
+    # and the mask the eviction decision gives for the workload's layer scores
+    masks["evict 30%"] = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    for name, m in masks.items():
+        print(f"[evict] masked decode '{name}' num_splits={num_splits}", flush=True)
+        want = _masked_oracle(w, inp, cache, m)
+        gm = torch.from_numpy(m.view(np.int32)).cuda()
+        out = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
+                              q_pos=d["q_pos"], num_splits=num_splits, keep_mask=gm)
+        torch.cuda.synchronize()
+        o = out.cpu().double().numpy()
+        assert not np.isnan(o).any()
+        if name == "none in one sequence":
+            assert np.all(o[:, 1] == 0)
+            assert rel_err(out[:, :1], want[:, :1]) <= TOL
+        else:
+            assert rel_err(out, want) <= TOL, name
+
+
+def test_evict_then_decode_full_size_sampled():
+    w = synth.WORKLOADS["shared_latent_32k_evict30"]
+    inp = synth.make_inputs(w)
+    d = dev(inp)
+    seq = [w.T] * w.B
+    print("[evict] full size: select, compress, decode", flush=True)
+    gm = kvc.evict_select(d["layer_scores"], d["seq_len"], w.evict_ratio)
+    gc = gpu_cache(w, d)
+    out = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
+                          q_pos=d["q_pos"], keep_mask=gm)
+    torch.cuda.synchronize()
+    m = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    assert np.array_equal(_u32(gm), m)
+    print("[evict] full size: oracle compress and masked decode of sequence 3, kv head 4", flush=True)
+    cache = oracle_cache(w, inp)
+    sel_b = np.zeros(w.B, np.uint8); sel_b[3] = 1
+    sel_h = np.zeros(w.n_kv_heads, np.uint8); sel_h[4] = 1
+    want = _masked_oracle(w, inp, cache, m, sel_b, sel_h)
+    assert rel_err(out, want) <= TOL
