@@ -142,7 +142,7 @@ def other_workloads(steps: int, warmup: int) -> dict:
                 times.append(xe[0].elapsed_time(xe[1]))
             inp["wk"], inp["wv"] = wk, wv
             extra = {"tucker_expand_ms_median": round(sorted(times)[2], 5),
-                     "per_sequence_w_bytes": 2 * wk.numel() * 2}
+                     "per_sequence_w_bytes": 2 * wk.numel() * 2, "kv_split": w.tucker[0]}
         keep = None
         if w.evict_ratio:  # the block's eviction decision from its layers' scores (prefill side; timed on its own)
             xe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -156,7 +156,7 @@ def other_workloads(steps: int, warmup: int) -> dict:
             kept = int(sum(bin(x & 0xFFFFFFFF).count("1") for x in keep.view(-1).tolist()))
             extra = {"evict_select_ms_median": round(sorted(times)[2], 5), "kept_fraction": round(kept / (w.B * w.T), 4)}
         plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
-                              q_pos=inp["q_pos"], keep_mask=keep)
+                              q_pos=inp["q_pos"], keep_mask=keep, kv_split=w.tucker[0] if w.tucker else 0)
         for k in ("lat_k", "lat_v", "res_k", "res_v"):
             inp[k] = None
         n = max(20, steps // 10)

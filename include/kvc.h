@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum {
   KVC_OK = 0,
@@ -159,6 +159,12 @@ typedef struct {
                                  /*   all kept; per-head mode: NULL.  4-byte aligned              */
   int32_t keep_words;            /* words per sequence of keep_mask (tokens past 32 keep_words   */
                                  /*   count as evicted)                                           */
+  int32_t kv_split;              /* shared mode: 0, or latent / 2 when the latent's lower half    */
+                                 /*   feeds only the keys and the upper half only the values (W_k */
+                                 /*   zero on rows >= latent / 2, W_v zero below: keys and values */
+                                 /*   with their own token factors, kvc_tucker_expand).  The      */
+                                 /*   kernel then skips those zero products; the output is that   */
+                                 /*   of the full product.  Per-head mode: 0                      */
 } kvc_decode_in;
 
 /* Inputs of kvc_dense_decode_attn: plain attention over a paged bf16 cache. */

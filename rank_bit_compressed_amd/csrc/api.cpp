@@ -151,6 +151,7 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
   if (in->B <= 0 || in->max_blocks <= 0 || in->max_T <= 0 || in->num_splits < 0) return KVC_ERR_INVALID_ARG;
   if (in->w_seq_stride < 0 || in->w_seq_stride % 8 || (!L.shared && in->w_seq_stride)) return KVC_ERR_INVALID_ARG;
   if (in->keep_mask && (!L.shared || in->keep_words < 1)) return KVC_ERR_INVALID_ARG;
+  if (in->kv_split && (!L.shared || 2 * in->kv_split != L.r_k_cap)) return KVC_ERR_INVALID_ARG;
   if (in->keep_mask && ((uintptr_t)in->keep_mask & 3)) return KVC_ERR_MISALIGNED;
   if ((int64_t)in->max_blocks * L.page_size < in->max_T) return KVC_ERR_INVALID_ARG;
   if (in->q_dtype != KVC_F32 && in->q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;

@@ -96,8 +96,11 @@ __device__ inline int qfrag_index(int head, int dim) {
   return (((head * SNB + g) * 2 + st) * 2 + hf) * 8 + e;
 }
 
-// KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it)
-template <bool KEEP>
+// KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it).
+// SPLIT: latent coordinates below SLAT / 2 feed only the keys and the rest only the values (W_k zero on the upper
+// rows, W_v on the lower, as for keys and values with their own token factors): waves 0-1 then do only the key
+// work and waves 2-3 only the value product; their skipped products are exact zeros, so the output is the same.
+template <bool KEEP, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr SharedLds LY = shared_lds();
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   // 64 + 16g + r - 16; step j: k-slot 8hf + e <-> latent coordinate 128w + 8 (8hf + j) + perm8(e), i.e.
   // element e of code dword 8hf + j of the wave's 64 code bytes (the order a code dword dequantizes).
   h8 wf[SNB][SNJ];
-  {
+  if (!SPLIT || wv < 2) {
     const int width = a.Hkv * SD;
     const uint16_t* W = a.wk + (size_t)b * a.w_stride + (size_t)l * SLAT * width + (size_t)h * SD;
 #pragma unroll
@@ -281,6 +284,10 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // wave keeps both units busy.
     const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SD) + (t & 3) * (SNB * 4) + hf;
     f16v_t sc = {};
+    if (SPLIT && wv >= 2) {  // value waves: only the next super-tile's value tile
+#pragma unroll
+      for (int jj = 0; jj < SNJ; ++jj) *(h8*)(vdst + SCS * jj) = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
+    } else {
     f16v_t kp[SNB];
 #pragma unroll
     for (int g = 0; g <= SNB; ++g) {
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
         for (int jj = 2 * g; jj < 2 * g + 2; ++jj) {
           bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
-          *(h8*)(vdst + SCS * jj) = bn[jj];
+          if (!SPLIT) *(h8*)(vdst + SCS * jj) = bn[jj];  // key waves of a split latent make no value product
         }
       }
       if (g > 0) {
@@ -311,6 +318,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five vector instructions
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the previous block's score products
+    }
     }
     float* spb = sp + (k & 1) * (4 * 32 * SGQ);
     if (hf == 0) *(f4*)(spb + (wv * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
@@ -360,10 +368,10 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     wave_lds_sync();
     // P as the A operand of the 16x16x32 value product: row l % 16 <-> head l % 4, k-slot 8g + j <-> token 8g + j
     // (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
-    const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
     // value latent: step nt covers chunks 2nt, 2nt + 1; column n <-> coordinate 128w + 16nt + 8(n/8) + perm8(n%8);
     // lane rho points at the 4 columns 4(q4 % 2).. of chunk (2nt + q4 / 2, token 8g + 4v + rho / 4)
-    {
+    if (!SPLIT || wv >= 2) {
+      const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
       const int q4 = rho & 3;
       const uint8_t* vb = vt_w + (k & 1) * SVT + SCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
       h8 vt[SNJ];
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 // eight independent partial sums).
 __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, int64_t w_stride,
                                                           float* out, int B, int Hkv, int Hq, int n_splits,
-                                                          int part_stride) {
+                                                          int part_stride, int c_begin) {
   __shared__ float cst[SLAT];
   __shared__ float lst;
   int id = blockIdx.x;
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
   const size_t width = (size_t)Hkv * SD;
   const uint16_t* W = wv + (size_t)b * w_stride + (size_t)l * SLAT * width + (size_t)h * SD + d;
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = 0; i < SLAT; i += 8) {
+  for (int i = c_begin; i < SLAT; i += 8) {  // (a split latent: W_v is zero below c_begin)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] += __builtin_bit_cast(float, (uint32_t)W[(size_t)(i + e) * width] << 16) * cst[i + e];
   }
@@ -482,21 +490,30 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
   const int lds = shared_lds().total;
-  const void* kern = in.keep_mask ? (const void*)decode_shared_kernel<true> : (const void*)decode_shared_kernel<false>;
+  const bool split = in.kv_split == SLAT / 2;
+  const void* kern = in.keep_mask ? (split ? (const void*)decode_shared_kernel<true, true>
+                                           : (const void*)decode_shared_kernel<true, false>)
+                                  : (split ? (const void*)decode_shared_kernel<false, true>
+                                           : (const void*)decode_shared_kernel<false, false>);
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
   e = mark(g_marks.begin, st);
   if (e != hipSuccess) return e;
-  if (in.keep_mask)
-    hipLaunchKernelGGL(decode_shared_kernel<true>, dim3(grid), dim3(256), lds, st, a);
+  if (in.keep_mask && split)
+    hipLaunchKernelGGL((decode_shared_kernel<true, true>), dim3(grid), dim3(256), lds, st, a);
+  else if (in.keep_mask)
+    hipLaunchKernelGGL((decode_shared_kernel<true, false>), dim3(grid), dim3(256), lds, st, a);
+  else if (split)
+    hipLaunchKernelGGL((decode_shared_kernel<false, true>), dim3(grid), dim3(256), lds, st, a);
   else
-    hipLaunchKernelGGL(decode_shared_kernel<false>, dim3(grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((decode_shared_kernel<false, false>), dim3(grid), dim3(256), lds, st, a);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,
-                     in.w_seq_stride, out, in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride);
+                     in.w_seq_stride, out, in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride,
+                     split ? SLAT / 2 : 0);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ class DecodeIn(C.Structure):
     _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32), ("block_table", C.c_void_p),
                 ("seq_len", C.c_void_p), ("q_pos", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32),
                 ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32), ("w_seq_stride", C.c_int64),
-                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32)]
+                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32), ("kv_split", C.c_int32)]
 
 
 class DenseIn(C.Structure):
@@ -233,7 +233,7 @@ def _q_dtype(q):
 
 
 def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, w_seq_stride=0,
-              keep_mask=None) -> DecodeIn:
+              keep_mask=None, kv_split=0) -> DecodeIn:
     B, max_blocks = block_table.shape
     words = 0
     if keep_mask is not None:
@@ -242,7 +242,7 @@ def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, 
         words = keep_mask.shape[1]
     return DecodeIn(B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len), _ptr(q_pos), _ptr(q), _q_dtype(q),
                     _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits, w_seq_stride,
-                    _ptr(keep_mask), words)
+                    _ptr(keep_mask), words, kv_split)
 
 
 def _w_stride(layout, wk, wv, B):
@@ -255,12 +255,13 @@ def _w_stride(layout, wk, wv, B):
 
 
 def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                num_splits=0, out=None, ws=None, events=None, keep_mask=None):
+                num_splits=0, out=None, ws=None, events=None, keep_mask=None, kv_split=0):
     """kvc_decode_attn -> fp32 [(L,) B, Hq, d].  events: optional (begin, end) pair of recorded-once
     torch.cuda.Event objects; the call then goes through kvc_decode_attn_timed, which records them around
     the attention kernel alone.  Shared mode: wk, wv [L, latent, Hkv * d] for all sequences, or
     [B, L, latent, Hkv * d] (contiguous), one pair per sequence; keep_mask: optional int32 [B, words] token
-    keep mask (as kvc_evict_select writes it)."""
+    keep mask (as kvc_evict_select writes it); kv_split: latent / 2 for a latent whose lower half holds only
+    key coordinates and upper half only value coordinates (keys and values with their own token factors)."""
     B = block_table.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -268,7 +269,7 @@ def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk,
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
-                    keep_mask)
+                    keep_mask, kv_split)
     c = cache.c()
     if events is None:
         _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
@@ -287,7 +288,7 @@ class DecodePlan:
     they hold at launch time.  Calls enqueue on the current stream, like decode_attn."""
 
     def __init__(self, layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                 num_splits=0, out=None, ws=None, keep_mask=None):
+                 num_splits=0, out=None, ws=None, keep_mask=None, kv_split=0):
         B = block_table.shape[0]
         self.out = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
         need = decode_workspace_bytes(layout, B, max_T, num_splits)
@@ -296,7 +297,7 @@ class DecodePlan:
         self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws, keep_mask)
         self._layout, self._cache = layout, cache.c()
         self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
-                             keep_mask)
+                             keep_mask, kv_split)
         self._args = (C.byref(self._layout), C.byref(self._cache), C.byref(self._in), _ptr(self.out), _ptr(ws),
                       ws.numel())
         self._fn, self._fn_timed = lib().kvc_decode_attn, lib().kvc_decode_attn_timed

@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 4
+    assert kvc.lib().kvc_abi_version() == 5
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -54,7 +54,7 @@ def test_calls_reject_bad_arguments_without_launching():
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 0, 100, 0, C.byref(out)) == -1
     assert lib.kvc_decode_workspace_bytes(C.byref(L), 2, 100, 0, C.byref(out)) == 0 and out.value > 0
     cache = kvc.Cache(None, 0, None, None, None, None, 0)
-    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0, 0, None, 0)
+    inp = kvc.DecodeIn(2, 1, 100, None, None, None, None, 0, None, None, 0, 0, None, 0, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(16), C.c_void_p(16), 1 << 20,
                                None) == -1
     cin = kvc.CompressIn(0, 2, 100, 1, *([None] * 11))
@@ -62,7 +62,7 @@ def test_calls_reject_bad_arguments_without_launching():
     # misaligned pointers are refused before any launch
     cache = kvc.Cache(C.c_void_p(16), 1 << 30, C.c_void_p(32), C.c_void_p(48), C.c_void_p(64), None, 4)
     inp = kvc.DecodeIn(2, 1, 100, C.c_void_p(80), C.c_void_p(96), None, C.c_void_p(113), 1, C.c_void_p(128),
-                       C.c_void_p(144), 0, 0, None, 0)
+                       C.c_void_p(144), 0, 0, None, 0, 0)
     assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), C.c_void_p(160), C.c_void_p(176), 1 << 30,
                                None) == -4
 
@@ -186,7 +186,7 @@ def test_tucker_and_per_sequence_w_rejections_without_launching():
     for name, stride in (("varrank_paged_32k", 8), ("shared_latent_32k", 12), ("shared_latent_32k", -8)):
         w = synth.WORKLOADS[name]
         L = kvc.make_layout(**w.layout_kwargs())
-        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, stride, None, 0)
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, stride, None, 0, 0)
         assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == -1
 
 
@@ -205,5 +205,16 @@ def test_evict_and_keep_mask_rejections_without_launching():
                                     ("shared_latent_32k", p(194), 4, -4)):
         w = synth.WORKLOADS[name]
         L = kvc.make_layout(**w.layout_kwargs())
-        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, mask, words)
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, mask, words, 0)
         assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == want
+
+
+def test_kv_split_only_halves_a_block_shared_latent():
+    lib = kvc.lib()
+    p = C.c_void_p
+    cache = kvc.Cache(p(16), 1 << 30, p(32), p(48), p(64), None, 4)
+    for name, split in (("varrank_paged_32k", 32), ("shared_latent_32k", 128), ("shared_latent_32k", -256)):
+        w = synth.WORKLOADS[name]
+        L = kvc.make_layout(**w.layout_kwargs())
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, None, 0, split)
+        assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == -1

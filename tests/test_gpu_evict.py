@@ -106,6 +106,16 @@ def test_masked_decode_matches_oracle(num_splits):
         out = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
                               q_pos=d["q_pos"], num_splits=num_splits, keep_mask=gm)
         torch.cuda.synchronize()
+        if name == "random":  # the split variant under a mask, on a W with zero halves: the plain masked bits
+            wk2, wv2 = d["wk"].clone(), d["wv"].clone()
+            wk2[:, 256:] = 0
+            wv2[:, :256] = 0
+            a = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], wk2, wv2, w.T, q_pos=d["q_pos"],
+                                num_splits=num_splits, keep_mask=gm)
+            s = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], wk2, wv2, w.T, q_pos=d["q_pos"],
+                                num_splits=num_splits, keep_mask=gm, kv_split=256)
+            torch.cuda.synchronize()
+            assert torch.equal(a, s)
         o = out.cpu().double().numpy()
         assert not np.isnan(o).any()
         if name == "none in one sequence":

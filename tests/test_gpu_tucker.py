@@ -121,8 +121,16 @@ def test_tucker_decode_matches_oracle(kw, seq):
     d = dev(inp)
     gc = gpu_cache(w, d)
     gwk, gwv = _gpu_w(w, d)
-    out = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"])
+    L = gpu_layout(w)
+    out = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"])
+    # the split latent skips the zero halves of W_k and W_v: exact zeros, so the same bits
+    split = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"],
+                            kv_split=w.tucker[0])
+    ones = torch.full((w.B, -(-w.T // 32)), -1, dtype=torch.int32, device="cuda")
+    split_masked = kvc.decode_attn(L, gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"],
+                                   kv_split=w.tucker[0], keep_mask=ones)
     torch.cuda.synchronize()
+    assert torch.equal(out, split) and torch.equal(out, split_masked)
     gp = gc.pool.cpu().numpy()
     assert np.array_equal(gp[:len(cache[0])], cache[0])
     err = rel_err(out, want)
@@ -158,7 +166,8 @@ def test_tucker_fullsize_sampled():
     d = dev(inp)
     gc = gpu_cache(w, d)
     gwk, gwv = _gpu_w(w, d)
-    out = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"])
+    out = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"],
+                          kv_split=w.tucker[0])
     torch.cuda.synchronize()
     assert np.array_equal(gc.pool.cpu().numpy()[:len(cache[0])], cache[0])
     print("[tucker] full size: oracle decode of sequence 1, kv heads 2 and 6", flush=True)
