@@ -406,6 +406,21 @@ typedef struct {
  * outside (0, 1] or null pointers, MISALIGNED for pointers not 4-byte aligned. */
 kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream);
 
+/* Flags of kvc_decode_check (or-ed). */
+#define KVC_BAD_SEQ_LEN 1  /* a seq_len outside 1..min(max_T, max_blocks * page_size)              */
+#define KVC_BAD_PAGE 2     /* a block-table entry of a used block outside 0..n_pages-1              */
+#define KVC_BAD_OFFSET 4   /* a used page whose page_off lies outside 0..pool_bytes-1               */
+#define KVC_BAD_Q_POS 8    /* a negative q_pos                                                      */
+#define KVC_BAD_RANK 16    /* variable rank: a used slot whose rank is not a multiple of 8 in 8..cap */
+
+/* Opt-in check of the tables kvc_decode_attn reads and trusts (a bad page id there is undefined behaviour):
+ * compares the sequence lengths, the used block-table entries, their page offsets, q_pos and (variable
+ * rank) the used slots' ranks with their bounds, reading nothing through them.  Writes the or of the
+ * KVC_BAD_* flags found, 0 if none, to flags (one int32 in device memory).  One workgroup; asynchronous on
+ * stream: read flags after synchronizing.  INVALID_ARG for null tables or sizes out of range. */
+kvc_status kvc_decode_check(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                            int32_t* flags, void* stream);
+
 /* Workspace bytes of kvc_dense_decode_attn for these inputs. */
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
 

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librbc_kvc.so")
-SOURCES = ["api.cpp", "decode_head.hip", "decode_int4.hip", "decode_res.hip", "decode_shared.hip", "compress.hip", "dense.hip", "fit.hip", "alloc.hip", "plan.cpp", "tucker.hip", "evict.hip"]
+SOURCES = ["api.cpp", "decode_head.hip", "decode_int4.hip", "decode_res.hip", "decode_shared.hip", "compress.hip", "dense.hip", "fit.hip", "alloc.hip", "plan.cpp", "tucker.hip", "evict.hip", "check.hip"]
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated (fp16 packed math is unaffected)
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",

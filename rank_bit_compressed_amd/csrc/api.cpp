@@ -38,6 +38,8 @@ kvc_status rank_alloc_impl(const kvc_alloc_in& in, uint8_t* ranks, hipStream_t s
 kvc_status plan_impl(const kvc_plan_in& in, int32_t* choice, double* lambda);
 kvc_status tucker_impl(const kvc_tucker_in& in, uint16_t* w, float* w32, hipStream_t st);
 kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st);
+kvc_status check_impl(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, int32_t* flags,
+                      hipStream_t st);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
                       size_t* need);
 
@@ -254,6 +256,14 @@ kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32,
 kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream) {
   if (!in) return KVC_ERR_INVALID_ARG;
   return evict_impl(*in, keep_mask, (hipStream_t)stream);
+}
+
+kvc_status kvc_decode_check(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                            int32_t* flags, void* stream) {
+  const kvc_status s = check_layout(layout);
+  if (s == KVC_ERR_INVALID_ARG) return s;
+  if (!cache || !in) return KVC_ERR_INVALID_ARG;
+  return check_impl(*layout, *cache, *in, flags, (hipStream_t)stream);
 }
 
 kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes) {

@@ -26,7 +26,7 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
            "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
-           "kvc_evict_select"]
+           "kvc_evict_select", "kvc_decode_check"]
 
 
 class KvcError(RuntimeError):
@@ -130,6 +130,7 @@ def lib():
         L.kvc_plan_budget.argtypes = [P, P, P]; L.kvc_plan_budget.restype = C.c_int32
         L.kvc_tucker_expand.argtypes = [P, P, P, P]; L.kvc_tucker_expand.restype = C.c_int32
         L.kvc_evict_select.argtypes = [P, P, P]; L.kvc_evict_select.restype = C.c_int32
+        L.kvc_decode_check.argtypes = [P, P, P, P, P]; L.kvc_decode_check.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -471,3 +472,16 @@ def evict_select(scores, seq_len, keep_ratio, out=None):
     inp = EvictIn(B, max_T, n_layers, float(keep_ratio), _ptr(seq_len), _ptr(scores))
     _check(lib().kvc_evict_select(C.byref(inp), _ptr(out), _stream()), "kvc_evict_select")
     return out
+
+
+BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK = 1, 2, 4, 8, 16
+
+
+def decode_check(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, q_pos=None) -> int:
+    """kvc_decode_check: the or of the KVC_BAD_* flags of these tables (0 = fine).  Synchronizes."""
+    flags = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    q = torch.empty(16, dtype=torch.float32, device=block_table.device)
+    inp = decode_in(block_table, seq_len, q, q, q, max_T, q_pos)
+    _check(lib().kvc_decode_check(C.byref(layout), C.byref(cache.c()), C.byref(inp), _ptr(flags), _stream()),
+           "kvc_decode_check")
+    return int(flags[0].item())

@@ -218,3 +218,16 @@ def test_kv_split_only_halves_a_block_shared_latent():
         L = kvc.make_layout(**w.layout_kwargs())
         inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, None, 0, split)
         assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == -1
+
+
+def test_decode_check_rejections_without_launching():
+    lib = kvc.lib()
+    p = C.c_void_p
+    L = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].layout_kwargs())
+    cache = kvc.Cache(p(16), 1 << 30, p(32), None, None, None, 4)       # variable rank without tok_rank
+    inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, None, 0, 0)
+    assert lib.kvc_decode_check(C.byref(L), C.byref(cache), C.byref(inp), p(256), None) == -1
+    cache = kvc.Cache(p(16), 1 << 30, p(32), p(48), p(64), None, 4)
+    assert lib.kvc_decode_check(C.byref(L), C.byref(cache), C.byref(inp), None, None) == -1
+    inp = kvc.DecodeIn(0, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, None, 0, 0)
+    assert lib.kvc_decode_check(C.byref(L), C.byref(cache), C.byref(inp), p(256), None) == -1
