@@ -9,7 +9,8 @@
 // position.  One workgroup per sequence: bisection over the 32-bit order key of the block score finds the
 // n-th largest key K (32 counting passes); tokens above K are kept, and tokens equal to K in position order
 // until n are kept (a workgroup prefix count over 1024-token chunks).  Each wave writes the two mask words of
-// its 64 tokens from one ballot.
+// its 64 tokens from one ballot.  Up to 32768 tokens per sequence the keys are computed once into LDS and the
+// passes read them there; longer sequences recompute them from the scores in every pass.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -20,7 +21,8 @@ namespace kvc {
 
 namespace {
 
-constexpr int ET = 1024;  // threads per workgroup
+constexpr int ET = 1024;             // threads per workgroup
+constexpr int EVICT_LDS_TOKENS = 32768;  // keys staged in LDS up to this many tokens per sequence
 
 struct EvictArgs {
   const float* scores;  // [n_layers][B][max_T]
@@ -43,13 +45,20 @@ __device__ inline uint32_t key_at(const EvictArgs& e, const float* s, int t) {
   return order_key(a);
 }
 
+template <bool STAGE>
 __global__ __launch_bounds__(ET) void evict_select_kernel(EvictArgs e) {
   __shared__ int red[ET / 64];
+  extern __shared__ uint32_t keys[];  // STAGE: the sequence's keys
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int T = max(0, min(e.seq_len[b], e.max_T));  // (a length outside 0..max_T is the caller's error)
   const float* s = e.scores + (size_t)b * e.max_T;
   uint32_t* out = e.mask + (size_t)b * e.words;
   const int n_keep = T <= 0 ? 0 : min(T, max(1, (int)floor(e.keep_ratio * (double)T)));
+  if (STAGE) {
+    for (int t = tid; t < T; t += ET) keys[t] = key_at(e, s, t);
+    __syncthreads();
+  }
+  auto key = [&](int t) { return STAGE ? keys[t] : key_at(e, s, t); };
 
   // workgroup sum of one int per thread (every thread gets it)
   auto wg_sum = [&](int c) {
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(ET) void evict_select_kernel(EvictArgs e) {
   };
   auto count_ge = [&](uint32_t K) {
     int c = 0;
-    for (int t = tid; t < T; t += ET) c += key_at(e, s, t) >= K;
+    for (int t = tid; t < T; t += ET) c += key(t) >= K;
     return wg_sum(c);
   };
 
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(ET) void evict_select_kernel(EvictArgs e) {
     const int t = base + tid;
     bool gt = false, eq = false;
     if (n_keep > 0 && t < T) {
-      const uint32_t k = key_at(e, s, t);
+      const uint32_t k = key(t);
       gt = k > K;
       eq = k == K;
     }
@@ -122,8 +131,16 @@ kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st) {
   for (const void* p : ptrs)
     if ((uintptr_t)p & 3) return KVC_ERR_MISALIGNED;
   EvictArgs e{in.scores, in.seq_len, mask, in.B, in.max_T, in.n_layers, (in.max_T + 31) / 32, in.keep_ratio};
-  hipLaunchKernelGGL(evict_select_kernel, dim3(in.B), dim3(ET), 0, st, e);
-  const hipError_t err = hipGetLastError();
+  hipError_t err;
+  if (in.max_T <= EVICT_LDS_TOKENS) {
+    const int lds = in.max_T * 4;
+    err = hipFuncSetAttribute((const void*)evict_select_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return hip_fail(err);
+    hipLaunchKernelGGL(evict_select_kernel<true>, dim3(in.B), dim3(ET), lds, st, e);
+  } else {
+    hipLaunchKernelGGL(evict_select_kernel<false>, dim3(in.B), dim3(ET), 0, st, e);
+  }
+  err = hipGetLastError();
   return err == hipSuccess ? KVC_OK : hip_fail(err);
 }
 

@@ -49,6 +49,13 @@ def test_select_many_ties_integer_scores():
     _select_case(s, [5000, 4097, 1024, 33], 0.999)
 
 
+def test_select_longer_than_the_lds_stage():
+    # past 32768 tokens per sequence the keys are recomputed from the scores in every pass
+    s = torch.stack([synth.make_salience(2, 40000, seed=60 + l) for l in range(2)])
+    s[:, 1, 35000:] = 2.0
+    _select_case(s, [40000, 36001], 0.2)
+
+
 def test_select_full_size():
     w = synth.WORKLOADS["shared_latent_32k_evict30"]
     inp = synth.make_inputs(w)
