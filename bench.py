@@ -279,6 +279,45 @@ def alloc_workload(steps: int) -> dict:
             "ladder": ALLOC_LADDER, "mean_rank_target": ALLOC_MEAN, "mean_rank_allocated": round(mean_rank, 3)}
 
 
+def step_percentiles(torch, plan, dev, n=100) -> dict:
+    """p10 / median / p90 in ms over n steps, warm (one cache, back to back, so its 126 MB can stay in the 256 MB
+    last-level cache) and cold (1 GiB written before each step, outside the events).  "kernel": the attention
+    kernel alone, from the library's events around its launch; "step": kernel + merge from events around the
+    call (cold only: back to back, such events would also time host enqueue gaps); "step_mean": warm steps
+    between two events around all n."""
+    def pct(xs):
+        xs = sorted(xs)
+        return {q: round(xs[min(len(xs) - 1, int(f * (len(xs) - 1) + 0.5))], 5)
+                for q, f in (("p10", 0.1), ("median", 0.5), ("p90", 0.9))}
+
+    def evs(m):
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(m)]
+        for a, b in e:
+            a.record()
+            b.record()
+        return e
+
+    kev, sev, blk = evs(n), evs(n), evs(1)[0]
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    blk[0].record()
+    for i in range(n):
+        plan(kev[i])
+    blk[1].record()
+    torch.cuda.synchronize()
+    res = {"n": n, "warm": {"kernel": pct([a.elapsed_time(b) for a, b in kev]),
+                            "step_mean": round(blk[0].elapsed_time(blk[1]) / n, 5)}}
+    for i in range(n):
+        flush.fill_(float(i))
+        sev[i][0].record()
+        plan(kev[i])
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    res["cold"] = {"kernel": pct([a.elapsed_time(b) for a, b in kev]), "step": pct([a.elapsed_time(b) for a, b in sev])}
+    del flush
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +385,7 @@ def main():
     acct = accounting.compressed_stream_bytes(w, inp["ranks"], [w.T] * w.B)
     alg_bytes = acct["stream"] + acct["tables"]
     achieved = alg_bytes / (kernel_avg * 1e-3) / 1e9
+    step_ms = step_percentiles(torch, plans[0], dev)
 
     dense = None
     if not args.no_dense:
@@ -396,6 +436,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(KERNEL),
                      "kernel": KERNEL, "kernel_ms_avg": round(kernel_avg, 5)},
         "context_tokens_per_s": round(w.B * w.T / (ms_per_step * 1e-3), 1),
+        "step_ms": step_ms,
         "compressed_bytes_per_step": alg_bytes,
         "dense": dense,
     }
