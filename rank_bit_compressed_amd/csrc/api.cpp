@@ -86,7 +86,9 @@ static void choose_splits(const kvc_layout& L, int B, int max_T, int requested, 
   const int items = B * L.n_kv_heads * (L.shared ? L.n_layers : 1);
   int s = requested;
   if (s <= 0) {
-    const int target = L.shared ? 256 : 512;  // workgroups: one (block-shared) or two per compute unit
+    // workgroups: one per compute unit for the kernels that hold one (block-shared, INT4 residual), else two
+    const bool one_per_cu = L.shared || head_decode_path(L) == KVC_PATH_RES;
+    const int target = one_per_cu ? 256 : 512;
     s = std::max(1, (target + items - 1) / items);
   }
   s = std::max(1, std::min(s, n_units));
