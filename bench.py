@@ -98,7 +98,7 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core);
 # the block-shared latent under one eviction decision for its layers (the decision timed on its own).
 OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2",
-         "tucker_group_32k", "shared_latent_32k_evict30")
+         "tucker_group_32k", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered")
 
 
 def decode_flops(w) -> int:
@@ -153,8 +153,10 @@ def other_workloads(steps: int, warmup: int) -> dict:
                 xe[1].record()
                 torch.cuda.synchronize()
                 times.append(xe[0].elapsed_time(xe[1]))
-            kept = int(sum(bin(x & 0xFFFFFFFF).count("1") for x in keep.view(-1).tolist()))
-            extra = {"evict_select_ms_median": round(sorted(times)[2], 5), "kept_fraction": round(kept / (w.B * w.T), 4)}
+            words = keep.view(-1).tolist()
+            kept = int(sum(bin(x & 0xFFFFFFFF).count("1") for x in words))
+            extra = {"evict_select_ms_median": round(sorted(times)[2], 5), "kept_fraction": round(kept / (w.B * w.T), 4),
+                     "empty_super_tile_fraction": round(sum(1 for x in words if x == 0) / len(words), 4)}
         plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
                               q_pos=inp["q_pos"], keep_mask=keep, kv_split=w.tucker[0] if w.tucker else 0)
         for k in ("lat_k", "lat_v", "res_k", "res_v"):
@@ -177,6 +179,8 @@ def other_workloads(steps: int, warmup: int) -> dict:
         acct = accounting.compressed_stream_bytes(w, inp["ranks"], [w.T] * w.B)
         nbytes = acct["stream"] + acct["tables"]
         flops = decode_flops(w)
+        if w.evict_ratio:  # attention runs over the kept tokens only (every token's latent is still read)
+            flops = int(round(flops * extra["kept_fraction"]))
         path = {kvc.PATH_HEAD: "general per-head kernel", kvc.PATH_INT4: "INT4 kernel",
                 kvc.PATH_SHARED: "block-shared kernel", kvc.PATH_RES: "INT4 residual kernel"}[kvc.decode_path(L)]
         r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),

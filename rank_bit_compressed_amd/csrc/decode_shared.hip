@@ -284,9 +284,17 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // wave keeps both units busy.
     const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SD) + (t & 3) * (SNB * 4) + hf;
     f16v_t sc = {};
+    // a super-tile whose tokens are all evicted contributes nothing: only the next one's dequantization runs
+    const bool empty = KEEP && tkeep[k] == 0u;
     if (SPLIT && wv >= 2) {  // value waves: only the next super-tile's value tile
 #pragma unroll
       for (int jj = 0; jj < SNJ; ++jj) *(h8*)(vdst + SCS * jj) = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
+    } else if (empty) {
+#pragma unroll
+      for (int jj = 0; jj < SNJ; ++jj) {
+        bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
+        if (!SPLIT) *(h8*)(vdst + SCS * jj) = bn[jj];
+      }
     } else {
     f16v_t kp[SNB];
 #pragma unroll
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
     // value latent: step nt covers chunks 2nt, 2nt + 1; column n <-> coordinate 128w + 16nt + 8(n/8) + perm8(n%8);
     // lane rho points at the 4 columns 4(q4 % 2).. of chunk (2nt + q4 / 2, token 8g + 4v + rho / 4)
-    if (!SPLIT || wv >= 2) {
+    if ((!SPLIT || wv >= 2) && !empty) {
       const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
       const int q4 = rho & 3;
       const uint8_t* vb = vt_w + (k & 1) * SVT + SCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;

@@ -28,7 +28,8 @@ Distributions (the pages give shapes, not data):
   * salience for the rank-allocation tests: exp(N(0, 1.5^2)) per token, a
     heavy-tailed positive spread like attention mass, rounded to fp32; the
     per-layer token scores of an evicting block-shared workload are one such
-    draw per layer;
+    draw per layer (or, clustered, exp(u + 0.3 n) with u ~ N(0, 1.5^2) per run
+    of tokens shared by the layers and n ~ N(0, 1) per token and layer);
   * partial Tucker factors of a layer group (keys and values separately), per
     sequence: token factor rows N(0, 1/T) per element (the scale of a factor
     with orthonormal columns over T tokens); the feature factor an orthonormal
@@ -75,6 +76,7 @@ class Workload:
     w_std: float = 0.0            # block-shared mode: W entries N(0, w_std^2)
     tucker: tuple = ()            # block-shared from partial Tucker factors: (key r_t, value r_t, r_f)
     evict_ratio: float = 0.0      # block-shared: share of tokens the block's eviction decision keeps
+    evict_cluster: int = 0        # > 0: token scores clustered in runs of this many tokens (see make_layer_scores)
     seed: int = 0
 
     def scaled(self, **kw) -> "Workload":
@@ -128,6 +130,12 @@ WORKLOADS = {
                                           head_dim=128, r_k=512, r_v=512, group=64, shared=True, n_layers=4,
                                           rope_theta=500000.0, latent_decay=0.0, w_std=1.0 / math.sqrt(512.0),
                                           evict_ratio=0.3, seed=14),
+    # the same with token importance clustered in runs of 256 tokens, so that whole super-tiles are evicted
+    "shared_latent_32k_evict30_clustered": Workload("shared_latent_32k_evict30_clustered", B=4, T=32768,
+                                                    n_q_heads=32, n_kv_heads=8, head_dim=128, r_k=512, r_v=512,
+                                                    group=64, shared=True, n_layers=4, rope_theta=500000.0,
+                                                    latent_decay=0.0, w_std=1.0 / math.sqrt(512.0),
+                                                    evict_ratio=0.3, evict_cluster=256, seed=14),
     # the lower-bit codecs of the BellowsKV page's retention table on per-head latents: the 32K variable-rank
     # workload with INT3 latents, and the 8K layer with 3-bit keys and 2-bit values
     "varrank_paged_32k_int3": Workload("varrank_paged_32k_int3", B=16, T=32768, n_q_heads=32, n_kv_heads=8,
@@ -226,13 +234,28 @@ def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
     else:
         out["wk"] = _orthonormal(w, 8, d, w.r_k, Hkv).to(torch.bfloat16).to(dev)
         out["wv"] = _orthonormal(w, 9, d, w.r_v, Hkv).to(torch.bfloat16).to(dev)
-    if w.evict_ratio:  # per-layer token importance of the block (the salience law, one draw per layer)
-        out["layer_scores"] = torch.stack([make_salience(B, T, seed=w.seed * 10 + l, device=dev)
-                                           for l in range(w.n_layers)]).contiguous()
+    if w.evict_ratio:
+        out["layer_scores"] = make_layer_scores(w, dev)
     qshape = ((w.n_layers,) if w.shared else ()) + (B, w.n_q_heads, d)
     q = torch.randn(qshape, generator=_gen(w, 10, "cpu"), dtype=torch.float32) / 8.0
     out["q"] = (q.to(torch.bfloat16) if w.q_bf16 else q).to(dev)
     return out
+
+
+def make_layer_scores(w: Workload, device="cpu") -> torch.Tensor:
+    """fp32 [n_layers, B, T] per-layer token importance of a block: one salience draw per layer, or (evict_cluster
+    c > 0) exp(u + 0.3 n) with u ~ N(0, 1.5^2) per run of c tokens, shared by the block's layers, and n ~ N(0, 1)
+    per token and layer."""
+    B, T = w.B, w.T
+    if not w.evict_cluster:
+        return torch.stack([make_salience(B, T, seed=w.seed * 10 + l, device=device)
+                            for l in range(w.n_layers)]).contiguous()
+    c = w.evict_cluster
+    g = _gen(w, 40, "cpu")
+    u = 1.5 * torch.randn(B, -(-T // c), generator=g, dtype=torch.float64)
+    u = u.repeat_interleave(c, dim=1)[:, :T]
+    n = torch.randn(w.n_layers, B, T, generator=g, dtype=torch.float64)
+    return torch.exp(u[None] + 0.3 * n).to(torch.float32).to(device).contiguous()
 
 
 def make_dense_inputs(w: Workload, device="cpu") -> dict:

@@ -74,7 +74,8 @@ def test_decode_path_selection():
     want = {"tiny": kvc.PATH_HEAD, "llama8b_layer_8k": kvc.PATH_INT4, "varrank_paged_32k": kvc.PATH_INT4,
             "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
             "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4,
-            "tucker_group_32k": kvc.PATH_SHARED, "shared_latent_32k_evict30": kvc.PATH_SHARED}
+            "tucker_group_32k": kvc.PATH_SHARED, "shared_latent_32k_evict30": kvc.PATH_SHARED,
+            "shared_latent_32k_evict30_clustered": kvc.PATH_SHARED}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)

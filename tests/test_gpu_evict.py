@@ -104,8 +104,11 @@ def test_masked_decode_matches_oracle(num_splits):
     torch.cuda.synchronize()
     assert torch.equal(plain, all_kept)
     masks = _masks(w, seq, np.random.default_rng(5))
-    # and the mask the eviction decision gives for the workload's layer scores
+    # and the masks the eviction decision gives for the workload's layer scores, i.i.d. and clustered in runs
+    # of 64 tokens (whole super-tiles evicted)
     masks["evict 30%"] = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    masks["evict 30% clustered"] = E.keep_mask(synth.make_layer_scores(w.scaled(evict_cluster=64)).numpy(), seq,
+                                               w.evict_ratio)
     for name, m in masks.items():
         print(f"[evict] masked decode '{name}' num_splits={num_splits}", flush=True)
         want = _masked_oracle(w, inp, cache, m)
