@@ -362,3 +362,105 @@ def test_projection_identities_on_an_exact_orthonormal_basis():
         assert np.allclose(np.einsum("thd,hdr->thr", e[0], Bm), 0, atol=1e-6)
         recon = np.einsum("thr,hdr->thd", lat[0].astype(np.float64), Bm) + e[0]
         assert np.allclose(recon, x[0].numpy(), atol=1e-6)
+
+
+# ---------------------------------------------------------------- layer axis of the block-shared mode
+
+def dequant_shared_latent(lat, group):
+    """The stored block-shared latent as the decode must see it: each group of `group` coordinates quantized by
+    the INT4 quantizer and dequantized as code * scale + zero (computed here from the quantizer's outputs)."""
+    T, n = lat.shape
+    S, Z, Q = ref.quant_int4(lat.reshape(T * n // group, group))
+    deq = Q * S.view(np.float16).astype(np.float64)[:, None] + Z.view(np.float16).astype(np.float64)[:, None]
+    return deq.reshape(T, n)
+
+
+@pytest.mark.parametrize("n_layers", [2, 4])
+def test_shared_layers_each_use_their_own_up_projection_and_query(n_layers):
+    # BellowsKV, "Share the Input, Not the Cache": every layer of the block rebuilds its keys and values from the
+    # one stored latent through its own up-projection.  Layer l's output is textbook attention with q[l], keys
+    # W_k[l]^T c and values W_v[l]^T c, everything here computed in numpy from the quantizer's outputs; the
+    # per-layer W and q all differ, so a wrong layer stride in the oracle reads another layer's operands.
+    w = synth.WORKLOADS["shared_latent_32k"].scaled(B=2, T=300, n_layers=n_layers, page_size=64,
+                                                     shuffle_pages=True)
+    inp = synth.make_inputs(w, seq_len=[300, 171])
+    out = oracle_decode(w, inp, oracle_cache(w, inp))
+    Wk = inp["wk"].double().numpy(); Wv = inp["wv"].double().numpy()
+    q = np_f32(inp["q"])
+    assert out.shape == (n_layers, w.B, 32, 128)
+    for b in range(w.B):
+        T = int(inp["seq_len"][b])
+        c = dequant_shared_latent(np_f32(inp["lat_k"])[b, :T], w.group)
+        for l in range(n_layers):
+            for h in (0, 5, 7):
+                k = c @ Wk[l][:, 128 * h: 128 * h + 128]
+                v = c @ Wv[l][:, 128 * h: 128 * h + 128]
+                want = sdpa64(rope_complex(q[l, b, 4 * h: 4 * h + 4], T, w.rope_theta),
+                              rope_complex(k, np.arange(T), w.rope_theta), v)
+                assert np.allclose(out[l, b, 4 * h: 4 * h + 4], want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_shared_layers_with_embedded_per_layer_bases_equal_per_head_mode():
+    # two layers, each with its own per-head bases embedded block-diagonally in W[l]: layer l of the shared
+    # decode equals the per-head decode of the same latents with layer l's bases and query
+    wp = synth.WORKLOADS["llama8b_layer_8k"].scaled(T=200, r_k=64, r_v=64, group=64, page_size=64)
+    per_layer = []
+    for l in range(2):
+        inp = synth.make_inputs(wp.scaled(seed=100 + l))
+        per_layer.append(inp)
+    base = per_layer[0]
+    lat = base["lat_k"]
+    ws = synth.WORKLOADS["shared_latent_32k"].scaled(B=1, T=200, n_layers=2, page_size=64)
+    Hkv, d = 8, 128
+    W = {n: torch.zeros(2, 512, Hkv * d, dtype=torch.bfloat16) for n in ("wk", "wv")}
+    for l in range(2):
+        for name in ("wk", "wv"):
+            for h in range(Hkv):
+                W[name][l, 64 * h: 64 * h + 64, d * h: d * h + d] = per_layer[l][name][h].T
+    q = torch.stack([per_layer[l]["q"] for l in range(2)])
+    inps = dict(base, lat_k=lat.reshape(1, 200, 512).contiguous(), lat_v=None, wk=W["wk"], wv=W["wv"], q=q)
+    out_s = oracle_decode(ws, inps, oracle_cache(ws, inps))
+    for l in range(2):
+        inpl = dict(per_layer[l], lat_k=lat, lat_v=lat.clone())
+        out_p = oracle_decode(wp, inpl, oracle_cache(wp, inpl))
+        assert np.allclose(out_s[l], out_p, rtol=0, atol=1e-13 * np.abs(out_p).max())
+
+
+# ---------------------------------------------------------------- projection under per-token ranks
+
+def test_variable_rank_projection_truncates_to_each_tokens_rank():
+    # VarRate, "Method": a token of rank r keeps r coordinates.  On an exactly orthonormal basis (the Sylvester
+    # blocks H_64 / 8, entries +-1/8, exact in bf16) the projection of token t must be B_r^T x in its first r
+    # coordinates and zero past them, and the residual must be H (x - B_r B_r^T x) over r columns only: the
+    # columns r..cap-1 are left in the residual.  All expected values are numpy here.
+    w = synth.WORKLOADS["residual_128k"].scaled(B=2, T=40, page_size=64, r_k=64, r_v=64, variable_rank=True,
+                                                rank_choices=(8, 16, 32, 64), rank_probs=(0.4, 0.3, 0.2, 0.1))
+    H64 = scipy.linalg.hadamard(64) / 8.0
+    Q = np.kron(np.eye(2), H64)                                  # 128 x 128, exactly orthonormal
+    rng = np.random.default_rng(3)
+    perms = [rng.permutation(128) for _ in range(8)]             # a different column choice per KV head
+    Bk = torch.tensor(np.stack([Q[:, p[:64]] for p in perms]), dtype=torch.float32).to(torch.bfloat16)
+    Bv = torch.tensor(np.stack([Q[:, p[64:]] for p in perms]), dtype=torch.float32).to(torch.bfloat16)
+    ranks = synth.make_inputs(w)["ranks"]
+    seq = np.array([40, 23], np.int32)
+    g = torch.Generator().manual_seed(11)
+    kk = torch.randn(2, 40, 8, 128, generator=g); vv = torch.randn(2, 40, 8, 128, generator=g)
+    lk, lv, rk, rv = ref.project(layout(w), seq, 40, np_any(ranks), kk.numpy(), vv.numpy(), np_u16(Bk), np_u16(Bv))
+    H128 = scipy.linalg.hadamard(128) / math.sqrt(128)
+    seen = set()
+    for lat, res, Bm, x in ((lk, rk, Bk, kk), (lv, rv, Bv, vv)):
+        Bm = Bm.double().numpy()                                 # [Hkv, d, 64]
+        for b in range(2):
+            for t in range(int(seq[b])):
+                r = int(ranks[b, t]); seen.add(r)
+                xt = x[b, t].double().numpy()                    # [Hkv, d]
+                c = np.einsum("hd,hdr->hr", xt, Bm[:, :, :r])
+                assert np.allclose(lat[b, t, :, :r], c, rtol=0, atol=1e-5)
+                assert not lat[b, t, :, r:].any()
+                e = xt - np.einsum("hr,hdr->hd", c, Bm[:, :, :r])
+                assert np.allclose(res[b, t], e @ H128, rtol=0, atol=1e-5)
+                if r < 64:                                       # the dropped columns stay in the residual
+                    assert np.abs(np.einsum("hd,hdr->hr", e, Bm[:, :, r:])).max() > 1e-2
+            for t in range(int(seq[b]), 40):                     # rows past the length are left alone
+                assert not lat[b, t].any() and not res[b, t].any()
+    assert seen == {8, 16, 32, 64}
