@@ -412,10 +412,16 @@ kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* s
 #define KVC_BAD_OFFSET 4   /* a used page whose page_off lies outside 0..pool_bytes-1               */
 #define KVC_BAD_Q_POS 8    /* a negative q_pos                                                      */
 #define KVC_BAD_RANK 16    /* variable rank: a used slot whose rank is not a multiple of 8 in 8..cap */
+#define KVC_BAD_TOK_OFF 32 /* variable rank: a used page whose tok_off row is not the exclusive prefix of its
+                              tok_rank row (ranks in bits 0-15, ceil(rank / group) in bits 16-31, entry
+                              page_size the totals), or one of whose slots holds a rank above the cap     */
+#define KVC_BAD_RECORD 64  /* a used page whose record (n_kv_heads head blocks, sized from the page's
+                              totals or the uniform rank) starts inside the pool but ends past pool_bytes */
 
 /* Opt-in check of the tables kvc_decode_attn reads and trusts (a bad page id there is undefined behaviour):
- * compares the sequence lengths, the used block-table entries, their page offsets, q_pos and (variable
- * rank) the used slots' ranks with their bounds, reading nothing through them.  Writes the or of the
+ * compares the sequence lengths, the used block-table entries, their page offsets and record ends, q_pos
+ * and (variable rank) the used slots' ranks and every offset row of a used page with their bounds and with
+ * each other, reading nothing through them.  Writes the or of the
  * KVC_BAD_* flags found, 0 if none, to flags (one int32 in device memory).  One workgroup; asynchronous on
  * stream: read flags after synchronizing.  INVALID_ARG for null tables or sizes out of range. */
 kvc_status kvc_decode_check(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,

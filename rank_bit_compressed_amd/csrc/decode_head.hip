@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
             const float* src = (const float*)(sb + S.kc + kco) + 8 * w;
             for (int j = 0; j < 8; ++j) kb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
           } else {
-            const uint32_t x = codes8_as_nibbles<KB>(sb + S.kc + kco + KB * w);
+            const uint32_t x = codes8_as_nibbles<KB>(sb + S.kc, kco + KB * w);
             const uint32_t sz = *(const uint32_t*)(sb + S.km + kmo + 4 * ((8 * w) / a.G));
             kb[c] = dequant_int4x8(x, ok ? sz : 0u);
           }
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void decode_head_kernel(DecodeHeadArgs a) {
             const float* src = (const float*)(sb + S.vc + vco) + 8 * w;
             for (int j = 0; j < 8; ++j) vb[c][j] = ok ? (_Float16)src[j] : (_Float16)0.0f;
           } else {
-            const uint32_t x = codes8_as_nibbles<VB>(sb + S.vc + vco + VB * w);
+            const uint32_t x = codes8_as_nibbles<VB>(sb + S.vc, vco + VB * w);
             const uint32_t sz = *(const uint32_t*)(sb + S.vm + vmo + 4 * ((8 * w) / a.G));
             vb[c] = dequant_int4x8(x, ok ? sz : 0u);
           }

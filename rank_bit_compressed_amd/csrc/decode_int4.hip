@@ -54,8 +54,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 namespace i4 {
 constexpr int D = 128, GQ = 4, NP = 64;
 constexpr int MAX_SPLIT_PAGES = 128;
-constexpr float TAU = 8.0f;  // lazy-max slack, log2 units
-constexpr int STATIC_LDS = 4 * 2 * GQ * (NP + 4) * 4 + 4 * 32 * GQ * 2;  // the kernel's own LDS arrays (bytes)
+constexpr float TAU = 8.0f;   // lazy-max slack, log2 units
+constexpr int QROW = NP + 4;  // dwords per row of the rotated-query and RoPE tables (padded against bank conflicts)
+// the kernel's own LDS arrays (bytes): per wave the two query variants x 4 heads, the RoPE factors of in-block
+// positions 0..31, per wave the probabilities of a super-tile, per wave the decode order of its 64 slots
+constexpr int STATIC_LDS = 4 * 2 * GQ * QROW * 4 + 32 * QROW * 4 + 4 * 32 * GQ * 2 + 4 * 64;
 
 struct Lds {
   int meta_addr, meta_hb, meta_page, theta, qsrc, stage, stage_bytes, off_bytes, total;
@@ -106,8 +109,37 @@ __device__ inline void vmcnt_wait(int k) {
   }
 }
 
+// The lane index computed afresh (volatile, so that it is not merged with another computation of it and kept
+// in a register across a loop).
+__device__ inline int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+template <int N>
+struct Steps {
+  static constexpr int value = N;
+};
+
+// x through an identity DPP move (quad_perm 0,1,2,3).  A select between two entries of one vector is otherwise
+// turned into an extract at a computed index, lowered as a chain of compares and selects over every entry; with
+// one operand passed through here it stays one v_cndmask.
+__device__ inline float dpp_id(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xE4, 0xF, 0xF, false));
+}
+
 // KS, VS: 16-coordinate steps of the key / value rank caps (2..4); VT: 32-coordinate value tiles; KB, VB: bits
 // of the key / value codes (4, or the lower-bit codecs 3 and 2, spread to the INT4 nibble layout as they are read)
+//
+// Wave w decodes the 64 slots 64w..64w+63 of every page (two 32-token super-tiles; a page of fewer slots
+// leaves later waves idle).  Variable rank: the wave takes its 64 slots in order of their number of
+// 16-coordinate steps (the "class", ceil(rank / 16)), equal classes in slot order -- a ballot per class, no
+// exchange with the other waves -- so that a super-tile runs only the steps of its largest rank instead of the
+// cap's.  Its token at page slot s = 32 v + u then sits at an arbitrary lane: R(t0 + 32 v + u) = R(t0 + 32 v)
+// R(u), R(u) for u < 32 from an LDS table on the key side, R(q_pos - t0 - 32 v) q on the query side as the two
+// variants of the wave's block, which fill the rows of the score product (rows 8i..8i+7 hold variant i % 2,
+// head = row % 4), so that every lane holds both variants' scores of its token and keeps one.
 template <int KS, int VS, bool VAR, int STG, int KB, int VB>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   using namespace i4;
@@ -129,14 +161,19 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   const int qpos = a.q_pos ? a.q_pos[b] : T;
   const int lb0 = split * a.pages_per_split;
   const int n_pages = max(0, min((T + P - 1) / P, lb0 + a.pages_per_split) - lb0);
-  // Per-wave buffers that the page copies never touch live in arrays of their own, so that the compiler can
-  // tell their reads apart from the LDS the copies write and does not wait for copies in flight before them.
-  // qbuf: per wave two super-tiles of rotated query, rows padded by 4 dwords; pbuf: per wave the
-  // probabilities of 32 tokens x 4 heads, fp16.
-  __shared__ __attribute__((aligned(16))) uint32_t qbuf_all[4 * 2 * GQ * (NP + 4)];
+  // Buffers that the page copies never touch live in arrays of their own, so that the compiler can tell
+  // their reads apart from the LDS the copies write and does not wait for copies in flight before them.
+  // qbuf: per wave the two query variants x 4 heads (row 4 v + head), fp16 pairs (x_j, x_{j+64}); rtab:
+  // (cos, sin)(u theta_j) for u < 32; pbuf: per wave the probabilities of 32 tokens x 4 heads, fp16; sorder:
+  // per wave the decode order of its 64 slots.
+  __shared__ __attribute__((aligned(16))) uint32_t qbuf_all[4 * 2 * GQ * QROW];
+  __shared__ __attribute__((aligned(16))) uint32_t rtab[32 * QROW];
   __shared__ __attribute__((aligned(16))) _Float16 pbuf_all[4 * 32 * GQ];
-  static_assert(sizeof(qbuf_all) + sizeof(pbuf_all) == STATIC_LDS, "static LDS accounting");
-  uint32_t* qbuf = qbuf_all + wv * 2 * GQ * (NP + 4);
+  __shared__ uint8_t sorder_all[4 * 64];
+  static_assert(sizeof(qbuf_all) + sizeof(rtab) + sizeof(pbuf_all) + sizeof(sorder_all) == STATIC_LDS,
+                "static LDS accounting");
+  uint32_t* qbuf = qbuf_all + wv * 2 * GQ * QROW;
+  uint8_t* sorder = sorder_all + wv * 64;
 
   // ---- page addresses of the split
   for (int i = tid; i < n_pages; i += 256) {
@@ -179,18 +216,6 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   // ---- RoPE frequencies, once per workgroup: theta_j (fp64 pow) in turns per position
   double* tturn = (double*)(smem + LY.theta);
   if (tid < NP) tturn[tid] = (a.theta > 0.0 ? pow(a.theta, -2.0 * tid / D) : 0.0) * 0.15915494309189535;
-  __syncthreads();
-  // RoPE factors (cos, sin)(t theta_j) of this lane's slot t: pair j = 32m + 8(i/4) + 4hf + i%4 for
-  // accumulator entry i of tiles m and m + 2; |t theta_j| < 32 turns, where v_sin / v_cos are accurate
-  uint32_t rf[2][16];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = 32 * m + 8 * (i / 4) + 4 * hf + i % 4;
-      const float rev = (float)(t * tturn[j]);
-      rf[m][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-    }
   // one-hot B operands of the value transpose: k-slot 8hf + j of step s holds coordinate 16s + 8hf + perm8(j);
   // it goes to column (16 (s % 2) + 8hf + perm8(j)) of value tile s / 2
   h8 ohv[2];
@@ -221,46 +246,56 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     qsrc[j * 8 + hq] = x0 * sc;
     qsrc[j * 8 + 4 + hq] = x1 * sc;
   }
+  __syncthreads();  // frequencies and the scaled query visible
+  // (cos, sin)(u theta_j) for u < 32 and every pair j; |u theta_j| < 32 turns, where v_sin / v_cos are accurate
+  for (int e = tid; e < 32 * NP; e += 256) {
+    const int u = e / NP, j = e % NP;
+    const float rev = (float)(u * tturn[j]);
+    rtab[u * QROW + j] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+  }
   const double fj = tturn[lane];  // turns per position of pair `lane` (query rotation)
 
   // ---- page staging.  Wave w copies the 16-byte chunks 256k + 64w + l of the head block (and a share of
-  // the page's offset row) into buffer i % 2; it returns the number of copy instructions the wave issued.
-  auto issue = [&](int i) -> int {
+  // the page's offset row) into buffer i % 2.
+  auto issue = [&](int i) {
     uint8_t* dst = smem + LY.stage + (i % 2) * LY.stage_bytes;
     const int bytes = __builtin_amdgcn_readfirstlane(meta_hb[i]);
     // buffer resources: scalar base and size (reads past the size return zeros)
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.pool + uniform64(meta_addr[i])), (short)0, bytes, 0x00020000);
-    int cnt = 0;
+    // The lane index is recomputed here, and the lane test compares it with a scalar count of 16-byte chunks:
+    // a register kept across the page loop for it, or a per-copy lane offset, could be spilled, and the wait
+    // for its reload would also wait for the copies issued before it.
+    const int ln = fresh_lane_id();
 #pragma unroll
     for (int k = 0; k < STG; ++k) {
       const int base = 16 * (256 * k + 64 * wv);
       if (base >= bytes) break;  // wave-uniform: every issued copy has lane 0 active
-      if (base + 16 * lane < bytes)
+      if (ln < ((bytes - base) >> 4))
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + LY.off_bytes + base),
-                                                 16, 16 * lane, base, 0, 0);
-      ++cnt;
+                                                 16, 16 * ln, base, 0, 0);
     }
     if constexpr (VAR) {
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.tok_off + (size_t)__builtin_amdgcn_readfirstlane(meta_page[i]) * (P + 1)), (short)0, 4 * (P + 1),
           0x00020000);
-      for (int base = 64 * wv; base <= P; base += 256) {
+      for (int base = 64 * wv; base <= P; base += 256)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (__attribute__((address_space(3))) void*)(dst + 4 * base), 4,
-                                                 4 * lane, 4 * base, 0, 0);
-        ++cnt;
-      }
+                                                 4 * ln, 4 * base, 0, 0);
     }
-    return cnt;
   };
-  // this wave's copies except the last `keep` issued have landed (the explicit wait), and after the barrier
-  // everyone's have.  The copies write LDS directly, and LDS is coherent within the workgroup, so the barrier
-  // needs no memory fence of its own: a workgroup-scope one would make every wave wait for its copies still
-  // in flight.  The wavefront-scope LDS fences only keep the compiler from moving LDS accesses across it.
-  auto settle = [&](int keep) {
-    vmcnt_wait(keep);
+  // every copy this wave issued has landed, and after the barrier everyone's have.  The copies write LDS
+  // directly, and LDS is coherent within the workgroup, so the barrier needs no memory fence of its own.  The
+  // wavefront-scope LDS fences only keep the compiler from moving LDS accesses across it.
+  auto settle = [&]() {
+    vmcnt_wait(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   };
 
@@ -280,12 +315,13 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
 
   struct Words {  // a lane's LDS words for one super-tile: code dword and (scale, zero) word per step
     uint32_t k[KS], pk[KS];
-    int co_v, po_v, r;
+    int co_v, po_v, r, rv, slot, ns;  // r, rv: key and value rank (0 past the sequence end); slot in the page
+    bool ok;
   };
 
-  __syncthreads();  // page addresses and the scaled query visible
+  __syncthreads();  // page addresses, the RoPE table visible
   if (n_pages > 0) issue(0);
-  settle(0);
+  settle();
   for (int ip = 0; ip < n_pages; ++ip) {
     if (ip + 1 < n_pages) issue(ip + 1);  // into the buffer everyone finished with before the last barrier
     const uint32_t* so = (const uint32_t*)(smem + LY.stage + (ip % 2) * LY.stage_bytes);
@@ -298,178 +334,225 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     } else {
       S = a.S_uniform;
     }
-    // the 16 codes of step s take 2 KB bytes; this lane's half hf reads the KB bytes of codes 16 s + 8 hf ..
-    const uint8_t* kcs = sb + S.kc + KB * hf;
-    const uint8_t* vcs = sb + S.vc + VB * hf;
+    const uint8_t* kcs = sb + S.kc;
+    const uint8_t* vcs = sb + S.vc;
     const uint8_t* kms = sb + S.km;
     const uint8_t* vms = sb + S.vm;
     const int page_t0 = (lb0 + ip) * P;
-    const int n_st = min(P, T - page_t0 + 31) / 32;    // super-tiles of this page holding tokens
-    const int nst_w = (n_st > wv) + (n_st > wv + 4);  // this wave's: super-tiles wv and wv + 4
-    if (nst_w > 0) {
-      // queries rotated by the bases of this wave's super-tiles, q~ = R(q_pos - t0) q; lane j: pair j
-      {
-        const f4 qa = *(const f4*)&qsrc[lane * 8], qb = *(const f4*)&qsrc[lane * 8 + 4];
-        for (int k = 0; k < nst_w; ++k) {
-          double rev = (double)(qpos - page_t0 - 32 * (wv + 4 * k)) * fj;
-          rev -= rint(rev);  // |rev| <= 1/2 turn; v_sin / v_cos take turns
-          const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+    const int pb = 64 * wv;                                   // this wave's first slot of the page
+    const int nvb = max(0, min(64, min(P, T - page_t0) - pb));  // its slots holding tokens
+    // the two query variants of the wave's block, q~ = R(q_pos - t0 - pb - 32 v) q, v = 0, 1; lane j: pair j
+    {
+      const f4 qa = *(const f4*)&qsrc[lane * 8], qb = *(const f4*)&qsrc[lane * 8 + 4];
 #pragma unroll
-          for (int hq = 0; hq < GQ; ++hq)
-            qbuf[(k * GQ + hq) * (NP + 4) + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-
-      // the key LDS words of super-tile k of this wave (slot 32 (wv + 4k) + t), issued one super-tile ahead,
-      // and the value offsets (the value words are read when the keys are done)
-      auto fetch = [&](int k) -> Words {
-        const int slot = 32 * (wv + 4 * k) + t;
-        int r, co_k, po_k;
-        Words w;
-        if constexpr (VAR) {
-          const uint32_t o0 = so[slot], o1 = so[slot + 1];
-          r = (int)((o1 - o0) & 0xFFFFu);  // 0 for slots past the sequence end
-          co_k = w.co_v = (int)((o0 & 0xFFFFu) * KB / 8);
-          po_k = w.po_v = (int)(o0 >> 16) * 4;
-        } else {
-          r = a.rk;
-          co_k = slot * kcb;
-          w.co_v = slot * vcb;
-          po_k = slot * kmb;
-          w.po_v = slot * vmb;
-        }
-        w.r = r;
+      for (int v = 0; v < 2; ++v) {
+        double rev = (double)(qpos - page_t0 - pb - 32 * v) * fj;
+        rev -= rint(rev);  // |rev| <= 1/2 turn; v_sin / v_cos take turns
+        const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          w.k[s] = codes8_as_nibbles<KB>(kcs + co_k + 2 * KB * s);
-          w.pk[s] = lds_u32(kms, po_k + 4 * ((16 * s + 8 * hf) / a.G));
-          if constexpr (VAR) w.pk[s] = pair_if(16 * s + 8 * hf < r, w.pk[s]);
-        }
-        return w;
-      };
-
-      Words nxt = fetch(0);
-      for (int k = 0; k < nst_w; ++k) {
-        const Words cur = nxt;
-        if (k + 1 < nst_w) nxt = fetch(k + 1);
-        const uint32_t* qrow = qbuf + (k * GQ + (t & 3)) * (NP + 4) + 4 * hf;
-        const int t0 = page_t0 + 32 * (wv + 4 * k);
-        uint32_t vw[VS], vp[VS];
-#pragma unroll
-        for (int s = 0; s < VS; ++s) {
-          vw[s] = codes8_as_nibbles<VB>(vcs + cur.co_v + 2 * VB * s);
-          vp[s] = lds_u32(vms, cur.po_v + 4 * ((16 * s + 8 * hf) / a.G));
-          if constexpr (VAR) vp[s] = pair_if(16 * s + 8 * hf < cur.r, vp[s]);
-        }
-
-        // ---- keys: dequantize all steps, then per half m the tiles m and m + 2 (head dims d and d + 64),
-        // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
-        h8 kb[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(cur.k[s], cur.pk[s]);
-        f16v sc = {};
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f16v ka = {}, kz = {};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            ka = mfma32(bf[s][m], kb[s], ka);
-            kz = mfma32(bf[s][m + 2], kb[s], kz);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            h8 kq;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const h2 rr = as_h2(rope_pair(pack_h2(ka[4 * q + p], kz[4 * q + p]), rf[m][4 * q + p]));
-              kq[2 * p] = rr.x;
-              kq[2 * p + 1] = rr.y;
-            }
-            const h8 qf = *(const h8*)(qrow + 32 * m + 8 * q);
-            sc = mfma32(qf, kq, sc);
-          }
-        }
-
-        // ---- values: dequantize, transpose into (coordinate, token) tiles through one-hot MFMAs
-        h8 vop[VT][2];
-        {
-          f16v vt[VT];
-#pragma unroll
-          for (int w = 0; w < VT; ++w) vt[w] = f16v{};
-#pragma unroll
-          for (int s = 0; s < VS; ++s) vt[s / 2] = mfma32(dequant_int4x8(vw[s], vp[s]), ohv[s & 1], vt[s / 2]);
-#pragma unroll
-          for (int w = 0; w < VT; ++w) {
-            vop[w][0] = cvt_h8(vt[w], 0);
-            vop[w][1] = cvt_h8(vt[w], 8);
-          }
-        }
-
-        // ---- online softmax; lane (token t) holds the scores of heads 0-3 in sc[0..3]
-        float s4[4] = {sc[0] - m_ref[0], sc[1] - m_ref[1], sc[2] - m_ref[2], sc[3] - m_ref[3]};
-        if (t0 + 32 > T && t0 + t >= T)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s4[i] = -INFINITY;
-        const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-        if (fresh || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
-          // exact per-head maximum over the super-tile, then raise the reference (or set it, first time)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float c = s4[i];
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) c = fmaxf(c, __shfl_xor(c, o));
-            const float d = fresh ? c : fmaxf(c, 0.0f);
-            const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-d);
-#pragma unroll
-            for (int w = 0; w < VT; ++w) acc[w][i] *= alpha;
-            psum[i] *= alpha;
-            s4[i] -= d;
-            m_ref[i] += d;
-          }
-          fresh = false;
-        }
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s4[i]);  // 2^-inf = 0
-          psum[i] += p[i];
-        }
-        // P^T through LDS: token t's four probabilities, then the transposing read.  Lane group G (lanes
-        // 16G..16G+15, half G / 2) reads the rows of tokens 16w + 8u + 4(G / 2) + (l % 16) / 4; lane i of the group
-        // receives head i % 4 of those 4 tokens (k-slots 8hf + 4u + 0..3)
-        if (hf == 0) {
-          const h4 pv4 = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-          *(h4*)(pbuf + 4 * t) = pv4;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        h8 pop[2];
-#pragma unroll
-        for (int w = 0; w < 2; ++w)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int tok = 16 * w + 8 * u + 4 * hf + (lane & 15) / 4;
-            const h4 x = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                    (__attribute__((address_space(3))) i16x4*)(pbuf + 4 * tok)));
-            pop[w][4 * u + 0] = x[0];
-            pop[w][4 * u + 1] = x[1];
-            pop[w][4 * u + 2] = x[2];
-            pop[w][4 * u + 3] = x[3];
-          }
-        // acc[head, coordinate] += sum_t p[head, t] v[t, coordinate]; rows replicate the 4 heads
-#pragma unroll
-        for (int w = 0; w < VT; ++w) {
-          const f16v o = mfma32(pop[1], vop[w][1], mfma32(pop[0], vop[w][0], f16v{}));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[w][i] += o[i];
-        }
+        for (int hq = 0; hq < GQ; ++hq)
+          qbuf[(v * GQ + hq) * QROW + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
       }
     }
-    settle(0);  // the next page landed (and everyone is done with this buffer)
+    // decode order of the wave's slots (variable rank): lane l holds slot pb + l, of class c (0 past the end)
+    if constexpr (VAR) {
+      int c = 0;
+      if (lane < nvb) {
+        const int r = (int)((so[pb + lane + 1] - so[pb + lane]) & 0xFFFFu);
+        c = min(KS, max(1, (r + 15) >> 4));
+      }
+      int base = 0, pos = 0;
+#pragma unroll
+      for (int cl = 1; cl <= KS; ++cl) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(c == cl);
+        if (c == cl) pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        base += (int)__builtin_popcountll(m);
+      }
+      if (c > 0) sorder[pos] = (uint8_t)lane;
+    }
+    wave_sync();  // query variants and the order visible to the whole wave
+    const uint32_t* qrow = qbuf + (((t >> 3) & 1) * GQ + (t & 3)) * QROW + 4 * hf;  // score A operand row t
+    const int nst_w = (nvb + 31) / 32;
+
+    // the LDS words of super-tile k of this wave (decode position 32 k + t of its block), one super-tile ahead
+    auto fetch = [&](int k) -> Words {
+      const int idx = 32 * k + t;
+      Words w;
+      w.ok = idx < nvb;
+      int co_k, po_k;
+      if constexpr (VAR) {
+        w.slot = pb + (w.ok ? (int)sorder[idx] : 0);
+        const uint32_t o0 = so[w.slot], o1 = so[w.slot + 1];
+        w.r = w.rv = w.ok ? (int)((o1 - o0) & 0xFFFFu) : 0;
+        co_k = w.co_v = (int)((o0 & 0xFFFFu) * KB / 8);
+        po_k = w.po_v = (int)(o0 >> 16) * 4;
+        // steps of the super-tile: the class of its last token (the order puts classes in increasing order)
+        const int cls = min(KS, max(1, (w.r + 15) >> 4));
+        w.ns = __builtin_amdgcn_readlane(cls, min(31, nvb - 1 - 32 * k));
+      } else {
+        w.slot = pb + idx;
+        w.r = w.ok ? a.rk : 0;
+        w.rv = w.ok ? a.rv : 0;
+        co_k = w.slot * kcb;
+        w.co_v = w.slot * vcb;
+        po_k = w.slot * kmb;
+        w.po_v = w.slot * vmb;
+        w.ns = KS;
+      }
+      // every step's words are read (a step past the token's rank reads bytes of the same head block, and its
+      // scale and zero are zeroed); the super-tile uses the first ns of them
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        w.k[s] = codes8_as_nibbles<KB>(kcs, co_k + KB * hf + 2 * KB * s);
+        w.pk[s] = pair_if(16 * s + 8 * hf < w.r, lds_u32(kms, po_k + 4 * ((16 * s + 8 * hf) / a.G)));
+      }
+      return w;
+    };
+
+    // One super-tile with NS key steps (NSV value steps, NT value tiles), straight-line code for each NS.
+    auto tile = [&](auto nsc, const Words& cur, int k) {
+      constexpr int NS = decltype(nsc)::value;
+      constexpr int NSV = VAR ? NS : VS;  // variable rank: one rank for K and V
+      constexpr int NT = (NSV + 1) / 2;
+      uint32_t vw[NSV], vp[NSV];
+#pragma unroll
+      for (int s = 0; s < NSV; ++s) {
+        vw[s] = codes8_as_nibbles<VB>(vcs, cur.co_v + VB * hf + 2 * VB * s);
+        vp[s] = pair_if(16 * s + 8 * hf < cur.rv, lds_u32(vms, cur.po_v + 4 * ((16 * s + 8 * hf) / a.G)));
+      }
+
+      // ---- keys: dequantize the steps, then per half m the tiles m and m + 2 (head dims d and d + 64), RoPE R(u)
+      // of the token's in-block position u, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots
+      // 8hf + 2p, 8hf + 2p + 1)
+      h8 kb[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kb[s] = dequant_int4x8(cur.k[s], cur.pk[s]);
+      const uint32_t* rrow = rtab + (cur.slot & 31) * QROW + 4 * hf;
+      f16v sc = {};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f16v ka = {}, kz = {};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          ka = mfma32(bf[s][m], kb[s], ka);
+          kz = mfma32(bf[s][m + 2], kb[s], kz);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u4 rf = *(const u4*)(rrow + 32 * m + 8 * q);
+          h8 kq;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const h2 rr = as_h2(rope_pair(pack_h2(ka[4 * q + p], kz[4 * q + p]), rf[p]));
+            kq[2 * p] = rr.x;
+            kq[2 * p + 1] = rr.y;
+          }
+          const h8 qf = *(const h8*)(qrow + 32 * m + 8 * q);
+          sc = mfma32(qf, kq, sc);
+        }
+      }
+
+      // ---- values: dequantize, transpose into (coordinate, token) tiles through one-hot MFMAs
+      h8 vop[NT][2];
+      {
+        f16v vt[NT];
+#pragma unroll
+        for (int w = 0; w < NT; ++w) vt[w] = f16v{};
+#pragma unroll
+        for (int s = 0; s < NSV; ++s) vt[s / 2] = mfma32(dequant_int4x8(vw[s], vp[s]), ohv[s & 1], vt[s / 2]);
+#pragma unroll
+        for (int w = 0; w < NT; ++w) {
+          vop[w][0] = cvt_h8(vt[w], 0);
+          vop[w][1] = cvt_h8(vt[w], 8);
+        }
+      }
+
+      // ---- the token's four scores: entries 0-3 hold variant 0, entries 4-7 variant 1 (rows 8i + 4hf + head)
+      float s4[4];
+      {
+        const bool v1 = (cur.slot & 32) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = (v1 ? dpp_id(sc[4 + i]) : sc[i]) - m_ref[i];
+      }
+      if (32 * (k + 1) > nvb && !cur.ok)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = -INFINITY;
+      const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      if (fresh || __builtin_amdgcn_ballot_w64(mx > TAU) != 0) {
+        // exact per-head maximum over the super-tile, then raise the reference (or set it, first time)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float c = s4[i];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) c = fmaxf(c, __shfl_xor(c, o));
+          const float d = fresh ? c : fmaxf(c, 0.0f);
+          const float alpha = fresh ? 1.0f : __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+          for (int w = 0; w < VT; ++w) acc[w][i] *= alpha;
+          psum[i] *= alpha;
+          s4[i] -= d;
+          m_ref[i] += d;
+        }
+        fresh = false;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s4[i]);  // 2^-inf = 0
+        psum[i] += p[i];
+      }
+      // P^T through LDS: token t's four probabilities, then the transposing read.  Lane group G (lanes
+      // 16G..16G+15, half G / 2) reads the rows of tokens 16w + 8u + 4(G / 2) + (l % 16) / 4; lane i of the group
+      // receives head i % 4 of those 4 tokens (k-slots 8hf + 4u + 0..3)
+      if (hf == 0) {
+        const h4 pv4 = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        *(h4*)(pbuf + 4 * t) = pv4;
+      }
+      wave_sync();
+      h8 pop[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int tok = 16 * w + 8 * u + 4 * hf + (lane & 15) / 4;
+          const h4 x = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                  (__attribute__((address_space(3))) i16x4*)(pbuf + 4 * tok)));
+          pop[w][4 * u + 0] = x[0];
+          pop[w][4 * u + 1] = x[1];
+          pop[w][4 * u + 2] = x[2];
+          pop[w][4 * u + 3] = x[3];
+        }
+      // acc[head, coordinate] += sum_t p[head, t] v[t, coordinate]; rows replicate the 4 heads.  Tiles past the
+      // super-tile's steps would add only zeros and are skipped.
+#pragma unroll
+      for (int w = 0; w < NT; ++w) {
+        const f16v o = mfma32(pop[1], vop[w][1], mfma32(pop[0], vop[w][0], f16v{}));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[w][i] += o[i];
+      }
+    };
+
+    auto run = [&](const Words& cur, int k) {
+      if constexpr (VAR) {
+        switch (cur.ns) {  // wave-uniform
+          case 1: tile(Steps<1>{}, cur, k); break;
+          case 2: tile(Steps<2 <= KS ? 2 : KS>{}, cur, k); break;
+          case 3: tile(Steps<3 <= KS ? 3 : KS>{}, cur, k); break;
+          default: tile(Steps<KS>{}, cur, k); break;
+        }
+      } else {
+        tile(Steps<KS>{}, cur, k);
+      }
+    };
+    // the wave's (at most) two super-tiles, the second's words read before the first is decoded
+    if (nst_w > 0) {
+      const Words w0 = fetch(0);
+      Words w1 = {};
+      if (nst_w > 1) w1 = fetch(1);
+      run(w0, 0);
+      if (nst_w > 1) run(w1, 1);
+    }
+    settle();  // the next page landed (and everyone is done with this buffer)
   }
 
   // ---- partial of the workgroup: the four waves' (m, l, acc) combined in LDS (the staging buffers are

@@ -80,26 +80,27 @@ __host__ __device__ inline int64_t uniform_page_bytes(const kvc_layout& L) {
   return S.hb * L.n_kv_heads;
 }
 
-// Eight b-bit codes (b = 2, 3, 4) starting at a byte address of LDS or global memory (any alignment), as the
+// Eight b-bit codes (b = 2, 3, 4) starting at byte off of a 4-byte-aligned buffer in LDS or global memory, as the
 // INT4 dword layout (code k in the low b bits of nibble k) that dequant_int4x8 takes.  The codes of a slot form a
 // little-endian bit string, code i at bits b*i.., so the 8 codes of group w start at byte b*w.  Reads up to 7
-// bytes past the group, which the 16-byte padding of every section keeps inside the block.
+// bytes past the group, which the 16-byte padding of every section keeps inside the block.  The address is kept
+// as base + offset (never rebuilt from an integer): that keeps the read an LDS read the compiler can tell apart
+// from the copies in flight into other LDS buffers.
 template <int B>
-__device__ inline uint32_t codes8_as_nibbles(const uint8_t* p) {
+__device__ inline uint32_t codes8_as_nibbles(const uint8_t* base, int off) {
   if constexpr (B == 4) {
-    return *(const uint32_t*)p;
+    return *(const uint32_t*)(base + off);
   } else if constexpr (B == 2) {
-    uint32_t y = *(const uint16_t*)p;  // 2-byte aligned: slot offsets are multiples of r / 4 bytes, r % 8 == 0
+    uint32_t y = *(const uint16_t*)(base + off);  // 2-byte aligned: slot offsets are multiples of r / 4 bytes, r % 8 == 0
     y = (y | (y << 8)) & 0x00FF00FFu;
     y = (y | (y << 4)) & 0x0F0F0F0Fu;
     y = (y | (y << 2)) & 0x33333333u;
     return y;
   } else {
-    const uintptr_t ad = (uintptr_t)p;
-    const uint32_t* w = (const uint32_t*)(ad & ~(uintptr_t)3);
-    const uint32_t sh = 8u * (uint32_t)(ad & 3u);
-    const uint64_t both = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-    const uint32_t x = (uint32_t)(both >> sh) & 0xFFFFFFu;   // codes 0..7 at bits 3k
+    // the two aligned words around the group, and v_alignbyte for the 3 bytes from byte off (a 64-bit shift
+    // costs more instructions; and as read here, the compiler does not make the reads wait for copies in flight)
+    const uint32_t* w = (const uint32_t*)(base + (off & ~3));
+    const uint32_t x = __builtin_amdgcn_alignbyte(w[1], w[0], (uint32_t)(off & 3)) & 0xFFFFFFu;  // codes 0..7 at bits 3k
     uint32_t y = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);      // codes 0-3 at bits 0.., codes 4-7 at bits 16..
     y = (y & 0x003F003Fu) | ((y & 0x0FC00FC0u) << 2);        // code pairs at bytes 0..3
     y = (y & 0x07070707u) | ((y & 0x38383838u) << 1);        // code k at bits 4k

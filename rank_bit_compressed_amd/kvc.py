@@ -138,8 +138,45 @@ def lib():
 def _ptr(t):
     if t is None:
         return None
-    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError("device tensors must be contiguous CUDA/HIP tensors")
     return C.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None):
+    """Raise ValueError unless tensor t has this dtype (and shape, where given)."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out):
+    """Dtypes and shapes of a decode call's tensors against the layout, before the C ABI sees raw pointers
+    (an int64 block table or a q of the wrong rank would otherwise be read as something else)."""
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    B = block_table.shape[0]
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (B,))
+    Hq, Hkv, d = layout.n_q_heads, layout.n_kv_heads, layout.head_dim
+    if layout.shared:
+        qs = (layout.n_layers, B, Hq, d)
+        ws = (layout.n_layers, layout.r_k_cap, Hkv * d)
+        for name, w in (("wk", wk), ("wv", wv)):
+            _need(w, name, torch.bfloat16)
+            if tuple(w.shape) != ws and tuple(w.shape) != (B, *ws):
+                raise ValueError(f"{name} must have shape {ws} or {(B, *ws)}, got {tuple(w.shape)}")
+    else:
+        qs = (B, Hq, d)
+        _need(wk, "wk", torch.bfloat16, (Hkv, d, layout.r_k_cap))
+        _need(wv, "wv", torch.bfloat16, (Hkv, d, layout.r_v_cap))
+    if tuple(q.shape) != qs:
+        raise ValueError(f"q must have shape {qs}, got {tuple(q.shape)}")
+    if out is not None:
+        _need(out, "out", torch.float32, qs)
 
 
 def _stream():
@@ -263,6 +300,7 @@ def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk,
     [B, L, latent, Hkv * d] (contiguous), one pair per sequence; keep_mask: optional int32 [B, words] token
     keep mask (as kvc_evict_select writes it); kv_split: latent / 2 for a latent whose lower half holds only
     key coordinates and upper half only value coordinates (keys and values with their own token factors)."""
+    _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
     B = block_table.shape[0]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -290,6 +328,7 @@ class DecodePlan:
 
     def __init__(self, layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
                  num_splits=0, out=None, ws=None, keep_mask=None, kv_split=0):
+        _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
         B = block_table.shape[0]
         self.out = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
         need = decode_workspace_bytes(layout, B, max_T, num_splits)
@@ -474,7 +513,7 @@ def evict_select(scores, seq_len, keep_ratio, out=None):
     return out
 
 
-BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK = 1, 2, 4, 8, 16
+BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK, BAD_TOK_OFF, BAD_RECORD = 1, 2, 4, 8, 16, 32, 64
 
 
 def decode_check(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, q_pos=None) -> int:

@@ -232,3 +232,31 @@ def test_decode_check_rejections_without_launching():
     assert lib.kvc_decode_check(C.byref(L), C.byref(cache), C.byref(inp), None, None) == -1
     inp = kvc.DecodeIn(0, 1, 100, p(80), p(96), None, p(112), 1, p(128), p(144), 0, 0, None, 0, 0)
     assert lib.kvc_decode_check(C.byref(L), C.byref(cache), C.byref(inp), p(256), None) == -1
+
+
+def test_binding_checks_decode_tensors_before_the_abi():
+    # the binding rejects wrong dtypes and shapes before any raw pointer reaches the C ABI (an int64 block table
+    # would otherwise be read as int32 page ids); runs on CPU tensors, nothing is launched
+    import torch
+    w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=2, T=300)
+    inp = synth.make_inputs(w)
+    L = kvc.make_layout(**w.layout_kwargs())
+    args = dict(block_table=inp["block_table"], seq_len=inp["seq_len"], q=inp["q"], wk=inp["wk"], wv=inp["wv"],
+                q_pos=inp["q_pos"], out=None)
+    kvc._check_decode_args(L, **args)
+    for key, bad in (("block_table", inp["block_table"].long()), ("seq_len", inp["seq_len"].long()),
+                     ("q_pos", inp["q_pos"][:1]), ("q", inp["q"][None]), ("wk", inp["wk"].half()),
+                     ("wv", inp["wv"][:, :, :32]), ("out", torch.empty(inp["q"].shape, dtype=torch.bfloat16))):
+        with pytest.raises(ValueError):
+            kvc._check_decode_args(L, **dict(args, **{key: bad}))
+    ws = synth.WORKLOADS["shared_latent_32k"].scaled(B=2, T=300, n_layers=2)
+    si = synth.make_inputs(ws)
+    Ls = kvc.make_layout(**ws.layout_kwargs())
+    sargs = dict(block_table=si["block_table"], seq_len=si["seq_len"], q=si["q"], wk=si["wk"], wv=si["wv"],
+                 q_pos=si["q_pos"], out=None)
+    kvc._check_decode_args(Ls, **sargs)
+    kvc._check_decode_args(Ls, **dict(sargs, wk=si["wk"].expand(2, -1, -1, -1), wv=si["wv"].expand(2, -1, -1, -1)))
+    with pytest.raises(ValueError):                   # one layer's query under a two-layer layout
+        kvc._check_decode_args(Ls, **dict(sargs, q=si["q"][0]))
+    with pytest.raises(ValueError):
+        kvc._ptr(torch.zeros(4))                      # not a device tensor

@@ -42,8 +42,36 @@ def test_check_flags_each_corruption():
     cache.page_off[page] = keep
     slot = cache.tok_rank[page, 5].clone()
     cache.tok_rank[page, 5] = 7
-    assert ck() == kvc.BAD_RANK
+    assert ck() == kvc.BAD_RANK | kvc.BAD_TOK_OFF      # the offset row no longer sums this rank
     cache.tok_rank[page, 5] = slot
+    assert ck() == 0
+    # offset rows: one interior word, the totals word, and an unused slot's rank above the cap
+    P = w.page_size
+    for col, delta in ((17, 1), (P, 1 << 16), (0, 8)):
+        keep_off = cache.tok_off[page, col].clone()
+        cache.tok_off[page, col] += delta
+        print(f"[check] tok_off[{page}, {col}] += {delta}", flush=True)
+        assert ck() == kvc.BAD_TOK_OFF
+        cache.tok_off[page, col] = keep_off
+    # an unused slot (sequence 1 holds 351 tokens: 95 slots of its third page) with a rank above the cap and an
+    # offset row rebuilt to match it: only the cap is wrong
+    last = int(d["block_table"][1, 2])
+    keep_r, keep_row = cache.tok_rank[last].clone(), cache.tok_off[last].clone()
+    cache.tok_rank[last, 120] = 72
+    r = cache.tok_rank[last].to(torch.int64)
+    g = (r + w.group - 1) // w.group
+    pre = torch.cat([torch.zeros(1, dtype=torch.int64, device=r.device), torch.cumsum(r, 0)])
+    pre_g = torch.cat([torch.zeros(1, dtype=torch.int64, device=r.device), torch.cumsum(g, 0)])
+    cache.tok_off[last] = (pre | (pre_g << 16)).to(cache.tok_off.dtype)
+    f = ck()
+    assert f & kvc.BAD_TOK_OFF and f & ~(kvc.BAD_TOK_OFF | kvc.BAD_RECORD) == 0
+    cache.tok_rank[last], cache.tok_off[last] = keep_r, keep_row
+    assert ck() == 0
+    # a record that starts inside the pool but runs past its end
+    keep = cache.page_off[page].clone()
+    cache.page_off[page] = cache.pool.numel() - 16
+    assert ck() == kvc.BAD_RECORD
+    cache.page_off[page] = keep
     sl = d["seq_len"].clone(); sl[0] = 0
     assert ck(bt=bt, sl=sl, qp=qp) == kvc.BAD_PAGE | kvc.BAD_SEQ_LEN | kvc.BAD_Q_POS
     assert ck() == 0
@@ -57,3 +85,8 @@ def test_check_uniform_and_shared_layouts():
         bt = d["block_table"].clone()
         bt[0, 0] = w.n_pages + 3
         assert kvc.decode_check(L, cache, bt, d["seq_len"], w.T, d["q_pos"]) == kvc.BAD_PAGE
+        page = int(d["block_table"][0, 1])
+        keep = cache.page_off[page].clone()
+        cache.page_off[page] = cache.pool.numel() - 1
+        assert kvc.decode_check(L, cache, d["block_table"], d["seq_len"], w.T, d["q_pos"]) == kvc.BAD_RECORD
+        cache.page_off[page] = keep
