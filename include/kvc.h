@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 5
+#define KVC_ABI_VERSION 6
 
 typedef enum {
   KVC_OK = 0,
@@ -77,7 +77,9 @@ typedef enum {
   KVC_ERR_UNSUPPORTED = -2,     /* valid, but no kernel for this geometry                 */
   KVC_ERR_WORKSPACE = -3,       /* workspace or pool smaller than required                */
   KVC_ERR_MISALIGNED = -4,      /* a pointer is not 16-byte aligned                       */
-  KVC_ERR_HIP = -5              /* a HIP runtime call failed (see kvc_last_hip_error)     */
+  KVC_ERR_HIP = -5,             /* a HIP runtime call failed (see kvc_last_hip_error)     */
+  KVC_ERR_SCRATCH = -6          /* kvc_decode_attn_noalloc: the step needs more scratch than
+                                   KVC_NOALLOC_SCRATCH_BYTES (ABI version 6)              */
 } kvc_status;
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
@@ -237,6 +239,22 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
 kvc_status kvc_decode_attn_timed(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
                                  float* out, void* ws, size_t ws_bytes, void* stream, void* ev_begin,
                                  void* ev_end);
+
+/* Bytes of the device array that holds kvc_decode_attn_noalloc's split partials (8 MiB; the largest
+ * workload here, 8 sequences of 131072 tokens with the rotated residual, needs 3 MiB). */
+#define KVC_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* kvc_decode_attn for callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid device allocation.  The same kernels and results as kvc_decode_attn with the same
+ * num_splits, but the split partials go to a file-scope device array of KVC_NOALLOC_SCRATCH_BYTES per GPU,
+ * which the library holds until the process ends; nothing is allocated or freed (the array's device address is
+ * looked up once per GPU, on that GPU's first call, with hipGetSymbolAddress).  The caller still passes the
+ * inputs and out.  Returns KVC_ERR_SCRATCH, before any device call, when kvc_decode_workspace_bytes for these
+ * sizes exceeds KVC_NOALLOC_SCRATCH_BYTES; otherwise the statuses of kvc_decode_attn.  All calls on one GPU
+ * share its array: calls that overlap on one GPU (other streams, other threads) race and give wrong results.
+ * Each call writes every partial it reads, so the array needs no clearing between calls. */
+kvc_status kvc_decode_attn_noalloc(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
+                                   float* out, void* stream);
 
 /* Which decode kernel kvc_decode_attn runs for a layout: KVC_PATH_INT4 (per-head INT4 latents,
  * head_dim 128, no residual: the fast kernel), KVC_PATH_RES (per-head INT4 latents with the 2-bit

@@ -119,6 +119,7 @@ const char* kvc_status_string(int32_t s) {
     case KVC_ERR_WORKSPACE: return "workspace or pool too small";
     case KVC_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case KVC_ERR_HIP: return "HIP runtime error";
+    case KVC_ERR_SCRATCH: return "decode needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

@@ -20,13 +20,13 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "kvc.h")
 KVC_F32, KVC_BF16 = 0, 1
 KVC_FROM_LATENT, KVC_FROM_DENSE = 0, 1
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported geometry", -3: "workspace or pool too small",
-          -4: "pointer not 16-byte aligned", -5: "HIP runtime error"}
+          -4: "pointer not 16-byte aligned", -5: "HIP runtime error", -6: "decode needs more scratch than the no-allocation entry point holds"}
 EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_layout_check", "kvc_pool_bytes_max",
            "kvc_compress", "kvc_decode_workspace_bytes", "kvc_decode_attn", "kvc_dense_workspace_bytes",
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
            "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
-           "kvc_evict_select", "kvc_decode_check"]
+           "kvc_evict_select", "kvc_decode_check", "kvc_decode_attn_noalloc"]
 
 
 class KvcError(RuntimeError):
@@ -131,6 +131,7 @@ def lib():
         L.kvc_tucker_expand.argtypes = [P, P, P, P]; L.kvc_tucker_expand.restype = C.c_int32
         L.kvc_evict_select.argtypes = [P, P, P]; L.kvc_evict_select.restype = C.c_int32
         L.kvc_decode_check.argtypes = [P, P, P, P, P]; L.kvc_decode_check.restype = C.c_int32
+        L.kvc_decode_attn_noalloc.argtypes = [P, P, P, P, P]; L.kvc_decode_attn_noalloc.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -317,6 +318,25 @@ def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk,
         eb, ee = (_event_handle(e) for e in events)
         _check(lib().kvc_decode_attn_timed(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws),
                                            ws.numel(), _stream(), eb, ee), "kvc_decode_attn_timed")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # KVC_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attn_noalloc(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
+                        num_splits=0, out=None, keep_mask=None, kv_split=0):
+    """kvc_decode_attn_noalloc -> fp32 [(L,) B, Hq, d]: the decode step with its split partials in the library's
+    device array (no workspace argument; the library allocates nothing).  Calls overlapping on one GPU race."""
+    _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
+    B = block_table.shape[0]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
+                    keep_mask, kv_split)
+    c = cache.c()
+    _check(lib().kvc_decode_attn_noalloc(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _stream()),
+           "kvc_decode_attn_noalloc")
     return out
 
 

@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 5
+    assert kvc.lib().kvc_abi_version() == 6
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -260,3 +260,17 @@ def test_binding_checks_decode_tensors_before_the_abi():
         kvc._check_decode_args(Ls, **dict(sargs, q=si["q"][0]))
     with pytest.raises(ValueError):
         kvc._ptr(torch.zeros(4))                      # not a device tensor
+
+
+def test_noalloc_rejects_sizes_beyond_its_array_before_any_device_call():
+    # 64 sequences of 131072 tokens with the residual need more split partials than the no-allocation entry point's
+    # array holds: the call returns KVC_ERR_SCRATCH from host code, reading no pointer (all null here)
+    w = synth.WORKLOADS["residual_128k"]
+    L = kvc.make_layout(**w.layout_kwargs())
+    assert kvc.decode_workspace_bytes(L, 64, 131072) > kvc.NOALLOC_SCRATCH_BYTES
+    assert kvc.decode_workspace_bytes(L, w.B, w.T) <= kvc.NOALLOC_SCRATCH_BYTES
+    inp = kvc.DecodeIn(64, 512, 131072, None, None, None, None, kvc.KVC_BF16, None, None, 0, 0, None, 0, 0)
+    cache = kvc.Cache(None, 0, None, None, None, None, 1)
+    assert kvc.lib().kvc_decode_attn_noalloc(C.byref(L), C.byref(cache), C.byref(inp), None, None) == -6
+    assert kvc.lib().kvc_status_string(-6).startswith(b"decode needs more scratch")
+    assert kvc.lib().kvc_decode_attn_noalloc(C.byref(L), C.byref(cache), None, None, None) == -1
