@@ -118,7 +118,7 @@ def decode_flops(w, ranks=None) -> int:
     return n_tok * (2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.r_v * w.n_q_heads) + score
 
 
-def other_workloads(steps: int, warmup: int) -> dict:
+def other_workloads(steps: int, warmup: int, peaks: dict) -> dict:
     """Each other workload at its full size: median kernel time (library events around the attention
     kernel), wall time per call, and the figure of its own bound."""
     import torch
@@ -194,9 +194,11 @@ def other_workloads(steps: int, warmup: int) -> dict:
         elif w.shared:
             r["bound"] = "mfma"
             r["frac_of_f16_mfma_peak"] = round(r["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)
+            r["frac_of_measured_mfma"] = round(r["tflops"] / peaks["mfma_f16_tflops"], 4)
         else:
             r["bound"] = "hbm"
             r["frac_of_hbm_peak"] = round(r["hbm_gbs"] / HBM_PEAK_GBS, 4)
+            r["frac_of_measured_hbm"] = round(r["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
         res[name] = r
         del plan, cache, inp
         torch.cuda.empty_cache()
@@ -286,6 +288,52 @@ def alloc_workload(steps: int) -> dict:
             "ladder": ALLOC_LADDER, "mean_rank_target": ALLOC_MEAN, "mean_rank_allocated": round(mean_rank, 3)}
 
 
+def measured_peaks(torch, dev) -> dict:
+    """Measured peaks beside the published ones: the HBM read rate of a plain 16-byte-per-lane stream over 4 GiB
+    (kvc_probe_stream_read) and the rate of the fp16 32x32x16 matrix instruction on register operands
+    (kvc_probe_mfma_f16); median of 5 timed runs each, after 2 untimed."""
+    from rank_bit_compressed_amd import kvc
+
+    def timed(fn, n=5):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    grid = 32768
+    sink = torch.empty(grid, dtype=torch.int32, device=dev)
+    ms = timed(lambda: kvc.probe_stream_read(buf, grid, sink))
+    del buf
+    iters, mgrid = 4000, 256 * 8
+    fsink = torch.empty(mgrid, dtype=torch.float32, device=dev)
+    mms = timed(lambda: kvc.probe_mfma_f16(iters, mgrid, fsink))
+    clk = clock_mhz(torch, dev)  # right behind the last matrix-instruction run
+    flops = mgrid * 4 * iters * 8 * 2 * 32 * 32 * 16
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_read_bytes": nbytes,
+            "mfma_f16_tflops": round(flops / (mms * 1e-3) / 1e12, 1), "clock_mhz_after_mfma": clk,
+            "kernels": "kvc_probe_stream_read (16-byte nontemporal loads, 8 in flight, 32768 x 256 lanes over 4 GiB), "
+                       "kvc_probe_mfma_f16 "
+                       "(8 independent v_mfma_f32_32x32x16_f16 chains per wave, 8192 waves)"}
+
+
+def clock_mhz(torch, dev) -> float:
+    """Shader clock now (kvc_probe_clock: s_memtime cycles over 100 MHz s_memrealtime ticks)."""
+    from rank_bit_compressed_amd import kvc
+    out = torch.zeros(3, dtype=torch.int64, device=dev)
+    kvc.probe_clock(out)
+    c, r, _ = out.tolist()
+    return round(c / max(r, 1) * 100.0, 1)
+
+
 def step_percentiles(torch, plan, dev, n=100) -> dict:
     """p10 / median / p90 in ms over n steps, warm (one cache, back to back, so its 126 MB can stay in the 256 MB
     last-level cache) and cold (1 GiB written before each step, outside the events).  "kernel": the attention
@@ -311,16 +359,19 @@ def step_percentiles(torch, plan, dev, n=100) -> dict:
     for i in range(n):
         plan(kev[i])
     blk[1].record()
+    clk_warm = clock_mhz(torch, dev)  # enqueued right behind the warm block
     torch.cuda.synchronize()
     res = {"n": n, "warm": {"kernel": pct([a.elapsed_time(b) for a, b in kev]),
-                            "step_mean": round(blk[0].elapsed_time(blk[1]) / n, 5)}}
+                            "step_mean": round(blk[0].elapsed_time(blk[1]) / n, 5), "clock_mhz_after": clk_warm}}
     for i in range(n):
         flush.fill_(float(i))
         sev[i][0].record()
         plan(kev[i])
         sev[i][1].record()
+    clk_cold = clock_mhz(torch, dev)
     torch.cuda.synchronize()
-    res["cold"] = {"kernel": pct([a.elapsed_time(b) for a, b in kev]), "step": pct([a.elapsed_time(b) for a, b in sev])}
+    res["cold"] = {"kernel": pct([a.elapsed_time(b) for a, b in kev]), "step": pct([a.elapsed_time(b) for a, b in sev]),
+                   "clock_mhz_after": clk_cold}
     del flush
     return res
 
@@ -401,7 +452,9 @@ def main():
     acct = accounting.compressed_stream_bytes(w, inp["ranks"], [w.T] * w.B)
     alg_bytes = acct["stream"] + acct["tables"]
     achieved = alg_bytes / (kernel_avg * 1e-3) / 1e9
+    clk_timed = clock_mhz(torch, dev)  # right after the timed steps
     step_ms = step_percentiles(torch, plans[0], dev)
+    peaks = measured_peaks(torch, dev)
 
     dense = None
     if not args.no_dense:
@@ -427,6 +480,8 @@ def main():
         d_ms = (time.perf_counter() - t0) * 1e3 / nd
         d_bytes = w.B * w.T * accounting.dense_bytes_per_token(w.n_kv_heads, w.head_dim)
         dense = {"ms_per_step": round(d_ms, 5), "hbm_gbs": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "frac_of_measured_hbm": round(d_bytes / (d_ms * 1e-3) / 1e9 / peaks["hbm_read_gbs"], 4),
                  "bytes": d_bytes, "speedup_compressed_vs_dense": round(d_ms / ms_per_step, 3)}
         del dd
 
@@ -450,14 +505,18 @@ def main():
                    "block_table": "shuffled", "rope_theta": w.rope_theta},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(KERNEL),
-                     "kernel": KERNEL, "kernel_ms_avg": round(kernel_avg, 5)},
+                     "kernel": KERNEL, "kernel_ms_avg": round(kernel_avg, 5),
+                     "peak_measured": peaks["hbm_read_gbs"],
+                     "frac_of_measured": round(achieved / peaks["hbm_read_gbs"], 4),
+                     "clock_mhz_after_timed_steps": clk_timed},
+        "measured_peaks": peaks,
         "context_tokens_per_s": round(w.B * w.T / (ms_per_step * 1e-3), 1),
         "step_ms": step_ms,
         "compressed_bytes_per_step": alg_bytes,
         "dense": dense,
     }
     if not args.no_other:
-        line["other_workloads"] = other_workloads(args.steps, args.warmup)
+        line["other_workloads"] = other_workloads(args.steps, args.warmup, peaks)
         line["other_workloads"]["basis_fit_prefill_32k"] = fit_workload(args.steps)
         line["other_workloads"]["rank_alloc_prefill_32k"] = alloc_workload(args.steps)
     if not args.no_cpu_baseline:

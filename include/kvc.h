@@ -453,6 +453,23 @@ kvc_status kvc_dense_workspace_bytes(const kvc_dense_in* in, size_t* bytes);
  * out: fp32 [B][Hq][d]. */
 kvc_status kvc_dense_decode_attn(const kvc_dense_in* in, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Measurement probes (not on the decode path): measured peaks to set beside the published ones. ---- */
+
+/* Reads `bytes` (a multiple of 16) of device memory at src once, 16 bytes per lane with nontemporal loads, eight in
+ * flight per lane, over `grid` workgroups of 256 lanes; sink: [grid] uint32 (the xor of what each workgroup read).
+ * Time it with events on `stream`: bytes / time is the HBM read rate a plain stream reaches (use a buffer well
+ * beyond the 256 MB last-level cache).  Asynchronous; INVALID_ARG for bad sizes or a pointer not 16-byte aligned. */
+kvc_status kvc_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
+
+/* `grid` workgroups of 4 waves, each wave running `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16 on
+ * register operands (2 * 32 * 32 * 16 flops each); sink: [grid] floats, normally left unwritten.  Time it with
+ * events: the flops over the time is the rate the fp16 matrix instruction of the decode kernels reaches. */
+kvc_status kvc_probe_mfma_f16(int32_t iters, int32_t grid, float* sink, void* stream);
+
+/* One wave spins `spins` iterations and writes out[0] = shader clock cycles (s_memtime) and out[1] = ticks of the
+ * 100 MHz reference (s_memrealtime) over the spin: out[0] / out[1] * 100 is the shader clock in MHz at that time. */
+kvc_status kvc_probe_clock(int32_t spins, uint64_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

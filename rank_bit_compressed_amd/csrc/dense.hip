@@ -2,11 +2,13 @@
 //
 // Same decomposition as the compressed kernel: one workgroup (4 waves) per (sequence, kv head,
 // context split), 32-token super-tiles, per-wave online softmax, the four waves combined in LDS at the
-// end, and a merge kernel over the splits.  Per 16-token block, lane (token l%16, group g) loads its
-// token's key dims (d/4)g .. (d/4)(g+1)-1 with 16-byte loads, one super-tile ahead of the one it computes
-// (the stream is the whole cost, so loads stay in flight during the arithmetic); scores S^T = K Q^T on
-// the bf16 MFMA (k-slot 8g + j of chunk c <-> dim (d/4)g + 8c + j); values go through a one-hot bf16 MFMA
-// (a register transpose, exact) and the value product runs on the fp16 MFMA with fp16 probabilities.
+// end, and a merge kernel over the splits.  Per 16-token block, lane (token l%16, group g) loads, for each
+// 32-dim chunk c, its token's dims 32c + 8g .. 32c + 8g + 7 with a 16-byte nontemporal load, so that the four
+// lanes of a token read one contiguous 64-byte run per instruction; the loads run one super-tile ahead of
+// the one computed (the stream is the whole cost, so loads stay in flight during the arithmetic).  Scores
+// S^T = K Q^T on the bf16 MFMA (k-slot 8g + j of chunk c <-> dim 32c + 8g + j); values go through a one-hot
+// bf16 MFMA (a register transpose, exact) and the value product runs on the fp16 MFMA with fp16
+// probabilities; value tile nt holds dims 16 nt .. 16 nt + 15.
 #include <math.h>
 
 #include <algorithm>
@@ -32,10 +34,9 @@ static constexpr int DGQ = 4;
 __device__ inline f4 mfma_bf16(bf8 a, bf8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
 template <int D>
-__global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
+__global__ __launch_bounds__(256, 2) void dense_kernel(DenseArgs a) {
   constexpr int QC = D / 32;  // chunks of the score product
   constexpr int NT = D / 16;  // N-tiles of the value product
-  constexpr int DL = D / 4;   // head dims per lane group: lane group g holds dims DL*g .. DL*g + DL - 1
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int n = lane & 15, g = lane >> 4;
@@ -45,18 +46,28 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
   const int T = a.seq_len[b];
   const int P = a.P;
 
-  // Q^T as the B operand: column hq = n (rows >= DGQ zero), k-slot 8g + j of chunk c <-> dim DL*g + 8c + j
+  // Q^T as the B operand: column hq = n (rows >= DGQ zero), k-slot 8g + j of chunk c <-> dim 32c + 8g + j
+  // (eight consecutive dims per lane and chunk: one 16-byte load of a bf16 query, two of an fp32 one)
   bf8 qop[QC];
-  for (int c = 0; c < QC; ++c)
-    for (int j = 0; j < 8; ++j) {
-      const int dim = DL * g + 8 * c + j;
-      float x = 0.0f;
-      if (n < DGQ) {
-        const size_t idx = ((size_t)b * a.Hq + h * DGQ + n) * D + dim;
-        x = a.q_bf16 ? __builtin_bit_cast(float, (uint32_t)((const uint16_t*)a.q)[idx] << 16) : ((const float*)a.q)[idx];
+  {
+    const size_t qrow = ((size_t)b * a.Hq + h * DGQ + min(n, DGQ - 1)) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      bf8 x;
+      if (a.q_bf16) {
+        x = *(const bf8*)((const uint16_t*)a.q + qrow + 32 * c);
+      } else {
+        const f4 lo = *(const f4*)((const float*)a.q + qrow + 32 * c);
+        const f4 hi = *(const f4*)((const float*)a.q + qrow + 32 * c + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = (__bf16)lo[j];
+          x[4 + j] = (__bf16)hi[j];
+        }
       }
-      qop[c][j] = (__bf16)x;
+      qop[c] = n < DGQ ? x : bf8{};
     }
+  }
   bf8 oh[2];
   for (int e = 0; e < 2; ++e)
     for (int j = 0; j < 8; ++j) oh[e][j] = (__bf16)((8 * g + j == 16 * e + n) ? 1.0f : 0.0f);
@@ -74,31 +85,23 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
   auto load = [&](int st, bf8 (&kc)[2][QC], bf8 (&vc)[2][QC]) {
     const int t0 = st * 32;
     const int page = uniform(a.block_table[(size_t)b * a.max_blocks + t0 / P]);
-    const size_t head_base = ((size_t)page * a.Hkv + h) * P;
+    const size_t head_base = ((size_t)page * a.Hkv + h) * P + (t0 % P);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int tt = min(16 * blk + n, T - 1 - t0);
-      const size_t row = (head_base + (t0 % P) + tt) * D + DL * g;
+      const size_t row = (head_base + tt) * D + 8 * g;
+      const bf8* kr = (const bf8*)(a.k_pages + row);
+      const bf8* vr = (const bf8*)(a.v_pages + row);
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        kc[blk][c] = *(const bf8*)(a.k_pages + row + 8 * c);
-        vc[blk][c] = *(const bf8*)(a.v_pages + row + 8 * c);
+        kc[blk][c] = __builtin_nontemporal_load(kr + 4 * c);
+        vc[blk][c] = __builtin_nontemporal_load(vr + 4 * c);
       }
     }
   };
-  bf8 kn[2][QC], vn[2][QC];
-  if (st_begin + wv < st_end) load(st_begin + wv, kn, vn);
-  for (int st = st_begin + wv; st < st_end; st += 4) {
+  // one super-tile: scores, online softmax, value product
+  auto tile = [&](int st, const bf8 (&kcur)[2][QC], const bf8 (&vcur)[2][QC]) {
     const int t0 = st * 32;
-    bf8 kcur[2][QC], vcur[2][QC];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        kcur[blk][c] = kn[blk][c];
-        vcur[blk][c] = vn[blk][c];
-      }
-    if (st + 4 < st_end) load(st + 4, kn, vn);
     float sc[2][4];
     h4 vtb[NT][2];
 #pragma unroll
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
       f4 s4 = {0, 0, 0, 0};
       for (int c = 0; c < QC; ++c) s4 = mfma_bf16(kc[c], qop[c], s4);
       for (int i = 0; i < 4; ++i) sc[blk][i] = s4[i] * qscale;
-      // transpose: chunk c, half e -> column n holds dim DL(2e + n/8) + 8c + n%8 of tokens 4g..4g+3
+      // transpose: chunk c, half e -> column n holds dim 32c + 16e + n of tokens 4g..4g+3
       for (int c = 0; c < QC; ++c)
         for (int e = 0; e < 2; ++e) {
           const f4 tr = mfma_bf16(vc[c], oh[e], f4{0, 0, 0, 0});
@@ -148,6 +151,20 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
                      vtb[nt][1][0], vtb[nt][1][1], vtb[nt][1][2], vtb[nt][1][3]};
       acc[nt] = mfma16x16x32(pop, vt, acc[nt]);
     }
+  };
+  bf8 kn[2][QC], vn[2][QC];
+  if (st_begin + wv < st_end) load(st_begin + wv, kn, vn);
+  for (int st = st_begin + wv; st < st_end; st += 4) {
+    bf8 kcur[2][QC], vcur[2][QC];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        kcur[blk][c] = kn[blk][c];
+        vcur[blk][c] = vn[blk][c];
+      }
+    if (st + 4 < st_end) load(st + 4, kn, vn);
+    tile(st, kcur, vcur);
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -159,8 +176,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
     mine[DGQ + lane] = l_run;
   }
   for (int nt = 0; nt < NT; ++nt) {
-    const int c = nt >> 1, e = nt & 1;
-    const int dim = DL * (2 * e + (n >> 3)) + 8 * c + (n & 7);
+    const int dim = 16 * nt + n;
     for (int i = 0; i < 4; ++i) {
       const int hq = 4 * g + i;
       if (hq < DGQ) mine[2 * DGQ + hq * D + dim] = acc[nt][i];

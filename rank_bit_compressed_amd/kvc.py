@@ -26,7 +26,8 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_dense_decode_attn", "kvc_decode_path", "kvc_decode_attn_timed", "kvc_fit_workspace_bytes",
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
            "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
-           "kvc_evict_select", "kvc_decode_check", "kvc_decode_attn_noalloc"]
+           "kvc_evict_select", "kvc_decode_check", "kvc_decode_attn_noalloc", "kvc_probe_stream_read",
+           "kvc_probe_mfma_f16", "kvc_probe_clock"]
 
 
 class KvcError(RuntimeError):
@@ -132,6 +133,9 @@ def lib():
         L.kvc_evict_select.argtypes = [P, P, P]; L.kvc_evict_select.restype = C.c_int32
         L.kvc_decode_check.argtypes = [P, P, P, P, P]; L.kvc_decode_check.restype = C.c_int32
         L.kvc_decode_attn_noalloc.argtypes = [P, P, P, P, P]; L.kvc_decode_attn_noalloc.restype = C.c_int32
+        L.kvc_probe_stream_read.argtypes = [P, C.c_size_t, P, C.c_int32, P]; L.kvc_probe_stream_read.restype = C.c_int32
+        L.kvc_probe_mfma_f16.argtypes = [C.c_int32, C.c_int32, P, P]; L.kvc_probe_mfma_f16.restype = C.c_int32
+        L.kvc_probe_clock.argtypes = [C.c_int32, P, P]; L.kvc_probe_clock.restype = C.c_int32
         _lib = L
     return _lib
 
@@ -544,3 +548,18 @@ def decode_check(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T
     _check(lib().kvc_decode_check(C.byref(layout), C.byref(cache.c()), C.byref(inp), _ptr(flags), _stream()),
            "kvc_decode_check")
     return int(flags[0].item())
+
+
+def probe_stream_read(buf, grid: int, sink):
+    """kvc_probe_stream_read over the whole uint8 device tensor buf (enqueued on the current stream)."""
+    _check(lib().kvc_probe_stream_read(_ptr(buf), buf.numel(), _ptr(sink), grid, _stream()), "kvc_probe_stream_read")
+
+
+def probe_mfma_f16(iters: int, grid: int, sink):
+    """kvc_probe_mfma_f16: grid x 4 waves x iters x 8 matrix instructions of 32768 flops each."""
+    _check(lib().kvc_probe_mfma_f16(iters, grid, _ptr(sink), _stream()), "kvc_probe_mfma_f16")
+
+
+def probe_clock(out, spins: int = 200000):
+    """kvc_probe_clock into out (int64 [3] device tensor); shader MHz = out[0] / out[1] * 100 after a sync."""
+    _check(lib().kvc_probe_clock(spins, _ptr(out), _stream()), "kvc_probe_clock")
