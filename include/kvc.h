@@ -148,6 +148,13 @@ typedef struct {
   int32_t q_dtype;               /* kvc_dtype                                                   */
   const uint16_t* wk;            /* bf16 basis [Hkv][d][r_k_cap]; shared: W_k [L][latent][Hkv*d] */
   const uint16_t* wv;            /* bf16 basis [Hkv][d][r_v_cap]; shared: W_v [L][latent][Hkv*d] */
+                                 /*   The matrix instructions take wk and wv as fp16, converted   */
+                                 /*   exactly only for entries of magnitude 2^-14 .. 65504 (fp16's */
+                                 /*   normal range; the orthonormal bases and the 1/sqrt(512)-scale */
+                                 /*   W of the workloads here lie well inside it): larger entries */
+                                 /*   overflow to infinity, smaller ones lose bits (subnormals down */
+                                 /*   to 2^-24, then zero).  Outside that range the result is not */
+                                 /*   the attention the header defines.                            */
   int32_t num_splits;            /* context splits per (sequence, head); 0 = automatic          */
   int64_t w_seq_stride;          /* shared mode: elements from one sequence's W_k (and W_v) to  */
                                  /*   the next, a multiple of 8; 0 = one pair for all sequences  */

@@ -16,6 +16,14 @@ with U_t [T, r_t] and U_f [d, r_f] orthonormal and the core G [r_t, r_f, H, L]. 
     group, and head h of layer l rebuilds its (pre-RoPE) key from it through W_hl = U_f G[:, :, h, l]^T
     ([d, r_t]): k = W_hl U_t[t].  That is the block-shared form (one latent per token, per-layer
     up-projections), with W_hl per sequence because the core is fitted per prefill cache.
+  * The randomized token factor (FlashJoLT replaces the exact token-mode SVD with a randomized approximation;
+    the pages name no scheme): randomized subspace iteration on the token-mode unfolding A = X_(1) [T, D] --
+    the range finder of Halko, Martinsson and Tropp (2011) with q power iterations -- started from a Gaussian
+    test matrix Omega [D, r_t] that the caller draws.  The sketch is as wide as the token rank (no
+    oversampling and no closing small SVD): the partial Tucker form depends on U_t only through its span,
+    since the core absorbs any rotation of it.  Every orthonormalisation is the Q factor of the QR
+    decomposition with a positive diagonal R, which is unique for a full-rank argument.
+    PARITY UNPINNED beyond the invariants, closed forms and bounds of its pins (no page prints a worked example).
 """
 import numpy as np
 
@@ -76,3 +84,44 @@ def to_bf16_bits(x):
     m, e = np.frexp(x)                                       # x = m 2^e, 0.5 <= |m| < 1
     r = np.ldexp(np.rint(m * 256.0), e - 8)                  # exact in fp32
     return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def orth(y):
+    """Q factor of the QR decomposition of y [n, k] (n >= k) with a positive diagonal R (numpy's QR, then the
+    signs of Q's columns flipped where R's diagonal is negative): the unique such orthonormal basis of the
+    column space when y has full column rank."""
+    q, r = np.linalg.qr(np.asarray(y, dtype=np.float64))
+    sgn = np.where(np.diag(r) < 0, -1.0, 1.0)
+    return q * sgn
+
+
+def randomized_range(a, omega, q):
+    """Randomized subspace iteration on a [T, D] from omega [D, k]: Q = orth(a omega), then q times
+    Z = orth(a^T Q), Q = orth(a Z).  Returns Q [T, k], an orthonormal basis of range((a a^T)^q a omega)."""
+    a = np.asarray(a, dtype=np.float64)
+    Q = orth(a @ np.asarray(omega, dtype=np.float64))
+    for _ in range(q):
+        Z = orth(a.T @ Q)
+        Q = orth(a @ Z)
+    return Q
+
+
+def fit_randomized(x_tlhd, r_t, r_f, omega, q):
+    """Partial Tucker factors of one sequence's layer group from x_tlhd [T, L, H, d] (token, layer, head,
+    feature; the token-mode unfolding's columns are taken in that (l, h, i) order, which is also the row order
+    of omega [L * H * d, r_t]): the randomized token factor u_t [T, r_t], the exact feature factor u_f [d, r_f]
+    (leading left singular vectors of the feature-mode unfolding, largest-magnitude entry of each column
+    positive) and the core projected on both, in the up-projection expansion's layout [L, H, r_t, r_f]."""
+    x = np.asarray(x_tlhd, dtype=np.float64)
+    T = x.shape[0]
+    u_t = randomized_range(x.reshape(T, -1), omega, q)
+    xs = np.transpose(x, (0, 3, 2, 1))                       # [T, d, H, L], the convention of hosvd
+    u_f = _leading(unfold(xs, 1), r_f)
+    core = np.tensordot(u_t.T, xs, axes=(1, 0))              # [r_t, d, H, L]
+    core = np.tensordot(u_f.T, core, axes=(1, 1))            # [r_f, r_t, H, L]
+    return u_t, u_f, np.transpose(core, (3, 2, 1, 0))        # [L, H, r_t, r_f]
+
+
+def core_to_hosvd_layout(core_lhcj):
+    """core [L, H, r_t, r_f] (the expansion's layout) -> [r_t, r_f, H, L] (reconstruct's)."""
+    return np.transpose(np.asarray(core_lhcj), (2, 3, 1, 0))

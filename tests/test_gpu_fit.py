@@ -204,3 +204,40 @@ def test_fit_timed_entry_matches_and_brackets_the_gram_kernel():
     inner, outer = ev[2].elapsed_time(ev[3]), ev[0].elapsed_time(ev[1])
     assert 0 < inner <= outer
     assert ev[0].elapsed_time(ev[2]) >= 0 and ev[3].elapsed_time(ev[1]) >= 0
+
+
+def test_fitted_bases_project_elementwise_in_compress_from_dense():
+    # Element parity of the fit -> compress chain at per-token ranks: bases fitted by the fit oracle (fp64 SVD,
+    # rounded to bf16 by the oracle) are given to both kvc_compress (from dense, on the GPU) and the projection
+    # oracle; the GPU's fp32 latents (coordinates past each token's rank zero) equal the oracle's projection.
+    # The bases come from the oracle, not from the GPU fit, so no oracle input is a GPU output.
+    from oracle import ref
+    from oracle import tucker as TK
+    from tests.helpers import layout, np_any, np_u16
+    w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=2, T=600)
+    inp = synth.make_inputs(w, seq_len=[600, 523])
+    seq = [600, 523]
+    k = synth.make_prefill_rows(w.B, w.T, w.n_kv_heads, 128, seed=4)
+    v = synth.make_prefill_rows(w.B, w.T, w.n_kv_heads, 128, seed=5)
+    bases = []
+    for x, r in ((k, w.r_k), (v, w.r_v)):
+        b64, _ = F.fit_basis(x.numpy(), seq, r)                     # [Hkv][d][r] fp64
+        bases.append(torch.from_numpy(TK.to_bf16_bits(b64).view(np.int16)).view(torch.bfloat16).contiguous())
+    bk, bv = bases
+    L = kvc.make_layout(**w.layout_kwargs())
+    cache = kvc.DeviceCache.allocate(L, w.n_pages)
+    sl = inp["seq_len"].cuda()
+    lk = torch.zeros_like(inp["lat_k"]).cuda(); lv = torch.zeros_like(inp["lat_v"]).cuda()
+    kvc.compress(L, cache, inp["block_table"].cuda(), sl, w.T, ranks=inp["ranks"].cuda(), lat_k=lk, lat_v=lv,
+                 k=k.cuda().contiguous(), v=v.cuda().contiguous(), basis_k=bk.cuda(), basis_v=bv.cuda())
+    torch.cuda.synchronize()
+    olk, olv, _, _ = ref.project(layout(w), np_any(inp["seq_len"]), w.T, np_any(inp["ranks"]), k.numpy(), v.numpy(),
+                                 np_u16(bk), np_u16(bv))
+    ranks = np_any(inp["ranks"])
+    for got, want in ((lk, olk), (lv, olv)):
+        g_ = got.cpu().numpy()
+        for b in range(w.B):
+            assert np.allclose(g_[b, :seq[b]], want[b, :seq[b]], rtol=0, atol=1e-5 * np.abs(want).max())
+            # coordinates past each token's rank are zero on both sides
+            past = np.arange(g_.shape[-1])[None, None, :] >= ranks[b, :seq[b], None, None]
+            assert not g_[b, :seq[b]][np.broadcast_to(past, g_[b, :seq[b]].shape)].any()

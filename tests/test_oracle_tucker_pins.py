@@ -6,6 +6,7 @@ The form ("JoLT: Near-Lossless KV Cache Compression" thesis page, "How JoLT work
 truncated, heads and layers kept whole.
 """
 import numpy as np
+import pytest
 
 from oracle import tucker as TK
 
@@ -121,3 +122,115 @@ def test_bf16_rounding_ties_to_even():
     assert bits[4] == 0x3F81
     back = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert abs(back[5] - 3.0e-3) <= 2.0 ** -8 * 3.0e-3              # the unit roundoff of 8 significant bits
+
+
+# ---------------------------------------------------------------- randomized token factor (FlashJoLT reading)
+
+def _svd_matrix(rng, T, D, sig):
+    """A = U diag(sig) V^T with random orthonormal U [T, n], V [D, n], n = len(sig)."""
+    n = len(sig)
+    return _orth(rng, T, n) @ np.diag(sig) @ _orth(rng, D, n).T
+
+
+def test_orth_is_the_qr_factor_with_positive_diagonal():
+    # Q orthonormal, Q^T y upper triangular with a positive diagonal (the definition), and equal to classical
+    # Gram-Schmidt in fp64 on a well-conditioned y (an independent route to the same unique factor)
+    rng = np.random.default_rng(20)
+    y = rng.standard_normal((50, 7))
+    q = TK.orth(y)
+    r = q.T @ y
+    assert np.allclose(q.T @ q, np.eye(7), atol=1e-13)
+    assert np.allclose(np.tril(r, -1), 0, atol=1e-12) and (np.diag(r) > 0).all()
+    assert np.allclose(q @ r, y, atol=1e-12)
+    gs = np.zeros_like(y)
+    for j in range(7):
+        v = y[:, j] - gs[:, :j] @ (gs[:, :j].T @ y[:, j])
+        gs[:, j] = v / np.linalg.norm(v)
+    assert np.allclose(q, gs, atol=1e-12)
+
+
+@pytest.mark.parametrize("q", [0, 1, 3])
+def test_randomized_range_is_exact_on_planted_rank(q):
+    # rank(A) = k = sketch width: the range is recovered exactly whatever q
+    rng = np.random.default_rng(21)
+    a = _svd_matrix(rng, 200, 60, np.linspace(5.0, 0.5, 8))
+    u = np.linalg.svd(a, full_matrices=False)[0][:, :8]
+    Q = TK.randomized_range(a, rng.standard_normal((60, 8)), q)
+    assert np.allclose(Q.T @ Q, np.eye(8), atol=1e-12)
+    assert np.allclose(Q @ Q.T, u @ u.T, atol=1e-9)
+
+
+@pytest.mark.parametrize("q", [0, 1, 2])
+def test_randomized_range_within_the_deterministic_bound(q):
+    # Halko, Martinsson & Tropp (2011), Theorem 9.1 (Frobenius form), for the sketch width k = target rank: with
+    # Omega_1 = V_1^T Omega (k x k, invertible almost surely) and Omega_2 = V_2^T Omega,
+    #   |(I - QQ^T) B|_F^2 <= |S_2|_F^2 + |S_2 Omega_2 Omega_1^-1|_F^2
+    # for B with singular values S; applied to B = (A A^T)^q A, singular values sigma^(2q+1), whose sketch the
+    # power scheme computes.  A slowly decaying spectrum, five draws of Omega.
+    rng = np.random.default_rng(22)
+    T, D, k = 300, 80, 10
+    sig = 4.0 * (1.0 + np.arange(D)) ** -0.6
+    U, V = _orth(rng, T, D), _orth(rng, D, D)
+    a = U @ np.diag(sig) @ V.T
+    s_q = sig ** (2 * q + 1)
+    b = U @ np.diag(s_q) @ V.T
+    for _ in range(5):
+        om = rng.standard_normal((D, k))
+        Q = TK.randomized_range(a, om, q)
+        err2 = np.sum(((np.eye(T) - Q @ Q.T) @ b) ** 2)
+        o1, o2 = V[:, :k].T @ om, V[:, k:].T @ om
+        bound2 = np.sum(s_q[k:] ** 2) + np.sum((np.diag(s_q[k:]) @ o2 @ np.linalg.inv(o1)) ** 2)
+        assert err2 <= bound2 * (1 + 1e-9), (err2, bound2)
+        assert err2 >= np.sum(s_q[k:] ** 2) * (1 - 1e-9)     # never better than the optimal rank-k subspace
+
+
+def test_power_iterations_converge_to_the_leading_subspace():
+    # a gap sigma_{k+1} / sigma_k = 0.5: the largest principal angle between range(Q) and the leading k left
+    # singular vectors obeys tan(theta) <= |S_2^(2q+1) Omega_2 Omega_1^-1 S_1^-(2q+1)|_2 and shrinks with q
+    rng = np.random.default_rng(23)
+    T, D, k = 250, 60, 6
+    sig = np.concatenate([np.linspace(4.0, 2.0, k), 1.0 * 0.97 ** np.arange(D - k)])
+    U, V = _orth(rng, T, D), _orth(rng, D, D)
+    a = U @ np.diag(sig) @ V.T
+    om = rng.standard_normal((D, k))
+    o1, o2 = V[:, :k].T @ om, V[:, k:].T @ om
+    prev = None
+    for q in range(5):
+        Q = TK.randomized_range(a, om, q)
+        sin_max = np.linalg.norm(Q - U[:, :k] @ (U[:, :k].T @ Q), 2)   # |(I - U_k U_k^T) Q|_2
+        e = 2 * q + 1
+        tan_b = np.linalg.norm(np.diag(sig[k:] ** e) @ o2 @ np.linalg.inv(o1) @ np.diag(sig[:k] ** -e), 2)
+        assert sin_max <= tan_b / np.sqrt(1 + tan_b ** 2) + 1e-10
+        if prev is not None:
+            assert sin_max < prev
+        prev = sin_max
+    assert prev < 1e-2
+
+
+def test_unfolding_column_order_pairs_with_omega_rows():
+    # permuting the unfolding's columns and Omega's rows alike changes nothing
+    rng = np.random.default_rng(24)
+    a = rng.standard_normal((90, 40))
+    om = rng.standard_normal((40, 5))
+    perm = rng.permutation(40)
+    assert np.allclose(TK.randomized_range(a, om, 1), TK.randomized_range(a[:, perm], om[perm], 1), atol=1e-12)
+
+
+def test_fit_randomized_on_a_planted_group():
+    # a planted partial Tucker tensor (token rank 5, feature rank 4) in the [T, L, H, d] layout: exact
+    # reconstruction, the feature factor of the exact HOSVD, and the core equal to the projection computed
+    # element by element
+    rng = np.random.default_rng(25)
+    T, L, H, d, r_t, r_f = 40, 2, 3, 12, 5, 4
+    u_t, u_f, core = _planted(rng, T=T, d=d, H=H, L=L, r_t=r_t, r_f=r_f)
+    xs = TK.reconstruct(u_t, u_f, core)                    # [T, d, H, L]
+    x = np.transpose(xs, (0, 3, 2, 1))                     # [T, L, H, d]
+    om = rng.standard_normal((L * H * d, r_t))
+    gt, gf, gc = TK.fit_randomized(x, r_t, r_f, om, 1)
+    assert gc.shape == (L, H, r_t, r_f)
+    assert np.allclose(TK.reconstruct(gt, gf, TK.core_to_hosvd_layout(gc)), xs, atol=1e-10)
+    assert np.allclose(gf, TK.hosvd(xs, r_t, r_f)[1], atol=1e-10)
+    assert np.allclose(gt @ gt.T, u_t @ u_t.T, atol=1e-9)
+    for l, h, c, j in [(0, 0, 0, 0), (1, 2, 4, 3), (0, 1, 2, 1), (1, 0, 3, 2)]:
+        want = sum(gt[t, c] * gf[i, j] * x[t, l, h, i] for t in range(T) for i in range(d))
+        assert abs(gc[l, h, c, j] - want) < 1e-10
