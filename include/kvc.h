@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 6
+#define KVC_ABI_VERSION 7
 
 typedef enum {
   KVC_OK = 0,
@@ -409,6 +409,46 @@ typedef struct {
  * (values' rows zero) and W_v the reverse.  Asynchronous on stream.  INVALID_ARG for bad sizes or null
  * pointers, UNSUPPORTED for d != 128, MISALIGNED for pointers not 4-byte aligned. */
 kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32, void* stream);
+
+/* Inputs of kvc_tucker_fit (device memory). */
+typedef struct {
+  int32_t B, max_T;              /* sequences, token rows of x per sequence                        */
+  int32_t n_layers;              /* L, layers of the group                                         */
+  int32_t n_kv_heads;            /* Hkv                                                            */
+  int32_t head_dim;              /* d (128)                                                        */
+  int32_t r_t;                   /* token rank: a multiple of 4, 4..256, at most seq_len[b]        */
+  int32_t r_f;                   /* feature rank: a multiple of 4, 4..d                            */
+  int32_t power_iters;           /* q, 0..8                                                        */
+  int32_t ut_ld;                 /* row stride of u_t in floats, a multiple of 4 >= r_t (0: r_t)   */
+  const int32_t* seq_len;        /* [B] token rows used per sequence (clamped to 0..max_T)         */
+  const float* x;                /* [B][max_T][L][Hkv][d] the group's keys (or values), fp32       */
+  const float* omega;            /* [L*Hkv*d][r_t] Gaussian test matrix, rows in (l, h, i) order    */
+} kvc_tucker_fit_in;
+
+/* Workspace bytes of kvc_tucker_fit for these sizes (pointers are not read). */
+kvc_status kvc_tucker_fit_workspace_bytes(const kvc_tucker_fit_in* in, size_t* bytes);
+
+/* Partial Tucker factors of each sequence's layer group ("JoLT: Near-Lossless KV Cache Compression" thesis
+ * page, "How JoLT works": token and feature modes truncated, heads and layers kept; "A JoLT for the KV cache",
+ * abstract: FlashJoLT's randomized token-mode factor).  With A the sequence's token-mode unfolding (row t:
+ * x[b][t][...] flattened in (l, h, i) order, rows t < seq_len[b]):
+ *   u_t [B][max_T][ut_ld]: columns 0..r_t-1 the randomized subspace iteration Q = orth(A omega), then
+ *     power_iters times Z = orth(A^T Q), Q = orth(A Z), where orth(Y) is the Q factor of Y's QR decomposition
+ *     with a positive diagonal R (CholeskyQR2, Gram matrices and Cholesky factors in fp64, products in fp32);
+ *     rows t >= seq_len[b] are zero; other columns are not written;
+ *   u_f [B][d][r_f]: the r_f leading left singular vectors of the feature-mode unfolding (every (t, l, h)
+ *     row of the sequence), ordered and signed as by kvc_fit_basis;
+ *   core [B][L][Hkv][r_t][r_f]: core[b][l][h][c][j] = sum_t sum_i u_t[b][t][c] x[b][t][l][h][i] u_f[b][i][j],
+ *     the layout kvc_tucker_expand takes.
+ * info [B] (optional): 0, or 1 where an orthonormalisation met a numerically dependent column (a Cholesky
+ * pivot at or below 2^-40 of its diagonal entry: seq_len[b] < r_t, a token rank above the numerical rank of
+ * the rows at fp32 precision) or a non-finite one; that sequence's factors are then unspecified (finite
+ * where its rows are).  Products are summed in a fixed order: deterministic.  x, omega, u_t, u_f, core and
+ * ws 16-byte aligned (MISALIGNED otherwise).  INVALID_ARG for bad sizes or null pointers, UNSUPPORTED for
+ * d != 128 or ranks outside the ranges above, WORKSPACE for ws_bytes below kvc_tucker_fit_workspace_bytes.
+ * Asynchronous on stream. */
+kvc_status kvc_tucker_fit(const kvc_tucker_fit_in* in, float* u_t, float* u_f, float* core, int32_t* info, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* Inputs of kvc_evict_select (device memory). */
 typedef struct {

@@ -37,6 +37,8 @@ kvc_status salience_impl(const kvc_salience_in& in, float* out, void* ws, size_t
 kvc_status rank_alloc_impl(const kvc_alloc_in& in, uint8_t* ranks, hipStream_t st);
 kvc_status plan_impl(const kvc_plan_in& in, int32_t* choice, double* lambda);
 kvc_status tucker_impl(const kvc_tucker_in& in, uint16_t* w, float* w32, hipStream_t st);
+kvc_status tfit_impl(const kvc_tucker_fit_in& in, float* u_t, float* u_f, float* core, int32_t* info, void* ws,
+                     size_t ws_bytes, hipStream_t st, size_t* bytes_out);
 kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st);
 kvc_status check_impl(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, int32_t* flags,
                       hipStream_t st);
@@ -254,6 +256,17 @@ kvc_status kvc_plan_budget(const kvc_plan_in* in, int32_t* choice, double* lambd
 kvc_status kvc_tucker_expand(const kvc_tucker_in* in, uint16_t* w, float* w_f32, void* stream) {
   if (!in) return KVC_ERR_INVALID_ARG;
   return tucker_impl(*in, w, w_f32, (hipStream_t)stream);
+}
+
+kvc_status kvc_tucker_fit_workspace_bytes(const kvc_tucker_fit_in* in, size_t* bytes) {
+  if (!in || !bytes) return KVC_ERR_INVALID_ARG;
+  return tfit_impl(*in, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr, bytes);
+}
+
+kvc_status kvc_tucker_fit(const kvc_tucker_fit_in* in, float* u_t, float* u_f, float* core, int32_t* info, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!in) return KVC_ERR_INVALID_ARG;
+  return tfit_impl(*in, u_t, u_f, core, info, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
 kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream) {

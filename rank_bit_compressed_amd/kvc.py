@@ -27,7 +27,7 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
            "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
            "kvc_evict_select", "kvc_decode_check", "kvc_decode_attn_noalloc", "kvc_probe_stream_read",
-           "kvc_probe_mfma_f16", "kvc_probe_clock"]
+           "kvc_probe_mfma_f16", "kvc_probe_clock", "kvc_tucker_fit_workspace_bytes", "kvc_tucker_fit"]
 
 
 class KvcError(RuntimeError):
@@ -519,6 +519,56 @@ def tucker_expand(u_f, core, latent, row0=0, w=None, want_f32=False):
     _check(lib().kvc_tucker_expand(C.byref(inp), _ptr(w.view(torch.int16)), _ptr(w32), _stream()),
            "kvc_tucker_expand")
     return w, w32
+
+
+class TuckerFitIn(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("B", "max_T", "n_layers", "n_kv_heads", "head_dim", "r_t", "r_f",
+                                         "power_iters", "ut_ld")] + \
+               [("seq_len", C.c_void_p), ("x", C.c_void_p), ("omega", C.c_void_p)]
+
+
+def tucker_fit_in(x, seq_len, omega, r_t, r_f, power_iters, ut_ld=0) -> TuckerFitIn:
+    B, max_T, L, Hkv, d = x.shape
+    return TuckerFitIn(B, max_T, L, Hkv, d, r_t, r_f, power_iters, ut_ld, _ptr(seq_len), _ptr(x), _ptr(omega))
+
+
+def tucker_fit_workspace_bytes(inp: TuckerFitIn) -> int:
+    out = C.c_size_t()
+    _check(lib().kvc_tucker_fit_workspace_bytes(C.byref(inp), C.byref(out)), "kvc_tucker_fit_workspace_bytes")
+    return out.value
+
+
+def tucker_fit(x, seq_len, omega, r_t, r_f, power_iters, u_t=None, ws=None):
+    """kvc_tucker_fit: x fp32 [B, max_T, L, Hkv, d], seq_len int32 [B], omega fp32 [L * Hkv * d, r_t] (device) ->
+    (u_t fp32 [B, max_T, r_t] or the given u_t view, u_f fp32 [B, d, r_f], core fp32 [B, L, Hkv, r_t, r_f],
+    info int32 [B]).  A given u_t is a [B, max_T, r_t] view with unit column stride (for instance columns of a
+    wider latent buffer); its row stride is passed as ut_ld."""
+    B, max_T, L, Hkv, d = x.shape
+    for t in (x, omega):
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("tucker_fit takes contiguous fp32 x and omega")
+    if tuple(omega.shape) != (L * Hkv * d, r_t):
+        raise ValueError(f"omega must be [{L * Hkv * d}, {r_t}]")
+    if seq_len.dtype != torch.int32 or tuple(seq_len.shape) != (B,):
+        raise ValueError("seq_len must be int32 [B]")
+    dev = x.device
+    if u_t is None:
+        u_t = torch.empty(B, max_T, r_t, dtype=torch.float32, device=dev)
+    if (u_t.dtype != torch.float32 or tuple(u_t.shape) != (B, max_T, r_t) or u_t.stride(2) != 1
+            or u_t.stride(0) != max_T * u_t.stride(1)):
+        raise ValueError("u_t must be an fp32 [B, max_T, r_t] view with unit column stride and rows of one stride")
+    u_f = torch.empty(B, d, r_f, dtype=torch.float32, device=dev)
+    core = torch.empty(B, L, Hkv, r_t, r_f, dtype=torch.float32, device=dev)
+    info = torch.empty(B, dtype=torch.int32, device=dev)
+    inp = tucker_fit_in(x, seq_len, omega, r_t, r_f, power_iters, u_t.stride(1))
+    need = tucker_fit_workspace_bytes(inp)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not u_t.is_cuda:
+        raise ValueError("u_t must be a CUDA/HIP tensor")
+    _check(lib().kvc_tucker_fit(C.byref(inp), C.c_void_p(u_t.data_ptr()), _ptr(u_f), _ptr(core), _ptr(info), _ptr(ws), ws.numel(),
+                                _stream()), "kvc_tucker_fit")
+    return u_t, u_f, core, info
 
 
 class EvictIn(C.Structure):

@@ -37,7 +37,13 @@ Distributions (the pages give shapes, not data):
     sqrt(T d / (r_t r_f)) * s_c, s_c = (c + 1)^-0.35 normalised to mean square
     1 over c (a decaying token-mode spectrum), so rebuilt keys and values have
     about unit variance like the other workloads.  The block-shared latent of
-    such a workload is the key factor row followed by the value factor row.
+    such a workload is the key factor row followed by the value factor row;
+  * a layer group's keys or values for the partial Tucker fit (fp32 [B, max_T, L, Hkv, d]), per sequence:
+    R planted token components, x[t, l, h, :] = sum_c a[t, c] s_c F (f * z[c, l, h, :]) + noise e, with a, z
+    and e i.i.d. N(0, 1), s_c = c^-decay_t, f_i = i^-decay_f, F a seeded orthogonal d x d matrix, divided
+    by the expected element RMS, so the token mode has a decaying spectrum of rank R plus a noise floor and
+    the feature mode a decaying spectrum without repeated values;
+  * the Gaussian test matrix of the randomized fit: N(0, 1) per element, fp32.
 """
 from __future__ import annotations
 
@@ -302,3 +308,34 @@ def make_salience(B: int, max_T: int, seed: int = 0, device="cpu") -> torch.Tens
     g = torch.Generator(device=torch.device(device))
     g.manual_seed(seed * 1000 + 33)
     return torch.exp(1.5 * torch.randn(B, max_T, generator=g, device=device, dtype=torch.float64)).to(torch.float32)
+
+
+def make_group_rows(B: int, max_T: int, n_layers: int, n_kv_heads: int, head_dim: int, seed: int = 0, device="cpu",
+                    rank: int = 512, decay_t: float = 0.5, decay_f: float = 0.7, noise: float = 0.05) -> torch.Tensor:
+    """fp32 [B, max_T, L, Hkv, d] keys or values of a layer group (seeded; the law is in the module docstring)."""
+    dev = torch.device(device)
+    D = n_layers * n_kv_heads * head_dim
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000 + 34)
+    gz = torch.Generator(device=dev)
+    gz.manual_seed(seed * 1000 + 35)
+    f = _decay_scale(head_dim, decay_f, "cpu").double()
+    s = _decay_scale(rank, decay_t, "cpu").double()
+    rms = math.sqrt(float((s ** 2).sum() * (f ** 2).mean()) + noise ** 2)
+    x = torch.empty(B, max_T, n_layers, n_kv_heads, head_dim, dtype=torch.float32, device=dev)
+    for b in range(B):
+        q, r = torch.linalg.qr(torch.randn(head_dim, head_dim, generator=g, dtype=torch.float64))
+        F = (q * torch.sign(torch.diagonal(r))).to(torch.float32).to(dev)
+        z = torch.randn(rank, n_layers * n_kv_heads, head_dim, generator=gz, device=dev) * f.float().to(dev)
+        m = (z @ F.T).reshape(rank, D) * s.float().to(dev)[:, None]
+        a = torch.randn(max_T, rank, generator=gz, device=dev)
+        e = torch.randn(max_T, D, generator=gz, device=dev)
+        x[b] = ((a @ m + noise * e) / rms).view(max_T, n_layers, n_kv_heads, head_dim)
+    return x
+
+
+def make_omega(rows: int, cols: int, seed: int = 0, device="cpu") -> torch.Tensor:
+    """fp32 [rows, cols] Gaussian test matrix (seeded, N(0, 1), drawn on the CPU)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000 + 36)
+    return torch.randn(rows, cols, generator=g, dtype=torch.float32).to(device)

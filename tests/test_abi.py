@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 6
+    assert kvc.lib().kvc_abi_version() == 7
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -274,3 +274,22 @@ def test_noalloc_rejects_sizes_beyond_its_array_before_any_device_call():
     assert kvc.lib().kvc_decode_attn_noalloc(C.byref(L), C.byref(cache), C.byref(inp), None, None) == -6
     assert kvc.lib().kvc_status_string(-6).startswith(b"decode needs more scratch")
     assert kvc.lib().kvc_decode_attn_noalloc(C.byref(L), C.byref(cache), None, None, None) == -1
+
+
+def test_tucker_fit_rejects_bad_sizes_before_launch():
+    def fin(**kw):
+        a = dict(B=2, max_T=300, n_layers=2, n_kv_heads=2, head_dim=128, r_t=48, r_f=32, power_iters=1, ut_ld=0)
+        a.update(kw)
+        return kvc.TuckerFitIn(*a.values(), None, None, None)
+    out = C.c_size_t()
+    assert kvc.lib().kvc_tucker_fit_workspace_bytes(C.byref(fin()), C.byref(out)) == 0 and out.value > 0
+    small = out.value
+    assert kvc.lib().kvc_tucker_fit_workspace_bytes(C.byref(fin(power_iters=0)), C.byref(out)) == 0
+    assert out.value < small                                       # no separate Q buffer without power iterations
+    for bad, want in ((dict(r_t=6), -2), (dict(r_t=260), -2), (dict(r_f=130), -2), (dict(r_f=2), -2),
+                      (dict(head_dim=64), -2), (dict(B=0), -1), (dict(power_iters=9), -1), (dict(ut_ld=40), -1),
+                      (dict(ut_ld=50), -1), (dict(max_T=0), -1)):
+        assert kvc.lib().kvc_tucker_fit_workspace_bytes(C.byref(fin(**bad)), C.byref(out)) == want, bad
+    # null inputs with a valid geometry: rejected before any device call
+    assert kvc.lib().kvc_tucker_fit(C.byref(fin()), None, None, None, None, None, 0, None) == -1
+    assert kvc.lib().kvc_tucker_fit(None, None, None, None, None, None, 0, None) == -1
