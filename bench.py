@@ -245,6 +245,57 @@ def fit_workload(steps: int) -> dict:
             "rest_of_call": "split reduction and the per-head Jacobi eigensolver (one workgroup per head)"}
 
 
+TFIT_SHAPE = (4, 32768, 4, 8, 128)   # the Tucker group: sequences, tokens, layers, KV heads, head dim
+TFIT_RANKS = (256, 256, 64, 1)       # key and value token ranks, feature rank, power iterations
+
+
+def tucker_fit_workload(steps: int) -> dict:
+    """kvc_tucker_fit of the keys and of the values of the 4 x 32K-token, 4-layer, 8-head group (token ranks
+    256 + 256, feature rank 64, one power iteration): median time of the two calls (events on the library's
+    stream around both), and the large products' figure against the fp32 matrix peak.  Algorithmic flops: the
+    four products with the token-mode unfolding per sequence and fit (A Omega, A^T Q, A Z, Q^T A), 2 T D r_t
+    each; the orthonormalisations, the feature fit and the core's last product are counted as overhead."""
+    import torch
+    from rank_bit_compressed_amd import kvc, synth
+
+    B, T, L, H, d = TFIT_SHAPE
+    rtk, rtv, rf, q = TFIT_RANKS
+    D = L * H * d
+    xk = synth.make_group_rows(B, T, L, H, d, seed=8, device="cuda")
+    xv = synth.make_group_rows(B, T, L, H, d, seed=9, device="cuda")
+    ok, ov = synth.make_omega(D, rtk, seed=8, device="cuda"), synth.make_omega(D, rtv, seed=9, device="cuda")
+    sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    lat = torch.empty(B, T, rtk + rtv, device="cuda")
+    need = max(kvc.tucker_fit_workspace_bytes(kvc.tucker_fit_in(xk, sl, ok, rtk, rf, q, rtk + rtv)),
+               kvc.tucker_fit_workspace_bytes(kvc.tucker_fit_in(xv, sl, ov, rtv, rf, q, rtk + rtv)))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def run():
+        kvc.tucker_fit(xk, sl, ok, rtk, rf, q, u_t=lat[:, :, :rtk], ws=ws)
+        kvc.tucker_fit(xv, sl, ov, rtv, rf, q, u_t=lat[:, :, rtk:], ws=ws)
+
+    n = max(5, steps // 200)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+    flops = sum(4 * 2 * B * T * D * r for r in (rtk, rtv))
+    tflops = flops / (ms * 1e-3) / 1e12
+    del xk, xv, ws, lat
+    torch.cuda.empty_cache()
+    return {"kernel": "gemm_kernel (fp32 matrix instructions) and the CholeskyQR2 orthonormalisations",
+            "shape": {"sequences": B, "tokens": T, "layers": L, "kv_heads": H, "head_dim": d, "r_t_keys": rtk,
+                      "r_t_values": rtv, "r_f": rf, "power_iters": q},
+            "ms_per_group_fit_median": round(ms, 4), "product_flops": flops, "tflops": round(tflops, 1),
+            "bound": "mfma", "frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4)}
+
+
 def alloc_workload(steps: int) -> dict:
     """kvc_salience (window queries over the prefill keys) and kvc_rank_alloc on the prefill of the 32K workload:
     median times from events on the library's stream (the current torch stream).  Algorithmic flops of the
@@ -384,6 +435,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads' figures")
+    ap.add_argument("--only", choices=["tucker_fit_group_32k"], help="run only this prefill-side figure and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path here "
@@ -393,6 +445,9 @@ def main():
     import torch
     from rank_bit_compressed_amd import accounting, kvc, synth
 
+    if args.only == "tucker_fit_group_32k":
+        print(json.dumps({"workload": args.only, **tucker_fit_workload(args.steps)}), flush=True)
+        return
     w = synth.WORKLOADS[WORKLOAD]
     dev = "cuda"
     inp = synth.make_inputs(w, device=dev)
@@ -519,6 +574,7 @@ def main():
         line["other_workloads"] = other_workloads(args.steps, args.warmup, peaks)
         line["other_workloads"]["basis_fit_prefill_32k"] = fit_workload(args.steps)
         line["other_workloads"]["rank_alloc_prefill_32k"] = alloc_workload(args.steps)
+        line["other_workloads"]["tucker_fit_group_32k"] = tucker_fit_workload(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, {k: (v.cpu() if v is not None else None) for k, v in cpu_inp.items()})
     print(json.dumps(line), flush=True)

@@ -4,24 +4,27 @@
 // Work decomposition: one workgroup (4 waves) per (sequence b, KV head h, context split of pages).
 // The workgroup copies each page's head-h block (codes, scale/zero pairs) and the page's offset row
 // from HBM into LDS with buffer loads that write LDS directly, two buffers deep (the next page in
-// flight while one is decoded; a third buffer measured no faster).  Wave w decodes the 32-token super-tiles w and w + 4 of every page
-// and keeps its own online-softmax state.
+// flight while one is decoded; a third buffer measured no faster).  Wave w decodes the 64 slots
+// 64w..64w+63 of every page as two 32-token super-tiles and keeps its own online-softmax state.
+// Under variable rank the wave first orders its 64 slots by their number of 16-coordinate steps (the
+// kernel body below), so that a super-tile runs only the steps its largest rank needs.
 //
 // All products are v_mfma_f32_32x32x16_f16 (on gfx950 it does twice the work of the 16x16x32 form in
-// the same issue time).  Lane l serves token l % 32 of the super-tile, and its half l / 32 selects
-// the eight k-slots it supplies.  Per super-tile:
+// the same issue time).  Lane l serves one token of the super-tile (slot order, or the rank order), and
+// its half l / 32 selects the eight k-slots it supplies.  Per super-tile:
 //   K codes -> fp16 (code * scale + zero; 8 coordinates per lane per 16-coordinate step)
 //   -> K_pre = B_k c (4 tiles of 32 head dims; the basis fragments stay in registers)
-//   -> RoPE R(s) in packed fp16 on the pairs (j, j + 64), which sit in one lane (tiles m and m + 2)
-//   -> S = Q~ K~^T (rows: query heads, replicated; columns: tokens), accumulated onto -m so the
-//      scores come out shifted by the running reference maximum; each lane then holds the four
-//      heads' scores of its token
+//   -> RoPE R(u) in packed fp16 on the pairs (j, j + 64), which sit in one lane (tiles m and m + 2)
+//   -> S = Q~ K~^T (rows: the wave's two query variants x 4 heads, replicated; columns: tokens),
+//      accumulated onto -m so the scores come out shifted by the running reference maximum; each lane
+//      keeps the four heads' scores of its token's variant
 //   -> p = 2^s; P^T through a one-hot MFMA (tokens move into the reduction slots)
 //   V codes -> fp16 -> V^T through one-hot MFMAs -> acc += P V_latent (rows: heads, columns:
 //   latent coordinates).  The value basis is applied once per (b, head) in the merge, since
 //   sum_t p_t B c_t = B sum_t p_t c_t.
-// RoPE is split as R(t0 + s) = R(t0) R(s): R(s) for the lane's slot s < 32 is held in registers;
-// R(q_pos - t0) is applied to the query once per super-tile.
+// RoPE is split as R(t0 + 32 v + u) = R(t0 + 32 v) R(u) for page slot 32 v + u: R(u), u < 32, from an LDS
+// table on the key side; R(q_pos - t0 - 32 v) q on the query side, the two variants v = 0, 1 of the wave's
+// block rotated once per page.
 // Softmax keeps a reference maximum m per head and only raises it (rescaling acc and l) when a score
 // exceeds it by more than 2^8 in the exp2 domain; the probabilities then stay below 256, within the
 // fp16 operand range at full relative precision.  The merge uses the same m.

@@ -396,4 +396,31 @@ kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32
   return KVC_OK;
 }
 
+// The two passes of fit_impl as separate launches, for callers that fit several independent row sets: the
+// Gram matrices of in's heads into gram [Hkv][D][D] (part: fit_part_floats(in) floats), and the eigensolver
+// over n such matrices at once (one workgroup each).
+size_t fit_part_floats(const kvc_fit_in& in) {
+  return fit::part_floats(in.n_kv_heads, fit::slices(in.n_kv_heads, in.B, in.max_T));
+}
+
+hipError_t fit_gram_launch(const kvc_fit_in& in, float* part, float* gram, hipStream_t st) {
+  using namespace fit;
+  const int n_slices = slices(in.n_kv_heads, in.B, in.max_T);
+  fit_gram_kernel<<<in.n_kv_heads * n_slices, 256, 0, st>>>(in.x, in.seq_len, in.B, in.max_T, in.n_kv_heads, n_slices,
+                                                             part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  fit_reduce_kernel<<<in.n_kv_heads * NT * 4, 256, 0, st>>>(part, n_slices, gram);
+  return hipGetLastError();
+}
+
+hipError_t fit_eig_launch(const float* gram, int n, int rank, int r_cap, uint16_t* basis_bf16, float* basis_f32,
+                          float* sigma2, hipStream_t st) {
+  using namespace fit;
+  hipError_t e = hipFuncSetAttribute((const void*)fit_eig_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)EIG_LDS);
+  if (e != hipSuccess) return e;
+  fit_eig_kernel<<<n, EIG_THREADS, EIG_LDS, st>>>(gram, rank, r_cap, basis_bf16, basis_f32, sigma2);
+  return hipGetLastError();
+}
+
 }  // namespace kvc

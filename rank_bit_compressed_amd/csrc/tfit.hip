@@ -23,13 +23,16 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvc_common.hpp"
 
 namespace kvc {
 
-kvc_status fit_impl(const kvc_fit_in& in, uint16_t* basis_bf16, float* basis_f32, float* sigma2, void* ws,
-                    size_t ws_bytes, hipStream_t st, size_t* bytes_out);
+size_t fit_part_floats(const kvc_fit_in& in);
+hipError_t fit_gram_launch(const kvc_fit_in& in, float* part, float* gram, hipStream_t st);
+hipError_t fit_eig_launch(const float* gram, int n, int rank, int r_cap, uint16_t* basis_bf16, float* basis_f32,
+                          float* sigma2, hipStream_t st);
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -39,8 +42,7 @@ constexpr int LS = BM + 4;        // LDS row stride of the operand tiles (floats
 constexpr int RMAX = 256;         // largest token rank
 constexpr int CP = 64;            // Cholesky panel width
 constexpr int CT = 1024;          // Cholesky threads
-constexpr int CROWS = CT / CP;    // row groups of a panel
-constexpr int CSLOT = RMAX / CROWS;
+constexpr int STG_LOADS = (RMAX - CP) * CP / CT;      // staging loads per thread for one finished panel
 constexpr int GT = 64;            // Gram tile
 constexpr int GR = 32;            // Gram rows per LDS stage
 constexpr int D = 128;            // head dimension
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256) void gram64_kernel(const float* __restrict__ y
   }
 }
 
-// G[b] lower triangle = sum over splits of the partials, in split order
+// G[b] = sum over splits of the partials (lower triangle), in split order, mirrored into the upper one
 __global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict__ part, int splits, int B, int r,
                                                        double* __restrict__ G) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -265,6 +267,7 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const double* __restrict_
   double s = part[e];
   for (int k = 1; k < splits; ++k) s += part[k * n + e];
   G[e] = s;
+  G[e - ij + (int64_t)j * r + i] = s;  // the mirror entry: G is stored whole
 }
 
 __device__ inline double readlane_f64(double v, int ln) {
@@ -272,84 +275,105 @@ __device__ inline double readlane_f64(double v, int ln) {
   return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(w.x, ln), __builtin_amdgcn_readlane(w.y, ln)));
 }
 
-// Cholesky factor of G[b] (fp64, lower triangle read), G = L L^T, one workgroup per sequence; writes
-// Lt[b][m][i] = L[i][m] (i >= m).  Left-looking by panels of 64 columns: the panel's rows are updated with the
-// finished columns (staged through LDS 16 at a time), then factored right-looking with the panel held in
-// registers (thread: column c0 + tid % 64, rows tid / 64 + 16 s) and column j broadcast through LDS at step j:
-// entry (i, m) loses a[i][j] a[m][j] / a[j][j], and L[i][m] = a[i][m] / sqrt(a[m][m]) at the end.  A pivot
-// a[j][j] is the squared distance of column j of Y from the span of the columns before it; one at or below
-// 2^-40 G[j][j] (an angle under about 8 fp32 roundoffs: numerically dependent at the precision of Y), or
-// not finite, sets info[b] = 1 and the factor is replaced by the identity.
+// Cholesky factor of G[b] (fp64, full symmetric), G = L L^T, one workgroup of 16 waves per sequence; writes
+// Lt[b][m][i] = L[i][m] (i >= m).  Left-looking by panels of 64 columns: the panel's entries are updated with
+// the finished panels (each staged through LDS whole), then factored right-looking in registers.  Wave w holds
+// the panel's columns w, w + 16, w + 32, w + 48 and lane l its rows l, l + 64, ... ; at step j the wave that
+// holds column j broadcasts it (and the reciprocal of its pivot) through LDS, and entry (i, m), m > j, loses
+// a[i][j] a[m][j] / a[j][j]; at the end L[i][m] = a[i][m] / sqrt(a[m][m]).  Every branch is uniform over a
+// wave.  A pivot a[j][j] is the squared distance of column j of Y from the span of the columns before it; one
+// at or below 2^-40 G[j][j] (an angle under about 8 fp32 roundoffs: numerically dependent at the precision of
+// Y), or not finite, sets info[b] = 1 and the factor is replaced by the identity.
 __global__ __launch_bounds__(CT) void chol_kernel(const double* __restrict__ Gm, double* __restrict__ Ltm, int r,
                                                   int32_t* __restrict__ info) {
+  constexpr int NW = CT / 64;           // waves
+  constexpr int KC = CP / NW;           // panel columns per wave
+  constexpr int SR = RMAX / 64;         // row slots per lane
+  constexpr int SR1 = (RMAX - CP) / 64; // row slots that exist past the first panel
   __shared__ double colb[2][RMAX];
-  __shared__ double stg[RMAX][17];
+  __shared__ double rcpb[2];
+  __shared__ double stg[RMAX - CP][CP + 1];
   __shared__ int bad;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int tc = tid & (CP - 1), tr = tid / CP;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const double* G = Gm + (int64_t)b * r * r;
   double* Lt = Ltm + (int64_t)b * r * r;
   if (tid == 0) bad = 0;
   __syncthreads();
   for (int c0 = 0; c0 < r; c0 += CP) {
     const int w = min(CP, r - c0), rows = r - c0;
-    double a[CSLOT];
+    double a[KC][SR], gdiag[KC], piv[KC];
 #pragma unroll
-    for (int s = 0; s < CSLOT; ++s) {
-      const int i = tr + CROWS * s;
-      a[s] = (tc < w && i < rows && i >= tc) ? G[(int64_t)(c0 + i) * r + c0 + tc] : 0.0;
+    for (int k = 0; k < KC; ++k) {
+      const int m = wv + NW * k;
+      gdiag[k] = m < w ? G[(int64_t)(c0 + m) * r + c0 + m] : 1.0;
+      piv[k] = 1.0;
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        const int i = lane + 64 * s;
+        a[k][s] = (m < w && i < rows) ? G[(int64_t)(c0 + m) * r + c0 + i] : 0.0;  // G symmetric: row m
+      }
     }
-    const double gdiag = tc < w ? G[(int64_t)(c0 + tc) * r + c0 + tc] : 0.0;
-    for (int m0 = 0; m0 < c0; m0 += 16) {
-      for (int e = tid; e < rows * 16; e += CT) {
-        const int mm = e / rows, ii = e - mm * rows;
-        stg[ii][mm] = Lt[(int64_t)(m0 + mm) * r + c0 + ii];
+    // left-looking update by the finished panels; past the first panel at most RMAX - CP rows remain
+    for (int m0 = 0; m0 < c0; m0 += CP) {
+#pragma unroll 4
+      for (int q = 0; q < STG_LOADS; ++q) {
+        const int e = tid + CT * q, mm = e / (RMAX - CP), ii = e - mm * (RMAX - CP);
+        if (ii < rows) stg[ii][mm] = Lt[(int64_t)(m0 + mm) * r + c0 + ii];
       }
       __syncthreads();
-      if (tc < w) {
-#pragma unroll 4
-        for (int mm = 0; mm < 16; ++mm) {
-          const double lj = stg[tc][mm];
+#pragma unroll 2
+      for (int mm = 0; mm < CP; ++mm) {
+        double li[SR1];
 #pragma unroll
-          for (int s = 0; s < CSLOT; ++s) {
-            const int i = tr + CROWS * s;
-            if (i < rows) a[s] -= stg[i][mm] * lj;
-          }
+        for (int s = 0; s < SR1; ++s) li[s] = stg[lane + 64 * s][mm];  // rows past `rows`: stale, never stored
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const double lm = stg[wv + NW * k][mm];
+#pragma unroll
+          for (int s = 0; s < SR1; ++s) a[k][s] = __builtin_fma(-li[s], lm, a[k][s]);
         }
       }
       __syncthreads();
     }
-    double piv = 1.0;
     for (int j = 0; j < w; ++j) {
       double* cb = colb[j & 1];
-      if (tc == j) {
+      const int kj = j / NW;
+      if (wv == j % NW) {
+        // entries above the diagonal or past `rows` are written too: they only meet entries never stored
 #pragma unroll
-        for (int s = 0; s < CSLOT; ++s) {
-          const int i = tr + CROWS * s;
-          if (i >= j && i < rows) cb[i] = a[s];
-        }
+        for (int k = 0; k < KC; ++k)
+          if (k == kj) {
+#pragma unroll
+            for (int s = 0; s < SR; ++s) cb[lane + 64 * s] = a[k][s];
+            if (lane == j) {
+              rcpb[j & 1] = 1.0 / a[k][0];
+              if (!(a[k][0] > 0x1p-40 * gdiag[k])) bad = 1;
+            }
+          }
       }
       __syncthreads();
-      const double d = cb[j];
-      if (tc == j) {
-        piv = d;
-        if (!(d > 0x1p-40 * gdiag)) bad = 1;
-      }
-      if (tc > j && tc < w) {
-        const double f = cb[tc] / d;
 #pragma unroll
-        for (int s = 0; s < CSLOT; ++s) {
-          const int i = tr + CROWS * s;
-          if (i >= tc && i < rows) a[s] -= cb[i] * f;
+      for (int k = 0; k < KC; ++k) {
+        const int m = wv + NW * k;
+        if (m == j) piv[k] = cb[j];
+        if (m > j && m < w) {
+          const double f = cb[m] * rcpb[j & 1];
+#pragma unroll
+          for (int s = 0; s < SR; ++s) a[k][s] = __builtin_fma(-cb[lane + 64 * s], f, a[k][s]);
         }
       }
     }
-    if (tc < w) {
-      const double rs = 1.0 / sqrt(piv);
 #pragma unroll
-      for (int s = 0; s < CSLOT; ++s) {
-        const int i = tr + CROWS * s;
-        if (i >= tc && i < rows) Lt[(int64_t)(c0 + tc) * r + c0 + i] = i == tc ? sqrt(piv) : a[s] * rs;
+    for (int k = 0; k < KC; ++k) {
+      const int m = wv + NW * k;
+      if (m < w) {
+        const double sq = sqrt(piv[k]), rs = 1.0 / sq;
+#pragma unroll
+        for (int s = 0; s < SR; ++s) {
+          const int i = lane + 64 * s;
+          if (i >= m && i < rows) Lt[(int64_t)(c0 + m) * r + c0 + i] = i == m ? sq : a[k][s] * rs;
+        }
       }
     }
     __syncthreads();
@@ -414,7 +438,7 @@ struct Plan {
   int64_t D;          // columns of the token-mode unfolding
   int ksplit, kchunk; // split of the token sum in A^T Q and Q^T A
   int gsplit_t, gchunk_t, gsplit_d, gchunk_d;
-  size_t o_y, o_q1, o_q, o_z, o_z1, o_kp, o_gp, o_g, o_lt, o_ri, o_len, o_fit, total;
+  size_t o_y, o_q1, o_q, o_z, o_z1, o_kp, o_gp, o_g, o_lt, o_ri, o_len, o_fit, o_fg, total;
   size_t fit_bytes;
 };
 
@@ -430,6 +454,41 @@ inline void gram_split(int rows, int r, int B, int* splits, int* chunk) {
 }
 
 }  // namespace tf
+
+namespace {
+// The feature factor does not depend on the token factor, so it runs on a stream of the library's own (one per
+// device, default priority), forked from and joined back to the caller's stream with events; its eigensolver
+// (one workgroup per sequence) then overlaps the token factor's products.  The lock is held while a call
+// enqueues its fork and join, so calls from several host threads keep their event pairs apart.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& s = g_side[dev];
+  if (!s.st) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    s.st = st;
+    s.fork = f;
+    s.join = j;
+  }
+  return &s;
+}
+}  // namespace
 
 static kvc_fit_in feature_fit_in(const kvc_tucker_fit_in& in, int64_t rows_per_token, const int32_t* lens4, int b) {
   kvc_fit_in f{};
@@ -469,12 +528,7 @@ static kvc_status tfit_plan(const kvc_tucker_fit_in& in, tf::Plan* p) {
   p->ksplit = (int)((T + kc - 1) / kc);
   gram_split((int)T, (int)r, (int)B, &p->gsplit_t, &p->gchunk_t);
   gram_split((int)p->D, (int)r, (int)B, &p->gsplit_d, &p->gchunk_d);
-  kvc_fit_in f = feature_fit_in(in, rpt, nullptr, 0);
-  f.seq_len = nullptr;
-  f.x = nullptr;
-  size_t fb = 0;
-  kvc_status s = fit_impl(f, nullptr, nullptr, nullptr, nullptr, 0, nullptr, &fb);
-  if (s != KVC_OK) return s;
+  const size_t fb = fit_part_floats(feature_fit_in(in, rpt, nullptr, 0)) * 4;  // one sequence's partial Grams
   p->fit_bytes = fb;
   const size_t ybytes = al((size_t)B * T * r * 4), zbytes = al((size_t)B * p->D * r * 4);
   const int gs = std::max(p->gsplit_t, p->gsplit_d);
@@ -491,6 +545,7 @@ static kvc_status tfit_plan(const kvc_tucker_fit_in& in, tf::Plan* p) {
   p->o_ri = o;  o += al((size_t)B * r * r * 4);
   p->o_len = o; o += al((size_t)B * 20);
   p->o_fit = o; o += al(fb);
+  p->o_fg = o;  o += al((size_t)B * D * D * 4);
   p->total = o;
   return KVC_OK;
 }
@@ -583,6 +638,21 @@ kvc_status tfit_impl(const kvc_tucker_fit_in& in, float* u_t, float* u_f, float*
                      info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
+  // U_f on the side stream (when one is available; otherwise in order on the caller's stream): the basis fit of
+  // each sequence's (t, l, h) rows, its Gram matrix, then one eigensolver launch for all sequences
+  std::lock_guard<std::mutex> side_lock(g_side_mu);
+  SideStream* side = side_stream();
+  hipStream_t fst = st;
+  if (side && hipEventRecord(side->fork, st) == hipSuccess && hipStreamWaitEvent(side->st, side->fork, 0) == hipSuccess)
+    fst = side->st;
+  float* fg = (float*)(w + p.o_fg);
+  for (int b = 0; b < B; ++b) {
+    const kvc_fit_in f = feature_fit_in(in, rpt, lens4, b);
+    if ((e = fit_gram_launch(f, (float*)(w + p.o_fit), fg + (int64_t)b * tf::D * tf::D, fst)) != hipSuccess)
+      return hip_fail(e);
+  }
+  if ((e = fit_eig_launch(fg, B, in.r_f, in.r_f, nullptr, u_f, nullptr, fst)) != hipSuccess) return hip_fail(e);
+  if (fst != st && (e = hipEventRecord(side->join, fst)) != hipSuccess) return hip_fail(e);
   const int64_t sx = (int64_t)T * DX;  // batch stride of x
   // Y = A Omega
   GemmArgs g{};
@@ -666,12 +736,8 @@ kvc_status tfit_impl(const kvc_tucker_fit_in& in, float* u_t, float* u_f, float*
   hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((np_ / 4 + 255) / 256)), dim3(256), 0, st, kp, np_, p.ksplit, z,
                      np_);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
-  // U_f: the basis fit of the sequence's (t, l, h) rows
-  for (int b = 0; b < B; ++b) {
-    const kvc_fit_in f = feature_fit_in(in, rpt, lens4, b);
-    s = fit_impl(f, nullptr, u_f + (int64_t)b * tf::D * in.r_f, nullptr, w + p.o_fit, p.fit_bytes, st, nullptr);
-    if (s != KVC_OK) return s;
-  }
+  // the core needs U_f: join the side stream
+  if (fst != st && (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return hip_fail(e);
   // core[b][l][h] = P[b][:, (l, h) block] U_f[b]
   GemmArgs gc{};
   gc.a = z;

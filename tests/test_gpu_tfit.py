@@ -7,7 +7,8 @@ Tolerances (u = 2^-24, the fp32 unit roundoff):
     the products in fp32 (e of a few u) and the Gram and Cholesky factors in fp64, so each column may move by
     about kappa u; a CPU emulation of the same arithmetic (fp32 products, fp64 Gram/Cholesky, two passes)
     moved columns by at most 0.7 kappa(A Omega) u + 1e-6 over kappa from 10 to 1e4 and q = 0..2, the power
-    iterations adding nothing above that.  Allowed per column: (32 kappa + 256) u in the 2-norm;
+    iterations adding nothing above that, and the GPU's own columns moved by about the same (measured: at most
+    0.6 kappa u + 1.2e-6 on these cases).  Allowed per column: (4 kappa + 64) u in the 2-norm;
   * feature factor: the basis fit's bounds (Davis-Kahan per separated column, Eckart-Young for the subspace)
     with delta = 8 u sqrt(n) |G|_F + 400 u lambda_max over the n = seq_len L Hkv rows;
   * core: equal, entry by entry, to the projection of x on the GPU's own factors computed in fp64, within
@@ -51,7 +52,7 @@ def _check_seq(xs, ut, uf, core, omega, r_t, r_f, q, label, feature=True):
     sv = np.linalg.svd(A @ omega, compute_uv=False)
     kappa = sv[0] / sv[-1]
     col = np.linalg.norm(ut - ou, axis=0)
-    tol = (32 * kappa + 256) * U
+    tol = (4 * kappa + 64) * U
     print(f"    {label}: kappa(A omega) {kappa:.3g}, token factor max column error {col.max():.3g} (tol {tol:.3g})",
           flush=True)
     assert col.max() <= tol, (label, col.max(), tol)
