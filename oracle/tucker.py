@@ -23,7 +23,9 @@ with U_t [T, r_t] and U_f [d, r_f] orthonormal and the core G [r_t, r_f, H, L]. 
     oversampling and no closing small SVD): the partial Tucker form depends on U_t only through its span,
     since the core absorbs any rotation of it.  Every orthonormalisation is the Q factor of the QR
     decomposition with a positive diagonal R, which is unique for a full-rank argument.
-    PARITY UNPINNED beyond the invariants, closed forms and bounds of its pins (no page prints a worked example).
+    Pinned (tests/test_oracle_tucker_pins.py) by the uniqueness of that QR factor, exactness on planted rank, Halko,
+    Martinsson and Tropp's deterministic error bound and the power iteration's principal-angle bound; no page
+    prints a worked example to compare against.
 """
 import numpy as np
 
