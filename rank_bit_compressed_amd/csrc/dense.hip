@@ -2,20 +2,23 @@
 //
 // Same decomposition as the compressed kernel: one workgroup (4 waves) per (sequence, kv head,
 // context split), 32-token super-tiles, per-wave online softmax, the four waves combined in LDS at the
-// end, and a merge kernel over the splits.  Per 16-token block, lane (token l%16, group g) loads, for each
-// 32-dim chunk c, its token's dims 32c + 8g .. 32c + 8g + 7 with a 16-byte nontemporal load, so that the four
-// lanes of a token read one contiguous 64-byte run per instruction; the loads run one super-tile ahead of
-// the one computed (the stream is the whole cost, so loads stay in flight during the arithmetic).  Scores
-// S^T = K Q^T on the bf16 MFMA (k-slot 8g + j of chunk c <-> dim 32c + 8g + j); values go through a one-hot
-// bf16 MFMA (a register transpose, exact) and the value product runs on the fp16 MFMA with fp16
-// probabilities; value tile nt holds dims 16 nt .. 16 nt + 15.
+// end, and a merge kernel over the splits.  A super-tile's keys (and values) of one head are 32 rows of
+// D bf16, contiguous within a page, so each wave reads them with 16-byte nontemporal loads in which the 64
+// lanes cover 1 KB of consecutive bytes (one full run of cache lines per instruction: the read pattern
+// the stream probe sustains); it stores them to its own LDS tile (rows padded by 16 bytes, so that the
+// column-wise reads below hit distinct banks) and reads them back in the matrix instructions' operand
+// layout.  The loads run one super-tile ahead of the one computed.  Scores S^T = K Q^T on the bf16 MFMA
+// (k-slot 8g + j of chunk c <-> dim 32c + 8g + j); values go through a one-hot bf16 MFMA (a register
+// transpose, exact) and the value product runs on the fp16 MFMA with fp16 probabilities; value tile nt
+// holds dims 16 nt .. 16 nt + 15.
 #include <math.h>
 
 #include <algorithm>
 
-#include "kvc_common.hpp"
+#include "lds_copy.hpp"
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 namespace kvc {
 
@@ -79,25 +82,47 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseArgs a) {
   const int n_st = (T + 31) / 32;
   const int st_begin = split * a.st_per_split;
   const int st_end = min(n_st, st_begin + a.st_per_split);
-  // this lane's keys and values of super-tile st.  Tokens past the sequence end read the last token's row
-  // instead (real, finite data; their scores are masked, so they get probability 0): the loads are then
-  // unconditional and the compiler can count them, leaving the next super-tile's loads in flight.
-  auto load = [&](int st, bf8 (&kc)[2][QC], bf8 (&vc)[2][QC]) {
+  // Keys and values of super-tile st as whole rows: load instruction i, lane l holds the 16 bytes at
+  // 16 (64 i + l) of the tile, i.e. piece l % PC of row LR i + l / PC.  Rows past the sequence end read
+  // the last token's row instead (real, finite data; their scores are masked, so they get probability 0).
+  constexpr int RB = 2 * D;           // bytes per row
+  constexpr int PC = RB / 16;         // 16-byte pieces per row
+  constexpr int LR = 64 / PC;         // rows per load instruction
+  constexpr int NI = 32 / LR;         // load instructions per super-tile and tensor
+  constexpr int RS = RB + 16;         // LDS row stride
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][2][32 * RS];
+  uint8_t* ktile = tiles[wv][0];
+  uint8_t* vtile = tiles[wv][1];
+  auto load = [&](int st, u4v (&kr)[NI], u4v (&vr)[NI]) {
     const int t0 = st * 32;
     const int page = uniform(a.block_table[(size_t)b * a.max_blocks + t0 / P]);
     const size_t head_base = ((size_t)page * a.Hkv + h) * P + (t0 % P);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int tt = min(16 * blk + n, T - 1 - t0);
-      const size_t row = (head_base + tt) * D + 8 * g;
-      const bf8* kr = (const bf8*)(a.k_pages + row);
-      const bf8* vr = (const bf8*)(a.v_pages + row);
+    for (int i = 0; i < NI; ++i) {
+      const int r = min(LR * i + lane / PC, T - 1 - t0);
+      const size_t off = (head_base + r) * D + 8 * (lane % PC);
+      kr[i] = __builtin_nontemporal_load((const u4v*)(a.k_pages + off));
+      vr[i] = __builtin_nontemporal_load((const u4v*)(a.v_pages + off));
+    }
+  };
+  auto stage = [&](const u4v (&kr)[NI], const u4v (&vr)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int o = (LR * i + lane / PC) * RS + 16 * (lane % PC);
+      *(u4v*)(ktile + o) = kr[i];
+      *(u4v*)(vtile + o) = vr[i];
+    }
+  };
+  // the operands of super-tile st from the tiles: lane (n, g) takes row 16 blk + n, dims 32 c + 8 g .. + 7
+  auto operands = [&](bf8 (&kc)[2][QC], bf8 (&vc)[2][QC]) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
-        kc[blk][c] = __builtin_nontemporal_load(kr + 4 * c);
-        vc[blk][c] = __builtin_nontemporal_load(vr + 4 * c);
+        const int o = (16 * blk + n) * RS + 16 * (4 * c + g);
+        kc[blk][c] = *(const bf8*)(ktile + o);
+        vc[blk][c] = *(const bf8*)(vtile + o);
       }
-    }
   };
   // one super-tile: scores, online softmax, value product
   auto tile = [&](int st, const bf8 (&kcur)[2][QC], const bf8 (&vcur)[2][QC]) {
@@ -152,19 +177,16 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseArgs a) {
       acc[nt] = mfma16x16x32(pop, vt, acc[nt]);
     }
   };
-  bf8 kn[2][QC], vn[2][QC];
+  u4v kn[NI], vn[NI];
   if (st_begin + wv < st_end) load(st_begin + wv, kn, vn);
   for (int st = st_begin + wv; st < st_end; st += 4) {
-    bf8 kcur[2][QC], vcur[2][QC];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        kcur[blk][c] = kn[blk][c];
-        vcur[blk][c] = vn[blk][c];
-      }
+    stage(kn, vn);
     if (st + 4 < st_end) load(st + 4, kn, vn);
+    wave_lds_sync();
+    bf8 kcur[2][QC], vcur[2][QC];
+    operands(kcur, vcur);
     tile(st, kcur, vcur);
+    wave_lds_sync();  // the tile's reads are done before the next super-tile is staged over it
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
