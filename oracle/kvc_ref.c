@@ -29,7 +29,7 @@
  *   is two fp16 values, scale first.  Residual element i of a slot is bits
  *   2(i%4)..2(i%4)+1 of byte i/4.
  *
- *   Shared mode: a record is Lc (P x latent/2 code bytes) then Lm
+ *   Shared mode: a record is Lc (P x latent*latent_bits/8 code bytes) then Lm
  *   (P x latent/G pairs), each padded to 16 bytes.
  *
  *   Uniform rank: every slot of every page holds r_k_cap / r_v_cap, so all
@@ -240,7 +240,9 @@ int kvc_ref_layout_check(const kvc_ref_layout* L) {
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_REF_EINVAL;
   if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_REF_EINVAL;
   if (L->shared) {
-    if (L->n_layers <= 0 || L->latent_bits != 4 || lat_bits(L, 1) != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
+    /* one latent for keys and values: one width (BellowsKV's retention table lists INT4 and INT3 for it) */
+    if (L->n_layers <= 0 || !quant_bits_ok(L->latent_bits) || lat_bits(L, 1) != L->latent_bits || L->variable_rank ||
+        L->r_k_cap != L->r_v_cap)
       return KVC_REF_EINVAL;
   } else if (L->n_layers != 1) {
     return KVC_REF_EINVAL;
@@ -279,7 +281,7 @@ static sections head_sections(const kvc_ref_layout* L, int sum_code_k, int sum_c
 int64_t kvc_ref_page_bytes_uniform(const kvc_ref_layout* L) {
   if (kvc_ref_layout_check(L)) return KVC_REF_EINVAL;
   int64_t P = L->page_size;
-  if (L->shared) return pad16(P * L->r_k_cap / 2) + pad16(P * 4 * ceil_div(L->r_k_cap, L->group));
+  if (L->shared) return pad16(P * L->r_k_cap * L->latent_bits / 8) + pad16(P * 4 * ceil_div(L->r_k_cap, L->group));
   sections S = head_sections(L, (int)(P * code_bytes(L, 0, L->r_k_cap)), (int)(P * code_bytes(L, 1, L->r_v_cap)),
                              (int)(P * meta_bytes(L, 0, L->r_k_cap)), (int)(P * meta_bytes(L, 1, L->r_v_cap)));
   return S.total * L->n_kv_heads;
@@ -442,9 +444,10 @@ int64_t kvc_ref_compress(const kvc_ref_layout* L, int B, int max_T, int max_bloc
       if (L->shared) {
         int lat = L->r_k_cap, G = L->group;
         uint8_t* rec = pool + page_off[p];
-        uint8_t* codes = rec + (int64_t)s * (lat / 2);
-        uint8_t* meta = rec + pad16((int64_t)P * lat / 2) + (int64_t)s * 4 * ceil_div(lat, G);
-        pack_latent(L, 4, lat_k + ((size_t)b * max_T + t) * lat, lat, codes, meta);
+        const int lb = L->latent_bits;
+        uint8_t* codes = rec + (int64_t)s * (lat * lb / 8);
+        uint8_t* meta = rec + pad16((int64_t)P * lat * lb / 8) + (int64_t)s * 4 * ceil_div(lat, G);
+        pack_latent(L, lb, lat_k + ((size_t)b * max_T + t) * lat, lat, codes, meta);
         continue;
       }
       for (int h = 0; h < Hkv; ++h) {
@@ -571,9 +574,10 @@ static void rebuild_token(const kvc_ref_layout* L, int which, int layer, int b, 
   if (L->shared) {
     int lat = L->r_k_cap;
     const uint8_t* rec = pool + page_off[p];
-    const uint8_t* codes = rec + (int64_t)s * (lat / 2);
-    const uint8_t* meta = rec + pad16((int64_t)P * lat / 2) + (int64_t)s * 4 * ceil_div(lat, L->group);
-    unpack_latent(L, 4, codes, meta, lat, lat, c);
+    const int lb = L->latent_bits;
+    const uint8_t* codes = rec + (int64_t)s * (lat * lb / 8);
+    const uint8_t* meta = rec + pad16((int64_t)P * lat * lb / 8) + (int64_t)s * 4 * ceil_div(lat, L->group);
+    unpack_latent(L, lb, codes, meta, lat, lat, c);
     rebuild_shared(w + (size_t)layer * lat * Hkv * d, lat, Hkv * d, h * d, d, c, x);
     return;
   }

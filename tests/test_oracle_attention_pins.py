@@ -298,6 +298,33 @@ def test_pool_holds_the_quantizer_outputs(name, bits):
                 assert meta[g0 // w.group, 0] == S[0] and meta[g0 // w.group, 1] == Z[0]
 
 
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_shared_pool_holds_the_quantizer_outputs(bits):
+    # block-shared records (BellowsKV, "Reading the Retention Table": INT4 and INT3 on the shared latent): slot s
+    # of a page holds latent * b / 8 code bytes (the latent's little-endian bit string) after s such slots, then,
+    # past the 16-byte-padded code section, 4 bytes per group; read here from that description alone
+    w = synth.WORKLOADS["shared_latent_32k"].scaled(B=2, T=300, page_size=64, latent_bits=bits)
+    inp = synth.make_inputs(w, seq_len=[300, 129])
+    pool, page_off, _, _ = oracle_cache(w, inp)
+    bt = np_any(inp["block_table"])
+    lat = np_f32(inp["lat_k"])
+    P, Lt, G = w.page_size, w.r_k, w.group
+    cb = Lt * bits // 8
+    pad = lambda x: (x + 15) // 16 * 16
+    assert np.array_equal(page_off, np.arange(w.n_pages) * (pad(P * cb) + pad(P * 4 * (Lt // G))))
+    for (b, t) in [(0, 0), (0, 299), (1, 128), (1, 63), (0, 64)]:
+        p, sl = int(bt[b, t // P]), t % P
+        rec = int(page_off[p])
+        by = pool[rec + sl * cb: rec + (sl + 1) * cb]
+        codes = (np.unpackbits(by, bitorder="little").reshape(Lt, bits).astype(np.int64) << np.arange(bits)).sum(1)
+        m0 = rec + pad(P * cb) + sl * 4 * (Lt // G)
+        meta = pool[m0: m0 + 4 * (Lt // G)].view(np.uint16).reshape(-1, 2)
+        for g0 in range(0, Lt, G):
+            S, Z, Q = ref.quant_intb(lat[b, t, g0: g0 + G][None], bits)
+            assert np.array_equal(codes[g0: g0 + G], Q[0])
+            assert meta[g0 // G, 0] == S[0] and meta[g0 // G, 1] == Z[0]
+
+
 def test_offsets_are_prefix_sums_and_total_is_closed_form():
     w = synth.WORKLOADS["varrank_paged_32k"].scaled(B=3, T=1000)
     inp = synth.make_inputs(w, seq_len=[1000, 999, 1])
@@ -400,17 +427,19 @@ def test_shared_layers_each_use_their_own_up_projection_and_query(n_layers):
                 assert np.allclose(out[l, b, 4 * h: 4 * h + 4], want, rtol=0, atol=1e-12 * np.abs(want).max())
 
 
-def test_shared_layers_with_embedded_per_layer_bases_equal_per_head_mode():
+@pytest.mark.parametrize("bits", [4, 3, 2])
+def test_shared_layers_with_embedded_per_layer_bases_equal_per_head_mode(bits):
     # two layers, each with its own per-head bases embedded block-diagonally in W[l]: layer l of the shared
-    # decode equals the per-head decode of the same latents with layer l's bases and query
-    wp = synth.WORKLOADS["llama8b_layer_8k"].scaled(T=200, r_k=64, r_v=64, group=64, page_size=64)
+    # decode equals the per-head decode of the same latents with layer l's bases and query, at each code width
+    # (a shared group of 64 coordinates is one head's group, so both modes quantize alike)
+    wp = synth.WORKLOADS["llama8b_layer_8k"].scaled(T=200, r_k=64, r_v=64, group=64, page_size=64, latent_bits=bits)
     per_layer = []
     for l in range(2):
         inp = synth.make_inputs(wp.scaled(seed=100 + l))
         per_layer.append(inp)
     base = per_layer[0]
     lat = base["lat_k"]
-    ws = synth.WORKLOADS["shared_latent_32k"].scaled(B=1, T=200, n_layers=2, page_size=64)
+    ws = synth.WORKLOADS["shared_latent_32k"].scaled(B=1, T=200, n_layers=2, page_size=64, latent_bits=bits)
     Hkv, d = 8, 128
     W = {n: torch.zeros(2, 512, Hkv * d, dtype=torch.bfloat16) for n in ("wk", "wv")}
     for l in range(2):
