@@ -98,7 +98,8 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # and head from the 512-dim latent) and the 128K rotated-residual cache (HBM); the lower-bit codecs; and a layer
 # group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core);
 # the block-shared latent under one eviction decision for its layers (the decision timed on its own).
-OTHER = ("llama8b_layer_8k", "shared_latent_32k", "residual_128k", "varrank_paged_32k_int3", "llama8b_layer_8k_k3v2",
+OTHER = ("llama8b_layer_8k", "shared_latent_32k", "shared_latent_32k_int3", "residual_128k", "varrank_paged_32k_int3",
+         "llama8b_layer_8k_k3v2",
          "tucker_group_32k", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered")
 
 

@@ -64,7 +64,9 @@ static kvc_status check_layout(const kvc_layout* L) {
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_ERR_INVALID_ARG;
   if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_ERR_INVALID_ARG;
   if (L->shared) {
-    if (L->n_layers <= 0 || lat_bits_k(*L) != 4 || lat_bits_v(*L) != 4 || L->variable_rank || L->r_k_cap != L->r_v_cap)
+    // one latent for keys and values: one width (4, or the lower-bit codecs 3 and 2)
+    if (L->n_layers <= 0 || lat_bits_k(*L) == 32 || lat_bits_v(*L) != lat_bits_k(*L) || L->variable_rank ||
+        L->r_k_cap != L->r_v_cap)
       return KVC_ERR_INVALID_ARG;
   } else if (L->n_layers != 1) {
     return KVC_ERR_INVALID_ARG;

@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(PackArgs a, int groups
   if (a.shared) {
     r = a.rk;
     src = a.lat_k + ((size_t)b * a.max_T + t) * r;
-    codes = rec + (int64_t)slot * (r / 2);
-    meta = rec + pad16((int64_t)P * r / 2) + (int64_t)slot * 4 * ceil_div(r, a.G);
+    codes = rec + (int64_t)slot * (r * bits / 8);
+    meta = rec + pad16((int64_t)P * r * bits / 8) + (int64_t)slot * 4 * ceil_div(r, a.G);
   } else {
     const int h = item >> 1, which = item & 1;
     const int rcap = which ? a.rv : a.rk;

@@ -100,8 +100,12 @@ __device__ inline int qfrag_index(int head, int dim) {
 // SPLIT: latent coordinates below SLAT / 2 feed only the keys and the rest only the values (W_k zero on the upper
 // rows, W_v on the lower, as for keys and values with their own token factors): waves 0-1 then do only the key
 // work and waves 2-3 only the value product; their skipped products are exact zeros, so the output is the same.
-template <bool KEEP, bool SPLIT>
+// KB: latent code bits (4; or 3 and 2, whose codes a wave stages token-major and spreads to the INT4 nibble layout)
+template <bool KEEP, bool SPLIT, int KB>
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
+  constexpr int CB = SLAT * KB / 8;  // code bytes per token
+  constexpr int QB = CB / 4;         // a wave's quarter of them
+  constexpr int NCH = QB / 16;       // its 16-byte chunks per token
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr SharedLds LY = shared_lds();
   const int tid = threadIdx.x, lane = tid & 63;
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   for (int k = tid; k < n_tiles; k += 256) {  // page record of each super-tile, its first slot, its keep word
     const int t0 = (st_begin + k) * 32;
     const int page = a.block_table[(size_t)b * a.max_blocks + t0 / P];
-    taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * (SLAT / 2);
+    taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * CB;
     const int wd = t0 >> 5;
     if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
   }
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   float* sp = (float*)(smem + LY.sp);
   _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * SGQ;
 
-  const int64_t meta_base = pad16((int64_t)P * SLAT / 2);
+  const int64_t meta_base = pad16((int64_t)P * CB);
 
   // ---- staging: this wave's part of super-tile k into ring slot k % 4; past the last super-tile the slot gets a
   // copy of the last one, which keeps the number of copies in flight constant.  Always four copy instructions:
@@ -206,13 +210,20 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // resource based at the super-tile's codes: its pairs start meta_base - 256 slot0 bytes further (within the
     // same page record)
     const int64_t at = uniform64(taddr[kk]);
-    const int pairs_at = (int)meta_base - slot0 * (SLAT / 2) + slot0 * mpt;
+    const int pairs_at = (int)meta_base - slot0 * CB + slot0 * mpt;
     const i32x4_t rs = buffer_rsrc(a.pool + at, pairs_at + 32 * mpt);
     const uint32_t dst = raw_lds + (k & 3) * SRAW;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int p = 64 * r + lane;
-      copy16_to_lds(rs, dst + 1024 * r, (p & 31) * (SLAT / 2) + 64 * wv + 16 * (p >> 5));
+      if (KB == 4) {
+        copy16_to_lds(rs, dst + 1024 * r, (p & 31) * CB + QB * wv + 16 * (p >> 5));
+      } else {
+        // token-major: LDS chunk p <- token p / NCH's chunk p % NCH (lanes past 32 NCH repeat the last chunk into
+        // the unused end of the slot, keeping two copy instructions per super-tile)
+        const int pc = min(p, 32 * NCH - 1);
+        copy16_to_lds(rs, dst + 1024 * r, (pc / NCH) * CB + QB * wv + 16 * (pc % NCH));
+      }
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -235,16 +246,31 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   // 8hf + j of the wave's part, the k-slot order of wf) and into fp16 tile vb: chunk c (code dword c, 8
   // coordinates) of token t at byte SCS c + 16 t
   const int gr0 = ((SQC * wv + 64 * hf) >> lg) - g0, gr1 = ((SQC * wv + 64 * hf + 32) >> lg) - g0;
+  // the lane's eight code groups of a staged super-tile as INT4 dwords: group j = coordinates 8 (8hf + j)..
+  // of the wave's quarter of token t
+  auto code_words = [&](const uint8_t* raw, uint32_t (&xs)[8]) {
+    if (KB == 4) {
+      // (dword reads: the compiler merges them, and unlike a vector read of this copy target it then adds no
+      // wait for every copy in flight)
+      const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);       // chunk 2hf: dwords 8hf + 0..3
+      const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xs[j] = c0[j];
+        xs[4 + j] = c1[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = codes8_as_nibbles<KB>(raw + QB * t, KB * (8 * hf + j));
+    }
+  };
   auto dequant = [&](int k, h8 (&bf)[SNJ], int vb) {
     const uint8_t* raw = raw_w + (k & 3) * SRAW;
-    // (dword reads: the compiler merges them, and unlike a vector read of this copy target it then adds no wait
-    // for every copy in flight)
-    const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);       // chunk 2hf: dwords 8hf + 0..3
-    const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
     const uint32_t z0 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr1));
     uint8_t* dst = vt_w + vb * SVT + SCS * 8 * hf + 16 * t;
-    const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    uint32_t xs[8];
+    code_words(raw, xs);
 #pragma unroll
     for (int j = 0; j < SNJ; ++j) {
       bf[j] = dequant_int4x8(xs[j], j < 4 ? z0 : z1);
@@ -271,9 +297,8 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     // sources of super-tile k + 1's dequantization (dword reads: see dequant)
     const uint8_t* rawn = raw_w + ((k + 1) & 3) * SRAW;
-    const uint32_t* c0 = (const uint32_t*)(rawn + (64 * hf + t) * 16);
-    const uint32_t* c1 = (const uint32_t*)(rawn + (64 * hf + 32 + t) * 16);
-    const uint32_t xs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    uint32_t xs[8];
+    code_words(rawn, xs);
     const uint32_t z0 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr1));
     uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + SCS * 8 * hf + 16 * t;
@@ -479,12 +504,36 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
 int shared_max_tiles_per_split() { return SMAX_TILES; }
 
 bool shared_supported(const kvc_layout& L) {
+  const int kb = lat_bits_k(L);
   return L.shared && L.head_dim == SD && L.r_k_cap == SLAT && L.n_q_heads == SGQ * L.n_kv_heads &&
-         lat_bits_k(L) == 4 && lat_bits_v(L) == 4 && L.group >= 32 && L.group <= SLAT && (L.group & (L.group - 1)) == 0;
+         (kb == 4 || kb == 3 || kb == 2) && lat_bits_v(L) == kb && L.group >= 32 && L.group <= SLAT &&
+         (L.group & (L.group - 1)) == 0;
 }
 
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {
   return (size_t)L.n_layers * L.n_kv_heads * B * n_splits * (2 * SGQ + SGQ * SLAT) * sizeof(float);
+}
+
+template <bool KEEP, bool SPLIT, int KB>
+static hipError_t launch_shared_one(int grid, int lds, hipStream_t st, const DecodeSharedArgs& a) {
+  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB>;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB>), dim3(grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <bool KEEP, bool SPLIT>
+static hipError_t launch_shared_bits(int kb, int grid, int lds, hipStream_t st, const DecodeSharedArgs& a) {
+  if (kb == 3) return launch_shared_one<KEEP, SPLIT, 3>(grid, lds, st, a);
+  if (kb == 2) return launch_shared_one<KEEP, SPLIT, 2>(grid, lds, st, a);
+  return launch_shared_one<KEEP, SPLIT, 4>(grid, lds, st, a);
+}
+
+static hipError_t launch_shared_variant(bool keep, bool split, int kb, int grid, int lds, hipStream_t st,
+                                        const DecodeSharedArgs& a) {
+  if (keep) return split ? launch_shared_bits<true, true>(kb, grid, lds, st, a) : launch_shared_bits<true, false>(kb, grid, lds, st, a);
+  return split ? launch_shared_bits<false, true>(kb, grid, lds, st, a) : launch_shared_bits<false, false>(kb, grid, lds, st, a);
 }
 
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
@@ -499,24 +548,11 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
   const int lds = shared_lds().total;
   const bool split = in.kv_split == SLAT / 2;
-  const void* kern = in.keep_mask ? (split ? (const void*)decode_shared_kernel<true, true>
-                                           : (const void*)decode_shared_kernel<true, false>)
-                                  : (split ? (const void*)decode_shared_kernel<false, true>
-                                           : (const void*)decode_shared_kernel<false, false>);
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
+  const int kb = lat_bits_k(L);
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
-  e = mark(g_marks.begin, st);
+  hipError_t e = mark(g_marks.begin, st);
   if (e != hipSuccess) return e;
-  if (in.keep_mask && split)
-    hipLaunchKernelGGL((decode_shared_kernel<true, true>), dim3(grid), dim3(256), lds, st, a);
-  else if (in.keep_mask)
-    hipLaunchKernelGGL((decode_shared_kernel<true, false>), dim3(grid), dim3(256), lds, st, a);
-  else if (split)
-    hipLaunchKernelGGL((decode_shared_kernel<false, true>), dim3(grid), dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL((decode_shared_kernel<false, false>), dim3(grid), dim3(256), lds, st, a);
-  e = hipGetLastError();
+  e = launch_shared_variant(in.keep_mask != nullptr, split, kb, grid, lds, st, a);
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,

@@ -71,7 +71,8 @@ __host__ __device__ inline int slot_meta_bytes(int latent_bits, int r, int G) {
 // Uniform-rank page record size (per-head or shared mode).
 __host__ __device__ inline int64_t uniform_page_bytes(const kvc_layout& L) {
   const int P = L.page_size;
-  if (L.shared) return pad16((int64_t)P * L.r_k_cap / 2) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
+  if (L.shared)
+    return pad16((int64_t)P * L.r_k_cap * lat_bits_k(L) / 8) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
   HeadSections S = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
                                  (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
                                  (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),

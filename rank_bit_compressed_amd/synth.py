@@ -148,6 +148,11 @@ WORKLOADS = {
                                        head_dim=128, r_k=64, r_v=64, group=32, latent_bits=3,
                                        rope_theta=500000.0, variable_rank=True, rank_choices=(8, 16, 32, 64),
                                        rank_probs=(0.4, 0.3, 0.2, 0.1), shuffle_pages=True, seed=13),
+    # the block-shared latent in INT3, the BellowsKV retention table's INT3 row
+    "shared_latent_32k_int3": Workload("shared_latent_32k_int3", B=4, T=32768, n_q_heads=32, n_kv_heads=8,
+                                       head_dim=128, r_k=512, r_v=512, group=64, latent_bits=3, shared=True,
+                                       n_layers=4, rope_theta=500000.0, latent_decay=0.0,
+                                       w_std=1.0 / math.sqrt(512.0), seed=14),
     "llama8b_layer_8k_k3v2": Workload("llama8b_layer_8k_k3v2", B=1, T=8192, n_q_heads=32, n_kv_heads=8,
                                       head_dim=128, r_k=48, r_v=64, group=32, latent_bits=3, latent_bits_v=2,
                                       rope_theta=500000.0, seed=12),

@@ -75,7 +75,7 @@ def test_decode_path_selection():
             "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
             "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4,
             "tucker_group_32k": kvc.PATH_SHARED, "shared_latent_32k_evict30": kvc.PATH_SHARED,
-            "shared_latent_32k_evict30_clustered": kvc.PATH_SHARED}
+            "shared_latent_32k_evict30_clustered": kvc.PATH_SHARED, "shared_latent_32k_int3": kvc.PATH_SHARED}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
@@ -159,8 +159,8 @@ def test_low_bit_layouts_check_and_route():
         assert kvc.layout_check(kvc.make_layout(**base.scaled(**kw).layout_kwargs())) == want, kw
     bad_var = synth.WORKLOADS["varrank_paged_32k"].scaled(latent_bits=3, latent_bits_v=2)
     assert kvc.layout_check(kvc.make_layout(**bad_var.layout_kwargs())) == -1
-    shared3 = synth.WORKLOADS["shared_latent_32k"].scaled(latent_bits=3)
-    assert kvc.layout_check(kvc.make_layout(**shared3.layout_kwargs())) == -1
+    shared32 = synth.WORKLOADS["shared_latent_32k"].scaled(latent_bits=3, latent_bits_v=2)  # one latent: one width
+    assert kvc.layout_check(kvc.make_layout(**shared32.layout_kwargs())) == -1
     # pool sizes follow r * b / 8 code bytes: K 48 x 3 / 8 = 18, V 64 x 2 / 8 = 16 per slot
     L = kvc.make_layout(**base.scaled(latent_bits=3, latent_bits_v=2).layout_kwargs())
     assert kvc.pool_bytes_max(L, 10) == 10 * 8 * 256 * (18 + 16 + 8 + 8)
@@ -293,3 +293,15 @@ def test_tucker_fit_rejects_bad_sizes_before_launch():
     # null inputs with a valid geometry: rejected before any device call
     assert kvc.lib().kvc_tucker_fit(C.byref(fin()), None, None, None, None, None, 0, None) == -1
     assert kvc.lib().kvc_tucker_fit(None, None, None, None, None, None, 0, None) == -1
+
+
+def test_shared_layout_widths():
+    # one latent for keys and values: one width, 4, 3 or 2 bits
+    for bits, bits_v, want in ((4, 0, 0), (3, 0, 0), (2, 0, 0), (3, 3, 0), (3, 2, -1), (32, 0, -1)):
+        L = kvc.make_layout(**synth.WORKLOADS["shared_latent_32k"].scaled(latent_bits=bits, latent_bits_v=bits_v)
+                            .layout_kwargs())
+        assert kvc.layout_check(L) == want, (bits, bits_v)
+    L = kvc.make_layout(**synth.WORKLOADS["shared_latent_32k_int3"].layout_kwargs())
+    w = synth.WORKLOADS["shared_latent_32k_int3"]
+    # a page of 256 slots: 512 x 3 / 8 = 192 code bytes, then 512 / 64 = 8 (scale, zero) pairs of 4 bytes per slot
+    assert kvc.pool_bytes_max(L, w.n_pages) == w.n_pages * (256 * 192 + 256 * 8 * 4)

@@ -19,6 +19,9 @@ CASES = [
     ("llama8b_layer_8k", dict(T=600, latent_bits=3, latent_bits_v=2), None),
     ("varrank_paged_32k", dict(B=3, T=2000, latent_bits=2), [2000, 1999, 33]),
     ("residual_128k", dict(B=2, T=700, latent_bits=3), [700, 512]),
+    # the lower-bit codecs on the block-shared latent (one width for the latent)
+    ("shared_latent_32k", dict(B=2, T=600, latent_bits=3), [600, 1]),
+    ("shared_latent_32k", dict(B=2, T=300, page_size=64, latent_bits=2), [300, 65]),
 ]
 
 

@@ -36,6 +36,10 @@ CASES = [
     ("llama8b_layer_8k", dict(T=700, r_k=40, r_v=40, latent_bits=3), None),
     ("llama8b_layer_8k", dict(B=2, T=500, r_k=40, r_v=40, latent_bits=3, latent_bits_v=2), [500, 77]),
     ("varrank_paged_32k", dict(B=2, T=800, r_k=48, r_v=48, rank_choices=(8, 16, 32, 48), latent_bits=2), [800, 301]),
+    # lower-bit codecs on the block-shared latent: INT3 (4 layers, ragged tails) and INT2 (2 layers, pages of 64)
+    ("shared_latent_32k", dict(B=2, T=600, latent_bits=3), [600, 33]),
+    ("shared_latent_32k", dict(B=1, T=300, n_layers=2, page_size=64, latent_bits=2), None),
+    ("shared_latent_32k", dict(B=2, T=500, group=128, latent_bits=3), [500, 1]),
 ]
 
 

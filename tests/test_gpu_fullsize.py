@@ -80,6 +80,13 @@ def test_fullsize_shared_latent_32k():
     _check(w, inp, [2], [5], compare_whole_pool=True)
 
 
+def test_fullsize_shared_latent_32k_int3():
+    # the 4 x 32K block-shared latent in INT3 (BellowsKV's INT3 row)
+    w = synth.WORKLOADS["shared_latent_32k_int3"]
+    inp = synth.make_inputs(w, device="cuda")
+    _check(w, inp, [1], [3], compare_whole_pool=True)
+
+
 def test_fullsize_residual_128k():
     w = synth.WORKLOADS["residual_128k"]
     inp = synth.make_inputs(w, device="cuda")
