@@ -388,7 +388,8 @@ def clock_mhz(torch, dev) -> float:
 
 def step_percentiles(torch, plan, dev, n=100) -> dict:
     """p10 / median / p90 in ms over n steps, warm (one cache, back to back, so its 126 MB can stay in the 256 MB
-    last-level cache) and cold (1 GiB written before each step, outside the events).  "kernel": the attention
+    last-level cache) and cold (1 GiB written before each step, outside the events), each after 0.1 s of
+    untimed steps (the clock drops while the GPU idles, e.g. during the single-wave clock probe before).  "kernel": the attention
     kernel alone, from the library's events around its launch; "step": kernel + merge from events around the
     call (cold only: back to back, such events would also time host enqueue gaps); "step_mean": warm steps
     between two events around all n."""
@@ -404,9 +405,18 @@ def step_percentiles(torch, plan, dev, n=100) -> dict:
             b.record()
         return e
 
+    def settle():
+        # the clock falls while the GPU idles (after a probe, between samples): untimed steps first
+        t = time.perf_counter()
+        while time.perf_counter() - t < 0.1:
+            for _ in range(16):
+                plan()
+            torch.cuda.synchronize()
+
     kev, sev, blk = evs(n), evs(n), evs(1)[0]
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    settle()
     blk[0].record()
     for i in range(n):
         plan(kev[i])
@@ -415,6 +425,7 @@ def step_percentiles(torch, plan, dev, n=100) -> dict:
     torch.cuda.synchronize()
     res = {"n": n, "warm": {"kernel": pct([a.elapsed_time(b) for a, b in kev]),
                             "step_mean": round(blk[0].elapsed_time(blk[1]) / n, 5), "clock_mhz_after": clk_warm}}
+    settle()
     for i in range(n):
         flush.fill_(float(i))
         sev[i][0].record()
