@@ -109,3 +109,141 @@ def test_masked_attention_single_and_no_token():
     none[1] = one[1]
     z = _dec(w, inp, cache, keep=none)
     assert np.all(z[:, 0] == 0) and np.allclose(z[:, 1], a[:, 1], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- compaction of the evicted tokens
+
+def _mask_of(kept):
+    B, n = kept.shape
+    words = -(-n // 32)
+    k = np.zeros((B, words * 32), bool)
+    k[:, :n] = kept
+    return (k.reshape(B, words, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+
+
+def test_compact_slots_hand_worked():
+    # tile 0 opens at block 0; 130 is in block 4, four blocks on, so it opens tile 1 (slots 32..); 200 (block 6)
+    # joins it; 500 (block 15) opens tile 2 at slot 64
+    s = E.compact_slots([0, 1, 2, 130, 131, 200, 500])
+    assert s == [0, 1, 2] + [-1] * 29 + [130, 131, 200] + [-1] * 29 + [500]
+    assert E.compact_slots([0, 127]) == [0, 127]                    # block 3: within the span
+    assert E.compact_slots([0, 128]) == [0] + [-1] * 31 + [128]     # block 4: a new tile
+    assert E.compact_slots(range(40)) == list(range(40))             # a full tile closes with no empty slot
+    assert E.compact_slots([31, 32, 159]) == [31, 32] + [-1] * 30 + [159]   # base is the first token's block
+    assert E.compact_slots([]) == []
+
+
+@pytest.mark.parametrize("density,cluster", [(0.3, 0), (0.02, 0), (0.9, 0), (0.3, 256), (1.0, 0)])
+def test_compact_slots_invariants(density, cluster):
+    # what the layout rule fixes, checked on the result: every kept token once, in increasing position; tiles of
+    # 32 slots whose tokens lie within SPAN blocks of the first token's block; empty slots only after a tile's last
+    # token; a tile closes early only when the next token is out of its span; length at most the sequence's
+    rng = np.random.default_rng(int(density * 100) + cluster)
+    for T in (1, 31, 33, 700, 5000):
+        if cluster:
+            runs = rng.random(-(-T // cluster)) < density
+            kept = np.repeat(runs, cluster)[:T]
+        else:
+            kept = rng.random(T) < density
+        pos = np.nonzero(kept)[0]
+        s = np.array(E.compact_slots(pos), np.int64)
+        assert np.array_equal(s[s >= 0], pos)
+        assert len(s) <= T and (len(s) == 0 or s[-1] >= 0)
+        tiles = [s[i: i + 32] for i in range(0, len(s), 32)]
+        for i, t in enumerate(tiles):
+            tok = t[t >= 0]
+            assert t[0] >= 0 and np.array_equal(t[: len(tok)], tok)          # tokens first, then empty slots
+            base = t[0] // 32
+            assert np.all(tok // 32 - base < E.SPAN)
+            if i + 1 < len(tiles) and len(tok) < 32:
+                assert tiles[i + 1][0] // 32 - base >= E.SPAN
+
+
+def _slot_latent(pool, rec, sl, P, lat_n, G, bits):
+    """The dequantized latent in slot sl of the record at rec, read from the format description alone: code
+    section of P slots of lat_n * bits / 8 bytes (little-endian bit strings), padded to 16, then P slots of
+    (scale, zero) fp16 pairs, one per group."""
+    cb = lat_n * bits // 8
+    by = pool[rec + sl * cb: rec + (sl + 1) * cb]
+    codes = (np.unpackbits(by, bitorder="little").reshape(lat_n, bits).astype(np.int64) << np.arange(bits)).sum(1)
+    m0 = rec + (P * cb + 15) // 16 * 16 + sl * 4 * (lat_n // G)
+    meta = pool[m0: m0 + 4 * (lat_n // G)].view(np.float16).reshape(-1, 2).astype(np.float64)
+    return codes * np.repeat(meta[:, 0], G) + np.repeat(meta[:, 1], G), by, pool[m0: m0 + 4 * (lat_n // G)]
+
+
+def _compact_case(bits=4, seed=3):
+    w = synth.WORKLOADS["shared_latent_32k"].scaled(B=2, T=700, n_layers=2, page_size=64, latent_bits=bits,
+                                                     shuffle_pages=True)
+    seq = [700, 333]
+    inp = synth.make_inputs(w, seq_len=seq)
+    cache = oracle_cache(w, inp)
+    rng = np.random.default_rng(seed)
+    kept = rng.random((w.B, w.T)) < 0.3
+    kept[0, 200:330] = False                       # a gap of four blocks: tiles close early
+    keep = _mask_of(kept)
+    obt = rng.permutation(w.n_pages).astype(np.int32).reshape(w.B, -1)
+    rec = cache[1][1] - cache[1][0]
+    out0 = np.full(w.n_pages * rec, 0xAB, np.uint8)
+    res = E.compact(512, bits, w.group, w.page_size, inp["block_table"].numpy(), seq, keep, cache[0], cache[1], obt,
+                    np.arange(w.n_pages, dtype=np.int64) * rec, out0)
+    return w, inp, cache, seq, kept, keep, obt, rec, out0, res
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_compacted_records_hold_the_source_records(bits):
+    w, inp, cache, seq, kept, keep, obt, rec, out0, (pool2, tok_pos, out_len) = _compact_case(bits)
+    P, bt = w.page_size, inp["block_table"].numpy()
+    lat = np_f32(inp["lat_k"])
+    for b in range(w.B):
+        pos = np.nonzero(kept[b, :seq[b]])[0]
+        assert np.array_equal(tok_pos[b, :out_len[b]], E.compact_slots(pos))
+        assert np.all(tok_pos[b, out_len[b]:] == -1)
+        used_pages = -(-int(out_len[b]) // P)
+        for i in range(obt.shape[1]):
+            r = int(obt[b, i]) * rec
+            if i >= used_pages:                     # pages past the compacted length are left as they were
+                assert np.all(pool2[r: r + rec] == 0xAB)
+                continue
+            for s in range(P):
+                p = tok_pos[b, i * P + s]
+                got, by, meta = _slot_latent(pool2, r, s, P, 512, w.group, bits)
+                if p < 0:
+                    assert not by.any() and not meta.any()
+                    continue
+                src = int(cache[1][int(bt[b, p // P])])
+                want, by0, meta0 = _slot_latent(cache[0], src, p % P, P, 512, w.group, bits)
+                assert np.array_equal(by, by0) and np.array_equal(meta, meta0)
+                # and the bytes are the quantizer's outputs for that token's latent
+                for g0 in (0, 256):
+                    S, Z, Q = ref.quant_intb(lat[b, p, g0: g0 + w.group][None], bits)
+                    deq = Q[0] * ref.f16_to_f64(int(S[0])) + ref.f16_to_f64(int(Z[0]))
+                    assert np.array_equal(got[g0: g0 + w.group], deq)
+
+
+def test_compacted_cache_attention_is_the_masked_attention():
+    # attention over the compacted cache, computed in numpy from the compacted records and the recorded positions
+    # (keys W_k[l]^T c rotated at the slot's source position, the query at its own), equals the oracle's attention
+    # over the source cache under the keep mask
+    from tests.test_oracle_attention_pins import rope_complex
+    from tests.helpers import sdpa64
+    w, inp, cache, seq, kept, keep, obt, rec, out0, (pool2, tok_pos, out_len) = _compact_case(4, seed=9)
+    pool, page_off, tok_rank, tok_off = cache
+    want = ref.decode_attn(layout(w), np_any(inp["block_table"]), np.asarray(seq, np.int32), np_any(inp["q_pos"]),
+                           pool, page_off, tok_rank, tok_off, np_f32(inp["q"]), np_u16(inp["wk"]), np_u16(inp["wv"]),
+                           keep=keep)
+    Wk = inp["wk"].double().numpy(); Wv = inp["wv"].double().numpy()
+    q = np_f32(inp["q"])
+    P = w.page_size
+    for b in range(w.B):
+        slots = [(i, int(p)) for i, p in enumerate(tok_pos[b, :out_len[b]]) if p >= 0]
+        c = np.stack([_slot_latent(pool2, int(obt[b, i // P]) * rec, i % P, P, 512, w.group, 4)[0] for i, _ in slots])
+        pos = np.array([p for _, p in slots])
+        qp = int(inp["q_pos"][b])
+        for l in range(w.n_layers):
+            for h in (0, 3, 7):
+                k = c @ Wk[l][:, 128 * h: 128 * h + 128]
+                v = c @ Wv[l][:, 128 * h: 128 * h + 128]
+                got = sdpa64(rope_complex(q[l, b, 4 * h: 4 * h + 4], qp, w.rope_theta),
+                             rope_complex(k, pos, w.rope_theta), v)
+                assert np.allclose(got, want[l, b, 4 * h: 4 * h + 4], rtol=0,
+                                   atol=1e-11 * np.abs(got).max()), (b, l, h)
