@@ -97,10 +97,12 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # a latency figure), the block-shared latent (bound by the matrix cores: the key up-projection of every layer
 # and head from the 512-dim latent) and the 128K rotated-residual cache (HBM); the lower-bit codecs; and a layer
 # group in partial Tucker form (the block-shared kernel over per-sequence up-projections expanded from the core);
-# the block-shared latent under one eviction decision for its layers (the decision timed on its own).
+# the block-shared latent under one eviction decision for its layers (the decision timed on its own), masked in
+# place or compacted out of the pages (the compaction timed on its own).
 OTHER = ("llama8b_layer_8k", "shared_latent_32k", "shared_latent_32k_int3", "residual_128k", "varrank_paged_32k_int3",
          "llama8b_layer_8k_k3v2",
-         "tucker_group_32k", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered")
+         "tucker_group_32k", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered",
+         "shared_latent_32k_evict30_compact")
 
 
 def decode_flops(w, ranks=None) -> int:
@@ -119,14 +121,14 @@ def decode_flops(w, ranks=None) -> int:
     return n_tok * (2 * w.head_dim * w.r_k * w.n_kv_heads + 2 * w.r_v * w.n_q_heads) + score
 
 
-def other_workloads(steps: int, warmup: int, peaks: dict) -> dict:
+def other_workloads(steps: int, warmup: int, peaks: dict, names=OTHER) -> dict:
     """Each other workload at its full size: median kernel time (library events around the attention
     kernel), wall time per call, and the figure of its own bound."""
     import torch
     from rank_bit_compressed_amd import accounting, kvc, synth
 
     res = {}
-    for name in OTHER:
+    for name in names:
         w = synth.WORKLOADS[name]
         inp = synth.make_inputs(w, device="cuda")
         L = kvc.make_layout(**w.layout_kwargs())
@@ -161,8 +163,29 @@ def other_workloads(steps: int, warmup: int, peaks: dict) -> dict:
             kept = int(sum(bin(x & 0xFFFFFFFF).count("1") for x in words))
             extra = {"evict_select_ms_median": round(sorted(times)[2], 5), "kept_fraction": round(kept / (w.B * w.T), 4),
                      "empty_super_tile_fraction": round(sum(1 for x in words if x == 0) / len(words), 4)}
-        plan = kvc.DecodePlan(L, cache, inp["block_table"], inp["seq_len"], inp["q"], inp["wk"], inp["wv"], w.T,
-                              q_pos=inp["q_pos"], keep_mask=keep, kv_split=w.tucker[0] if w.tucker else 0)
+        dcache, bt, sl, tok_pos, max_T = cache, inp["block_table"], inp["seq_len"], None, w.T
+        if w.evict_compact:  # kept tokens moved into new pages (prefill side; timed on its own)
+            rec = int(cache.page_off[1].item() - cache.page_off[0].item())
+            dcache = kvc.DeviceCache(L, torch.zeros_like(cache.pool), torch.arange(w.n_pages, dtype=torch.int64,
+                                     device="cuda") * rec, None, None, torch.zeros(2, dtype=torch.int64, device="cuda"),
+                                     w.n_pages)
+            bt = inp["block_table"].flip(1).contiguous()
+            xe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            for _ in range(5):
+                xe[0].record()
+                sl, tok_pos = kvc.evict_compact(L, cache, dcache, inp["block_table"], inp["seq_len"], keep, bt)
+                xe[1].record()
+                torch.cuda.synchronize()
+                times.append(xe[0].elapsed_time(xe[1]))
+            extra["evict_compact_ms_median"] = round(sorted(times)[2], 5)
+            extra["slots_fraction"] = round(int(sl.sum().item()) / (w.B * w.T), 4)
+            max_T = max(1, int(sl.max().item()))  # the compacted lengths size the decode's grid
+            keep = None
+            del cache
+            cache = dcache
+        plan = kvc.DecodePlan(L, dcache, bt, sl, inp["q"], inp["wk"], inp["wv"], max_T, q_pos=inp["q_pos"],
+                              keep_mask=keep, kv_split=w.tucker[0] if w.tucker else 0, tok_pos=tok_pos)
         for k in ("lat_k", "lat_v", "res_k", "res_v"):
             inp[k] = None
         n = max(20, steps // 10)
@@ -185,6 +208,8 @@ def other_workloads(steps: int, warmup: int, peaks: dict) -> dict:
         flops = decode_flops(w, inp["ranks"])
         if w.evict_ratio:  # attention runs over the kept tokens only (every token's latent is still read)
             flops = int(round(flops * extra["kept_fraction"]))
+        if w.evict_compact:  # ... and only the compacted slots are read
+            nbytes = int(round(acct["stream"] * extra["slots_fraction"])) + acct["tables"]
         path = {kvc.PATH_HEAD: "general per-head kernel", kvc.PATH_INT4: "INT4 kernel",
                 kvc.PATH_SHARED: "block-shared kernel", kvc.PATH_RES: "INT4 residual kernel"}[kvc.decode_path(L)]
         r = {"kernel": path, "kernel_ms_median": round(k_ms, 5), "ms_per_call": round(wall_ms, 5),
@@ -201,7 +226,7 @@ def other_workloads(steps: int, warmup: int, peaks: dict) -> dict:
             r["frac_of_hbm_peak"] = round(r["hbm_gbs"] / HBM_PEAK_GBS, 4)
             r["frac_of_measured_hbm"] = round(r["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
         res[name] = r
-        del plan, cache, inp
+        del plan, cache, dcache, inp
         torch.cuda.empty_cache()
     return res
 
@@ -466,7 +491,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads' figures")
-    ap.add_argument("--only", choices=["tucker_fit_group_32k"], help="run only this prefill-side figure and print it")
+    ap.add_argument("--only", choices=["tucker_fit_group_32k", *OTHER],
+                    help="run only this figure (the Tucker fit or one of the other decode workloads) and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path here "
@@ -478,6 +504,10 @@ def main():
 
     if args.only == "tucker_fit_group_32k":
         print(json.dumps({"workload": args.only, **tucker_fit_workload(args.steps)}), flush=True)
+        return
+    if args.only:
+        print(json.dumps({"workload": args.only, **other_workloads(args.steps, args.warmup, measured_peaks(torch, "cuda"),
+                                                                    (args.only,))[args.only]}), flush=True)
         return
     w = synth.WORKLOADS[WORKLOAD]
     dev = "cuda"

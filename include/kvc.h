@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 7
+#define KVC_ABI_VERSION 8
 
 typedef enum {
   KVC_OK = 0,
@@ -174,6 +174,15 @@ typedef struct {
                                  /*   with their own token factors, kvc_tucker_expand).  The      */
                                  /*   kernel then skips those zero products; the output is that   */
                                  /*   of the full product.  Per-head mode: 0                      */
+  const int32_t* tok_pos;        /* shared mode, optional (ABI version 8): [B][max_blocks *       */
+                                 /*   page_size] source position of the token in each slot of a   */
+                                 /*   compacted cache (kvc_evict_compact), -1 for a slot with no  */
+                                 /*   token.  Keys are rotated at these positions and slots of -1 */
+                                 /*   take no part.  Within each 32-slot tile the tokens must lie */
+                                 /*   within 4 blocks of 32 positions of the tile's first slot's   */
+                                 /*   block (the layout kvc_evict_compact writes; other tokens are */
+                                 /*   ignored).  Requires q_pos and no keep_mask.  NULL: slot t   */
+                                 /*   holds position t.  4-byte aligned                           */
 } kvc_decode_in;
 
 /* Inputs of kvc_dense_decode_attn: plain attention over a paged bf16 cache. */
@@ -470,6 +479,35 @@ typedef struct {
  * One workgroup per sequence; deterministic; asynchronous on stream.  INVALID_ARG for bad sizes, a ratio
  * outside (0, 1] or null pointers, MISALIGNED for pointers not 4-byte aligned. */
 kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream);
+
+/* Inputs of kvc_evict_compact (device memory unless noted). */
+typedef struct {
+  int32_t B, max_blocks;         /* sequences; width of both block tables (host values)          */
+  const int32_t* block_table;    /* [B][max_blocks] pages of the source cache                    */
+  const int32_t* seq_len;        /* [B] tokens per source sequence, 0..max_blocks * page_size    */
+  const uint32_t* keep_mask;     /* [B][keep_words], as kvc_evict_select writes it               */
+  int32_t keep_words;            /* words per sequence of keep_mask (host value, >= 1)           */
+  const int32_t* out_block_table;/* [B][max_blocks] pages of the destination cache, distinct      */
+} kvc_compact_in;
+
+/* Compaction of the evicted tokens out of a block-shared cache ("BellowsKV" page, "Three Measurements, Three
+ * Operators": the one decision is applied to the shared latent, so evicted tokens leave the cache and a decode
+ * reads and computes only the kept ones).  Sequence b's kept tokens (bit set, position below seq_len[b]) move, in
+ * increasing position, into consecutive slots of the pages out_block_table[b][0..], each with its slot bytes
+ * (codes and scale/zero pairs) unchanged.  Slots come in tiles of 32; a tile holds only tokens within 4 blocks of
+ * 32 positions of its first token's block: a token starts a new tile when the current one is full or its block
+ * is 4 or more past the first token's, and the slots a closed tile leaves over hold no token (zero bytes).
+ * Writes out_seq_len[b] (slots up to the last token, at most seq_len[b]), tok_pos[b][0 .. max_blocks *
+ * page_size) (source position of each slot, -1 where there is no token: the table kvc_decode_attn takes) and
+ * every slot of the destination pages below out_seq_len[b] (other pages are left as they were).  dst->page_off
+ * holds the destination record offsets (multiples of 16; the same record layout and size as the source).
+ * Decoding the result with tok_pos and the sequence's own q_pos gives the attention over the kept tokens that
+ * the keep mask gives on the source cache.  Two launches (a scan per sequence, then a copy per destination
+ * page); deterministic; asynchronous on stream.  INVALID_ARG for a per-head layout, null pointers or sizes out
+ * of range (max_blocks * page_size above 262144), UNSUPPORTED for a layout the block-shared decode does not
+ * serve, MISALIGNED for pointers not 16-byte aligned. */
+kvc_status kvc_evict_compact(const kvc_layout* layout, const kvc_cache* src, const kvc_cache* dst,
+                             const kvc_compact_in* in, int32_t* out_seq_len, int32_t* tok_pos, void* stream);
 
 /* Flags of kvc_decode_check (or-ed). */
 #define KVC_BAD_SEQ_LEN 1  /* a seq_len outside 1..min(max_T, max_blocks * page_size)              */

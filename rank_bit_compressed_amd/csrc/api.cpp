@@ -40,6 +40,8 @@ kvc_status tucker_impl(const kvc_tucker_in& in, uint16_t* w, float* w32, hipStre
 kvc_status tfit_impl(const kvc_tucker_fit_in& in, float* u_t, float* u_f, float* core, int32_t* info, void* ws,
                      size_t ws_bytes, hipStream_t st, size_t* bytes_out);
 kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st);
+kvc_status compact_impl(const kvc_layout& L, const kvc_cache& src, const kvc_cache& dst, const kvc_compact_in& in,
+                        int32_t* out_len, int32_t* tok_pos, hipStream_t st);
 kvc_status check_impl(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, int32_t* flags,
                       hipStream_t st);
 kvc_status dense_impl(const kvc_dense_in& in, float* out, void* ws, size_t ws_bytes, hipStream_t st,
@@ -162,6 +164,8 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
   if (in->keep_mask && (!L.shared || in->keep_words < 1)) return KVC_ERR_INVALID_ARG;
   if (in->kv_split && (!L.shared || 2 * in->kv_split != L.r_k_cap)) return KVC_ERR_INVALID_ARG;
   if (in->keep_mask && ((uintptr_t)in->keep_mask & 3)) return KVC_ERR_MISALIGNED;
+  if (in->tok_pos && (!L.shared || in->keep_mask || !in->q_pos)) return KVC_ERR_INVALID_ARG;
+  if (in->tok_pos && ((uintptr_t)in->tok_pos & 3)) return KVC_ERR_MISALIGNED;
   if ((int64_t)in->max_blocks * L.page_size < in->max_T) return KVC_ERR_INVALID_ARG;
   if (in->q_dtype != KVC_F32 && in->q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;
   if (!cache->pool || !cache->page_off || cache->n_pages <= 0) return KVC_ERR_INVALID_ARG;
@@ -274,6 +278,14 @@ kvc_status kvc_tucker_fit(const kvc_tucker_fit_in* in, float* u_t, float* u_f, f
 kvc_status kvc_evict_select(const kvc_evict_in* in, uint32_t* keep_mask, void* stream) {
   if (!in) return KVC_ERR_INVALID_ARG;
   return evict_impl(*in, keep_mask, (hipStream_t)stream);
+}
+
+kvc_status kvc_evict_compact(const kvc_layout* layout, const kvc_cache* src, const kvc_cache* dst,
+                             const kvc_compact_in* in, int32_t* out_seq_len, int32_t* tok_pos, void* stream) {
+  kvc_status s = check_layout(layout);
+  if (s) return s;
+  if (!src || !dst || !in) return KVC_ERR_INVALID_ARG;
+  return compact_impl(*layout, *src, *dst, *in, out_seq_len, tok_pos, (hipStream_t)stream);
 }
 
 kvc_status kvc_decode_check(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,

@@ -41,6 +41,10 @@ static constexpr int SNJ = SQC / 16;    // 16-coordinate steps per wave
 static constexpr int SNB = SD / 32;     // 32-dim blocks of the head
 static constexpr float STAU = 8.0f;     // lazy-max slack, log2 units
 static constexpr int SRAW = 2048 + 512; // ring slot: a wave's codes of 32 tokens, then its pairs (two copies)
+static constexpr int SVAR = 4;          // positions mode: query bases per super-tile (blocks of 32 positions)
+static constexpr int SRT = 36;          // positions mode: dwords per row of the RoPE factor table (32 + padding)
+static constexpr int SQB = SD + 8;      // fp16 per rotated query head (and variant) in LDS: 256 bytes + 16 of padding,
+                                        // so that the score operand reads of 16 heads x variants hit distinct banks
 // a wave's fp16 tile: chunk c (8 coordinates) of token t at byte SCS c + 16 t, 16 chunks; the row of a chunk is
 // padded from 512 to 576 bytes so that the transposing reads of a step (two chunks, token groups 256 bytes
 // apart) hit distinct banks
@@ -60,6 +64,8 @@ struct DecodeSharedArgs {
   int64_t w_stride;  // elements between sequences' W_k (0: one for all)
   const uint32_t* keep;  // token keep mask [B][keep_words] (bit t % 32 of word t / 32), or null
   int keep_words;
+  const int32_t* tok_pos;  // positions mode: source position of each slot [B][pos_row], -1 for none
+  int pos_row;
   float* ws;
   int q_bf16, B, Hkv, Hq, L, max_blocks, P, G, n_splits, st_per_split, part_stride;
   double theta;
@@ -68,19 +74,23 @@ struct DecodeSharedArgs {
 static constexpr int SMAX_TILES = 1024;  // super-tiles per split (the page record address of each)
 
 struct SharedLds {
-  int raw, vt, qt, theta, sp, pt, addr, keep, total;
+  int raw, vt, qt, theta, sp, pt, addr, keep, rtab, posr, total;
 };
-__host__ __device__ constexpr SharedLds shared_lds() {
+// pos: the positions mode (a ring of the super-tiles' slot positions, SVAR query bases per super-tile, a table of
+// the RoPE factors of the 32 in-block offsets)
+__host__ __device__ constexpr SharedLds shared_lds(bool pos) {
   SharedLds L{};
   int o = 0;
-  L.raw = o; o += 4 * 4 * SRAW;                 // per wave: staging ring of 4 super-tiles
-  L.vt = o; o += 4 * 2 * SVT;                   // per wave: fp16 value tiles, x 2
-  L.qt = o; o += 3 * SGQ * SD * 2;              // rotated query in fragment order, fp16, x 3
-  L.theta = o; o += (SD / 2) * 8;               // RoPE frequencies, turns per position
-  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;          // partial scores [buffer][wave][token][head], x 2
-  L.pt = o; o += 4 * 32 * SGQ * 2;              // probabilities [wave][token][head] fp16
-  L.addr = o; o += SMAX_TILES * 8;              // page record address of each super-tile
-  L.keep = o; o += SMAX_TILES * 4;              // keep-mask word of each super-tile
+  L.raw = o; o += 4 * 4 * SRAW;                          // per wave: staging ring of 4 super-tiles
+  L.vt = o; o += 4 * 2 * SVT;                            // per wave: fp16 value tiles, x 2
+  L.qt = o; o += 3 * (pos ? SVAR : 1) * SGQ * SQB * 2;   // rotated query (variants) in fragment order, fp16, x 3
+  L.theta = o; o += (SD / 2) * 8;                        // RoPE frequencies, turns per position
+  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;                   // partial scores [buffer][wave][token][head], x 2
+  L.pt = o; o += 4 * 32 * SGQ * 2;                       // probabilities [wave][token][head] fp16
+  L.addr = o; o += SMAX_TILES * 8;                       // page record address of each super-tile
+  L.keep = o; o += SMAX_TILES * 4;                       // keep-mask word (positions mode: base block) of each
+  L.rtab = o; o += pos ? 64 * SRT * 4 : 0;               // positions mode: RoPE factors [half][offset u][32]
+  L.posr = o; o += pos ? 8 * 32 * 4 : 0;                 // positions mode: slot positions of super-tile k at k % 8
   L.total = o;
   return L;
 }
@@ -89,11 +99,11 @@ __device__ inline f16v_t mfma32s(h8 a, h8 b, f16v_t c) { return __builtin_amdgcn
 
 // fragment order of the rotated query: element e of (head, block g, step st, lane half hf) is head dim
 // 64 (e % 2) + 16 g + 8 st + 4 hf + e / 2, the k-slot order of the rotated keys of block g (each RoPE pair's
-// x and y side by side)
+// x and y side by side); heads SQB elements apart
 __device__ inline int qfrag_index(int head, int dim) {
   const int xy = dim >> 6, r = dim & 63, g = r >> 4, rem = r & 15;
   const int st = rem >> 3, hf = (rem >> 2) & 1, e = 2 * (rem & 3) + xy;
-  return (((head * SNB + g) * 2 + st) * 2 + hf) * 8 + e;
+  return head * SQB + ((g * 2 + st) * 2 + hf) * 8 + e;
 }
 
 // KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it).
@@ -101,13 +111,17 @@ __device__ inline int qfrag_index(int head, int dim) {
 // rows, W_v on the lower, as for keys and values with their own token factors): waves 0-1 then do only the key
 // work and waves 2-3 only the value product; their skipped products are exact zeros, so the output is the same.
 // KB: latent code bits (4; or 3 and 2, whose codes a wave stages token-major and spreads to the INT4 nibble layout)
-template <bool KEEP, bool SPLIT, int KB>
+// POS: a compacted cache whose slots hold tokens at the source positions tok_pos (no keep mask).  A super-tile's
+// tokens lie within SVAR blocks of 32 positions from its first slot's block `base` (the layout the compaction
+// writes): a token at position 32 (base + v) + u is rotated by R(u), from a table, and scored against the query
+// rotated by R(q_pos - 32 (base + v)), one of SVAR variants in the score operand's rows.  Other slots take no part.
+template <bool KEEP, bool SPLIT, int KB, bool POS>
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
   constexpr int CB = SLAT * KB / 8;  // code bytes per token
   constexpr int QB = CB / 4;         // a wave's quarter of them
   constexpr int NCH = QB / 16;       // its 16-byte chunks per token
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr SharedLds LY = shared_lds();
+  constexpr SharedLds LY = shared_lds(POS);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 31, hf = lane >> 5, rho = lane & 15, grp = lane >> 4;
@@ -164,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       qy = q[qj + SD / 2] * sc;
     }
   }
-  const int qix = qfrag_index(qh, qj), qiy = qfrag_index(qh, qj + SD / 2);
+  const int qix = qfrag_index(qh, qj);
   const int n_st = (T + 31) / 32;
   const int st_begin = split * a.st_per_split;
   const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
@@ -176,25 +190,53 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * CB;
     const int wd = t0 >> 5;
     if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
+    if (POS) {  // base block of the super-tile: its first slot's (none: no slot of the tile is valid)
+      const int p0 = a.tok_pos[(size_t)b * a.pos_row + t0];
+      tkeep[k] = (uint32_t)(p0 >= 0 ? p0 >> 5 : 1 << 30);
+    }
   }
+  uint32_t* rtab = (uint32_t*)(smem + LY.rtab);
   __syncthreads();
+  if (POS) {  // RoPE factors of in-block offset u, laid out as the lane of half hf takes them (rf below)
+    for (int e = tid; e < 64 * 32; e += 256) {
+      const int u = e >> 6, hh = (e >> 5) & 1, g = (e >> 3) & 3, i = e & 7;
+      const float rev = (float)(u * tturn[16 * g + 8 * (i >> 2) + 4 * hh + (i & 3)]);
+      rtab[(32 * hh + u) * SRT + 8 * g + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    }
+  }
   const double fq = tturn[qj];
   // RoPE factors of this lane's slot t: block g's up-projection entry i (0..7) is row 8(i/4) + 4hf + i%4 (< 16),
   // paired with entry i + 8 (that row + 16): frequency 16g + row; |t theta| < 32 turns, where v_sin / v_cos are
   // accurate
+  // (positions mode: per super-tile from the table, at the token's own in-block offset)
   uint32_t rf[SNB][8];
+  if (!POS) {
 #pragma unroll
-  for (int g = 0; g < SNB; ++g)
+    for (int g = 0; g < SNB; ++g)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
-      rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+      for (int i = 0; i < 8; ++i) {
+        const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
+        rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+      }
+  }
+  // positions mode: this thread's query pair rotated on from variant 0 to variant v by R(-32 v theta), v < SVAR
+  float vc[SVAR], vs[SVAR];
+  if (POS) {
+#pragma unroll
+    for (int v = 1; v < SVAR; ++v) {
+      double rev = -32.0 * v * fq;
+      rev -= rint(rev);
+      vc[v] = __builtin_amdgcn_cosf((float)rev);
+      vs[v] = __builtin_amdgcn_sinf((float)rev);
     }
+  }
 
   uint8_t* raw_w = smem + LY.raw + wv * 4 * SRAW;  // this wave's ring; super-tile k in slot k % 4
+  const int32_t* posr = (const int32_t*)(smem + LY.posr);
+  const uint32_t posr_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.posr));
   const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw_w));
   uint8_t* vt_w = smem + LY.vt + wv * 2 * SVT;     // this wave's fp16 tiles; super-tile k in k % 2
-  _Float16* qts = (_Float16*)(smem + LY.qt);       // rotated query of super-tile k: qts + (k % 3) * SGQ * SD
+  _Float16* qts = (_Float16*)(smem + LY.qt);       // rotated query of super-tile k: buffer k % 3 (see rot_q)
   float* sp = (float*)(smem + LY.sp);
   _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * SGQ;
 
@@ -230,6 +272,9 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       const int q = 64 * r + lane, tok = q >> 2, i = q & 3;
       copy4_to_lds(rs, dst + 2048 + 256 * r, pairs_at + tok * mpt + 4 * (g0 + (i & (npw - 1))));
     }
+    if (POS && wv == 0 && lane < 32)  // the 32 slots' source positions, for every wave (read after a barrier)
+      copy4_to_lds(buffer_rsrc(a.tok_pos + (size_t)b * a.pos_row + (st_begin + kk) * 32, 128),
+                   posr_lds + (k & 7) * 128, 4 * lane);
   };
 
   f4 acc[SNJ];  // value latent on this wave's coordinates, 16 per step, rows = query heads (replicated)
@@ -277,23 +322,36 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       *(h8*)(dst + SCS * j) = bf[j];
     }
   };
-  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order
-  auto rot_q = [&](int k) {
-    double rev = (double)(qpos - (st_begin + k) * 32) * fq;
+  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order.  Positions mode:
+  // the SVAR variants R(q_pos - 32 (base + v)) q into buffer k % 3 (variant v at its v-th quarter)
+  // (base: positions mode, the super-tile's base block).  A pair's x and y are adjacent elements (qiy = qix + 1).
+  auto rot_q = [&](int k, uint32_t base) {
+    const double t0 = POS ? 32.0 * (double)base : (double)((st_begin + k) * 32);
+    double rev = ((double)qpos - t0) * fq;
     rev -= rint(rev);
     const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-    _Float16* qt = qts + (k % 3) * SGQ * SD;
-    qt[qix] = (_Float16)(qx * cs - qy * sn);
-    qt[qiy] = (_Float16)(qy * cs + qx * sn);
+    _Float16* qt = qts + (k % 3) * (POS ? SVAR : 1) * SGQ * SQB;
+    const float x0 = qx * cs - qy * sn, y0 = qy * cs + qx * sn;
+    *(uint32_t*)(qt + qix) = pack_h2(x0, y0);
+    if (POS) {
+#pragma unroll
+      for (int v = 1; v < SVAR; ++v)
+        *(uint32_t*)(qt + v * SGQ * SQB + qix) = pack_h2(x0 * vc[v] - y0 * vs[v], y0 * vc[v] + x0 * vs[v]);
+    }
   };
 
   // One super-tile: bc holds its B fragments (its fp16 tile is buffer k % 2); the next super-tile is dequantized
   // into bn on the way.
-  auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ]) {
+  // pc: positions mode, this lane's slot position in super-tile k (read with k's code words); pn gets k + 1's
+  auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ], int pc, int& pn) {
     issue(k + 4);  // ring slot k % 4 held super-tile k, dequantized in the previous step
     const int t0 = (st_begin + k) * 32;
-    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each) may still be in flight
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each; wave 0 of the positions mode five) may still
+    // be in flight
+    if (POS && wv == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     // sources of super-tile k + 1's dequantization (dword reads: see dequant)
     const uint8_t* rawn = raw_w + ((k + 1) & 3) * SRAW;
@@ -302,12 +360,38 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     const uint32_t z0 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr1));
     uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + SCS * 8 * hf + 16 * t;
+    const uint32_t base2 = POS ? tkeep[min(k + 2, n_tiles - 1)] : 0u;  // super-tile k + 2's, for its query
+
+    // positions mode: the token's block offset v from the super-tile's base picks its query variant, its in-block
+    // offset u its RoPE factors; other lanes hold the factors of their slot t
+    int vsel = 0;
+    bool valid = true;
+    uint32_t rk[SNB][8];
+    if constexpr (POS) {
+      const int v = (pc >> 5) - (int)tkeep[k];
+      valid = pc >= 0 && v >= 0 && v < SVAR;
+      vsel = valid ? v : 0;
+      const u32x4_t* src = (const u32x4_t*)(rtab + (32 * hf + (pc & 31)) * SRT);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4_t x = src[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rk[j >> 1][4 * (j & 1) + e] = x[e];
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < SNB; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rk[g][i] = rf[g][i];
+    }
 
     // ---- partial keys over this wave's coordinates (block by block), RoPE, partial scores of the four heads.
     // The instruction stream interleaves each block's matrix instructions with vector work that does not wait
     // for them (two chunks of the next super-tile's dequantization, the previous block's RoPE), so that one
     // wave keeps both units busy.
-    const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SD) + (t & 3) * (SNB * 4) + hf;
+    // score operand row t: query head t % 4 (positions mode: of variant (t / 4) % SVAR)
+    const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? (t >> 2) & (SVAR - 1) : 0)) * SGQ * SQB +
+                               (t & 3) * SQB) + hf;
     f16v_t sc = {};
     // a super-tile whose tokens are all evicted contributes nothing: only the next one's dequantization runs
     const bool empty = KEEP && tkeep[k] == 0u;
@@ -338,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         // rotated pairs (x, y) of rows 8st + 4hf + m, m < 4, are the k-slots 8hf + 2m, 2m + 1 of score step st
         u32x4_t kr[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rf[g - 1][i]);
+        for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rk[g - 1][i]);
         sc = mfma32s(qf[4 * (g - 1)], __builtin_bit_cast(h8, kr[0]), sc);
         sc = mfma32s(qf[4 * (g - 1) + 2], __builtin_bit_cast(h8, kr[1]), sc);
       }
@@ -354,9 +438,12 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     }
     }
     float* spb = sp + (k & 1) * (4 * 32 * SGQ);
-    if (hf == 0) *(f4*)(spb + (wv * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
+    // row 8 (j / 4) + 4 hf + j % 4 of entry j: this lane half holds variants hf (entries 0-3) and 2 + hf (4-7)
+    if (POS ? hf == (vsel & 1) : hf == 0)
+      *(f4*)(spb + (wv * 32 + t) * SGQ) = (POS && (vsel >> 1)) ? f4{sc[4], sc[5], sc[6], sc[7]} : f4{sc[0], sc[1], sc[2], sc[3]};
     lds_barrier();
-    rot_q(k + 2);  // buffer (k + 2) % 3 was last read before the previous barrier
+    if (POS) pn = posr[((k + 1) & 7) * 32 + t];  // wave 0 waited for its copy before the barrier
+    rot_q(k + 2, base2);  // buffer (k + 2) % 3 was last read before the previous barrier
 
     // ---- scores of the four heads for token t (the same in every wave), lazy online softmax
     float s4[SGQ];
@@ -364,14 +451,15 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       f4 tot = *(const f4*)(spb + t * SGQ);
 #pragma unroll
       for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
-      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u));  // past the end or evicted: no weight
+      // past the end, evicted, or (positions mode) no token: no weight
+      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u)) && valid;
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) s4[i] = kept ? tot[i] - m_ref[i] : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
     // the first super-tile with a kept token sets the reference maximum; one with none (possible under a keep
     // mask only) leaves it unset
-    if (KEEP ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
+    if ((KEEP || POS) ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
              : fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
       float alpha[SGQ];
 #pragma unroll
@@ -419,19 +507,23 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // prologue: super-tiles 0-3 in flight, wait for 0, dequantize it; rotated queries of 0 and 1
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue(j);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    if (POS && wv == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     h8 ba[SNJ], bb[SNJ];
     dequant(0, ba, 0);
-    rot_q(0);
-    rot_q(1);
+    rot_q(0, POS ? tkeep[0] : 0u);
+    rot_q(1, POS ? tkeep[min(1, n_tiles - 1)] : 0u);
     lds_barrier();
+    int pa = POS ? posr[t] : 0, pb = 0;
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
-      step(k, ba, bb);
-      step(k + 1, bb, ba);
+      step(k, ba, bb, pa, pb);
+      step(k + 1, bb, ba, pb, pa);
     }
-    if (k < n_tiles) step(k, ba, bb);
+    if (k < n_tiles) step(k, ba, bb, pa, pb);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies past the end land before the workgroup exits
   }
 
@@ -514,26 +606,29 @@ size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {
   return (size_t)L.n_layers * L.n_kv_heads * B * n_splits * (2 * SGQ + SGQ * SLAT) * sizeof(float);
 }
 
-template <bool KEEP, bool SPLIT, int KB>
-static hipError_t launch_shared_one(int grid, int lds, hipStream_t st, const DecodeSharedArgs& a) {
-  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB>;
+template <bool KEEP, bool SPLIT, int KB, bool POS>
+static hipError_t launch_shared_one(int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB, POS>;
+  const int lds = shared_lds(POS).total;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB, POS>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-template <bool KEEP, bool SPLIT>
-static hipError_t launch_shared_bits(int kb, int grid, int lds, hipStream_t st, const DecodeSharedArgs& a) {
-  if (kb == 3) return launch_shared_one<KEEP, SPLIT, 3>(grid, lds, st, a);
-  if (kb == 2) return launch_shared_one<KEEP, SPLIT, 2>(grid, lds, st, a);
-  return launch_shared_one<KEEP, SPLIT, 4>(grid, lds, st, a);
+template <bool KEEP, bool SPLIT, bool POS>
+static hipError_t launch_shared_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  if (kb == 3) return launch_shared_one<KEEP, SPLIT, 3, POS>(grid, st, a);
+  if (kb == 2) return launch_shared_one<KEEP, SPLIT, 2, POS>(grid, st, a);
+  return launch_shared_one<KEEP, SPLIT, 4, POS>(grid, st, a);
 }
 
-static hipError_t launch_shared_variant(bool keep, bool split, int kb, int grid, int lds, hipStream_t st,
+// keep mask and positions are exclusive (the entry point rejects both)
+static hipError_t launch_shared_variant(bool keep, bool pos, bool split, int kb, int grid, hipStream_t st,
                                         const DecodeSharedArgs& a) {
-  if (keep) return split ? launch_shared_bits<true, true>(kb, grid, lds, st, a) : launch_shared_bits<true, false>(kb, grid, lds, st, a);
-  return split ? launch_shared_bits<false, true>(kb, grid, lds, st, a) : launch_shared_bits<false, false>(kb, grid, lds, st, a);
+  if (keep) return split ? launch_shared_bits<true, true, false>(kb, grid, st, a) : launch_shared_bits<true, false, false>(kb, grid, st, a);
+  if (pos) return split ? launch_shared_bits<false, true, true>(kb, grid, st, a) : launch_shared_bits<false, false, true>(kb, grid, st, a);
+  return split ? launch_shared_bits<false, true, false>(kb, grid, st, a) : launch_shared_bits<false, false, false>(kb, grid, st, a);
 }
 
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
@@ -542,17 +637,17 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   a.pool = C.pool; a.page_off = C.page_off; a.block_table = in.block_table; a.seq_len = in.seq_len;
   a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk; a.w_stride = in.w_seq_stride; a.ws = (float*)ws;
   a.keep = in.keep_mask; a.keep_words = in.keep_words;
+  a.tok_pos = in.tok_pos; a.pos_row = in.max_blocks * L.page_size;
   a.q_bf16 = in.q_dtype == KVC_BF16;
   a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.L = L.n_layers; a.max_blocks = in.max_blocks;
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
   a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
-  const int lds = shared_lds().total;
   const bool split = in.kv_split == SLAT / 2;
   const int kb = lat_bits_k(L);
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
   hipError_t e = mark(g_marks.begin, st);
   if (e != hipSuccess) return e;
-  e = launch_shared_variant(in.keep_mask != nullptr, split, kb, grid, lds, st, a);
+  e = launch_shared_variant(in.keep_mask != nullptr, in.tok_pos != nullptr, split, kb, grid, st, a);
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,

@@ -121,7 +121,141 @@ __global__ __launch_bounds__(ET) void evict_select_kernel(EvictArgs e) {
   }
 }
 
+// ---- compaction of the evicted tokens (block-shared cache): kept tokens in position order into tiles of CT = 32
+// slots, a tile spanning at most CSPAN blocks of 32 positions from its first token's block; each slot records its
+// source position.
+constexpr int CT = 32, CSPAN = 4;
+constexpr int CMAX_BLOCKS = 8192;  // 32-position blocks per sequence: two LDS words each
+
+struct CompactArgs {
+  const uint8_t* src;
+  const int64_t* src_off;
+  const int32_t* bt;
+  const int32_t* seq_len;
+  const uint32_t* keep;
+  uint8_t* dst;
+  const int64_t* dst_off;
+  const int32_t* obt;
+  int32_t* out_len;
+  int32_t* tok_pos;
+  int keep_words, max_blocks, P, cb, moff, mb;
+};
+
+// One workgroup per sequence.  The tile rule is a left-to-right recurrence, but it only changes state at a
+// block's first kept token, so one thread walks the blocks (a popcount each) and gives each block the slot of its
+// first kept token; within a block the kept tokens take consecutive slots (a tile that fills mid-block continues
+// in the next slot, which opens the next tile with the same block as its base).  Then every thread writes the
+// positions of its blocks' tokens, after the row is set to -1.
+__global__ __launch_bounds__(256) void compact_scan_kernel(CompactArgs a) {
+  extern __shared__ uint32_t cl[];  // [n_blk] keep words, then [n_blk] first slots
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int row = a.max_blocks * a.P;
+  const int T = max(0, min(min(a.seq_len[b], row), 32 * a.keep_words));
+  const int n_blk = (T + 31) / 32;
+  uint32_t* words = cl;
+  int* first = (int*)(cl + n_blk);
+  for (int i = tid; i < n_blk; i += 256) {
+    uint32_t w = a.keep[(size_t)b * a.keep_words + i];
+    const int left = T - 32 * i;  // positions of this block below T
+    if (left < 32) w &= (1u << left) - 1u;
+    words[i] = w;
+  }
+  int32_t* pos = a.tok_pos + (size_t)b * row;
+  for (int i = tid; i < row; i += 256) pos[i] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    int slot = 0, count = 0, base = 0;
+    for (int i = 0; i < n_blk; ++i) {
+      const int c = __builtin_popcount(words[i]);
+      if (c == 0) continue;
+      if (count > 0 && i - base >= CSPAN) {  // out of the tile's span: close it, its spare slots stay empty
+        slot = (slot + CT - 1) / CT * CT;
+        count = 0;
+      }
+      if (count == 0) base = i;
+      first[i] = slot;
+      slot += c;
+      count += c;
+      if (count >= CT) {  // the tile filled at one of this block's tokens; the rest open the next tile here
+        count -= CT;
+        base = i;
+      }
+    }
+    a.out_len[b] = slot;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_blk; i += 256) {
+    uint32_t w = words[i];
+    int s = first[i];
+    while (w) {
+      pos[s++] = 32 * i + __builtin_ctz(w);
+      w &= w - 1u;
+    }
+  }
+}
+
+// One workgroup per (sequence, destination page): every slot of a page below the compacted length gets its
+// token's code and pair bytes, or zeros (no token); pages past it are left alone.  Dword copies (code and pair
+// sections of a slot are whole dwords).
+__global__ __launch_bounds__(256) void compact_copy_kernel(CompactArgs a) {
+  const int b = blockIdx.x / a.max_blocks, i = blockIdx.x % a.max_blocks;
+  const int len = a.out_len[b];
+  if (i * a.P >= len) return;
+  const int row = a.max_blocks * a.P;
+  const int32_t* pos = a.tok_pos + (size_t)b * row + (size_t)i * a.P;
+  uint32_t* dst = (uint32_t*)(a.dst + a.dst_off[a.obt[(size_t)b * a.max_blocks + i]]);
+  const int cw = a.cb / 4, mw = a.mb / 4;
+  for (int e = threadIdx.x; e < a.P * (cw + mw); e += 256) {
+    const bool code = e < a.P * cw;
+    const int s = code ? e / cw : (e - a.P * cw) / mw;
+    const int k = code ? e % cw : (e - a.P * cw) % mw;
+    const int p = i * a.P + s < len ? pos[s] : -1;
+    uint32_t v = 0u;
+    if (p >= 0) {
+      const uint32_t* src = (const uint32_t*)(a.src + a.src_off[a.bt[(size_t)b * a.max_blocks + p / a.P]]);
+      v = code ? src[(p % a.P) * cw + k] : src[a.moff / 4 + (p % a.P) * mw + k];
+    }
+    if (code)
+      dst[s * cw + k] = v;
+    else
+      dst[a.moff / 4 + s * mw + k] = v;
+  }
+}
+
 }  // namespace
+
+bool shared_supported(const kvc_layout& L);
+
+kvc_status compact_impl(const kvc_layout& L, const kvc_cache& src, const kvc_cache& dst, const kvc_compact_in& in,
+                        int32_t* out_len, int32_t* tok_pos, hipStream_t st) {
+  if (!L.shared) return KVC_ERR_INVALID_ARG;
+  if (in.B < 1 || in.max_blocks < 1 || in.keep_words < 1 || !in.block_table || !in.seq_len || !in.keep_mask ||
+      !in.out_block_table || !out_len || !tok_pos || !src.pool || !src.page_off || !dst.pool || !dst.page_off)
+    return KVC_ERR_INVALID_ARG;
+  if ((int64_t)in.max_blocks * L.page_size > (int64_t)32 * CMAX_BLOCKS || in.B > (1 << 20)) return KVC_ERR_INVALID_ARG;
+  if (!shared_supported(L)) return KVC_ERR_UNSUPPORTED;
+  const void* ptrs[] = {in.block_table, in.seq_len, in.out_block_table, out_len, tok_pos, src.pool, src.page_off,
+                        dst.pool, dst.page_off};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return KVC_ERR_MISALIGNED;
+  if ((uintptr_t)in.keep_mask & 3) return KVC_ERR_MISALIGNED;
+  CompactArgs a;
+  a.src = src.pool; a.src_off = src.page_off; a.bt = in.block_table; a.seq_len = in.seq_len; a.keep = in.keep_mask;
+  a.dst = dst.pool; a.dst_off = dst.page_off; a.obt = in.out_block_table; a.out_len = out_len; a.tok_pos = tok_pos;
+  a.keep_words = in.keep_words; a.max_blocks = in.max_blocks; a.P = L.page_size;
+  a.cb = L.r_k_cap * L.latent_bits / 8;
+  a.moff = (int)pad16((int64_t)L.page_size * a.cb);
+  a.mb = 4 * (L.r_k_cap / L.group);
+  const int n_blk = (in.max_blocks * L.page_size + 31) / 32;
+  const int lds = 8 * n_blk;
+  hipError_t err = hipFuncSetAttribute((const void*)compact_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return hip_fail(err);
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(in.B), dim3(256), lds, st, a);
+  if ((err = hipGetLastError()) != hipSuccess) return hip_fail(err);
+  hipLaunchKernelGGL(compact_copy_kernel, dim3(in.B * in.max_blocks), dim3(256), 0, st, a);
+  err = hipGetLastError();
+  return err == hipSuccess ? KVC_OK : hip_fail(err);
+}
 
 kvc_status evict_impl(const kvc_evict_in& in, uint32_t* mask, hipStream_t st) {
   if (in.B < 1 || in.max_T < 1 || in.n_layers < 1 || !in.seq_len || !in.scores || !mask) return KVC_ERR_INVALID_ARG;

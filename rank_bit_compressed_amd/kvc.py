@@ -27,7 +27,8 @@ EXPORTS = ["kvc_abi_version", "kvc_status_string", "kvc_last_hip_error", "kvc_la
            "kvc_fit_basis", "kvc_fit_basis_timed", "kvc_salience_workspace_bytes", "kvc_salience",
            "kvc_rank_alloc", "kvc_plan_budget", "kvc_tucker_expand",
            "kvc_evict_select", "kvc_decode_check", "kvc_decode_attn_noalloc", "kvc_probe_stream_read",
-           "kvc_probe_mfma_f16", "kvc_probe_clock", "kvc_tucker_fit_workspace_bytes", "kvc_tucker_fit"]
+           "kvc_probe_mfma_f16", "kvc_probe_clock", "kvc_tucker_fit_workspace_bytes", "kvc_tucker_fit",
+           "kvc_evict_compact"]
 
 
 class KvcError(RuntimeError):
@@ -64,7 +65,8 @@ class DecodeIn(C.Structure):
     _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("max_T", C.c_int32), ("block_table", C.c_void_p),
                 ("seq_len", C.c_void_p), ("q_pos", C.c_void_p), ("q", C.c_void_p), ("q_dtype", C.c_int32),
                 ("wk", C.c_void_p), ("wv", C.c_void_p), ("num_splits", C.c_int32), ("w_seq_stride", C.c_int64),
-                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32), ("kv_split", C.c_int32)]
+                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32), ("kv_split", C.c_int32),
+                ("tok_pos", C.c_void_p)]
 
 
 class DenseIn(C.Structure):
@@ -131,6 +133,7 @@ def lib():
         L.kvc_plan_budget.argtypes = [P, P, P]; L.kvc_plan_budget.restype = C.c_int32
         L.kvc_tucker_expand.argtypes = [P, P, P, P]; L.kvc_tucker_expand.restype = C.c_int32
         L.kvc_evict_select.argtypes = [P, P, P]; L.kvc_evict_select.restype = C.c_int32
+        L.kvc_evict_compact.argtypes = [P, P, P, P, P, P, P]; L.kvc_evict_compact.restype = C.c_int32
         L.kvc_decode_check.argtypes = [P, P, P, P, P]; L.kvc_decode_check.restype = C.c_int32
         L.kvc_decode_attn_noalloc.argtypes = [P, P, P, P, P]; L.kvc_decode_attn_noalloc.restype = C.c_int32
         L.kvc_probe_stream_read.argtypes = [P, C.c_size_t, P, C.c_int32, P]; L.kvc_probe_stream_read.restype = C.c_int32
@@ -276,16 +279,18 @@ def _q_dtype(q):
 
 
 def decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos=None, num_splits=0, w_seq_stride=0,
-              keep_mask=None, kv_split=0) -> DecodeIn:
+              keep_mask=None, kv_split=0, tok_pos=None, page_size=0) -> DecodeIn:
     B, max_blocks = block_table.shape
     words = 0
     if keep_mask is not None:
         if keep_mask.dtype != torch.int32 or keep_mask.dim() != 2 or keep_mask.shape[0] != B:
             raise ValueError("keep_mask must be an int32 (uint32 bits) tensor [B, words]")
         words = keep_mask.shape[1]
+    if tok_pos is not None:
+        _need(tok_pos, "tok_pos", torch.int32, (B, max_blocks * page_size))
     return DecodeIn(B, max_blocks, max_T, _ptr(block_table), _ptr(seq_len), _ptr(q_pos), _ptr(q), _q_dtype(q),
                     _ptr(wk.view(torch.int16)), _ptr(wv.view(torch.int16)), num_splits, w_seq_stride,
-                    _ptr(keep_mask), words, kv_split)
+                    _ptr(keep_mask), words, kv_split, _ptr(tok_pos))
 
 
 def _w_stride(layout, wk, wv, B):
@@ -298,13 +303,15 @@ def _w_stride(layout, wk, wv, B):
 
 
 def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                num_splits=0, out=None, ws=None, events=None, keep_mask=None, kv_split=0):
+                num_splits=0, out=None, ws=None, events=None, keep_mask=None, kv_split=0, tok_pos=None):
     """kvc_decode_attn -> fp32 [(L,) B, Hq, d].  events: optional (begin, end) pair of recorded-once
     torch.cuda.Event objects; the call then goes through kvc_decode_attn_timed, which records them around
     the attention kernel alone.  Shared mode: wk, wv [L, latent, Hkv * d] for all sequences, or
     [B, L, latent, Hkv * d] (contiguous), one pair per sequence; keep_mask: optional int32 [B, words] token
     keep mask (as kvc_evict_select writes it); kv_split: latent / 2 for a latent whose lower half holds only
-    key coordinates and upper half only value coordinates (keys and values with their own token factors)."""
+    key coordinates and upper half only value coordinates (keys and values with their own token factors);
+    tok_pos: optional int32 [B, max_blocks * page_size] source positions of a compacted cache's slots (as
+    evict_compact writes them; q_pos required)."""
     _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
     B = block_table.shape[0]
     if out is None:
@@ -313,7 +320,7 @@ def decode_attn(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk,
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
-                    keep_mask, kv_split)
+                    keep_mask, kv_split, tok_pos, layout.page_size)
     c = cache.c()
     if events is None:
         _check(lib().kvc_decode_attn(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _ptr(ws), ws.numel(),
@@ -329,7 +336,7 @@ NOALLOC_SCRATCH_BYTES = 8 << 20  # KVC_NOALLOC_SCRATCH_BYTES
 
 
 def decode_attn_noalloc(layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                        num_splits=0, out=None, keep_mask=None, kv_split=0):
+                        num_splits=0, out=None, keep_mask=None, kv_split=0, tok_pos=None):
     """kvc_decode_attn_noalloc -> fp32 [(L,) B, Hq, d]: the decode step with its split partials in the library's
     device array (no workspace argument; the library allocates nothing).  Calls overlapping on one GPU race."""
     _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
@@ -337,7 +344,7 @@ def decode_attn_noalloc(layout: Layout, cache: DeviceCache, block_table, seq_len
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     inp = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
-                    keep_mask, kv_split)
+                    keep_mask, kv_split, tok_pos, layout.page_size)
     c = cache.c()
     _check(lib().kvc_decode_attn_noalloc(C.byref(layout), C.byref(c), C.byref(inp), _ptr(out), _stream()),
            "kvc_decode_attn_noalloc")
@@ -351,17 +358,17 @@ class DecodePlan:
     they hold at launch time.  Calls enqueue on the current stream, like decode_attn."""
 
     def __init__(self, layout: Layout, cache: DeviceCache, block_table, seq_len, q, wk, wv, max_T, q_pos=None,
-                 num_splits=0, out=None, ws=None, keep_mask=None, kv_split=0):
+                 num_splits=0, out=None, ws=None, keep_mask=None, kv_split=0, tok_pos=None):
         _check_decode_args(layout, block_table, seq_len, q, wk, wv, q_pos, out)
         B = block_table.shape[0]
         self.out = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=q.device)
         need = decode_workspace_bytes(layout, B, max_T, num_splits)
         if ws is None or ws.numel() < need:
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-        self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws, keep_mask)
+        self._keep = (layout, cache, block_table, seq_len, q, wk, wv, q_pos, ws, keep_mask, tok_pos)
         self._layout, self._cache = layout, cache.c()
         self._in = decode_in(block_table, seq_len, q, wk, wv, max_T, q_pos, num_splits, _w_stride(layout, wk, wv, B),
-                             keep_mask, kv_split)
+                             keep_mask, kv_split, tok_pos, layout.page_size)
         self._args = (C.byref(self._layout), C.byref(self._cache), C.byref(self._in), _ptr(self.out), _ptr(ws),
                       ws.numel())
         self._fn, self._fn_timed = lib().kvc_decode_attn, lib().kvc_decode_attn_timed
@@ -585,6 +592,33 @@ def evict_select(scores, seq_len, keep_ratio, out=None):
     inp = EvictIn(B, max_T, n_layers, float(keep_ratio), _ptr(seq_len), _ptr(scores))
     _check(lib().kvc_evict_select(C.byref(inp), _ptr(out), _stream()), "kvc_evict_select")
     return out
+
+
+class CompactIn(C.Structure):
+    _fields_ = [("B", C.c_int32), ("max_blocks", C.c_int32), ("block_table", C.c_void_p), ("seq_len", C.c_void_p),
+                ("keep_mask", C.c_void_p), ("keep_words", C.c_int32), ("out_block_table", C.c_void_p)]
+
+
+def evict_compact(layout: Layout, src: DeviceCache, dst: DeviceCache, block_table, seq_len, keep_mask,
+                  out_block_table, out_seq_len=None, tok_pos=None):
+    """kvc_evict_compact: the kept tokens of a block-shared cache moved into dst's pages out_block_table
+    (dst.page_off set by the caller).  Returns (out_seq_len int32 [B], tok_pos int32 [B, max_blocks * P])."""
+    B, max_blocks = block_table.shape
+    _need(block_table, "block_table", torch.int32)
+    _need(out_block_table, "out_block_table", torch.int32, (B, max_blocks))
+    _need(seq_len, "seq_len", torch.int32, (B,))
+    if keep_mask.dtype != torch.int32 or keep_mask.dim() != 2 or keep_mask.shape[0] != B:
+        raise ValueError("keep_mask must be an int32 (uint32 bits) tensor [B, words]")
+    if out_seq_len is None:
+        out_seq_len = torch.empty(B, dtype=torch.int32, device=block_table.device)
+    if tok_pos is None:
+        tok_pos = torch.empty(B, max_blocks * layout.page_size, dtype=torch.int32, device=block_table.device)
+    _need(tok_pos, "tok_pos", torch.int32, (B, max_blocks * layout.page_size))
+    inp = CompactIn(B, max_blocks, _ptr(block_table), _ptr(seq_len), _ptr(keep_mask), keep_mask.shape[1],
+                    _ptr(out_block_table))
+    _check(lib().kvc_evict_compact(C.byref(layout), C.byref(src.c()), C.byref(dst.c()), C.byref(inp),
+                                   _ptr(out_seq_len), _ptr(tok_pos), _stream()), "kvc_evict_compact")
+    return out_seq_len, tok_pos
 
 
 BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK, BAD_TOK_OFF, BAD_RECORD = 1, 2, 4, 8, 16, 32, 64

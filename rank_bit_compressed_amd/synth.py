@@ -83,6 +83,7 @@ class Workload:
     tucker: tuple = ()            # block-shared from partial Tucker factors: (key r_t, value r_t, r_f)
     evict_ratio: float = 0.0      # block-shared: share of tokens the block's eviction decision keeps
     evict_cluster: int = 0        # > 0: token scores clustered in runs of this many tokens (see make_layer_scores)
+    evict_compact: bool = False   # the evicted tokens are compacted out of the pages before the decode
     seed: int = 0
 
     def scaled(self, **kw) -> "Workload":
@@ -136,6 +137,12 @@ WORKLOADS = {
                                           head_dim=128, r_k=512, r_v=512, group=64, shared=True, n_layers=4,
                                           rope_theta=500000.0, latent_decay=0.0, w_std=1.0 / math.sqrt(512.0),
                                           evict_ratio=0.3, seed=14),
+    # the same with the evicted tokens compacted out of the pages (the decode reads the kept tokens only)
+    "shared_latent_32k_evict30_compact": Workload("shared_latent_32k_evict30_compact", B=4, T=32768, n_q_heads=32,
+                                                  n_kv_heads=8, head_dim=128, r_k=512, r_v=512, group=64, shared=True,
+                                                  n_layers=4, rope_theta=500000.0, latent_decay=0.0,
+                                                  w_std=1.0 / math.sqrt(512.0), evict_ratio=0.3, evict_compact=True,
+                                                  seed=14),
     # the same with token importance clustered in runs of 256 tokens, so that whole super-tiles are evicted
     "shared_latent_32k_evict30_clustered": Workload("shared_latent_32k_evict30_clustered", B=4, T=32768,
                                                     n_q_heads=32, n_kv_heads=8, head_dim=128, r_k=512, r_v=512,

@@ -21,7 +21,7 @@ def test_library_exports_header():
     L = C.CDLL(kvc.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert kvc.lib().kvc_abi_version() == 7
+    assert kvc.lib().kvc_abi_version() == 8
     assert kvc.lib().kvc_status_string(-3) == b"workspace or pool too small"
 
 
@@ -75,7 +75,8 @@ def test_decode_path_selection():
             "shared_latent_32k": kvc.PATH_SHARED, "residual_128k": kvc.PATH_RES,
             "varrank_paged_32k_int3": kvc.PATH_INT4, "llama8b_layer_8k_k3v2": kvc.PATH_INT4,
             "tucker_group_32k": kvc.PATH_SHARED, "shared_latent_32k_evict30": kvc.PATH_SHARED,
-            "shared_latent_32k_evict30_clustered": kvc.PATH_SHARED, "shared_latent_32k_int3": kvc.PATH_SHARED}
+            "shared_latent_32k_evict30_clustered": kvc.PATH_SHARED,
+            "shared_latent_32k_evict30_compact": kvc.PATH_SHARED, "shared_latent_32k_int3": kvc.PATH_SHARED}
     for name, w in synth.WORKLOADS.items():
         assert kvc.decode_path(kvc.make_layout(**w.layout_kwargs())) == want[name], name
         small = w.scaled(B=2, T=700, page_size=128) if not w.shared else w.scaled(B=1, T=700)
@@ -305,3 +306,38 @@ def test_shared_layout_widths():
     w = synth.WORKLOADS["shared_latent_32k_int3"]
     # a page of 256 slots: 512 x 3 / 8 = 192 code bytes, then 512 / 64 = 8 (scale, zero) pairs of 4 bytes per slot
     assert kvc.pool_bytes_max(L, w.n_pages) == w.n_pages * (256 * 192 + 256 * 8 * 4)
+
+
+def test_compaction_and_positions_rejections_without_launching():
+    lib = kvc.lib()
+    p = C.c_void_p
+    shared = kvc.make_layout(**synth.WORKLOADS["shared_latent_32k"].layout_kwargs())
+    perhead = kvc.make_layout(**synth.WORKLOADS["varrank_paged_32k"].layout_kwargs())
+    src = kvc.Cache(p(16), 1 << 30, p(32), None, None, None, 4)
+    dst = kvc.Cache(p(4096), 1 << 30, p(8192), None, None, None, 4)
+    good = dict(B=2, max_blocks=4, block_table=p(80), seq_len=p(96), keep_mask=p(112), keep_words=32,
+                out_block_table=p(128))
+
+    def compact(L=shared, s=src, d=dst, out=p(160), pos=p(176), **kw):
+        f = dict(good, **kw)
+        inp = kvc.CompactIn(f["B"], f["max_blocks"], f["block_table"], f["seq_len"], f["keep_mask"], f["keep_words"],
+                            f["out_block_table"])
+        return lib.kvc_evict_compact(C.byref(L), C.byref(s), C.byref(d), C.byref(inp), out, pos, None)
+
+    assert compact(L=perhead) == -1                          # per-head caches have no block-level decision
+    for bad in (dict(B=0), dict(max_blocks=0), dict(keep_words=0), dict(keep_mask=None), dict(out_block_table=None),
+                dict(block_table=None), dict(max_blocks=2049)):   # 2049 pages of 128 slots: past 262144
+        assert compact(**bad) == -1, bad
+    assert compact(out=None) == -1 and compact(pos=None) == -1
+    assert compact(d=kvc.Cache(None, 0, None, None, None, None, 4)) == -1
+    assert compact(block_table=p(84)) == -4 and compact(keep_mask=p(114)) == -4 and compact(pos=p(180)) == -4
+    odd = kvc.make_layout(**synth.WORKLOADS["shared_latent_32k"].layout_kwargs())
+    odd.r_k_cap = odd.r_v_cap = 256                          # a latent the block-shared decode does not serve
+    assert compact(L=odd) == -2
+    # positions: block-shared only, with q_pos and no keep mask, 4-byte aligned
+    cache = kvc.Cache(p(16), 1 << 30, p(32), p(48), p(64), None, 4)
+    for L, qpos, mask, words, tp, want in ((perhead, p(100), None, 0, p(192), -1), (shared, None, None, 0, p(192), -1),
+                                           (shared, p(100), p(208), 4, p(192), -1),
+                                           (shared, p(100), None, 0, p(194), -4)):
+        inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), qpos, p(112), 1, p(128), p(144), 0, 0, mask, words, 0, tp)
+        assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == want

@@ -154,3 +154,135 @@ def test_evict_then_decode_full_size_sampled():
     sel_h = np.zeros(w.n_kv_heads, np.uint8); sel_h[4] = 1
     want = _masked_oracle(w, inp, cache, m, sel_b, sel_h)
     assert rel_err(out, want) <= TOL
+
+
+# ---------------------------------------------------------------- compaction and the decode over positions
+
+def _compact_pair(w, inp, d, mask_np, seed=11):
+    """GPU compaction of the cache compressed from inp under mask_np, and the oracle's from the oracle's cache
+    (the two source pools are bit-identical: compression is tested bit for bit).  Returns the GPU outputs and
+    the oracle's (pool, tok_pos, out_len)."""
+    gc = gpu_cache(w, d)
+    rec = int(gc.page_off[1].item() - gc.page_off[0].item())
+    dst = kvc.DeviceCache(gc.layout, torch.full_like(gc.pool, 0xAB), torch.arange(w.n_pages, dtype=torch.int64,
+                          device="cuda") * rec, None, None, torch.zeros(2, dtype=torch.int64, device="cuda"), w.n_pages)
+    obt = torch.from_numpy(np.random.default_rng(seed).permutation(w.n_pages).astype(np.int32).reshape(w.B, -1))
+    gm = torch.from_numpy(np.ascontiguousarray(mask_np).view(np.int32)).cuda()
+    out_len, tok_pos = kvc.evict_compact(gpu_layout(w), gc, dst, d["block_table"], d["seq_len"], gm, obt.cuda())
+    torch.cuda.synchronize()
+    cache = oracle_cache(w, inp)
+    want = E.compact(w.r_k, w.latent_bits, w.group, w.page_size, inp["block_table"].numpy(),
+                     inp["seq_len"].numpy(), mask_np, cache[0], cache[1], obt.numpy(),
+                     np.arange(w.n_pages, dtype=np.int64) * rec, np.full(gc.pool.numel(), 0xAB, np.uint8))
+    return gc, dst, obt.cuda(), out_len, tok_pos, gm, cache, want
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_compaction_matches_oracle_bit_for_bit(bits):
+    w = synth.WORKLOADS["shared_latent_32k_evict30"].scaled(B=2, T=700, page_size=64, latent_bits=bits)
+    seq = [700, 333]
+    inp = synth.make_inputs(w, seq_len=seq)
+    d = dev(inp)
+    masks = _masks(w, seq, np.random.default_rng(8))
+    masks["evict 30%"] = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    masks["all"] = np.full_like(masks["random"], 0xFFFFFFFF)
+    for name, m in masks.items():
+        print(f"[compact] bits={bits} mask '{name}'", flush=True)
+        gc, dst, obt, out_len, tok_pos, gm, cache, (pool2, pos2, len2) = _compact_pair(w, inp, d, m)
+        assert np.array_equal(out_len.cpu().numpy(), len2), name
+        assert np.array_equal(tok_pos.cpu().numpy(), pos2), name
+        assert np.array_equal(dst.pool.cpu().numpy(), pool2), name
+        if name == "all":  # keeping everything moves every token to its own slot
+            assert np.array_equal(len2, seq)
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_compacted_decode_matches_masked_oracle(num_splits):
+    w = synth.WORKLOADS["shared_latent_32k_evict30"].scaled(B=2, T=700, page_size=64)
+    seq = [700, 333]
+    inp = synth.make_inputs(w, seq_len=seq)
+    d = dev(inp)
+    L = gpu_layout(w)
+    masks = _masks(w, seq, np.random.default_rng(5))
+    masks["evict 30%"] = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    masks["evict 30% clustered"] = E.keep_mask(synth.make_layer_scores(w.scaled(evict_cluster=64)).numpy(), seq,
+                                               w.evict_ratio)
+    sparse = np.random.default_rng(3).random((w.B, 32 * masks["random"].shape[1])) < 0.03
+    masks["3% (tiles closed by the span)"] = (sparse.reshape(w.B, -1, 32).astype(np.uint64)
+                                              << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+    for name, m in masks.items():
+        print(f"[compact] decode over positions, mask '{name}' num_splits={num_splits}", flush=True)
+        gc, dst, obt, out_len, tok_pos, gm, cache, _ = _compact_pair(w, inp, d, m)
+        want = _masked_oracle(w, inp, cache, m)
+        args = (L, dst, obt, out_len, d["q"], d["wk"], d["wv"], w.T)
+        out = kvc.decode_attn(*args, q_pos=d["q_pos"], num_splits=num_splits, tok_pos=tok_pos)
+        again = kvc.decode_attn(*args, q_pos=d["q_pos"], num_splits=num_splits, tok_pos=tok_pos)
+        na = kvc.decode_attn_noalloc(*args, q_pos=d["q_pos"], num_splits=num_splits, tok_pos=tok_pos)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again) and torch.equal(out, na)
+        o = out.cpu().double().numpy()
+        assert not np.isnan(o).any()
+        if name == "none in one sequence":
+            assert int(out_len[1].item()) == 0 and np.all(o[:, 1] == 0)
+            assert rel_err(out[:, :1], want[:, :1]) <= TOL
+        else:
+            assert rel_err(out, want) <= TOL, name
+        if name == "random":  # the split-latent variant over positions gives the plain variant's bits
+            wk2, wv2 = d["wk"].clone(), d["wv"].clone()
+            wk2[:, 256:] = 0
+            wv2[:, :256] = 0
+            a = kvc.decode_attn(L, dst, obt, out_len, d["q"], wk2, wv2, w.T, q_pos=d["q_pos"], num_splits=num_splits,
+                                tok_pos=tok_pos)
+            s = kvc.decode_attn(L, dst, obt, out_len, d["q"], wk2, wv2, w.T, q_pos=d["q_pos"], num_splits=num_splits,
+                                tok_pos=tok_pos, kv_split=256)
+            torch.cuda.synchronize()
+            assert torch.equal(a, s)
+
+
+def test_compacted_decode_int3():
+    w = synth.WORKLOADS["shared_latent_32k_evict30"].scaled(B=2, T=600, page_size=128, latent_bits=3)
+    seq = [600, 411]
+    inp = synth.make_inputs(w, seq_len=seq)
+    d = dev(inp)
+    m = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    gc, dst, obt, out_len, tok_pos, gm, cache, _ = _compact_pair(w, inp, d, m)
+    out = kvc.decode_attn(gpu_layout(w), dst, obt, out_len, d["q"], d["wk"], d["wv"], w.T, q_pos=d["q_pos"],
+                          tok_pos=tok_pos)
+    torch.cuda.synchronize()
+    assert rel_err(out, _masked_oracle(w, inp, cache, m)) <= TOL
+
+
+def test_compact_then_decode_full_size_sampled():
+    w = synth.WORKLOADS["shared_latent_32k_evict30"]
+    inp = synth.make_inputs(w)
+    d = dev(inp)
+    seq = [w.T] * w.B
+    print("[compact] full size: select, compress, compact, decode over positions", flush=True)
+    gm = kvc.evict_select(d["layer_scores"], d["seq_len"], w.evict_ratio)
+    gc = gpu_cache(w, d)
+    rec = int(gc.page_off[1].item() - gc.page_off[0].item())
+    dst = kvc.DeviceCache(gc.layout, torch.zeros_like(gc.pool), torch.arange(w.n_pages, dtype=torch.int64,
+                          device="cuda") * rec, None, None, torch.zeros(2, dtype=torch.int64, device="cuda"), w.n_pages)
+    obt = d["block_table"].flip(1).contiguous()
+    out_len, tok_pos = kvc.evict_compact(gpu_layout(w), gc, dst, d["block_table"], d["seq_len"], gm, obt)
+    out = kvc.decode_attn(gpu_layout(w), dst, obt, out_len, d["q"], d["wk"], d["wv"], w.T, q_pos=d["q_pos"],
+                          tok_pos=tok_pos)
+    masked = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
+                             q_pos=d["q_pos"], keep_mask=gm)
+    torch.cuda.synchronize()
+    m = E.keep_mask(inp["layer_scores"].numpy(), seq, w.evict_ratio)
+    assert np.array_equal(_u32(gm), m)
+    # the compacted length: every kept token once, tiles of 32 within 4 blocks (layout from the oracle's rule)
+    lens = out_len.cpu().numpy()
+    for b in range(w.B):
+        want_slots = E.compact_slots(np.nonzero(E.mask_bits(m, w.T)[b])[0])
+        assert lens[b] == len(want_slots)
+        assert np.array_equal(tok_pos[b, : lens[b]].cpu().numpy(), want_slots)
+    print(f"[compact] full size: {lens.tolist()} slots of {w.T}", flush=True)
+    assert rel_err(out, masked.cpu().double().numpy()) <= TOL
+    print("[compact] full size: oracle masked decode of sequence 1, kv head 6", flush=True)
+    cache = oracle_cache(w, inp)
+    sel_b = np.zeros(w.B, np.uint8); sel_b[1] = 1
+    sel_h = np.zeros(w.n_kv_heads, np.uint8); sel_h[6] = 1
+    want = _masked_oracle(w, inp, cache, m, sel_b, sel_h)
+    assert rel_err(out, want) <= TOL
