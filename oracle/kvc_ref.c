@@ -30,7 +30,11 @@
  *   2(i%4)..2(i%4)+1 of byte i/4.
  *
  *   Shared mode: a record is Lc (P x latent*latent_bits/8 code bytes) then Lm
- *   (P x latent/G pairs), each padded to 16 bytes.
+ *   (P x latent/G pairs), each padded to 16 bytes.  With the rotated residual
+ *   (JoLT: a Tucker form plus a rotated low-bit residual; each layer and head
+ *   has its own) then Kr, Vr (one part per (layer, kv head), layer-major, of
+ *   P x 32 code bytes) and Ks, Vs (one part per (layer, kv head) of P x fp16,
+ *   each part padded to 16 bytes).
  *
  *   Uniform rank: every slot of every page holds r_k_cap / r_v_cap, so all
  *   records have the same size.  Variable rank: slot s of page p holds rank
@@ -238,7 +242,7 @@ int kvc_ref_layout_check(const kvc_ref_layout* L) {
   if (L->r_k_cap <= 0 || L->r_v_cap <= 0 || L->r_k_cap % 8 || L->r_v_cap % 8) return KVC_REF_EINVAL;
   if (L->latent_bits != 32 && (L->group <= 0 || L->group % 8)) return KVC_REF_EINVAL;
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_REF_EINVAL;
-  if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_REF_EINVAL;
+  if (L->residual_bits && L->head_dim != 128) return KVC_REF_EINVAL;
   if (L->shared) {
     /* one latent for keys and values: one width (BellowsKV's retention table lists INT4 and INT3 for it) */
     if (L->n_layers <= 0 || !quant_bits_ok(L->latent_bits) || lat_bits(L, 1) != L->latent_bits || L->variable_rank ||
@@ -278,10 +282,32 @@ static sections head_sections(const kvc_ref_layout* L, int sum_code_k, int sum_c
   return S;
 }
 
+/* Block-shared record: [Lc codes][Lm pairs], each padded to 16 bytes; with the residual (residual_bits = 2) then
+ * [Kr][Vr][Ks][Vs], each holding one part per (layer, kv head) in layer-major order: P x d/4 code bytes per part,
+ * P x fp16 scales per part padded to 16 bytes.  Returns the latent part's bytes. */
+static int64_t shared_latent_bytes(const kvc_ref_layout* L) {
+  int64_t P = L->page_size;
+  return pad16(P * L->r_k_cap * L->latent_bits / 8) + pad16(P * 4 * ceil_div(L->r_k_cap, L->group));
+}
+
+/* the residual codes and scales of slot s for (layer, head) in a block-shared record */
+static void shared_residual_at(const kvc_ref_layout* L, const uint8_t* rec, int layer, int head, int s,
+                               const uint8_t** kr, const uint8_t** vr, const uint8_t** ks, const uint8_t** vs) {
+  int64_t P = L->page_size, n = (int64_t)L->n_layers * L->n_kv_heads, idx = (int64_t)layer * L->n_kv_heads + head;
+  int64_t cb = L->head_dim / 4, sb = pad16(P * 2);
+  const uint8_t* base = rec + shared_latent_bytes(L);
+  *kr = base + (idx * P + s) * cb;
+  *vr = base + (n + idx) * P * cb + s * cb;
+  *ks = base + 2 * n * P * cb + idx * sb + 2 * s;
+  *vs = base + 2 * n * P * cb + (n + idx) * sb + 2 * s;
+}
+
 int64_t kvc_ref_page_bytes_uniform(const kvc_ref_layout* L) {
   if (kvc_ref_layout_check(L)) return KVC_REF_EINVAL;
   int64_t P = L->page_size;
-  if (L->shared) return pad16(P * L->r_k_cap * L->latent_bits / 8) + pad16(P * 4 * ceil_div(L->r_k_cap, L->group));
+  if (L->shared)
+    return shared_latent_bytes(L) +
+           (L->residual_bits ? 2 * (int64_t)L->n_layers * L->n_kv_heads * (P * L->head_dim / 4 + pad16(P * 2)) : 0);
   sections S = head_sections(L, (int)(P * code_bytes(L, 0, L->r_k_cap)), (int)(P * code_bytes(L, 1, L->r_v_cap)),
                              (int)(P * meta_bytes(L, 0, L->r_k_cap)), (int)(P * meta_bytes(L, 1, L->r_v_cap)));
   return S.total * L->n_kv_heads;
@@ -448,6 +474,17 @@ int64_t kvc_ref_compress(const kvc_ref_layout* L, int B, int max_T, int max_bloc
         uint8_t* codes = rec + (int64_t)s * (lat * lb / 8);
         uint8_t* meta = rec + pad16((int64_t)P * lat * lb / 8) + (int64_t)s * 4 * ceil_div(lat, G);
         pack_latent(L, lb, lat_k + ((size_t)b * max_T + t) * lat, lat, codes, meta);
+        if (L->residual_bits) {  /* res_k, res_v [B][max_T][n_layers][Hkv][d] */
+          int d = L->head_dim;
+          for (int l = 0; l < L->n_layers; ++l)
+            for (int h = 0; h < Hkv; ++h) {
+              const uint8_t *kr, *vr, *ks, *vs;
+              shared_residual_at(L, rec, l, h, s, &kr, &vr, &ks, &vs);
+              size_t tk = (((size_t)b * max_T + t) * L->n_layers + l) * Hkv + h;
+              pack_residual(res_k + tk * d, d, (uint8_t*)kr, (uint8_t*)ks);
+              pack_residual(res_v + tk * d, d, (uint8_t*)vr, (uint8_t*)vs);
+            }
+        }
         continue;
       }
       for (int h = 0; h < Hkv; ++h) {
@@ -579,6 +616,12 @@ static void rebuild_token(const kvc_ref_layout* L, int which, int layer, int b, 
     const uint8_t* meta = rec + pad16((int64_t)P * lat * lb / 8) + (int64_t)s * 4 * ceil_div(lat, L->group);
     unpack_latent(L, lb, codes, meta, lat, lat, c);
     rebuild_shared(w + (size_t)layer * lat * Hkv * d, lat, Hkv * d, h * d, d, c, x);
+    if (L->residual_bits) {  /* the (layer, head)'s own rotated residual */
+      const uint8_t *kr, *vr, *ks, *vs;
+      shared_residual_at(L, rec, layer, h, s, &kr, &vr, &ks, &vs);
+      unpack_residual(which ? vr : kr, which ? vs : ks, d, e);
+      add_residual(H, d, e, x);
+    }
     return;
   }
   slot_view v = locate(L, pool, page_off, tok_rank, tok_off, p, s, h);

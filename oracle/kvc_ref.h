@@ -45,7 +45,7 @@ typedef struct {
   int r_v_cap;       /* value rank (cap); shared: equal to r_k_cap             */
   int group;         /* quantization group size along the latent axis          */
   int latent_bits;   /* key latent: 2, 3, 4 (codes + fp16 scale/zero) or 32 (fp32) */
-  int residual_bits; /* 0 or 2 (Hadamard-rotated 2-bit residual, head_dim 128) */
+  int residual_bits; /* 0 or 2 (Hadamard-rotated 2-bit residual, head_dim 128; per layer and head in shared mode) */
   int page_size;     /* tokens per page                                        */
   int variable_rank; /* 1: one rank per token, shared by K, V and all heads    */
   double rope_theta; /* RoPE base; 0 switches RoPE off                         */
@@ -77,7 +77,8 @@ void kvc_ref_quant_res2_n(const float* y, int64_t n_rows, int n, uint16_t* s16, 
 /* --- compression (from fp32 latents / rotated residuals) ---
  * block_table [B][max_blocks]; seq_len [B]; ranks [B][max_T] (variable_rank only)
  * lat_k, lat_v: [B][max_T][Hkv][r_cap] fp32 (shared mode: lat_k [B][max_T][latent])
- * res_k, res_v: [B][max_T][Hkv][128] fp32, already in the rotated domain (residual only)
+ * res_k, res_v: [B][max_T][Hkv][128] fp32 (shared mode: [B][max_T][n_layers][Hkv][128]), already in the
+ *   rotated domain (residual only)
  * outputs: pool (pool_bytes), page_off [n_pages], tok_rank [n_pages][P], tok_off [n_pages][P+1]
  * returns total bytes used (>= 0) or a negative status. */
 int64_t kvc_ref_compress(const kvc_ref_layout* L, int B, int max_T, int max_blocks,

@@ -237,9 +237,10 @@ def make_inputs(w: Workload, device="cpu", seq_len=None) -> dict:
             lk *= _decay_scale(w.r_k, w.latent_decay, dev)
             lv *= _decay_scale(w.r_v, w.latent_decay, dev)
         out["lat_k"], out["lat_v"] = lk, lv
-    if w.residual_bits:
-        out["res_k"] = torch.randn(B, T, Hkv, d, generator=_gen(w, 5, dev), device=dev) * w.residual_std
-        out["res_v"] = torch.randn(B, T, Hkv, d, generator=_gen(w, 6, dev), device=dev) * w.residual_std
+    if w.residual_bits:  # block-shared mode: one residual per layer and head ([B, T, L, Hkv, d])
+        rshape = (B, T, w.n_layers, Hkv, d) if w.shared else (B, T, Hkv, d)
+        out["res_k"] = torch.randn(rshape, generator=_gen(w, 5, dev), device=dev) * w.residual_std
+        out["res_v"] = torch.randn(rshape, generator=_gen(w, 6, dev), device=dev) * w.residual_std
     else:
         out["res_k"] = out["res_v"] = None
     if w.tucker:

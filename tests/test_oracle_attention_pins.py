@@ -493,3 +493,94 @@ def test_variable_rank_projection_truncates_to_each_tokens_rank():
             for t in range(int(seq[b]), 40):                     # rows past the length are left alone
                 assert not lat[b, t].any() and not res[b, t].any()
     assert seen == {8, 16, 32, 64}
+
+
+# ---------------------------------------------------------------- rotated residual on the block-shared latent
+# (JoLT index, Abstract, and JoLT thesis, "How JoLT works": the Tucker form plus a rotated low-bit residual; each
+# layer and head keeps its own residual of what its up-projection leaves)
+
+def _shared_res_case(n_layers=2, T=200, seq=(200, 77), B=2):
+    w = synth.WORKLOADS["shared_latent_32k"].scaled(B=B, T=T, n_layers=n_layers, page_size=64, residual_bits=2,
+                                                     residual_std=0.3, shuffle_pages=True)
+    inp = synth.make_inputs(w, seq_len=list(seq))
+    return w, inp
+
+
+def test_shared_zero_residual_equals_no_residual():
+    w, inp = _shared_res_case()
+    inp["res_k"] = torch.zeros_like(inp["res_k"]); inp["res_v"] = torch.zeros_like(inp["res_v"])
+    out_r = oracle_decode(w, inp, oracle_cache(w, inp))
+    wn = w.scaled(residual_bits=0)
+    inpn = dict(inp, res_k=None, res_v=None)
+    out_n = oracle_decode(wn, inpn, oracle_cache(wn, inpn))
+    assert np.array_equal(out_r, out_n)
+
+
+def test_shared_residual_record_holds_the_quantizer_outputs():
+    # read from the format description alone: after the latent's two sections, Kr and Vr hold one part of P x 32
+    # code bytes per (layer, kv head) in layer-major order, then Ks and Vs one part of P fp16 scales (padded to
+    # 16 bytes) per (layer, kv head); residual element i is bits 2(i % 4).. of byte i / 4
+    w, inp = _shared_res_case(n_layers=3)
+    pool, page_off, _, _ = oracle_cache(w, inp)
+    bt = np_any(inp["block_table"])
+    P, Hkv, NL = w.page_size, w.n_kv_heads, w.n_layers
+    pad = lambda x: (x + 15) // 16 * 16
+    lat_bytes = pad(P * 256) + pad(P * 4 * (512 // w.group))
+    n = NL * Hkv
+    assert np.array_equal(page_off, np.arange(w.n_pages) * (lat_bytes + 2 * n * (P * 32 + pad(2 * P))))
+    for (b, t, l, h) in [(0, 0, 0, 0), (0, 199, 2, 7), (1, 76, 1, 3), (1, 64, 0, 5), (0, 130, 2, 0)]:
+        rec = int(page_off[int(bt[b, t // P])]) + lat_bytes
+        s, idx = t % P, l * Hkv + h
+        for part, name in ((0, "res_k"), (1, "res_v")):
+            by = pool[rec + (part * n + idx) * P * 32 + s * 32: rec + (part * n + idx) * P * 32 + (s + 1) * 32]
+            codes = (by[:, None] >> (2 * np.arange(4))) & 3
+            sc = pool[rec + 2 * n * P * 32 + (part * n + idx) * pad(2 * P) + 2 * s:][:2].view(np.uint16)[0]
+            S, Q = ref.quant_res2(np_f32(inp[name])[b, t, l, h][None])
+            assert np.array_equal(codes.reshape(-1), Q[0]) and sc == S[0], (b, t, l, h, name)
+
+
+def test_shared_residual_adds_each_layer_and_heads_hadamard_of_its_codes():
+    # keys W_k[l]^T c + H e_k[l, h] and values W_v[l]^T c + H e_v[l, h], e the dequantized 2-bit codes of that
+    # layer and head (from the quantizer's outputs), H from scipy's Sylvester matrix; textbook attention in numpy
+    w, inp = _shared_res_case(n_layers=2)
+    out = oracle_decode(w, inp, oracle_cache(w, inp))
+    H = scipy.linalg.hadamard(128) / math.sqrt(128)
+    Wk = inp["wk"].double().numpy(); Wv = inp["wv"].double().numpy()
+    q = np_f32(inp["q"])
+    for b in range(w.B):
+        T = int(inp["seq_len"][b])
+        c = dequant_shared_latent(np_f32(inp["lat_k"])[b, :T], w.group)
+        for l in range(w.n_layers):
+            for h in (0, 6):
+                kv = []
+                for name, W in (("res_k", Wk), ("res_v", Wv)):
+                    S, Q = ref.quant_res2(np_f32(inp[name])[b, :T, l, h])
+                    e = (Q.astype(np.float64) - 1.5) * S.view(np.float16).astype(np.float64)[:, None]
+                    kv.append(c @ W[l][:, 128 * h: 128 * h + 128] + e @ H.T)
+                want = sdpa64(rope_complex(q[l, b, 4 * h: 4 * h + 4], T, w.rope_theta),
+                              rope_complex(kv[0], np.arange(T), w.rope_theta), kv[1])
+                assert np.allclose(out[l, b, 4 * h: 4 * h + 4], want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_shared_residual_with_embedded_per_layer_bases_equals_per_head_residual_mode():
+    # two layers, each with its own per-head bases embedded block-diagonally in W[l] and its own residuals: layer l
+    # of the shared decode equals the per-head residual decode of the same latents and layer l's residuals
+    wp = synth.WORKLOADS["residual_128k"].scaled(B=1, T=200, r_k=64, r_v=64, group=64, page_size=64)
+    per_layer = [synth.make_inputs(wp.scaled(seed=200 + l)) for l in range(2)]
+    base = per_layer[0]
+    lat = base["lat_k"]
+    ws = synth.WORKLOADS["shared_latent_32k"].scaled(B=1, T=200, n_layers=2, page_size=64, residual_bits=2)
+    Hkv, d = 8, 128
+    W = {n: torch.zeros(2, 512, Hkv * d, dtype=torch.bfloat16) for n in ("wk", "wv")}
+    for l in range(2):
+        for name in ("wk", "wv"):
+            for h in range(Hkv):
+                W[name][l, 64 * h: 64 * h + 64, d * h: d * h + d] = per_layer[l][name][h].T
+    q = torch.stack([per_layer[l]["q"] for l in range(2)])
+    res = {n: torch.stack([per_layer[l][n] for l in range(2)], dim=2).contiguous() for n in ("res_k", "res_v")}
+    inps = dict(base, lat_k=lat.reshape(1, 200, 512).contiguous(), lat_v=None, wk=W["wk"], wv=W["wv"], q=q, **res)
+    out_s = oracle_decode(ws, inps, oracle_cache(ws, inps))
+    for l in range(2):
+        inpl = dict(per_layer[l], lat_k=lat, lat_v=lat.clone())
+        out_p = oracle_decode(wp, inpl, oracle_cache(wp, inpl))
+        assert np.allclose(out_s[l], out_p, rtol=0, atol=1e-13 * np.abs(out_p).max())
