@@ -101,7 +101,7 @@ ALLOC_LADDER, ALLOC_WEIGHTS, ALLOC_MEAN = [8, 16, 32, 64], [1.0, 0.45, 0.2], 20.
 # place or compacted out of the pages (the compaction timed on its own).
 OTHER = ("llama8b_layer_8k", "shared_latent_32k", "shared_latent_32k_int3", "residual_128k", "varrank_paged_32k_int3",
          "llama8b_layer_8k_k3v2",
-         "tucker_group_32k", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered",
+         "tucker_group_32k", "tucker_group_32k_res", "shared_latent_32k_evict30", "shared_latent_32k_evict30_clustered",
          "shared_latent_32k_evict30_compact")
 
 

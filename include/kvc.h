@@ -56,8 +56,12 @@
  *  tok_rank[p][s] (0 for unused slots) is the rank of K and V for all heads,
  *  and tok_off[p][s] holds the exclusive prefix over slots of the ranks
  *  (bits 0-15) and of ceil(rank/group) (bits 16-31); tok_off[p][P] = totals.
- *  Block-shared mode: a record is Lc (P x latent/2 code bytes) and Lm
- *  (P x latent/group pairs), each padded to 16 bytes.
+ *  Block-shared mode: a record is Lc (P x latent*b/8 code bytes) and Lm
+ *  (P x latent/group pairs), each padded to 16 bytes; with the residual
+ *  (each layer and kv head its own: JoLT thesis page, "How JoLT works", a
+ *  Tucker form plus a rotated low-bit residual) then Kr and Vr (one part of
+ *  P x 32 code bytes per (layer, kv head), layer-major) and Ks and Vs (one
+ *  part of P fp16 scales per (layer, kv head), each padded to 16 bytes).
  */
 #ifndef KVC_H
 #define KVC_H
@@ -95,7 +99,8 @@ typedef struct {
   int32_t r_v_cap;        /* value rank (cap); shared: equal to r_k_cap                    */
   int32_t group;          /* quantization group along the latent axis (multiple of 16)     */
   int32_t latent_bits;    /* key latent: 2, 3, 4 (codes + fp16 scale/zero) or 32 (fp32)   */
-  int32_t residual_bits;  /* 0 or 2 (Hadamard-rotated residual; head_dim 128, per-head)    */
+  int32_t residual_bits;  /* 0 or 2 (Hadamard-rotated residual; head_dim 128; shared mode:  */
+                          /*   one per layer and kv head, INT4 latent)                     */
   int32_t page_size;      /* tokens per page, a multiple of 32, at most 256                */
   int32_t variable_rank;  /* 1: per-token rank in tok_rank / tok_off                       */
   double rope_theta;      /* RoPE base (rotate-half pairs (j, j + d/2)); 0 = no RoPE       */
@@ -123,7 +128,8 @@ typedef struct {
   const int32_t* seq_len;        /* [B], 1..max_T tokens to compress per sequence               */
   const uint8_t* ranks;          /* [B][max_T] variable rank: multiple of 8 in [8, cap]        */
   /* FROM_LATENT: fp32 latents [B][max_T][Hkv][r_cap] (shared mode: lat_k [B][max_T][latent]),
-   * rotated-domain residuals [B][max_T][Hkv][head_dim] (residual_bits = 2).
+   * rotated-domain residuals [B][max_T][Hkv][head_dim] (residual_bits = 2; shared mode
+   * [B][max_T][n_layers][Hkv][head_dim]).
    * FROM_DENSE: these four are outputs (required): the fp32 projection c = B_r^T k truncated to
    * the token's rank, and the rotated truncation residual H (k - B_r c), which are then quantized. */
   float* lat_k;
@@ -237,12 +243,13 @@ kvc_status kvc_decode_workspace_bytes(const kvc_layout* layout, int32_t B, int32
 
 /* One decode step of softmax attention over the compressed cache (hot path).
  * For every sequence b, layer l (shared mode) and query head h with kv head g = h / (Hq/Hkv):
- *   k_t = B_k[g] c_k(t) [+ H e_k(t)]   (shared: W_k[l][:, g*d:(g+1)*d]^T c(t))
+ *   k_t = B_k[g] c_k(t) [+ H e_k(t)]   (shared: W_k[l][:, g*d:(g+1)*d]^T c(t) [+ H e_k(l, g, t)])
  *   v_t = B_v[g] c_v(t) [+ H e_v(t)]
  *   out[l][b][h] = sum_t softmax_t( RoPE(q, q_pos) . RoPE(k_t, t) / sqrt(d) ) v_t,  t < seq_len[b]
  * with c the dequantized latent (code * scale + zero, zero beyond the token's rank), e the
  * dequantized rotated residual and H the normalized 128-point Sylvester Hadamard.
- * out: fp32 [(n_layers)][B][Hq][d].  ws: workspace of kvc_decode_workspace_bytes. */
+ * out: fp32 [(n_layers)][B][Hq][d].  ws: workspace of kvc_decode_workspace_bytes.  A block-shared layout with
+ * the residual takes no keep_mask or tok_pos (UNSUPPORTED). */
 kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,
                            float* out, void* ws, size_t ws_bytes, void* stream);
 
@@ -505,7 +512,7 @@ typedef struct {
  * the keep mask gives on the source cache.  Two launches (a scan per sequence, then a copy per destination
  * page); deterministic; asynchronous on stream.  INVALID_ARG for a per-head layout, null pointers or sizes out
  * of range (max_blocks * page_size above 262144), UNSUPPORTED for a layout the block-shared decode does not
- * serve, MISALIGNED for pointers not 16-byte aligned. */
+ * serve or one with the residual, MISALIGNED for pointers not 16-byte aligned (keep_mask: 4-byte). */
 kvc_status kvc_evict_compact(const kvc_layout* layout, const kvc_cache* src, const kvc_cache* dst,
                              const kvc_compact_in* in, int32_t* out_seq_len, int32_t* tok_pos, void* stream);
 

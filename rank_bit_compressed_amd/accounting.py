@@ -21,12 +21,15 @@ def compressed_stream_bytes(w, ranks: torch.Tensor | None, seq_len) -> dict:
     per (token, kv head): K codes r_k * b_k / 8 + 4 bytes per group (b_k the key latent bits), V likewise with b_v,
     and for the rotated residual
     2 x (32 code bytes + 2 scale bytes); block-shared mode: per token latent * b / 8 + 4 per group (b the
-    latent bits), read once for all layers and heads.  Variable rank adds the per-token rank byte and 4-byte offset word.
+    latent bits), read once for all layers and heads, plus with the residual 2 x (32 + 2) per layer and head.
+    Variable rank adds the per-token rank byte and 4-byte offset word.
     """
     seq_len = [int(x) for x in seq_len]
     n_tok = sum(seq_len)
     if w.shared:
         per_tok = w.r_k * w.latent_bits // 8 + 4 * math.ceil(w.r_k / w.group)
+        if w.residual_bits:
+            per_tok += w.n_layers * w.n_kv_heads * 2 * (w.head_dim * w.residual_bits // 8 + 2)
         return {"stream": n_tok * per_tok, "tables": 0, "tokens": n_tok}
     Hkv = w.n_kv_heads
     bk = w.latent_bits

@@ -64,7 +64,7 @@ static kvc_status check_layout(const kvc_layout* L) {
   if (L->r_k_cap > 1024 || L->r_v_cap > 1024) return KVC_ERR_INVALID_ARG;
   if (L->latent_bits != 32 && (L->group <= 0 || L->group % 8)) return KVC_ERR_INVALID_ARG;
   if (L->residual_bits != 0 && L->residual_bits != 2) return KVC_ERR_INVALID_ARG;
-  if (L->residual_bits && (L->head_dim != 128 || L->shared)) return KVC_ERR_INVALID_ARG;
+  if (L->residual_bits && L->head_dim != 128) return KVC_ERR_INVALID_ARG;
   if (L->shared) {
     // one latent for keys and values: one width (4, or the lower-bit codecs 3 and 2)
     if (L->n_layers <= 0 || lat_bits_k(*L) == 32 || lat_bits_v(*L) != lat_bits_k(*L) || L->variable_rank ||
@@ -165,6 +165,7 @@ kvc_status kvc_decode_attn(const kvc_layout* layout, const kvc_cache* cache, con
   if (in->kv_split && (!L.shared || 2 * in->kv_split != L.r_k_cap)) return KVC_ERR_INVALID_ARG;
   if (in->keep_mask && ((uintptr_t)in->keep_mask & 3)) return KVC_ERR_MISALIGNED;
   if (in->tok_pos && (!L.shared || in->keep_mask || !in->q_pos)) return KVC_ERR_INVALID_ARG;
+  if (L.shared && L.residual_bits && (in->keep_mask || in->tok_pos)) return KVC_ERR_UNSUPPORTED;
   if (in->tok_pos && ((uintptr_t)in->tok_pos & 3)) return KVC_ERR_MISALIGNED;
   if ((int64_t)in->max_blocks * L.page_size < in->max_T) return KVC_ERR_INVALID_ARG;
   if (in->q_dtype != KVC_F32 && in->q_dtype != KVC_BF16) return KVC_ERR_INVALID_ARG;

@@ -109,6 +109,8 @@ struct PackArgs {
   const uint8_t* tok_rank;
   const uint32_t* tok_off;
   int B, max_T, max_blocks, P, Hkv, d, rk, rv, G, latent_bits, latent_bits_v, residual, variable_rank, shared;
+  int n_layers;  // shared mode: layers with their own residuals
+  int64_t lat_bytes;  // shared mode: bytes of the latent's sections of a record
   HeadSections S_uniform;
 };
 
@@ -191,25 +193,39 @@ __global__ __launch_bounds__(256) void pack_latent_kernel(PackArgs a, int groups
   *(uint32_t*)(meta + 4 * gi) = (uint32_t)s16 | ((uint32_t)z16 << 16);
 }
 
-// Thread = (b, t, head, which): 2-bit quantizer of the 128-value rotated residual.
+// Thread = (b, t, [layer,] head, which): 2-bit quantizer of the 128-value rotated residual.  Block-shared mode:
+// one residual per (layer, head), res_k / res_v [B][max_T][n_layers][Hkv][d].
 __global__ __launch_bounds__(256) void pack_residual_kernel(PackArgs a) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t tok = idx / (2 * a.Hkv);
+  const int nl = a.shared ? a.n_layers : 1;
+  const int64_t tok = idx / (2 * a.Hkv * nl);
   if (tok >= (int64_t)a.B * a.max_T) return;
   const int b = (int)(tok / a.max_T), t = (int)(tok % a.max_T);
   if (t >= a.seq_len[b]) return;
-  const int h = (int)(idx % (2 * a.Hkv)) >> 1, which = (int)(idx & 1);
+  const int lh = (int)(idx % (2 * a.Hkv * nl)) >> 1, which = (int)(idx & 1);  // lh = layer * Hkv + head
+  const int h = lh % a.Hkv;
   const int P = a.P, page = a.block_table[(size_t)b * a.max_blocks + t / P], slot = t % P;
-  HeadSections S;
-  if (a.variable_rank) {
-    const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
-    const int64_t cb = (int64_t)(tot & 0xFFFFu) * a.latent_bits / 8, mb = 4 * (int64_t)(tot >> 16);
-    S = head_sections(cb, cb, mb, mb, P, a.d, 1);
+  const float* y = (which ? a.res_v : a.res_k) + (((size_t)b * a.max_T + t) * a.Hkv * nl + lh) * a.d;
+  uint8_t* codes;
+  uint16_t* scale;
+  if (a.shared) {
+    uint8_t* rec = a.pool + a.page_off[page];
+    const int n = a.n_layers * a.Hkv;
+    codes = rec + shared_res_part(a.lat_bytes, P, a.d, n, which, lh) + (int64_t)slot * (a.d / 4);
+    scale = (uint16_t*)(rec + shared_res_part(a.lat_bytes, P, a.d, n, 2 + which, lh)) + slot;
   } else {
-    S = a.S_uniform;
+    HeadSections S;
+    if (a.variable_rank) {
+      const uint32_t tot = a.tok_off[(size_t)page * (P + 1) + P];
+      const int64_t cb = (int64_t)(tot & 0xFFFFu) * a.latent_bits / 8, mb = 4 * (int64_t)(tot >> 16);
+      S = head_sections(cb, cb, mb, mb, P, a.d, 1);
+    } else {
+      S = a.S_uniform;
+    }
+    uint8_t* hb = a.pool + a.page_off[page] + (int64_t)h * S.hb;
+    codes = hb + (which ? S.vr : S.kr) + (int64_t)slot * (a.d / 4);
+    scale = (uint16_t*)(hb + (which ? S.vs : S.ks)) + slot;
   }
-  uint8_t* hb = a.pool + a.page_off[page] + (int64_t)h * S.hb;
-  const float* y = (which ? a.res_v : a.res_k) + (((size_t)b * a.max_T + t) * a.Hkv + h) * a.d;
   float amax = 0.0f;
   for (int i = 0; i < a.d; ++i) {
     const float m = fabsf(y[i]);
@@ -217,7 +233,6 @@ __global__ __launch_bounds__(256) void pack_residual_kernel(PackArgs a) {
   }
   const uint16_t s16 = f16_bits(__fdiv_rn(amax, 1.5f));
   const float s = f16_val(s16);
-  uint8_t* codes = hb + (which ? S.vr : S.kr) + (int64_t)slot * (a.d / 4);
   for (int i0 = 0; i0 < a.d; i0 += 16) {
     uint32_t word = 0;
     for (int j = 0; j < 16; ++j) {
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(256) void pack_residual_kernel(PackArgs a) {
     }
     *(uint32_t*)(codes + i0 / 4) = word;
   }
-  *(uint16_t*)(hb + (which ? S.vs : S.ks) + 2 * slot) = s16;
+  *scale = s16;
 }
 
 #pragma clang fp contract(on)
@@ -369,6 +384,7 @@ kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const k
   a.d = d; a.rk = L.r_k_cap; a.rv = L.r_v_cap; a.G = L.group; a.latent_bits = lat_bits_k(L);
   a.latent_bits_v = lat_bits_v(L);
   a.residual = L.residual_bits; a.variable_rank = L.variable_rank; a.shared = L.shared;
+  a.n_layers = L.n_layers; a.lat_bytes = shared_latent_bytes(L);
   a.S_uniform = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
                               (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
                               (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),
@@ -378,7 +394,7 @@ kvc_status compress_impl(const kvc_layout& L, const kvc_compress_in& in, const k
   hipLaunchKernelGGL(pack_latent_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a, gpi);
   KVC_CHECK();
   if (L.residual_bits) {
-    const int64_t rt = (int64_t)in.B * in.max_T * 2 * Hkv;
+    const int64_t rt = (int64_t)in.B * in.max_T * 2 * Hkv * (L.shared ? L.n_layers : 1);
     hipLaunchKernelGGL(pack_residual_kernel, dim3((unsigned)((rt + 255) / 256)), dim3(256), 0, st, a);
     KVC_CHECK();
   }

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "lds_copy.hpp"
+#include "res_codes.hpp"
 
 namespace kvc {
 
@@ -43,6 +44,9 @@ static constexpr float STAU = 8.0f;     // lazy-max slack, log2 units
 static constexpr int SRAW = 2048 + 512; // ring slot: a wave's codes of 32 tokens, then its pairs (two copies)
 static constexpr int SVAR = 4;          // positions mode: query bases per super-tile (blocks of 32 positions)
 static constexpr int SRT = 36;          // positions mode: dwords per row of the RoPE factor table (32 + padding)
+static constexpr int SRR = 2048 + 128;  // residual mode: a super-tile's K and V residual codes, then their scales
+static constexpr int SRRN = 6;          // residual mode: super-tiles in the shared residual ring
+static constexpr int SRCS = 32 * 16 + 64;  // residual mode: bytes per chunk row of a value-residual tile (padded)
 static constexpr int SQB = SD + 8;      // fp16 per rotated query head (and variant) in LDS: 256 bytes + 16 of padding,
                                         // so that the score operand reads of 16 heads x variants hit distinct banks
 // a wave's fp16 tile: chunk c (8 coordinates) of token t at byte SCS c + 16 t, 16 chunks; the row of a chunk is
@@ -66,6 +70,8 @@ struct DecodeSharedArgs {
   int keep_words;
   const int32_t* tok_pos;  // positions mode: source position of each slot [B][pos_row], -1 for none
   int pos_row;
+  int64_t lat_bytes;  // residual mode: bytes of a record's latent sections
+  int rec_bytes;      // residual mode: bytes of a record
   float* ws;
   int q_bf16, B, Hkv, Hq, L, max_blocks, P, G, n_splits, st_per_split, part_stride;
   double theta;
@@ -74,11 +80,12 @@ struct DecodeSharedArgs {
 static constexpr int SMAX_TILES = 1024;  // super-tiles per split (the page record address of each)
 
 struct SharedLds {
-  int raw, vt, qt, theta, sp, pt, addr, keep, rtab, posr, total;
+  int raw, vt, qt, theta, sp, pt, addr, keep, rtab, posr, rres, vres, pt2, total;
 };
 // pos: the positions mode (a ring of the super-tiles' slot positions, SVAR query bases per super-tile, a table of
-// the RoPE factors of the 32 in-block offsets)
-__host__ __device__ constexpr SharedLds shared_lds(bool pos) {
+// the RoPE factors of the 32 in-block offsets).  res: the residual mode (a ring of the super-tiles' residual codes
+// and scales shared by the waves, per-wave value-residual tiles, the probabilities times the value scales).
+__host__ __device__ constexpr SharedLds shared_lds(bool pos, bool res = false) {
   SharedLds L{};
   int o = 0;
   L.raw = o; o += 4 * 4 * SRAW;                          // per wave: staging ring of 4 super-tiles
@@ -91,6 +98,9 @@ __host__ __device__ constexpr SharedLds shared_lds(bool pos) {
   L.keep = o; o += SMAX_TILES * 4;                       // keep-mask word (positions mode: base block) of each
   L.rtab = o; o += pos ? 64 * SRT * 4 : 0;               // positions mode: RoPE factors [half][offset u][32]
   L.posr = o; o += pos ? 8 * 32 * 4 : 0;                 // positions mode: slot positions of super-tile k at k % 8
+  L.rres = o; o += res ? SRRN * SRR : 0;                 // residual mode: ring of the super-tiles' residuals
+  L.vres = o; o += res ? 16 * SRCS : 0;                  // residual mode: value waves' fp16 tiles, 16 chunks in all
+  L.pt2 = o; o += res ? 4 * 32 * SGQ * 2 : 0;            // residual mode: [wave][token][head] p * value scale
   L.total = o;
   return L;
 }
@@ -111,17 +121,27 @@ __device__ inline int qfrag_index(int head, int dim) {
 // rows, W_v on the lower, as for keys and values with their own token factors): waves 0-1 then do only the key
 // work and waves 2-3 only the value product; their skipped products are exact zeros, so the output is the same.
 // KB: latent code bits (4; or 3 and 2, whose codes a wave stages token-major and spreads to the INT4 nibble layout)
+// RES: the rotated 2-bit residual of each (layer, head) (KB = 4, no keep mask, no positions).  Its codes and scales
+// are staged by waves 0-2 (one copy each per super-tile) into a ring every wave reads after the next score barrier.
+// Keys: the key waves add K_res = (s / sqrt(128)) (H' c - 192 [d = 0]) of their head-dim blocks (the fp8 matrix
+// instruction with the +-1 Hadamard, as in the per-head residual kernel) to their partial keys before RoPE.
+// Values: the value waves accumulate sum_t p_t s_t (2c - 3) / (2 sqrt(128)) on their share of the 128 rotated
+// coordinates; the merge applies H'.
 // POS: a compacted cache whose slots hold tokens at the source positions tok_pos (no keep mask).  A super-tile's
 // tokens lie within SVAR blocks of 32 positions from its first slot's block `base` (the layout the compaction
 // writes): a token at position 32 (base + v) + u is rotated by R(u), from a table, and scored against the query
 // rotated by R(q_pos - 32 (base + v)), one of SVAR variants in the score operand's rows.  Other slots take no part.
-template <bool KEEP, bool SPLIT, int KB, bool POS>
+template <bool KEEP, bool SPLIT, int KB, bool POS, bool RES>
 __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
   constexpr int CB = SLAT * KB / 8;  // code bytes per token
   constexpr int QB = CB / 4;         // a wave's quarter of them
   constexpr int NCH = QB / 16;       // its 16-byte chunks per token
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr SharedLds LY = shared_lds(POS);
+  constexpr SharedLds LY = shared_lds(POS, RES);
+  constexpr int NKW = SPLIT ? 2 : 4;   // waves doing key work (the first NKW)
+  constexpr int NRB = 4 / NKW;         // residual mode: head-dim blocks of keys per key wave (blocks wv + NKW j)
+  constexpr int CPW = 128 / NKW;       // residual mode: value coordinates per value wave (the last NKW waves)
+  constexpr int RST = CPW / 16;        // residual mode: 16-coordinate value steps per value wave
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 31, hf = lane >> 5, rho = lane & 15, grp = lane >> 4;
@@ -157,6 +177,31 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         // the fragments stay in the accumulator registers (the matrix instructions read their A operand from
         // there directly; the vector registers are needed for the rest)
         asm volatile("" : "=a"(wf[g][j]) : "0"(f));
+      }
+    }
+  }
+  // residual mode: +-1 Hadamard rows of this key wave's head-dim blocks g = wv + NKW j as fp8 A fragments (row t <->
+  // the block's head dim, byte b of lane half hf's 32 of block-half be <-> coordinate 64 be + res8_coord(hf, b);
+  // e4m3 +1 = 0x38, -1 = 0xB8), kept in the accumulator registers the fp8 products read directly
+  v8i_t hr[NRB][2];
+  if (RES && (!SPLIT || wv < 2)) {
+#pragma unroll
+    for (int j = 0; j < NRB; ++j) {
+      const int g = wv + NKW * j;
+      const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
+#pragma unroll
+      for (int be = 0; be < 2; ++be) {
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 64 * be + res8_coord(hf, 4 * o + q);
+            w |= ((__builtin_popcount(dim & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
+          }
+          hr[j][be][o] = (int)w;
+        }
+        asm volatile("" : "=a"(hr[j][be]) : "0"(hr[j][be]));
       }
     }
   }
@@ -239,6 +284,11 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   _Float16* qts = (_Float16*)(smem + LY.qt);       // rotated query of super-tile k: buffer k % 3 (see rot_q)
   float* sp = (float*)(smem + LY.sp);
   _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * SGQ;
+  const uint8_t* rres = smem + LY.rres;  // residual mode: super-tile k's residual at rres + (k % SRRN) * SRR
+  const uint32_t rres_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.rres));
+  uint8_t* vr_w = smem + LY.vres + max(0, wv - (4 - NKW)) * (CPW / 8) * SRCS;  // value waves' residual tiles
+  _Float16* pt2 = (_Float16*)(smem + LY.pt2) + wv * 32 * SGQ;
+  constexpr float RSCALE = 0.04419417382415922f;  // 1 / (2 sqrt(128))
 
   const int64_t meta_base = pad16((int64_t)P * CB);
 
@@ -275,11 +325,25 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     if (POS && wv == 0 && lane < 32)  // the 32 slots' source positions, for every wave (read after a barrier)
       copy4_to_lds(buffer_rsrc(a.tok_pos + (size_t)b * a.pos_row + (st_begin + kk) * 32, 128),
                    posr_lds + (k & 7) * 128, 4 * lane);
+    if (RES && wv < 3) {  // the super-tile's residual of this (layer, head): K codes, V codes, both scales
+      const i32x4_t rr = buffer_rsrc(a.pool + (at - (int64_t)slot0 * CB), a.rec_bytes);
+      const uint32_t rdst = rres_lds + (k % SRRN) * SRR;
+      const int n = a.L * a.Hkv, idx = l * a.Hkv + h;
+      if (wv < 2)
+        copy16_to_lds(rr, rdst + 1024 * wv, (int)shared_res_part(a.lat_bytes, P, SD, n, wv, idx) + 32 * slot0 +
+                                                16 * lane);
+      else if (lane < 32)
+        copy4_to_lds(rr, rdst + 2048, (int)shared_res_part(a.lat_bytes, P, SD, n, 2 + (lane >> 4), idx) +
+                                          2 * slot0 + 4 * (lane & 15));
+    }
   };
 
   f4 acc[SNJ];  // value latent on this wave's coordinates, 16 per step, rows = query heads (replicated)
 #pragma unroll
   for (int i = 0; i < SNJ; ++i) acc[i] = f4{0, 0, 0, 0};
+  f4 accr[RST];  // residual mode: the rotated value residual on this value wave's coordinates
+#pragma unroll
+  for (int i = 0; i < RST; ++i) accr[i] = f4{0, 0, 0, 0};
   float m_ref[SGQ], psum[SGQ];
 #pragma unroll
   for (int i = 0; i < SGQ; ++i) {
@@ -346,9 +410,9 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ], int pc, int& pn) {
     issue(k + 4);  // ring slot k % 4 held super-tile k, dequantized in the previous step
     const int t0 = (st_begin + k) * 32;
-    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each; wave 0 of the positions mode five) may still
-    // be in flight
-    if (POS && wv == 0)
+    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each; five for wave 0 of the positions mode and
+    // waves 0-2 of the residual mode) may still be in flight
+    if ((POS && wv == 0) || (RES && wv < 3))
       __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
@@ -393,6 +457,25 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? (t >> 2) & (SVAR - 1) : 0)) * SGQ * SQB +
                                (t & 3) * SQB) + hf;
     f16v_t sc = {};
+    // residual mode: the key residual codes of this lane's token (one per byte: the fp8 B operands of H' c) and its
+    // scale; super-tile k's residual is visible since the previous barrier.  H' c of a block is formed beside the
+    // block's up-projection and added, scaled, before the block's RoPE.
+    f16v_t ra = {};
+    v8i_t er[2];
+    float ksc = 0.0f;
+    if (RES && (!SPLIT || wv < 2)) {
+      const uint8_t* rr = rres + (k % SRRN) * SRR;
+      uint32_t krw[4];
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(rr + 32 * t + 4 * (4 * be + 2 * hf + i));
+      ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rr + 2048 + 2 * t)) * (2.0f * RSCALE);
+#pragma unroll
+      for (int be = 0; be < 2; ++be)
+#pragma unroll
+        for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
+    }
     // a super-tile whose tokens are all evicted contributes nothing: only the next one's dequantization runs
     const bool empty = KEEP && tkeep[k] == 0u;
     if (SPLIT && wv >= 2) {  // value waves: only the next super-tile's value tile
@@ -412,6 +495,14 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         kp[g] = f16v_t{};
 #pragma unroll
         for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
+        if (RES) {  // H' c of block g, if it is one of this wave's (exact integers)
+#pragma unroll
+          for (int j = 0; j < NRB; ++j)
+            if (g == wv + NKW * j) {
+              ra = mfma_f8_codes(hr[j][1], er[1], mfma_f8_codes(hr[j][0], er[0], f16v_t{}));
+              if (g == 0 && hf == 0) ra[0] -= 192.0f;  // H' 1 is 128 at head dim 0 (row 0): the -1.5 offset
+            }
+        }
 #pragma unroll
         for (int jj = 2 * g; jj < 2 * g + 2; ++jj) {
           bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
@@ -419,6 +510,13 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         }
       }
       if (g > 0) {
+        if (RES) {  // the key residual of block g - 1, if it is one of this wave's
+#pragma unroll
+          for (int j = 0; j < NRB; ++j)
+            if (g - 1 == wv + NKW * j)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) kp[g - 1][i] += ksc * ra[i];
+        }
         // rotated pairs (x, y) of rows 8st + 4hf + m, m < 4, are the k-slots 8hf + 2m, 2m + 1 of score step st
         u32x4_t kr[2];
 #pragma unroll
@@ -477,6 +575,11 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       for (int nt = 0; nt < SNJ; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha[i];
+      if (RES)
+#pragma unroll
+        for (int nt = 0; nt < RST; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accr[nt][i] *= alpha[i];
       fresh = false;
     }
     float p[SGQ];
@@ -486,7 +589,28 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       psum[i] += p[i];
     }
     if (hf == 0) *(h4*)(pt + SGQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    // residual mode, value waves: the token's 2c - 3 over this wave's coordinates into its tile (chunk 2 jj + hf <->
+    // coordinates CPW vw + 16 jj + res_coord(hf, e)), and p times the token's value scale / (2 sqrt(128))
+    if (RES && (!SPLIT || wv >= 2)) {
+      const uint8_t* rr = rres + (k % SRRN) * SRR;
+      const int vw = wv - (4 - NKW);
+#pragma unroll
+      for (int jj = 0; jj < RST; ++jj)
+        *(h8*)(vr_w + SRCS * (2 * jj + hf) + 16 * t) =
+            res_2c3(*(const uint32_t*)(rr + 1024 + 32 * t + 4 * (RST * vw + jj)), hf);
+      const float vsc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rr + 2048 + 64 + 2 * t)) * RSCALE;
+      if (hf == 0)
+        *(h4*)(pt2 + SGQ * t) = h4{(_Float16)(p[0] * vsc), (_Float16)(p[1] * vsc), (_Float16)(p[2] * vsc),
+                                   (_Float16)(p[3] * vsc)};
+    }
     wave_lds_sync();
+    if (RES && (!SPLIT || wv >= 2)) {  // the rotated value residual: (p s) x (2c - 3), 16 coordinates per step
+      const h8 pops = lds_tr8s(pt2 + SGQ * (8 * grp + (rho >> 2)), pt2 + SGQ * (8 * grp + 4 + (rho >> 2)));
+      const int q4 = rho & 3;
+      const uint8_t* vb = vr_w + SRCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
+#pragma unroll
+      for (int nt = 0; nt < RST; ++nt) accr[nt] = mfma16x16x32(pops, lds_tr8s(vb + 2 * SRCS * nt, vb + 2 * SRCS * nt + 64), accr[nt]);
+    }
     // P as the A operand of the 16x16x32 value product: row l % 16 <-> head l % 4, k-slot 8g + j <-> token 8g + j
     // (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
     // value latent: step nt covers chunks 2nt, 2nt + 1; column n <-> coordinate 128w + 16nt + 8(n/8) + perm8(n%8);
@@ -507,7 +631,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // prologue: super-tiles 0-3 in flight, wait for 0, dequantize it; rotated queries of 0 and 1
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue(j);
-    if (POS && wv == 0)
+    if ((POS && wv == 0) || (RES && wv < 3))
       __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
@@ -547,16 +671,26 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[2 * SGQ + i * SLAT + coord] = acc[nt][i];
     }
+    if (RES && (!SPLIT || wv >= 2)) {  // residual column n of step nt: chunk 2nt + n / 8, element n % 8
+#pragma unroll
+      for (int nt = 0; nt < RST; ++nt) {
+        const int coord = CPW * (wv - (4 - NKW)) + 16 * nt + res_coord(rho >> 3, rho & 7);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[2 * SGQ + SGQ * SLAT + i * SD + coord] = accr[nt][i];
+      }
+    }
   }
 }
 
-// out[l][b][h*4 + hq] = W_v[l][:, h*128 : (h+1)*128]^T c* / l*, over the splits' partials: one workgroup per
-// (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the threads,
-// eight independent partial sums).
+// out[l][b][h*4 + hq] = (W_v[l][:, h*128 : (h+1)*128]^T c* + H' r*) / l*, over the splits' partials (r*: the
+// rotated value residual of the residual mode, H' the +-1 Hadamard; its accumulators carry 1 / sqrt(128)): one
+// workgroup per (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the
+// threads, eight independent partial sums).
 __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, int64_t w_stride,
                                                           float* out, int B, int Hkv, int Hq, int n_splits,
-                                                          int part_stride, int c_begin) {
+                                                          int part_stride, int c_begin, int res) {
   __shared__ float cst[SLAT];
+  __shared__ float rst[SD];
   __shared__ float lst;
   int id = blockIdx.x;
   const int hq_all = id % Hq; id /= Hq;
@@ -567,7 +701,7 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
   const float* parts = ws + (((size_t)l * Hkv + h) * B + b) * n_splits * part_stride;
   float m = -INFINITY;
   for (int p = 0; p < n_splits; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
-  float lsum = 0.0f, c[SLAT / SD];
+  float lsum = 0.0f, c[SLAT / SD], r = 0.0f;
 #pragma unroll
   for (int k = 0; k < SLAT / SD; ++k) c[k] = 0.0f;
   for (int p = 0; p < n_splits; ++p) {
@@ -577,9 +711,11 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
     lsum += w * pp[SGQ + hq];
 #pragma unroll
     for (int k = 0; k < SLAT / SD; ++k) c[k] += w * pp[2 * SGQ + hq * SLAT + d + SD * k];
+    if (res) r += w * pp[2 * SGQ + SGQ * SLAT + hq * SD + d];
   }
 #pragma unroll
   for (int k = 0; k < SLAT / SD; ++k) cst[d + SD * k] = c[k];
+  rst[d] = r;
   if (d == 0) lst = lsum;
   __syncthreads();
   const size_t width = (size_t)Hkv * SD;
@@ -589,7 +725,12 @@ __global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] += __builtin_bit_cast(float, (uint32_t)W[(size_t)(i + e) * width] << 16) * cst[i + e];
   }
-  const float sum = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+  float sum = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+  if (res) {
+    float rr = 0.0f;
+    for (int i = 0; i < SD; ++i) rr += (__builtin_popcount(d & i) & 1) ? -rst[i] : rst[i];
+    sum += rr;
+  }
   out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = lst > 0.0f ? sum / lst : 0.0f;  // zero: no token kept
 }
 
@@ -599,20 +740,22 @@ bool shared_supported(const kvc_layout& L) {
   const int kb = lat_bits_k(L);
   return L.shared && L.head_dim == SD && L.r_k_cap == SLAT && L.n_q_heads == SGQ * L.n_kv_heads &&
          (kb == 4 || kb == 3 || kb == 2) && lat_bits_v(L) == kb && L.group >= 32 && L.group <= SLAT &&
-         (L.group & (L.group - 1)) == 0;
+         (L.group & (L.group - 1)) == 0 && (!L.residual_bits || kb == 4);
 }
+
+static int shared_part_stride(const kvc_layout& L) { return 2 * SGQ + SGQ * SLAT + (L.residual_bits ? SGQ * SD : 0); }
 
 size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {
-  return (size_t)L.n_layers * L.n_kv_heads * B * n_splits * (2 * SGQ + SGQ * SLAT) * sizeof(float);
+  return (size_t)L.n_layers * L.n_kv_heads * B * n_splits * shared_part_stride(L) * sizeof(float);
 }
 
-template <bool KEEP, bool SPLIT, int KB, bool POS>
+template <bool KEEP, bool SPLIT, int KB, bool POS, bool RES = false>
 static hipError_t launch_shared_one(int grid, hipStream_t st, const DecodeSharedArgs& a) {
-  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB, POS>;
-  const int lds = shared_lds(POS).total;
+  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB, POS, RES>;
+  const int lds = shared_lds(POS, RES).total;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB, POS>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB, POS, RES>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -623,9 +766,12 @@ static hipError_t launch_shared_bits(int kb, int grid, hipStream_t st, const Dec
   return launch_shared_one<KEEP, SPLIT, 4, POS>(grid, st, a);
 }
 
-// keep mask and positions are exclusive (the entry point rejects both)
-static hipError_t launch_shared_variant(bool keep, bool pos, bool split, int kb, int grid, hipStream_t st,
+// keep mask, positions and the residual are exclusive (the entry point rejects their combinations; the residual
+// mode has INT4 latents)
+static hipError_t launch_shared_variant(bool keep, bool pos, bool res, bool split, int kb, int grid, hipStream_t st,
                                         const DecodeSharedArgs& a) {
+  if (res) return split ? launch_shared_one<false, true, 4, false, true>(grid, st, a)
+                        : launch_shared_one<false, false, 4, false, true>(grid, st, a);
   if (keep) return split ? launch_shared_bits<true, true, false>(kb, grid, st, a) : launch_shared_bits<true, false, false>(kb, grid, st, a);
   if (pos) return split ? launch_shared_bits<false, true, true>(kb, grid, st, a) : launch_shared_bits<false, false, true>(kb, grid, st, a);
   return split ? launch_shared_bits<false, true, false>(kb, grid, st, a) : launch_shared_bits<false, false, false>(kb, grid, st, a);
@@ -638,21 +784,23 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
   a.q_pos = in.q_pos; a.q = in.q; a.wk = in.wk; a.w_stride = in.w_seq_stride; a.ws = (float*)ws;
   a.keep = in.keep_mask; a.keep_words = in.keep_words;
   a.tok_pos = in.tok_pos; a.pos_row = in.max_blocks * L.page_size;
+  a.lat_bytes = shared_latent_bytes(L); a.rec_bytes = (int)uniform_page_bytes(L);
   a.q_bf16 = in.q_dtype == KVC_BF16;
   a.B = in.B; a.Hkv = L.n_kv_heads; a.Hq = L.n_q_heads; a.L = L.n_layers; a.max_blocks = in.max_blocks;
   a.P = L.page_size; a.G = L.group; a.n_splits = n_splits; a.st_per_split = st_per_split;
-  a.part_stride = 2 * SGQ + SGQ * SLAT; a.theta = L.rope_theta;
+  a.part_stride = shared_part_stride(L); a.theta = L.rope_theta;
   const bool split = in.kv_split == SLAT / 2;
   const int kb = lat_bits_k(L);
   const int grid = L.n_layers * L.n_kv_heads * in.B * n_splits;
   hipError_t e = mark(g_marks.begin, st);
   if (e != hipSuccess) return e;
-  e = launch_shared_variant(in.keep_mask != nullptr, in.tok_pos != nullptr, split, kb, grid, st, a);
+  e = launch_shared_variant(in.keep_mask != nullptr, in.tok_pos != nullptr, L.residual_bits != 0, split, kb, grid,
+                            st, a);
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,
                      in.w_seq_stride, out, in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride,
-                     split ? SLAT / 2 : 0);
+                     split ? SLAT / 2 : 0, L.residual_bits != 0);
   return hipGetLastError();
 }
 

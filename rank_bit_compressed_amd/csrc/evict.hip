@@ -233,7 +233,7 @@ kvc_status compact_impl(const kvc_layout& L, const kvc_cache& src, const kvc_cac
       !in.out_block_table || !out_len || !tok_pos || !src.pool || !src.page_off || !dst.pool || !dst.page_off)
     return KVC_ERR_INVALID_ARG;
   if ((int64_t)in.max_blocks * L.page_size > (int64_t)32 * CMAX_BLOCKS || in.B > (1 << 20)) return KVC_ERR_INVALID_ARG;
-  if (!shared_supported(L)) return KVC_ERR_UNSUPPORTED;
+  if (!shared_supported(L) || L.residual_bits) return KVC_ERR_UNSUPPORTED;  // (records with residuals: not moved)
   const void* ptrs[] = {in.block_table, in.seq_len, in.out_block_table, out_len, tok_pos, src.pool, src.page_off,
                         dst.pool, dst.page_off};
   for (const void* p : ptrs)

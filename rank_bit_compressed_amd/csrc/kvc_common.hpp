@@ -68,11 +68,27 @@ __host__ __device__ inline int slot_meta_bytes(int latent_bits, int r, int G) {
   return latent_bits == 32 ? 0 : 4 * ceil_div(r, G);
 }
 
+// Block-shared record: the latent's code and pair sections (each padded to 16), then with the rotated residual
+// Kr, Vr (one part of P x d/4 code bytes per (layer, kv head), layer-major) and Ks, Vs (one part of P fp16 scales,
+// padded to 16, per (layer, kv head)).  Bytes of the latent's part:
+__host__ __device__ inline int64_t shared_latent_bytes(const kvc_layout& L) {
+  const int P = L.page_size;
+  return pad16((int64_t)P * L.r_k_cap * lat_bits_k(L) / 8) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
+}
+// Byte offset in a block-shared record of residual part `part` (0 Kr, 1 Vr, 2 Ks, 3 Vs) of (layer, kv head) idx.
+__host__ __device__ inline int64_t shared_res_part(int64_t lat_bytes, int P, int d, int n_parts, int part, int idx) {
+  const int64_t cb = (int64_t)P * (d / 4), sb = pad16((int64_t)P * 2);
+  if (part < 2) return lat_bytes + ((int64_t)part * n_parts + idx) * cb;
+  return lat_bytes + 2 * n_parts * cb + ((int64_t)(part - 2) * n_parts + idx) * sb;
+}
+
 // Uniform-rank page record size (per-head or shared mode).
 __host__ __device__ inline int64_t uniform_page_bytes(const kvc_layout& L) {
   const int P = L.page_size;
   if (L.shared)
-    return pad16((int64_t)P * L.r_k_cap * lat_bits_k(L) / 8) + pad16((int64_t)P * 4 * ceil_div(L.r_k_cap, L.group));
+    return shared_latent_bytes(L) + (L.residual_bits ? 2 * (int64_t)L.n_layers * L.n_kv_heads *
+                                                           ((int64_t)P * (L.head_dim / 4) + pad16((int64_t)P * 2))
+                                                     : 0);
   HeadSections S = head_sections((int64_t)P * slot_code_bytes(lat_bits_k(L), L.r_k_cap),
                                  (int64_t)P * slot_code_bytes(lat_bits_v(L), L.r_v_cap),
                                  (int64_t)P * slot_meta_bytes(lat_bits_k(L), L.r_k_cap, L.group),

@@ -132,6 +132,10 @@ WORKLOADS = {
     "tucker_group_32k": Workload("tucker_group_32k", B=4, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
                                  r_k=512, r_v=512, group=64, shared=True, n_layers=4, rope_theta=500000.0,
                                  latent_decay=0.0, tucker=(256, 256, 64), seed=16),
+    # the same group with the rotated 2-bit residual of each layer and head (JoLT: Tucker form plus residual)
+    "tucker_group_32k_res": Workload("tucker_group_32k_res", B=4, T=32768, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                     r_k=512, r_v=512, group=64, shared=True, n_layers=4, rope_theta=500000.0,
+                                     latent_decay=0.0, tucker=(256, 256, 64), residual_bits=2, seed=16),
     # the block-shared latent with one eviction decision for its 4 layers, keeping 30% of every sequence
     "shared_latent_32k_evict30": Workload("shared_latent_32k_evict30", B=4, T=32768, n_q_heads=32, n_kv_heads=8,
                                           head_dim=128, r_k=512, r_v=512, group=64, shared=True, n_layers=4,

@@ -22,6 +22,8 @@ CASES = [
     # the lower-bit codecs on the block-shared latent (one width for the latent)
     ("shared_latent_32k", dict(B=2, T=600, latent_bits=3), [600, 1]),
     ("shared_latent_32k", dict(B=2, T=300, page_size=64, latent_bits=2), [300, 65]),
+    # the rotated residual of each layer and head on the block-shared latent
+    ("shared_latent_32k", dict(B=2, T=300, page_size=64, n_layers=3, residual_bits=2, residual_std=0.3), [300, 97]),
 ]
 
 
