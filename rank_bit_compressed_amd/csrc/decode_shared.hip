@@ -461,21 +461,8 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // scale; super-tile k's residual is visible since the previous barrier.  H' c of a block is formed beside the
     // block's up-projection and added, scaled, before the block's RoPE.
     f16v_t ra = {};
-    v8i_t er[2];
     float ksc = 0.0f;
-    if (RES && (!SPLIT || wv < 2)) {
-      const uint8_t* rr = rres + (k % SRRN) * SRR;
-      uint32_t krw[4];
-#pragma unroll
-      for (int be = 0; be < 2; ++be)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(rr + 32 * t + 4 * (4 * be + 2 * hf + i));
-      ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rr + 2048 + 2 * t)) * (2.0f * RSCALE);
-#pragma unroll
-      for (int be = 0; be < 2; ++be)
-#pragma unroll
-        for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
-    }
+    const uint8_t* rrk = rres + (k % SRRN) * SRR;
     // a super-tile whose tokens are all evicted contributes nothing: only the next one's dequantization runs
     const bool empty = KEEP && tkeep[k] == 0u;
     if (SPLIT && wv >= 2) {  // value waves: only the next super-tile's value tile
@@ -499,6 +486,18 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
           for (int j = 0; j < NRB; ++j)
             if (g == wv + NKW * j) {
+              uint32_t krw[4];
+#pragma unroll
+              for (int be = 0; be < 2; ++be)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                  krw[2 * be + i] = *(const uint32_t*)(rrk + 32 * t + 4 * (4 * be + 2 * hf + i));
+              ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rrk + 2048 + 2 * t)) * (2.0f * RSCALE);
+              v8i_t er[2];  // the codes one per byte (the fp8 B operands): byte q of dword o = code m + 4q, m = o % 4
+#pragma unroll
+              for (int be = 0; be < 2; ++be)
+#pragma unroll
+                for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
               ra = mfma_f8_codes(hr[j][1], er[1], mfma_f8_codes(hr[j][0], er[0], f16v_t{}));
               if (g == 0 && hf == 0) ra[0] -= 192.0f;  // H' 1 is 128 at head dim 0 (row 0): the -1.5 offset
             }
@@ -770,8 +769,9 @@ static hipError_t launch_shared_bits(int kb, int grid, hipStream_t st, const Dec
 // mode has INT4 latents)
 static hipError_t launch_shared_variant(bool keep, bool pos, bool res, bool split, int kb, int grid, hipStream_t st,
                                         const DecodeSharedArgs& a) {
-  if (res) return split ? launch_shared_one<false, true, 4, false, true>(grid, st, a)
-                        : launch_shared_one<false, false, 4, false, true>(grid, st, a);
+  // the residual mode runs the plain-latent form also for a split latent: the products it then makes are exact
+  // zeros, and the output is the full product's
+  if (res) return launch_shared_one<false, false, 4, false, true>(grid, st, a);
   if (keep) return split ? launch_shared_bits<true, true, false>(kb, grid, st, a) : launch_shared_bits<true, false, false>(kb, grid, st, a);
   if (pos) return split ? launch_shared_bits<false, true, true>(kb, grid, st, a) : launch_shared_bits<false, false, true>(kb, grid, st, a);
   return split ? launch_shared_bits<false, true, false>(kb, grid, st, a) : launch_shared_bits<false, false, false>(kb, grid, st, a);
