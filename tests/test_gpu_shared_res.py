@@ -57,3 +57,29 @@ def test_shared_residual_rejects_masks_and_positions():
     with pytest.raises(kvc.KvcError):
         kvc.decode_attn(gpu_layout(w), c, d["block_table"], d["seq_len"], d["q"], d["wk"], d["wv"], w.T,
                         q_pos=d["q_pos"], keep_mask=keep)
+
+
+@pytest.mark.timeout(600)
+def test_tucker_group_with_residual_full_size_sampled():
+    # the full 4-sequence, 32K-token, 4-layer Tucker group with every layer's and head's residual; compression bit
+    # for bit, the oracle's decode for one sequence and one KV head (all four layers)
+    from tests.test_gpu_tucker import _gpu_w, _oracle_decode, _oracle_w
+    w = synth.WORKLOADS["tucker_group_32k_res"]
+    inp = synth.make_inputs(w)
+    print("[shared res] full size: oracle compress", flush=True)
+    cache = oracle_cache(w, inp)
+    wk, wv = _oracle_w(w, inp)
+    d = dev(inp)
+    gc = gpu_cache(w, d)
+    gwk, gwv = _gpu_w(w, d)
+    out = kvc.decode_attn(gpu_layout(w), gc, d["block_table"], d["seq_len"], d["q"], gwk, gwv, w.T, q_pos=d["q_pos"],
+                          kv_split=w.tucker[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.pool.cpu().numpy()[:len(cache[0])], cache[0])
+    del d, gc
+    torch.cuda.empty_cache()
+    print("[shared res] full size: oracle decode of sequence 2, kv head 5", flush=True)
+    want = _oracle_decode(w, inp, cache, wk, wv, [2], [5])
+    err = rel_err(out, want)
+    print(f"    rel err {err:.3e}", flush=True)
+    assert err <= TOL
