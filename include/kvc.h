@@ -527,11 +527,15 @@ kvc_status kvc_evict_compact(const kvc_layout* layout, const kvc_cache* src, con
                               page_size the totals), or one of whose slots holds a rank above the cap     */
 #define KVC_BAD_RECORD 64  /* a used page whose record (n_kv_heads head blocks, sized from the page's
                               totals or the uniform rank) starts inside the pool but ends past pool_bytes */
+#define KVC_BAD_TOK_POS 128 /* with tok_pos: a 32-slot tile below seq_len whose first slot holds no token
+                              while a later one does, or holding a token 4 or more blocks of 32 positions past
+                              the first slot's block, or positions not increasing over a sequence's tokens
+                              (the decode would skip such a token).  A compacted length of 0 is valid. */
 
 /* Opt-in check of the tables kvc_decode_attn reads and trusts (a bad page id there is undefined behaviour):
- * compares the sequence lengths, the used block-table entries, their page offsets and record ends, q_pos
- * and (variable rank) the used slots' ranks and every offset row of a used page with their bounds and with
- * each other, reading nothing through them.  Writes the or of the
+ * compares the sequence lengths, the used block-table entries, their page offsets and record ends, q_pos,
+ * (variable rank) the used slots' ranks and every offset row of a used page, and (tok_pos) the slot positions
+ * with their bounds and with each other, reading nothing through them.  Writes the or of the
  * KVC_BAD_* flags found, 0 if none, to flags (one int32 in device memory).  One workgroup; asynchronous on
  * stream: read flags after synchronizing.  INVALID_ARG for null tables or sizes out of range. */
 kvc_status kvc_decode_check(const kvc_layout* layout, const kvc_cache* cache, const kvc_decode_in* in,

@@ -17,6 +17,7 @@ struct CheckArgs {
   const int64_t* page_off;
   const uint8_t* tok_rank;
   const uint32_t* tok_off;
+  const int32_t* tok_pos;  // compacted cache: source position of each slot [B][max_blocks * P], -1 for none
   int64_t pool_bytes;
   int64_t record_uniform;  // bytes of a page record when ranks are uniform
   int B, max_blocks, max_T, P, n_pages, r_cap, G, Hkv, d, bits_k, bits_v, residual;
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(256) void decode_check_kernel(CheckArgs a, int32_t*
   for (int b = 0; b < a.B; ++b) {
     const int T = a.seq_len[b];
     if (threadIdx.x == 0) {
-      if (T < 1 || T > limit) my |= KVC_BAD_SEQ_LEN;
+      if (T < (a.tok_pos ? 0 : 1) || T > limit) my |= KVC_BAD_SEQ_LEN;
       if (a.q_pos && a.q_pos[b] < 0) my |= KVC_BAD_Q_POS;
     }
     const int Tc = max(0, min(T, limit));
@@ -73,6 +74,26 @@ __global__ __launch_bounds__(256) void decode_check_kernel(CheckArgs a, int32_t*
       }
       if (off >= 0 && off < a.pool_bytes && rec > a.pool_bytes - off) my |= KVC_BAD_RECORD;
     }
+    if (a.tok_pos) {  // tiles of 32 slots: the first slot holds a token if any does, every token within 4 blocks
+      // of 32 positions of the first's block, tokens increasing (also across the tile before)
+      const int32_t* pos = a.tok_pos + (size_t)b * a.max_blocks * a.P;
+      for (int i = threadIdx.x; 32 * i < Tc; i += 256) {
+        const int end = min(32 * i + 32, Tc);
+        int prev = -1;
+        for (int s = 32 * i - 1; s >= 0 && s >= 32 * i - 32; --s)  // the last token of the tile before
+          if (pos[s] >= 0) {
+            prev = pos[s];
+            break;
+          }
+        const int p0 = pos[32 * i];
+        for (int s = 32 * i; s < end; ++s) {
+          const int p = pos[s];
+          if (p < 0) continue;
+          if (p0 < 0 || (p >> 5) - (p0 >> 5) >= 4 || p <= prev) my |= KVC_BAD_TOK_POS;
+          prev = p;
+        }
+      }
+    }
   }
   atomicOr(&f, my);
   __syncthreads();
@@ -87,7 +108,7 @@ kvc_status check_impl(const kvc_layout& L, const kvc_cache& C, const kvc_decode_
       in.max_blocks <= 0 || in.max_T <= 0 || (L.variable_rank && (!C.tok_rank || !C.tok_off)))
     return KVC_ERR_INVALID_ARG;
   CheckArgs a{in.block_table, in.seq_len, in.q_pos, C.page_off, L.variable_rank ? C.tok_rank : nullptr,
-              L.variable_rank ? C.tok_off : nullptr, C.pool_bytes, uniform_page_bytes(L), in.B, in.max_blocks,
+              L.variable_rank ? C.tok_off : nullptr, L.shared ? in.tok_pos : nullptr, C.pool_bytes, uniform_page_bytes(L), in.B, in.max_blocks,
               in.max_T, L.page_size, C.n_pages, L.r_k_cap, L.group, L.n_kv_heads, L.head_dim, lat_bits_k(L),
               lat_bits_v(L), L.residual_bits};
   hipLaunchKernelGGL(decode_check_kernel, dim3(1), dim3(256), 0, st, a, flags);

@@ -621,14 +621,15 @@ def evict_compact(layout: Layout, src: DeviceCache, dst: DeviceCache, block_tabl
     return out_seq_len, tok_pos
 
 
-BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK, BAD_TOK_OFF, BAD_RECORD = 1, 2, 4, 8, 16, 32, 64
+BAD_SEQ_LEN, BAD_PAGE, BAD_OFFSET, BAD_Q_POS, BAD_RANK, BAD_TOK_OFF, BAD_RECORD, BAD_TOK_POS = (1, 2, 4, 8, 16, 32,
+                                                                                    64, 128)
 
 
-def decode_check(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, q_pos=None) -> int:
+def decode_check(layout: Layout, cache: DeviceCache, block_table, seq_len, max_T, q_pos=None, tok_pos=None) -> int:
     """kvc_decode_check: the or of the KVC_BAD_* flags of these tables (0 = fine).  Synchronizes."""
     flags = torch.empty(4, dtype=torch.int32, device=block_table.device)
     q = torch.empty(16, dtype=torch.float32, device=block_table.device)
-    inp = decode_in(block_table, seq_len, q, q, q, max_T, q_pos)
+    inp = decode_in(block_table, seq_len, q, q, q, max_T, q_pos, tok_pos=tok_pos, page_size=layout.page_size)
     _check(lib().kvc_decode_check(C.byref(layout), C.byref(cache.c()), C.byref(inp), _ptr(flags), _stream()),
            "kvc_decode_check")
     return int(flags[0].item())

@@ -90,3 +90,33 @@ def test_check_uniform_and_shared_layouts():
         cache.page_off[page] = cache.pool.numel() - 1
         assert kvc.decode_check(L, cache, d["block_table"], d["seq_len"], w.T, d["q_pos"]) == kvc.BAD_RECORD
         cache.page_off[page] = keep
+
+
+def test_check_slot_positions_of_a_compacted_cache():
+    import numpy as np
+    w = synth.WORKLOADS["shared_latent_32k_evict30"].scaled(B=2, T=600, page_size=64)
+    d = dev(synth.make_inputs(w, seq_len=[600, 333]))
+    cache = gpu_cache(w, d)
+    L = gpu_layout(w)
+    keep = torch.from_numpy((np.random.default_rng(4).random((2, 19 * 32)) < 0.3).reshape(2, 19, 32)
+                            .astype(np.uint64).__lshift__(np.arange(32, dtype=np.uint64)).sum(-1)
+                            .astype(np.uint32).view(np.int32)).cuda()
+    keep[1] = 0                               # sequence 1 keeps nothing: a compacted length of 0
+    dst = kvc.DeviceCache(L, torch.zeros_like(cache.pool), cache.page_off.clone(), None, None,
+                          torch.zeros(2, dtype=torch.int64, device="cuda"), w.n_pages)
+    out_len, tok_pos = kvc.evict_compact(L, cache, dst, d["block_table"], d["seq_len"], keep, d["block_table"])
+    torch.cuda.synchronize()
+    ck = lambda tp=tok_pos, sl=out_len: kvc.decode_check(L, dst, d["block_table"], sl, w.T, d["q_pos"], tok_pos=tp)
+    print("[check] compacted positions", flush=True)
+    assert int(out_len[1]) == 0 and ck() == 0
+    n = int(out_len[0])
+    for name, edit in (("first slot empty", lambda tp: tp[0].__setitem__(32, -1)),
+                       ("out of the span", lambda tp: tp[0].__setitem__(33, int(tp[0, 32]) + 4 * 32 + 5)),
+                       ("not increasing", lambda tp: tp[0].__setitem__(40, int(tp[0, 39])))):
+        tp = tok_pos.clone()
+        assert n > 64 and bool((tp[0, 32:41] >= 0).all())
+        edit(tp)
+        print(f"[check] {name}", flush=True)
+        assert ck(tp=tp) == kvc.BAD_TOK_POS, name
+    # without positions, a length of 0 is still an error
+    assert kvc.decode_check(L, dst, d["block_table"], out_len, w.T, d["q_pos"]) == kvc.BAD_SEQ_LEN
