@@ -142,10 +142,11 @@ struct CompactArgs {
 };
 
 // One workgroup per sequence.  The tile rule is a left-to-right recurrence, but it only changes state at a
-// block's first kept token, so one thread walks the blocks (a popcount each) and gives each block the slot of its
-// first kept token; within a block the kept tokens take consecutive slots (a tile that fills mid-block continues
-// in the next slot, which opens the next tile with the same block as its base).  Then every thread writes the
-// positions of its blocks' tokens, after the row is set to -1.
+// block's first kept token, so wave 0 walks the blocks with wave-uniform (scalar) state: 64 mask words at a time
+// are loaded into its lanes and read back one by one, a popcount each, giving each block the slot of its first
+// kept token; within a block the kept tokens take consecutive slots (a tile that fills mid-block continues in the
+// next slot, which opens the next tile with the same block as its base).  Then every thread writes the positions
+// of its blocks' tokens, after the row is set to -1.
 __global__ __launch_bounds__(256) void compact_scan_kernel(CompactArgs a) {
   extern __shared__ uint32_t cl[];  // [n_blk] keep words, then [n_blk] first slots
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -163,25 +164,33 @@ __global__ __launch_bounds__(256) void compact_scan_kernel(CompactArgs a) {
   int32_t* pos = a.tok_pos + (size_t)b * row;
   for (int i = tid; i < row; i += 256) pos[i] = -1;
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {  // wave 0; slot, count and base are the same in every lane
+    const int lane = tid;
     int slot = 0, count = 0, base = 0;
-    for (int i = 0; i < n_blk; ++i) {
-      const int c = __builtin_popcount(words[i]);
-      if (c == 0) continue;
-      if (count > 0 && i - base >= CSPAN) {  // out of the tile's span: close it, its spare slots stay empty
-        slot = (slot + CT - 1) / CT * CT;
-        count = 0;
+    for (int c0 = 0; c0 < n_blk; c0 += 64) {
+      const uint32_t wl = c0 + lane < n_blk ? words[c0 + lane] : 0u;
+      int fr = 0;
+      const int m = min(64, n_blk - c0);
+      for (int j = 0; j < m; ++j) {
+        const int c = __builtin_popcount((uint32_t)__builtin_amdgcn_readlane((int)wl, j));
+        if (c == 0) continue;
+        const int i = c0 + j;
+        if (count > 0 && i - base >= CSPAN) {  // out of the tile's span: close it, its spare slots stay empty
+          slot = (slot + CT - 1) / CT * CT;
+          count = 0;
+        }
+        if (count == 0) base = i;
+        fr = lane == j ? slot : fr;
+        slot += c;
+        count += c;
+        if (count >= CT) {  // the tile filled at one of this block's tokens; the rest open the next tile here
+          count -= CT;
+          base = i;
+        }
       }
-      if (count == 0) base = i;
-      first[i] = slot;
-      slot += c;
-      count += c;
-      if (count >= CT) {  // the tile filled at one of this block's tokens; the rest open the next tile here
-        count -= CT;
-        base = i;
-      }
+      if (c0 + lane < n_blk) first[c0 + lane] = fr;
     }
-    a.out_len[b] = slot;
+    if (lane == 0) a.out_len[b] = slot;
   }
   __syncthreads();
   for (int i = tid; i < n_blk; i += 256) {
