@@ -681,6 +681,351 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   }
 }
 
+// ---- The role-split form (no positions, no residual): 8 waves, two per SIMD.  Waves 0-3 are key waves and waves
+// 4-7 value waves; key wave w and value wave 4 + w share latent quarter w and, as a workgroup's waves are placed
+// round-robin over the SIMDs, one SIMD.  The one-wave-per-SIMD form above runs a super-tile's vector and matrix work
+// largely one after the other; here a SIMD runs a key wave's matrix chain beside a value wave's vector work.
+// Between the barriers of super-tiles k - 1 and k:
+//   value wave w: stages its quarter's codes and pairs (a four-deep ring of direct-to-LDS copies), dequantizes
+//     super-tile k + 1 into the quarter's fp16 tile, runs the online softmax of super-tile k - 1 from the four
+//     partial scores and its value product on the tile of k - 1, and rotates the query of super-tile k + 2;
+//   key wave w: reads super-tile k's B fragments back from the quarter's tile, up-projects them (W_k's slice in the
+//     accumulator registers), rotates and scores them, and writes its partial scores.
+// The products, their operands and their order are those of decode_shared_kernel, so the output is the same.
+// RoPE on one fp16 pair v = (x, y) with f = (cos, sin), as rope_pair: the same two packed operations and
+// roundings, with f's halves picked by operand selects, so that the compiler keeps one register per factor word
+// instead of hoisting its two swizzled copies (cos, cos) and (sin, sin) out of the loop.
+__device__ inline uint32_t rope_pair_sel(uint32_t v, uint32_t f) {
+  uint32_t t, r;
+  asm("v_pk_mul_f16 %0, %1, %2 op_sel:[0,1] op_sel_hi:[1,1]" : "=v"(t) : "v"(v), "v"(f));  // (x sin, y sin)
+  asm("v_pk_fma_f16 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[1,0,0] neg_lo:[0,0,1]"      // (x cos - y sin,
+      : "=v"(r) : "v"(v), "v"(f), "v"(t));                                                //  y cos + x sin)
+  return r;
+}
+
+struct RoleLds {
+  int raw, vt, qt, theta, sp, pt, addr, keep, total;
+};
+__host__ __device__ constexpr RoleLds role_lds() {
+  RoleLds L{};
+  int o = 0;
+  L.raw = o; o += 4 * 4 * SRAW;             // per value wave: staging ring of 4 super-tiles
+  L.vt = o; o += 4 * 2 * SVT;               // per quarter: fp16 tiles of two super-tiles
+  L.qt = o; o += 3 * SGQ * SQB * 2;         // rotated query in fragment order, fp16, x 3
+  L.theta = o; o += (SD / 2) * 8;           // RoPE frequencies, turns per position
+  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;      // partial scores [buffer][key wave][token][head]
+  L.pt = o; o += 4 * 32 * SGQ * 2;          // probabilities [value wave][token][head] fp16
+  L.addr = o; o += SMAX_TILES * 8;          // page record address of each super-tile
+  L.keep = o; o += SMAX_TILES * 4;          // keep-mask word of each super-tile
+  L.total = o;
+  return L;
+}
+
+template <bool KEEP, bool SPLIT, int KB>
+__global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeSharedArgs a) {
+  constexpr int CB = SLAT * KB / 8;  // code bytes per token
+  constexpr int QB = CB / 4;         // a quarter of them
+  constexpr int NCH = QB / 16;       // its 16-byte chunks per token
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr RoleLds LY = role_lds();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool keyw = wid < 4;
+  const int wq = wid & 3;  // latent quarter
+  const int t = lane & 31, hf = lane >> 5, rho = lane & 15, grp = lane >> 4;
+  int id = blockIdx.x;
+  const int split = id % a.n_splits; id /= a.n_splits;
+  const int b = id % a.B; id /= a.B;
+  const int h = id % a.Hkv;
+  const int l = id / a.Hkv;
+  const int T = a.seq_len[b];
+  const int qpos = a.q_pos ? a.q_pos[b] : T;
+  const int P = a.P;
+  const int mpt = 4 * (SLAT / a.G);             // pair bytes per token
+  const int lg = __builtin_ctz(a.G);            // G is a power of two (32 .. 512)
+  const int npw = max(1, SQC >> lg);            // pairs per token over a quarter's coordinates (1, 2 or 4)
+  const int g0 = (SQC * wq) >> lg;              // the first of them
+
+  double* tturn = (double*)(smem + LY.theta);
+  if (tid < SD / 2) tturn[tid] = (a.theta > 0.0 ? pow(a.theta, -2.0 * tid / SD) : 0.0) * 0.15915494309189535;
+  const int n_st = (T + 31) / 32;
+  const int st_begin = split * a.st_per_split;
+  const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
+  int64_t* taddr = (int64_t*)(smem + LY.addr);
+  uint32_t* tkeep = (uint32_t*)(smem + LY.keep);
+  for (int k = tid; k < n_tiles; k += 512) {  // page record of each super-tile, its keep word
+    const int t0 = (st_begin + k) * 32;
+    const int page = a.block_table[(size_t)b * a.max_blocks + t0 / P];
+    taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * CB;
+    const int wd = t0 >> 5;
+    if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
+  }
+  _Float16* qts = (_Float16*)(smem + LY.qt);  // rotated query of super-tile k: buffer k % 3
+  float* sp = (float*)(smem + LY.sp);
+  const uint8_t* vt_q = smem + LY.vt + wq * 2 * SVT;  // the quarter's fp16 tiles; super-tile k in k % 2
+  __syncthreads();
+
+  if (keyw) {
+    // ---- W_k[l]'s slice of this quarter as A fragments in the accumulator registers (the layout of
+    // decode_shared_kernel: block g row t <-> head dim t < 16 ? 16g + t : 64 + 16g + t - 16; step j k-slot 8hf + e
+    // <-> latent coordinate 128w + 8 (8hf + j) + perm8(e))
+    h8 wf[SNB][SNJ];
+    if (!SPLIT || wq < 2) {
+      const int width = a.Hkv * SD;
+      const uint16_t* W = a.wk + (size_t)b * a.w_stride + (size_t)l * SLAT * width + (size_t)h * SD;
+#pragma unroll
+      for (int g = 0; g < SNB; ++g) {
+        const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
+#pragma unroll
+        for (int j = 0; j < SNJ; ++j) {
+          h8 f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = bf16_to_h(W[(size_t)(SQC * wq + 8 * (8 * hf + j) + perm8(e)) * width + dim]);
+          asm volatile("" : "=a"(wf[g][j]) : "0"(f));
+        }
+      }
+    }
+    // RoPE factors of this lane's slot t: block g's up-projection entry i is row 8(i/4) + 4hf + i%4, paired with
+    // entry i + 8; frequency 16g + that row
+    uint32_t rf[SNB][8];
+#pragma unroll
+    for (int g = 0; g < SNB; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
+        rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+      }
+    lds_barrier();  // the value waves' prologue: the tile of super-tile 0, the rotated queries of 0 and 1
+    for (int k = 0; k < n_tiles; ++k) {
+      const bool empty = KEEP && __builtin_amdgcn_readfirstlane(tkeep[k]) == 0u;
+      f16v_t sc = {};
+      if ((!SPLIT || wq < 2) && !empty) {
+        const uint8_t* tl = vt_q + (k & 1) * SVT + SCS * 8 * hf + 16 * t;
+        h8 bc[SNJ];
+#pragma unroll
+        for (int j = 0; j < SNJ; ++j) bc[j] = *(const h8*)(tl + SCS * j);
+        // score operand row t: query head t % 4
+        const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SQB + (t & 3) * SQB) + hf;
+#pragma unroll
+        for (int g = 0; g < SNB; ++g) {
+          f16v_t kp = {};
+#pragma unroll
+          for (int j = 0; j < SNJ; ++j) kp = mfma32s(wf[g][j], bc[j], kp);
+          u32x4_t kr[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair_sel(pack_h2(kp[i], kp[i + 8]), rf[g][i]);
+          sc = mfma32s(qf[4 * g], __builtin_bit_cast(h8, kr[0]), sc);
+          sc = mfma32s(qf[4 * g + 2], __builtin_bit_cast(h8, kr[1]), sc);
+        }
+      }
+      if (hf == 0) *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
+      lds_barrier();
+    }
+    return;
+  }
+
+  // ---- value wave of quarter wq
+  uint8_t* raw_w = smem + LY.raw + wq * 4 * SRAW;  // its ring; super-tile k in slot k % 4
+  const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw_w));
+  _Float16* pt = (_Float16*)(smem + LY.pt) + wq * 32 * SGQ;
+  const int64_t meta_base = pad16((int64_t)P * CB);
+  // this thread's query pair for the per-tile rotation: head wq, pair lane, scaled for exp2
+  const int qj = lane;
+  float qx, qy;
+  {
+    const float sc = 1.4426950408889634f / sqrtf((float)SD);
+    const size_t base = (((size_t)l * a.B + b) * a.Hq + h * SGQ + wq) * SD;
+    if (a.q_bf16) {
+      const uint16_t* q = (const uint16_t*)a.q + base;
+      qx = __builtin_bit_cast(float, (uint32_t)q[qj] << 16) * sc;
+      qy = __builtin_bit_cast(float, (uint32_t)q[qj + SD / 2] << 16) * sc;
+    } else {
+      const float* q = (const float*)a.q + base;
+      qx = q[qj] * sc;
+      qy = q[qj + SD / 2] * sc;
+    }
+  }
+  const int qix = qfrag_index(wq, qj);
+  const double fq = tturn[qj];
+
+  // staging of this quarter of super-tile k into ring slot k % 4, as in decode_shared_kernel (past the last
+  // super-tile the slot gets a copy of the last one; always four copy instructions)
+  auto issue = [&](int k) {
+    const int kk = min(k, n_tiles - 1);
+    const int slot0 = ((st_begin + kk) * 32) % P;
+    const int64_t at = uniform64(taddr[kk]);
+    const int pairs_at = (int)meta_base - slot0 * CB + slot0 * mpt;
+    const i32x4_t rs = buffer_rsrc(a.pool + at, pairs_at + 32 * mpt);
+    const uint32_t dst = raw_lds + (k & 3) * SRAW;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int p = 64 * r + lane;
+      if (KB == 4) {
+        copy16_to_lds(rs, dst + 1024 * r, (p & 31) * CB + QB * wq + 16 * (p >> 5));
+      } else {
+        const int pc = min(p, 32 * NCH - 1);
+        copy16_to_lds(rs, dst + 1024 * r, (pc / NCH) * CB + QB * wq + 16 * (pc % NCH));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int q = 64 * r + lane, tok = q >> 2, i = q & 3;
+      copy4_to_lds(rs, dst + 2048 + 256 * r, pairs_at + tok * mpt + 4 * (g0 + (i & (npw - 1))));
+    }
+  };
+  const int gr0 = ((SQC * wq + 64 * hf) >> lg) - g0, gr1 = ((SQC * wq + 64 * hf + 32) >> lg) - g0;
+  // the lane's eight code groups of a staged super-tile as INT4 dwords (group j = coordinates 8 (8hf + j).. of
+  // the quarter of token t), and its two scale/zero pairs
+  auto load_words = [&](int k, uint32_t (&xs)[8], uint32_t& z0, uint32_t& z1) {
+    const uint8_t* raw = raw_w + (k & 3) * SRAW;
+    if (KB == 4) {
+      const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);
+      const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xs[j] = c0[j];
+        xs[4 + j] = c1[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = codes8_as_nibbles<KB>(raw + QB * t, KB * (8 * hf + j));
+    }
+    z0 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr0));
+    z1 = *(const uint32_t*)(raw + 2048 + 4 * (4 * t + gr1));
+  };
+  // super-tile k's fp16 chunks into tile k % 2: chunk c (code dword c, 8 coordinates) of token t at byte SCS c + 16t
+  auto store_tile = [&](int k, const uint32_t (&xs)[8], uint32_t z0, uint32_t z1) {
+    uint8_t* dst = (uint8_t*)vt_q + (k & 1) * SVT + SCS * 8 * hf + 16 * t;
+#pragma unroll
+    for (int j = 0; j < SNJ; ++j) *(h8*)(dst + SCS * j) = dequant_int4x8(xs[j], j < 4 ? z0 : z1);
+  };
+  auto rot_q = [&](int k) {
+    const double t0 = (double)((st_begin + k) * 32);
+    double rev = ((double)qpos - t0) * fq;
+    rev -= rint(rev);
+    const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+    _Float16* qt = qts + (k % 3) * SGQ * SQB;
+    *(uint32_t*)(qt + qix) = pack_h2(qx * cs - qy * sn, qy * cs + qx * sn);
+  };
+
+  f4 acc[SNJ];  // value latent on this quarter's coordinates, 16 per step, rows = query heads (replicated)
+#pragma unroll
+  for (int i = 0; i < SNJ; ++i) acc[i] = f4{0, 0, 0, 0};
+  float m_ref[SGQ], psum[SGQ];
+#pragma unroll
+  for (int i = 0; i < SGQ; ++i) {
+    m_ref[i] = 0.0f;
+    psum[i] = 0.0f;
+  }
+  bool fresh = true;
+  // the scores of super-tile k (the four key waves' partials), lazy online softmax, value product on tile k % 2
+  auto soft_value = [&](int k) {
+    const int t0 = (st_begin + k) * 32;
+    const bool empty = KEEP && tkeep[k] == 0u;
+    const float* spb = sp + (k & 1) * (4 * 32 * SGQ);
+    float s4[SGQ];
+    {
+      f4 tot = *(const f4*)(spb + t * SGQ);
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
+      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u));
+#pragma unroll
+      for (int i = 0; i < SGQ; ++i) s4[i] = kept ? tot[i] - m_ref[i] : -INFINITY;
+    }
+    const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+    if (KEEP ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
+             : fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
+      float alpha[SGQ];
+#pragma unroll
+      for (int i = 0; i < SGQ; ++i) {
+        float c = s4[i];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) c = fmaxf(c, __shfl_xor(c, o));
+        const float d = fresh ? c : fmaxf(c, 0.0f);
+        alpha[i] = fresh ? 1.0f : __builtin_amdgcn_exp2f(-d);
+        psum[i] *= alpha[i];
+        s4[i] -= d;
+        m_ref[i] += d;
+      }
+#pragma unroll
+      for (int nt = 0; nt < SNJ; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha[i];
+      fresh = false;
+    }
+    float p[SGQ];
+#pragma unroll
+    for (int i = 0; i < SGQ; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s4[i]);
+      psum[i] += p[i];
+    }
+    if (hf == 0) *(h4*)(pt + SGQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    wave_lds_sync();
+    // the value product as in decode_shared_kernel (P as the A operand of 16x16x32 products, the tile's chunks
+    // read transposed as the B operand)
+    if ((!SPLIT || wq >= 2) && !empty) {
+      const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
+      const int q4 = rho & 3;
+      const uint8_t* vb = vt_q + (k & 1) * SVT + SCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
+      h8 vt[SNJ];
+#pragma unroll
+      for (int nt = 0; nt < SNJ; ++nt) vt[nt] = lds_tr8s(vb + 2 * SCS * nt, vb + 2 * SCS * nt + 64);
+#pragma unroll
+      for (int nt = 0; nt < SNJ; ++nt) acc[nt] = mfma16x16x32(pop, vt[nt], acc[nt]);
+    }
+  };
+
+  if (n_tiles > 0) {
+    // prologue: super-tiles 0-3 in flight, wait for 0, its tile; rotated queries of 0 and 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue(j);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    uint32_t xs[8], z0, z1;
+    load_words(0, xs, z0, z1);
+    store_tile(0, xs, z0, z1);
+    rot_q(0);
+    rot_q(1);
+  }
+  lds_barrier();
+  for (int k = 0; k < n_tiles; ++k) {
+    issue(k + 4);  // ring slot k % 4 held super-tile k, stored into its tile before the previous barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);  // super-tile k + 1 landed; k + 2 .. k + 4 may be in flight
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    uint32_t xs[8], z0, z1;
+    load_words(k + 1, xs, z0, z1);
+    if (k > 0) soft_value(k - 1);  // reads tile (k - 1) % 2, which super-tile k + 1 then takes
+    store_tile(k + 1, xs, z0, z1);
+    rot_q(k + 2);  // buffer (k + 2) % 3 was last read by the key waves before the previous barrier
+    lds_barrier();
+  }
+  if (n_tiles > 0) soft_value(n_tiles - 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies past the end land before the workgroup exits
+
+  // ---- partial: m[4], l[4] (the same in every value wave), acc[4][512] (quarter w: coordinates 128w..128w+127)
+#pragma unroll
+  for (int i = 0; i < SGQ; ++i) {
+    float v = hf == 0 ? psum[i] : 0.0f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    psum[i] = v;
+  }
+  float* part = a.ws + ((((size_t)l * a.Hkv + h) * a.B + b) * a.n_splits + split) * a.part_stride;
+  if (wq == 0 && lane < SGQ) {
+    part[lane] = fresh ? -INFINITY : m_ref[lane];
+    part[SGQ + lane] = psum[lane];
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int nt = 0; nt < SNJ; ++nt) {
+      const int coord = SQC * wq + 16 * nt + 8 * (rho >> 3) + perm8(rho & 7);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[2 * SGQ + i * SLAT + coord] = acc[nt][i];
+    }
+  }
+}
+
 // out[l][b][h*4 + hq] = (W_v[l][:, h*128 : (h+1)*128]^T c* + H' r*) / l*, over the splits' partials (r*: the
 // rotated value residual of the residual mode, H' the +-1 Hadamard; its accumulators carry 1 / sqrt(128)): one
 // workgroup per (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the
@@ -758,6 +1103,23 @@ static hipError_t launch_shared_one(int grid, hipStream_t st, const DecodeShared
   return hipGetLastError();
 }
 
+template <bool KEEP, bool SPLIT, int KB>
+static hipError_t launch_role_one(int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  const void* kern = (const void*)decode_shared_role_kernel<KEEP, SPLIT, KB>;
+  constexpr int lds = role_lds().total;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_shared_role_kernel<KEEP, SPLIT, KB>), dim3(grid), dim3(512), lds, st, a);
+  return hipGetLastError();
+}
+
+template <bool KEEP, bool SPLIT>
+static hipError_t launch_role_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  if (kb == 3) return launch_role_one<KEEP, SPLIT, 3>(grid, st, a);
+  if (kb == 2) return launch_role_one<KEEP, SPLIT, 2>(grid, st, a);
+  return launch_role_one<KEEP, SPLIT, 4>(grid, st, a);
+}
+
 template <bool KEEP, bool SPLIT, bool POS>
 static hipError_t launch_shared_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
   if (kb == 3) return launch_shared_one<KEEP, SPLIT, 3, POS>(grid, st, a);
@@ -772,9 +1134,9 @@ static hipError_t launch_shared_variant(bool keep, bool pos, bool res, bool spli
   // the residual mode runs the plain-latent form also for a split latent: the products it then makes are exact
   // zeros, and the output is the full product's
   if (res) return launch_shared_one<false, false, 4, false, true>(grid, st, a);
-  if (keep) return split ? launch_shared_bits<true, true, false>(kb, grid, st, a) : launch_shared_bits<true, false, false>(kb, grid, st, a);
   if (pos) return split ? launch_shared_bits<false, true, true>(kb, grid, st, a) : launch_shared_bits<false, false, true>(kb, grid, st, a);
-  return split ? launch_shared_bits<false, true, false>(kb, grid, st, a) : launch_shared_bits<false, false, false>(kb, grid, st, a);
+  if (keep) return split ? launch_role_bits<true, true>(kb, grid, st, a) : launch_role_bits<true, false>(kb, grid, st, a);
+  return split ? launch_role_bits<false, true>(kb, grid, st, a) : launch_role_bits<false, false>(kb, grid, st, a);
 }
 
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
