@@ -25,6 +25,10 @@
 //     v_mfma_f32_16x16x32_f16, whose token-major operands come from the private tile through transposing
 //     LDS reads.
 // The value up-projection W_v is applied once per (layer, sequence, head) in the merge kernel.
+//
+// Two forms of this layout: decode_shared_role_kernel (further below: 8 waves, key waves and value waves on each
+// SIMD) serves the plain, keep-mask and split-latent modes; decode_shared_kernel (one wave per SIMD, described
+// above) the positions and residual modes.  Their products, operands and order are the same.
 #include <math.h>
 
 #include <algorithm>
