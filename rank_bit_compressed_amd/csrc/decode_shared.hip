@@ -811,16 +811,33 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
         for (int j = 0; j < SNJ; ++j) bc[j] = *(const h8*)(tl + SCS * j);
         // score operand row t: query head t % 4
         const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SQB + (t & 3) * SQB) + hf;
+        // block g's chain, then block g - 1's RoPE and score products, interleaved with it by the scheduling groups
+        // below (one matrix instruction, then up to three vector ones), so that a block's vector work runs under
+        // the next block's matrix chain
+        f16v_t kp[SNB];
+#pragma unroll
+        for (int g = 0; g <= SNB; ++g) {
+          if (g < SNB) {
+            kp[g] = f16v_t{};
+#pragma unroll
+            for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
+          }
+          if (g > 0) {
+            u32x4_t kr[2];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair_sel(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rf[g - 1][i]);
+            sc = mfma32s(qf[4 * (g - 1)], __builtin_bit_cast(h8, kr[0]), sc);
+            sc = mfma32s(qf[4 * (g - 1) + 2], __builtin_bit_cast(h8, kr[1]), sc);
+          }
+        }
 #pragma unroll
         for (int g = 0; g < SNB; ++g) {
-          f16v_t kp = {};
 #pragma unroll
-          for (int j = 0; j < SNJ; ++j) kp = mfma32s(wf[g][j], bc[j], kp);
-          u32x4_t kr[2];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair_sel(pack_h2(kp[i], kp[i + 8]), rf[g][i]);
-          sc = mfma32s(qf[4 * g], __builtin_bit_cast(h8, kr[0]), sc);
-          sc = mfma32s(qf[4 * g + 2], __builtin_bit_cast(h8, kr[1]), sc);
+          for (int j = 0; j < SNJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
       if (hf == 0) *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
