@@ -708,30 +708,37 @@ __device__ inline uint32_t rope_pair_sel(uint32_t v, uint32_t f) {
 }
 
 struct RoleLds {
-  int raw, vt, qt, theta, sp, pt, addr, keep, total;
+  int raw, vt, qt, theta, sp, pt, addr, keep, rtab, posr, total;
 };
-__host__ __device__ constexpr RoleLds role_lds() {
+// pos: the positions mode (SVAR query variants per super-tile, the RoPE factors of the 32 in-block offsets, a ring
+// of the super-tiles' slot positions)
+__host__ __device__ constexpr RoleLds role_lds(bool pos) {
   RoleLds L{};
   int o = 0;
-  L.raw = o; o += 4 * 4 * SRAW;             // per value wave: staging ring of 4 super-tiles
-  L.vt = o; o += 4 * 2 * SVT;               // per quarter: fp16 tiles of two super-tiles
-  L.qt = o; o += 3 * SGQ * SQB * 2;         // rotated query in fragment order, fp16, x 3
-  L.theta = o; o += (SD / 2) * 8;           // RoPE frequencies, turns per position
-  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;      // partial scores [buffer][key wave][token][head]
-  L.pt = o; o += 4 * 32 * SGQ * 2;          // probabilities [value wave][token][head] fp16
-  L.addr = o; o += SMAX_TILES * 8;          // page record address of each super-tile
-  L.keep = o; o += SMAX_TILES * 4;          // keep-mask word of each super-tile
+  L.raw = o; o += 4 * 4 * SRAW;                        // per value wave: staging ring of 4 super-tiles
+  L.vt = o; o += 4 * 2 * SVT;                          // per quarter: fp16 tiles of two super-tiles
+  L.qt = o; o += 3 * (pos ? SVAR : 1) * SGQ * SQB * 2;  // rotated query (variants) in fragment order, fp16, x 3
+  L.theta = o; o += (SD / 2) * 8;                      // RoPE frequencies, turns per position
+  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;                 // partial scores [buffer][key wave][token][head]
+  L.pt = o; o += 4 * 32 * SGQ * 2;                     // probabilities [value wave][token][head] fp16
+  L.addr = o; o += SMAX_TILES * 8;                     // page record address of each super-tile
+  L.keep = o; o += SMAX_TILES * 4;                     // keep-mask word (positions mode: base block) of each
+  L.rtab = o; o += pos ? 64 * SRT * 4 : 0;             // positions mode: RoPE factors [half][offset u][32]
+  L.posr = o; o += pos ? 8 * 32 * 4 : 0;               // positions mode: slot positions of super-tile k at k % 8
   L.total = o;
   return L;
 }
 
-template <bool KEEP, bool SPLIT, int KB>
+// POS: the positions mode of decode_shared_kernel (a compacted cache: slot positions tok_pos, SVAR query variants
+// per super-tile, R(u) of each token's in-block offset u from a table).  Value wave 0 also copies each
+// super-tile's 32 slot positions into a ring that both roles read after the barrier that follows its wait.
+template <bool KEEP, bool SPLIT, int KB, bool POS>
 __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeSharedArgs a) {
   constexpr int CB = SLAT * KB / 8;  // code bytes per token
   constexpr int QB = CB / 4;         // a quarter of them
   constexpr int NCH = QB / 16;       // its 16-byte chunks per token
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr RoleLds LY = role_lds();
+  constexpr RoleLds LY = role_lds(POS);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool keyw = wid < 4;
@@ -757,14 +764,19 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
   const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
   int64_t* taddr = (int64_t*)(smem + LY.addr);
   uint32_t* tkeep = (uint32_t*)(smem + LY.keep);
-  for (int k = tid; k < n_tiles; k += 512) {  // page record of each super-tile, its keep word
+  for (int k = tid; k < n_tiles; k += 512) {  // page record of each super-tile, its keep word (or base block)
     const int t0 = (st_begin + k) * 32;
     const int page = a.block_table[(size_t)b * a.max_blocks + t0 / P];
     taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * CB;
     const int wd = t0 >> 5;
     if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
+    if (POS) {  // base block of the super-tile: its first slot's (none: no slot of the tile is valid)
+      const int p0 = a.tok_pos[(size_t)b * a.pos_row + t0];
+      tkeep[k] = (uint32_t)(p0 >= 0 ? p0 >> 5 : 1 << 30);
+    }
   }
-  _Float16* qts = (_Float16*)(smem + LY.qt);  // rotated query of super-tile k: buffer k % 3
+  const int32_t* posr = (const int32_t*)(smem + LY.posr);
+  _Float16* qts = (_Float16*)(smem + LY.qt);  // rotated query of super-tile k: buffer k % 3 (variant v at its v-th quarter)
   float* sp = (float*)(smem + LY.sp);
   const uint8_t* vt_q = smem + LY.vt + wq * 2 * SVT;  // the quarter's fp16 tiles; super-tile k in k % 2
   __syncthreads();
@@ -791,26 +803,52 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
       }
     }
     // RoPE factors of this lane's slot t: block g's up-projection entry i is row 8(i/4) + 4hf + i%4, paired with
-    // entry i + 8; frequency 16g + that row
+    // entry i + 8; frequency 16g + that row.  Positions mode: a table of the factors of every in-block offset u,
+    // laid out as a lane of half hh takes them, read per super-tile at the token's own u.
     uint32_t rf[SNB][8];
-#pragma unroll
-    for (int g = 0; g < SNB; ++g)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
-        rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    uint32_t* rtab = (uint32_t*)(smem + LY.rtab);
+    if (POS) {
+      for (int e = tid; e < 64 * 32; e += 256) {
+        const int u = e >> 6, hh = (e >> 5) & 1, g = (e >> 3) & 3, i = e & 7;
+        const float rev = (float)(u * tturn[16 * g + 8 * (i >> 2) + 4 * hh + (i & 3)]);
+        rtab[(32 * hh + u) * SRT + 8 * g + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
       }
+    } else {
+#pragma unroll
+      for (int g = 0; g < SNB; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
+          rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+        }
+    }
     lds_barrier();  // the value waves' prologue: the tile of super-tile 0, the rotated queries of 0 and 1
     for (int k = 0; k < n_tiles; ++k) {
       const bool empty = KEEP && __builtin_amdgcn_readfirstlane(tkeep[k]) == 0u;
+      // positions mode: the token's block offset v from the super-tile's base picks its query variant, its
+      // in-block offset u its RoPE factors (slots of -1 or outside the SVAR blocks take no part)
+      int vsel = 0;
+      if constexpr (POS) {
+        const int pc = posr[(k & 7) * 32 + t];
+        const int v = (pc >> 5) - (int)tkeep[k];
+        vsel = pc >= 0 && v >= 0 && v < SVAR ? v : 0;
+        const u32x4_t* src = (const u32x4_t*)(rtab + (32 * hf + (pc & 31)) * SRT);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4_t x = src[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rf[j >> 1][4 * (j & 1) + e] = x[e];
+        }
+      }
       f16v_t sc = {};
       if ((!SPLIT || wq < 2) && !empty) {
         const uint8_t* tl = vt_q + (k & 1) * SVT + SCS * 8 * hf + 16 * t;
         h8 bc[SNJ];
 #pragma unroll
         for (int j = 0; j < SNJ; ++j) bc[j] = *(const h8*)(tl + SCS * j);
-        // score operand row t: query head t % 4
-        const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SQB + (t & 3) * SQB) + hf;
+        // score operand row t: query head t % 4 (positions mode: of variant (t / 4) % SVAR)
+        const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? (t >> 2) & (SVAR - 1) : 0)) * SGQ * SQB +
+                                   (t & 3) * SQB) + hf;
         // block g's chain, then block g - 1's RoPE and score products, interleaved with it by the scheduling groups
         // below (one matrix instruction, then up to three vector ones), so that a block's vector work runs under
         // the next block's matrix chain
@@ -840,7 +878,10 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
-      if (hf == 0) *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
+      // row 8 (j / 4) + 4 hf + j % 4 of entry j: this lane half holds variants hf (entries 0-3) and 2 + hf (4-7)
+      if (POS ? hf == (vsel & 1) : hf == 0)
+        *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + t) * SGQ) =
+            (POS && (vsel >> 1)) ? f4{sc[4], sc[5], sc[6], sc[7]} : f4{sc[0], sc[1], sc[2], sc[3]};
       lds_barrier();
     }
     return;
@@ -869,9 +910,22 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
   }
   const int qix = qfrag_index(wq, qj);
   const double fq = tturn[qj];
+  // positions mode: this thread's query pair rotated on from variant 0 to variant v by R(-32 v theta), v < SVAR
+  float vc[SVAR], vs[SVAR];
+  if (POS) {
+#pragma unroll
+    for (int v = 1; v < SVAR; ++v) {
+      double rev = -32.0 * v * fq;
+      rev -= rint(rev);
+      vc[v] = __builtin_amdgcn_cosf((float)rev);
+      vs[v] = __builtin_amdgcn_sinf((float)rev);
+    }
+  }
+  const uint32_t posr_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.posr));
 
   // staging of this quarter of super-tile k into ring slot k % 4, as in decode_shared_kernel (past the last
-  // super-tile the slot gets a copy of the last one; always four copy instructions)
+  // super-tile the slot gets a copy of the last one; always four copy instructions, and value wave 0 of the
+  // positions mode a fifth: the 32 slot positions into ring slot k % 8)
   auto issue = [&](int k) {
     const int kk = min(k, n_tiles - 1);
     const int slot0 = ((st_begin + kk) * 32) % P;
@@ -894,6 +948,9 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
       const int q = 64 * r + lane, tok = q >> 2, i = q & 3;
       copy4_to_lds(rs, dst + 2048 + 256 * r, pairs_at + tok * mpt + 4 * (g0 + (i & (npw - 1))));
     }
+    if (POS && wq == 0 && lane < 32)
+      copy4_to_lds(buffer_rsrc(a.tok_pos + (size_t)b * a.pos_row + (st_begin + kk) * 32, 128), posr_lds + (k & 7) * 128,
+                   4 * lane);
   };
   const int gr0 = ((SQC * wq + 64 * hf) >> lg) - g0, gr1 = ((SQC * wq + 64 * hf + 32) >> lg) - g0;
   // the lane's eight code groups of a staged super-tile as INT4 dwords (group j = coordinates 8 (8hf + j).. of
@@ -921,13 +978,21 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
 #pragma unroll
     for (int j = 0; j < SNJ; ++j) *(h8*)(dst + SCS * j) = dequant_int4x8(xs[j], j < 4 ? z0 : z1);
   };
-  auto rot_q = [&](int k) {
-    const double t0 = (double)((st_begin + k) * 32);
+  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order; positions mode: the SVAR
+  // variants R(q_pos - 32 (base + v)) q (base: the super-tile's base block)
+  auto rot_q = [&](int k, uint32_t base) {
+    const double t0 = POS ? 32.0 * (double)base : (double)((st_begin + k) * 32);
     double rev = ((double)qpos - t0) * fq;
     rev -= rint(rev);
     const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-    _Float16* qt = qts + (k % 3) * SGQ * SQB;
-    *(uint32_t*)(qt + qix) = pack_h2(qx * cs - qy * sn, qy * cs + qx * sn);
+    _Float16* qt = qts + (k % 3) * (POS ? SVAR : 1) * SGQ * SQB;
+    const float x0 = qx * cs - qy * sn, y0 = qy * cs + qx * sn;
+    *(uint32_t*)(qt + qix) = pack_h2(x0, y0);
+    if (POS) {
+#pragma unroll
+      for (int v = 1; v < SVAR; ++v)
+        *(uint32_t*)(qt + v * SGQ * SQB + qix) = pack_h2(x0 * vc[v] - y0 * vs[v], y0 * vc[v] + x0 * vs[v]);
+    }
   };
 
   f4 acc[SNJ];  // value latent on this quarter's coordinates, 16 per step, rows = query heads (replicated)
@@ -950,12 +1015,19 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
       f4 tot = *(const f4*)(spb + t * SGQ);
 #pragma unroll
       for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
-      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u));
+      bool valid = true;
+      if (POS) {  // a slot of -1, or outside the super-tile's SVAR blocks: no token
+        const int pc = posr[(k & 7) * 32 + t];
+        const int v = (pc >> 5) - (int)tkeep[k];
+        valid = pc >= 0 && v >= 0 && v < SVAR;
+      }
+      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u)) && valid;
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) s4[i] = kept ? tot[i] - m_ref[i] : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-    if (KEEP ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
+    // the first super-tile with a kept token sets the reference maximum (one with none leaves it unset)
+    if ((KEEP || POS) ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
              : fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
       float alpha[SGQ];
 #pragma unroll
@@ -1001,24 +1073,33 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
     // prologue: super-tiles 0-3 in flight, wait for 0, its tile; rotated queries of 0 and 1
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue(j);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+    if (POS && wq == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     uint32_t xs[8], z0, z1;
     load_words(0, xs, z0, z1);
     store_tile(0, xs, z0, z1);
-    rot_q(0);
-    rot_q(1);
+    rot_q(0, POS ? tkeep[0] : 0u);
+    rot_q(1, POS ? tkeep[min(1, n_tiles - 1)] : 0u);
   }
   lds_barrier();
   for (int k = 0; k < n_tiles; ++k) {
     issue(k + 4);  // ring slot k % 4 held super-tile k, stored into its tile before the previous barrier
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 12);  // super-tile k + 1 landed; k + 2 .. k + 4 may be in flight
+    // super-tile k + 1 landed; the copies of k + 2 .. k + 4 (four each, five for value wave 0 of the positions
+    // mode) may be in flight
+    if (POS && wq == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     uint32_t xs[8], z0, z1;
     load_words(k + 1, xs, z0, z1);
     if (k > 0) soft_value(k - 1);  // reads tile (k - 1) % 2, which super-tile k + 1 then takes
     store_tile(k + 1, xs, z0, z1);
-    rot_q(k + 2);  // buffer (k + 2) % 3 was last read by the key waves before the previous barrier
+    // buffer (k + 2) % 3 was last read by the key waves before the previous barrier
+    rot_q(k + 2, POS ? tkeep[min(k + 2, n_tiles - 1)] : 0u);
     lds_barrier();
   }
   if (n_tiles > 0) soft_value(n_tiles - 1);
@@ -1124,28 +1205,22 @@ static hipError_t launch_shared_one(int grid, hipStream_t st, const DecodeShared
   return hipGetLastError();
 }
 
-template <bool KEEP, bool SPLIT, int KB>
+template <bool KEEP, bool SPLIT, int KB, bool POS>
 static hipError_t launch_role_one(int grid, hipStream_t st, const DecodeSharedArgs& a) {
-  const void* kern = (const void*)decode_shared_role_kernel<KEEP, SPLIT, KB>;
-  constexpr int lds = role_lds().total;
+  const void* kern = (const void*)decode_shared_role_kernel<KEEP, SPLIT, KB, POS>;
+  constexpr int lds = role_lds(POS).total;
+  static_assert(lds <= 160 * 1024, "LDS of the role-split kernel");
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_shared_role_kernel<KEEP, SPLIT, KB>), dim3(grid), dim3(512), lds, st, a);
+  hipLaunchKernelGGL((decode_shared_role_kernel<KEEP, SPLIT, KB, POS>), dim3(grid), dim3(512), lds, st, a);
   return hipGetLastError();
 }
 
-template <bool KEEP, bool SPLIT>
-static hipError_t launch_role_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
-  if (kb == 3) return launch_role_one<KEEP, SPLIT, 3>(grid, st, a);
-  if (kb == 2) return launch_role_one<KEEP, SPLIT, 2>(grid, st, a);
-  return launch_role_one<KEEP, SPLIT, 4>(grid, st, a);
-}
-
 template <bool KEEP, bool SPLIT, bool POS>
-static hipError_t launch_shared_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
-  if (kb == 3) return launch_shared_one<KEEP, SPLIT, 3, POS>(grid, st, a);
-  if (kb == 2) return launch_shared_one<KEEP, SPLIT, 2, POS>(grid, st, a);
-  return launch_shared_one<KEEP, SPLIT, 4, POS>(grid, st, a);
+static hipError_t launch_role_bits(int kb, int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  if (kb == 3) return launch_role_one<KEEP, SPLIT, 3, POS>(grid, st, a);
+  if (kb == 2) return launch_role_one<KEEP, SPLIT, 2, POS>(grid, st, a);
+  return launch_role_one<KEEP, SPLIT, 4, POS>(grid, st, a);
 }
 
 // keep mask, positions and the residual are exclusive (the entry point rejects their combinations; the residual
@@ -1155,9 +1230,9 @@ static hipError_t launch_shared_variant(bool keep, bool pos, bool res, bool spli
   // the residual mode runs the plain-latent form also for a split latent: the products it then makes are exact
   // zeros, and the output is the full product's
   if (res) return launch_shared_one<false, false, 4, false, true>(grid, st, a);
-  if (pos) return split ? launch_shared_bits<false, true, true>(kb, grid, st, a) : launch_shared_bits<false, false, true>(kb, grid, st, a);
-  if (keep) return split ? launch_role_bits<true, true>(kb, grid, st, a) : launch_role_bits<true, false>(kb, grid, st, a);
-  return split ? launch_role_bits<false, true>(kb, grid, st, a) : launch_role_bits<false, false>(kb, grid, st, a);
+  if (pos) return split ? launch_role_bits<false, true, true>(kb, grid, st, a) : launch_role_bits<false, false, true>(kb, grid, st, a);
+  if (keep) return split ? launch_role_bits<true, true, false>(kb, grid, st, a) : launch_role_bits<true, false, false>(kb, grid, st, a);
+  return split ? launch_role_bits<false, true, false>(kb, grid, st, a) : launch_role_bits<false, false, false>(kb, grid, st, a);
 }
 
 hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const kvc_decode_in& in, float* out,
