@@ -26,9 +26,10 @@
 //     LDS reads.
 // The value up-projection W_v is applied once per (layer, sequence, head) in the merge kernel.
 //
-// Two forms of this layout: decode_shared_role_kernel (further below: 8 waves, key waves and value waves on each
-// SIMD) serves the plain, keep-mask and split-latent modes; decode_shared_kernel (one wave per SIMD, described
-// above) the positions and residual modes.  Their products, operands and order are the same.
+// Two kernels use this layout: decode_shared_role_kernel (further below: 8 waves, key waves and value waves on
+// each SIMD) serves the plain, keep-mask, split-latent and positions modes at every code width;
+// decode_shared_res_kernel (one wave per SIMD, as described above) the residual mode, whose residual operands do
+// not fit the registers of the role split.  Their common products, operands and order are the same.
 #include <math.h>
 
 #include <algorithm>
@@ -84,27 +85,22 @@ struct DecodeSharedArgs {
 static constexpr int SMAX_TILES = 1024;  // super-tiles per split (the page record address of each)
 
 struct SharedLds {
-  int raw, vt, qt, theta, sp, pt, addr, keep, rtab, posr, rres, vres, pt2, total;
+  int raw, vt, qt, theta, sp, pt, addr, rres, vres, pt2, total;
 };
-// pos: the positions mode (a ring of the super-tiles' slot positions, SVAR query bases per super-tile, a table of
-// the RoPE factors of the 32 in-block offsets).  res: the residual mode (a ring of the super-tiles' residual codes
-// and scales shared by the waves, per-wave value-residual tiles, the probabilities times the value scales).
-__host__ __device__ constexpr SharedLds shared_lds(bool pos, bool res = false) {
+// the LDS of the one-wave-per-SIMD kernel (the residual mode)
+__host__ __device__ constexpr SharedLds shared_lds() {
   SharedLds L{};
   int o = 0;
-  L.raw = o; o += 4 * 4 * SRAW;                          // per wave: staging ring of 4 super-tiles
-  L.vt = o; o += 4 * 2 * SVT;                            // per wave: fp16 value tiles, x 2
-  L.qt = o; o += 3 * (pos ? SVAR : 1) * SGQ * SQB * 2;   // rotated query (variants) in fragment order, fp16, x 3
-  L.theta = o; o += (SD / 2) * 8;                        // RoPE frequencies, turns per position
-  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;                   // partial scores [buffer][wave][token][head], x 2
-  L.pt = o; o += 4 * 32 * SGQ * 2;                       // probabilities [wave][token][head] fp16
-  L.addr = o; o += SMAX_TILES * 8;                       // page record address of each super-tile
-  L.keep = o; o += SMAX_TILES * 4;                       // keep-mask word (positions mode: base block) of each
-  L.rtab = o; o += pos ? 64 * SRT * 4 : 0;               // positions mode: RoPE factors [half][offset u][32]
-  L.posr = o; o += pos ? 8 * 32 * 4 : 0;                 // positions mode: slot positions of super-tile k at k % 8
-  L.rres = o; o += res ? SRRN * SRR : 0;                 // residual mode: ring of the super-tiles' residuals
-  L.vres = o; o += res ? 16 * SRCS : 0;                  // residual mode: value waves' fp16 tiles, 16 chunks in all
-  L.pt2 = o; o += res ? 4 * 32 * SGQ * 2 : 0;            // residual mode: [wave][token][head] p * value scale
+  L.raw = o; o += 4 * 4 * SRAW;          // per wave: staging ring of 4 super-tiles
+  L.vt = o; o += 4 * 2 * SVT;            // per wave: fp16 value tiles, x 2
+  L.qt = o; o += 3 * SGQ * SQB * 2;      // rotated query in fragment order, fp16, x 3
+  L.theta = o; o += (SD / 2) * 8;        // RoPE frequencies, turns per position
+  L.sp = o; o += 2 * 4 * 32 * SGQ * 4;   // partial scores [buffer][wave][token][head], x 2
+  L.pt = o; o += 4 * 32 * SGQ * 2;       // probabilities [wave][token][head] fp16
+  L.addr = o; o += SMAX_TILES * 8;       // page record address of each super-tile
+  L.rres = o; o += SRRN * SRR;           // ring of the super-tiles' residuals
+  L.vres = o; o += 16 * SRCS;            // the waves' fp16 value-residual tiles, 16 chunks in all
+  L.pt2 = o; o += 4 * 32 * SGQ * 2;      // [wave][token][head] p * value scale
   L.total = o;
   return L;
 }
@@ -120,32 +116,19 @@ __device__ inline int qfrag_index(int head, int dim) {
   return head * SQB + ((g * 2 + st) * 2 + hf) * 8 + e;
 }
 
-// KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it).
-// SPLIT: latent coordinates below SLAT / 2 feed only the keys and the rest only the values (W_k zero on the upper
-// rows, W_v on the lower, as for keys and values with their own token factors): waves 0-1 then do only the key
-// work and waves 2-3 only the value product; their skipped products are exact zeros, so the output is the same.
-// KB: latent code bits (4; or 3 and 2, whose codes a wave stages token-major and spreads to the INT4 nibble layout)
-// RES: the rotated 2-bit residual of each (layer, head) (KB = 4, no keep mask, no positions).  Its codes and scales
-// are staged by waves 0-2 (one copy each per super-tile) into a ring every wave reads after the next score barrier.
-// Keys: the key waves add K_res = (s / sqrt(128)) (H' c - 192 [d = 0]) of their head-dim blocks (the fp8 matrix
-// instruction with the +-1 Hadamard, as in the per-head residual kernel) to their partial keys before RoPE.
-// Values: the value waves accumulate sum_t p_t s_t (2c - 3) / (2 sqrt(128)) on their share of the 128 rotated
-// coordinates; the merge applies H'.
-// POS: a compacted cache whose slots hold tokens at the source positions tok_pos (no keep mask).  A super-tile's
-// tokens lie within SVAR blocks of 32 positions from its first slot's block `base` (the layout the compaction
-// writes): a token at position 32 (base + v) + u is rotated by R(u), from a table, and scored against the query
-// rotated by R(q_pos - 32 (base + v)), one of SVAR variants in the score operand's rows.  Other slots take no part.
-template <bool KEEP, bool SPLIT, int KB, bool POS, bool RES>
-__global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs a) {
-  constexpr int CB = SLAT * KB / 8;  // code bytes per token
-  constexpr int QB = CB / 4;         // a wave's quarter of them
-  constexpr int NCH = QB / 16;       // its 16-byte chunks per token
+// The residual mode: the rotated 2-bit residual of each (layer, head) on top of the INT4 latent (no keep mask, no
+// positions; a split latent runs this plain-latent form, whose extra products are then exact zeros).  Waves 0-2
+// each stage one more part of every super-tile (the (layer, head)'s K residual codes, V residual codes, both scale
+// rows) into a ring every wave reads after the next score barrier.  Keys: wave w adds
+// K_res = (s / sqrt(128)) (H' c - 192 [d = 0]) of head-dim block w (the fp8 matrix instruction with the +-1
+// Hadamard, as in the per-head residual kernel) to its partial keys before RoPE.  Values: wave w accumulates
+// sum_t p_t s_t (2c - 3) / (2 sqrt(128)) on rotated coordinates 32w .. 32w + 31; the merge applies H'.
+__global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedArgs a) {
+  constexpr int CB = SLAT / 2;  // code bytes per token (INT4)
+  constexpr int QB = CB / 4;    // a wave's quarter of them
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr SharedLds LY = shared_lds(POS, RES);
-  constexpr int NKW = SPLIT ? 2 : 4;   // waves doing key work (the first NKW)
-  constexpr int NRB = 4 / NKW;         // residual mode: head-dim blocks of keys per key wave (blocks wv + NKW j)
-  constexpr int CPW = 128 / NKW;       // residual mode: value coordinates per value wave (the last NKW waves)
-  constexpr int RST = CPW / 16;        // residual mode: 16-coordinate value steps per value wave
+  constexpr SharedLds LY = shared_lds();
+  constexpr int RST = 2;        // 16-coordinate steps of the wave's 32 rotated value-residual coordinates
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 31, hf = lane >> 5, rho = lane & 15, grp = lane >> 4;
@@ -166,7 +149,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   // 64 + 16g + r - 16; step j: k-slot 8hf + e <-> latent coordinate 128w + 8 (8hf + j) + perm8(e), i.e.
   // element e of code dword 8hf + j of the wave's 64 code bytes (the order a code dword dequantizes).
   h8 wf[SNB][SNJ];
-  if (!SPLIT || wv < 2) {
+  {
     const int width = a.Hkv * SD;
     const uint16_t* W = a.wk + (size_t)b * a.w_stride + (size_t)l * SLAT * width + (size_t)h * SD;
 #pragma unroll
@@ -184,29 +167,25 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       }
     }
   }
-  // residual mode: +-1 Hadamard rows of this key wave's head-dim blocks g = wv + NKW j as fp8 A fragments (row t <->
-  // the block's head dim, byte b of lane half hf's 32 of block-half be <-> coordinate 64 be + res8_coord(hf, b);
-  // e4m3 +1 = 0x38, -1 = 0xB8), kept in the accumulator registers the fp8 products read directly
-  v8i_t hr[NRB][2];
-  if (RES && (!SPLIT || wv < 2)) {
+  // +-1 Hadamard rows of this wave's head-dim block (block w) as fp8 A fragments (row t <-> the block's head dim,
+  // byte b of lane half hf's 32 of block-half be <-> coordinate 64 be + res8_coord(hf, b); e4m3 +1 = 0x38,
+  // -1 = 0xB8), kept in the accumulator registers the fp8 products read directly
+  v8i_t hr[2];
+  {
+    const int dim = t < 16 ? 16 * wv + t : 64 + 16 * wv + (t - 16);
 #pragma unroll
-    for (int j = 0; j < NRB; ++j) {
-      const int g = wv + NKW * j;
-      const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
+    for (int be = 0; be < 2; ++be) {
 #pragma unroll
-      for (int be = 0; be < 2; ++be) {
+      for (int o = 0; o < 8; ++o) {
+        uint32_t w = 0;
 #pragma unroll
-        for (int o = 0; o < 8; ++o) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = 64 * be + res8_coord(hf, 4 * o + q);
-            w |= ((__builtin_popcount(dim & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
-          }
-          hr[j][be][o] = (int)w;
+        for (int q = 0; q < 4; ++q) {
+          const int i = 64 * be + res8_coord(hf, 4 * o + q);
+          w |= ((__builtin_popcount(dim & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
         }
-        asm volatile("" : "=a"(hr[j][be]) : "0"(hr[j][be]));
+        hr[be][o] = (int)w;
       }
+      asm volatile("" : "=a"(hr[be]) : "0"(hr[be]));
     }
   }
   double* tturn = (double*)(smem + LY.theta);
@@ -232,74 +211,45 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   const int st_begin = split * a.st_per_split;
   const int n_tiles = max(0, min(n_st, st_begin + a.st_per_split) - st_begin);
   int64_t* taddr = (int64_t*)(smem + LY.addr);
-  uint32_t* tkeep = (uint32_t*)(smem + LY.keep);
-  for (int k = tid; k < n_tiles; k += 256) {  // page record of each super-tile, its first slot, its keep word
+  for (int k = tid; k < n_tiles; k += 256) {  // page record of each super-tile (at its first slot)
     const int t0 = (st_begin + k) * 32;
     const int page = a.block_table[(size_t)b * a.max_blocks + t0 / P];
     taddr[k] = a.page_off[page] + (int64_t)(t0 % P) * CB;
-    const int wd = t0 >> 5;
-    if (KEEP) tkeep[k] = wd < a.keep_words ? a.keep[(size_t)b * a.keep_words + wd] : 0u;
-    if (POS) {  // base block of the super-tile: its first slot's (none: no slot of the tile is valid)
-      const int p0 = a.tok_pos[(size_t)b * a.pos_row + t0];
-      tkeep[k] = (uint32_t)(p0 >= 0 ? p0 >> 5 : 1 << 30);
-    }
   }
-  uint32_t* rtab = (uint32_t*)(smem + LY.rtab);
   __syncthreads();
-  if (POS) {  // RoPE factors of in-block offset u, laid out as the lane of half hf takes them (rf below)
-    for (int e = tid; e < 64 * 32; e += 256) {
-      const int u = e >> 6, hh = (e >> 5) & 1, g = (e >> 3) & 3, i = e & 7;
-      const float rev = (float)(u * tturn[16 * g + 8 * (i >> 2) + 4 * hh + (i & 3)]);
-      rtab[(32 * hh + u) * SRT + 8 * g + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-    }
-  }
   const double fq = tturn[qj];
   // RoPE factors of this lane's slot t: block g's up-projection entry i (0..7) is row 8(i/4) + 4hf + i%4 (< 16),
   // paired with entry i + 8 (that row + 16): frequency 16g + row; |t theta| < 32 turns, where v_sin / v_cos are
   // accurate
-  // (positions mode: per super-tile from the table, at the token's own in-block offset)
   uint32_t rf[SNB][8];
-  if (!POS) {
 #pragma unroll
-    for (int g = 0; g < SNB; ++g)
+  for (int g = 0; g < SNB; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
-        rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-      }
-  }
-  // positions mode: this thread's query pair rotated on from variant 0 to variant v by R(-32 v theta), v < SVAR
-  float vc[SVAR], vs[SVAR];
-  if (POS) {
-#pragma unroll
-    for (int v = 1; v < SVAR; ++v) {
-      double rev = -32.0 * v * fq;
-      rev -= rint(rev);
-      vc[v] = __builtin_amdgcn_cosf((float)rev);
-      vs[v] = __builtin_amdgcn_sinf((float)rev);
+    for (int i = 0; i < 8; ++i) {
+      const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
+      rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
     }
-  }
 
   uint8_t* raw_w = smem + LY.raw + wv * 4 * SRAW;  // this wave's ring; super-tile k in slot k % 4
-  const int32_t* posr = (const int32_t*)(smem + LY.posr);
-  const uint32_t posr_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.posr));
   const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw_w));
   uint8_t* vt_w = smem + LY.vt + wv * 2 * SVT;     // this wave's fp16 tiles; super-tile k in k % 2
   _Float16* qts = (_Float16*)(smem + LY.qt);       // rotated query of super-tile k: buffer k % 3 (see rot_q)
   float* sp = (float*)(smem + LY.sp);
   _Float16* pt = (_Float16*)(smem + LY.pt) + wv * 32 * SGQ;
-  const uint8_t* rres = smem + LY.rres;  // residual mode: super-tile k's residual at rres + (k % SRRN) * SRR
+  const uint8_t* rres = smem + LY.rres;  // super-tile k's residual at rres + (k % SRRN) * SRR
   const uint32_t rres_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.rres));
-  uint8_t* vr_w = smem + LY.vres + max(0, wv - (4 - NKW)) * (CPW / 8) * SRCS;  // value waves' residual tiles
+  uint8_t* vr_w = smem + LY.vres + wv * 4 * SRCS;  // this wave's value-residual tile (4 chunk rows)
   _Float16* pt2 = (_Float16*)(smem + LY.pt2) + wv * 32 * SGQ;
   constexpr float RSCALE = 0.04419417382415922f;  // 1 / (2 sqrt(128))
 
   const int64_t meta_base = pad16((int64_t)P * CB);
 
   // ---- staging: this wave's part of super-tile k into ring slot k % 4; past the last super-tile the slot gets a
-  // copy of the last one, which keeps the number of copies in flight constant.  Always four copy instructions:
+  // copy of the last one, which keeps the number of copies in flight constant.  Four copy instructions, and a
+  // fifth for waves 0-2 (the residual):
   //   codes: 32 tokens x 4 chunks (bytes 64w + 16c .. of each token), slot p = 32c + t <- token t's chunk c;
-  //   pairs: dword 4 t + i <- pair g0 + (i mod npw) of token t, i < 4 (two instructions, 16 tokens each).
+  //   pairs: dword 4 t + i <- pair g0 + (i mod npw) of token t, i < 4 (two instructions, 16 tokens each);
+  //   residual: wave 0 the K codes, wave 1 the V codes (32 bytes per token), wave 2 both scale rows.
   auto issue = [&](int k) {
     const int kk = min(k, n_tiles - 1);
     const int slot0 = ((st_begin + kk) * 32) % P;
@@ -312,24 +262,14 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int p = 64 * r + lane;
-      if (KB == 4) {
-        copy16_to_lds(rs, dst + 1024 * r, (p & 31) * CB + QB * wv + 16 * (p >> 5));
-      } else {
-        // token-major: LDS chunk p <- token p / NCH's chunk p % NCH (lanes past 32 NCH repeat the last chunk into
-        // the unused end of the slot, keeping two copy instructions per super-tile)
-        const int pc = min(p, 32 * NCH - 1);
-        copy16_to_lds(rs, dst + 1024 * r, (pc / NCH) * CB + QB * wv + 16 * (pc % NCH));
-      }
+      copy16_to_lds(rs, dst + 1024 * r, (p & 31) * CB + QB * wv + 16 * (p >> 5));
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int q = 64 * r + lane, tok = q >> 2, i = q & 3;
       copy4_to_lds(rs, dst + 2048 + 256 * r, pairs_at + tok * mpt + 4 * (g0 + (i & (npw - 1))));
     }
-    if (POS && wv == 0 && lane < 32)  // the 32 slots' source positions, for every wave (read after a barrier)
-      copy4_to_lds(buffer_rsrc(a.tok_pos + (size_t)b * a.pos_row + (st_begin + kk) * 32, 128),
-                   posr_lds + (k & 7) * 128, 4 * lane);
-    if (RES && wv < 3) {  // the super-tile's residual of this (layer, head): K codes, V codes, both scales
+    if (wv < 3) {  // the super-tile's residual of this (layer, head): K codes, V codes, both scales
       const i32x4_t rr = buffer_rsrc(a.pool + (at - (int64_t)slot0 * CB), a.rec_bytes);
       const uint32_t rdst = rres_lds + (k % SRRN) * SRR;
       const int n = a.L * a.Hkv, idx = l * a.Hkv + h;
@@ -345,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   f4 acc[SNJ];  // value latent on this wave's coordinates, 16 per step, rows = query heads (replicated)
 #pragma unroll
   for (int i = 0; i < SNJ; ++i) acc[i] = f4{0, 0, 0, 0};
-  f4 accr[RST];  // residual mode: the rotated value residual on this value wave's coordinates
+  f4 accr[RST];  // the rotated value residual on this wave's coordinates
 #pragma unroll
   for (int i = 0; i < RST; ++i) accr[i] = f4{0, 0, 0, 0};
   float m_ref[SGQ], psum[SGQ];
@@ -360,21 +300,15 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
   // coordinates) of token t at byte SCS c + 16 t
   const int gr0 = ((SQC * wv + 64 * hf) >> lg) - g0, gr1 = ((SQC * wv + 64 * hf + 32) >> lg) - g0;
   // the lane's eight code groups of a staged super-tile as INT4 dwords: group j = coordinates 8 (8hf + j)..
-  // of the wave's quarter of token t
+  // of the wave's quarter of token t.  (Dword reads: the compiler merges them, and unlike a vector read of this
+  // copy target it then adds no wait for every copy in flight.)
   auto code_words = [&](const uint8_t* raw, uint32_t (&xs)[8]) {
-    if (KB == 4) {
-      // (dword reads: the compiler merges them, and unlike a vector read of this copy target it then adds no
-      // wait for every copy in flight)
-      const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);       // chunk 2hf: dwords 8hf + 0..3
-      const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
+    const uint32_t* c0 = (const uint32_t*)(raw + (64 * hf + t) * 16);       // chunk 2hf: dwords 8hf + 0..3
+    const uint32_t* c1 = (const uint32_t*)(raw + (64 * hf + 32 + t) * 16);  // chunk 2hf + 1: dwords 8hf + 4..7
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xs[j] = c0[j];
-        xs[4 + j] = c1[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xs[j] = codes8_as_nibbles<KB>(raw + QB * t, KB * (8 * hf + j));
+    for (int j = 0; j < 4; ++j) {
+      xs[j] = c0[j];
+      xs[4 + j] = c1[j];
     }
   };
   auto dequant = [&](int k, h8 (&bf)[SNJ], int vb) {
@@ -390,95 +324,50 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       *(h8*)(dst + SCS * j) = bf[j];
     }
   };
-  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order.  Positions mode:
-  // the SVAR variants R(q_pos - 32 (base + v)) q into buffer k % 3 (variant v at its v-th quarter)
-  // (base: positions mode, the super-tile's base block).  A pair's x and y are adjacent elements (qiy = qix + 1).
-  auto rot_q = [&](int k, uint32_t base) {
-    const double t0 = POS ? 32.0 * (double)base : (double)((st_begin + k) * 32);
+  // rotated query q~ = R(q_pos - t0) q of super-tile k into buffer k % 3, in fragment order.  A pair's x and y are
+  // adjacent elements (qiy = qix + 1).
+  auto rot_q = [&](int k) {
+    const double t0 = (double)((st_begin + k) * 32);
     double rev = ((double)qpos - t0) * fq;
     rev -= rint(rev);
     const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-    _Float16* qt = qts + (k % 3) * (POS ? SVAR : 1) * SGQ * SQB;
+    _Float16* qt = qts + (k % 3) * SGQ * SQB;
     const float x0 = qx * cs - qy * sn, y0 = qy * cs + qx * sn;
     *(uint32_t*)(qt + qix) = pack_h2(x0, y0);
-    if (POS) {
-#pragma unroll
-      for (int v = 1; v < SVAR; ++v)
-        *(uint32_t*)(qt + v * SGQ * SQB + qix) = pack_h2(x0 * vc[v] - y0 * vs[v], y0 * vc[v] + x0 * vs[v]);
-    }
   };
 
   // One super-tile: bc holds its B fragments (its fp16 tile is buffer k % 2); the next super-tile is dequantized
   // into bn on the way.
-  // pc: positions mode, this lane's slot position in super-tile k (read with k's code words); pn gets k + 1's
-  auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ], int pc, int& pn) {
+  auto step = [&](int k, h8 (&bc)[SNJ], h8 (&bn)[SNJ]) {
     issue(k + 4);  // ring slot k % 4 held super-tile k, dequantized in the previous step
     const int t0 = (st_begin + k) * 32;
-    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each; five for wave 0 of the positions mode and
-    // waves 0-2 of the residual mode) may still be in flight
-    if ((POS && wv == 0) || (RES && wv < 3))
+    // super-tile k + 1 landed: the copies of k + 2 .. k + 4 (four each; five for waves 0-2) may still be in flight
+    if (wv < 3)
       __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    // sources of super-tile k + 1's dequantization (dword reads: see dequant)
+    // sources of super-tile k + 1's dequantization (dword reads: see code_words)
     const uint8_t* rawn = raw_w + ((k + 1) & 3) * SRAW;
     uint32_t xs[8];
     code_words(rawn, xs);
     const uint32_t z0 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr0));
     const uint32_t z1 = *(const uint32_t*)(rawn + 2048 + 4 * (4 * t + gr1));
     uint8_t* vdst = vt_w + ((k + 1) & 1) * SVT + SCS * 8 * hf + 16 * t;
-    const uint32_t base2 = POS ? tkeep[min(k + 2, n_tiles - 1)] : 0u;  // super-tile k + 2's, for its query
-
-    // positions mode: the token's block offset v from the super-tile's base picks its query variant, its in-block
-    // offset u its RoPE factors; other lanes hold the factors of their slot t
-    int vsel = 0;
-    bool valid = true;
-    uint32_t rk[SNB][8];
-    if constexpr (POS) {
-      const int v = (pc >> 5) - (int)tkeep[k];
-      valid = pc >= 0 && v >= 0 && v < SVAR;
-      vsel = valid ? v : 0;
-      const u32x4_t* src = (const u32x4_t*)(rtab + (32 * hf + (pc & 31)) * SRT);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4_t x = src[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rk[j >> 1][4 * (j & 1) + e] = x[e];
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < SNB; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rk[g][i] = rf[g][i];
-    }
 
     // ---- partial keys over this wave's coordinates (block by block), RoPE, partial scores of the four heads.
     // The instruction stream interleaves each block's matrix instructions with vector work that does not wait
     // for them (two chunks of the next super-tile's dequantization, the previous block's RoPE), so that one
     // wave keeps both units busy.
-    // score operand row t: query head t % 4 (positions mode: of variant (t / 4) % SVAR)
-    const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? (t >> 2) & (SVAR - 1) : 0)) * SGQ * SQB +
-                               (t & 3) * SQB) + hf;
+    // score operand row t: query head t % 4
+    const h8* qf = (const h8*)(qts + (k % 3) * SGQ * SQB + (t & 3) * SQB) + hf;
     f16v_t sc = {};
-    // residual mode: the key residual codes of this lane's token (one per byte: the fp8 B operands of H' c) and its
-    // scale; super-tile k's residual is visible since the previous barrier.  H' c of a block is formed beside the
-    // block's up-projection and added, scaled, before the block's RoPE.
+    // the key residual codes of this lane's token (one per byte: the fp8 B operands of H' c) and its scale;
+    // super-tile k's residual is visible since the previous barrier.  H' c of block w is formed beside that
+    // block's up-projection and added, scaled, before its RoPE.
     f16v_t ra = {};
     float ksc = 0.0f;
     const uint8_t* rrk = rres + (k % SRRN) * SRR;
-    // a super-tile whose tokens are all evicted contributes nothing: only the next one's dequantization runs
-    const bool empty = KEEP && tkeep[k] == 0u;
-    if (SPLIT && wv >= 2) {  // value waves: only the next super-tile's value tile
-#pragma unroll
-      for (int jj = 0; jj < SNJ; ++jj) *(h8*)(vdst + SCS * jj) = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
-    } else if (empty) {
-#pragma unroll
-      for (int jj = 0; jj < SNJ; ++jj) {
-        bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
-        if (!SPLIT) *(h8*)(vdst + SCS * jj) = bn[jj];
-      }
-    } else {
     f16v_t kp[SNB];
 #pragma unroll
     for (int g = 0; g <= SNB; ++g) {
@@ -486,44 +375,35 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
         kp[g] = f16v_t{};
 #pragma unroll
         for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
-        if (RES) {  // H' c of block g, if it is one of this wave's (exact integers)
+        if (g == wv) {  // H' c of this wave's block (exact integers)
+          uint32_t krw[4];
 #pragma unroll
-          for (int j = 0; j < NRB; ++j)
-            if (g == wv + NKW * j) {
-              uint32_t krw[4];
+          for (int be = 0; be < 2; ++be)
 #pragma unroll
-              for (int be = 0; be < 2; ++be)
+            for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(rrk + 32 * t + 4 * (4 * be + 2 * hf + i));
+          ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rrk + 2048 + 2 * t)) * (2.0f * RSCALE);
+          v8i_t er[2];  // the codes one per byte (the fp8 B operands): byte q of dword o = code m + 4q, m = o % 4
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                  krw[2 * be + i] = *(const uint32_t*)(rrk + 32 * t + 4 * (4 * be + 2 * hf + i));
-              ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rrk + 2048 + 2 * t)) * (2.0f * RSCALE);
-              v8i_t er[2];  // the codes one per byte (the fp8 B operands): byte q of dword o = code m + 4q, m = o % 4
+          for (int be = 0; be < 2; ++be)
 #pragma unroll
-              for (int be = 0; be < 2; ++be)
-#pragma unroll
-                for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
-              ra = mfma_f8_codes(hr[j][1], er[1], mfma_f8_codes(hr[j][0], er[0], f16v_t{}));
-              if (g == 0 && hf == 0) ra[0] -= 192.0f;  // H' 1 is 128 at head dim 0 (row 0): the -1.5 offset
-            }
+            for (int o = 0; o < 8; ++o) er[be][o] = (int)((krw[2 * be + (o >> 2)] >> (2 * (o & 3))) & 0x03030303u);
+          ra = mfma_f8_codes(hr[1], er[1], mfma_f8_codes(hr[0], er[0], f16v_t{}));
+          if (g == 0 && hf == 0) ra[0] -= 192.0f;  // H' 1 is 128 at head dim 0 (row 0): the -1.5 offset
         }
 #pragma unroll
         for (int jj = 2 * g; jj < 2 * g + 2; ++jj) {
           bn[jj] = dequant_int4x8(xs[jj], jj < 4 ? z0 : z1);
-          if (!SPLIT) *(h8*)(vdst + SCS * jj) = bn[jj];  // key waves of a split latent make no value product
+          *(h8*)(vdst + SCS * jj) = bn[jj];
         }
       }
       if (g > 0) {
-        if (RES) {  // the key residual of block g - 1, if it is one of this wave's
+        if (g - 1 == wv)  // the key residual of block g - 1, if it is this wave's
 #pragma unroll
-          for (int j = 0; j < NRB; ++j)
-            if (g - 1 == wv + NKW * j)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) kp[g - 1][i] += ksc * ra[i];
-        }
+          for (int i = 0; i < 16; ++i) kp[g - 1][i] += ksc * ra[i];
         // rotated pairs (x, y) of rows 8st + 4hf + m, m < 4, are the k-slots 8hf + 2m, 2m + 1 of score step st
         u32x4_t kr[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rk[g - 1][i]);
+        for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rf[g - 1][i]);
         sc = mfma32s(qf[4 * (g - 1)], __builtin_bit_cast(h8, kr[0]), sc);
         sc = mfma32s(qf[4 * (g - 1) + 2], __builtin_bit_cast(h8, kr[1]), sc);
       }
@@ -537,14 +417,11 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the previous block's score products
     }
-    }
     float* spb = sp + (k & 1) * (4 * 32 * SGQ);
-    // row 8 (j / 4) + 4 hf + j % 4 of entry j: this lane half holds variants hf (entries 0-3) and 2 + hf (4-7)
-    if (POS ? hf == (vsel & 1) : hf == 0)
-      *(f4*)(spb + (wv * 32 + t) * SGQ) = (POS && (vsel >> 1)) ? f4{sc[4], sc[5], sc[6], sc[7]} : f4{sc[0], sc[1], sc[2], sc[3]};
+    // row 8 (j / 4) + 4 hf + j % 4 of entry j: lane half 0 holds the four heads in entries 0-3
+    if (hf == 0) *(f4*)(spb + (wv * 32 + t) * SGQ) = f4{sc[0], sc[1], sc[2], sc[3]};
     lds_barrier();
-    if (POS) pn = posr[((k + 1) & 7) * 32 + t];  // wave 0 waited for its copy before the barrier
-    rot_q(k + 2, base2);  // buffer (k + 2) % 3 was last read before the previous barrier
+    rot_q(k + 2);  // buffer (k + 2) % 3 was last read before the previous barrier
 
     // ---- scores of the four heads for token t (the same in every wave), lazy online softmax
     float s4[SGQ];
@@ -552,16 +429,12 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       f4 tot = *(const f4*)(spb + t * SGQ);
 #pragma unroll
       for (int w2 = 1; w2 < 4; ++w2) tot += *(const f4*)(spb + (w2 * 32 + t) * SGQ);
-      // past the end, evicted, or (positions mode) no token: no weight
-      const bool kept = t0 + t < T && (!KEEP || ((tkeep[k] >> t) & 1u)) && valid;
+      const bool kept = t0 + t < T;  // past the end: no weight
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) s4[i] = kept ? tot[i] - m_ref[i] : -INFINITY;
     }
     const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-    // the first super-tile with a kept token sets the reference maximum; one with none (possible under a keep
-    // mask only) leaves it unset
-    if ((KEEP || POS) ? __builtin_amdgcn_ballot_w64(fresh ? mx > -INFINITY : mx > STAU) != 0
-             : fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
+    if (fresh || __builtin_amdgcn_ballot_w64(mx > STAU) != 0) {
       float alpha[SGQ];
 #pragma unroll
       for (int i = 0; i < SGQ; ++i) {
@@ -578,11 +451,10 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       for (int nt = 0; nt < SNJ; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha[i];
-      if (RES)
 #pragma unroll
-        for (int nt = 0; nt < RST; ++nt)
+      for (int nt = 0; nt < RST; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) accr[nt][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) accr[nt][i] *= alpha[i];
       fresh = false;
     }
     float p[SGQ];
@@ -592,22 +464,21 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
       psum[i] += p[i];
     }
     if (hf == 0) *(h4*)(pt + SGQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-    // residual mode, value waves: the token's 2c - 3 over this wave's coordinates into its tile (chunk 2 jj + hf <->
-    // coordinates CPW vw + 16 jj + res_coord(hf, e)), and p times the token's value scale / (2 sqrt(128))
-    if (RES && (!SPLIT || wv >= 2)) {
+    // the token's 2c - 3 over this wave's coordinates into its tile (chunk 2 jj + hf <-> coordinates
+    // 32 w + 16 jj + res_coord(hf, e)), and p times the token's value scale / (2 sqrt(128))
+    {
       const uint8_t* rr = rres + (k % SRRN) * SRR;
-      const int vw = wv - (4 - NKW);
 #pragma unroll
       for (int jj = 0; jj < RST; ++jj)
         *(h8*)(vr_w + SRCS * (2 * jj + hf) + 16 * t) =
-            res_2c3(*(const uint32_t*)(rr + 1024 + 32 * t + 4 * (RST * vw + jj)), hf);
+            res_2c3(*(const uint32_t*)(rr + 1024 + 32 * t + 4 * (RST * wv + jj)), hf);
       const float vsc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rr + 2048 + 64 + 2 * t)) * RSCALE;
       if (hf == 0)
         *(h4*)(pt2 + SGQ * t) = h4{(_Float16)(p[0] * vsc), (_Float16)(p[1] * vsc), (_Float16)(p[2] * vsc),
                                    (_Float16)(p[3] * vsc)};
     }
     wave_lds_sync();
-    if (RES && (!SPLIT || wv >= 2)) {  // the rotated value residual: (p s) x (2c - 3), 16 coordinates per step
+    {  // the rotated value residual: (p s) x (2c - 3), 16 coordinates per step
       const h8 pops = lds_tr8s(pt2 + SGQ * (8 * grp + (rho >> 2)), pt2 + SGQ * (8 * grp + 4 + (rho >> 2)));
       const int q4 = rho & 3;
       const uint8_t* vb = vr_w + SRCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
@@ -618,7 +489,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // (g = l / 16); lane rho of its group points at the row of token 8g + 4v + rho / 4
     // value latent: step nt covers chunks 2nt, 2nt + 1; column n <-> coordinate 128w + 16nt + 8(n/8) + perm8(n%8);
     // lane rho points at the 4 columns 4(q4 % 2).. of chunk (2nt + q4 / 2, token 8g + 4v + rho / 4)
-    if ((!SPLIT || wv >= 2) && !empty) {
+    {
       const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
       const int q4 = rho & 3;
       const uint8_t* vb = vt_w + (k & 1) * SVT + SCS * (q4 >> 1) + (8 * grp + (rho >> 2)) * 16 + (q4 & 1) * 8;
@@ -634,27 +505,27 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
     // prologue: super-tiles 0-3 in flight, wait for 0, dequantize it; rotated queries of 0 and 1
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue(j);
-    if ((POS && wv == 0) || (RES && wv < 3))
+    if (wv < 3)
       __builtin_amdgcn_s_waitcnt(0x0F70 | 15);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     h8 ba[SNJ], bb[SNJ];
     dequant(0, ba, 0);
-    rot_q(0, POS ? tkeep[0] : 0u);
-    rot_q(1, POS ? tkeep[min(1, n_tiles - 1)] : 0u);
+    rot_q(0);
+    rot_q(1);
     lds_barrier();
-    int pa = POS ? posr[t] : 0, pb = 0;
     int k = 0;
     for (; k + 1 < n_tiles; k += 2) {
-      step(k, ba, bb, pa, pb);
-      step(k + 1, bb, ba, pb, pa);
+      step(k, ba, bb);
+      step(k + 1, bb, ba);
     }
-    if (k < n_tiles) step(k, ba, bb, pa, pb);
+    if (k < n_tiles) step(k, ba, bb);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies past the end land before the workgroup exits
   }
 
-  // ---- partial: m[4], l[4] (the same in every wave), acc[4][512] (wave w: coordinates 128w..128w+127)
+  // ---- partial: m[4], l[4] (the same in every wave), acc[4][512] (wave w: coordinates 128w..128w+127), then the
+  // rotated value residual accr[4][128] (wave w: coordinates 32w..32w+31)
 #pragma unroll
   for (int i = 0; i < SGQ; ++i) {
     float v = hf == 0 ? psum[i] : 0.0f;
@@ -674,28 +545,26 @@ __global__ __launch_bounds__(256, 1) void decode_shared_kernel(DecodeSharedArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[2 * SGQ + i * SLAT + coord] = acc[nt][i];
     }
-    if (RES && (!SPLIT || wv >= 2)) {  // residual column n of step nt: chunk 2nt + n / 8, element n % 8
 #pragma unroll
-      for (int nt = 0; nt < RST; ++nt) {
-        const int coord = CPW * (wv - (4 - NKW)) + 16 * nt + res_coord(rho >> 3, rho & 7);
+    for (int nt = 0; nt < RST; ++nt) {  // residual column n of step nt: chunk 2nt + n / 8, element n % 8
+      const int coord = 32 * wv + 16 * nt + res_coord(rho >> 3, rho & 7);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[2 * SGQ + SGQ * SLAT + i * SD + coord] = accr[nt][i];
-      }
+      for (int i = 0; i < 4; ++i) part[2 * SGQ + SGQ * SLAT + i * SD + coord] = accr[nt][i];
     }
   }
 }
 
-// ---- The role-split form (no positions, no residual): 8 waves, two per SIMD.  Waves 0-3 are key waves and waves
-// 4-7 value waves; key wave w and value wave 4 + w share latent quarter w and, as a workgroup's waves are placed
-// round-robin over the SIMDs, one SIMD.  The one-wave-per-SIMD form above runs a super-tile's vector and matrix work
-// largely one after the other; here a SIMD runs a key wave's matrix chain beside a value wave's vector work.
-// Between the barriers of super-tiles k - 1 and k:
+// ---- The role-split form (all modes but the residual): 8 waves, two per SIMD.  Waves 0-3 are key waves and
+// waves 4-7 value waves; key wave w and value wave 4 + w share latent quarter w and, as a workgroup's waves are
+// placed round-robin over the SIMDs, one SIMD.  The one-wave-per-SIMD layout above runs a super-tile's vector and
+// matrix work largely one after the other; here a SIMD runs a key wave's matrix chain beside a value wave's vector
+// work.  Between the barriers of super-tiles k - 1 and k:
 //   value wave w: stages its quarter's codes and pairs (a four-deep ring of direct-to-LDS copies), dequantizes
 //     super-tile k + 1 into the quarter's fp16 tile, runs the online softmax of super-tile k - 1 from the four
 //     partial scores and its value product on the tile of k - 1, and rotates the query of super-tile k + 2;
 //   key wave w: reads super-tile k's B fragments back from the quarter's tile, up-projects them (W_k's slice in the
 //     accumulator registers), rotates and scores them, and writes its partial scores.
-// The products, their operands and their order are those of decode_shared_kernel, so the output is the same.
+// The products, their operands and their order are those of the one-wave layout, so the output is the same.
 // RoPE on one fp16 pair v = (x, y) with f = (cos, sin), as rope_pair: the same two packed operations and
 // roundings, with f's halves picked by operand selects, so that the compiler keeps one register per factor word
 // instead of hoisting its two swizzled copies (cos, cos) and (sin, sin) out of the loop.
@@ -729,9 +598,19 @@ __host__ __device__ constexpr RoleLds role_lds(bool pos) {
   return L;
 }
 
-// POS: the positions mode of decode_shared_kernel (a compacted cache: slot positions tok_pos, SVAR query variants
-// per super-tile, R(u) of each token's in-block offset u from a table).  Value wave 0 also copies each
-// super-tile's 32 slot positions into a ring that both roles read after the barrier that follows its wait.
+// KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it); a
+// super-tile whose tokens are all evicted is skipped by the key waves and adds nothing in the value waves.
+// SPLIT: latent coordinates below SLAT / 2 feed only the keys and the rest only the values (W_k zero on the upper
+// rows, W_v on the lower, as for keys and values with their own token factors): key waves 2-3 and the value
+// products of value waves 0-1 are skipped; those products are exact zeros, so the output is the same.
+// KB: latent code bits (4; or 3 and 2, whose codes a value wave stages token-major and spreads to the INT4 nibble
+// layout).
+// POS: a compacted cache whose slots hold tokens at the source positions tok_pos (no keep mask).  A super-tile's
+// tokens lie within SVAR blocks of 32 positions from its first slot's block `base` (the layout the compaction
+// writes): a token at position 32 (base + v) + u is rotated by R(u), from a table, and scored against the query
+// rotated by R(q_pos - 32 (base + v)), one of SVAR variants in the score operand's rows; other slots take no part.
+// Value wave 0 also copies each super-tile's 32 slot positions into a ring that both roles read after the barrier
+// that follows its wait.
 template <bool KEEP, bool SPLIT, int KB, bool POS>
 __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeSharedArgs a) {
   constexpr int CB = SLAT * KB / 8;  // code bytes per token
@@ -783,7 +662,7 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
 
   if (keyw) {
     // ---- W_k[l]'s slice of this quarter as A fragments in the accumulator registers (the layout of
-    // decode_shared_kernel: block g row t <-> head dim t < 16 ? 16g + t : 64 + 16g + t - 16; step j k-slot 8hf + e
+    // decode_shared_res_kernel: block g row t <-> head dim t < 16 ? 16g + t : 64 + 16g + t - 16; step j k-slot 8hf + e
     // <-> latent coordinate 128w + 8 (8hf + j) + perm8(e))
     h8 wf[SNB][SNJ];
     if (!SPLIT || wq < 2) {
@@ -923,7 +802,7 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
   }
   const uint32_t posr_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem + LY.posr));
 
-  // staging of this quarter of super-tile k into ring slot k % 4, as in decode_shared_kernel (past the last
+  // staging of this quarter of super-tile k into ring slot k % 4, as in decode_shared_res_kernel (past the last
   // super-tile the slot gets a copy of the last one; always four copy instructions, and value wave 0 of the
   // positions mode a fifth: the 32 slot positions into ring slot k % 8)
   auto issue = [&](int k) {
@@ -1055,7 +934,7 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
     }
     if (hf == 0) *(h4*)(pt + SGQ * t) = h4{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     wave_lds_sync();
-    // the value product as in decode_shared_kernel (P as the A operand of 16x16x32 products, the tile's chunks
+    // the value product as in decode_shared_res_kernel (P as the A operand of 16x16x32 products, the tile's chunks
     // read transposed as the B operand)
     if ((!SPLIT || wq >= 2) && !empty) {
       const h8 pop = lds_tr8s(pt + SGQ * (8 * grp + (rho >> 2)), pt + SGQ * (8 * grp + 4 + (rho >> 2)));
@@ -1195,13 +1074,13 @@ size_t shared_ws_bytes(const kvc_layout& L, int B, int n_splits) {
   return (size_t)L.n_layers * L.n_kv_heads * B * n_splits * shared_part_stride(L) * sizeof(float);
 }
 
-template <bool KEEP, bool SPLIT, int KB, bool POS, bool RES = false>
-static hipError_t launch_shared_one(int grid, hipStream_t st, const DecodeSharedArgs& a) {
-  const void* kern = (const void*)decode_shared_kernel<KEEP, SPLIT, KB, POS, RES>;
-  const int lds = shared_lds(POS, RES).total;
+static hipError_t launch_shared_res(int grid, hipStream_t st, const DecodeSharedArgs& a) {
+  const void* kern = (const void*)decode_shared_res_kernel;
+  constexpr int lds = shared_lds().total;
+  static_assert(lds <= 160 * 1024, "LDS of the residual-mode kernel");
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_shared_kernel<KEEP, SPLIT, KB, POS, RES>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(decode_shared_res_kernel, dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1229,7 +1108,7 @@ static hipError_t launch_shared_variant(bool keep, bool pos, bool res, bool spli
                                         const DecodeSharedArgs& a) {
   // the residual mode runs the plain-latent form also for a split latent: the products it then makes are exact
   // zeros, and the output is the full product's
-  if (res) return launch_shared_one<false, false, 4, false, true>(grid, st, a);
+  if (res) return launch_shared_res(grid, st, a);
   if (pos) return split ? launch_role_bits<false, true, true>(kb, grid, st, a) : launch_role_bits<false, false, true>(kb, grid, st, a);
   if (keep) return split ? launch_role_bits<true, true, false>(kb, grid, st, a) : launch_role_bits<true, false, false>(kb, grid, st, a);
   return split ? launch_role_bits<false, true, false>(kb, grid, st, a) : launch_role_bits<false, false, false>(kb, grid, st, a);
