@@ -48,7 +48,7 @@ static constexpr int SNB = SD / 32;     // 32-dim blocks of the head
 static constexpr float STAU = 8.0f;     // lazy-max slack, log2 units
 static constexpr int SRAW = 2048 + 512; // ring slot: a wave's codes of 32 tokens, then its pairs (two copies)
 static constexpr int SVAR = 4;          // positions mode: query bases per super-tile (blocks of 32 positions)
-static constexpr int SRT = 36;          // positions mode: dwords per row of the RoPE factor table (32 + padding)
+static constexpr int RT16 = 20;         // positions mode: dwords per row of the role kernel's RoPE factor table
 static constexpr int SRR = 2048 + 128;  // residual mode: a super-tile's K and V residual codes, then their scales
 static constexpr int SRRN = 6;          // residual mode: super-tiles in the shared residual ring
 static constexpr int SRCS = 32 * 16 + 64;  // residual mode: bytes per chunk row of a value-residual tile (padded)
@@ -592,12 +592,19 @@ __host__ __device__ constexpr RoleLds role_lds(bool pos) {
   L.pt = o; o += 4 * 32 * SGQ * 2;                     // probabilities [value wave][token][head] fp16
   L.addr = o; o += SMAX_TILES * 8;                     // page record address of each super-tile
   L.keep = o; o += SMAX_TILES * 4;                     // keep-mask word (positions mode: base block) of each
-  L.rtab = o; o += pos ? 64 * SRT * 4 : 0;             // positions mode: RoPE factors [half][offset u][32]
+  L.rtab = o; o += pos ? 4 * 32 * RT16 * 4 : 0;       // positions mode: RoPE factors [group][offset u][16]
   L.posr = o; o += pos ? 8 * 32 * 4 : 0;               // positions mode: slot positions of super-tile k at k % 8
   L.total = o;
   return L;
 }
 
+// fragment order of the rotated query for the role-split kernel's 16x16x32 score products: element e of (head, tile
+// pair m, lane group g) is head dim 16m + 4g + e/2 + 64 (e % 2), the k-slot order of the rotated keys of tiles m and
+// m + 4; heads SQB elements apart
+__device__ inline int qfrag16_index(int head, int dim) {
+  const int xy = dim >> 6, r = dim & 63, m = r >> 4, g = (r >> 2) & 3, i = r & 3;
+  return head * SQB + (m * 4 + g) * 8 + 2 * i + xy;
+}
 // KEEP: a token keep mask is applied (a separate instantiation, so that the unmasked kernel carries none of it); a
 // super-tile whose tokens are all evicted is skipped by the key waves and adds nothing in the value waves.
 // SPLIT: latent coordinates below SLAT / 2 feed only the keys and the rest only the values (W_k zero on the upper
@@ -661,106 +668,136 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
   __syncthreads();
 
   if (keyw) {
-    // ---- W_k[l]'s slice of this quarter as A fragments in the accumulator registers (the layout of
-    // decode_shared_res_kernel: block g row t <-> head dim t < 16 ? 16g + t : 64 + 16g + t - 16; step j k-slot 8hf + e
-    // <-> latent coordinate 128w + 8 (8hf + j) + perm8(e))
-    h8 wf[SNB][SNJ];
+    // ---- W_k[l]'s slice of this quarter as A fragments of v_mfma_f32_16x16x32_f16 in the accumulator registers:
+    // row tile m (16 head dims: 16m + r for m < 4, 64 + 16(m - 4) + r above, so that tiles m and m + 4 hold the RoPE
+    // pairs (j, j + 64)), row r = lane % 16; k-step s, k-slot 8 grp + e <-> latent coordinate
+    // 128w + 8 (4s + grp) + perm8(e), i.e. element e of code dword 4s + grp of the quarter (the order a code dword
+    // dequantizes)
+    h8 wf[2 * SNB][SNJ / 2];
     if (!SPLIT || wq < 2) {
       const int width = a.Hkv * SD;
       const uint16_t* W = a.wk + (size_t)b * a.w_stride + (size_t)l * SLAT * width + (size_t)h * SD;
 #pragma unroll
-      for (int g = 0; g < SNB; ++g) {
-        const int dim = t < 16 ? 16 * g + t : 64 + 16 * g + (t - 16);
+      for (int m = 0; m < 2 * SNB; ++m) {
+        const int dim = m < SNB ? 16 * m + rho : 64 + 16 * (m - SNB) + rho;
 #pragma unroll
-        for (int j = 0; j < SNJ; ++j) {
+        for (int s = 0; s < SNJ / 2; ++s) {
           h8 f;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            f[e] = bf16_to_h(W[(size_t)(SQC * wq + 8 * (8 * hf + j) + perm8(e)) * width + dim]);
-          asm volatile("" : "=a"(wf[g][j]) : "0"(f));
+            f[e] = bf16_to_h(W[(size_t)(SQC * wq + 8 * (4 * s + grp) + perm8(e)) * width + dim]);
+          asm volatile("" : "=a"(wf[m][s]) : "0"(f));
         }
       }
     }
-    // RoPE factors of this lane's slot t: block g's up-projection entry i is row 8(i/4) + 4hf + i%4, paired with
-    // entry i + 8; frequency 16g + that row.  Positions mode: a table of the factors of every in-block offset u,
-    // laid out as a lane of half hh takes them, read per super-tile at the token's own u.
-    uint32_t rf[SNB][8];
+    // RoPE factors of this lane's two tokens 16 n + rho: tile pair m's output entry i (0..3) is head dims
+    // 16m + 4 grp + i and + 64, frequency 16m + 4 grp + i; |u theta| < 32 turns, where v_sin / v_cos are accurate.
+    // Positions mode: a table of the factors of every in-block offset u as a lane of group gg takes them
+    // ([gg][u], rows of RT16 dwords), read per super-tile at the tokens' own offsets.
+    uint32_t rf[2][SNB * 4];
     uint32_t* rtab = (uint32_t*)(smem + LY.rtab);
     if (POS) {
-      for (int e = tid; e < 64 * 32; e += 256) {
-        const int u = e >> 6, hh = (e >> 5) & 1, g = (e >> 3) & 3, i = e & 7;
-        const float rev = (float)(u * tturn[16 * g + 8 * (i >> 2) + 4 * hh + (i & 3)]);
-        rtab[(32 * hh + u) * SRT + 8 * g + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+      for (int e = tid; e < 4 * 32 * 16; e += 256) {
+        const int gg = e >> 9, u = (e >> 4) & 31, m = (e >> 2) & 3, i = e & 3;
+        const float rev = (float)(u * tturn[16 * m + 4 * gg + i]);
+        rtab[(32 * gg + u) * RT16 + 4 * m + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
       }
     } else {
 #pragma unroll
-      for (int g = 0; g < SNB; ++g)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float rev = (float)(t * tturn[16 * g + 8 * (i >> 2) + 4 * hf + (i & 3)]);
-          rf[g][i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-        }
+        for (int m = 0; m < SNB; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float rev = (float)((16 * n + rho) * tturn[16 * m + 4 * grp + i]);
+            rf[n][4 * m + i] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+          }
     }
-    lds_barrier();  // the value waves' prologue: the tile of super-tile 0, the rotated queries of 0 and 1
+    lds_barrier();  // the value waves' prologue: the tile of super-tile 0, the rotated queries of 0 and 1; the table
     for (int k = 0; k < n_tiles; ++k) {
       const bool empty = KEEP && __builtin_amdgcn_readfirstlane(tkeep[k]) == 0u;
-      // positions mode: the token's block offset v from the super-tile's base picks its query variant, its
-      // in-block offset u its RoPE factors (slots of -1 or outside the SVAR blocks take no part)
-      int vsel = 0;
+      // positions mode: a token's block offset v from the super-tile's base picks its query variant, its in-block
+      // offset u its RoPE factors (slots of -1 or outside the SVAR blocks take no part)
+      int vsel[2] = {0, 0};
       if constexpr (POS) {
-        const int pc = posr[(k & 7) * 32 + t];
-        const int v = (pc >> 5) - (int)tkeep[k];
-        vsel = pc >= 0 && v >= 0 && v < SVAR ? v : 0;
-        const u32x4_t* src = (const u32x4_t*)(rtab + (32 * hf + (pc & 31)) * SRT);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x4_t x = src[j];
+        for (int n = 0; n < 2; ++n) {
+          const int pc = posr[(k & 7) * 32 + 16 * n + rho];
+          const int v = (pc >> 5) - (int)tkeep[k];
+          vsel[n] = pc >= 0 && v >= 0 && v < SVAR ? v : 0;
+          const u32x4_t* src = (const u32x4_t*)(rtab + (32 * grp + (pc & 31)) * RT16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rf[j >> 1][4 * (j & 1) + e] = x[e];
+          for (int m = 0; m < SNB; ++m) {
+            const u32x4_t x = src[m];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rf[n][4 * m + i] = x[i];
+          }
         }
       }
-      f16v_t sc = {};
+      f4 sc[2] = {};  // scores of tokens 16 n + rho: rows 4 grp + i <-> head i (positions mode: of variant grp)
       if ((!SPLIT || wq < 2) && !empty) {
-        const uint8_t* tl = vt_q + (k & 1) * SVT + SCS * 8 * hf + 16 * t;
-        h8 bc[SNJ];
+        // B fragments: k-step s, token half n: chunk 4s + grp of token 16 n + rho
+        const uint8_t* tl = vt_q + (k & 1) * SVT + SCS * grp + 16 * rho;
+        h8 bc[SNJ / 2][2];
 #pragma unroll
-        for (int j = 0; j < SNJ; ++j) bc[j] = *(const h8*)(tl + SCS * j);
-        // score operand row t: query head t % 4 (positions mode: of variant (t / 4) % SVAR)
-        const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? (t >> 2) & (SVAR - 1) : 0)) * SGQ * SQB +
-                                   (t & 3) * SQB) + hf;
-        // block g's chain, then block g - 1's RoPE and score products, interleaved with it by the scheduling groups
-        // below (one matrix instruction, then up to three vector ones), so that a block's vector work runs under
-        // the next block's matrix chain
-        f16v_t kp[SNB];
+        for (int s = 0; s < SNJ / 2; ++s)
 #pragma unroll
-        for (int g = 0; g <= SNB; ++g) {
-          if (g < SNB) {
-            kp[g] = f16v_t{};
+          for (int n = 0; n < 2; ++n) bc[s][n] = *(const h8*)(tl + SCS * 4 * s + 256 * n);
+        // score A operand: row rho <-> head rho % 4 (positions mode: of variant rho / 4), the k-slots of lane group
+        // grp for tile pair m at fragment 4m + grp
+        const h8* qf = (const h8*)(qts + ((k % 3) * (POS ? SVAR : 1) + (POS ? rho >> 2 : 0)) * SGQ * SQB +
+                                   (rho & 3) * SQB) + grp;
+        // tile pair m (head dims of tiles m and m + 4; four independent accumulator chains), then tile pair m - 1's
+        // RoPE and score products, so that one pair's vector work goes under the next pair's matrix instructions
+        f4 kx[SNB][2], ky[SNB][2];
 #pragma unroll
-            for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
+        for (int m = 0; m <= SNB; ++m) {
+          if (m < SNB) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              kx[m][n] = f4{0, 0, 0, 0};
+              ky[m][n] = f4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int s = 0; s < SNJ / 2; ++s)
+#pragma unroll
+              for (int n = 0; n < 2; ++n) {
+                kx[m][n] = mfma16x16x32(wf[m][s], bc[s][n], kx[m][n]);
+                ky[m][n] = mfma16x16x32(wf[m + SNB][s], bc[s][n], ky[m][n]);
+              }
           }
-          if (g > 0) {
-            u32x4_t kr[2];
+          if (m > 0) {
+            const h8 qa = qf[4 * (m - 1)];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kr[i >> 2][i & 3] = rope_pair_sel(pack_h2(kp[g - 1][i], kp[g - 1][i + 8]), rf[g - 1][i]);
-            sc = mfma32s(qf[4 * (g - 1)], __builtin_bit_cast(h8, kr[0]), sc);
-            sc = mfma32s(qf[4 * (g - 1) + 2], __builtin_bit_cast(h8, kr[1]), sc);
+            for (int n = 0; n < 2; ++n) {
+              u32x4_t kr;  // k-slots 8 grp + 2i, + 1 <-> the rotated pair (x, y) of head dims 16(m-1) + 4 grp + i, + 64
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                kr[i] = rope_pair_sel(pack_h2(kx[m - 1][n][i], ky[m - 1][n][i]), rf[n][4 * (m - 1) + i]);
+              sc[n] = mfma16x16x32(qa, __builtin_bit_cast(h8, kr), sc[n]);
+            }
           }
         }
+        // a split latent leaves key waves 0-1 beside value waves that make no value product: there one matrix
+        // instruction, then up to two vector ones, measured faster (515 against 551 us on the Tucker group); with
+        // every wave busy the compiler's own order is (614 against 648 us on the block-shared 32K step)
+        if constexpr (SPLIT) {
 #pragma unroll
-        for (int g = 0; g < SNB; ++g) {
+          for (int m = 0; m < SNB; ++m) {
 #pragma unroll
-          for (int j = 0; j < SNJ; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            for (int j = 0; j < 16; ++j) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
-      // row 8 (j / 4) + 4 hf + j % 4 of entry j: this lane half holds variants hf (entries 0-3) and 2 + hf (4-7)
-      if (POS ? hf == (vsel & 1) : hf == 0)
-        *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + t) * SGQ) =
-            (POS && (vsel >> 1)) ? f4{sc[4], sc[5], sc[6], sc[7]} : f4{sc[0], sc[1], sc[2], sc[3]};
+      // lane group 0 holds the four heads of its tokens (positions mode: group vsel, the token's variant)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        if (POS ? grp == vsel[n] : grp == 0)
+          *(f4*)(sp + (k & 1) * (4 * 32 * SGQ) + (wq * 32 + 16 * n + rho) * SGQ) = sc[n];
       lds_barrier();
     }
     return;
@@ -787,7 +824,7 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
       qy = q[qj + SD / 2] * sc;
     }
   }
-  const int qix = qfrag_index(wq, qj);
+  const int qix = qfrag16_index(wq, qj);
   const double fq = tturn[qj];
   // positions mode: this thread's query pair rotated on from variant 0 to variant v by R(-32 v theta), v < SVAR
   float vc[SVAR], vs[SVAR];
