@@ -29,7 +29,8 @@
 // Two kernels use this layout: decode_shared_role_kernel (further below: 8 waves, key waves and value waves on
 // each SIMD) serves the plain, keep-mask, split-latent and positions modes at every code width;
 // decode_shared_res_kernel (one wave per SIMD, as described above) the residual mode, whose residual operands do
-// not fit the registers of the role split.  Their common products, operands and order are the same.
+// not fit the registers of the role split.  The role split's key waves use 16x16x32 products instead of the
+// 32x32x16 ones above (the same sums in another order).
 #include <math.h>
 
 #include <algorithm>
@@ -563,8 +564,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedA
 //     super-tile k + 1 into the quarter's fp16 tile, runs the online softmax of super-tile k - 1 from the four
 //     partial scores and its value product on the tile of k - 1, and rotates the query of super-tile k + 2;
 //   key wave w: reads super-tile k's B fragments back from the quarter's tile, up-projects them (W_k's slice in the
-//     accumulator registers), rotates and scores them, and writes its partial scores.
-// The products, their operands and their order are those of the one-wave layout, so the output is the same.
+//     accumulator registers) on v_mfma_f32_16x16x32_f16, rotates and scores them, and writes its partial scores.
 // RoPE on one fp16 pair v = (x, y) with f = (cos, sin), as rope_pair: the same two packed operations and
 // roundings, with f's halves picked by operand selects, so that the compiler keeps one register per factor word
 // instead of hoisting its two swizzled copies (cos, cos) and (sin, sin) out of the loop.
