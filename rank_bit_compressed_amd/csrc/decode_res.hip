@@ -146,8 +146,10 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
     }
   }
   // ---- +-1 Hadamard fragments of the fp8 key residual product: head-dim tile mt (row r = t <-> dim 32 mt + r),
-  // coordinate block be; byte b of this lane's 32 <-> coordinate 64 be + res8_coord(hf, b); e4m3 +1 = 0x38,
-  // -1 = 0xB8.  The A and B operands share the lane/byte -> k assignment, so the pairing holds whatever it is.
+  // product be; byte b of this lane's 32 <-> coordinate 64 hf + 32 be + res8_coord(0, b) (a lane half reads its
+  // token's residual code dwords 4hf..4hf+3 in one 16-byte read, and product be takes dwords 2be, 2be + 1 of them);
+  // e4m3 +1 = 0x38, -1 = 0xB8.  The A and B operands share the lane/byte -> k assignment, so the pairing holds
+  // whatever it is.
   v8i_t hf8[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
         uint32_t w = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = 64 * be + res8_coord(hf, 4 * o + q);
+          const int i = 64 * hf + 32 * be + res8_coord(0, 4 * o + q);
           w |= ((__builtin_popcount((32 * mt + t) & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
         }
         hf8[mt][be][o] = (int)w;
@@ -280,44 +282,55 @@ __global__ __launch_bounds__(256, 1) void decode_res_kernel(ResArgs a) {
       const int t0 = page_t0 + 32 * (wv + 4 * k);
       const uint32_t* qrow = qbuf + (k * GQ + (t & 3)) * (NP + 4) + 4 * hf;
 
-      // ---- this lane's words: key and value code dwords (2s + hf) with their pairs, residual code dwords (32
-      // bytes per token; dword j holds the codes of coordinates 16j ..), residual scales
-      uint32_t kw[KS], kp[KS], vw[VS], vp[VS], krw[4], vrw[8];
+      // ---- this lane's key words: key code dwords (2s + hf) with their pairs, its half's residual code dwords
+      // 4hf..4hf+3 (32 bytes per token; dword j holds the codes of coordinates 16j ..), residual scales
+      uint32_t kw[KS], kp[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         kw[s] = *(const uint32_t*)(sb + S.kc + slot * kcb + 8 * s + 4 * hf);
         kp[s] = *(const uint32_t*)(sb + S.km + slot * kmb + 4 * ((16 * s + 8 * hf) / a.G));
       }
-#pragma unroll
-      for (int s = 0; s < VS; ++s) {
-        vw[s] = *(const uint32_t*)(sb + S.vc + slot * vcb + 8 * s + 4 * hf);
-        vp[s] = *(const uint32_t*)(sb + S.vm + slot * vmb + 4 * ((16 * s + 8 * hf) / a.G));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vrw[j] = *(const uint32_t*)(sb + S.vr + 32 * slot + 4 * j);
-#pragma unroll
-      for (int be = 0; be < 2; ++be)  // key residual dwords 4 be + 2hf, + 1 (this lane half's codes of block be)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(sb + S.kr + 32 * slot + 4 * (4 * be + 2 * hf + i));
+      const u4 krw = *(const u4*)(sb + S.kr + 32 * slot + 16 * hf);
       // key residual: K_res = (s / sqrt(128)) (H' c - 1.5 H' 1); value residual: (2c - 3) s / (2 sqrt(128))
       const float ks = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.ks + 2 * slot)) * (2.0f * rscale);
       const float vs = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(sb + S.vs + 2 * slot)) * rscale;
 
-      // ---- values into this wave's fp16 tiles (chunk c of token t at byte CS c + 16 t): latent chunks 2s + hf,
-      // residual 2c - 3 of chunk 2j + hf (coordinates 16j + res_coord(hf, e))
+      // ---- values into this wave's fp16 tiles (chunk c of token t at byte CS c + 16 t): chunk c of the latent is
+      // code dword c (pair of coordinate 8c), the residual's chunks 2j, 2j + 1 come from its code dword j
+      // (coordinates 16j + res_coord(e, ...), e = 0, 1).  Lane half hf takes the latent's dwords VS hf.. and the
+      // residual's dwords 4hf..4hf+3 of its token, each in one wide read: a lane octet's reads, 32 bytes apart, meet
+      // two to a bank, where four-byte reads of the 32-byte token rows met eight to a bank.
+      {
+        uint32_t vq[VS];
+        if constexpr (VS == 4) {
+          const u4 x = *(const u4*)(sb + S.vc + slot * vcb + 16 * hf);
 #pragma unroll
-      for (int s = 0; s < VS; ++s)
-        *(h8*)(vlat + CS * (2 * s + hf) + 16 * t) = dequant_int4x8(vw[s], vp[s]);
+          for (int i = 0; i < 4; ++i) vq[i] = x[i];
+        } else {
+          static_assert(VS == 2, "value steps");
+          const u2 x = *(const u2*)(sb + S.vc + slot * vcb + 8 * hf);
+          vq[0] = x[0];
+          vq[1] = x[1];
+        }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *(h8*)(vres + CS * (2 * j + hf) + 16 * t) = res_2c3(vrw[j], hf);
+        for (int i = 0; i < VS; ++i) {
+          const int c = VS * hf + i;  // chunk = code dword of the token
+          const uint32_t pr = *(const uint32_t*)(sb + S.vm + slot * vmb + 4 * ((8 * c) / a.G));
+          *(h8*)(vlat + CS * c + 16 * t) = dequant_int4x8(vq[i], pr);
+        }
+        const u4 rq = *(const u4*)(sb + S.vr + 32 * slot + 16 * hf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *(h8*)(vres + CS * (8 * hf + i) + 16 * t) = res_2c3(rq[i >> 1], i & 1);
+      }
 
       // ---- keys: latent and residual operands, then per half m the tiles m and m + 2 (head dims d, d + 64),
       // RoPE, and the score steps u = 4m + q (pairs 32m + 8q + 4hf + p in k-slots 8hf + 2p, 8hf + 2p + 1)
       h8 kb[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) kb[s] = dequant_int4x8(kw[s], kp[s]);
-      // key residual codes one per byte (fp8 B operands of blocks 0 and 1): byte q of dword o = code m + 4q of
-      // source dword o / 4, m = o % 4
+      // key residual codes one per byte (fp8 B operands of products 0 and 1): byte q of dword o = code m + 4q of
+      // the lane's code dword 2be + o / 4, m = o % 4
       v8i_t er[2];
 #pragma unroll
       for (int be = 0; be < 2; ++be)

@@ -21,6 +21,11 @@ CASES = [
     ("varrank_paged_32k", dict(B=2, T=300, page_size=32), [300, 17]),
     ("residual_128k", dict(B=2, T=700), [700, 512]),
     ("residual_128k", dict(B=3, T=1500, page_size=64), [1500, 1025, 31]),
+    # the residual kernel's other rank variants: 4 key and value steps; 2 of each (half-width value code reads),
+    # groups of 16 (a pair word per chunk)
+    ("residual_128k", dict(B=2, T=700, r_k=64, r_v=64, page_size=128), [700, 255]),
+    ("residual_128k", dict(B=2, T=600, r_k=32, r_v=32, page_size=128), [600, 129]),
+    ("residual_128k", dict(B=2, T=500, r_k=48, r_v=64, group=16, page_size=128), [500, 33]),
     # ranks that are not multiples of 16: the general per-head kernel's residual path
     ("residual_128k", dict(B=2, T=700, r_k=40, r_v=56), [700, 300]),
     ("shared_latent_32k", dict(B=2, T=600), [600, 33]),
