@@ -169,8 +169,9 @@ __global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedA
     }
   }
   // +-1 Hadamard rows of this wave's head-dim block (block w) as fp8 A fragments (row t <-> the block's head dim,
-  // byte b of lane half hf's 32 of block-half be <-> coordinate 64 be + res8_coord(hf, b); e4m3 +1 = 0x38,
-  // -1 = 0xB8), kept in the accumulator registers the fp8 products read directly
+  // byte b of lane half hf's 32 of product be <-> coordinate 64 hf + 32 be + res8_coord(0, b): a lane half reads
+  // its token's residual code dwords 4hf..4hf+3 with one 16-byte read, and product be takes dwords 2be, 2be + 1 of
+  // them; e4m3 +1 = 0x38, -1 = 0xB8), kept in the accumulator registers the fp8 products read directly
   v8i_t hr[2];
   {
     const int dim = t < 16 ? 16 * wv + t : 64 + 16 * wv + (t - 16);
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedA
         uint32_t w = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int i = 64 * be + res8_coord(hf, 4 * o + q);
+          const int i = 64 * hf + 32 * be + res8_coord(0, 4 * o + q);
           w |= ((__builtin_popcount(dim & i) & 1) ? 0xB8u : 0x38u) << (8 * q);
         }
         hr[be][o] = (int)w;
@@ -377,11 +378,9 @@ __global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedA
 #pragma unroll
         for (int j = 0; j < SNJ; ++j) kp[g] = mfma32s(wf[g][j], bc[j], kp[g]);
         if (g == wv) {  // H' c of this wave's block (exact integers)
-          uint32_t krw[4];
-#pragma unroll
-          for (int be = 0; be < 2; ++be)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) krw[2 * be + i] = *(const uint32_t*)(rrk + 32 * t + 4 * (4 * be + 2 * hf + i));
+          // (one 16-byte read of the half's code dwords; four-byte reads of the 32-byte token rows met eight lanes
+          // to a bank)
+          const u4 krw = *(const u4*)(rrk + 32 * t + 16 * hf);
           ksc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rrk + 2048 + 2 * t)) * (2.0f * RSCALE);
           v8i_t er[2];  // the codes one per byte (the fp8 B operands): byte q of dword o = code m + 4q, m = o % 4
 #pragma unroll
@@ -469,10 +468,10 @@ __global__ __launch_bounds__(256, 1) void decode_shared_res_kernel(DecodeSharedA
     // 32 w + 16 jj + res_coord(hf, e)), and p times the token's value scale / (2 sqrt(128))
     {
       const uint8_t* rr = rres + (k % SRRN) * SRR;
+      static_assert(RST == 2, "the wave's two residual code dwords in one read");
+      const u2 rw = *(const u2*)(rr + 1024 + 32 * t + 8 * wv);
 #pragma unroll
-      for (int jj = 0; jj < RST; ++jj)
-        *(h8*)(vr_w + SRCS * (2 * jj + hf) + 16 * t) =
-            res_2c3(*(const uint32_t*)(rr + 1024 + 32 * t + 4 * (RST * wv + jj)), hf);
+      for (int jj = 0; jj < RST; ++jj) *(h8*)(vr_w + SRCS * (2 * jj + hf) + 16 * t) = res_2c3(rw[jj], hf);
       const float vsc = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)(rr + 2048 + 64 + 2 * t)) * RSCALE;
       if (hf == 0)
         *(h4*)(pt2 + SGQ * t) = h4{(_Float16)(p[0] * vsc), (_Float16)(p[1] * vsc), (_Float16)(p[2] * vsc),
