@@ -1045,54 +1045,78 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
 
 // out[l][b][h*4 + hq] = (W_v[l][:, h*128 : (h+1)*128]^T c* + H' r*) / l*, over the splits' partials (r*: the
 // rotated value residual of the residual mode, H' the +-1 Hadamard; its accumulators carry 1 / sqrt(128)): one
-// workgroup per (layer, sequence, query head), thread d computes output dim d (W_v rows read coalesced across the
-// threads, eight independent partial sums).
-__global__ __launch_bounds__(SD) void merge_shared_kernel(const float* ws, const uint16_t* wv, int64_t w_stride,
+// workgroup of 256 threads per (layer, sequence, query head).  The splits' (m, l, acc) are combined into c* (two
+// latent coordinates per thread); then thread t takes head dims 8 (t % 16) .. + 7 and latent rows 32 (t / 16) .. + 31,
+// reading each W_v row segment with one 16-byte load (all of them in flight together; one W_v element per thread and
+// row left this kernel waiting on 64 rounds of loads), and the 16 row groups' partial sums are added in LDS in a
+// fixed order.
+__global__ __launch_bounds__(256) void merge_shared_kernel(const float* ws, const uint16_t* wv, int64_t w_stride,
                                                           float* out, int B, int Hkv, int Hq, int n_splits,
                                                           int part_stride, int c_begin, int res) {
+  constexpr int RG = 16, RPG = SLAT / RG;  // row groups, rows per group
+  static_assert(SLAT == 2 * 256 && SD == 8 * 16, "thread mapping");
   __shared__ float cst[SLAT];
   __shared__ float rst[SD];
   __shared__ float lst;
+  __shared__ float red[RG][SD + 4];
   int id = blockIdx.x;
   const int hq_all = id % Hq; id /= Hq;
   const int b = id % B;
   const int l = id / B;
   const int h = hq_all / SGQ, hq = hq_all % SGQ;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const float* parts = ws + (((size_t)l * Hkv + h) * B + b) * n_splits * part_stride;
   float m = -INFINITY;
   for (int p = 0; p < n_splits; ++p) m = fmaxf(m, parts[(size_t)p * part_stride + hq]);
-  float lsum = 0.0f, c[SLAT / SD], r = 0.0f;
-#pragma unroll
-  for (int k = 0; k < SLAT / SD; ++k) c[k] = 0.0f;
+  float lsum = 0.0f, c0 = 0.0f, c1 = 0.0f, r = 0.0f;
+#pragma unroll 4
   for (int p = 0; p < n_splits; ++p) {
     const float* pp = parts + (size_t)p * part_stride;
     const float mp = pp[hq];
     const float w = mp == -INFINITY ? 0.0f : exp2f(mp - m);
     lsum += w * pp[SGQ + hq];
-#pragma unroll
-    for (int k = 0; k < SLAT / SD; ++k) c[k] += w * pp[2 * SGQ + hq * SLAT + d + SD * k];
-    if (res) r += w * pp[2 * SGQ + SGQ * SLAT + hq * SD + d];
+    c0 += w * pp[2 * SGQ + hq * SLAT + tid];
+    c1 += w * pp[2 * SGQ + hq * SLAT + tid + 256];
+    if (res && tid < SD) r += w * pp[2 * SGQ + SGQ * SLAT + hq * SD + tid];
   }
-#pragma unroll
-  for (int k = 0; k < SLAT / SD; ++k) cst[d + SD * k] = c[k];
-  rst[d] = r;
-  if (d == 0) lst = lsum;
+  cst[tid] = c0;
+  cst[tid + 256] = c1;
+  if (tid < SD) rst[tid] = r;
+  if (tid == 0) lst = lsum;
   __syncthreads();
+  const int cg = tid % 16, rg = tid / 16;
   const size_t width = (size_t)Hkv * SD;
-  const uint16_t* W = wv + (size_t)b * w_stride + (size_t)l * SLAT * width + (size_t)h * SD + d;
+  const uint16_t* W = wv + (size_t)b * w_stride + (size_t)l * SLAT * width + (size_t)h * SD + 8 * cg;
   float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = c_begin; i < SLAT; i += 8) {  // (a split latent: W_v is zero below c_begin)
+  if (RPG * (rg + 1) > c_begin) {  // (a split latent: W_v is zero below c_begin, a multiple of RPG)
+    u4 wr[RPG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] += __builtin_bit_cast(float, (uint32_t)W[(size_t)(i + e) * width] << 16) * cst[i + e];
+    for (int i = 0; i < RPG; ++i) wr[i] = *(const u4*)(W + (size_t)(RPG * rg + i) * width);
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const float cv = cst[RPG * rg + i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w2 = wr[i][e >> 1];
+        o[e] += __builtin_bit_cast(float, (e & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16)) * cv;
+      }
+    }
   }
-  float sum = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
-  if (res) {
-    float rr = 0.0f;
-    for (int i = 0; i < SD; ++i) rr += (__builtin_popcount(d & i) & 1) ? -rst[i] : rst[i];
-    sum += rr;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][8 * cg + e] = o[e];
+  __syncthreads();
+  if (tid < SD) {
+    const int d = tid;
+    float sum = 0.0f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) sum += red[g][d];
+    if (res) {
+      float rr = 0.0f;
+      for (int i = 0; i < SD; ++i) rr += (__builtin_popcount(d & i) & 1) ? -rst[i] : rst[i];
+      sum += rr;
+    }
+    out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = lst > 0.0f ? sum / lst : 0.0f;  // zero: no token kept
   }
-  out[(((size_t)l * B + b) * Hq + hq_all) * SD + d] = lst > 0.0f ? sum / lst : 0.0f;  // zero: no token kept
 }
 
 int shared_max_tiles_per_split() { return SMAX_TILES; }
@@ -1171,7 +1195,7 @@ hipError_t launch_decode_shared(const kvc_layout& L, const kvc_cache& C, const k
                             st, a);
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(SD), 0, st, a.ws, in.wv,
+  hipLaunchKernelGGL(merge_shared_kernel, dim3(L.n_layers * in.B * L.n_q_heads), dim3(256), 0, st, a.ws, in.wv,
                      in.w_seq_stride, out, in.B, L.n_kv_heads, L.n_q_heads, n_splits, a.part_stride,
                      split ? SLAT / 2 : 0, L.residual_bits != 0);
   return hipGetLastError();
