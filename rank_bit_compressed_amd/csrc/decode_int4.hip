@@ -603,28 +603,32 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   }
 }
 
-// Final combine over the context splits and the value basis: one workgroup per (sequence, query head),
-// thread d computes out[d] = (B_v c*)[d] / l* with c* = sum_s 2^(m_s - m*) acc_s, l* = sum_s 2^(m_s - m*) l_s.
-// The kernel is a chain of memory round trips, so its loads are issued together: the value basis row at the
-// start, then every split's (m, l, acc) in groups of up to 16, combined with a running maximum (the same
-// value as a maximum taken first, up to rounding).
+// Final combine over the context splits and the value basis: one workgroup of 256 threads per (sequence, KV head).
+// Thread (hq, c) = (t / NC, t % NC) combines c*[hq][c] = sum_s 2^(m_s - m*) acc_s and l*[hq] = sum_s 2^(m_s - m*) l_s
+// over the splits; thread t then computes out[d] = (B_v c*)[d] / l* for d = t % 128 and the query heads 2 (t / 128)
+// and 2 (t / 128) + 1, with the basis row d loaded once for both.  The kernel is a chain of memory round trips, so
+// its loads are issued together: the value basis row at the start, then every split's (m, l, acc) in groups of up to
+// 16, combined with a running maximum (the same value as a maximum taken first, up to rounding).  The four query
+// heads of a KV head share one workgroup, so the basis rows are read once per KV head.
 template <int NC>
-__global__ __launch_bounds__(128) void merge_int4_kernel(const float* ws, const uint16_t* wv, float* out, int Hkv,
+__global__ __launch_bounds__(256) void merge_int4_kernel(const float* ws, const uint16_t* wv, float* out, int Hkv,
                                                           int Hq, int rv, int n_splits, int part_stride) {
   constexpr int NB = NC / 8;  // 16-byte groups of the value basis row
   constexpr int SG = 16;      // splits loaded together
-  __shared__ float cst[NC];
-  __shared__ float lst;
-  const int bq = blockIdx.x, hq_all = bq % Hq, b = bq / Hq;
-  const int h = hq_all / i4::GQ, hq = hq_all % i4::GQ;
+  static_assert(i4::GQ * NC <= 256 && i4::D * 2 == 256, "thread mapping");
+  __shared__ float cst[i4::GQ][NC];
+  __shared__ float lst[i4::GQ];
+  const int bh = blockIdx.x, h = bh % Hkv, b = bh / Hkv;
   const int tid = threadIdx.x;
-  const uint16_t* row = wv + ((size_t)h * i4::D + tid) * rv;  // B_v row d = tid, rv bf16 values
+  const int d = tid % i4::D, hp = tid / i4::D;  // output dim, pair of query heads
+  const uint16_t* row = wv + ((size_t)h * i4::D + d) * rv;  // B_v row d, rv bf16 values
   u4 braw[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) braw[i] = 8 * i < rv ? *(const u4*)(row + 8 * i) : u4{0, 0, 0, 0};
   const float* parts = ws + (size_t)(b * Hkv + h) * n_splits * part_stride;
-  if (tid < NC) {
-    float mx = -INFINITY, c = 0.0f, l = 0.0f;
+  if (tid < i4::GQ * NC) {
+    const int hq = tid / NC, c = tid % NC;
+    float mx = -INFINITY, cc = 0.0f, l = 0.0f;
     for (int s0 = 0; s0 < n_splits; s0 += SG) {
       float ms[SG], ls[SG], as[SG];
 #pragma unroll
@@ -633,33 +637,37 @@ __global__ __launch_bounds__(128) void merge_int4_kernel(const float* ws, const 
         const float* ps = parts + (size_t)(ok ? s0 + u : 0) * part_stride;
         ms[u] = ok ? ps[hq] : -INFINITY;
         ls[u] = ok ? ps[i4::GQ + hq] : 0.0f;
-        as[u] = ok ? ps[2 * i4::GQ + hq * NC + tid] : 0.0f;
+        as[u] = ok ? ps[2 * i4::GQ + hq * NC + c] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < SG; ++u) {
         if (ms[u] == -INFINITY) continue;  // a split with no token
         const float mn = fmaxf(mx, ms[u]);
         const float a0 = mx == -INFINITY ? 0.0f : exp2f(mx - mn), a1 = exp2f(ms[u] - mn);
-        c = c * a0 + a1 * as[u];
+        cc = cc * a0 + a1 * as[u];
         l = l * a0 + a1 * ls[u];
         mx = mn;
       }
     }
-    cst[tid] = c;
-    if (tid == 0) lst = l;
+    cst[hq][c] = cc;
+    if (c == 0) lst[hq] = l;
   }
   __syncthreads();
-  float o = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    if (8 * i >= rv) break;
+  for (int k = 0; k < 2; ++k) {
+    const int hq = 2 * hp + k;
+    float o = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w = braw[i][e >> 1];
-      o += __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * cst[8 * i + e];
+    for (int i = 0; i < NB; ++i) {
+      if (8 * i >= rv) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = braw[i][e >> 1];
+        o += __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * cst[hq][8 * i + e];
+      }
     }
+    out[((size_t)b * Hq + h * i4::GQ + hq) * i4::D + d] = o / lst[hq];
   }
-  out[((size_t)b * Hq + hq_all) * i4::D + tid] = o / lst;
 }
 
 template <int KS, int VS, bool VAR, int STG, int KB, int VB>
@@ -677,7 +685,7 @@ static hipError_t launch_int4(const Int4Args& a, int grid, const uint16_t* wv, f
   if (e == hipSuccess) e = mark(g_marks.end, st);
   if (e != hipSuccess) return e;
   constexpr int NC = 32 * ((VS + 1) / 2);
-  hipLaunchKernelGGL((merge_int4_kernel<NC>), dim3(a.B * a.Hq), dim3(128), 0, st, a.ws, wv, out, a.Hkv, a.Hq, a.rv,
+  hipLaunchKernelGGL((merge_int4_kernel<NC>), dim3(a.B * a.Hkv), dim3(256), 0, st, a.ws, wv, out, a.Hkv, a.Hq, a.rv,
                      a.n_splits, a.part_stride);
   return hipGetLastError();
 }
