@@ -556,6 +556,24 @@ static hipError_t launch_res(const ResArgs& a, int grid, const uint16_t* wv, flo
 
 int res_max_pages_per_split() { return rsd::MAX_SPLIT_PAGES; }
 
+// The compiled variants (key steps, value steps, staging rounds), used both to decide support and to launch, so that
+// a layout this kernel accepts always has a variant.  The value path reads a lane half's code dwords with one 8- or
+// 16-byte read, so the value steps are 2 or 4.
+#define KVC_RES_VARIANTS(X) \
+  X(3, 4, 10)               \
+  X(4, 4, 10)               \
+  X(2, 2, 10)               \
+  X(2, 4, 10)               \
+  X(4, 2, 10)
+
+static bool res_has_variant(int ks, int vs, int stg) {
+#define KVC_RES_HAS(KS_, VS_, STG_) \
+  if (ks == KS_ && vs == VS_ && stg <= STG_) return true;
+  KVC_RES_VARIANTS(KVC_RES_HAS)
+#undef KVC_RES_HAS
+  return false;
+}
+
 // The layouts this kernel serves; the rest of the residual layouts go to the general kernel.
 bool res_supported(const kvc_layout& L, int64_t hb) {
   if (L.shared || lat_bits_k(L) != 4 || lat_bits_v(L) != 4 || L.residual_bits != 2 || L.head_dim != 128 || L.variable_rank) return false;
@@ -563,6 +581,7 @@ bool res_supported(const kvc_layout& L, int64_t hb) {
   if (L.r_k_cap > 64 || L.r_v_cap > 64 || L.r_k_cap < 17 || L.r_v_cap < 17 || L.group % 16) return false;
   if (L.r_k_cap % 16 || L.r_v_cap % 16) return false;  // whole steps: no code or pair read past the rank
   if (hb > 16 * 256 * 10) return false;
+  if (!res_has_variant(L.r_k_cap / 16, L.r_v_cap / 16, ceil_div((int)hb, 16 * 256))) return false;
   return rsd::lds_layout(hb).total <= 160 * 1024;
 }
 
@@ -581,9 +600,7 @@ hipError_t launch_decode_res(const kvc_layout& L, const kvc_cache& C, const kvc_
   const int stg = ceil_div((int)S.hb, 16 * 256);
 #define KVC_TRYR(KS_, VS_, STG_) \
   if (KS == KS_ && VS == VS_ && stg <= STG_) return launch_res<KS_, VS_, STG_>(a, grid, in.wv, out, st);
-  KVC_TRYR(3, 4, 10)
-  KVC_TRYR(4, 4, 10)
-  KVC_TRYR(2, 2, 10)
+  KVC_RES_VARIANTS(KVC_TRYR)
 #undef KVC_TRYR
   return hipErrorInvalidValue;
 }

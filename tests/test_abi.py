@@ -341,3 +341,20 @@ def test_compaction_and_positions_rejections_without_launching():
                                            (shared, p(100), None, 0, p(194), -4)):
         inp = kvc.DecodeIn(2, 1, 100, p(80), p(96), qpos, p(112), 1, p(128), p(144), 0, 0, mask, words, 0, tp)
         assert lib.kvc_decode_attn(C.byref(L), C.byref(cache), C.byref(inp), p(160), p(176), 1 << 30, None) == want
+
+
+def test_residual_layouts_route_to_a_compiled_variant():
+    # the residual kernel takes a layout only when a variant is compiled for its key and value steps (value steps 2
+    # or 4); a layout with none goes to the general kernel, or is refused up front when that has none either, never
+    # accepted and then failed at launch
+    base = synth.WORKLOADS["residual_128k"].scaled(B=2, T=600, page_size=128)
+    for kw, path in [(dict(r_k=48, r_v=64), kvc.PATH_RES), (dict(r_k=64, r_v=64), kvc.PATH_RES),
+                     (dict(r_k=32, r_v=32), kvc.PATH_RES), (dict(r_k=32, r_v=64), kvc.PATH_RES),
+                     (dict(r_k=64, r_v=32), kvc.PATH_RES),
+                     (dict(r_k=48, r_v=48), kvc.PATH_HEAD),  # three value steps: the general kernel
+                     (dict(r_k=40, r_v=56), kvc.PATH_HEAD),  # ranks off the 16-coordinate steps
+                     (dict(r_k=48, r_v=32), None)]:          # valid, but no kernel variant: UNSUPPORTED
+        L = kvc.make_layout(**base.scaled(**kw).layout_kwargs())
+        assert kvc.layout_check(L) == (-2 if path is None else 0), kw
+        if path is not None:
+            assert kvc.decode_path(L) == path, kw

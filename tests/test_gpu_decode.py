@@ -26,6 +26,8 @@ CASES = [
     ("residual_128k", dict(B=2, T=700, r_k=64, r_v=64, page_size=128), [700, 255]),
     ("residual_128k", dict(B=2, T=600, r_k=32, r_v=32, page_size=128), [600, 129]),
     ("residual_128k", dict(B=2, T=500, r_k=48, r_v=64, group=16, page_size=128), [500, 33]),
+    ("residual_128k", dict(B=2, T=600, r_k=32, r_v=64, page_size=128), [600, 97]),
+    ("residual_128k", dict(B=2, T=600, r_k=64, r_v=32, page_size=128), [600, 300]),
     # ranks that are not multiples of 16: the general per-head kernel's residual path
     ("residual_128k", dict(B=2, T=700, r_k=40, r_v=56), [700, 300]),
     ("shared_latent_32k", dict(B=2, T=600), [600, 33]),
