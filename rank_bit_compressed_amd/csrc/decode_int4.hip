@@ -15,16 +15,15 @@
 //   K codes -> fp16 (code * scale + zero; 8 coordinates per lane per 16-coordinate step)
 //   -> K_pre = B_k c (4 tiles of 32 head dims; the basis fragments stay in registers)
 //   -> RoPE R(u) in packed fp16 on the pairs (j, j + 64), which sit in one lane (tiles m and m + 2)
-//   -> S = Q~ K~^T (rows: the wave's two query variants x 4 heads, replicated; columns: tokens),
-//      accumulated onto -m so the scores come out shifted by the running reference maximum; each lane
-//      keeps the four heads' scores of its token's variant
+//   -> S = Q~ K~^T (rows: the 4 heads of the wave's rotated query, replicated; columns: tokens), each lane
+//      keeping the four heads' scores of its token
 //   -> p = 2^s; P^T through a one-hot MFMA (tokens move into the reduction slots)
 //   V codes -> fp16 -> V^T through one-hot MFMAs -> acc += P V_latent (rows: heads, columns:
 //   latent coordinates).  The value basis is applied once per (b, head) in the merge, since
 //   sum_t p_t B c_t = B sum_t p_t c_t.
-// RoPE is split as R(t0 + 32 v + u) = R(t0 + 32 v) R(u) for page slot 32 v + u: R(u), u < 32, from an LDS
-// table on the key side; R(q_pos - t0 - 32 v) q on the query side, the two variants v = 0, 1 of the wave's
-// block rotated once per page.
+// RoPE is split as R(t0 + pb + u) = R(t0 + pb) R(u) for the slot pb + u of the wave whose first slot is pb:
+// R(u), u < 64, from an LDS table on the key side; R(q_pos - t0 - pb) q on the query side, rotated once per page
+// and wave.
 // Softmax keeps a reference maximum m per head and only raises it (rescaling acc and l) when a score
 // exceeds it by more than 2^8 in the exp2 domain; the probabilities then stay below 256, within the
 // fp16 operand range at full relative precision.  The merge uses the same m.
@@ -59,9 +58,10 @@ constexpr int D = 128, GQ = 4, NP = 64;
 constexpr int MAX_SPLIT_PAGES = 128;
 constexpr float TAU = 8.0f;   // lazy-max slack, log2 units
 constexpr int QROW = NP + 4;  // dwords per row of the rotated-query and RoPE tables (padded against bank conflicts)
-// the kernel's own LDS arrays (bytes): per wave the two query variants x 4 heads, the RoPE factors of in-block
-// positions 0..31, per wave the probabilities of a super-tile, per wave the decode order of its 64 slots
-constexpr int STATIC_LDS = 4 * 2 * GQ * QROW * 4 + 32 * QROW * 4 + 4 * 32 * GQ * 2 + 4 * 64;
+// the kernel's own LDS arrays (bytes): per wave the rotated query of 4 heads, the RoPE factors of the offsets
+// 0..63 from a wave's first slot, per wave the probabilities of a super-tile, per wave the decode order of its 64
+// slots
+constexpr int STATIC_LDS = 4 * GQ * QROW * 4 + 64 * QROW * 4 + 4 * 32 * GQ * 2 + 4 * 64;
 
 struct Lds {
   int meta_addr, meta_hb, meta_page, theta, qsrc, stage, stage_bytes, off_bytes, total;
@@ -125,13 +125,6 @@ struct Steps {
   static constexpr int value = N;
 };
 
-// x through an identity DPP move (quad_perm 0,1,2,3).  A select between two entries of one vector is otherwise
-// turned into an extract at a computed index, lowered as a chain of compares and selects over every entry; with
-// one operand passed through here it stays one v_cndmask.
-__device__ inline float dpp_id(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xE4, 0xF, 0xF, false));
-}
-
 // KS, VS: 16-coordinate steps of the key / value rank caps (2..4); VT: 32-coordinate value tiles; KB, VB: bits
 // of the key / value codes (4, or the lower-bit codecs 3 and 2, spread to the INT4 nibble layout as they are read)
 //
@@ -139,10 +132,8 @@ __device__ inline float dpp_id(float x) {
 // leaves later waves idle).  Variable rank: the wave takes its 64 slots in order of their number of
 // 16-coordinate steps (the "class", ceil(rank / 16)), equal classes in slot order -- a ballot per class, no
 // exchange with the other waves -- so that a super-tile runs only the steps of its largest rank instead of the
-// cap's.  Its token at page slot s = 32 v + u then sits at an arbitrary lane: R(t0 + 32 v + u) = R(t0 + 32 v)
-// R(u), R(u) for u < 32 from an LDS table on the key side, R(q_pos - t0 - 32 v) q on the query side as the two
-// variants of the wave's block, which fill the rows of the score product (rows 8i..8i+7 hold variant i % 2,
-// head = row % 4), so that every lane holds both variants' scores of its token and keeps one.
+// cap's.  Its token at page slot pb + u then sits at an arbitrary lane and reads its own R(u) from the table; the
+// query side is the same for all 64 slots, so every row of the score product holds a head of one rotated query.
 template <int KS, int VS, bool VAR, int STG, int KB, int VB>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   using namespace i4;
@@ -166,16 +157,16 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
   const int n_pages = max(0, min((T + P - 1) / P, lb0 + a.pages_per_split) - lb0);
   // Buffers that the page copies never touch live in arrays of their own, so that the compiler can tell
   // their reads apart from the LDS the copies write and does not wait for copies in flight before them.
-  // qbuf: per wave the two query variants x 4 heads (row 4 v + head), fp16 pairs (x_j, x_{j+64}); rtab:
-  // (cos, sin)(u theta_j) for u < 32; pbuf: per wave the probabilities of 32 tokens x 4 heads, fp16; sorder:
+  // qbuf: per wave the rotated query of 4 heads (row = head), fp16 pairs (x_j, x_{j+64}); rtab:
+  // (cos, sin)(u theta_j) for u < 64; pbuf: per wave the probabilities of 32 tokens x 4 heads, fp16; sorder:
   // per wave the decode order of its 64 slots.
-  __shared__ __attribute__((aligned(16))) uint32_t qbuf_all[4 * 2 * GQ * QROW];
-  __shared__ __attribute__((aligned(16))) uint32_t rtab[32 * QROW];
+  __shared__ __attribute__((aligned(16))) uint32_t qbuf_all[4 * GQ * QROW];
+  __shared__ __attribute__((aligned(16))) uint32_t rtab[64 * QROW];
   __shared__ __attribute__((aligned(16))) _Float16 pbuf_all[4 * 32 * GQ];
   __shared__ uint8_t sorder_all[4 * 64];
   static_assert(sizeof(qbuf_all) + sizeof(rtab) + sizeof(pbuf_all) + sizeof(sorder_all) == STATIC_LDS,
                 "static LDS accounting");
-  uint32_t* qbuf = qbuf_all + wv * 2 * GQ * QROW;
+  uint32_t* qbuf = qbuf_all + wv * GQ * QROW;
   uint8_t* sorder = sorder_all + wv * 64;
 
   // ---- page addresses of the split
@@ -250,11 +241,13 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     qsrc[j * 8 + 4 + hq] = x1 * sc;
   }
   __syncthreads();  // frequencies and the scaled query visible
-  // (cos, sin)(u theta_j) for u < 32 and every pair j; |u theta_j| < 32 turns, where v_sin / v_cos are accurate
-  for (int e = tid; e < 32 * NP; e += 256) {
+  // (cos, sin)(u theta_j) for the offsets u < 64 of a wave's slots from its base and every pair j (the angle reduced
+  // to half a turn in fp64; v_sin / v_cos take turns)
+  for (int e = tid; e < 64 * NP; e += 256) {
     const int u = e / NP, j = e % NP;
-    const float rev = (float)(u * tturn[j]);
-    rtab[u * QROW + j] = pack_h2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+    double rev = u * tturn[j];
+    rev -= rint(rev);
+    rtab[u * QROW + j] = pack_h2(__builtin_amdgcn_cosf((float)rev), __builtin_amdgcn_sinf((float)rev));
   }
   const double fj = tturn[lane];  // turns per position of pair `lane` (query rotation)
 
@@ -344,18 +337,15 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
     const int page_t0 = (lb0 + ip) * P;
     const int pb = 64 * wv;                                   // this wave's first slot of the page
     const int nvb = max(0, min(64, min(P, T - page_t0) - pb));  // its slots holding tokens
-    // the two query variants of the wave's block, q~ = R(q_pos - t0 - pb - 32 v) q, v = 0, 1; lane j: pair j
+    // the query rotated to the wave's base slot, q~ = R(q_pos - t0 - pb) q; lane j: pair j
     {
       const f4 qa = *(const f4*)&qsrc[lane * 8], qb = *(const f4*)&qsrc[lane * 8 + 4];
+      double rev = (double)(qpos - page_t0 - pb) * fj;
+      rev -= rint(rev);  // |rev| <= 1/2 turn; v_sin / v_cos take turns
+      const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        double rev = (double)(qpos - page_t0 - pb - 32 * v) * fj;
-        rev -= rint(rev);  // |rev| <= 1/2 turn; v_sin / v_cos take turns
-        const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-#pragma unroll
-        for (int hq = 0; hq < GQ; ++hq)
-          qbuf[(v * GQ + hq) * QROW + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
-      }
+      for (int hq = 0; hq < GQ; ++hq)
+        qbuf[hq * QROW + lane] = pack_h2(qa[hq] * cs - qb[hq] * sn, qb[hq] * cs + qa[hq] * sn);
     }
     // decode order of the wave's slots (variable rank): lane l holds slot pb + l, of class c (0 past the end)
     if constexpr (VAR) {
@@ -373,8 +363,8 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
       }
       if (c > 0) sorder[pos] = (uint8_t)lane;
     }
-    wave_sync();  // query variants and the order visible to the whole wave
-    const uint32_t* qrow = qbuf + (((t >> 3) & 1) * GQ + (t & 3)) * QROW + 4 * hf;  // score A operand row t
+    wave_sync();  // the rotated query and the order visible to the whole wave
+    const uint32_t* qrow = qbuf + (t & 3) * QROW + 4 * hf;  // score A operand row t: head t % 4
     const int nst_w = (nvb + 31) / 32;
 
     // the LDS words of super-tile k of this wave (decode position 32 k + t of its block), one super-tile ahead
@@ -430,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
       h8 kb[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) kb[s] = dequant_int4x8(cur.k[s], cur.pk[s]);
-      const uint32_t* rrow = rtab + (cur.slot & 31) * QROW + 4 * hf;
+      const uint32_t* rrow = rtab + (cur.slot & 63) * QROW + 4 * hf;  // R(u), u = the slot's offset from pb
       f16v sc = {};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -470,13 +460,10 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(Int4Args a) {
         }
       }
 
-      // ---- the token's four scores: entries 0-3 hold variant 0, entries 4-7 variant 1 (rows 8i + 4hf + head)
+      // ---- the token's four scores: entries 0-3 (rows 4hf + head)
       float s4[4];
-      {
-        const bool v1 = (cur.slot & 32) != 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s4[i] = (v1 ? dpp_id(sc[4 + i]) : sc[i]) - m_ref[i];
-      }
+      for (int i = 0; i < 4; ++i) s4[i] = sc[i] - m_ref[i];
       if (32 * (k + 1) > nvb && !cur.ok)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s4[i] = -INFINITY;
