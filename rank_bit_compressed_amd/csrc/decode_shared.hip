@@ -802,6 +802,11 @@ __global__ __launch_bounds__(512, 1) void decode_shared_role_kernel(DecodeShared
     return;
   }
 
+  // The value waves go first at the SIMD's issue arbiter: they stage and dequantize the tiles the key waves' chains
+  // read, and run the softmax and value product between the barriers (measured 648 -> 619 us on the block-shared
+  // 32K step, 659 -> 647 on the keep-mask form, the INT3 and positions forms unchanged).  Not for a split latent,
+  // whose key waves 0-1 are the critical path (516 -> 613 us on the Tucker group).
+  if constexpr (!SPLIT) __builtin_amdgcn_s_setprio(1);
   // ---- value wave of quarter wq
   uint8_t* raw_w = smem + LY.raw + wq * 4 * SRAW;  // its ring; super-tile k in slot k % 4
   const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw_w));
